@@ -1,0 +1,373 @@
+"""CPU oracle for selective sparse attention (test infrastructure only).
+
+This module is the plain, slow, obviously-correct statement of what the GPU
+library computes. It is test infrastructure: only the test-suite, the smoke
+check and the benchmark's CPU-baseline leg may import it. It shares no code
+with the GPU path (the HIP library and its Python binding) and imports nothing
+from it; both sides are fed the same seeded inputs.
+
+Everything is computed in float64 from exactly decoded inputs.
+
+What is computed (sources are the five pages on sparse attention):
+
+* Attention restricted to a visible key set S(i): softmax(q k^T / sqrt(d)) V
+  with every key outside S(i) masked to -inf before the softmax
+  ("A Guide to Sparse Attention in Large Models", section 2 "Core
+  Motivation", mask formula, and section 4.1 "Mask-based Implementation").
+  The literal "QK^T * Mask + (1-Mask)*(-inf)" formula multiplies 0 by -inf;
+  it is read as a masked fill, as the page's own example does.
+* Causality: a query at position p sees keys 0..p ("Sparse Attention",
+  lower-triangular dense pattern, cost N^2/2).
+* Sliding window of w keys including the query itself, plus g global tokens
+  at positions 0..g-1 ("Sparse Attention", sliding window + global figure,
+  cost N*w + N*g; "A Guide ...", section 2 pattern list).
+* Block-sparse selection: keys pooled by mean over 64-token blocks, each
+  query scores blocks by an unscaled dot product with the pooled key and keeps
+  the top blocks ("Sparse Attention Is Reshaping Production AI", "Learned
+  Block Routing" example), restricted here to complete past blocks, unioned
+  with the local window.
+* Token top-K from a lightweight indexer ("Sparse Attention for Long-Context
+  LLM Inference", sections on the lightweight indexer and Top-K;
+  "Sparse Attention in 2026", DSA paragraph): score s(i,j) is either
+  q_I . k_I,j or sum_h w_h * ReLU(q_I,h . k_I,j), the indexer carries no
+  positional encoding, and the K highest scoring past keys are kept.
+
+Selection keys. The pages fix no precision for the scores. Selection is made
+on key(j) = the float32 nearest (ties to even) to the exact real-valued score,
+with -0 read as +0, ordered by (key descending, index ascending). This key
+has one value whatever order a machine sums in, which is what makes index sets
+comparable bit for bit. It is obtained by a certified float64 evaluation (the
+float32 rounding of every point of a rigorous error interval agrees) and, when
+that fails, by exact rational arithmetic.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+from typing import Dict, Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+U52 = 2.0 ** -52
+
+# --------------------------------------------------------------------------
+# exact decoding of the storage formats
+# --------------------------------------------------------------------------
+
+
+def _fp8_e4m3fn_value(code: int) -> float:
+    """OCP 8-bit E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; 0x7F NaN."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * math.ldexp(m, -9)          # subnormal: m/8 * 2^-6
+    return sign * math.ldexp(8 + m, e - 10)      # (1 + m/8) * 2^(e-7)
+
+
+_FP8_TABLE = np.array([_fp8_e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+
+
+def decode(a: np.ndarray, fmt: str) -> np.ndarray:
+    """Storage array -> float64 (exact)."""
+    if fmt == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if fmt == "bf16":
+        bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    if fmt == "fp8":
+        return _FP8_TABLE[np.asarray(a, dtype=np.uint8)]
+    raise ValueError(fmt)
+
+
+# --------------------------------------------------------------------------
+# exact rounding of a rational to float32
+# --------------------------------------------------------------------------
+
+
+def f32_nearest(x: Fraction) -> np.float32:
+    """The float32 nearest to the rational x, ties to even (IEEE 754 RNE)."""
+    if x == 0:
+        return np.float32(0.0)
+    neg = x < 0
+    a = -x if neg else x
+    # exponent e with 2^e <= a < 2^(e+1)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if (Fraction(2) ** e) > a:
+        e -= 1
+    elif (Fraction(2) ** (e + 1)) <= a:
+        e += 1
+    quantum_exp = max(e, -126) - 23            # spacing of float32 around a
+    scaled = a / (Fraction(2) ** quantum_exp)
+    n = scaled.numerator // scaled.denominator
+    rem = scaled - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    if n * (Fraction(2) ** quantum_exp) > Fraction((2 - 2 ** -23)) * Fraction(2) ** 127:
+        val = math.inf
+    else:
+        val = math.ldexp(n, quantum_exp)
+    return np.float32(-val if neg else val)
+
+
+def _frac(v: float) -> Fraction:
+    return Fraction(float(v))
+
+
+def exact_dot(q: np.ndarray, k: np.ndarray) -> Fraction:
+    return sum((_frac(a) * _frac(b) for a, b in zip(q, k)), Fraction(0))
+
+
+def exact_key_dot(q: np.ndarray, k: np.ndarray) -> np.float32:
+    return f32_nearest(exact_dot(q, k))
+
+
+def exact_key_weighted_relu(qh: np.ndarray, w: np.ndarray, k: np.ndarray) -> np.float32:
+    total = Fraction(0)
+    for h in range(qh.shape[0]):
+        dh = exact_dot(qh[h], k)
+        if dh > 0:
+            total += _frac(w[h]) * dh
+    return f32_nearest(total)
+
+
+def exact_key_block(q: np.ndarray, kblock: np.ndarray) -> np.float32:
+    total = Fraction(0)
+    for t in range(kblock.shape[0]):
+        total += exact_dot(q, kblock[t])
+    return f32_nearest(total / kblock.shape[0])
+
+
+# --------------------------------------------------------------------------
+# selection keys, certified in float64 with exact fallback
+# --------------------------------------------------------------------------
+
+
+def _certify(y: np.ndarray, e: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    lo = (y - e).astype(np.float32)
+    hi = (y + e).astype(np.float32)
+    ok = lo == hi
+    return (lo + np.float32(0.0)), ok          # + 0.0 turns -0 into +0
+
+
+def keys_dot(q: np.ndarray, K: np.ndarray) -> np.ndarray:
+    """key(j) = nearest float32 of q . K[j] (exact real), for every row of K."""
+    n, d = K.shape
+    if n == 0:
+        return np.zeros(0, np.float32)
+    y = K @ q
+    A = np.abs(K) @ np.abs(q)
+    e = 2.0 * (d + 4) * U52 * A + 1e-300
+    keys, ok = _certify(y, e)
+    for j in np.nonzero(~ok)[0]:
+        keys[j] = exact_key_dot(q, K[j])
+    return keys
+
+
+def keys_weighted_relu(Q: np.ndarray, w: np.ndarray, K: np.ndarray) -> np.ndarray:
+    """key(j) = nearest float32 of sum_h w_h * max(0, Q[h] . K[j]) (exact real)."""
+    n, d = K.shape
+    H = Q.shape[0]
+    if n == 0:
+        return np.zeros(0, np.float32)
+    D = K @ Q.T                                   # [n, H]
+    A = np.abs(K) @ np.abs(Q).T
+    E = 2.0 * (d + 4) * U52 * A + 1e-300
+    pos = D > E
+    neg = D < -E
+    sign_ok = np.all(pos | neg | (w[None, :] == 0), axis=1)
+    R = np.where(pos, D, 0.0)
+    s = R @ w
+    Es = np.where(pos, E, 0.0) @ np.abs(w) + 2.0 * (H + 4) * U52 * (np.abs(R) @ np.abs(w)) + 1e-300
+    keys, ok = _certify(s, Es)
+    ok &= sign_ok
+    for j in np.nonzero(~ok)[0]:
+        keys[j] = exact_key_weighted_relu(Q, w, K[j])
+    return keys
+
+
+def keys_blocks(q: np.ndarray, K: np.ndarray, bs: int, n_blocks: int) -> np.ndarray:
+    """key(b) = nearest float32 of (1/bs) * sum_{t in block b} q . K[t] (exact real)."""
+    d = K.shape[1]
+    if n_blocks == 0:
+        return np.zeros(0, np.float32)
+    Kb = K[: n_blocks * bs].reshape(n_blocks, bs, d)
+    ksum = Kb.sum(axis=1)
+    kabs = np.abs(Kb).sum(axis=1)
+    y = (ksum @ q) / bs
+    A = (kabs @ np.abs(q)) / bs
+    e = 2.0 * (bs + d + 8) * U52 * A + 1e-300
+    keys, ok = _certify(y, e)
+    for b in np.nonzero(~ok)[0]:
+        keys[b] = exact_key_block(q, Kb[b])
+    return keys
+
+
+# --------------------------------------------------------------------------
+# top-K and visible sets
+# --------------------------------------------------------------------------
+
+
+def topk(keys: np.ndarray, K: int) -> np.ndarray:
+    """Indices of the min(K, n) largest keys, ties to the lower index; ascending."""
+    n = keys.shape[0]
+    kk = min(K, n)
+    order = np.lexsort((np.arange(n), -keys.astype(np.float64)))
+    return np.sort(order[:kk]).astype(np.int32)
+
+
+def window_global_set(p: int, w: int, g: int) -> np.ndarray:
+    """Keys j <= p with j >= p - w + 1 (window incl. self) or j < g (global)."""
+    win = np.arange(max(0, p - w + 1), p + 1)
+    glob = np.arange(0, min(g, p + 1))
+    return np.union1d(win, glob).astype(np.int32)
+
+
+def eligible_blocks(p: int, bs: int) -> int:
+    """Complete past blocks: block b is eligible when its last key bs*b+bs-1 <= p."""
+    return (p + 1) // bs
+
+
+def block_select(q: np.ndarray, K: np.ndarray, p: int, bs: int, nb: int) -> np.ndarray:
+    ne = eligible_blocks(p, bs)
+    keys = keys_blocks(q, K, bs, ne)
+    return topk(keys, nb)
+
+
+def blocks_set(blocks: Sequence[int], p: int, bs: int, w: int) -> np.ndarray:
+    parts = [np.arange(bs * b, bs * b + bs) for b in blocks]
+    parts.append(np.arange(max(0, p - w + 1), p + 1))
+    s = np.unique(np.concatenate(parts)) if parts else np.zeros(0, np.int64)
+    return s[s <= p].astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+
+
+def masked_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, S: np.ndarray,
+                     scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Dense masked attention over candidate keys K[0..n) with visible set S.
+
+    q [H, d]; K, V [n, d]; returns O [H, d] and LSE [H] (natural log).
+    """
+    z = (q @ K.T) * scale                        # [H, n]
+    mask = np.zeros(K.shape[0], dtype=bool)
+    mask[S] = True
+    z = np.where(mask[None, :], z, -np.inf)
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    l = e.sum(axis=1, keepdims=True)
+    O = (e @ V) / l
+    lse = (m + np.log(l))[:, 0]
+    return O, lse
+
+
+def softmax_rows(q: np.ndarray, K: np.ndarray, S: np.ndarray, scale: float) -> np.ndarray:
+    """The masked softmax probabilities (for checking that rows sum to one)."""
+    z = (q @ K.T) * scale
+    mask = np.zeros(K.shape[0], dtype=bool)
+    mask[S] = True
+    z = np.where(mask[None, :], z, -np.inf)
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    return e / e.sum(axis=1, keepdims=True)
+
+
+# --------------------------------------------------------------------------
+# workload driver
+# --------------------------------------------------------------------------
+
+
+class Rows:
+    """Oracle results for a list of (request, query row) pairs."""
+
+    def __init__(self) -> None:
+        self.sets: Dict[Tuple[int, int, int], np.ndarray] = {}      # (b, group, r) -> S
+        self.keys: Dict[Tuple[int, int, int], np.ndarray] = {}      # token/block keys
+        self.blocks: Dict[Tuple[int, int, int], np.ndarray] = {}    # (b, head, r) -> blocks
+        self.O: Dict[Tuple[int, int], np.ndarray] = {}              # (b, r) -> [Hq, d]
+        self.lse: Dict[Tuple[int, int], np.ndarray] = {}
+        self.pairs = 0
+        self.candidates = 0
+
+
+def run(wl, inp: Dict[str, np.ndarray], rows: Iterable[Tuple[int, int]],
+        attention: bool = True, keep_keys: bool = False) -> Rows:
+    """Run the full hot path for the given (request, query row) pairs.
+
+    ``wl`` is a workload description (attributes as in the input generator:
+    kind, Hq, Hkv, d, dtype, H_I, G_sel, score_mode, topk, window, ...).
+    """
+    res = Rows()
+    ctx = np.asarray(inp["ctx_len"]).astype(np.int64)
+    Q = inp["q"]
+    Kst = inp["k"]
+    Vst = inp["v"]
+    scale = 1.0 / math.sqrt(wl.d)
+    qpk = wl.Hq // wl.Hkv
+    for (b, r) in rows:
+        L = int(ctx[b])
+        p = L - wl.Nq + r
+        n = p + 1
+        Kb = [decode(Kst[b, h, :n], wl.dtype) for h in range(wl.Hkv)]
+        # visible set per query head
+        S_of_head: List[np.ndarray] = [None] * wl.Hq
+        if wl.kind in ("topk", "dsa_prefill", "dsa_decode"):
+            qi = decode(inp["q_idx"][b, r], wl.idx_q_dtype)            # [H_I, d_I]
+            hpg = wl.H_I // wl.G_sel
+            w = np.asarray(inp["w"], dtype=np.float32).astype(np.float64)
+            for g in range(wl.G_sel):
+                kg = g if wl.G_k == wl.G_sel else 0
+                Ki = decode(inp["k_idx"][b, :n, kg], wl.idx_k_dtype)
+                if wl.score_mode == "dot":
+                    keys = keys_dot(qi[g * hpg], Ki)
+                else:
+                    keys = keys_weighted_relu(qi[g * hpg:(g + 1) * hpg], w[g * hpg:(g + 1) * hpg], Ki)
+                S = topk(keys, wl.topk)
+                res.sets[(b, g, r)] = S
+                if keep_keys:
+                    res.keys[(b, g, r)] = keys
+                for h in range(wl.Hq):
+                    if h // (wl.Hq // wl.G_sel) == g:
+                        S_of_head[h] = S
+        elif wl.kind == "window_global":
+            S = window_global_set(p, wl.window, wl.n_global)
+            res.sets[(b, 0, r)] = S
+            S_of_head = [S] * wl.Hq
+        elif wl.kind == "blocks":
+            for h in range(wl.Hq):
+                qh = decode(Q[b, h, r], wl.dtype)
+                ne = eligible_blocks(p, wl.block_size)
+                keys = keys_blocks(qh, Kb[h // qpk], wl.block_size, ne)
+                blk = topk(keys, wl.top_blocks)
+                res.blocks[(b, h, r)] = blk
+                if keep_keys:
+                    res.keys[(b, h, r)] = keys
+                S = blocks_set(blk, p, wl.block_size, wl.window)
+                res.sets[(b, h, r)] = S
+                S_of_head[h] = S
+        elif wl.kind == "dense":
+            S = np.arange(n, dtype=np.int32)
+            res.sets[(b, 0, r)] = S
+            S_of_head = [S] * wl.Hq
+        else:
+            raise ValueError(wl.kind)
+        res.candidates += n * wl.Hq
+        res.pairs += sum(len(s) for s in S_of_head)
+        if attention:
+            O = np.zeros((wl.Hq, wl.d))
+            lse = np.zeros(wl.Hq)
+            for h in range(wl.Hq):
+                qh = decode(Q[b, h, r], wl.dtype)[None, :]
+                kvh = h // qpk
+                Vh = decode(Vst[b, kvh, :n], wl.dtype)
+                o, l = masked_attention(qh, Kb[kvh], Vh, S_of_head[h], scale)
+                O[h] = o[0]
+                lse[h] = l[0]
+            res.O[(b, r)] = O
+            res.lse[(b, r)] = lse
+    return res
+

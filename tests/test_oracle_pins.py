@@ -1,0 +1,382 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix.
+
+None of these compares the oracle with itself: each uses a library routine
+(torch SDPA, numpy's correctly rounded float casts, math.fsum), a hand-worked
+value, a closed form or a brute-force enumeration.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from fine_grained_top_amd import inputs as gen
+from fine_grained_top_amd import metrics
+import oracle as orc
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- formats
+def test_decode_fp8_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = orc.decode(codes, "fp8")
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    finite = ~np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    assert np.array_equal(mine[finite], ref[finite])
+    assert orc.decode(np.array([0x7E], np.uint8), "fp8")[0] == 448.0
+    assert orc.decode(np.array([0x01], np.uint8), "fp8")[0] == 2.0 ** -9
+
+
+def test_decode_bf16_matches_torch():
+    bits = np.random.default_rng(0).integers(0, 1 << 16, size=4096, dtype=np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]          # drop inf/nan
+    mine = orc.decode(bits, "bf16")
+    ref = torch.from_numpy(bits.astype(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(mine, ref)
+
+
+def test_generator_encodings_match_torch_rounding():
+    """The generator's RNE encoders agree with torch's casts (fp32 -> bf16 / fp8)."""
+    x = np.random.default_rng(1).standard_normal(20000).astype(np.float32)
+    x[:4] = [0.0, -0.0, 448.0, 2.0 ** -10]
+    b = gen.f32_to_bf16_bits(x)
+    tb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    assert np.array_equal(b, tb)
+    f8 = gen.f32_to_e4m3fn_bits(x)
+    t8 = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(f8, t8)
+
+
+# ---------------------------------------------------------------- exact keys
+def test_f32_nearest_matches_numpy_cast():
+    """Exact RNE rounding of rationals agrees with numpy's correctly rounded
+    float64 -> float32 cast on doubles (normal, subnormal and tie cases)."""
+    rng = np.random.default_rng(2)
+    xs = list(rng.standard_normal(2000) * 10.0 ** rng.integers(-40, 38, 2000))
+    f32 = rng.standard_normal(300).astype(np.float32)
+    nxt = np.nextafter(f32, np.float32(np.inf))
+    xs += list((f32.astype(np.float64) + nxt.astype(np.float64)) / 2)   # exact midpoints
+    xs += [2.0 ** -149, 3 * 2.0 ** -150, 2.0 ** -150, 1.5 * 2.0 ** -149, 2.0 ** -126 * (1 - 2 ** -25)]
+    for x in xs:
+        assert orc.f32_nearest(Fraction(x)) == np.float32(x), x
+
+
+def test_exact_keys_hand_worked_ties():
+    for c in _gold("f32_rounding.json")["cases"]:
+        q = np.array(c["q"])
+        k = np.array(c["k"])[None, :]
+        key = orc.keys_dot(q, k)[0]
+        assert key == np.float32(c["f32"]), c
+        assert not np.signbit(key)
+
+
+def test_keys_dot_equals_fsum_rounding():
+    """Random fp32 dot products: nearest float32 of the exact sum equals numpy's
+    cast of math.fsum (correctly rounded double) whenever that double is not a
+    float32 halfway point (never, for these draws)."""
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal(32).astype(np.float32).astype(np.float64)
+    K = rng.standard_normal((3000, 32)).astype(np.float32).astype(np.float64)
+    keys = orc.keys_dot(q, K)
+    ref = np.array([np.float32(math.fsum(q * K[j])) for j in range(K.shape[0])])
+    assert np.array_equal(keys, ref)
+
+
+def _brute_weighted_relu(Q, w, k):
+    tot = Fraction(0)
+    for h in range(Q.shape[0]):
+        dh = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(Q[h], k))
+        tot += Fraction(float(w[h])) * max(Fraction(0), dh)
+    return tot
+
+
+def test_keys_weighted_relu_brute_force():
+    rng = np.random.default_rng(4)
+    Q = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(rng.standard_normal((4, 16)).astype(np.float32))).astype(np.float64)
+    K = gen.e4m3fn_bits_to_f32(gen.f32_to_e4m3fn_bits(rng.standard_normal((400, 16)).astype(np.float32))).astype(np.float64)
+    w = rng.random(4).astype(np.float32).astype(np.float64)
+    keys = orc.keys_weighted_relu(Q, w, K)
+    for j in range(K.shape[0]):
+        ex = _brute_weighted_relu(Q, w, K[j])
+        # compare against numpy's cast of the exact value's nearest double when unambiguous
+        assert keys[j] == np.float32(float(ex))
+        assert abs(float(keys[j]) - float(ex)) <= abs(float(ex)) * 2 ** -24 + 1e-300
+    # a hand-worked case: heads [1,0] and [0,1], w = (0.5, 2), key (3, -1) -> 0.5*3 = 1.5
+    assert orc.keys_weighted_relu(np.eye(2), np.array([0.5, 2.0]), np.array([[3.0, -1.0]]))[0] == 1.5
+    # every head negative -> +0
+    z = orc.keys_weighted_relu(np.eye(2), np.array([0.5, 2.0]), np.array([[-3.0, -1.0]]))[0]
+    assert z == 0.0 and not np.signbit(z)
+
+
+def test_keys_blocks_brute_force():
+    rng = np.random.default_rng(5)
+    d, bs, nb = 8, 4, 6
+    q = rng.standard_normal(d)
+    K = rng.standard_normal((bs * nb + 3, d))
+    keys = orc.keys_blocks(q, K, bs, nb)
+    for b in range(nb):
+        ex = sum(Fraction(float(a)) * Fraction(float(c)) for t in range(bs)
+                 for a, c in zip(q, K[b * bs + t])) / bs
+        assert keys[b] == np.float32(float(ex))
+        assert abs(float(keys[b]) - float(ex)) <= abs(float(ex)) * 2 ** -24 + 1e-300
+    # hand-worked: q = (1, 2), block of two keys (1, 0) and (3, 1) -> ((1) + (3 + 2)) / 2 = 3
+    assert orc.keys_blocks(np.array([1.0, 2.0]), np.array([[1.0, 0.0], [3.0, 1.0]]), 2, 1)[0] == 3.0
+
+
+# ---------------------------------------------------------------- top-K (P-f)
+def _brute_topk(keys, K):
+    remaining = list(range(len(keys)))
+    out = []
+    for _ in range(min(K, len(keys))):
+        best = remaining[0]
+        for j in remaining[1:]:
+            if keys[j] > keys[best]:          # strict: ties keep the lower index
+                best = j
+        out.append(best)
+        remaining.remove(best)
+    return sorted(out)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_brute_force_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 60))
+    keys = rng.integers(-3, 4, size=n).astype(np.float32)      # many ties
+    keys[rng.random(n) < 0.2] = -0.0
+    for K in (1, 3, n // 2 + 1, n, n + 5):
+        assert list(orc.topk(keys, K)) == _brute_topk(list(keys), K)
+
+
+def test_topk_equals_full_stable_sort():
+    rng = np.random.default_rng(7)
+    keys = rng.standard_normal(5000).astype(np.float32)
+    keys[::7] = keys[3]                     # ties
+    order = sorted(range(len(keys)), key=lambda j: (-float(keys[j]), j))
+    assert list(orc.topk(keys, 300)) == sorted(order[:300])
+
+
+# ---------------------------------------------------------------- attention
+def _sdpa_causal(q, k, v):
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=True).numpy()
+
+
+def test_full_topk_is_causal_sdpa():
+    """P-a: with K >= i+1 every row sees all past keys: equals causal SDPA (fp64)."""
+    import dataclasses
+    wl = dataclasses.replace(gen.WORKLOADS["tiny_topk_f32_small"], N=90, Nq=90, topk=1000, needles=0)
+    inp = gen.generate(wl)
+    res = orc.run(wl, inp, [(0, r) for r in range(wl.Nq)])
+    q = orc.decode(inp["q"][0], "f32")
+    k = orc.decode(inp["k"][0], "f32")
+    v = orc.decode(inp["v"][0], "f32")
+    ref = _sdpa_causal(q, k, v)[0]
+    got = np.stack([res.O[(0, r)][0] for r in range(wl.Nq)])
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def _fixed_pattern_mask(n, window, stride):
+    """The fixed local + dilated causal mask of 'Sparse Attention Is Reshaping
+    Production AI' (Fixed Patterns): a key is kept if it is not in the future
+    and either at most `window` positions back or at a multiple of `stride`."""
+    m = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        for j in range(i + 1):
+            m[i, j] = (i - j) <= window or (j % stride) == 0
+    return m
+
+
+def test_window_is_banded_attention():
+    """P-b: window of w keys (incl. self) plus one global token == the page's
+    fixed local+dilated mask with window w-1 and a stride longer than the
+    sequence; attention under it equals torch SDPA with that boolean mask."""
+    n, w, d = 70, 9, 16
+    rng = np.random.default_rng(8)
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    # with a stride longer than the sequence only key 0 is a stride position,
+    # so the page's mask is a w-key window plus one global token
+    mask = _fixed_pattern_mask(n, w - 1, 10 * n)
+    scale = 1 / math.sqrt(d)
+    for i in range(n):
+        S = orc.window_global_set(i, w, 1)
+        assert np.array_equal(S, np.nonzero(mask[i])[0])
+        o, _ = orc.masked_attention(q[i:i + 1], k[: i + 1], v[: i + 1], S, scale)
+        # the same attention via torch with an explicit boolean mask
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[i:i + 1]), torch.from_numpy(k[: i + 1]), torch.from_numpy(v[: i + 1]),
+            attn_mask=torch.from_numpy(mask[i, : i + 1][None, :])).numpy()
+        assert np.max(np.abs(o - ref)) < 1e-12
+
+
+def test_softmax_rows_sum_to_one():
+    """P-c."""
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((3, 32)) * 4
+    K = rng.standard_normal((500, 32))
+    V = rng.standard_normal((500, 32))
+    S = np.sort(rng.choice(500, 77, replace=False))
+    P = orc.softmax_rows(q, K, S, 1 / math.sqrt(32))
+    assert np.max(np.abs(P.sum(axis=1) - 1)) <= 1e-12
+    _, lse = orc.masked_attention(q, K, V, S, 1 / math.sqrt(32))
+    z = (q @ K[S].T) / math.sqrt(32)
+    assert np.max(np.abs(np.exp(z - lse[:, None]).sum(axis=1) - 1)) <= 1e-12
+
+
+def test_window_global_pair_counts():
+    """P-d: sum |S(i)| against the closed form, brute force and the pages' N*w + N*g."""
+    g = _gold("pages_arithmetic.json")["window_global_counts"]
+    for n, w, gg, expect in g["cases"]:
+        assert metrics.window_global_pairs(n, w, gg) == expect
+    for n, w, gg in [(12, 2, 2), (40, 7, 3), (33, 33, 0), (50, 10, 10), (16384, 512, 16)]:
+        tot = sum(len(orc.window_global_set(p, w, gg)) for p in range(n))
+        assert tot == metrics.window_global_pairs(n, w, gg)
+        if n <= 50:
+            brute = sum(1 for i in range(n) for j in range(i + 1) if j >= i - w + 1 or j < gg)
+            assert tot == brute
+        assert tot <= n * w + n * gg
+
+
+def test_pages_pair_arithmetic():
+    """P-e: the page's dense and window pair counts at N=128,000, w=4,096."""
+    g = _gold("pages_arithmetic.json")["pairs"]
+    N, w = g["N"], g["w"]
+    assert round(N * N / 1e9, 1) == g["dense_pairs_billion_printed"]
+    assert round(N * w / 1e9, 1) == g["window_pairs_billion_printed"]
+    assert N / w == 31.25 and round(N / w) != g["ratio_printed"] and abs(N / w - g["ratio_printed"]) < 1
+    assert round(g["N_small"] ** 2 / 1e6, 1) == g["entries_small_million_printed"]
+    # the causal window count the oracle implies has the page's N*w as its leading term
+    assert metrics.window_global_pairs(N, w, 0) == N * w - w * (w - 1) // 2
+
+
+def test_kv_cache_memory_example():
+    """P-l: the page's memory estimate (125 / 25 / 100 GB)."""
+    g = _gold("pages_arithmetic.json")["kv_cache_gb"]
+    a = g["args"]
+    dense = metrics.kv_cache_memory_gb(a["batch"], a["ctx"], a["kv_dim"], a["layers"], 0.0, a["bytes"])
+    sparse = metrics.kv_cache_memory_gb(a["batch"], a["ctx"], a["kv_dim"], a["layers"], 0.8, a["bytes"])
+    assert dense == g["dense"] and abs(sparse - g["sparse_0.8"]) < 1e-9
+    assert abs(dense - sparse - g["freed"]) < 1e-9
+
+
+# ---------------------------------------------------------------- workloads
+def test_tiny_needles_and_early_rows():
+    """P-g and P-h on the tiny fp32 workload (full size)."""
+    wl = gen.WORKLOADS["tiny_topk_f32"]
+    inp = gen.generate(wl)
+    rows = list(range(64)) + [int(i) for i in inp["needles"][:, 1]]
+    res = orc.run(wl, inp, [(0, r) for r in rows])
+    for (b, i, j) in inp["needles"]:
+        assert j in res.sets[(0, 0, int(i))]
+    q = orc.decode(inp["q"][0], "f32")
+    k = orc.decode(inp["k"][0], "f32")
+    v = orc.decode(inp["v"][0], "f32")
+    ref = _sdpa_causal(q[:, :64], k[:, :64], v[:, :64])[0]
+    for r in range(64):
+        assert np.array_equal(res.sets[(0, 0, r)], np.arange(r + 1))
+        assert np.max(np.abs(res.O[(0, r)][0] - ref[r])) < 1e-12
+
+
+def test_prefill_needles_selected():
+    """P-g on the DSA-style prefill workload: every planted needle is selected
+    by its query row (rows of the needles only, indexer + top-K)."""
+    wl = gen.WORKLOADS["dsa_prefill"]
+    inp = {}
+    inp["ctx_len"] = gen.lengths(wl)
+    inp["q_idx"] = gen.normal(wl.seed, gen.TID["q_idx"], (wl.B, wl.Nq, wl.H_I, wl.d_I), wl.idx_q_dtype)
+    inp["k_idx"] = gen.normal(wl.seed, gen.TID["k_idx"], (wl.B, wl.N, wl.G_k, wl.d_I), wl.idx_k_dtype)
+    inp["w"] = gen.uniform01(wl.seed, gen.TID["w"], (wl.H_I,))
+    needles = gen._plant_needles(wl, inp)
+    assert len(needles) == 655
+    w = inp["w"].astype(np.float64)
+    for (b, i, j) in needles[:40]:
+        qi = orc.decode(inp["q_idx"][b, i], "bf16")
+        Ki = orc.decode(inp["k_idx"][b, : i + 1, 0], "bf16")
+        S = orc.topk(orc.keys_weighted_relu(qi, w, Ki), wl.topk)
+        assert j in S
+
+
+def test_blocks_full_coverage_is_causal():
+    """P-i: with top_blocks >= eligible blocks and window >= p+1 -> full causal."""
+    import dataclasses
+    wl = dataclasses.replace(gen.WORKLOADS["block_sparse_small"], N=200, Nq=200, top_blocks=10,
+                             window=400, Hq=1, Hkv=1)
+    inp = gen.generate(wl)
+    res = orc.run(wl, inp, [(0, r) for r in range(0, 200, 7)])
+    q = orc.decode(inp["q"][0], "bf16")
+    k = orc.decode(inp["k"][0], "bf16")
+    v = orc.decode(inp["v"][0], "bf16")
+    ref = _sdpa_causal(q, k, v)[0]
+    for r in range(0, 200, 7):
+        assert np.array_equal(res.sets[(0, 0, r)], np.arange(r + 1))
+        assert np.max(np.abs(res.O[(0, r)][0] - ref[r])) < 1e-12
+
+
+def test_block_selection_brute_force():
+    """Block selection on a tiny case: pooled-mean scores by exact rationals,
+    ranked by brute force over all eligible blocks."""
+    rng = np.random.default_rng(10)
+    bs, d, n = 4, 6, 37
+    q = rng.standard_normal(d)
+    K = rng.standard_normal((n, d))
+    for p in (3, 4, 15, 36):
+        ne = (p + 1) // bs
+        ex = [sum(Fraction(float(a)) * Fraction(float(c)) for t in range(bs)
+                  for a, c in zip(q, K[b * bs + t])) / bs for b in range(ne)]
+        want = sorted(sorted(range(ne), key=lambda b: (-ex[b], b))[:3])
+        assert list(orc.block_select(q, K, p, bs, 3)) == want
+
+
+def test_gqa_equals_replicated_mha():
+    """P-j: a query-head group sharing one KV head equals MHA with K/V copied."""
+    rng = np.random.default_rng(11)
+    d, n = 16, 50
+    q = rng.standard_normal((4, d))
+    K = rng.standard_normal((n, d))
+    V = rng.standard_normal((n, d))
+    S = np.sort(rng.choice(n, 20, replace=False))
+    O, lse = orc.masked_attention(q, K, V, S, 0.25)
+    for h in range(4):
+        o1, l1 = orc.masked_attention(q[h:h + 1], K.copy(), V.copy(), S, 0.25)
+        assert np.max(np.abs(o1[0] - O[h])) < 1e-13 and abs(l1[0] - lse[h]) < 1e-13
+
+
+def test_decode_equals_last_prefill_row():
+    """P-k: the decode output of a request equals the prefill output at its last row."""
+    import dataclasses
+    wl = gen.WORKLOADS["dsa_decode_small"]
+    dec = dataclasses.replace(wl, B=1, N=700, len_range=(650, 700), topk=64)
+    inp = gen.generate(dec)
+    L = int(inp["ctx_len"][0])
+    rd = orc.run(dec, inp, [(0, 0)])
+    pre = dataclasses.replace(dec, Nq=L, len_range=None, N=L)
+    pin = dict(inp)
+    pin["ctx_len"] = np.array([L], np.int32)
+    pin["q"] = np.zeros((1, dec.Hq, L, dec.d), inp["q"].dtype)
+    pin["q"][:, :, L - 1] = inp["q"][:, :, 0]
+    pin["q_idx"] = np.zeros((1, L, dec.H_I, dec.d_I), inp["q_idx"].dtype)
+    pin["q_idx"][:, L - 1] = inp["q_idx"][:, 0]
+    pin["k"] = inp["k"][:, :, :L]
+    pin["v"] = inp["v"][:, :, :L]
+    pin["k_idx"] = inp["k_idx"][:, :L]
+    rp = orc.run(pre, pin, [(0, L - 1)])
+    assert np.array_equal(rd.O[(0, 0)], rp.O[(0, L - 1)])
+    for g in range(dec.G_sel):
+        assert np.array_equal(rd.sets[(0, g, 0)], rp.sets[(0, g, L - 1)])
+
+
+def test_generator_is_deterministic():
+    wl = gen.WORKLOADS["dsa_decode_small"]
+    a = gen.generate(wl)
+    b = gen.generate(wl)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
