@@ -1,0 +1,445 @@
+// Sparse attention over a visible key set S(i).
+//
+//  * attn_index_mfma: bf16, d = 128, index lists. One workgroup serves one
+//    (request, query row, gather group, split): the Hg <= 16 query heads that
+//    share both the index list and the KV head are the 16 MFMA rows, so one
+//    gather of each selected K/V row serves the whole group (GQA/MQA). Each
+//    wave walks tiles of 32 selected keys: K rows are loaded straight into
+//    MFMA operand registers (S^T = K Q^T, 16x16x32 bf16), the softmax is
+//    online in float32 (exp2 domain), V rows are staged in LDS and read back
+//    transposed as the B operand of O += P V. P enters the MFMA as a bf16
+//    hi/lo pair so the product keeps ~16 bits of P; with Hg <= 8 the lo part
+//    rides in the unused MFMA rows. Splits of the index list are merged by
+//    attn_combine with their (max, sum) pairs.
+//  * attn_generic: any mode, f32 or bf16, d <= 128; one wave per (row, head):
+//    lanes score 64 candidates at a time, then sweep them over the dims.
+#include "common.h"
+#include "internal.h"
+
+namespace sp {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- candidates
+// Enumerates the visible set of one query row: t -> key position or -1.
+struct Visible {
+  int mode, p, count;
+  const int32_t* list;   // index list (mode 1) or block list (mode 3)
+  int K;                 // list length
+  int g_end, w_start, bs, nb_keys;
+
+  SP_DEV void init(const AttnParams& a, int b, int h, int r, int pos) {
+    mode = a.mode;
+    p = pos;
+    list = nullptr;
+    K = a.K;
+    if (mode == 0) {
+      count = p + 1;
+    } else if (mode == 1) {
+      const int gsel = h / (a.Hq / a.G_sel);
+      list = a.sel + b * a.sels[0] + gsel * a.sels[1] + r * a.sels[2];
+      count = K;
+    } else if (mode == 2) {
+      g_end = min(a.n_global, p + 1);
+      w_start = max(max(0, p - a.window + 1), g_end);
+      count = g_end + max(0, p - w_start + 1);
+    } else {
+      list = a.sel + b * a.sels[0] + h * a.sels[1] + r * a.sels[2];
+      bs = a.bs;
+      w_start = max(0, p - a.window + 1);
+      nb_keys = K * bs;
+      count = nb_keys + max(0, p - w_start + 1);
+    }
+    if (p < 0) count = 0;
+  }
+  SP_DEV int key(int t) const {
+    if (mode == 0) return t;
+    if (mode == 1) {
+      const int j = list[t];
+      return (j >= 0 && j <= p) ? j : -1;
+    }
+    if (mode == 2) return t < g_end ? t : w_start + (t - g_end);
+    if (t < nb_keys) {
+      const int blk = list[t / bs];
+      if (blk < 0) return -1;
+      const int j = blk * bs + t % bs;
+      return (j < w_start && j <= p) ? j : -1;
+    }
+    return w_start + (t - nb_keys);
+  }
+};
+
+SP_DEV float ldv(const void* p, int dt, int64_t i) {
+  return dt == DT_F32 ? ((const float*)p)[i] : bf16_to_f32(((const uint16_t*)p)[i]);
+}
+
+// ---------------------------------------------------------------- generic
+__global__ __launch_bounds__(64) void attn_generic_kernel(AttnParams a) {
+  const int r = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int L = min(a.ctx_len ? a.ctx_len[b] : a.ctx, a.ctx);
+  const int pos = L - a.Nq + r;
+  const int kvh = h / (a.Hq / a.Hkv);
+  Visible vis;
+  vis.init(a, b, h, r, pos);
+  __shared__ float qs[128];
+  __shared__ float ps[64];
+  __shared__ int js[64];
+  const int64_t qb = b * a.q.s[0] + h * a.q.s[1] + r * a.q.s[2];
+  for (int c = lane; c < a.d; c += 64) qs[c] = ldv(a.q.p, a.q.dt, qb + c);
+  __syncthreads();
+  const int64_t kb = b * a.k.s[0] + kvh * a.k.s[1];
+  const int64_t vb = b * a.v.s[0] + kvh * a.v.s[1];
+  float m = -INFINITY, l = 0.f, acc0 = 0.f, acc1 = 0.f;
+  for (int t0 = 0; t0 < vis.count; t0 += 64) {
+    const int t = t0 + lane;
+    const int j = t < vis.count ? vis.key(t) : -1;
+    float z = -INFINITY;
+    if (j >= 0) {
+      float s = 0.f;
+      const int64_t kr = kb + (int64_t)j * a.k.s[2];
+      for (int c = 0; c < a.d; ++c) s = fmaf(qs[c], ldv(a.k.p, a.k.dt, kr + c), s);
+      z = s * a.scale;
+    }
+    const float tm = wave_max(z);
+    const float mn = fmaxf(m, tm);
+    float pj = 0.f, alpha = 1.f;
+    if (mn > -INFINITY) {
+      pj = j >= 0 ? expf(z - mn) : 0.f;
+      alpha = expf(m - mn);
+    }
+    l = l * alpha + wave_sum(pj);
+    m = mn;
+    acc0 *= alpha;
+    acc1 *= alpha;
+    ps[lane] = pj;
+    js[lane] = j;
+    __syncthreads();
+    const int nt = min(64, vis.count - t0);
+    for (int u = 0; u < nt; ++u) {
+      const int ju = js[u];
+      if (ju < 0) continue;
+      const float pu = ps[u];
+      const int64_t vr = vb + (int64_t)ju * a.v.s[2];
+      if (lane < a.d) acc0 = fmaf(pu, ldv(a.v.p, a.v.dt, vr + lane), acc0);
+      if (lane + 64 < a.d) acc1 = fmaf(pu, ldv(a.v.p, a.v.dt, vr + lane + 64), acc1);
+    }
+    __syncthreads();
+  }
+  float* o = a.o + b * a.os[0] + h * a.os[1] + r * a.os[2];
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (lane < a.d) o[lane] = acc0 * inv;
+  if (lane + 64 < a.d) o[lane + 64] = acc1 * inv;
+  if (a.lse && lane == 0) a.lse[((int64_t)b * a.Hq + h) * a.Nq + r] = l > 0.f ? m + logf(l) : -INFINITY;
+}
+
+// ---------------------------------------------------------------- MFMA gather
+constexpr int kVStride = 132;   // LDS row stride of staged V in 16-bit words (264 B)
+
+struct SplitInfo {
+  int nsplit, per;   // splits per row, list entries per split (multiple of 32)
+};
+
+template <bool PACKLO>
+__global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int Hg, SplitInfo si,
+                                                              float* part) {
+  const int split = blockIdx.x;
+  const int ngg = a.Hq / Hg;
+  const int rowid = blockIdx.y;             // (b, r, gg) flattened
+  const int gg = rowid % ngg;
+  const int r = (rowid / ngg) % a.Nq;
+  const int b = rowid / (ngg * a.Nq);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int qq = lane >> 4, c16 = lane & 15;
+  const int h0 = gg * Hg;
+  const int kvh = h0 / (a.Hq / a.Hkv);
+  const int gsel = h0 / (a.Hq / a.G_sel);
+  const int L = min(a.ctx_len ? a.ctx_len[b] : a.ctx, a.ctx);
+  const int pos = L - a.Nq + r;
+  const int32_t* list = a.sel + b * a.sels[0] + gsel * a.sels[1] + r * a.sels[2];
+  const int t_begin = split * si.per;
+  const int t_end = min(a.K, t_begin + si.per);
+
+  __shared__ __attribute__((aligned(16))) uint16_t vs[4][32 * kVStride];
+  __shared__ int idxs[4][32];
+
+  // Q^T as the B operand: lane holds head c16, dims 32*qq + 8*ks + v
+  bf16x8 Qb[4];
+  {
+    const int hh = c16;
+    if (hh < Hg) {
+      const uint16_t* qp = (const uint16_t*)a.q.p + b * a.q.s[0] + (h0 + hh) * a.q.s[1] + r * a.q.s[2] + 32 * qq;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) Qb[ks] = *(const bf16x8*)(qp + 8 * ks);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) Qb[ks] = (bf16x8){};
+    }
+  }
+  const float c = a.scale * kLog2e;
+  float m = -INFINITY, l = 0.f;
+  f32x4 O[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) O[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const uint16_t* kbase = (const uint16_t*)a.k.p + b * a.k.s[0] + kvh * a.k.s[1];
+  const uint16_t* vbase = (const uint16_t*)a.v.p + b * a.v.s[0] + kvh * a.v.s[1];
+
+  for (int t0 = t_begin + 32 * wid; t0 < t_end; t0 += 128) {
+    // tile of 32 list entries
+    if (lane < 32) {
+      const int t = t0 + lane;
+      int j = t < t_end ? list[t] : -1;
+      if (j > pos) j = -1;
+      idxs[wid][lane] = j;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // K rows for the two 16-key subtiles: row c16 (and 16 + c16), dims 32*qq..+32
+    u32x4 kr[2][4];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      int j = idxs[wid][16 * st + c16];
+      j = j < 0 ? 0 : j;
+      const uint16_t* kp = kbase + (int64_t)j * a.k.s[2] + 32 * qq;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kr[st][ks] = *(const u32x4*)(kp + 8 * ks);
+    }
+    // V rows: chunk u covers key qq + 4u, 16-byte column c16
+    u32x4 vr[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      int j = idxs[wid][qq + 4 * u];
+      j = j < 0 ? 0 : j;
+      vr[u] = *(const u32x4*)(vbase + (int64_t)j * a.v.s[2] + 8 * c16);
+    }
+    // S^T = K Q^T
+    f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&kr[0][ks], Qb[ks], S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&kr[1][ks], Qb[ks], S1, 0, 0, 0);
+    }
+    // lane: head c16, keys 4*qq + v (S0) and 16 + 4*qq + v (S1)
+    float z[8];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      z[v] = idxs[wid][4 * qq + v] >= 0 ? S0[v] * c : -INFINITY;
+      z[4 + v] = idxs[wid][16 + 4 * qq + v] >= 0 ? S1[v] * c : -INFINITY;
+    }
+    float tm = z[0];
+#pragma unroll
+    for (int v = 1; v < 8; ++v) tm = fmaxf(tm, z[v]);
+    tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
+    tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+    const float mn = fmaxf(m, tm);
+    float alpha = 1.f, ps = 0.f;
+    float pv[8];
+    if (mn > -INFINITY) {
+      alpha = exp2f(m - mn);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        pv[v] = exp2f(z[v] - mn);
+        ps += pv[v];
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 8; ++v) pv[v] = 0.f;
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l = l * alpha + ps;
+    m = mn;
+    // rescale O: lane holds rows (heads) 4*qq + v; alpha of head hh lives in lane hh
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      int hrow = 4 * qq + v;
+      if (PACKLO) hrow &= 7;
+      const float av = __shfl(alpha, hrow, 64);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) O[nt][v] *= av;
+    }
+    // P as the A operand (row = head c16, k = 8*qq + v <-> key mapping above)
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int v2 = 0; v2 < 4; ++v2) {
+      const float x0 = pv[2 * v2], x1 = pv[2 * v2 + 1];
+      const uint32_t h0b = f32_to_bf16_rne(x0), h1b = f32_to_bf16_rne(x1);
+      const float r0 = x0 - bf16_to_f32(h0b), r1 = x1 - bf16_to_f32(h1b);
+      ph[v2] = h0b | (h1b << 16);
+      pl[v2] = f32_to_bf16_rne(r0) | (f32_to_bf16_rne(r1) << 16);
+    }
+    // pv[0..3] are keys 4qq+0..3 (k = 8qq+0..3), pv[4..7] keys 16+4qq+0..3 (k = 8qq+4..7)
+    u32x4 Ahi, Alo;
+    if (PACKLO) {
+      // rows 0..7: hi of heads 0..7; rows 8..15: lo of heads 0..7 (fetched from lane - 8)
+      uint32_t plo_src[4];
+#pragma unroll
+      for (int v2 = 0; v2 < 4; ++v2) plo_src[v2] = __shfl(pl[v2], (lane & ~15) | (c16 & 7), 64);
+#pragma unroll
+      for (int v2 = 0; v2 < 4; ++v2) Ahi[v2] = c16 < 8 ? ph[v2] : plo_src[v2];
+    } else {
+#pragma unroll
+      for (int v2 = 0; v2 < 4; ++v2) {
+        Ahi[v2] = ph[v2];
+        Alo[v2] = pl[v2];
+      }
+    }
+    // stage V rows in LDS: row = key, 16-byte column c16
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      uint16_t* dst = &vs[wid][(qq + 4 * u) * kVStride + 8 * c16];
+      *(u32x2*)dst = (u32x2){vr[u][0], vr[u][1]};
+      *(u32x2*)(dst + 4) = (u32x2){vr[u][2], vr[u][3]};
+    }
+    __builtin_amdgcn_wave_barrier();
+    // B operand: column dim 16*nt + c16, k = 8*qq + v -> keys
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      uint16_t bv[8];
+      const int dcol = 16 * nt + c16;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        bv[v] = vs[wid][(4 * qq + v) * kVStride + dcol];
+        bv[4 + v] = vs[wid][(16 + 4 * qq + v) * kVStride + dcol];
+      }
+      u32x4 Bv;
+#pragma unroll
+      for (int v2 = 0; v2 < 4; ++v2) Bv[v2] = (uint32_t)bv[2 * v2] | ((uint32_t)bv[2 * v2 + 1] << 16);
+      O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&Ahi, *(const bf16x8*)&Bv, O[nt], 0, 0, 0);
+      if (!PACKLO)
+        O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&Alo, *(const bf16x8*)&Bv, O[nt], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // merge the 4 waves through LDS (reuses the V staging area)
+  __syncthreads();
+  float* red = (float*)&vs[0][0];                 // [4][16][128] partial O
+  float* ml = red + 4 * 16 * 128;                 // [4][16][2]
+  static_assert(sizeof(float) * (4 * 16 * 128 + 4 * 16 * 2) <= sizeof(uint16_t) * 4 * 32 * kVStride,
+                "merge area must fit in the V staging buffer");
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[(wid * 16 + 4 * qq + v) * 128 + 16 * nt + c16] = O[nt][v];
+  if (qq == 0) {
+    ml[(wid * 16 + c16) * 2 + 0] = m;
+    ml[(wid * 16 + c16) * 2 + 1] = l;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < Hg * 128; e += 256) {
+    const int hh = e >> 7, dd = e & 127;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[(w * 16 + hh) * 2]);
+    float Ls = 0.f, Os = 0.f;
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mw = ml[(w * 16 + hh) * 2];
+        const float f = mw > -INFINITY ? exp2f(mw - M) : 0.f;
+        Ls += ml[(w * 16 + hh) * 2 + 1] * f;
+        float ov = red[(w * 16 + hh) * 128 + dd];
+        if (PACKLO) ov += red[(w * 16 + hh + 8) * 128 + dd];
+        Os += ov * f;
+      }
+    }
+    if (si.nsplit == 1) {
+      float* o = a.o + b * a.os[0] + (h0 + hh) * a.os[1] + r * a.os[2];
+      o[dd] = Ls > 0.f ? Os / Ls : 0.f;
+      if (a.lse && dd == 0)
+        a.lse[((int64_t)b * a.Hq + h0 + hh) * a.Nq + r] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+    } else {
+      float* pp = part + (((int64_t)rowid * si.nsplit + split) * Hg + hh) * 130;
+      pp[dd] = Os;
+      if (dd == 0) {
+        pp[128] = M;
+        pp[129] = Ls;
+      }
+    }
+  }
+}
+
+// merge splits: one workgroup of 128 threads per (b, r, gather group, head)
+__global__ __launch_bounds__(128) void attn_combine_kernel(AttnParams a, int Hg, SplitInfo si,
+                                                           const float* part) {
+  const int ngg = a.Hq / Hg;
+  const int rowid = blockIdx.x, hh = blockIdx.y;
+  const int gg = rowid % ngg;
+  const int r = (rowid / ngg) % a.Nq;
+  const int b = rowid / (ngg * a.Nq);
+  const int dd = threadIdx.x;
+  float M = -INFINITY;
+  for (int s = 0; s < si.nsplit; ++s)
+    M = fmaxf(M, part[(((int64_t)rowid * si.nsplit + s) * Hg + hh) * 130 + 128]);
+  float Ls = 0.f, Os = 0.f;
+  if (M > -INFINITY)
+    for (int s = 0; s < si.nsplit; ++s) {
+      const float* pp = part + (((int64_t)rowid * si.nsplit + s) * Hg + hh) * 130;
+      const float f = pp[128] > -INFINITY ? exp2f(pp[128] - M) : 0.f;
+      Ls += pp[129] * f;
+      Os += pp[dd] * f;
+    }
+  const int h = gg * Hg + hh;
+  float* o = a.o + b * a.os[0] + h * a.os[1] + r * a.os[2];
+  o[dd] = Ls > 0.f ? Os / Ls : 0.f;
+  if (a.lse && dd == 0) a.lse[((int64_t)b * a.Hq + h) * a.Nq + r] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------- dispatch
+static int gather_group(const AttnParams& a) {
+  const int per_kv = a.Hq / a.Hkv, per_sel = a.Hq / a.G_sel;
+  return per_kv < per_sel ? per_kv : per_sel;
+}
+
+static bool mfma_index_ok(const AttnParams& a) {
+  return a.mode == 1 && a.q.dt == DT_BF16 && a.d == 128 && gather_group(a) <= 16;
+}
+
+static SplitInfo pick_split(const AttnParams& a, int Hg) {
+  const int rows = a.B * a.Nq * (a.Hq / Hg);
+  const int tiles = (a.K + 31) / 32;
+  int want = (2048 + rows - 1) / rows;            // aim for >= 2048 workgroups
+  int maxs = (tiles + 3) / 4;                     // at least 4 tiles (one per wave) per split
+  int ns = want < maxs ? want : maxs;
+  if (ns < 1) ns = 1;
+  int per_tiles = (tiles + ns - 1) / ns;
+  SplitInfo si;
+  si.per = per_tiles * 32;
+  si.nsplit = (a.K + si.per - 1) / si.per;
+  return si;
+}
+
+size_t attn_ws_bytes(const AttnParams& a) {
+  if (!mfma_index_ok(a)) return 0;
+  const int Hg = gather_group(a);
+  const SplitInfo si = pick_split(a, Hg);
+  if (si.nsplit == 1) return 0;
+  const size_t rows = (size_t)a.B * a.Nq * (a.Hq / Hg);
+  return rows * si.nsplit * Hg * 130 * sizeof(float);
+}
+
+hipError_t launch_attention(const AttnParams& a, hipStream_t st) {
+  if (mfma_index_ok(a)) {
+    const int Hg = gather_group(a);
+    const SplitInfo si = pick_split(a, Hg);
+    const int rows = a.B * a.Nq * (a.Hq / Hg);
+    float* part = (float*)a.ws;
+    dim3 grid(si.nsplit, rows);
+    if (Hg <= 8)
+      hipLaunchKernelGGL(attn_index_mfma_kernel<true>, grid, dim3(256), 0, st, a, Hg, si, part);
+    else
+      hipLaunchKernelGGL(attn_index_mfma_kernel<false>, grid, dim3(256), 0, st, a, Hg, si, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || si.nsplit == 1) return e;
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(rows, Hg), dim3(128), 0, st, a, Hg, si,
+                       (const float*)part);
+    return hipGetLastError();
+  }
+  dim3 grid(a.Nq, a.Hq, a.B);
+  hipLaunchKernelGGL(attn_generic_kernel, grid, dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace sp

@@ -1,0 +1,80 @@
+// Device helpers shared by the libspattn kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define SP_DEV __device__ __forceinline__
+
+namespace sp {
+
+constexpr int kWave = 64;
+
+SP_DEV float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+SP_DEV uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+// Two fp8 E4M3FN codes (bytes 2*HI, 2*HI+1 of w) -> packed bf16 pair (exact:
+// every E4M3FN value is a bf16 value).
+template <bool HI>
+SP_DEV uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  auto f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+  uint32_t a = __float_as_uint(f[0]);
+  uint32_t b = __float_as_uint(f[1]);
+  return (a >> 16) | (b & 0xFFFF0000u);
+}
+
+SP_DEV float fp8_to_f32(uint32_t code) {
+  auto f = __builtin_amdgcn_cvt_pk_f32_fp8(code & 0xFFu, false);
+  return f[0];
+}
+
+// Order-preserving map float -> uint32 (larger float => larger key); -0 -> +0.
+SP_DEV uint32_t f32_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+SP_DEV float order_key_f32(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// wave-level reductions (64 lanes)
+SP_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+SP_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+SP_DEV uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+// Number of active lanes below this one whose predicate is set.
+SP_DEV uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+SP_DEV uint64_t ballot(bool p) { return __ballot(p); }
+
+}  // namespace sp

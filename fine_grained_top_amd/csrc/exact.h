@@ -1,0 +1,256 @@
+// Exact selection keys on the device.
+//
+// A selection key is the float32 nearest (ties to even) to the exact real
+// value of a score: a dot product q.k, a ReLU-gated weighted sum of such dot
+// products over indexer heads, or the mean over a block of keys of q.k. The
+// key does not depend on summation order, so index sets chosen on it are
+// reproducible bit for bit on any machine.
+//
+// Evaluation: float64 with a rigorous error bound first (products of inputs
+// with <= 24-bit significands are exact in float64; an n-term float64 sum in
+// any order is within n * 2^-53 * sum|terms| of the exact sum). When the whole
+// error interval rounds to one float32 that value is the key. Otherwise (the
+// exact value sits next to a float32 rounding boundary) the sum is formed
+// exactly in a wide two's-complement fixed-point accumulator and rounded by
+// hand. Input significands are at most 24 bits, exponents within float32's.
+#pragma once
+#include "common.h"
+
+namespace sp {
+
+SP_DEV double load_f64(const void* p, int dtype, int64_t i) {
+  if (dtype == DT_F32) return (double)((const float*)p)[i];
+  if (dtype == DT_BF16) return (double)bf16_to_f32(((const uint16_t*)p)[i]);
+  return (double)fp8_to_f32(((const uint8_t*)p)[i]);
+}
+
+// value = m * 2^e with m an integer of at most 24 bits (exact for our formats).
+SP_DEV void split24(double v, int64_t& m, int& e, bool& neg) {
+  neg = v < 0;
+  double a = neg ? -v : v;
+  if (a == 0.0) { m = 0; e = 0; return; }
+  int ex;
+  double f = frexp(a, &ex);                 // a = f * 2^ex, f in [0.5, 1)
+  m = (int64_t)ldexp(f, 24);
+  e = ex - 24;
+}
+
+// Wide accumulator: NL little-endian 32-bit limbs, two's complement, value =
+// sum(limb_i * 2^(32 i)) * 2^BASE.
+template <int NL>
+struct WideAcc {
+  uint32_t l[NL];
+  SP_DEV void clear() {
+    for (int i = 0; i < NL; ++i) l[i] = 0;
+  }
+  // add (neg ? -1 : 1) * m * 2^bit, m < 2^57, bit >= 0
+  SP_DEV void add(uint64_t m, int bit, bool neg) {
+    if (m == 0) return;
+    int li = bit >> 5, sh = bit & 31;
+    uint32_t p[3];
+    p[0] = (uint32_t)(m << sh);
+    p[1] = sh ? (uint32_t)(m >> (32 - sh)) : (uint32_t)(m >> 32);
+    p[2] = sh ? (uint32_t)(m >> (64 - sh)) : 0u;
+    if (!neg) {
+      uint64_t c = 0;
+      for (int i = li; i < NL; ++i) {
+        uint64_t s = (uint64_t)l[i] + c + (i - li < 3 ? p[i - li] : 0u);
+        l[i] = (uint32_t)s;
+        c = s >> 32;
+        if (i - li >= 2 && c == 0) break;
+      }
+    } else {
+      int64_t br = 0;
+      for (int i = li; i < NL; ++i) {
+        int64_t s = (int64_t)l[i] - br - (int64_t)(i - li < 3 ? p[i - li] : 0u);
+        br = s < 0 ? 1 : 0;
+        l[i] = (uint32_t)s;
+        if (i - li >= 2 && br == 0) break;
+      }
+    }
+  }
+  SP_DEV bool negative() const { return (l[NL - 1] >> 31) != 0; }
+  SP_DEV bool zero() const {
+    for (int i = 0; i < NL; ++i)
+      if (l[i]) return false;
+    return true;
+  }
+  SP_DEV void negate() {
+    uint64_t c = 1;
+    for (int i = 0; i < NL; ++i) {
+      uint64_t s = (uint64_t)(~l[i]) + c;
+      l[i] = (uint32_t)s;
+      c = s >> 32;
+    }
+  }
+  SP_DEV int top_bit() const {
+    for (int i = NL - 1; i >= 0; --i)
+      if (l[i]) return 32 * i + 31 - __builtin_clz(l[i]);
+    return -1;
+  }
+  SP_DEV uint32_t bit(int b) const { return b < 0 ? 0u : (l[b >> 5] >> (b & 31)) & 1u; }
+  SP_DEV bool any_below(int b) const {   // any set bit at index < b
+    if (b <= 0) return false;
+    int li = b >> 5, sh = b & 31;
+    for (int i = 0; i < li; ++i)
+      if (l[i]) return true;
+    return sh ? (l[li] & ((1u << sh) - 1u)) != 0 : false;
+  }
+  SP_DEV uint32_t bits(int lo, int n) const {  // n <= 25 bits starting at lo (lo >= 0)
+    uint32_t r = 0;
+    for (int k = 0; k < n; ++k) r |= bit(lo + k) << k;
+    return r;
+  }
+};
+
+// Round (acc * 2^(base)) to the nearest float32, ties to even.
+template <int NL>
+SP_DEV float wide_to_f32(WideAcc<NL> acc, int base) {
+  bool neg = acc.negative();
+  if (neg) acc.negate();
+  int P = acc.top_bit();
+  if (P < 0) return 0.0f;
+  int E = P + base;
+  if (E > 127) return neg ? -INFINITY : INFINITY;
+  int qexp = (E > -126 ? E : -126) - 23;
+  int qb = qexp - base;               // bit index of the float32 ulp
+  uint32_t mant;
+  bool guard, sticky;
+  if (qb <= 0) {                       // every bit is kept
+    mant = acc.bits(0, P + 1) << (-qb);
+    guard = false;
+    sticky = false;
+  } else {
+    mant = acc.bits(qb, P - qb + 1);
+    guard = acc.bit(qb - 1) != 0;
+    sticky = acc.any_below(qb - 1);
+  }
+  if (guard && (sticky || (mant & 1u))) mant += 1u;
+  float r = ldexpf((float)mant, qexp);
+  return neg ? -r : r;
+}
+
+// Exact dot product sum_c q[c]*k[c] into an accumulator with base -352 (20 limbs).
+constexpr int kDotBase = -352;
+typedef WideAcc<20> DotAcc;
+SP_DEV void exact_dot_acc(DotAcc& acc, const void* q, int qt, int64_t qoff, const void* k, int kt,
+                          int64_t koff, int n) {
+  for (int c = 0; c < n; ++c) {
+    int64_t mq, mk;
+    int eq, ek;
+    bool nq, nk;
+    split24(load_f64(q, qt, qoff + c), mq, eq, nq);
+    split24(load_f64(k, kt, koff + c), mk, ek, nk);
+    if (mq == 0 || mk == 0) continue;
+    acc.add((uint64_t)mq * (uint64_t)mk, eq + ek - kDotBase, nq != nk);
+  }
+}
+
+// ---------------------------------------------------------------- keys
+
+struct IndexerRow {        // one query row of one selection group
+  const void* q;           // q_idx row base: head h at q + h*qh_stride
+  int qt;                  // dtype
+  int64_t qh_stride;       // elements between heads
+  const void* k;           // k_idx row base of key 0 for this group
+  int kt;
+  int64_t k_stride;        // elements between keys
+  const float* w;          // weights of the group's heads (stride w_stride), may be null in DOT
+  int64_t w_stride;
+  int H;                   // heads in the group (1 in DOT)
+  int d;                   // indexer head dim
+  int relu;                // 1 = weighted ReLU, 0 = plain dot
+};
+
+SP_DEV float exact_key_slow(const IndexerRow& r, int64_t j) {
+  int64_t koff = j * r.k_stride;
+  if (!r.relu) {
+    DotAcc acc;
+    acc.clear();
+    exact_dot_acc(acc, r.q, r.qt, 0, r.k, r.kt, koff, r.d);
+    return wide_to_f32(acc, kDotBase);
+  }
+  WideAcc<30> tot;   // base -544
+  tot.clear();
+  for (int h = 0; h < r.H; ++h) {
+    DotAcc acc;
+    acc.clear();
+    exact_dot_acc(acc, r.q, r.qt, h * r.qh_stride, r.k, r.kt, koff, r.d);
+    if (acc.negative() || acc.zero()) continue;      // ReLU
+    int64_t mw;
+    int ew;
+    bool nw;
+    split24((double)r.w[h * r.w_stride], mw, ew, nw);
+    if (mw == 0) continue;
+    for (int i = 0; i < 20; ++i)
+      if (acc.l[i]) tot.add((uint64_t)acc.l[i] * (uint64_t)mw, ew + kDotBase + 32 * i + 544, nw);
+  }
+  return wide_to_f32(tot, -544);
+}
+
+SP_DEV bool certify(double y, double e, float& key) {
+  float lo = (float)(y - e), hi = (float)(y + e);
+  key = lo + 0.0f;
+  return lo == hi;
+}
+
+// key of candidate j: float32 nearest to the exact score
+SP_DEV float exact_key(const IndexerRow& r, int64_t j) {
+  const double g52 = 2.220446049250313e-16;  // 2^-52
+  int64_t koff = j * r.k_stride;
+  if (!r.relu) {
+    double y = 0.0, A = 0.0;
+    for (int c = 0; c < r.d; ++c) {
+      double t = load_f64(r.q, r.qt, c) * load_f64(r.k, r.kt, koff + c);
+      y += t;
+      A += fabs(t);
+    }
+    float key;
+    if (certify(y, 2.0 * (r.d + 4) * g52 * A + 1e-300, key)) return key;
+    return exact_key_slow(r, j);
+  }
+  double s = 0.0, Es = 0.0, Ar = 0.0;
+  bool ok = true;
+  for (int h = 0; h < r.H; ++h) {
+    double y = 0.0, A = 0.0;
+    for (int c = 0; c < r.d; ++c) {
+      double t = load_f64(r.q, r.qt, h * r.qh_stride + c) * load_f64(r.k, r.kt, koff + c);
+      y += t;
+      A += fabs(t);
+    }
+    double E = 2.0 * (r.d + 4) * g52 * A + 1e-300;
+    double w = (double)r.w[h * r.w_stride];
+    if (y > E) {
+      s += w * y;
+      Es += fabs(w) * E;
+      Ar += fabs(w * y);
+    } else if (!(y < -E) && w != 0.0) {
+      ok = false;
+    }
+  }
+  float key;
+  if (ok && certify(s, Es + 2.0 * (r.H + 4) * g52 * Ar + 1e-300, key)) return key;
+  return exact_key_slow(r, j);
+}
+
+// Block key: float32 nearest to (1/bs) * sum_{t<bs} q . k[t]; bs a power of two.
+SP_DEV float exact_block_key(const void* q, int qt, const void* k, int kt, int64_t k_stride,
+                             int bs, int log2bs, int d) {
+  const double g52 = 2.220446049250313e-16;
+  double y = 0.0, A = 0.0;
+  for (int t = 0; t < bs; ++t)
+    for (int c = 0; c < d; ++c) {
+      double v = load_f64(q, qt, c) * load_f64(k, kt, t * k_stride + c);
+      y += v;
+      A += fabs(v);
+    }
+  double e = 2.0 * (bs * d + 8) * g52 * A + 1e-300;
+  float key;
+  if (certify(ldexp(y, -log2bs), ldexp(e, -log2bs), key)) return key;
+  DotAcc acc;
+  acc.clear();
+  for (int t = 0; t < bs; ++t) exact_dot_acc(acc, q, qt, 0, k, kt, t * k_stride, d);
+  return wide_to_f32(acc, kDotBase - log2bs);
+}
+
+}  // namespace sp

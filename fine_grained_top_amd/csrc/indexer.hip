@@ -1,0 +1,283 @@
+// Indexer scores: s(i,j) = q_I[i] . k_I[j]  or  sum_h w_h * max(0, q_I[i,h] . k_I[j]).
+//
+// Two kernels:
+//  * idx_mfma64: d_I = 64, bf16 queries, bf16 or fp8-e4m3 keys, one key head
+//    shared by every selection group, at most 128 (query row, head) slots per
+//    request (decode and short prefill). Keys stream from HBM once; each wave
+//    turns 32 keys into a 32x32x16 bf16 MFMA B operand (fp8 upconverted to
+//    bf16 exactly) against the resident query slots, and reduces the heads
+//    of a group in-lane in the epilogue.
+//  * idx_generic: any supported dtype/shape, one key per thread, FMA chain.
+// Both record, per 512/256-key chunk, the largest |k| element, from which
+// idx_err derives each row's rigorous bound |score - key|.
+#include "common.h"
+#include "internal.h"
+
+namespace sp {
+
+constexpr int kMfmaChunk = 512;   // keys per workgroup in idx_mfma64
+constexpr int kGenChunk = 256;    // keys per workgroup in idx_generic
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+SP_DEV float load_val(const void* p, int dt, int64_t i) {
+  if (dt == DT_F32) return ((const float*)p)[i];
+  if (dt == DT_BF16) return bf16_to_f32(((const uint16_t*)p)[i]);
+  return fp8_to_f32(((const uint8_t*)p)[i]);
+}
+
+// ----------------------------------------------------------------------------
+template <int KT, int NMB, int HPG, bool RELU>
+__global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int L = min(p.ctx_len ? p.ctx_len[b] : p.ctx, p.ctx);
+  const int j0 = blockIdx.x * kMfmaChunk;
+  if (j0 >= L) return;
+  const int M = p.Nq * p.H_I;
+  const int hshift = __builtin_ctz(p.H_I);
+
+  // A operands: query slot m = 32*mb + col, dims 32*half + 8*s + v (s = k-step)
+  bf16x8 A[NMB][4];
+  float W[NMB][16];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+    const int m = 32 * mb + col;
+    if (m < M) {
+      const int r = m >> hshift, h = m & (p.H_I - 1);
+      const uint16_t* qp = (const uint16_t*)p.q.p + b * p.q.s[0] + r * p.q.s[1] + h * p.q.s[2] + 32 * half;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) A[mb][s] = *(const bf16x8*)(qp + 8 * s);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) A[mb][s] = (bf16x8){};
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int ms = 32 * mb + 8 * (v >> 2) + 4 * half + (v & 3);
+      float wv = 0.f;
+      if (RELU && ms < M) {
+        const int r = ms >> hshift, h = ms & (p.H_I - 1);
+        wv = p.w[b * p.ws_[0] + r * p.ws_[1] + h * p.ws_[2]];
+      }
+      W[mb][v] = wv;
+    }
+  }
+
+  u16x2 kmx = {0, 0};
+  constexpr int TPW = kMfmaChunk / 32 / 4;   // tiles per wave
+  // raw key bytes for all tiles of this wave
+  u32x4 raw[TPW][KT == DT_FP8 ? 2 : 4];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int j = j0 + (wid + 4 * i) * 32 + col;
+    const int jc = j < L ? j : L - 1;
+    if (KT == DT_FP8) {
+      const uint8_t* kp = (const uint8_t*)p.k.p + b * p.k.s[0] + (int64_t)jc * p.k.s[1] + 32 * half;
+      raw[i][0] = *(const u32x4*)kp;
+      raw[i][1] = *(const u32x4*)(kp + 16);
+    } else {
+      const uint16_t* kp = (const uint16_t*)p.k.p + b * p.k.s[0] + (int64_t)jc * p.k.s[1] + 32 * half;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) raw[i][c] = *(const u32x4*)(kp + 8 * c);
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int j = j0 + (wid + 4 * i) * 32 + col;
+    // B operands (bf16) for the 4 k-steps
+    u32x4 Bw[4];
+    if (KT == DT_FP8) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t w0 = raw[i][s >> 1][2 * (s & 1)], w1 = raw[i][s >> 1][2 * (s & 1) + 1];
+        Bw[s][0] = fp8x2_to_bf16x2<false>(w0);
+        Bw[s][1] = fp8x2_to_bf16x2<true>(w0);
+        Bw[s][2] = fp8x2_to_bf16x2<false>(w1);
+        Bw[s][3] = fp8x2_to_bf16x2<true>(w1);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) Bw[s] = raw[i][s];
+    }
+    if (j < L) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t a = Bw[s][c] & 0x7FFF7FFFu;
+          kmx = __builtin_elementwise_max(kmx, *(const u16x2*)&a);
+        }
+    }
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[mb][s], *(const bf16x8*)&Bw[s], acc, 0, 0, 0);
+      // epilogue: lane holds key j, slots 32*mb + 8*(v/4) + 4*half + v%4
+#pragma unroll
+      for (int gi = 0; gi < 16 / HPG; ++gi) {
+        float sc = 0.f;
+#pragma unroll
+        for (int t = 0; t < HPG; ++t) {
+          const int v = gi * HPG + t;
+          sc = RELU ? fmaf(W[mb][v], fmaxf(acc[v], 0.f), sc) : acc[v];
+        }
+        const int v0 = gi * HPG;
+        const int m0 = 32 * mb + 8 * (v0 >> 2) + 4 * half + (v0 & 3);
+        if (m0 < M) {
+          const int r = m0 >> hshift, g = (m0 & (p.H_I - 1)) / HPG;
+          if (j <= L - p.Nq + r) p.scores[b * p.ss[0] + g * p.ss[1] + r * p.ss[2] + j] = sc;
+        }
+      }
+    }
+  }
+
+  // largest |k| element of this chunk (valid keys only)
+  __shared__ uint32_t red[4];
+  uint32_t km = max((uint32_t)kmx[0], (uint32_t)kmx[1]);
+  km = wave_max_u32(km);
+  if (lane == 0) red[wid] = km;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t m4 = max(max(red[0], red[1]), max(red[2], red[3]));
+    p.kmax[(int64_t)b * p.nchunk + blockIdx.x] = bf16_to_f32(m4);
+  }
+}
+
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void idx_generic_kernel(IndexerParams p) {
+  const int b = blockIdx.z;
+  const int row = blockIdx.y;
+  const int r = row / p.G_sel, g = row % p.G_sel;
+  const int L = min(p.ctx_len ? p.ctx_len[b] : p.ctx, p.ctx);
+  const int pos = L - p.Nq + r;
+  const int j0 = blockIdx.x * kGenChunk;
+  const int kg = p.G_k == 1 ? 0 : g;
+  const bool do_kmax = (r == 0) && (p.G_k == 1 ? g == 0 : true);
+  if (j0 >= L || (!do_kmax && j0 > pos)) return;
+  __shared__ float qs[4096];
+  __shared__ float wsm[64];
+  const int H = p.hpg, d = p.d_I;
+  for (int i = threadIdx.x; i < H * d; i += blockDim.x) {
+    const int h = i / d, c = i % d;
+    qs[i] = load_val(p.q.p, p.q.dt, b * p.q.s[0] + r * p.q.s[1] + (g * H + h) * p.q.s[2] + c);
+  }
+  if ((int)threadIdx.x < H)
+    wsm[threadIdx.x] = p.relu ? p.w[b * p.ws_[0] + r * p.ws_[1] + (g * H + threadIdx.x) * p.ws_[2]] : 1.f;
+  __syncthreads();
+  const int j = j0 + threadIdx.x;
+  float kmx = 0.f;
+  if (j < L) {
+    const int64_t kb = b * p.k.s[0] + (int64_t)j * p.k.s[1] + kg * p.k.s[2];
+    if (j <= pos) {
+      float s = 0.f;
+      for (int h = 0; h < H; ++h) {
+        float dd = 0.f;
+        for (int c = 0; c < d; ++c) dd = fmaf(qs[h * d + c], load_val(p.k.p, p.k.dt, kb + c), dd);
+        s = p.relu ? fmaf(wsm[h], fmaxf(dd, 0.f), s) : dd;
+      }
+      p.scores[b * p.ss[0] + g * p.ss[1] + r * p.ss[2] + j] = s;
+    }
+    if (do_kmax)
+      for (int c = 0; c < d; ++c) kmx = fmaxf(kmx, fabsf(load_val(p.k.p, p.k.dt, kb + c)));
+  }
+  if (do_kmax) {
+    __shared__ float red[4];
+    kmx = wave_max(kmx);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = kmx;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      p.kmax[((int64_t)b * p.G_k + kg) * p.nchunk + blockIdx.x] =
+          fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Row bound: |s~ - key| <= C * sum_h |w_h| * ||q_h||_1 * max|k|, where C covers
+// float32 accumulation of d products in any order (u = 2^-23, conservative for
+// MFMA and FMA chains alike), the ReLU/weight/head-sum chain, and the final
+// rounding of the exact score to float32; plus a 25% margin.
+__global__ void idx_err_kernel(IndexerParams p) {
+  const int row = blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = blockIdx.y;
+  if (row >= p.Nq * p.G_sel) return;
+  const int r = row / p.G_sel, g = row % p.G_sel;
+  const int kg = p.G_k == 1 ? 0 : g;
+  const int L = min(p.ctx_len ? p.ctx_len[b] : p.ctx, p.ctx);
+  const int nch = min(p.nchunk, (L + p.chunk - 1) / p.chunk);
+  float km = 0.f;
+  for (int c = 0; c < nch; ++c) km = fmaxf(km, p.kmax[((int64_t)b * p.G_k + kg) * p.nchunk + c]);
+  double coef = 0.0;
+  for (int h = 0; h < p.hpg; ++h) {
+    double a = 0.0;
+    for (int c = 0; c < p.d_I; ++c)
+      a += fabs((double)load_val(p.q.p, p.q.dt, b * p.q.s[0] + r * p.q.s[1] + (g * p.hpg + h) * p.q.s[2] + c));
+    const double wv = p.relu ? (double)p.w[b * p.ws_[0] + r * p.ws_[1] + (g * p.hpg + h) * p.ws_[2]] : 1.0;
+    coef += fabs(wv) * a;
+  }
+  const double u = 1.0 / 8388608.0;   // 2^-23
+  auto gam = [&](double n) { return n * u / (1.0 - n * u); };
+  const double C = 1.25 * (gam(p.d_I + 2) + gam(p.hpg + 2) * (1.0 + gam(p.d_I + 2)) + u);
+  const double e = C * coef * (double)km * (1.0 + 1e-6) + 1e-30;
+  p.err[((int64_t)b * p.G_sel + g) * p.Nq + r] = (float)e * (1.0f + 1e-6f);
+}
+
+size_t indexer_ws_bytes(int B, int G_k, int ctx) {
+  const int nchunk = (ctx + kGenChunk - 1) / kGenChunk;   // the larger count of the two kernels
+  return (size_t)B * G_k * nchunk * sizeof(float);
+}
+
+template <int KT, int NMB, int HPG, bool RELU>
+static void launch_mfma(const IndexerParams& p, hipStream_t st) {
+  dim3 grid((p.ctx + kMfmaChunk - 1) / kMfmaChunk, p.B);
+  hipLaunchKernelGGL((idx_mfma64_kernel<KT, NMB, HPG, RELU>), grid, dim3(256), 0, st, p);
+}
+
+template <int KT, int NMB>
+static void dispatch_hpg(const IndexerParams& p, hipStream_t st) {
+  if (!p.relu) return launch_mfma<KT, NMB, 1, false>(p, st);
+  if (p.hpg == 1) return launch_mfma<KT, NMB, 1, true>(p, st);
+  if (p.hpg == 2) return launch_mfma<KT, NMB, 2, true>(p, st);
+  return launch_mfma<KT, NMB, 4, true>(p, st);
+}
+
+template <int KT>
+static void dispatch_nmb(const IndexerParams& p, hipStream_t st) {
+  const int M = p.Nq * p.H_I;
+  if (M <= 32) return dispatch_hpg<KT, 1>(p, st);
+  if (M <= 64) return dispatch_hpg<KT, 2>(p, st);
+  return dispatch_hpg<KT, 4>(p, st);
+}
+
+static bool mfma_ok(const IndexerParams& p) {
+  const bool pow2 = p.H_I > 0 && (p.H_I & (p.H_I - 1)) == 0;
+  return p.d_I == 64 && p.q.dt == DT_BF16 && (p.k.dt == DT_BF16 || p.k.dt == DT_FP8) &&
+         p.G_k == 1 && (p.hpg == 1 || p.hpg == 2 || p.hpg == 4) && p.Nq * p.H_I <= 128 && pow2 &&
+         p.H_I <= 32 * 4;
+}
+
+hipError_t launch_index_scores(const IndexerParams& p0, hipStream_t st) {
+  IndexerParams p = p0;
+  if (mfma_ok(p)) {
+    p.chunk = kMfmaChunk;
+    p.nchunk = (p.ctx + kMfmaChunk - 1) / kMfmaChunk;
+    if (p.k.dt == DT_FP8) dispatch_nmb<DT_FP8>(p, st);
+    else dispatch_nmb<DT_BF16>(p, st);
+  } else {
+    p.chunk = kGenChunk;
+    p.nchunk = (p.ctx + kGenChunk - 1) / kGenChunk;
+    dim3 grid(p.nchunk, p.Nq * p.G_sel, p.B);
+    hipLaunchKernelGGL(idx_generic_kernel, grid, dim3(kGenChunk), 0, st, p);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !p.err) return e;
+  dim3 g2((p.Nq * p.G_sel + 255) / 256, p.B);
+  hipLaunchKernelGGL(idx_err_kernel, g2, dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace sp

@@ -1,0 +1,84 @@
+// Launch parameters shared between the C-ABI layer and the kernel sources.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sp {
+
+struct View4 {             // a validated strided view (strides in elements)
+  const void* p;
+  int dt;                  // 0 f32, 1 bf16, 2 fp8, 3 i32
+  int64_t n[4];
+  int64_t s[4];
+};
+
+// ---------------------------------------------------------------- indexer
+struct IndexerParams {
+  View4 q;                 // [B, Nq, H_I, d_I]
+  View4 k;                 // [B, ctx, G_k, d_I]
+  const float* w;          // [B, Nq, H_I] f32 (null in DOT mode)
+  int64_t ws_[3];
+  int B, Nq, H_I, d_I, G_sel, G_k, hpg, relu, ctx;
+  const int32_t* ctx_len;
+  float* scores;           // [B, G_sel, Nq, ctx]
+  int64_t ss[4];
+  float* err;              // [B, G_sel, Nq] or null
+  float* kmax;             // workspace [B, G_k, nchunk]
+  int chunk, nchunk;
+};
+size_t indexer_ws_bytes(int B, int G_k, int ctx);
+hipError_t launch_index_scores(const IndexerParams& p, hipStream_t st);
+
+// ---------------------------------------------------------------- top-K
+struct TopkParams {
+  const float* scores;     // [B, G, Nq, ctx]
+  int64_t ss[4];
+  const float* err;        // [B, G, Nq] or null (then selection on scores as given)
+  bool certified;
+  IndexerParams ix;        // rescoring inputs when certified
+  int B, G, Nq, ctx, K;
+  const int32_t* ctx_len;
+  int32_t* idx;            // [B, G, Nq, K]
+  int64_t is[4];
+  int32_t* count;          // [B, G, Nq] or null
+};
+hipError_t launch_topk(const TopkParams& p, hipStream_t st);
+
+// ---------------------------------------------------------------- block select
+struct BlockSelectParams {
+  View4 q;                 // [B, Hq, Nq, d]
+  View4 k;                 // [B, Hkv, ctx, d]
+  int B, Hq, Hkv, Nq, ctx, d, bs, log2bs, nb;
+  const int32_t* ctx_len;
+  int32_t* out;            // [B, Hq, Nq, nb]
+  int64_t os[4];
+  int32_t* count;
+  float* kbar;             // workspace [B, Hkv, ctx/bs, d] f32
+  float* kabs;             // workspace [B, Hkv, ctx/bs] f32: max_t,c |k| per block
+};
+size_t block_select_ws_bytes(int B, int Hkv, int ctx, int d, int bs);
+hipError_t launch_block_select(const BlockSelectParams& p, hipStream_t st);
+
+// ---------------------------------------------------------------- attention
+struct AttnParams {
+  View4 q;                 // [B, Hq, Nq, d]
+  View4 k, v;              // [B, Hkv, ctx, d]
+  int B, Hq, Hkv, Nq, ctx, d;
+  const int32_t* ctx_len;
+  float scale;
+  int mode;                // 0 dense, 1 index, 2 window/global, 3 blocks
+  const int32_t* sel;      // index list or block list
+  int64_t sels[4];
+  int G_sel, K;            // index list groups and width (or number of blocks)
+  int window, n_global, bs;
+  float* o;                // [B, Hq, Nq, d] f32
+  int64_t os[4];
+  float* lse;              // [B, Hq, Nq] or null
+  void* ws;
+  size_t ws_bytes;
+};
+size_t attn_ws_bytes(const AttnParams& p);
+hipError_t launch_attention(const AttnParams& p, hipStream_t st);
+
+}  // namespace sp

@@ -1,0 +1,97 @@
+// Workgroup-level selection primitives: ordered compaction and radix select.
+//
+// Keys are order-preserving 32-bit images of float32 values (f32_order_key),
+// so "largest float" is "largest key". Radix select finds the R-th largest
+// key of a set in three histogram passes (12 + 12 + 8 bits) over LDS, using
+// ballots and wave prefix counts for the bin search. Selections break ties
+// by index (lower first) through an ordered pass with a running tie rank.
+#pragma once
+#include "common.h"
+
+namespace sp {
+
+// Exclusive prefix count of `flag` over the workgroup in thread order, and
+// the total. `scratch` holds >= 1 + waves uint32 in LDS. Two barriers.
+template <int T>
+SP_DEV uint32_t block_prefix(bool flag, uint32_t* scratch, uint32_t& total) {
+  constexpr int NW = T / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const uint64_t m = ballot(flag);
+  const uint32_t below = lanes_below(m);
+  if (lane == 0) scratch[wid] = (uint32_t)__popcll(m);
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t c = scratch[w];
+    base += (w < wid) ? c : 0u;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
+  return base + below;
+}
+
+// Find the R-th largest key (R >= 1, R <= number of included elements).
+// get(i, key) returns true when element i takes part. On return: t = that
+// key, above = number of included elements with key > t.
+template <int T, typename Get>
+SP_DEV void radix_select(int n, uint32_t R, Get get, uint32_t* hist, uint32_t* sc,
+                         uint32_t& t, uint32_t& above) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  constexpr int NW = T / 64;
+  uint32_t prefix = 0, pmask = 0, acc_above = 0, need = R;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int sh = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+    const int nb = pass == 2 ? 256 : 4096;
+    for (int i = tid; i < nb; i += T) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += T) {
+      uint32_t k;
+      if (get(i, k) && (k & pmask) == prefix) atomicAdd(&hist[(k >> sh) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    // thread owns bins [lo, lo+per); suffix sums from the top
+    const int per = nb >= T ? nb / T : 1;
+    const int lo = tid * per;
+    uint32_t mine = 0;
+    if (lo < nb)
+      for (int q = 0; q < per; ++q) mine += hist[lo + q];
+    // inclusive suffix scan within the wave (higher lanes own higher bins)
+    uint32_t v = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t u = __shfl_down(v, o, 64);
+      if (lane + o < 64) v += u;
+    }
+    if (lane == 0) sc[wid] = v;   // wave total
+    __syncthreads();
+    uint32_t higher_waves = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) higher_waves += (w > wid) ? sc[w] : 0u;
+    uint32_t cum = higher_waves + (v - mine);   // elements in bins above mine
+    if (lo < nb && cum < need && cum + mine >= need) {
+      for (int q = per - 1; q >= 0; --q) {
+        const uint32_t h = hist[lo + q];
+        if (cum + h >= need) {
+          sc[NW] = (uint32_t)(lo + q);
+          sc[NW + 1] = cum;
+          break;
+        }
+        cum += h;
+      }
+    }
+    __syncthreads();
+    const uint32_t bin = sc[NW], ab = sc[NW + 1];
+    __syncthreads();
+    acc_above += ab;
+    need -= ab;
+    prefix |= bin << sh;
+    pmask |= (uint32_t)(nb - 1) << sh;
+  }
+  t = prefix;
+  above = acc_above;
+}
+
+}  // namespace sp

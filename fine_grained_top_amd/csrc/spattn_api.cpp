@@ -1,0 +1,430 @@
+// C ABI of libspattn: argument validation, workspace sizing and dispatch.
+// Validation runs entirely on the host before any HIP call, so every
+// argument error is reported without touching a device.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/spattn.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int elem_size(int dt) {
+  switch (dt) {
+    case SPATTN_F32: return 4;
+    case SPATTN_BF16: return 2;
+    case SPATTN_FP8_E4M3: return 1;
+    case SPATTN_I32: return 4;
+  }
+  return 0;
+}
+
+// basic structural checks; `aligned16` requires 16-byte aligned rows
+int check_tensor(const spattn_tensor* t, const char* name, int ndim, bool aligned16) {
+  if (!t) return fail(SPATTN_ERR_INVALID_ARG, "%s: null tensor", name);
+  if (!t->data) return fail(SPATTN_ERR_INVALID_ARG, "%s: null data pointer", name);
+  if (t->ndim != ndim) return fail(SPATTN_ERR_INVALID_ARG, "%s: expected %d dims, got %d", name, ndim, t->ndim);
+  if (!elem_size(t->dtype)) return fail(SPATTN_ERR_INVALID_ARG, "%s: unknown dtype %d", name, t->dtype);
+  for (int i = 0; i < ndim; ++i) {
+    if (t->shape[i] < 0) return fail(SPATTN_ERR_INVALID_ARG, "%s: negative extent", name);
+    if (t->stride[i] < 0) return fail(SPATTN_ERR_INVALID_ARG, "%s: negative stride", name);
+    if (t->shape[i] > (int64_t)1 << 31) return fail(SPATTN_ERR_UNSUPPORTED, "%s: extent too large", name);
+  }
+  if (t->shape[ndim - 1] > 1 && t->stride[ndim - 1] != 1)
+    return fail(SPATTN_ERR_INVALID_ARG, "%s: innermost dimension must be contiguous", name);
+  if (aligned16) {
+    const int es = elem_size(t->dtype);
+    if (((uintptr_t)t->data) % 16) return fail(SPATTN_ERR_INVALID_ARG, "%s: data not 16-byte aligned", name);
+    for (int i = 0; i < ndim - 1; ++i)
+      if ((t->stride[i] * es) % 16) return fail(SPATTN_ERR_INVALID_ARG, "%s: stride %d not a multiple of 16 bytes", name, i);
+  }
+  return SPATTN_OK;
+}
+
+sp::View4 view(const spattn_tensor* t) {
+  sp::View4 v{};
+  v.p = t->data;
+  v.dt = t->dtype;
+  for (int i = 0; i < 4; ++i) {
+    v.n[i] = i < t->ndim ? t->shape[i] : 1;
+    v.s[i] = i < t->ndim ? t->stride[i] : 0;
+  }
+  return v;
+}
+
+std::mutex g_dev_mu;
+int g_dev_state[64];   // 0 unknown, 1 ok, 2 unsupported
+
+int device_ok() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(SPATTN_ERR_NO_DEVICE, "no HIP device available");
+  }
+  if (dev >= 64) return fail(SPATTN_ERR_NO_DEVICE, "device index out of range");
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_dev_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(SPATTN_ERR_NO_DEVICE, "cannot query device %d", dev);
+    }
+    g_dev_state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  }
+  if (g_dev_state[dev] != 1) return fail(SPATTN_ERR_NO_DEVICE, "device %d is not gfx950", dev);
+  return SPATTN_OK;
+}
+
+int launched(hipError_t e) {
+  if (e != hipSuccess) return fail(SPATTN_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return SPATTN_OK;
+}
+
+// ------------------------------------------------------------------ indexer
+int check_indexer(const spattn_indexer* ix, int64_t* B, int64_t* Nq, int64_t* ctx, int64_t* G_sel) {
+  if (!ix) return fail(SPATTN_ERR_INVALID_ARG, "indexer: null");
+  int rc;
+  if ((rc = check_tensor(&ix->q_idx, "q_idx", 4, true))) return rc;
+  if ((rc = check_tensor(&ix->k_idx, "k_idx", 4, true))) return rc;
+  const spattn_tensor& q = ix->q_idx;
+  const spattn_tensor& k = ix->k_idx;
+  if (q.dtype != SPATTN_F32 && q.dtype != SPATTN_BF16)
+    return fail(SPATTN_ERR_UNSUPPORTED, "q_idx dtype must be f32 or bf16");
+  if (k.dtype != SPATTN_F32 && k.dtype != SPATTN_BF16 && k.dtype != SPATTN_FP8_E4M3)
+    return fail(SPATTN_ERR_UNSUPPORTED, "k_idx dtype must be f32, bf16 or fp8");
+  if (q.dtype == SPATTN_F32 && k.dtype != SPATTN_F32)
+    return fail(SPATTN_ERR_UNSUPPORTED, "f32 q_idx requires f32 k_idx");
+  if (q.shape[0] != k.shape[0]) return fail(SPATTN_ERR_INVALID_ARG, "q_idx/k_idx batch mismatch");
+  if (q.shape[3] != k.shape[3]) return fail(SPATTN_ERR_INVALID_ARG, "q_idx/k_idx head dim mismatch");
+  const int64_t H_I = q.shape[2], d_I = q.shape[3];
+  if (d_I < 1 || d_I > 256) return fail(SPATTN_ERR_UNSUPPORTED, "d_I must be in 1..256");
+  if (ix->score_mode != SPATTN_SCORE_DOT && ix->score_mode != SPATTN_SCORE_WEIGHTED_RELU)
+    return fail(SPATTN_ERR_INVALID_ARG, "unknown score mode %d", ix->score_mode);
+  const int hpg = ix->heads_per_group;
+  if (hpg < 1 || H_I % hpg) return fail(SPATTN_ERR_INVALID_ARG, "heads_per_group must divide H_I");
+  if (ix->score_mode == SPATTN_SCORE_DOT && hpg != 1)
+    return fail(SPATTN_ERR_INVALID_ARG, "DOT mode needs heads_per_group = 1");
+  if ((int64_t)hpg * d_I > 4096) return fail(SPATTN_ERR_UNSUPPORTED, "heads_per_group * d_I > 4096");
+  if (hpg > 64) return fail(SPATTN_ERR_UNSUPPORTED, "heads_per_group > 64");
+  const int64_t G = H_I / hpg;
+  if (k.shape[2] != 1 && k.shape[2] != G)
+    return fail(SPATTN_ERR_INVALID_ARG, "k_idx heads must be 1 or the number of selection groups");
+  if (ix->score_mode == SPATTN_SCORE_WEIGHTED_RELU) {
+    const spattn_tensor& w = ix->w;
+    if (!w.data) return fail(SPATTN_ERR_INVALID_ARG, "w: null data pointer");
+    if (w.ndim != 3 || w.dtype != SPATTN_F32) return fail(SPATTN_ERR_INVALID_ARG, "w must be f32 [B, Nq, H_I]");
+    if (w.shape[0] != q.shape[0] || w.shape[1] != q.shape[1] || w.shape[2] != H_I)
+      return fail(SPATTN_ERR_INVALID_ARG, "w shape must be [B, Nq, H_I]");
+    for (int i = 0; i < 3; ++i)
+      if (w.stride[i] < 0) return fail(SPATTN_ERR_INVALID_ARG, "w: negative stride");
+  }
+  *B = q.shape[0];
+  *Nq = q.shape[1];
+  *ctx = k.shape[1];
+  *G_sel = G;
+  if (*Nq < 1 || *ctx < 1 || *Nq > *ctx) return fail(SPATTN_ERR_INVALID_ARG, "need 1 <= Nq <= ctx");
+  return SPATTN_OK;
+}
+
+sp::IndexerParams indexer_params(const spattn_indexer* ix, const int32_t* ctx_len) {
+  sp::IndexerParams p{};
+  p.q = view(&ix->q_idx);
+  p.k = view(&ix->k_idx);
+  p.B = (int)ix->q_idx.shape[0];
+  p.Nq = (int)ix->q_idx.shape[1];
+  p.H_I = (int)ix->q_idx.shape[2];
+  p.d_I = (int)ix->q_idx.shape[3];
+  p.ctx = (int)ix->k_idx.shape[1];
+  p.G_k = (int)ix->k_idx.shape[2];
+  p.hpg = ix->heads_per_group;
+  p.G_sel = p.H_I / p.hpg;
+  p.relu = ix->score_mode == SPATTN_SCORE_WEIGHTED_RELU;
+  if (p.relu) {
+    p.w = (const float*)ix->w.data;
+    for (int i = 0; i < 3; ++i) p.ws_[i] = ix->w.stride[i];
+  }
+  p.ctx_len = ctx_len;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+SPATTN_API const char* spattn_version(void) { return "libspattn 0.1.0 (gfx950)"; }
+
+SPATTN_API const char* spattn_status_string(int status) {
+  switch (status) {
+    case SPATTN_OK: return "ok";
+    case SPATTN_ERR_INVALID_ARG: return "invalid argument";
+    case SPATTN_ERR_UNSUPPORTED: return "unsupported";
+    case SPATTN_ERR_WORKSPACE: return "workspace too small";
+    case SPATTN_ERR_NO_DEVICE: return "no usable device";
+    case SPATTN_ERR_LAUNCH: return "launch failed";
+  }
+  return "unknown status";
+}
+
+SPATTN_API const char* spattn_last_error_message(void) { return g_err.c_str(); }
+
+// ------------------------------------------------------------------ index scores
+SPATTN_API size_t spattn_index_scores_workspace(const spattn_indexer* ix) {
+  int64_t B, Nq, ctx, G;
+  if (check_indexer(ix, &B, &Nq, &ctx, &G)) return (size_t)-1;
+  return sp::indexer_ws_bytes((int)B, (int)ix->k_idx.shape[2], (int)ctx);
+}
+
+SPATTN_API int spattn_index_scores(const spattn_indexer* ix, const int32_t* ctx_len,
+                                   const spattn_tensor* scores_out, float* err_out, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  int64_t B, Nq, ctx, G;
+  int rc;
+  if ((rc = check_indexer(ix, &B, &Nq, &ctx, &G))) return rc;
+  if ((rc = check_tensor(scores_out, "scores_out", 4, false))) return rc;
+  if (scores_out->dtype != SPATTN_F32) return fail(SPATTN_ERR_INVALID_ARG, "scores_out must be f32");
+  if (scores_out->shape[0] != B || scores_out->shape[1] != G || scores_out->shape[2] != Nq ||
+      scores_out->shape[3] != ctx)
+    return fail(SPATTN_ERR_INVALID_ARG, "scores_out must be [B, G_sel, Nq, ctx]");
+  const size_t need = sp::indexer_ws_bytes((int)B, (int)ix->k_idx.shape[2], (int)ctx);
+  if (ws_bytes < need || (need && !ws)) return fail(SPATTN_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  if ((rc = device_ok())) return rc;
+  sp::IndexerParams p = indexer_params(ix, ctx_len);
+  p.scores = (float*)scores_out->data;
+  for (int i = 0; i < 4; ++i) p.ss[i] = scores_out->stride[i];
+  p.err = err_out;
+  p.kmax = (float*)ws;
+  return launched(sp::launch_index_scores(p, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------ top-K
+SPATTN_API size_t spattn_topk_workspace(const spattn_tensor*, const spattn_indexer*, int32_t,
+                                        uint32_t) {
+  return 0;
+}
+
+SPATTN_API int spattn_topk(const spattn_tensor* scores, const float* err, const spattn_indexer* ix,
+                           const int32_t* ctx_len, int32_t k, uint32_t flags,
+                           const spattn_tensor* idx_out, int32_t* count_out, void* ws,
+                           size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int rc;
+  if (flags & ~(SPATTN_TOPK_CERTIFIED | SPATTN_TOPK_FUSED_INDEX))
+    return fail(SPATTN_ERR_INVALID_ARG, "unknown flags");
+  if (flags & SPATTN_TOPK_FUSED_INDEX)
+    return fail(SPATTN_ERR_UNSUPPORTED, "fused indexer top-K is not available in this build");
+  if (k < 1 || k > 16384) return fail(SPATTN_ERR_INVALID_ARG, "k must be in 1..16384");
+  if ((rc = check_tensor(scores, "scores", 4, false))) return rc;
+  if (scores->dtype != SPATTN_F32) return fail(SPATTN_ERR_INVALID_ARG, "scores must be f32");
+  if ((rc = check_tensor(idx_out, "idx_out", 4, false))) return rc;
+  if (idx_out->dtype != SPATTN_I32) return fail(SPATTN_ERR_INVALID_ARG, "idx_out must be int32");
+  const int64_t B = scores->shape[0], G = scores->shape[1], Nq = scores->shape[2], ctx = scores->shape[3];
+  if (idx_out->shape[0] != B || idx_out->shape[1] != G || idx_out->shape[2] != Nq || idx_out->shape[3] != k)
+    return fail(SPATTN_ERR_INVALID_ARG, "idx_out must be [B, G, Nq, k]");
+  if (Nq < 1 || ctx < 1 || Nq > ctx) return fail(SPATTN_ERR_INVALID_ARG, "need 1 <= Nq <= ctx");
+  sp::TopkParams p{};
+  if (flags & SPATTN_TOPK_CERTIFIED) {
+    int64_t iB, iNq, ictx, iG;
+    if (!err) return fail(SPATTN_ERR_INVALID_ARG, "certified selection needs err");
+    if ((rc = check_indexer(ix, &iB, &iNq, &ictx, &iG))) return rc;
+    if (iB != B || iNq != Nq || ictx != ctx || iG != G)
+      return fail(SPATTN_ERR_INVALID_ARG, "indexer shapes do not match scores");
+    p.certified = true;
+    p.ix = indexer_params(ix, ctx_len);
+  }
+  if ((rc = device_ok())) return rc;
+  p.scores = (const float*)scores->data;
+  for (int i = 0; i < 4; ++i) {
+    p.ss[i] = scores->stride[i];
+    p.is[i] = idx_out->stride[i];
+  }
+  p.err = err;
+  p.B = (int)B;
+  p.G = (int)G;
+  p.Nq = (int)Nq;
+  p.ctx = (int)ctx;
+  p.K = k;
+  p.ctx_len = ctx_len;
+  p.idx = (int32_t*)idx_out->data;
+  p.count = count_out;
+  return launched(sp::launch_topk(p, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------ block select
+static int check_qk(const spattn_tensor* q, const spattn_tensor* k) {
+  int rc;
+  if ((rc = check_tensor(q, "q", 4, true))) return rc;
+  if ((rc = check_tensor(k, "k", 4, true))) return rc;
+  if (q->dtype != k->dtype) return fail(SPATTN_ERR_INVALID_ARG, "q and k dtypes differ");
+  if (q->dtype != SPATTN_F32 && q->dtype != SPATTN_BF16) return fail(SPATTN_ERR_UNSUPPORTED, "q/k dtype must be f32 or bf16");
+  if (q->shape[0] != k->shape[0] || q->shape[3] != k->shape[3])
+    return fail(SPATTN_ERR_INVALID_ARG, "q/k batch or head dim mismatch");
+  if (k->shape[1] < 1 || q->shape[1] % k->shape[1])
+    return fail(SPATTN_ERR_INVALID_ARG, "KV heads must divide query heads");
+  if (q->shape[3] != 64 && q->shape[3] != 128) return fail(SPATTN_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  if (q->shape[2] < 1 || q->shape[2] > k->shape[2]) return fail(SPATTN_ERR_INVALID_ARG, "need 1 <= Nq <= ctx");
+  return SPATTN_OK;
+}
+
+SPATTN_API size_t spattn_block_select_workspace(const spattn_tensor* q, const spattn_tensor* k,
+                                                int32_t block_size, int32_t top_blocks) {
+  if (check_qk(q, k) || block_size < 1 || top_blocks < 1) return (size_t)-1;
+  return sp::block_select_ws_bytes((int)k->shape[0], (int)k->shape[1], (int)k->shape[2], (int)k->shape[3], block_size);
+}
+
+SPATTN_API int spattn_block_select(const spattn_tensor* q, const spattn_tensor* k, const int32_t* ctx_len,
+                                   int32_t block_size, int32_t top_blocks, const spattn_tensor* blk_idx_out,
+                                   int32_t* blk_count_out, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_qk(q, k))) return rc;
+  if (block_size < 1 || (block_size & (block_size - 1)))
+    return fail(SPATTN_ERR_INVALID_ARG, "block_size must be a power of two");
+  if (top_blocks < 1) return fail(SPATTN_ERR_INVALID_ARG, "top_blocks must be >= 1");
+  if (k->shape[2] / block_size > 2048) return fail(SPATTN_ERR_UNSUPPORTED, "more than 2048 blocks per request");
+  if ((rc = check_tensor(blk_idx_out, "blk_idx_out", 4, false))) return rc;
+  if (blk_idx_out->dtype != SPATTN_I32) return fail(SPATTN_ERR_INVALID_ARG, "blk_idx_out must be int32");
+  if (blk_idx_out->shape[0] != q->shape[0] || blk_idx_out->shape[1] != q->shape[1] ||
+      blk_idx_out->shape[2] != q->shape[2] || blk_idx_out->shape[3] != top_blocks)
+    return fail(SPATTN_ERR_INVALID_ARG, "blk_idx_out must be [B, H_q, Nq, top_blocks]");
+  const size_t need = sp::block_select_ws_bytes((int)k->shape[0], (int)k->shape[1], (int)k->shape[2],
+                                                (int)k->shape[3], block_size);
+  if (ws_bytes < need || !ws) return fail(SPATTN_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  if ((rc = device_ok())) return rc;
+  sp::BlockSelectParams p{};
+  p.q = view(q);
+  p.k = view(k);
+  p.B = (int)q->shape[0];
+  p.Hq = (int)q->shape[1];
+  p.Nq = (int)q->shape[2];
+  p.d = (int)q->shape[3];
+  p.Hkv = (int)k->shape[1];
+  p.ctx = (int)k->shape[2];
+  p.bs = block_size;
+  p.log2bs = __builtin_ctz((unsigned)block_size);
+  p.nb = top_blocks;
+  p.ctx_len = ctx_len;
+  p.out = (int32_t*)blk_idx_out->data;
+  for (int i = 0; i < 4; ++i) p.os[i] = blk_idx_out->stride[i];
+  p.count = blk_count_out;
+  const size_t nbk = p.ctx / p.bs;
+  p.kbar = (float*)ws;
+  p.kabs = p.kbar + (size_t)p.B * p.Hkv * nbk * p.d;
+  return launched(sp::launch_block_select(p, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------ attention
+static int attn_setup(const spattn_tensor* q, const spattn_tensor* k, const spattn_tensor* v,
+                      const spattn_selection* sel, sp::AttnParams& p, bool need_v) {
+  int rc;
+  if ((rc = check_qk(q, k))) return rc;
+  if (need_v) {
+    if ((rc = check_tensor(v, "v", 4, true))) return rc;
+    if (v->dtype != k->dtype) return fail(SPATTN_ERR_INVALID_ARG, "v dtype differs from k");
+    for (int i = 0; i < 4; ++i)
+      if (v->shape[i] != k->shape[i]) return fail(SPATTN_ERR_INVALID_ARG, "v shape differs from k");
+  }
+  if (!sel) return fail(SPATTN_ERR_INVALID_ARG, "selection: null");
+  p = sp::AttnParams{};
+  p.q = view(q);
+  p.k = view(k);
+  if (need_v) p.v = view(v);
+  p.B = (int)q->shape[0];
+  p.Hq = (int)q->shape[1];
+  p.Nq = (int)q->shape[2];
+  p.d = (int)q->shape[3];
+  p.Hkv = (int)k->shape[1];
+  p.ctx = (int)k->shape[2];
+  p.mode = sel->mode;
+  p.G_sel = 1;
+  switch (sel->mode) {
+    case SPATTN_SEL_DENSE: break;
+    case SPATTN_SEL_INDEX: {
+      if ((rc = check_tensor(&sel->idx, "sel.idx", 4, false))) return rc;
+      if (sel->idx.dtype != SPATTN_I32) return fail(SPATTN_ERR_INVALID_ARG, "sel.idx must be int32");
+      const int64_t G = sel->idx.shape[1];
+      if (sel->idx.shape[0] != p.B || sel->idx.shape[2] != p.Nq || G < 1 || p.Hq % G)
+        return fail(SPATTN_ERR_INVALID_ARG, "sel.idx must be [B, G_sel, Nq, K] with G_sel | H_q");
+      if ((G % p.Hkv) && (p.Hkv % G))
+        return fail(SPATTN_ERR_INVALID_ARG, "G_sel and H_kv must divide one another");
+      p.G_sel = (int)G;
+      p.K = (int)sel->idx.shape[3];
+      p.sel = (const int32_t*)sel->idx.data;
+      for (int i = 0; i < 4; ++i) p.sels[i] = sel->idx.stride[i];
+      break;
+    }
+    case SPATTN_SEL_WINDOW_GLOBAL:
+      if (sel->window < 0 || sel->n_global < 0) return fail(SPATTN_ERR_INVALID_ARG, "window/n_global must be >= 0");
+      p.window = sel->window;
+      p.n_global = sel->n_global;
+      break;
+    case SPATTN_SEL_BLOCKS: {
+      if ((rc = check_tensor(&sel->idx, "sel.idx", 4, false))) return rc;
+      if (sel->idx.dtype != SPATTN_I32) return fail(SPATTN_ERR_INVALID_ARG, "sel.idx must be int32");
+      if (sel->idx.shape[0] != p.B || sel->idx.shape[1] != p.Hq || sel->idx.shape[2] != p.Nq)
+        return fail(SPATTN_ERR_INVALID_ARG, "block list must be [B, H_q, Nq, nb]");
+      if (sel->block_size < 1 || sel->window < 0) return fail(SPATTN_ERR_INVALID_ARG, "bad block_size/window");
+      p.K = (int)sel->idx.shape[3];
+      p.sel = (const int32_t*)sel->idx.data;
+      for (int i = 0; i < 4; ++i) p.sels[i] = sel->idx.stride[i];
+      p.bs = sel->block_size;
+      p.window = sel->window;
+      break;
+    }
+    default: return fail(SPATTN_ERR_INVALID_ARG, "unknown selection mode %d", sel->mode);
+  }
+  return SPATTN_OK;
+}
+
+SPATTN_API size_t spattn_sparse_attn_fwd_workspace(const spattn_tensor* q, const spattn_tensor* k,
+                                                   const spattn_selection* sel) {
+  sp::AttnParams p;
+  if (attn_setup(q, k, nullptr, sel, p, false)) return (size_t)-1;
+  return sp::attn_ws_bytes(p);
+}
+
+SPATTN_API int spattn_sparse_attn_fwd(const spattn_tensor* q, const spattn_tensor* k, const spattn_tensor* v,
+                                      const int32_t* ctx_len, float scale, const spattn_selection* sel,
+                                      const spattn_tensor* o_out, float* lse_out, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  sp::AttnParams p;
+  int rc;
+  if ((rc = attn_setup(q, k, v, sel, p, true))) return rc;
+  if ((rc = check_tensor(o_out, "o_out", 4, false))) return rc;
+  if (o_out->dtype != SPATTN_F32) return fail(SPATTN_ERR_INVALID_ARG, "o_out must be f32");
+  for (int i = 0; i < 4; ++i)
+    if (o_out->shape[i] != q->shape[i]) return fail(SPATTN_ERR_INVALID_ARG, "o_out shape must equal q's");
+  if (!(scale >= 0.f) || std::isinf(scale)) return fail(SPATTN_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  p.scale = scale == 0.f ? 1.0f / std::sqrt((float)p.d) : scale;
+  p.ctx_len = ctx_len;
+  p.o = (float*)o_out->data;
+  for (int i = 0; i < 4; ++i) p.os[i] = o_out->stride[i];
+  p.lse = lse_out;
+  const size_t need = sp::attn_ws_bytes(p);
+  if (ws_bytes < need || (need && !ws)) return fail(SPATTN_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  p.ws = ws;
+  p.ws_bytes = ws_bytes;
+  if ((rc = device_ok())) return rc;
+  return launched(sp::launch_attention(p, (hipStream_t)stream));
+}
+
+}  // extern "C"

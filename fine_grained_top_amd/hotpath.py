@@ -1,0 +1,100 @@
+"""The selective-sparse-attention hot path of one workload, on the GPU.
+
+Orchestration only: it moves the seeded inputs to the device, owns the output
+and workspace buffers, and calls the libspattn entry points in order
+(indexer scores -> certified top-K -> sparse attention; block selection ->
+block-sparse attention; or a fixed window + global pattern).
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import spattn as S
+from .inputs import Workload
+
+
+def to_device(arr: np.ndarray, fmt: str, device="cuda") -> torch.Tensor:
+    if fmt == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(device)
+    if fmt == "fp8":
+        return torch.from_numpy(np.ascontiguousarray(arr)).to(device)          # uint8 storage = E4M3FN
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+class HotPath:
+    """Buffers and calls for one workload; ``step()`` runs the whole path once."""
+
+    def __init__(self, wl: Workload, inp: Dict[str, np.ndarray], device="cuda"):
+        self.wl = wl
+        self.device = device
+        dt = wl.dtype
+        self.q = to_device(inp["q"], dt, device)
+        self.k = to_device(inp["k"], dt, device)
+        self.v = to_device(inp["v"], dt, device)
+        self.ctx_len = torch.from_numpy(inp["ctx_len"].astype(np.int32)).to(device)
+        self.o = torch.empty(wl.B, wl.Hq, wl.Nq, wl.d, dtype=torch.float32, device=device)
+        self.lse = torch.empty(wl.B, wl.Hq, wl.Nq, dtype=torch.float32, device=device)
+        self.idx = None
+        self.count = None
+        if wl.H_I:
+            self.q_idx = to_device(inp["q_idx"], wl.idx_q_dtype, device)
+            self.k_idx = to_device(inp["k_idx"], wl.idx_k_dtype, device)
+            w = torch.from_numpy(inp["w"].astype(np.float32)).to(device)
+            self.w = w.view(1, 1, wl.H_I).expand(wl.B, wl.Nq, wl.H_I)
+            mode = S.SCORE_WEIGHTED_RELU if wl.score_mode == "weighted_relu" else S.SCORE_DOT
+            self.ix = S.indexer(self.q_idx, self.k_idx, self.w if mode == S.SCORE_WEIGHTED_RELU else None,
+                                mode, wl.heads_per_group)
+            self.scores = torch.empty(wl.B, wl.G_sel, wl.Nq, wl.N, dtype=torch.float32, device=device)
+            self.err = torch.empty(wl.B, wl.G_sel, wl.Nq, dtype=torch.float32, device=device)
+            self.idx = torch.empty(wl.B, wl.G_sel, wl.Nq, wl.topk, dtype=torch.int32, device=device)
+            self.count = torch.empty(wl.B, wl.G_sel, wl.Nq, dtype=torch.int32, device=device)
+            self.sel = S.selection(S.SEL_INDEX, self.idx)
+        elif wl.kind == "blocks":
+            self.idx = torch.empty(wl.B, wl.Hq, wl.Nq, wl.top_blocks, dtype=torch.int32, device=device)
+            self.count = torch.empty(wl.B, wl.Hq, wl.Nq, dtype=torch.int32, device=device)
+            self.sel = S.selection(S.SEL_BLOCKS, self.idx, window=wl.window, block_size=wl.block_size)
+        elif wl.kind == "window_global":
+            self.sel = S.selection(S.SEL_WINDOW_GLOBAL, window=wl.window, n_global=wl.n_global)
+        else:
+            self.sel = S.selection(S.SEL_DENSE)
+        self.ws = torch.empty(self.ws_bytes(), dtype=torch.uint8, device=device)
+
+    def ws_bytes(self) -> int:
+        n = 0
+        if self.wl.H_I:
+            n = max(n, S.LIB.spattn_index_scores_workspace(S.ctypes.byref(self.ix)))
+        if self.wl.kind == "blocks":
+            tq, tk = S.tensor(self.q), S.tensor(self.k)
+            n = max(n, S.LIB.spattn_block_select_workspace(S.ctypes.byref(tq), S.ctypes.byref(tk),
+                                                           self.wl.block_size, self.wl.top_blocks))
+        tq, tk = S.tensor(self.q), S.tensor(self.k)
+        n = max(n, S.LIB.spattn_sparse_attn_fwd_workspace(S.ctypes.byref(tq), S.ctypes.byref(tk),
+                                                          S.ctypes.byref(self.sel)))
+        return max(n, 16)
+
+    # the individual stages
+    def index_scores(self, stream=None):
+        S.spattn_index_scores(self.ix, self.ctx_len, self.scores, self.err, self.ws, stream)
+
+    def topk(self, stream=None):
+        S.spattn_topk(self.scores, self.err, self.ix, self.ctx_len, self.wl.topk, S.TOPK_CERTIFIED,
+                      self.idx, self.count, None, stream)
+
+    def block_select(self, stream=None):
+        S.spattn_block_select(self.q, self.k, self.ctx_len, self.wl.block_size, self.wl.top_blocks,
+                              self.idx, self.count, self.ws, stream)
+
+    def attention(self, stream=None):
+        S.spattn_sparse_attn_fwd(self.q, self.k, self.v, self.ctx_len, 0.0, self.sel, self.o, self.lse,
+                                 self.ws, stream)
+
+    def step(self, stream=None):
+        if self.wl.H_I:
+            self.index_scores(stream)
+            self.topk(stream)
+        elif self.wl.kind == "blocks":
+            self.block_select(stream)
+        self.attention(stream)

@@ -1,0 +1,219 @@
+/*
+ * libspattn — selective sparse attention on AMD Instinct MI355X (gfx950).
+ *
+ * A lightweight indexer scores every past key for each query, a per-query
+ * top-K picks the visible key set S(i), and attention softmax(q k^T/sqrt(d)) V
+ * is computed over S(i) only. Fixed visible sets (sliding window + global
+ * tokens, block-sparse selection) are special cases of the same attention call.
+ *
+ * Sources of the method (the pages this library restates):
+ *  - "A Guide to Sparse Attention in Large Models", section 2 (attention
+ *    restricted to a visible key set S(i) through a mask) and section 4
+ *    (index-based and fused implementations);
+ *  - "Sparse Attention for Long-Context LLM Inference", sections on the
+ *    lightweight indexer ("coarse filter first, precise compute later") and
+ *    on Top-K candidate control;
+ *  - "Sparse Attention in 2026: Why It Finally Had to Be Native", DSA
+ *    paragraph (a few-head low-precision indexer, top-k key/value entries);
+ *  - "Sparse Attention Is Reshaping Production AI", fixed patterns and
+ *    learned block routing (mean-pooled block keys, top-k blocks);
+ *  - "Sparse Attention" (completesystemdesign.dev), sliding window + global
+ *    tokens and block-sparse patterns.
+ *
+ * Conventions shared by every call
+ *  - All tensors are caller-owned device buffers described by spattn_tensor
+ *    (strides in elements; the innermost dimension must have stride 1 and
+ *    rows must be 16-byte aligned where noted). The library never allocates
+ *    device memory, never synchronizes, and keeps no state between calls: a
+ *    call validates its arguments on the host and enqueues kernels on
+ *    `stream` (a hipStream_t; NULL = the default stream).
+ *  - Queries are the last Nq positions of each request's context: the query
+ *    in row r of request b sits at position p = ctx_len[b] - Nq + r and sees
+ *    keys 0..p (causal). Prefill has Nq = ctx_len, decode has Nq = 1.
+ *    `ctx_len` is a device int32 array [B] or NULL (every request holds the
+ *    full capacity `ctx` of the key tensors). Values must lie in [Nq, ctx];
+ *    they are read on the device and not checked by the host.
+ *  - Status codes: every call returns SPATTN_OK or an error; validation ends
+ *    before any launch, so a failed call enqueues nothing. Errors raised by
+ *    kernels at run time surface at the caller's next stream synchronization.
+ *    spattn_last_error_message() returns a thread-local description.
+ *  - Workspace: `ws` is caller-owned device scratch of at least the size the
+ *    matching *_workspace() query returns for the same arguments (0 is
+ *    allowed where the query returns 0). It need not be initialized.
+ */
+#ifndef SPATTN_H
+#define SPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPATTN_API __attribute__((visibility("default")))
+
+enum spattn_status {
+  SPATTN_OK = 0,
+  SPATTN_ERR_INVALID_ARG = 1,   /* null pointer, bad shape or stride, bad parameter */
+  SPATTN_ERR_UNSUPPORTED = 2,   /* valid but not implemented (dtype, head dim, sizes) */
+  SPATTN_ERR_WORKSPACE = 3,     /* ws_bytes below the size the *_workspace() query gives */
+  SPATTN_ERR_NO_DEVICE = 4,     /* no usable gfx950 device */
+  SPATTN_ERR_LAUNCH = 5         /* the HIP runtime refused a launch */
+};
+
+enum spattn_dtype { SPATTN_F32 = 0, SPATTN_BF16 = 1, SPATTN_FP8_E4M3 = 2, SPATTN_I32 = 3 };
+
+/* A strided view of a device buffer. ndim <= 4; unused trailing entries ignored. */
+typedef struct spattn_tensor {
+  void* data;
+  int32_t dtype;       /* enum spattn_dtype; FP8_E4M3 is OCP E4M3FN (bias 7, max 448, no inf) */
+  int32_t ndim;
+  int64_t shape[4];
+  int64_t stride[4];   /* in elements; 0 broadcasts */
+} spattn_tensor;
+
+/* Indexer score s(i,j) of key j for selection group g of query row i. */
+enum spattn_score_mode {
+  /* s = q_I[i,g] . k_I[j]  (one indexer head per group) */
+  SPATTN_SCORE_DOT = 0,
+  /* s = sum over the group's heads h of w[i,h] * max(0, q_I[i,h] . k_I[j]) */
+  SPATTN_SCORE_WEIGHTED_RELU = 1
+};
+
+/* Indexer inputs ("Sparse Attention for Long-Context LLM Inference",
+ * lightweight indexer; "Sparse Attention in 2026", DSA lightning indexer).
+ * The indexer takes no positions: its scores depend on content only. */
+typedef struct spattn_indexer {
+  spattn_tensor q_idx;    /* [B, Nq, H_I, d_I]  f32 | bf16 */
+  spattn_tensor k_idx;    /* [B, ctx, G_k, d_I] f32 | bf16 | fp8; G_k = 1 (shared by all
+                             selection groups) or G_k = G_sel (one key head per group) */
+  spattn_tensor w;        /* [B, Nq, H_I] f32 head weights, strides may be 0 (broadcast);
+                             ignored (may be empty) in DOT mode */
+  int32_t score_mode;     /* enum spattn_score_mode */
+  int32_t heads_per_group;/* H_I / G_sel; must be 1 in DOT mode */
+} spattn_indexer;
+
+/* How the visible key set S(i) of each query row is formed. */
+enum spattn_sel_mode {
+  SPATTN_SEL_DENSE = 0,          /* S = all keys 0..p (the conservative fallback) */
+  SPATTN_SEL_INDEX = 1,          /* S = explicit index list (e.g. from spattn_topk) */
+  SPATTN_SEL_WINDOW_GLOBAL = 2,  /* S = {p-window+1..p} U {0..n_global-1}, within 0..p */
+  SPATTN_SEL_BLOCKS = 3          /* S = selected blocks U {p-window+1..p}, within 0..p */
+};
+
+typedef struct spattn_selection {
+  int32_t mode;          /* enum spattn_sel_mode */
+  spattn_tensor idx;     /* INDEX: int32 [B, G_sel, Nq, K], ascending key positions, -1
+                            padded; G_sel divides H_q and G_sel | H_kv or H_kv | G_sel.
+                            BLOCKS: int32 [B, H_q, Nq, nb] block ids, -1 padded. */
+  int32_t window;        /* keys in the sliding window, the query itself included */
+  int32_t n_global;      /* WINDOW_GLOBAL: tokens 0..n_global-1 are visible to all rows */
+  int32_t block_size;    /* BLOCKS: tokens per block */
+} spattn_selection;
+
+/* ------------------------------------------------------------------------
+ * spattn_index_scores — indexer scores for every (query row, past key).
+ * Source: "Sparse Attention for Long-Context LLM Inference" (lightweight
+ * indexer outputs candidate scores for historical positions); "Sparse
+ * Attention in 2026" (DSA: few-head low-precision indexer, ReLU-gated heads).
+ *
+ *  scores_out: f32 [B, G_sel, Nq, ctx]; entry (b,g,r,j) for j <= p is the
+ *              score computed in float32 (MFMA or FMA accumulation); entries
+ *              with j > p are unspecified.
+ *  err_out:    optional f32 [B, G_sel, Nq]: a rigorous bound on
+ *              |scores_out - key| over the row, where key is the float32
+ *              nearest to the exact score. spattn_topk uses it to return
+ *              oracle-exact index sets.
+ *  Limits: d_I <= 256; f32 q_idx requires f32 k_idx.
+ * ---------------------------------------------------------------------- */
+SPATTN_API size_t spattn_index_scores_workspace(const spattn_indexer* ix);
+SPATTN_API int spattn_index_scores(const spattn_indexer* ix, const int32_t* ctx_len,
+                                   const spattn_tensor* scores_out, float* err_out,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * spattn_topk — per-row top-K of past keys.
+ * Source: "Sparse Attention for Long-Context LLM Inference", Top-K section
+ * (cap on candidates per step); "Sparse Attention in 2026", DSA paragraph
+ * (top-k key/value entries per query).
+ *
+ * Row (b,g,r) has candidates 0..p. The selected set is the min(K, p+1)
+ * candidates largest by (score descending, index ascending); written to
+ * idx_out int32 [B, G, Nq, K] in ascending index order, -1 padded, with the
+ * count in count_out int32 [B, G, Nq] (optional).
+ *
+ *  flags = 0: selection on the float32 values in `scores` as given.
+ *  flags = SPATTN_TOPK_CERTIFIED: `scores`/`err` come from spattn_index_scores
+ *      on indexer `ix`; selection is made on the exact keys (float32 nearest
+ *      to the exact score), with near-ties rescored exactly, so the result
+ *      equals exhaustive selection on exact keys.
+ *  flags = SPATTN_TOPK_FUSED_INDEX: `scores` and `err` are NULL; the scores are
+ *      computed from `ix` inside (no score matrix is materialized) and the
+ *      selection is certified as above.
+ *  Limits: 1 <= K <= 16384.
+ * ---------------------------------------------------------------------- */
+#define SPATTN_TOPK_CERTIFIED 1u
+#define SPATTN_TOPK_FUSED_INDEX 2u
+SPATTN_API size_t spattn_topk_workspace(const spattn_tensor* scores, const spattn_indexer* ix,
+                                        int32_t k, uint32_t flags);
+SPATTN_API int spattn_topk(const spattn_tensor* scores, const float* err,
+                           const spattn_indexer* ix, const int32_t* ctx_len, int32_t k,
+                           uint32_t flags, const spattn_tensor* idx_out, int32_t* count_out,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * spattn_block_select — block routing for block-sparse attention.
+ * Source: "Sparse Attention Is Reshaping Production AI", Learned Block
+ * Routing (keys mean-pooled per block, unscaled dot product with the query,
+ * top-k blocks); "Sparse Attention" (completesystemdesign.dev), NSA/MoBA-style
+ * block selection.
+ *
+ * For query row (b,h,r) at position p the eligible blocks are the complete
+ * past blocks {beta : block_size*beta + block_size - 1 <= p}. Each is scored by
+ * the float32 nearest to the exact mean over its keys of q.k (head h's own q
+ * and its KV head's k), and the min(top_blocks, #eligible) best by
+ * (score descending, block ascending) are written ascending to
+ * blk_idx_out int32 [B, H_q, Nq, top_blocks], -1 padded; counts optional.
+ *  q: [B, H_q, Nq, d] bf16|f32; k: [B, H_kv, ctx, d] same dtype; d in {64,128}.
+ * ---------------------------------------------------------------------- */
+SPATTN_API size_t spattn_block_select_workspace(const spattn_tensor* q, const spattn_tensor* k,
+                                                int32_t block_size, int32_t top_blocks);
+SPATTN_API int spattn_block_select(const spattn_tensor* q, const spattn_tensor* k,
+                                   const int32_t* ctx_len, int32_t block_size,
+                                   int32_t top_blocks, const spattn_tensor* blk_idx_out,
+                                   int32_t* blk_count_out, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/* ------------------------------------------------------------------------
+ * spattn_sparse_attn_fwd — attention restricted to S(i).
+ * Source: "A Guide to Sparse Attention in Large Models", section 2 (softmax
+ * over the visible key set, everything else masked) and sections 4.2-4.3
+ * (index-based and fused implementations that touch only the selected keys).
+ *
+ *  q: [B, H_q, Nq, d], k, v: [B, H_kv, ctx, d], same dtype (bf16 or f32),
+ *     d in {64, 128}, H_kv divides H_q (GQA/MQA). Rows 16-byte aligned.
+ *  scale: logit scale; 0 means 1/sqrt(d).
+ *  o_out: f32 [B, H_q, Nq, d]; lse_out: optional f32 [B, H_q, Nq], natural
+ *     log of the softmax denominator including the scale. A row with an empty
+ *     visible set gets O = 0 and LSE = -inf.
+ * Index entries outside 0..p and -1 padding are ignored.
+ * ---------------------------------------------------------------------- */
+SPATTN_API size_t spattn_sparse_attn_fwd_workspace(const spattn_tensor* q, const spattn_tensor* k,
+                                                   const spattn_selection* sel);
+SPATTN_API int spattn_sparse_attn_fwd(const spattn_tensor* q, const spattn_tensor* k,
+                                      const spattn_tensor* v, const int32_t* ctx_len,
+                                      float scale, const spattn_selection* sel,
+                                      const spattn_tensor* o_out, float* lse_out, void* ws,
+                                      size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ helpers */
+SPATTN_API const char* spattn_status_string(int status);
+SPATTN_API const char* spattn_version(void);
+/* Thread-local message describing the last failed call on this thread. */
+SPATTN_API const char* spattn_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPATTN_H */

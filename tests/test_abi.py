@@ -1,0 +1,131 @@
+"""The C ABI on the host: the library loads, exports every declared symbol,
+and rejects bad arguments before touching a device (no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from fine_grained_top_amd import spattn as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spattn.h")
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    return re.findall(r"SPATTN_API\s+[\w\s\*]+?\b(spattn_\w+)\s*\(", src)
+
+
+def test_header_symbols_exported():
+    names = declared_symbols()
+    assert len(names) >= 11
+    lib = ctypes.CDLL(S.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in S.spattn_version()
+    assert S.spattn_status_string(0) == "ok"
+    assert S.spattn_status_string(3) == "workspace too small"
+    assert S.spattn_status_string(99) == "unknown status"
+
+
+def _ix(q, k, w, mode, hpg):
+    return S.indexer(q, k, w, mode, hpg)
+
+
+def _call_scores(ix, scores, ws_bytes=4096):
+    so = S.tensor(scores)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8)
+    return S.LIB.spattn_index_scores(ctypes.byref(ix), None, ctypes.byref(so), None,
+                                     ws.data_ptr() if ws_bytes else None, ws_bytes, None)
+
+
+def test_index_scores_validation():
+    q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 64, 1, 64, dtype=torch.uint8)
+    w = torch.zeros(1, 4, 8)
+    sc = torch.zeros(1, 2, 4, 64)
+    ok = _ix(q, k, w, S.SCORE_WEIGHTED_RELU, 4)
+    # valid arguments reach the device check (no GPU here)
+    assert _call_scores(ok, sc) == 4
+    # heads_per_group must divide H_I
+    assert _call_scores(_ix(q, k, w, S.SCORE_WEIGHTED_RELU, 3), sc) == 1
+    # DOT needs one head per group
+    assert _call_scores(_ix(q, k, None, S.SCORE_DOT, 4), sc) == 1
+    # f32 queries with fp8 keys is not supported
+    assert _call_scores(_ix(q.float(), k, w, S.SCORE_WEIGHTED_RELU, 4), sc) == 2
+    # scores shape mismatch
+    assert _call_scores(ok, torch.zeros(1, 2, 4, 63)) == 1
+    # missing weights in weighted-ReLU mode
+    assert _call_scores(_ix(q, k, None, S.SCORE_WEIGHTED_RELU, 4), sc) == 1
+    # workspace too small
+    assert _call_scores(ok, sc, ws_bytes=0) == 3
+    # non-contiguous innermost dim
+    qt = torch.zeros(1, 4, 64, 8, dtype=torch.bfloat16).transpose(2, 3)
+    assert _call_scores(_ix(qt, k, w, S.SCORE_WEIGHTED_RELU, 4), sc) == 1
+    assert "contiguous" in S.spattn_last_error_message()
+
+
+def test_topk_validation():
+    sc = torch.zeros(1, 1, 4, 64)
+    io = torch.zeros(1, 1, 4, 8, dtype=torch.int32)
+
+    def call(k, flags, idx=io, err=None, ix=None):
+        s, o = S.tensor(sc), S.tensor(idx)
+        return S.LIB.spattn_topk(ctypes.byref(s), err, ix, None, k, flags, ctypes.byref(o), None, None, 0, None)
+
+    assert call(8, 0) == 4                      # valid: reaches the device check
+    assert call(0, 0) == 1                      # K must be >= 1
+    assert call(8, 0, idx=torch.zeros(1, 1, 4, 7, dtype=torch.int32)) == 1
+    assert call(8, S.TOPK_CERTIFIED) == 1       # certified needs err + indexer
+    assert call(8, 1 << 5) == 1                 # unknown flag
+    assert call(8, 0, idx=torch.zeros(1, 1, 4, 8, dtype=torch.float32)) == 1
+
+
+def test_attention_validation():
+    q = torch.zeros(1, 4, 8, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 16, 128, dtype=torch.bfloat16)
+    o = torch.zeros(1, 4, 8, 128)
+    idx = torch.zeros(1, 2, 8, 4, dtype=torch.int32)
+
+    def call(sel, qq=q, kk=k, vv=k, oo=o, scale=0.0):
+        tq, tk, tv, to = S.tensor(qq), S.tensor(kk), S.tensor(vv), S.tensor(oo)
+        ws = torch.zeros(1 << 20, dtype=torch.uint8)
+        return S.LIB.spattn_sparse_attn_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), None, scale,
+                                            ctypes.byref(sel), ctypes.byref(to), None, ws.data_ptr(),
+                                            ws.numel(), None)
+
+    assert call(S.selection(S.SEL_INDEX, idx)) == 4
+    assert call(S.selection(S.SEL_WINDOW_GLOBAL, window=8, n_global=2)) == 4
+    assert call(S.selection(S.SEL_DENSE)) == 4
+    assert call(S.selection(7)) == 1
+    assert call(S.selection(S.SEL_INDEX, idx.float())) == 1
+    assert call(S.selection(S.SEL_INDEX, torch.zeros(1, 3, 8, 4, dtype=torch.int32))) == 1   # 3 does not divide 4
+    assert call(S.selection(S.SEL_DENSE), qq=torch.zeros(1, 4, 8, 96, dtype=torch.bfloat16),
+                kk=torch.zeros(1, 2, 16, 96, dtype=torch.bfloat16),
+                vv=torch.zeros(1, 2, 16, 96, dtype=torch.bfloat16), oo=torch.zeros(1, 4, 8, 96)) == 2
+    assert call(S.selection(S.SEL_DENSE), kk=torch.zeros(1, 3, 16, 128, dtype=torch.bfloat16)) == 1
+    assert call(S.selection(S.SEL_DENSE), scale=float("nan")) == 1
+    assert call(S.selection(S.SEL_DENSE), oo=torch.zeros(1, 4, 8, 128, dtype=torch.bfloat16)) == 1
+
+
+def test_block_select_validation():
+    q = torch.zeros(1, 2, 128, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 128, 64, dtype=torch.bfloat16)
+    out = torch.zeros(1, 2, 128, 2, dtype=torch.int32)
+
+    def call(bs, nb, oo=out, ws_bytes=1 << 20):
+        tq, tk, to = S.tensor(q), S.tensor(k), S.tensor(oo)
+        ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8)
+        return S.LIB.spattn_block_select(ctypes.byref(tq), ctypes.byref(tk), None, bs, nb, ctypes.byref(to),
+                                         None, ws.data_ptr(), ws_bytes, None)
+
+    assert call(16, 2) == 4
+    assert call(24, 2) == 1                      # not a power of two
+    assert call(16, 0) == 1
+    assert call(16, 2, ws_bytes=8) == 3
+    assert call(16, 3) == 1                      # output width must equal top_blocks

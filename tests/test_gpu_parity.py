@@ -1,0 +1,273 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Index sets must match bit for bit; outputs within max-abs 1e-5 (fp32 inputs)
+or 2e-3 (bf16 inputs, fp32 accumulation); LSE within the same bounds.
+"""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from fine_grained_top_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "no GPU"
+    torch.cuda.init()
+
+
+def S():
+    from fine_grained_top_amd import spattn
+    return spattn
+
+
+def run(wl, inp):
+    from fine_grained_top_amd.hotpath import HotPath
+    say(f"[gpu] {wl.name}: B={wl.B} N={wl.N} Nq={wl.Nq} Hq={wl.Hq}")
+    hp = HotPath(wl, inp)
+    hp.step()
+    torch.cuda.synchronize()
+    return hp
+
+
+def oracle_rows(wl, inp, rows, attention=True):
+    import oracle as orc
+    return orc.run(wl, inp, rows, attention=attention)
+
+
+def check_sets(hp, res, rows, wl):
+    idx = hp.idx.cpu().numpy()
+    cnt = hp.count.cpu().numpy()
+    groups = wl.Hq if wl.kind == "blocks" else wl.G_sel
+    bad = 0
+    for (b, r) in rows:
+        for g in range(groups):
+            want = res.blocks[(b, g, r)] if wl.kind == "blocks" else res.sets[(b, g, r)]
+            got = idx[b, g, r]
+            ok = cnt[b, g, r] == len(want) and np.array_equal(got[:len(want)], want) and np.all(got[len(want):] == -1)
+            if not ok:
+                bad += 1
+                if bad <= 3:
+                    say(f"  set mismatch b={b} g={g} r={r}: count {cnt[b, g, r]} vs {len(want)}; "
+                        f"extra {sorted(set(got[:cnt[b, g, r]]) - set(want))[:8]} missing {sorted(set(want) - set(got))[:8]}")
+    assert bad == 0, f"{bad} rows differ"
+
+
+def check_out(hp, res, rows, tol):
+    O = hp.o.cpu().numpy()
+    lse = hp.lse.cpu().numpy()
+    worst = 0.0
+    worst_l = 0.0
+    for (b, r) in rows:
+        worst = max(worst, float(np.abs(O[b, :, r, :] - res.O[(b, r)]).max()))
+        worst_l = max(worst_l, float(np.abs(lse[b, :, r] - res.lse[(b, r)]).max()))
+    say(f"  max |O - O_oracle| = {worst:.3e}, max |LSE - LSE_oracle| = {worst_l:.3e} (tol {tol})")
+    assert worst <= tol and worst_l <= tol
+
+
+# ---------------------------------------------------------------- layout probes
+@pytest.mark.parametrize("kfmt", ["fp8", "bf16"])
+def test_indexer_operand_layout_probe(kfmt):
+    """One-hot queries read back every element of every key: checks the MFMA
+    operand/accumulator layouts and the fp8 -> bf16 conversion."""
+    from fine_grained_top_amd.hotpath import to_device
+    sp = S()
+    say(f"[gpu] layout probe {kfmt}")
+    B, Nq, ctx, d = 1, 64, 512, 64
+    rng = np.random.default_rng(0)
+    qv = np.zeros((B, Nq, 1, d), np.float32)
+    for r in range(Nq):
+        qv[0, r, 0, r] = 1.0
+    if kfmt == "fp8":
+        codes = rng.integers(0, 256, size=(B, ctx, 1, d)).astype(np.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0x11
+        kst = codes
+        kval = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().numpy()
+    else:
+        kf = rng.standard_normal((B, ctx, 1, d)).astype(np.float32)
+        kst = gen.f32_to_bf16_bits(kf)
+        kval = gen.bf16_bits_to_f32(kst)
+    q = to_device(gen.f32_to_bf16_bits(qv), "bf16")
+    k = to_device(kst, kfmt)
+    ix = sp.indexer(q, k, None, sp.SCORE_DOT, 1)
+    scores = torch.full((B, 1, Nq, ctx), float("nan"), device="cuda")
+    err = torch.empty(B, 1, Nq, device="cuda")
+    sp.spattn_index_scores(ix, None, scores, err)
+    torch.cuda.synchronize()
+    got = scores.cpu().numpy()
+    for r in range(Nq):
+        p = ctx - Nq + r
+        assert np.array_equal(got[0, 0, r, : p + 1], kval[0, : p + 1, 0, r]), r
+    e = err.cpu().numpy()
+    assert np.all(e > 0) and np.all(np.isfinite(e))
+
+
+# ---------------------------------------------------------------- small workloads, every row
+def _all_rows(wl, inp):
+    return [(b, r) for b in range(wl.B) for r in range(wl.Nq)]
+
+
+def test_tiny_fp32_full():
+    wl = gen.WORKLOADS["tiny_topk_f32"]
+    inp = gen.generate(wl)
+    hp = run(wl, inp)
+    rows = _all_rows(wl, inp)
+    res = oracle_rows(wl, inp, rows)
+    check_sets(hp, res, rows, wl)
+    check_out(hp, res, rows, 1e-5)
+    idx = hp.idx.cpu().numpy()
+    for (b, i, j) in inp["needles"]:
+        assert j in idx[b, 0, i]
+
+
+@pytest.mark.parametrize("name", ["dsa_decode_small", "dsa_prefill_small", "window_global_small",
+                                  "block_sparse_small", "tiny_topk_f32_small"])
+def test_small_workload(name):
+    wl = gen.WORKLOADS[name]
+    inp = gen.generate(wl)
+    hp = run(wl, inp)
+    rows = _all_rows(wl, inp)
+    res = oracle_rows(wl, inp, rows)
+    if hp.idx is not None:
+        check_sets(hp, res, rows, wl)
+    check_out(hp, res, rows, 1e-5 if wl.dtype == "f32" else 2e-3)
+
+
+def test_run_twice_is_bitwise_identical():
+    wl = gen.WORKLOADS["dsa_decode_small"]
+    inp = gen.generate(wl)
+    hp = run(wl, inp)
+    o1, i1 = hp.o.clone(), hp.idx.clone()
+    hp.step()
+    torch.cuda.synchronize()
+    assert torch.equal(hp.idx, i1)
+    assert torch.equal(hp.o, o1)
+
+
+# ---------------------------------------------------------------- top-K edge cases
+def _topk_on(scores_np, K, ctx_len=None, Nq=None):
+    sp = S()
+    B, G, nq, ctx = scores_np.shape
+    sc = torch.from_numpy(scores_np).cuda()
+    idx = torch.empty(B, G, nq, K, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(B, G, nq, dtype=torch.int32, device="cuda")
+    cl = None if ctx_len is None else torch.tensor(ctx_len, dtype=torch.int32, device="cuda")
+    sp.spattn_topk(sc, None, None, cl, K, 0, idx, cnt)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), cnt.cpu().numpy()
+
+
+def test_topk_ties_and_edges():
+    import oracle as orc
+    say("[gpu] top-K ties/edges")
+    rng = np.random.default_rng(5)
+    B, G, Nq, ctx = 2, 2, 40, 5000
+    sc = rng.integers(-4, 5, size=(B, G, Nq, ctx)).astype(np.float32)     # heavy ties
+    sc[0, 0] = 1.0                                                        # a row of all-equal
+    sc[1, 1, :, ::3] = -0.0
+    sc[1, 1, :, 1::3] = 0.0
+    ctx_len = [ctx, 3100]
+    for K in (1, 7, 2048, 4999, 6000):
+        idx, cnt = _topk_on(sc, K, ctx_len)
+        for b in range(B):
+            for g in range(G):
+                for r in range(Nq):
+                    p = ctx_len[b] - Nq + r
+                    want = orc.topk(sc[b, g, r, : p + 1], K)
+                    assert cnt[b, g, r] == len(want)
+                    assert np.array_equal(idx[b, g, r, : len(want)], want), (K, b, g, r)
+                    assert np.all(idx[b, g, r, len(want):] == -1)
+
+
+def test_topk_random_long_rows():
+    import oracle as orc
+    say("[gpu] top-K long rows")
+    rng = np.random.default_rng(6)
+    sc = rng.standard_normal((1, 3, 2, 131072)).astype(np.float32)
+    sc[0, 1] = np.round(sc[0, 1] * 8) / 8        # coarse values: ties at the boundary
+    idx, cnt = _topk_on(sc, 2048)
+    for g in range(3):
+        for r in range(2):
+            p = 131072 - 2 + r
+            want = orc.topk(sc[0, g, r, : p + 1], 2048)
+            assert np.array_equal(idx[0, g, r], want)
+
+
+def test_certified_selection_at_rounding_midpoints():
+    """Keys whose exact value is a float32 halfway point: the float32 scores tie,
+    the exact keys decide (ties to even), then lower index."""
+    import oracle as orc
+    sp = S()
+    say("[gpu] certified midpoints")
+    d, ctx, Nq = 8, 64, 1
+    q = np.zeros((1, Nq, 1, d), np.float32)
+    q[0, 0, 0, :2] = 1.0
+    k = np.zeros((1, ctx, 1, d), np.float32)
+    rng = np.random.default_rng(7)
+    k[0, :, 0, 0] = 1.0
+    tiny = np.float32(2.0 ** -24)
+    # exact 1 + 2^-24 (rounds to 1.0), 1 + 2^-24 + 2^-40 (rounds up), 1.0, 1 + 3*2^-24 (to 1 + 2^-22)
+    pattern = [tiny, tiny + np.float32(2.0 ** -40), 0.0, 3 * tiny]
+    for j in range(ctx):
+        k[0, j, 0, 1] = pattern[j % 4] if j % 5 else np.float32(-1.0)
+    for K in (3, 10, 20, 30):
+        qt = torch.from_numpy(q).cuda()
+        kt = torch.from_numpy(k).cuda()
+        ix = sp.indexer(qt, kt, None, sp.SCORE_DOT, 1)
+        scores = torch.empty(1, 1, Nq, ctx, device="cuda")
+        err = torch.empty(1, 1, Nq, device="cuda")
+        sp.spattn_index_scores(ix, None, scores, err)
+        idx = torch.empty(1, 1, Nq, K, dtype=torch.int32, device="cuda")
+        sp.spattn_topk(scores, err, ix, None, K, sp.TOPK_CERTIFIED, idx)
+        torch.cuda.synchronize()
+        keys = orc.keys_dot(q[0, 0, 0].astype(np.float64), k[0, :, 0].astype(np.float64))
+        want = orc.topk(keys, K)
+        assert np.array_equal(idx.cpu().numpy()[0, 0, 0], want), K
+
+
+# ---------------------------------------------------------------- full-size workloads
+def test_decode_full_every_row():
+    wl = gen.WORKLOADS["dsa_decode"]
+    say("[gpu] generating dsa_decode inputs")
+    inp = gen.generate(wl)
+    hp = run(wl, inp)
+    rows = _all_rows(wl, inp)
+    res = oracle_rows(wl, inp, rows)
+    check_sets(hp, res, rows, wl)
+    check_out(hp, res, rows, 2e-3)
+
+
+def _sample_rows(wl, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(range(min(8, wl.Nq)))
+    rows |= {wl.Nq - 1, wl.Nq - 2}
+    rows |= set(int(x) for x in rng.integers(0, wl.Nq, size=n))
+    return [(0, r) for r in sorted(rows)]
+
+
+@pytest.mark.parametrize("name,n", [("window_global", 48), ("block_sparse", 24), ("dsa_prefill", 24)])
+def test_full_size_sampled_rows(name, n):
+    wl = gen.WORKLOADS[name]
+    say(f"[gpu] generating {name} inputs")
+    inp = gen.generate(wl)
+    hp = run(wl, inp)
+    rows = _sample_rows(wl, n, 11)
+    if name == "dsa_prefill":
+        rows += [(0, int(i)) for i in inp["needles"][:8, 1]]
+    res = oracle_rows(wl, inp, rows)
+    if hp.idx is not None:
+        check_sets(hp, res, rows, wl)
+    check_out(hp, res, rows, 2e-3)
+    if name == "dsa_prefill":
+        idx = hp.idx.cpu().numpy()
+        for (b, i, j) in inp["needles"]:
+            assert j in idx[b, 0, i]
