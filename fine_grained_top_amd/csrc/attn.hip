@@ -364,27 +364,41 @@ __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int 
 // merge splits: one workgroup of 128 threads per (b, r, gather group, head)
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnParams a, int Hg, SplitInfo si,
                                                            const float* part) {
+  __shared__ float fw[256];
+  __shared__ float stat[2];
   const int ngg = a.Hq / Hg;
   const int rowid = blockIdx.x, hh = blockIdx.y;
   const int gg = rowid % ngg;
   const int r = (rowid / ngg) % a.Nq;
   const int b = rowid / (ngg * a.Nq);
   const int dd = threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < si.nsplit; ++s)
-    M = fmaxf(M, part[(((int64_t)rowid * si.nsplit + s) * Hg + hh) * 130 + 128]);
-  float Ls = 0.f, Os = 0.f;
-  if (M > -INFINITY)
-    for (int s = 0; s < si.nsplit; ++s) {
-      const float* pp = part + (((int64_t)rowid * si.nsplit + s) * Hg + hh) * 130;
-      const float f = pp[128] > -INFINITY ? exp2f(pp[128] - M) : 0.f;
-      Ls += pp[129] * f;
-      Os += pp[dd] * f;
-    }
+  const float* base = part + ((int64_t)rowid * si.nsplit * Hg + hh) * 130;
+  const int64_t sstride = (int64_t)Hg * 130;
+  // split maxima and sums
+  float mv = -INFINITY, lv = 0.f;
+  if (dd < si.nsplit) {
+    mv = base[dd * sstride + 128];
+    lv = base[dd * sstride + 129];
+  }
+  float M = wave_max(mv);
+  if (dd >= 64) M = -INFINITY;        // second wave holds no splits when nsplit <= 64
+  if (dd == 0) stat[0] = M;
+  __syncthreads();
+  M = stat[0];
+  const float f = (dd < si.nsplit && mv > -INFINITY) ? exp2f(mv - M) : 0.f;
+  if (dd < si.nsplit) fw[dd] = f;
+  float Lp = wave_sum(f * lv);
+  if (dd == 0) stat[1] = Lp;
+  __syncthreads();
+  const float Ls = stat[1];
+  float Os = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < si.nsplit; ++s) Os += base[s * sstride + dd] * fw[s];
   const int h = gg * Hg + hh;
   float* o = a.o + b * a.os[0] + h * a.os[1] + r * a.os[2];
-  o[dd] = Ls > 0.f ? Os / Ls : 0.f;
-  if (a.lse && dd == 0) a.lse[((int64_t)b * a.Hq + h) * a.Nq + r] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+  o[dd] = (M > -INFINITY && Ls > 0.f) ? Os / Ls : 0.f;
+  if (a.lse && dd == 0)
+    a.lse[((int64_t)b * a.Hq + h) * a.Nq + r] = (M > -INFINITY && Ls > 0.f) ? (M + log2f(Ls)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -403,6 +417,7 @@ static SplitInfo pick_split(const AttnParams& a, int Hg) {
   int want = (2048 + rows - 1) / rows;            // aim for >= 2048 workgroups
   int maxs = (tiles + 3) / 4;                     // at least 4 tiles (one per wave) per split
   int ns = want < maxs ? want : maxs;
+  if (ns > 64) ns = 64;
   if (ns < 1) ns = 1;
   int per_tiles = (tiles + ns - 1) / ns;
   SplitInfo si;

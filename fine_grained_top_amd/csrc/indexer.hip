@@ -201,8 +201,9 @@ __global__ __launch_bounds__(256) void idx_generic_kernel(IndexerParams p) {
 // float32 accumulation of d products in any order (u = 2^-23, conservative for
 // MFMA and FMA chains alike), the ReLU/weight/head-sum chain, and the final
 // rounding of the exact score to float32; plus a 25% margin.
-__global__ void idx_err_kernel(IndexerParams p) {
-  const int row = blockIdx.x * blockDim.x + threadIdx.x;
+__global__ __launch_bounds__(256) void idx_err_kernel(IndexerParams p) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int b = blockIdx.y;
   if (row >= p.Nq * p.G_sel) return;
   const int r = row / p.G_sel, g = row % p.G_sel;
@@ -210,15 +211,18 @@ __global__ void idx_err_kernel(IndexerParams p) {
   const int L = min(p.ctx_len ? p.ctx_len[b] : p.ctx, p.ctx);
   const int nch = min(p.nchunk, (L + p.chunk - 1) / p.chunk);
   float km = 0.f;
-  for (int c = 0; c < nch; ++c) km = fmaxf(km, p.kmax[((int64_t)b * p.G_k + kg) * p.nchunk + c]);
+  for (int c = lane; c < nch; c += 64) km = fmaxf(km, p.kmax[((int64_t)b * p.G_k + kg) * p.nchunk + c]);
+  km = wave_max(km);
   double coef = 0.0;
-  for (int h = 0; h < p.hpg; ++h) {
-    double a = 0.0;
-    for (int c = 0; c < p.d_I; ++c)
-      a += fabs((double)load_val(p.q.p, p.q.dt, b * p.q.s[0] + r * p.q.s[1] + (g * p.hpg + h) * p.q.s[2] + c));
+  for (int e = lane; e < p.hpg * p.d_I; e += 64) {
+    const int h = e / p.d_I, c = e % p.d_I;
+    const double qv = fabs((double)load_val(p.q.p, p.q.dt, b * p.q.s[0] + r * p.q.s[1] + (g * p.hpg + h) * p.q.s[2] + c));
     const double wv = p.relu ? (double)p.w[b * p.ws_[0] + r * p.ws_[1] + (g * p.hpg + h) * p.ws_[2]] : 1.0;
-    coef += fabs(wv) * a;
+    coef += fabs(wv) * qv;
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) coef += __shfl_xor(coef, o, 64);
+  if (lane) return;
   const double u = 1.0 / 8388608.0;   // 2^-23
   auto gam = [&](double n) { return n * u / (1.0 - n * u); };
   const double C = 1.25 * (gam(p.d_I + 2) + gam(p.hpg + 2) * (1.0 + gam(p.d_I + 2)) + u);
@@ -275,7 +279,7 @@ hipError_t launch_index_scores(const IndexerParams& p0, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !p.err) return e;
-  dim3 g2((p.Nq * p.G_sel + 255) / 256, p.B);
+  dim3 g2((p.Nq * p.G_sel + 3) / 4, p.B);
   hipLaunchKernelGGL(idx_err_kernel, g2, dim3(256), 0, st, p);
   return hipGetLastError();
 }

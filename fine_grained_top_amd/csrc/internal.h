@@ -42,7 +42,9 @@ struct TopkParams {
   int32_t* idx;            // [B, G, Nq, K]
   int64_t is[4];
   int32_t* count;          // [B, G, Nq] or null
+  void* ws;                // workspace (few-long-rows schedule)
 };
+size_t topk_ws_bytes(const TopkParams& p);
 hipError_t launch_topk(const TopkParams& p, hipStream_t st);
 
 // ---------------------------------------------------------------- block select

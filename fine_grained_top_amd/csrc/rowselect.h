@@ -32,6 +32,31 @@ SP_DEV uint32_t block_prefix(bool flag, uint32_t* scratch, uint32_t& total) {
   return base + below;
 }
 
+// Exclusive prefix sum of `v` over the workgroup in thread order, and the total.
+template <int T>
+SP_DEV uint32_t block_scan_sum(uint32_t v, uint32_t* scratch, uint32_t& total) {
+  constexpr int NW = T / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) scratch[wid] = incl;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t c = scratch[w];
+    base += (w < wid) ? c : 0u;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
+  return base + incl - v;
+}
+
 // Find the R-th largest key (R >= 1, R <= number of included elements).
 // get(i, key) returns true when element i takes part. On return: t = that
 // key, above = number of included elements with key > t.

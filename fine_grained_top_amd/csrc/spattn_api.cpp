@@ -217,17 +217,24 @@ SPATTN_API int spattn_index_scores(const spattn_indexer* ix, const int32_t* ctx_
 }
 
 // ------------------------------------------------------------------ top-K
-SPATTN_API size_t spattn_topk_workspace(const spattn_tensor*, const spattn_indexer*, int32_t,
-                                        uint32_t) {
-  return 0;
+SPATTN_API size_t spattn_topk_workspace(const spattn_tensor* scores, const spattn_indexer* ix, int32_t k,
+                                        uint32_t flags) {
+  (void)ix;
+  (void)flags;
+  if (check_tensor(scores, "scores", 4, false) || k < 1) return (size_t)-1;
+  sp::TopkParams p{};
+  p.B = (int)scores->shape[0];
+  p.G = (int)scores->shape[1];
+  p.Nq = (int)scores->shape[2];
+  p.ctx = (int)scores->shape[3];
+  p.K = k;
+  return sp::topk_ws_bytes(p);
 }
 
 SPATTN_API int spattn_topk(const spattn_tensor* scores, const float* err, const spattn_indexer* ix,
                            const int32_t* ctx_len, int32_t k, uint32_t flags,
                            const spattn_tensor* idx_out, int32_t* count_out, void* ws,
                            size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   int rc;
   if (flags & ~(SPATTN_TOPK_CERTIFIED | SPATTN_TOPK_FUSED_INDEX))
     return fail(SPATTN_ERR_INVALID_ARG, "unknown flags");
@@ -267,6 +274,9 @@ SPATTN_API int spattn_topk(const spattn_tensor* scores, const float* err, const 
   p.ctx_len = ctx_len;
   p.idx = (int32_t*)idx_out->data;
   p.count = count_out;
+  const size_t need = sp::topk_ws_bytes(p);
+  if (ws_bytes < need || (need && !ws)) return fail(SPATTN_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  p.ws = ws;
   return launched(sp::launch_topk(p, (hipStream_t)stream));
 }
 

@@ -66,6 +66,9 @@ class HotPath:
         n = 0
         if self.wl.H_I:
             n = max(n, S.LIB.spattn_index_scores_workspace(S.ctypes.byref(self.ix)))
+            ts = S.tensor(self.scores)
+            n = max(n, S.LIB.spattn_topk_workspace(S.ctypes.byref(ts), S.ctypes.byref(self.ix), self.wl.topk,
+                                                   S.TOPK_CERTIFIED))
         if self.wl.kind == "blocks":
             tq, tk = S.tensor(self.q), S.tensor(self.k)
             n = max(n, S.LIB.spattn_block_select_workspace(S.ctypes.byref(tq), S.ctypes.byref(tk),
@@ -81,7 +84,7 @@ class HotPath:
 
     def topk(self, stream=None):
         S.spattn_topk(self.scores, self.err, self.ix, self.ctx_len, self.wl.topk, S.TOPK_CERTIFIED,
-                      self.idx, self.count, None, stream)
+                      self.idx, self.count, self.ws, stream)
 
     def block_select(self, stream=None):
         S.spattn_block_select(self.q, self.k, self.ctx_len, self.wl.block_size, self.wl.top_blocks,
