@@ -233,6 +233,62 @@ SP_DEV float exact_key(const IndexerRow& r, int64_t j) {
   return exact_key_slow(r, j);
 }
 
+// The same key computed by a whole wave for one candidate j (wave-uniform):
+// lanes split the dimensions; every load of a group of four heads is issued
+// before any reduction, and per-head sums are reduced across the wave.
+SP_DEV float wave_exact_key(const IndexerRow& r, int64_t j) {
+  const double g52 = 2.220446049250313e-16;
+  const int lane = threadIdx.x & 63;
+  const int64_t koff = j * r.k_stride;
+  double s = 0.0, Es = 0.0, Ar = 0.0;
+  bool ok = true;
+  for (int h0 = 0; h0 < r.H; h0 += 4) {
+    double y[4] = {0.0, 0.0, 0.0, 0.0}, A[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int c = lane; c < r.d; c += 64) {
+      const double kv = load_f64(r.k, r.kt, koff + c);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (h0 + u < r.H) {
+          const double t = load_f64(r.q, r.qt, (h0 + u) * r.qh_stride + c) * kv;
+          y[u] += t;
+          A[u] += fabs(t);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        y[u] += __shfl_xor(y[u], o, 64);
+        A[u] += __shfl_xor(A[u], o, 64);
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (h0 + u >= r.H) break;
+      const double E = 2.0 * (r.d + 70) * g52 * A[u] + 1e-300;
+      if (!r.relu) {
+        float key;
+        if (certify(y[u], E, key)) return key;
+        ok = false;
+        break;
+      }
+      const double w = (double)r.w[(h0 + u) * r.w_stride];
+      if (y[u] > E) {
+        s += w * y[u];
+        Es += fabs(w) * E;
+        Ar += fabs(w * y[u]);
+      } else if (!(y[u] < -E) && w != 0.0) {
+        ok = false;
+      }
+    }
+    if (!r.relu) break;
+  }
+  float key = 0.f;
+  if (r.relu && ok && certify(s, Es + 2.0 * (r.H + 4) * g52 * Ar + 1e-300, key)) return key;
+  float slow = 0.f;
+  if (lane == 0) slow = exact_key_slow(r, j);
+  return __shfl(slow, 0, 64);
+}
+
 // Block key: float32 nearest to (1/bs) * sum_{t<bs} q . k[t]; bs a power of two.
 SP_DEV float exact_block_key(const void* q, int qt, const void* k, int kt, int64_t k_stride,
                              int bs, int log2bs, int d) {

@@ -58,23 +58,31 @@ SP_DEV uint32_t block_scan_sum(uint32_t v, uint32_t* scratch, uint32_t& total) {
 }
 
 // Find the R-th largest key (R >= 1, R <= number of included elements).
-// get(i, key) returns true when element i takes part. On return: t = that
-// key, above = number of included elements with key > t.
+// get(i, key) returns true when element i takes part. Keys are taken relative
+// to `base` and must lie in [base, base + 2^bits) for included elements; the
+// bits are consumed from the top in digits of at most 12. On return: t = that
+// key (absolute), above = number of included elements with key > t.
 template <int T, typename Get>
 SP_DEV void radix_select(int n, uint32_t R, Get get, uint32_t* hist, uint32_t* sc,
-                         uint32_t& t, uint32_t& above) {
+                         uint32_t& t, uint32_t& above, uint32_t base = 0u, int bits = 32) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   constexpr int NW = T / 64;
   uint32_t prefix = 0, pmask = 0, acc_above = 0, need = R;
+  int left = bits;
 #pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int sh = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
-    const int nb = pass == 2 ? 256 : 4096;
+  while (left > 0) {
+    const int width = left >= 12 ? 12 : left;
+    const int sh = left - width;
+    const int nb = 1 << width;
+    const uint32_t dmask = (uint32_t)(nb - 1);
     for (int i = tid; i < nb; i += T) hist[i] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += T) {
       uint32_t k;
-      if (get(i, k) && (k & pmask) == prefix) atomicAdd(&hist[(k >> sh) & (nb - 1)], 1u);
+      if (get(i, k)) {
+        k -= base;
+        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> sh) & dmask], 1u);
+      }
     }
     __syncthreads();
     // thread owns bins [lo, lo+per); suffix sums from the top
@@ -113,9 +121,10 @@ SP_DEV void radix_select(int n, uint32_t R, Get get, uint32_t* hist, uint32_t* s
     acc_above += ab;
     need -= ab;
     prefix |= bin << sh;
-    pmask |= (uint32_t)(nb - 1) << sh;
+    pmask |= dmask << sh;
+    left = sh;
   }
-  t = prefix;
+  t = prefix + base;
   above = acc_above;
 }
 

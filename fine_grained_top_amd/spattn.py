@@ -46,10 +46,10 @@ class Selection(ctypes.Structure):
                 ("n_global", ctypes.c_int32), ("block_size", ctypes.c_int32)]
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
-    lib = ctypes.CDLL(LIB_PATH)
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
     P = ctypes.POINTER
     vp, sz, i32, u32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_uint32
     sig = {

@@ -192,10 +192,11 @@ def test_topk_random_long_rows():
     import oracle as orc
     say("[gpu] top-K long rows")
     rng = np.random.default_rng(6)
-    sc = rng.standard_normal((1, 3, 2, 131072)).astype(np.float32)
+    sc = rng.standard_normal((1, 4, 2, 131072)).astype(np.float32)
     sc[0, 1] = np.round(sc[0, 1] * 8) / 8        # coarse values: ties at the boundary
+    sc[0, 3] = 0.5                               # all equal: too many candidates for the short list
     idx, cnt = _topk_on(sc, 2048)
-    for g in range(3):
+    for g in range(4):
         for r in range(2):
             p = 131072 - 2 + r
             want = orc.topk(sc[0, g, r, : p + 1], 2048)
