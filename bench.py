@@ -40,6 +40,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time separate indexer-scores and top-K calls instead of the fused call")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU runs are not part of "
@@ -58,7 +60,8 @@ def main():
     t0 = time.time()
     inp = gen.generate(wl)
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s; uploading {args.replicas} replicas")
-    paths = [HotPath(wl, inp) for _ in range(args.replicas)]
+    fused = bool(wl.H_I) and not args.unfused
+    paths = [HotPath(wl, inp, fused=fused) for _ in range(args.replicas)]
     # share one workspace and one set of intermediate buffers, as one layer's call would
     base = paths[0]
     for hp in paths[1:]:
@@ -69,7 +72,9 @@ def main():
 
     stream = torch.cuda.current_stream()
     stages = []
-    if wl.H_I:
+    if wl.H_I and fused:
+        stages = [("index_topk_fused", lambda hp: hp.topk_fused()), ("attention", lambda hp: hp.attention())]
+    elif wl.H_I:
         stages = [("index_scores", lambda hp: hp.index_scores()), ("topk", lambda hp: hp.topk()),
                   ("attention", lambda hp: hp.attention())]
     elif wl.kind == "blocks":
@@ -118,6 +123,7 @@ def main():
         score_bytes = int(lens.sum()) * wl.G_sel * 4
         alg["index_scores"] = kidx_bytes + score_bytes
         alg["topk"] = score_bytes + wl.B * wl.G_sel * wl.topk * 4
+        alg["index_topk_fused"] = kidx_bytes + wl.B * wl.G_sel * wl.topk * 4
         alg["attention"] = wl.B * wl.Hkv * wl.topk * wl.d * 2 * 2 + wl.B * wl.Hq * wl.d * (2 + 4)
     dom = max(stage_ms, key=stage_ms.get)
     roof = None
@@ -135,9 +141,13 @@ def main():
         per_stage[name] = e
     if "topk" in stage_ms:
         per_stage["topk"]["rows_per_s"] = round(wl.B * wl.G_sel * wl.Nq / (stage_ms["topk"] * 1e-3), 1)
-    if "index_scores" in stage_ms and wl.H_I:
-        flops = 2.0 * float(lens.sum()) * wl.H_I * wl.d_I
-        per_stage["index_scores"]["TFLOP_s"] = round(flops / (stage_ms["index_scores"] * 1e-3) / 1e12, 3)
+    for name in ("index_scores", "index_topk_fused"):
+        if name in stage_ms and wl.H_I:
+            flops = 2.0 * float(lens.sum()) * wl.H_I * wl.d_I
+            per_stage[name]["TFLOP_s"] = round(flops / (stage_ms[name] * 1e-3) / 1e12, 3)
+    if "index_topk_fused" in stage_ms:
+        per_stage["index_topk_fused"]["rows_per_s"] = round(
+            wl.B * wl.G_sel * wl.Nq / (stage_ms["index_topk_fused"] * 1e-3), 1)
 
     # CPU oracle on a bounded sample (also a parity spot check of the last GPU outputs)
     cpu = None
@@ -189,6 +199,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
+        "path": "fused indexer+top-K" if fused else "separate indexer and top-K calls",
         "config": {"workload": wl.name, "B": wl.B, "ctx_capacity": wl.N, "Nq": wl.Nq, "Hq": wl.Hq,
                    "Hkv": wl.Hkv, "d": wl.d, "H_I": wl.H_I, "d_I": wl.d_I, "topk": wl.topk,
                    "idx_k_dtype": wl.idx_k_dtype, "len_range": wl.len_range, "replicas": args.replicas},

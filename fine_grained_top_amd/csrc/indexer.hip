@@ -27,7 +27,7 @@ SP_DEV float load_val(const void* p, int dt, int64_t i) {
 }
 
 // ----------------------------------------------------------------------------
-template <int KT, int NMB, int HPG, bool RELU>
+template <int KT, int NMB, int HPG, bool RELU, bool FILTER>
 __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -37,6 +37,11 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
   if (j0 >= L) return;
   const int M = p.Nq * p.H_I;
   const int hshift = __builtin_ctz(p.H_I);
+  __shared__ uint32_t lcount[128];
+  if (FILTER) {
+    for (int i = threadIdx.x; i < 128; i += 256) lcount[i] = 0;
+    __syncthreads();
+  }
 
   // A operands: query slot m = 32*mb + col, dims 32*half + 8*s + v (s = k-step)
   bf16x8 A[NMB][4];
@@ -130,7 +135,22 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
         const int m0 = 32 * mb + 8 * (v0 >> 2) + 4 * half + (v0 & 3);
         if (m0 < M) {
           const int r = m0 >> hshift, g = (m0 & (p.H_I - 1)) / HPG;
-          if (j <= L - p.Nq + r) p.scores[b * p.ss[0] + g * p.ss[1] + r * p.ss[2] + j] = sc;
+          if (j <= L - p.Nq + r) {
+            if (!FILTER) {
+              p.scores[b * p.ss[0] + g * p.ss[1] + r * p.ss[2] + j] = sc;
+            } else {
+              const int row = (b * p.G_sel + g) * p.Nq + r;
+              if (sc >= p.tau[row]) {
+                const int lrow = g * p.Nq + r;
+                const uint32_t slot = atomicAdd(&lcount[lrow], 1u);
+                if (slot < (uint32_t)p.cap) {
+                  const int64_t o = ((int64_t)row * p.nchunk + blockIdx.x) * p.cap + slot;
+                  p.cand_k[o] = f32_order_key(sc);
+                  p.cand_j[o] = j;
+                }
+              }
+            }
+          }
         }
       }
     }
@@ -145,6 +165,14 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
   if (threadIdx.x == 0) {
     const uint32_t m4 = max(max(red[0], red[1]), max(red[2], red[3]));
     p.kmax[(int64_t)b * p.nchunk + blockIdx.x] = bf16_to_f32(m4);
+  }
+  if (FILTER) {
+    const int nrows = p.G_sel * p.Nq;
+    for (int i = threadIdx.x; i < nrows; i += 256) {
+      const int g = i / p.Nq, r = i % p.Nq;
+      const int row = (b * p.G_sel + g) * p.Nq + r;
+      p.cand_n[(int64_t)row * p.nchunk + blockIdx.x] = lcount[i];
+    }
   }
 }
 
@@ -235,26 +263,26 @@ size_t indexer_ws_bytes(int B, int G_k, int ctx) {
   return (size_t)B * G_k * nchunk * sizeof(float);
 }
 
-template <int KT, int NMB, int HPG, bool RELU>
+template <int KT, int NMB, int HPG, bool RELU, bool FILTER>
 static void launch_mfma(const IndexerParams& p, hipStream_t st) {
   dim3 grid((p.ctx + kMfmaChunk - 1) / kMfmaChunk, p.B);
-  hipLaunchKernelGGL((idx_mfma64_kernel<KT, NMB, HPG, RELU>), grid, dim3(256), 0, st, p);
+  hipLaunchKernelGGL((idx_mfma64_kernel<KT, NMB, HPG, RELU, FILTER>), grid, dim3(256), 0, st, p);
 }
 
-template <int KT, int NMB>
+template <int KT, int NMB, bool FILTER>
 static void dispatch_hpg(const IndexerParams& p, hipStream_t st) {
-  if (!p.relu) return launch_mfma<KT, NMB, 1, false>(p, st);
-  if (p.hpg == 1) return launch_mfma<KT, NMB, 1, true>(p, st);
-  if (p.hpg == 2) return launch_mfma<KT, NMB, 2, true>(p, st);
-  return launch_mfma<KT, NMB, 4, true>(p, st);
+  if (!p.relu) return launch_mfma<KT, NMB, 1, false, FILTER>(p, st);
+  if (p.hpg == 1) return launch_mfma<KT, NMB, 1, true, FILTER>(p, st);
+  if (p.hpg == 2) return launch_mfma<KT, NMB, 2, true, FILTER>(p, st);
+  return launch_mfma<KT, NMB, 4, true, FILTER>(p, st);
 }
 
-template <int KT>
+template <int KT, bool FILTER>
 static void dispatch_nmb(const IndexerParams& p, hipStream_t st) {
   const int M = p.Nq * p.H_I;
-  if (M <= 32) return dispatch_hpg<KT, 1>(p, st);
-  if (M <= 64) return dispatch_hpg<KT, 2>(p, st);
-  return dispatch_hpg<KT, 4>(p, st);
+  if (M <= 32) return dispatch_hpg<KT, 1, FILTER>(p, st);
+  if (M <= 64) return dispatch_hpg<KT, 2, FILTER>(p, st);
+  return dispatch_hpg<KT, 4, FILTER>(p, st);
 }
 
 static bool mfma_ok(const IndexerParams& p) {
@@ -269,8 +297,8 @@ hipError_t launch_index_scores(const IndexerParams& p0, hipStream_t st) {
   if (mfma_ok(p)) {
     p.chunk = kMfmaChunk;
     p.nchunk = (p.ctx + kMfmaChunk - 1) / kMfmaChunk;
-    if (p.k.dt == DT_FP8) dispatch_nmb<DT_FP8>(p, st);
-    else dispatch_nmb<DT_BF16>(p, st);
+    if (p.k.dt == DT_FP8) dispatch_nmb<DT_FP8, false>(p, st);
+    else dispatch_nmb<DT_BF16, false>(p, st);
   } else {
     p.chunk = kGenChunk;
     p.nchunk = (p.ctx + kGenChunk - 1) / kGenChunk;
@@ -281,6 +309,17 @@ hipError_t launch_index_scores(const IndexerParams& p0, hipStream_t st) {
   if (e != hipSuccess || !p.err) return e;
   dim3 g2((p.Nq * p.G_sel + 3) / 4, p.B);
   hipLaunchKernelGGL(idx_err_kernel, g2, dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+bool index_filter_ok(const IndexerParams& p) { return mfma_ok(p); }
+
+hipError_t launch_index_filter(const IndexerParams& p0, hipStream_t st) {
+  IndexerParams p = p0;
+  p.chunk = kMfmaChunk;
+  p.nchunk = (p.ctx + kMfmaChunk - 1) / kMfmaChunk;
+  if (p.k.dt == DT_FP8) dispatch_nmb<DT_FP8, true>(p, st);
+  else dispatch_nmb<DT_BF16, true>(p, st);
   return hipGetLastError();
 }
 

@@ -26,7 +26,15 @@ struct IndexerParams {
   float* err;              // [B, G_sel, Nq] or null
   float* kmax;             // workspace [B, G_k, nchunk]
   int chunk, nchunk;
+  // threshold filter (fused indexer + top-K): keep (key, index) pairs with score >= tau
+  const float* tau;        // [B, G_sel, Nq] or null (store every score instead)
+  uint32_t* cand_k;        // [rows][nchunk][cap] order keys
+  uint32_t* cand_j;        // [rows][nchunk][cap] key positions
+  uint32_t* cand_n;        // [rows][nchunk] number found (may exceed cap)
+  int cap;
 };
+bool index_filter_ok(const IndexerParams& p);
+hipError_t launch_index_filter(const IndexerParams& p, hipStream_t st);   // chunk = 512
 size_t indexer_ws_bytes(int B, int G_k, int ctx);
 hipError_t launch_index_scores(const IndexerParams& p, hipStream_t st);
 
@@ -46,6 +54,9 @@ struct TopkParams {
 };
 size_t topk_ws_bytes(const TopkParams& p);
 hipError_t launch_topk(const TopkParams& p, hipStream_t st);
+bool topk_fused_ok(const TopkParams& p);
+size_t topk_fused_ws_bytes(const TopkParams& p);
+hipError_t launch_topk_fused(const TopkParams& p, hipStream_t st);
 
 // ---------------------------------------------------------------- block select
 struct BlockSelectParams {

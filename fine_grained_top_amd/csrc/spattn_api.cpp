@@ -217,53 +217,47 @@ SPATTN_API int spattn_index_scores(const spattn_indexer* ix, const int32_t* ctx_
 }
 
 // ------------------------------------------------------------------ top-K
-SPATTN_API size_t spattn_topk_workspace(const spattn_tensor* scores, const spattn_indexer* ix, int32_t k,
-                                        uint32_t flags) {
-  (void)ix;
-  (void)flags;
-  if (check_tensor(scores, "scores", 4, false) || k < 1) return (size_t)-1;
-  sp::TopkParams p{};
-  p.B = (int)scores->shape[0];
-  p.G = (int)scores->shape[1];
-  p.Nq = (int)scores->shape[2];
-  p.ctx = (int)scores->shape[3];
-  p.K = k;
-  return sp::topk_ws_bytes(p);
-}
-
-SPATTN_API int spattn_topk(const spattn_tensor* scores, const float* err, const spattn_indexer* ix,
-                           const int32_t* ctx_len, int32_t k, uint32_t flags,
-                           const spattn_tensor* idx_out, int32_t* count_out, void* ws,
-                           size_t ws_bytes, void* stream) {
+static int topk_setup(const spattn_tensor* scores, const float* err, const spattn_indexer* ix,
+                      const int32_t* ctx_len, int32_t k, uint32_t flags, const spattn_tensor* idx_out,
+                      sp::TopkParams& p) {
   int rc;
+  p = sp::TopkParams{};
   if (flags & ~(SPATTN_TOPK_CERTIFIED | SPATTN_TOPK_FUSED_INDEX))
     return fail(SPATTN_ERR_INVALID_ARG, "unknown flags");
-  if (flags & SPATTN_TOPK_FUSED_INDEX)
-    return fail(SPATTN_ERR_UNSUPPORTED, "fused indexer top-K is not available in this build");
   if (k < 1 || k > 16384) return fail(SPATTN_ERR_INVALID_ARG, "k must be in 1..16384");
-  if ((rc = check_tensor(scores, "scores", 4, false))) return rc;
-  if (scores->dtype != SPATTN_F32) return fail(SPATTN_ERR_INVALID_ARG, "scores must be f32");
-  if ((rc = check_tensor(idx_out, "idx_out", 4, false))) return rc;
-  if (idx_out->dtype != SPATTN_I32) return fail(SPATTN_ERR_INVALID_ARG, "idx_out must be int32");
-  const int64_t B = scores->shape[0], G = scores->shape[1], Nq = scores->shape[2], ctx = scores->shape[3];
-  if (idx_out->shape[0] != B || idx_out->shape[1] != G || idx_out->shape[2] != Nq || idx_out->shape[3] != k)
-    return fail(SPATTN_ERR_INVALID_ARG, "idx_out must be [B, G, Nq, k]");
-  if (Nq < 1 || ctx < 1 || Nq > ctx) return fail(SPATTN_ERR_INVALID_ARG, "need 1 <= Nq <= ctx");
-  sp::TopkParams p{};
-  if (flags & SPATTN_TOPK_CERTIFIED) {
-    int64_t iB, iNq, ictx, iG;
-    if (!err) return fail(SPATTN_ERR_INVALID_ARG, "certified selection needs err");
-    if ((rc = check_indexer(ix, &iB, &iNq, &ictx, &iG))) return rc;
-    if (iB != B || iNq != Nq || ictx != ctx || iG != G)
-      return fail(SPATTN_ERR_INVALID_ARG, "indexer shapes do not match scores");
+  int64_t B, G, Nq, ctx;
+  if (flags & SPATTN_TOPK_FUSED_INDEX) {
+    if (scores || err) return fail(SPATTN_ERR_INVALID_ARG, "fused selection takes no scores or err");
+    if ((rc = check_indexer(ix, &B, &Nq, &ctx, &G))) return rc;
     p.certified = true;
     p.ix = indexer_params(ix, ctx_len);
+  } else {
+    if ((rc = check_tensor(scores, "scores", 4, false))) return rc;
+    if (scores->dtype != SPATTN_F32) return fail(SPATTN_ERR_INVALID_ARG, "scores must be f32");
+    B = scores->shape[0];
+    G = scores->shape[1];
+    Nq = scores->shape[2];
+    ctx = scores->shape[3];
+    if (Nq < 1 || ctx < 1 || Nq > ctx) return fail(SPATTN_ERR_INVALID_ARG, "need 1 <= Nq <= ctx");
+    if (flags & SPATTN_TOPK_CERTIFIED) {
+      int64_t iB, iNq, ictx, iG;
+      if (!err) return fail(SPATTN_ERR_INVALID_ARG, "certified selection needs err");
+      if ((rc = check_indexer(ix, &iB, &iNq, &ictx, &iG))) return rc;
+      if (iB != B || iNq != Nq || ictx != ctx || iG != G)
+        return fail(SPATTN_ERR_INVALID_ARG, "indexer shapes do not match scores");
+      p.certified = true;
+      p.ix = indexer_params(ix, ctx_len);
+    }
+    p.scores = (const float*)scores->data;
+    for (int i = 0; i < 4; ++i) p.ss[i] = scores->stride[i];
   }
-  if ((rc = device_ok())) return rc;
-  p.scores = (const float*)scores->data;
-  for (int i = 0; i < 4; ++i) {
-    p.ss[i] = scores->stride[i];
-    p.is[i] = idx_out->stride[i];
+  if (idx_out) {
+    if ((rc = check_tensor(idx_out, "idx_out", 4, false))) return rc;
+    if (idx_out->dtype != SPATTN_I32) return fail(SPATTN_ERR_INVALID_ARG, "idx_out must be int32");
+    if (idx_out->shape[0] != B || idx_out->shape[1] != G || idx_out->shape[2] != Nq || idx_out->shape[3] != k)
+      return fail(SPATTN_ERR_INVALID_ARG, "idx_out must be [B, G, Nq, k]");
+    p.idx = (int32_t*)idx_out->data;
+    for (int i = 0; i < 4; ++i) p.is[i] = idx_out->stride[i];
   }
   p.err = err;
   p.B = (int)B;
@@ -272,12 +266,34 @@ SPATTN_API int spattn_topk(const spattn_tensor* scores, const float* err, const 
   p.ctx = (int)ctx;
   p.K = k;
   p.ctx_len = ctx_len;
-  p.idx = (int32_t*)idx_out->data;
+  if ((flags & SPATTN_TOPK_FUSED_INDEX) && !sp::topk_fused_ok(p))
+    return fail(SPATTN_ERR_UNSUPPORTED,
+                "fused selection needs d_I = 64, bf16 q_idx, bf16/fp8 k_idx shared by all groups, "
+                "<= 4 heads per group, Nq * H_I <= 128 (power-of-two H_I) and ctx <= 262144");
+  return SPATTN_OK;
+}
+
+SPATTN_API size_t spattn_topk_workspace(const spattn_tensor* scores, const spattn_indexer* ix, int32_t k,
+                                        uint32_t flags) {
+  sp::TopkParams p;
+  if (topk_setup(scores, nullptr, ix, nullptr, k, flags & ~SPATTN_TOPK_CERTIFIED, nullptr, p)) return (size_t)-1;
+  return (flags & SPATTN_TOPK_FUSED_INDEX) ? sp::topk_fused_ws_bytes(p) : sp::topk_ws_bytes(p);
+}
+
+SPATTN_API int spattn_topk(const spattn_tensor* scores, const float* err, const spattn_indexer* ix,
+                           const int32_t* ctx_len, int32_t k, uint32_t flags, const spattn_tensor* idx_out,
+                           int32_t* count_out, void* ws, size_t ws_bytes, void* stream) {
+  sp::TopkParams p;
+  int rc;
+  if (!idx_out) return fail(SPATTN_ERR_INVALID_ARG, "idx_out: null tensor");
+  if ((rc = topk_setup(scores, err, ix, ctx_len, k, flags, idx_out, p))) return rc;
   p.count = count_out;
-  const size_t need = sp::topk_ws_bytes(p);
+  const bool fused = (flags & SPATTN_TOPK_FUSED_INDEX) != 0;
+  const size_t need = fused ? sp::topk_fused_ws_bytes(p) : sp::topk_ws_bytes(p);
   if (ws_bytes < need || (need && !ws)) return fail(SPATTN_ERR_WORKSPACE, "workspace needs %zu bytes", need);
   p.ws = ws;
-  return launched(sp::launch_topk(p, (hipStream_t)stream));
+  if ((rc = device_ok())) return rc;
+  return launched(fused ? sp::launch_topk_fused(p, (hipStream_t)stream) : sp::launch_topk(p, (hipStream_t)stream));
 }
 
 // ------------------------------------------------------------------ block select

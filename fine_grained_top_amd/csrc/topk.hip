@@ -46,7 +46,7 @@ struct RowCtx {
   int b, g, r, n;
   const float* s;
   int32_t* out;
-  uint32_t klo, khi;     // band limits as order keys (set after t is known)
+  float eps;             // certified: bound on |score - key| of this row
   IndexerRow ir;
 };
 
@@ -60,6 +60,7 @@ SP_DEV RowCtx row_ctx(const TopkParams& p, int row) {
   c.out = p.idx + c.b * p.is[0] + c.g * p.is[1] + c.r * p.is[2];
   c.s = p.scores + c.b * p.ss[0] + c.g * p.ss[1] + c.r * p.ss[2];
   c.ir = IndexerRow{};
+  c.eps = (p.certified && p.err) ? p.err[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] : 0.f;
   if (p.certified) {
     const IndexerParams& x = p.ix;
     const int hpg = x.hpg;
@@ -89,8 +90,7 @@ SP_DEV void band_limits(const TopkParams& p, const RowCtx& c, float tf, float lo
     khi = f32_order_key(hi_f);
     return;
   }
-  const float eps = p.err[((int64_t)c.b * p.G + c.g) * p.Nq + c.r];
-  const float E = 2.0f * eps * 1.0001f + 1e-30f;
+  const float E = 2.0f * c.eps * 1.0001f + 1e-30f;
   klo = f32_order_key(nextafterf(lo_f - E, -INFINITY));
   khi = f32_order_key(nextafterf(hi_f + E, INFINITY));
   (void)tf;
@@ -100,13 +100,13 @@ SP_DEV uint32_t exkey_of(const TopkParams& p, const RowCtx& c, int j, uint32_t k
   return p.certified ? f32_order_key(exact_key(c.ir, j)) : ks;
 }
 
-// The whole selection for one row by one workgroup of T threads.
-template <int T>
-SP_DEV void row_topk_single(const TopkParams& p, RowCtx& c, RowSmem& sm) {
+// The whole selection for one row by one workgroup of T threads; score(i)
+// gives the float32 score of candidate i.
+template <int T, typename Score>
+SP_DEV void row_topk_single(const TopkParams& p, RowCtx& c, RowSmem& sm, Score score) {
   const int tid = threadIdx.x;
   const int n = c.n, K = p.K;
-  const float* s = c.s;
-  auto skey = [&](int i) -> uint32_t { return f32_order_key(s[i]); };
+  auto skey = [&](int i) -> uint32_t { return f32_order_key(score(i)); };
   uint32_t t, above;
   radix_select<T>(n, (uint32_t)K, [&](int i, uint32_t& k) { k = skey(i); return true; }, sm.hist, sm.sc, t,
                   above);
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(TopkParams p) {
   __shared__ RowSmem sm;
   RowCtx c = row_ctx(p, blockIdx.x);
   if (c.n <= p.K) return write_all(p, c, kTkThreads);
-  row_topk_single<kTkThreads>(p, c, sm);
+  row_topk_single<kTkThreads>(p, c, sm, [&](int i) { return c.s[i]; });
   if (p.count && threadIdx.x == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = p.K;
 }
 
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kTkThreads) void mt_finalize_kernel(TopkParams p, M
   if (tid < nch) sm.coff[tid] = coff;
   const bool any_over = __syncthreads_or(over) != 0;
   if (any_over || n_cand > (uint32_t)kCandCap) {   // too many near the threshold: one pass over the row
-    row_topk_single<T>(p, c, sm.row);
+    row_topk_single<T>(p, c, sm.row, [&](int i) { return c.s[i]; });
     if (p.count && tid == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = p.K;
     return;
   }
@@ -476,6 +476,316 @@ __global__ __launch_bounds__(kTkThreads) void mt_finalize_kernel(TopkParams p, M
   }
   for (int i = (int)total + tid; i < p.K; i += T) c.out[i] = -1;
   if (p.count && tid == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = (int)min(total, (uint32_t)p.K);
+}
+
+// ---------------------------------------------------------------- fused indexer + top-K
+// The score matrix is never written. A pilot scores a 1/32 sample of each
+// row's keys (runs of 64 keys every 2048) and sets a threshold tau whose
+// expected number of survivors is about 1.5 K; the MFMA indexer then keeps
+// only (key, index) pairs with score >= tau; the finalize kernel selects the
+// exact top-K among them (certified, as above) after checking that every key
+// that could belong to it was kept (count >= K and t - 2 eps >= tau). When a
+// check fails the row is redone by recomputing scores, so the result never
+// depends on the sample.
+constexpr int kPilotStride = 2048, kPilotRun = 64, kPilotCap = 8192;
+
+// float32 score recomputed by one thread (FMA chains; within the same bound)
+SP_DEV float recompute_score(const IndexerRow& r, int64_t j) {
+  const int64_t koff = j * r.k_stride;
+  float s = 0.f;
+  for (int h = 0; h < r.H; ++h) {
+    float d = 0.f;
+    for (int c = 0; c < r.d; ++c)
+      d = fmaf((float)load_f64(r.q, r.qt, h * r.qh_stride + c), (float)load_f64(r.k, r.kt, koff + c), d);
+    s = r.relu ? fmaf(r.w[h * r.w_stride], fmaxf(d, 0.f), s) : d;
+  }
+  return s;
+}
+
+// rigorous |score~ - key| bound of a row, as computed by the indexer
+SP_DEV float row_eps(const TopkParams& p, const RowCtx& c, const float* kmax, int nchunk, int chunk,
+                     float* red) {
+  const IndexerParams& x = p.ix;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int L = min(p.ctx_len ? p.ctx_len[c.b] : p.ctx, p.ctx);
+  const int nch = min(nchunk, (L + chunk - 1) / chunk);
+  float km = 0.f;
+  for (int i = tid; i < nch; i += blockDim.x) km = fmaxf(km, kmax[(int64_t)c.b * nchunk + i]);
+  float coef = 0.f;
+  for (int e = tid; e < c.ir.H * c.ir.d; e += blockDim.x) {
+    const int h = e / c.ir.d, cc = e % c.ir.d;
+    const float qv = fabsf((float)load_f64(c.ir.q, c.ir.qt, h * c.ir.qh_stride + cc));
+    const float wv = c.ir.relu ? fabsf(c.ir.w[h * c.ir.w_stride]) : 1.f;
+    coef = fmaf(wv, qv, coef);
+  }
+  km = wave_max(km);
+  coef = wave_sum(coef);
+  if (lane == 0) {
+    red[wid] = km;
+    red[16 + wid] = coef;
+  }
+  __syncthreads();
+  float KM = 0.f, CO = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+    KM = fmaxf(KM, red[w]);
+    CO += red[16 + w];
+  }
+  __syncthreads();
+  const double u = 1.0 / 8388608.0;
+  auto gam = [&](double n) { return n * u / (1.0 - n * u); };
+  const double C = 1.25 * (gam(x.d_I + 2) + gam(x.hpg + 2) * (1.0 + gam(x.d_I + 2)) + u);
+  // coef was summed in float32: inflate by its own rounding bound
+  const double e = C * (double)CO * (1.0 + gam(x.hpg * x.d_I + 2)) * (double)KM * (1.0 + 1e-6) + 1e-30;
+  return (float)e * (1.0f + 1e-6f);
+}
+
+__global__ __launch_bounds__(kTkThreads) void fz_pilot_kernel(TopkParams p, float* tau) {
+  constexpr int T = kTkThreads;
+  __shared__ uint32_t skey[kPilotCap];
+  __shared__ uint32_t hist[4096];
+  __shared__ uint32_t sc[16];
+  __shared__ float qs[4 * 64];       // the fused path has d_I = 64 and <= 4 heads per group
+  __shared__ float wsh[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  RowCtx c = row_ctx(p, row);
+  if (c.n <= p.K) {
+    if (tid == 0) tau[row] = INFINITY;   // every key is selected; nothing to filter
+    return;
+  }
+  const IndexerRow& ir = c.ir;
+  for (int e = tid; e < ir.H * 64; e += T) qs[e] = (float)load_f64(ir.q, ir.qt, (e >> 6) * ir.qh_stride + (e & 63));
+  if (tid < ir.H) wsh[tid] = ir.relu ? ir.w[tid * ir.w_stride] : 1.f;
+  __syncthreads();
+  const int nsb = (c.n + kPilotStride - 1) / kPilotStride;
+  const int slots = nsb * kPilotRun;
+  int m = 0;
+  for (int i = tid; i < slots; i += T) {
+    const int j = (i / kPilotRun) * kPilotStride + (i % kPilotRun);
+    uint32_t key = 0u;
+    if (j < c.n) {
+      float kv[64];
+      if (ir.kt == DT_FP8) {
+        const u32x4* kp = (const u32x4*)((const uint8_t*)ir.k + (int64_t)j * ir.k_stride);
+        u32x4 raw[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) raw[u] = kp[u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u][v], false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u][v], true);
+            kv[16 * u + 4 * v + 0] = lo[0];
+            kv[16 * u + 4 * v + 1] = lo[1];
+            kv[16 * u + 4 * v + 2] = hi[0];
+            kv[16 * u + 4 * v + 3] = hi[1];
+          }
+      } else {
+        const u32x4* kp = (const u32x4*)((const uint16_t*)ir.k + (int64_t)j * ir.k_stride);
+        u32x4 raw[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) raw[u] = kp[u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            kv[8 * u + 2 * v] = __uint_as_float(raw[u][v] << 16);
+            kv[8 * u + 2 * v + 1] = __uint_as_float(raw[u][v] & 0xFFFF0000u);
+          }
+      }
+      float sc2 = 0.f;
+      for (int h = 0; h < ir.H; ++h) {
+        float d = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < 64; ++cc) d = fmaf(qs[h * 64 + cc], kv[cc], d);
+        sc2 = ir.relu ? fmaf(wsh[h], fmaxf(d, 0.f), sc2) : d;
+      }
+      key = f32_order_key(sc2);
+      ++m;
+    }
+    skey[i] = key;
+  }
+  uint32_t mt;
+  block_scan_sum<T>((uint32_t)m, sc, mt);
+  const uint64_t want = ((uint64_t)3 * p.K * mt + 2ull * c.n - 1) / (2ull * c.n) + 16;   // ~1.5 K survivors
+  const uint32_t R = (uint32_t)min((uint64_t)mt, want);
+  uint32_t t, above;
+  radix_select<T>(slots, R,
+                  [&](int i, uint32_t& k) {
+                    k = skey[i];
+                    return ((i / kPilotRun) * kPilotStride + (i % kPilotRun)) < c.n;
+                  },
+                  hist, sc, t, above);
+  if (tid == 0) tau[row] = order_key_f32(t);
+}
+
+struct FzWs {
+  float* tau;
+  float* kmax;
+  uint32_t* cand_n;
+  uint32_t* cand_k;
+  uint32_t* cand_j;
+  int nchunk, cap;
+};
+
+struct FzSmem {
+  RowSmem row;
+  uint32_t ck[kCandCap];
+  uint32_t cj[kCandCap];
+  uint32_t bm[kMaxWords];
+  uint32_t coff[kTkThreads + 1];
+  float red[32];
+};
+
+__global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs w) {
+  constexpr int T = kTkThreads;
+  __shared__ FzSmem sm;
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  RowCtx c = row_ctx(p, row);
+  if (c.n <= p.K) return write_all(p, c, T);
+  c.eps = row_eps(p, c, w.kmax, w.nchunk, 512, sm.red);
+  const float eps = c.eps;
+  auto fallback = [&]() {
+    row_topk_single<T>(p, c, sm.row, [&](int i) { return recompute_score(c.ir, i); });
+    if (p.count && tid == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = p.K;
+  };
+  // candidate counts of the chunks covering keys 0..p (nch <= T)
+  const int nch = (c.n + 511) / 512;
+  uint32_t my = 0;
+  bool over = false;
+  if (tid < nch) {
+    my = w.cand_n[(int64_t)row * w.nchunk + tid];
+    over = my > (uint32_t)w.cap;
+  }
+  uint32_t n_cand;
+  const uint32_t off = block_scan_sum<T>(my, sm.row.sc, n_cand);
+  if (tid < nch) sm.coff[tid] = off;
+  if (tid == 0) sm.coff[nch] = n_cand;
+  const bool any_over = __syncthreads_or(over) != 0;
+  if (any_over || n_cand < (uint32_t)p.K || n_cand > (uint32_t)kCandCap) return fallback();
+  // compact into LDS: candidate e belongs to the chunk whose offset range holds it
+  for (uint32_t e = tid; e < n_cand; e += T) {
+    int lo = 0, hi = nch;                   // coff[lo] <= e < coff[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (sm.coff[mid] <= e) lo = mid; else hi = mid;
+    }
+    const int64_t src = ((int64_t)row * w.nchunk + lo) * w.cap + (e - sm.coff[lo]);
+    sm.ck[e] = w.cand_k[src];
+    sm.cj[e] = w.cand_j[src];
+  }
+  const int nwords = (c.n + 31) >> 5;
+  for (int i = tid; i < nwords; i += T) sm.bm[i] = 0u;
+  __syncthreads();
+  const uint32_t base = f32_order_key(w.tau[row]);
+  uint32_t kmx = 0;
+  for (uint32_t i = tid; i < n_cand; i += T) kmx = max(kmx, sm.ck[i]);
+  kmx = wave_max_u32(kmx);
+  if (lane == 0) sm.row.sc[tid >> 6] = kmx;
+  __syncthreads();
+  for (int i = 0; i < T / 64; ++i) kmx = max(kmx, sm.row.sc[i]);
+  __syncthreads();
+  const int bits = 32 - __builtin_clz((kmx - base) | 1u);
+  uint32_t t, above;
+  radix_select<T>((int)n_cand, (uint32_t)p.K, [&](int i, uint32_t& k) { k = sm.ck[i]; return true; },
+                  sm.row.hist, sm.row.sc, t, above, base, bits);
+  const float tf = order_key_f32(t);
+  const float E = 2.0f * eps * 1.0001f + 1e-30f;
+  const uint32_t klo = f32_order_key(nextafterf(tf - E, -INFINITY));
+  const uint32_t khi = f32_order_key(nextafterf(tf + E, INFINITY));
+  if (klo < base) return fallback();        // part of the band may lie below tau
+  uint32_t n_in = 0;
+  if (tid == 0) sm.row.run[0] = 0;
+  __syncthreads();
+  for (uint32_t i = tid; i < n_cand; i += T) {
+    const uint32_t ks = sm.ck[i];
+    if (ks > khi) {
+      atomicOr(&sm.bm[sm.cj[i] >> 5], 1u << (sm.cj[i] & 31));
+      ++n_in;
+    } else if (ks >= klo) {
+      const uint32_t slot = atomicAdd(&sm.row.run[0], 1u);
+      if (slot < (uint32_t)kBandCap) {
+        sm.row.band_j[slot] = sm.cj[i];
+        sm.row.band_k[slot] = ks;
+      }
+    }
+  }
+  uint32_t tot_in;
+  block_scan_sum<T>(n_in, sm.row.sc, tot_in);
+  const uint32_t nb = sm.row.run[0];
+  if (nb > (uint32_t)kBandCap) return fallback();
+  const uint32_t R2 = (uint32_t)p.K - tot_in;
+  for (uint32_t e = tid >> 6; e < nb; e += T / 64) {
+    const float key = wave_exact_key(c.ir, sm.row.band_j[e]);
+    if (lane == 0) sm.row.band_k[e] = f32_order_key(key);
+  }
+  __syncthreads();
+  for (uint32_t e = tid; e < nb; e += T) {
+    const uint32_t ke = sm.row.band_k[e], je = sm.row.band_j[e];
+    uint32_t rank = 0;
+    for (uint32_t f = 0; f < nb; ++f) {
+      const uint32_t kf = sm.row.band_k[f];
+      rank += (kf > ke || (kf == ke && sm.row.band_j[f] < je)) ? 1u : 0u;
+    }
+    if (rank < R2) atomicOr(&sm.bm[je >> 5], 1u << (je & 31));
+  }
+  __syncthreads();
+  const int perw = (nwords + T - 1) / T;
+  const int w0 = tid * perw, w1 = min(nwords, w0 + perw);
+  uint32_t cnt = 0;
+  for (int i = w0; i < w1; ++i) cnt += __popc(sm.bm[i]);
+  uint32_t total;
+  uint32_t pos = block_scan_sum<T>(cnt, sm.row.sc, total);
+  for (int i = w0; i < w1; ++i) {
+    uint32_t m = sm.bm[i];
+    while (m) {
+      const int bit = __ffs(m) - 1;
+      m &= m - 1;
+      if (pos < (uint32_t)p.K) c.out[pos] = i * 32 + bit;
+      ++pos;
+    }
+  }
+  for (int i = (int)total + tid; i < p.K; i += T) c.out[i] = -1;
+  if (p.count && tid == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = (int)min(total, (uint32_t)p.K);
+}
+
+static constexpr int kFzCap = 512;   // = keys per indexer chunk: a chunk can never overflow
+
+bool topk_fused_ok(const TopkParams& p) {
+  return index_filter_ok(p.ix) && p.ctx <= kPilotCap / kPilotRun * kPilotStride &&
+         (p.ctx + 31) / 32 <= kMaxWords && (p.ctx + 511) / 512 <= kTkThreads;
+}
+
+size_t topk_fused_ws_bytes(const TopkParams& p) {
+  const int64_t rows = (int64_t)p.B * p.G * p.Nq;
+  const int64_t nchunk = (p.ctx + 511) / 512;
+  return (size_t)(rows + (int64_t)p.B * nchunk + rows * nchunk * (1 + 2 * kFzCap)) * 4;
+}
+
+hipError_t launch_topk_fused(const TopkParams& p, hipStream_t st) {
+  const int rows = p.B * p.G * p.Nq;
+  FzWs w;
+  w.nchunk = (p.ctx + 511) / 512;
+  w.cap = kFzCap;
+  float* base = (float*)p.ws;
+  w.tau = base;
+  w.kmax = w.tau + rows;
+  w.cand_n = (uint32_t*)(w.kmax + (int64_t)p.B * w.nchunk);
+  w.cand_k = w.cand_n + (int64_t)rows * w.nchunk;
+  w.cand_j = w.cand_k + (int64_t)rows * w.nchunk * w.cap;
+  hipLaunchKernelGGL(fz_pilot_kernel, dim3(rows), dim3(kTkThreads), 0, st, p, w.tau);
+  IndexerParams ix = p.ix;
+  ix.kmax = w.kmax;
+  ix.tau = w.tau;
+  ix.cand_k = w.cand_k;
+  ix.cand_j = w.cand_j;
+  ix.cand_n = w.cand_n;
+  ix.cap = w.cap;
+  ix.err = nullptr;
+  hipError_t e = launch_index_filter(ix, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fz_final_kernel, dim3(rows), dim3(kTkThreads), 0, st, p, w);
+  return hipGetLastError();
 }
 
 static bool use_multi(const TopkParams& p) {

@@ -27,9 +27,10 @@ def to_device(arr: np.ndarray, fmt: str, device="cuda") -> torch.Tensor:
 class HotPath:
     """Buffers and calls for one workload; ``step()`` runs the whole path once."""
 
-    def __init__(self, wl: Workload, inp: Dict[str, np.ndarray], device="cuda"):
+    def __init__(self, wl: Workload, inp: Dict[str, np.ndarray], device="cuda", fused: bool = False):
         self.wl = wl
         self.device = device
+        self.fused = fused
         dt = wl.dtype
         self.q = to_device(inp["q"], dt, device)
         self.k = to_device(inp["k"], dt, device)
@@ -69,6 +70,9 @@ class HotPath:
             ts = S.tensor(self.scores)
             n = max(n, S.LIB.spattn_topk_workspace(S.ctypes.byref(ts), S.ctypes.byref(self.ix), self.wl.topk,
                                                    S.TOPK_CERTIFIED))
+            if self.fused:
+                n = max(n, S.LIB.spattn_topk_workspace(None, S.ctypes.byref(self.ix), self.wl.topk,
+                                                       S.TOPK_FUSED_INDEX))
         if self.wl.kind == "blocks":
             tq, tk = S.tensor(self.q), S.tensor(self.k)
             n = max(n, S.LIB.spattn_block_select_workspace(S.ctypes.byref(tq), S.ctypes.byref(tk),
@@ -86,6 +90,10 @@ class HotPath:
         S.spattn_topk(self.scores, self.err, self.ix, self.ctx_len, self.wl.topk, S.TOPK_CERTIFIED,
                       self.idx, self.count, self.ws, stream)
 
+    def topk_fused(self, stream=None):
+        S.spattn_topk(None, None, self.ix, self.ctx_len, self.wl.topk, S.TOPK_FUSED_INDEX,
+                      self.idx, self.count, self.ws, stream)
+
     def block_select(self, stream=None):
         S.spattn_block_select(self.q, self.k, self.ctx_len, self.wl.block_size, self.wl.top_blocks,
                               self.idx, self.count, self.ws, stream)
@@ -95,7 +103,9 @@ class HotPath:
                                  self.ws, stream)
 
     def step(self, stream=None):
-        if self.wl.H_I:
+        if self.wl.H_I and self.fused:
+            self.topk_fused(stream)
+        elif self.wl.H_I:
             self.index_scores(stream)
             self.topk(stream)
         elif self.wl.kind == "blocks":

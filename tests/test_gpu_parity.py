@@ -272,3 +272,39 @@ def test_full_size_sampled_rows(name, n):
         idx = hp.idx.cpu().numpy()
         for (b, i, j) in inp["needles"]:
             assert j in idx[b, 0, i]
+
+
+# ---------------------------------------------------------------- fused indexer + top-K
+def run_fused(wl, inp):
+    from fine_grained_top_amd.hotpath import HotPath
+    say(f"[gpu] fused {wl.name}: B={wl.B} N={wl.N} Nq={wl.Nq}")
+    hp = HotPath(wl, inp, fused=True)
+    hp.step()
+    torch.cuda.synchronize()
+    return hp
+
+
+@pytest.mark.parametrize("name", ["dsa_decode_small", "dsa_decode"])
+def test_fused_index_topk(name):
+    wl = gen.WORKLOADS[name]
+    inp = gen.generate(wl)
+    hp = run_fused(wl, inp)
+    rows = _all_rows(wl, inp)
+    res = oracle_rows(wl, inp, rows)
+    check_sets(hp, res, rows, wl)
+    check_out(hp, res, rows, 2e-3)
+
+
+def test_fused_falls_back_when_the_sample_misleads():
+    """Keys inside the pilot's sample runs are made to score zero, so the
+    sampled threshold is useless; the fused call must still be exact."""
+    wl = dataclasses.replace(gen.WORKLOADS["dsa_decode_small"], B=2, N=40000, len_range=(36000, 40000), topk=512)
+    inp = gen.generate(wl)
+    codes = inp["k_idx"]
+    pos = np.arange(wl.N)
+    inside = (pos % 2048) < 64
+    codes[:, inside, 0, :] = 0                    # +0 keys: every score in the sample is 0
+    hp = run_fused(wl, inp)
+    rows = _all_rows(wl, inp)
+    res = oracle_rows(wl, inp, rows)
+    check_sets(hp, res, rows, wl)
