@@ -1,9 +1,10 @@
 """Benchmark: selective sparse attention hot path on one MI355X.
 
-One step = indexer scores -> certified top-K -> sparse attention for one
-batch of the DSA-style decode workload (8 requests, 128K-token capacity,
-lengths U[98304, 131072], 32 query / 8 KV heads, d = 128, bf16 KV cache,
-fp8-e4m3 indexer keys, top-2048 per request and KV group). Inputs are
+One step = indexer + certified top-K (one fused call; separate calls with
+--unfused) -> sparse attention, for one batch of the DSA-style decode
+workload (8 requests, 128K-token capacity, lengths U[98304, 131072], 32 query /
+8 KV heads, d = 128, bf16 KV cache, fp8-e4m3 indexer keys, top-2048 per request
+and KV group). Other workloads are selected with --workload. Inputs are
 resident in HBM before timing; R replicas of every input tensor are cycled so
 that consecutive steps touch different memory (the working set of one step,
 ~155 MB, would otherwise sit in the 256 MB last-level cache).
@@ -24,7 +25,72 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "sparse-attn queries/sec at 128K ctx (indexer+top-K+attn); % HBM / MFMA peak"
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_PEAK_TFS = 2500.0       # dense bf16 MFMA
+F32_PEAK_TFS = 157.3         # fp32 vector
+
+
+def roofline_of(a, ms):
+    """Roofline entry for one stage from its algorithmic bytes/flops and time."""
+    if a.get("bound") == "mfma":
+        ach = a["flops"] / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_PEAK_TFS, 4), "traffic": None, "alg_flops_per_launch": a["flops"],
+                "launch_ms": round(ms, 5)}
+    ach = a["bytes"] / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "alg_bytes_per_launch": a["bytes"],
+            "launch_ms": round(ms, 5)}
+
+
+def algorithmic(wl, inp, hp, fused):
+    """Algorithmic bytes (compulsory HBM traffic) and flops of one call of each stage."""
+    import numpy as np
+    from fine_grained_top_amd import metrics
+    e = 2 if wl.dtype == "bf16" else 4
+    lens = inp["ctx_len"].astype(np.int64)
+    qkv_out = wl.B * wl.Hq * wl.Nq * wl.d * (e + 4) + wl.B * wl.Hq * wl.Nq * 4   # q in, O and LSE out
+    out = {}
+    if wl.H_I:
+        kb = {"fp8": 1, "bf16": 2, "f32": 4}[wl.idx_k_dtype]
+        pos = np.concatenate([L - wl.Nq + np.arange(wl.Nq) for L in lens])
+        cand = float(np.sum(pos + 1))                      # (row, key) pairs scored per group
+        keys_read = float(lens.sum()) * wl.G_k * wl.d_I * kb
+        idx_bytes = wl.B * wl.G_sel * wl.Nq * wl.topk * 4
+        flops_idx = 2.0 * cand * wl.H_I * wl.d_I
+        score_bytes = cand * wl.G_sel * 4
+        out["index_scores"] = {"bytes": keys_read + score_bytes, "flops": flops_idx,
+                               "bound": "hbm" if wl.Nq == 1 else "mfma"}
+        out["topk"] = {"bytes": score_bytes + idx_bytes, "rows": wl.B * wl.G_sel * wl.Nq}
+        out["index_topk_fused"] = {"bytes": keys_read + idx_bytes, "flops": flops_idx,
+                                   "rows": wl.B * wl.G_sel * wl.Nq, "bound": "hbm" if wl.Nq == 1 else "mfma"}
+        sel = np.minimum(pos + 1, wl.topk).astype(np.float64)  # |S| per row
+        gath = float(sel.sum()) * (wl.Hq // max(wl.Hq // wl.G_sel, wl.Hq // wl.Hkv)) * wl.d * e * 2
+        pairs = float(sel.sum()) * wl.Hq / wl.G_sel * wl.G_sel
+        flops_att = 4.0 * pairs * wl.d
+        out["attention"] = {"bytes": gath + qkv_out, "flops": flops_att,
+                            "bound": "hbm" if wl.Nq == 1 else "mfma"}
+    elif wl.kind == "window_global":
+        pairs = float(metrics.window_global_pairs(wl.N, wl.window, wl.n_global)) * wl.Hq * wl.B
+        kv = wl.B * wl.Hkv * wl.N * wl.d * e * 2
+        out["attention"] = {"bytes": kv + qkv_out, "flops": 4.0 * pairs * wl.d, "bound": "hbm"}
+    elif wl.kind == "blocks":
+        blk = hp.idx.cpu().numpy()                       # [B, Hq, Nq, nb]
+        p = np.arange(wl.Nq)[None, None, :]
+        ws = np.maximum(0, p - wl.window + 1)
+        valid = blk >= 0
+        lo = blk * wl.block_size
+        in_win = np.clip(np.minimum(lo + wl.block_size, p[..., None] + 1) - np.maximum(lo, ws[..., None]), 0, None)
+        size = (valid * wl.block_size).sum(-1) - (valid * in_win).sum(-1) + (p - ws + 1)
+        pairs = float(size.sum())
+        kv = wl.B * wl.Hkv * wl.N * wl.d * e * 2
+        out["attention"] = {"bytes": kv + qkv_out, "flops": 4.0 * pairs * wl.d, "bound": "mfma",
+                            "pairs": pairs}
+        nbk = wl.N // wl.block_size
+        elig = float(np.sum(np.minimum((np.arange(wl.Nq) + 1) // wl.block_size, nbk))) * wl.Hq * wl.B
+        out["block_select"] = {"bytes": wl.B * wl.Hkv * wl.N * wl.d * e + wl.B * wl.Hq * wl.Nq * wl.d * e
+                               + blk.size * 4, "flops": 2.0 * elig * wl.d, "rows": wl.B * wl.Hq * wl.Nq}
+    return out
 
 
 def log(msg):
@@ -40,6 +106,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after timing, copy a 1 GiB buffer 3 times (a known-size kernel for PMC scaling)")
     ap.add_argument("--unfused", action="store_true",
                     help="time separate indexer-scores and top-K calls instead of the fused call")
     args = ap.parse_args()
@@ -62,6 +130,7 @@ def main():
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s; uploading {args.replicas} replicas")
     fused = bool(wl.H_I) and not args.unfused
     paths = [HotPath(wl, inp, fused=fused) for _ in range(args.replicas)]
+    fused = paths[0].fused
     # share one workspace and one set of intermediate buffers, as one layer's call would
     base = paths[0]
     for hp in paths[1:]:
@@ -114,40 +183,36 @@ def main():
         ts = [evs[i][si][0].elapsed_time(evs[i][si][1]) for i in range(args.steps)]
         stage_ms[name] = float(np.mean(ts))
 
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     queries = wl.B * wl.Nq
     lens = inp["ctx_len"].astype(np.int64)
-    # algorithmic bytes per launch of each stage
-    alg = {}
-    if wl.kind == "dsa_decode":
-        kidx_bytes = int(lens.sum()) * wl.d_I * 1
-        score_bytes = int(lens.sum()) * wl.G_sel * 4
-        alg["index_scores"] = kidx_bytes + score_bytes
-        alg["topk"] = score_bytes + wl.B * wl.G_sel * wl.topk * 4
-        alg["index_topk_fused"] = kidx_bytes + wl.B * wl.G_sel * wl.topk * 4
-        alg["attention"] = wl.B * wl.Hkv * wl.topk * wl.d * 2 * 2 + wl.B * wl.Hq * wl.d * (2 + 4)
+    alg = algorithmic(wl, inp, paths[(args.steps - 1) % len(paths)], fused)
     dom = max(stage_ms, key=stage_ms.get)
     roof = None
     if dom in alg:
-        achieved = alg[dom] / (stage_ms[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "alg_bytes_per_launch": alg[dom], "launch_ms": round(stage_ms[dom], 5)}
+        roof = roofline_of(alg[dom], stage_ms[dom])
+        roof["kernel"] = dom
     per_stage = {}
     for name, ms in stage_ms.items():
         e = {"ms": round(ms, 5)}
         if name in alg:
-            gbs = alg[name] / (ms * 1e-3) / 1e9
-            e.update({"alg_bytes": alg[name], "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+            a = alg[name]
+            e["alg_bytes"] = a["bytes"]
+            e["GB_s"] = round(a["bytes"] / (ms * 1e-3) / 1e9, 1)
+            e["hbm_frac"] = round(e["GB_s"] / HBM_PEAK_GBS, 4)
+            if a.get("flops"):
+                e["TFLOP_s"] = round(a["flops"] / (ms * 1e-3) / 1e12, 3)
+                e["mfma_frac"] = round(e["TFLOP_s"] / (MFMA_PEAK_TFS if wl.dtype == "bf16" else F32_PEAK_TFS), 4)
+            if a.get("rows"):
+                e["rows_per_s"] = round(a["rows"] / (ms * 1e-3), 1)
         per_stage[name] = e
-    if "topk" in stage_ms:
-        per_stage["topk"]["rows_per_s"] = round(wl.B * wl.G_sel * wl.Nq / (stage_ms["topk"] * 1e-3), 1)
-    for name in ("index_scores", "index_topk_fused"):
-        if name in stage_ms and wl.H_I:
-            flops = 2.0 * float(lens.sum()) * wl.H_I * wl.d_I
-            per_stage[name]["TFLOP_s"] = round(flops / (stage_ms[name] * 1e-3) / 1e12, 3)
-    if "index_topk_fused" in stage_ms:
-        per_stage["index_topk_fused"]["rows_per_s"] = round(
-            wl.B * wl.G_sel * wl.Nq / (stage_ms["index_topk_fused"] * 1e-3), 1)
 
     # CPU oracle on a bounded sample (also a parity spot check of the last GPU outputs)
     cpu = None

@@ -53,6 +53,9 @@ class HotPath:
             self.idx = torch.empty(wl.B, wl.G_sel, wl.Nq, wl.topk, dtype=torch.int32, device=device)
             self.count = torch.empty(wl.B, wl.G_sel, wl.Nq, dtype=torch.int32, device=device)
             self.sel = S.selection(S.SEL_INDEX, self.idx)
+            if self.fused and S.LIB.spattn_topk_workspace(None, S.ctypes.byref(self.ix), wl.topk,
+                                                          S.TOPK_FUSED_INDEX) == S.SIZE_MAX:
+                self.fused = False          # this indexer shape has no fused kernel: separate calls
         elif wl.kind == "blocks":
             self.idx = torch.empty(wl.B, wl.Hq, wl.Nq, wl.top_blocks, dtype=torch.int32, device=device)
             self.count = torch.empty(wl.B, wl.Hq, wl.Nq, dtype=torch.int32, device=device)
@@ -64,23 +67,23 @@ class HotPath:
         self.ws = torch.empty(self.ws_bytes(), dtype=torch.uint8, device=device)
 
     def ws_bytes(self) -> int:
-        n = 0
+        return max([v for v in self._ws_queries() if v != S.SIZE_MAX] + [16])
+
+    def _ws_queries(self):
+        q = []
+        byref = S.ctypes.byref
         if self.wl.H_I:
-            n = max(n, S.LIB.spattn_index_scores_workspace(S.ctypes.byref(self.ix)))
+            q.append(S.LIB.spattn_index_scores_workspace(byref(self.ix)))
             ts = S.tensor(self.scores)
-            n = max(n, S.LIB.spattn_topk_workspace(S.ctypes.byref(ts), S.ctypes.byref(self.ix), self.wl.topk,
-                                                   S.TOPK_CERTIFIED))
+            q.append(S.LIB.spattn_topk_workspace(byref(ts), byref(self.ix), self.wl.topk, S.TOPK_CERTIFIED))
             if self.fused:
-                n = max(n, S.LIB.spattn_topk_workspace(None, S.ctypes.byref(self.ix), self.wl.topk,
-                                                       S.TOPK_FUSED_INDEX))
-        if self.wl.kind == "blocks":
-            tq, tk = S.tensor(self.q), S.tensor(self.k)
-            n = max(n, S.LIB.spattn_block_select_workspace(S.ctypes.byref(tq), S.ctypes.byref(tk),
-                                                           self.wl.block_size, self.wl.top_blocks))
+                q.append(S.LIB.spattn_topk_workspace(None, byref(self.ix), self.wl.topk, S.TOPK_FUSED_INDEX))
         tq, tk = S.tensor(self.q), S.tensor(self.k)
-        n = max(n, S.LIB.spattn_sparse_attn_fwd_workspace(S.ctypes.byref(tq), S.ctypes.byref(tk),
-                                                          S.ctypes.byref(self.sel)))
-        return max(n, 16)
+        if self.wl.kind == "blocks":
+            q.append(S.LIB.spattn_block_select_workspace(byref(tq), byref(tk), self.wl.block_size,
+                                                         self.wl.top_blocks))
+        q.append(S.LIB.spattn_sparse_attn_fwd_workspace(byref(tq), byref(tk), byref(self.sel)))
+        return q
 
     # the individual stages
     def index_scores(self, stream=None):

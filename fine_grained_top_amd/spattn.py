@@ -22,6 +22,8 @@ SCORE_DOT, SCORE_WEIGHTED_RELU = 0, 1
 SEL_DENSE, SEL_INDEX, SEL_WINDOW_GLOBAL, SEL_BLOCKS = 0, 1, 2, 3
 TOPK_CERTIFIED, TOPK_FUSED_INDEX = 1, 2
 
+SIZE_MAX = ctypes.c_size_t(-1).value
+
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "NO_DEVICE", 5: "LAUNCH"}
 
 
