@@ -452,6 +452,7 @@ hipError_t launch_attention(const AttnParams& a, hipStream_t st) {
                        (const float*)part);
     return hipGetLastError();
   }
+  if (attn_tile_ok(a)) return launch_attn_tile(a, st);
   dim3 grid(a.Nq, a.Hq, a.B);
   hipLaunchKernelGGL(attn_generic_kernel, grid, dim3(64), 0, st, a);
   return hipGetLastError();

@@ -1,0 +1,267 @@
+// Tiled sparse attention for fixed visible sets (dense causal, sliding window
+// + global tokens, selected blocks + window), bf16, d = 128.
+//
+// One workgroup = 64 query rows of one (request, head); wave w owns rows
+// 16w..16w+15. Key tiles of 64 keys are visited in increasing order: the
+// global tiles and the band of the window (WINDOW_GLOBAL), every past tile
+// (DENSE), or the union of the rows' selected blocks and windows (BLOCKS,
+// from an LDS tile bitmap). K tiles are staged row-major and V tiles
+// transposed in LDS; the next tile is prefetched into registers while the
+// current one is consumed. Per wave and tile: S^T = K Q^T on
+// v_mfma_f32_16x16x32_bf16 (lane = query row, 4 keys per 16-key subtile),
+// per-element masks from the row's visible set, online softmax in float32
+// (exp2), and O += P V with P as a bf16 hi/lo pair. In BLOCKS mode a wave
+// skips a tile no row of its own can see.
+#include "common.h"
+#include "internal.h"
+
+namespace sp {
+
+constexpr int kTQ = 64, kTK = 64;
+constexpr int kKs = 136;       // K tile row stride in 16-bit words (272 B)
+constexpr int kVs = 72;        // V^T row stride in 16-bit words (144 B)
+constexpr int kMaxBlkWords = 64;   // per-row block bitmap words (<= 2048 blocks)
+constexpr float kLog2eT = 1.4426950408889634f;
+constexpr float kLn2T = 0.6931471805599453f;
+
+struct TileSmem {
+  uint16_t ks[kTK * kKs];
+  uint16_t vt[128 * kVs];
+  uint32_t tiles[64];                    // tile bitmap (<= 2048 tiles)
+  uint32_t rowblk[kTQ * kMaxBlkWords];   // BLOCKS: per-row selected-block bitmaps
+};
+
+__global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
+  __shared__ __attribute__((aligned(16))) TileSmem sm;
+  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int qq = lane >> 4, c16 = lane & 15;
+  const int kvh = h / (a.Hq / a.Hkv);
+  const int L = min(a.ctx_len ? a.ctx_len[b] : a.ctx, a.ctx);
+  const int q0 = qt * kTQ;
+  const int pbase = L - a.Nq;                      // position of row 0
+  const int prow_first = pbase + q0;
+  const int prow_last = pbase + min(q0 + kTQ, a.Nq) - 1;
+  const int ntiles_all = (L + kTK - 1) / kTK;
+  const int nbk = a.mode == 3 ? (a.ctx + a.bs - 1) / a.bs : 0;
+  const int bwords = (nbk + 31) >> 5;
+
+  // ---- tile set of this query tile
+  for (int i = tid; i < 64; i += 256) sm.tiles[i] = 0;
+  if (a.mode == 3)
+    for (int i = tid; i < kTQ * bwords; i += 256) sm.rowblk[i] = 0;
+  __syncthreads();
+  const int last_tile = prow_last >= 0 ? min(ntiles_all - 1, prow_last / kTK) : -1;
+  if (a.mode == 0) {
+    for (int t = tid; t <= last_tile; t += 256) atomicOr(&sm.tiles[t >> 5], 1u << (t & 31));
+  } else if (a.mode == 2) {
+    const int gt = (min(a.n_global, L) + kTK - 1) / kTK;
+    const int wt = max(0, prow_first - a.window + 1) / kTK;
+    for (int t = tid; t <= last_tile; t += 256)
+      if (t < gt || t >= wt) atomicOr(&sm.tiles[t >> 5], 1u << (t & 31));
+  } else {
+    const int wt = max(0, prow_first - a.window + 1) / kTK;
+    for (int t = wt + tid; t <= last_tile; t += 256) atomicOr(&sm.tiles[t >> 5], 1u << (t & 31));
+    for (int e = tid; e < kTQ * a.K; e += 256) {
+      const int rr = e / a.K, slot = e % a.K;
+      if (q0 + rr >= a.Nq) continue;
+      const int blk = a.sel[b * a.sels[0] + h * a.sels[1] + (int64_t)(q0 + rr) * a.sels[2] + slot];
+      if (blk < 0 || blk >= nbk) continue;
+      atomicOr(&sm.rowblk[rr * bwords + (blk >> 5)], 1u << (blk & 31));
+      const int t0 = (blk * a.bs) / kTK, t1 = min(ntiles_all - 1, (blk * a.bs + a.bs - 1) / kTK);
+      for (int t = t0; t <= t1; ++t) atomicOr(&sm.tiles[t >> 5], 1u << (t & 31));
+    }
+  }
+  __syncthreads();
+
+  // ---- per-lane row state: lane column c16 = query row 16*wid + c16
+  const int rloc = 16 * wid + c16;
+  const int rq = q0 + rloc;
+  const bool rvalid = rq < a.Nq;
+  const int prow = pbase + rq;
+  const int wstart = prow - a.window + 1;
+  bf16x8 Qb[4];
+  if (rvalid) {
+    const uint16_t* qp = (const uint16_t*)a.q.p + b * a.q.s[0] + h * a.q.s[1] + (int64_t)rq * a.q.s[2] + 32 * qq;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) Qb[s] = *(const bf16x8*)(qp + 8 * s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) Qb[s] = (bf16x8){};
+  }
+  const float cs = a.scale * kLog2eT;
+  float m = -INFINITY, l = 0.f;
+  f32x4 O[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) O[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const uint16_t* kbase = (const uint16_t*)a.k.p + b * a.k.s[0] + kvh * a.k.s[1];
+  const uint16_t* vbase = (const uint16_t*)a.v.p + b * a.v.s[0] + kvh * a.v.s[1];
+
+  // next tile after t (or -1)
+  auto next_tile = [&](int t) -> int {
+    for (int w = (t + 1) >> 5; w <= (last_tile >> 5) && w < 64; ++w) {
+      uint32_t bits = sm.tiles[w];
+      if (w == ((t + 1) >> 5)) bits &= ~0u << ((t + 1) & 31);
+      if (bits) {
+        const int nt = w * 32 + __builtin_ctz(bits);
+        return nt <= last_tile ? nt : -1;
+      }
+    }
+    return -1;
+  };
+  // prefetch of one tile: chunk c = tid + 256u -> key c/16, 16-byte column c%16
+  u32x4 pk[4], pv[4];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + 256 * u;
+      int j = t * kTK + (c >> 4);
+      j = j < L ? j : L - 1;
+      pk[u] = *(const u32x4*)(kbase + (int64_t)j * a.k.s[2] + 8 * (c & 15));
+      pv[u] = *(const u32x4*)(vbase + (int64_t)j * a.v.s[2] + 8 * (c & 15));
+    }
+  };
+  int t = last_tile >= 0 ? next_tile(-1) : -1;
+  if (t >= 0) load_tile(t);
+  while (t >= 0) {
+    // stage the prefetched tile
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + 256 * u;
+      const int key = c >> 4, col = c & 15;
+      *(u32x4*)&sm.ks[key * kKs + 8 * col] = pk[u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sm.vt[(8 * col + 2 * e) * kVs + key] = (uint16_t)(pv[u][e] & 0xFFFFu);
+        sm.vt[(8 * col + 2 * e + 1) * kVs + key] = (uint16_t)(pv[u][e] >> 16);
+      }
+    }
+    __syncthreads();
+    const int tn = next_tile(t);
+    if (tn >= 0) load_tile(tn);
+
+    const int j0 = t * kTK;
+    // does any row of this wave see this tile?
+    bool see = rvalid && prow >= j0;
+    if (see && a.mode == 2) see = (j0 + kTK - 1 >= wstart) || (j0 < a.n_global);
+    if (see && a.mode == 3) {
+      bool any = j0 + kTK - 1 >= wstart;
+      if (!any) {
+        const int b0 = j0 / a.bs, b1 = min(nbk - 1, (j0 + kTK - 1) / a.bs);
+        for (int bb = b0; bb <= b1 && !any; ++bb)
+          any = (sm.rowblk[rloc * bwords + (bb >> 5)] >> (bb & 31)) & 1u;
+      }
+      see = any;
+    }
+    if (__ballot(see)) {
+      // S^T for the 4 subtiles of 16 keys: lane holds row c16, keys 16*st + 4*qq + v
+      f32x4 S[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        S[st] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        const uint16_t* kr = &sm.ks[(16 * st + c16) * kKs + 32 * qq];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          S[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(kr + 8 * s), Qb[s], S[st], 0, 0, 0);
+      }
+      // masks: lane's keys j = j0 + 16*st + 4*qq + v for its row (column c16)
+      float z[16];
+      float tm = -INFINITY;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int j = j0 + 16 * st + 4 * qq + v;
+          bool vis = rvalid && j <= prow;
+          if (vis && a.mode == 2) vis = j >= wstart || j < a.n_global;
+          if (vis && a.mode == 3) {
+            const int bb = j / a.bs;
+            vis = j >= wstart || ((sm.rowblk[rloc * bwords + (bb >> 5)] >> (bb & 31)) & 1u);
+          }
+          const float zz = vis ? S[st][v] * cs : -INFINITY;
+          z[4 * st + v] = zz;
+          tm = fmaxf(tm, zz);
+        }
+      tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
+      tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+      const float mn = fmaxf(m, tm);
+      float alpha = 1.f, ps = 0.f;
+      if (mn > -INFINITY) {
+        alpha = exp2f(m - mn);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          z[i] = exp2f(z[i] - mn);
+          ps += z[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z[i] = 0.f;
+      }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      l = l * alpha + ps;
+      m = mn;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float av = __shfl(alpha, 4 * qq + v, 64);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) O[nt][v] *= av;
+      }
+      // O += P V, two halves of 32 keys; k = 8*qq + v <-> keys 4*qq+v (v<4), 16+4*qq+(v-4)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        u32x4 Ahi, Alo;
+#pragma unroll
+        for (int v2 = 0; v2 < 4; ++v2) {
+          const int i0 = (v2 < 2) ? (8 * hf + 2 * v2) : (8 * hf + 4 + 2 * (v2 - 2));
+          const float x0 = z[i0], x1 = z[i0 + 1];
+          const uint32_t h0b = f32_to_bf16_rne(x0), h1b = f32_to_bf16_rne(x1);
+          Ahi[v2] = h0b | (h1b << 16);
+          Alo[v2] = f32_to_bf16_rne(x0 - bf16_to_f32(h0b)) | (f32_to_bf16_rne(x1 - bf16_to_f32(h1b)) << 16);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const uint16_t* vr = &sm.vt[(16 * nt + c16) * kVs + 32 * hf + 4 * qq];
+          const u32x2 lo4 = *(const u32x2*)vr;          // keys 32hf + 4qq .. +3
+          const u32x2 hi4 = *(const u32x2*)(vr + 16);   // keys 32hf + 16 + 4qq .. +3
+          const u32x4 Bv = (u32x4){lo4[0], lo4[1], hi4[0], hi4[1]};
+          O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&Ahi, *(const bf16x8*)&Bv, O[nt], 0, 0, 0);
+          O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&Alo, *(const bf16x8*)&Bv, O[nt], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+    t = tn;
+  }
+
+  // ---- normalize and write: lane holds dims 16*nt + c16 of rows 4*qq + v (of this wave)
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int rr = 16 * wid + 4 * qq + v;
+    const float lr = __shfl(l, 4 * qq + v, 64);
+    const float mr = __shfl(m, 4 * qq + v, 64);
+    if (q0 + rr >= a.Nq) continue;
+    float* o = a.o + b * a.os[0] + h * a.os[1] + (int64_t)(q0 + rr) * a.os[2];
+    const float inv = lr > 0.f ? 1.f / lr : 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) o[16 * nt + c16] = O[nt][v] * inv;
+    if (a.lse && c16 == 0)
+      a.lse[((int64_t)b * a.Hq + h) * a.Nq + q0 + rr] = lr > 0.f ? (mr + log2f(lr)) * kLn2T : -INFINITY;
+  }
+}
+
+bool attn_tile_ok(const AttnParams& a) {
+  if (a.q.dt != DT_BF16 || a.d != 128 || a.mode == 1) return false;
+  if ((a.ctx + kTK - 1) / kTK > 2048) return false;
+  if (a.mode == 3 && ((a.ctx + a.bs - 1) / a.bs > 32 * kMaxBlkWords)) return false;
+  return true;
+}
+
+hipError_t launch_attn_tile(const AttnParams& a, hipStream_t st) {
+  dim3 grid((a.Nq + kTQ - 1) / kTQ, a.Hq, a.B);
+  hipLaunchKernelGGL(attn_tile_kernel, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace sp

@@ -118,9 +118,17 @@ __global__ __launch_bounds__(kBsThreads) void block_select_kernel(BlockSelectPar
   const float inv = ldexpf(1.0f, -p.log2bs);
   float amax = 0.f;
   for (int beta = tid; beta < ne; beta += T) {
-    const float* kr = kb + (int64_t)beta * p.d;
+    const f32x4* kr = (const f32x4*)(kb + (int64_t)beta * p.d);   // rows of d floats, 16-byte aligned
     float s = 0.f;
-    for (int c = 0; c < p.d; ++c) s = fmaf(qs[c], kr[c], s);
+    for (int c4 = 0; c4 < p.d / 4; c4 += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = kr[c4 + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = fmaf(qs[4 * (c4 + u) + e], v[u][e], s);
+    }
     keys[beta] = f32_order_key(s * inv);
     amax = fmaxf(amax, ka[beta]);
   }

@@ -37,18 +37,28 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
   if (j0 >= L) return;
   const int M = p.Nq * p.H_I;
   const int hshift = __builtin_ctz(p.H_I);
-  __shared__ uint32_t lcount[128];
-  if (FILTER) {
-    for (int i = threadIdx.x; i < 128; i += 256) lcount[i] = 0;
-    __syncthreads();
+  const int mbase = 128 * blockIdx.z;                 // first (row, head) slot of this workgroup
+  // causal skip: no row of this slot block sees any key of the chunk
+  {
+    const int rmax = min(p.Nq - 1, (mbase + 32 * NMB - 1) >> hshift);
+    if (j0 > L - p.Nq + rmax) return;
   }
+  __shared__ uint32_t lcount[128];
+  __shared__ float wsl[128];
+  for (int i = threadIdx.x; i < 128; i += 256) {
+    if (FILTER) lcount[i] = 0;
+    float wv = 0.f;
+    const int ms = mbase + i;
+    if (RELU && ms < M) wv = p.w[b * p.ws_[0] + (ms >> hshift) * p.ws_[1] + (ms & (p.H_I - 1)) * p.ws_[2]];
+    wsl[i] = wv;
+  }
+  __syncthreads();
 
-  // A operands: query slot m = 32*mb + col, dims 32*half + 8*s + v (s = k-step)
+  // A operands: query slot m = mbase + 32*mb + col, dims 32*half + 8*s + v (s = k-step)
   bf16x8 A[NMB][4];
-  float W[NMB][16];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
-    const int m = 32 * mb + col;
+    const int m = mbase + 32 * mb + col;
     if (m < M) {
       const int r = m >> hshift, h = m & (p.H_I - 1);
       const uint16_t* qp = (const uint16_t*)p.q.p + b * p.q.s[0] + r * p.q.s[1] + h * p.q.s[2] + 32 * half;
@@ -57,16 +67,6 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
     } else {
 #pragma unroll
       for (int s = 0; s < 4; ++s) A[mb][s] = (bf16x8){};
-    }
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int ms = 32 * mb + 8 * (v >> 2) + 4 * half + (v & 3);
-      float wv = 0.f;
-      if (RELU && ms < M) {
-        const int r = ms >> hshift, h = ms & (p.H_I - 1);
-        wv = p.w[b * p.ws_[0] + r * p.ws_[1] + h * p.ws_[2]];
-      }
-      W[mb][v] = wv;
     }
   }
 
@@ -129,10 +129,11 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
 #pragma unroll
         for (int t = 0; t < HPG; ++t) {
           const int v = gi * HPG + t;
-          sc = RELU ? fmaf(W[mb][v], fmaxf(acc[v], 0.f), sc) : acc[v];
+          const float wv = RELU ? wsl[32 * mb + 8 * (v >> 2) + 4 * half + (v & 3)] : 0.f;
+          sc = RELU ? fmaf(wv, fmaxf(acc[v], 0.f), sc) : acc[v];
         }
         const int v0 = gi * HPG;
-        const int m0 = 32 * mb + 8 * (v0 >> 2) + 4 * half + (v0 & 3);
+        const int m0 = mbase + 32 * mb + 8 * (v0 >> 2) + 4 * half + (v0 & 3);
         if (m0 < M) {
           const int r = m0 >> hshift, g = (m0 & (p.H_I - 1)) / HPG;
           if (j <= L - p.Nq + r) {
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
             } else {
               const int row = (b * p.G_sel + g) * p.Nq + r;
               if (sc >= p.tau[row]) {
-                const int lrow = g * p.Nq + r;
+                const int lrow = g * p.Nq + r;   // fused path: all slots in one block
                 const uint32_t slot = atomicAdd(&lcount[lrow], 1u);
                 if (slot < (uint32_t)p.cap) {
                   const int64_t o = ((int64_t)row * p.nchunk + blockIdx.x) * p.cap + slot;
@@ -265,7 +266,7 @@ size_t indexer_ws_bytes(int B, int G_k, int ctx) {
 
 template <int KT, int NMB, int HPG, bool RELU, bool FILTER>
 static void launch_mfma(const IndexerParams& p, hipStream_t st) {
-  dim3 grid((p.ctx + kMfmaChunk - 1) / kMfmaChunk, p.B);
+  dim3 grid((p.ctx + kMfmaChunk - 1) / kMfmaChunk, p.B, (p.Nq * p.H_I + 127) / 128);
   hipLaunchKernelGGL((idx_mfma64_kernel<KT, NMB, HPG, RELU, FILTER>), grid, dim3(256), 0, st, p);
 }
 
@@ -285,11 +286,13 @@ static void dispatch_nmb(const IndexerParams& p, hipStream_t st) {
   return dispatch_hpg<KT, 4, FILTER>(p, st);
 }
 
+// MFMA path: d_I = 64, bf16 queries, bf16/fp8 keys shared by every group,
+// <= 4 heads per group, power-of-two H_I <= 128 (a slot block never splits a row)
 static bool mfma_ok(const IndexerParams& p) {
   const bool pow2 = p.H_I > 0 && (p.H_I & (p.H_I - 1)) == 0;
   return p.d_I == 64 && p.q.dt == DT_BF16 && (p.k.dt == DT_BF16 || p.k.dt == DT_FP8) &&
-         p.G_k == 1 && (p.hpg == 1 || p.hpg == 2 || p.hpg == 4) && p.Nq * p.H_I <= 128 && pow2 &&
-         p.H_I <= 32 * 4;
+         p.G_k == 1 && (p.hpg == 1 || p.hpg == 2 || p.hpg == 4) && pow2 && p.H_I <= 128 &&
+         (int64_t)p.Nq * p.H_I <= (int64_t)128 * 65535;
 }
 
 hipError_t launch_index_scores(const IndexerParams& p0, hipStream_t st) {
@@ -312,7 +315,7 @@ hipError_t launch_index_scores(const IndexerParams& p0, hipStream_t st) {
   return hipGetLastError();
 }
 
-bool index_filter_ok(const IndexerParams& p) { return mfma_ok(p); }
+bool index_filter_ok(const IndexerParams& p) { return mfma_ok(p) && p.Nq * p.H_I <= 128; }
 
 hipError_t launch_index_filter(const IndexerParams& p0, hipStream_t st) {
   IndexerParams p = p0;

@@ -93,5 +93,7 @@ struct AttnParams {
 };
 size_t attn_ws_bytes(const AttnParams& p);
 hipError_t launch_attention(const AttnParams& p, hipStream_t st);
+bool attn_tile_ok(const AttnParams& p);
+hipError_t launch_attn_tile(const AttnParams& p, hipStream_t st);
 
 }  // namespace sp

@@ -208,6 +208,188 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(TopkParams p) {
   if (p.count && threadIdx.x == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = p.K;
 }
 
+// Visit s[0..n) as (j, order key) with U independent loads in flight per thread.
+template <int T, int U, typename F>
+SP_DEV void for_each_key(const float* s, int n, F f) {
+  for (int base = 0; base < n; base += T * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = base + u * T + (int)threadIdx.x;
+      v[u] = j < n ? s[j] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = base + u * T + (int)threadIdx.x;
+      if (j < n) f(j, f32_order_key(v[u]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- two-pass single-workgroup schedule
+// Rows of up to 65536 keys: pass 1 builds a 12-bit histogram in LDS and finds
+// the bin holding the K-th largest key; pass 2 sets a bitmap bit for every key
+// above that bin (plus the certification margin) and lists the keys inside it;
+// the short list is resolved exactly and the bitmap is written out in order.
+constexpr int kR2Words = 2048;      // bitmap words (65536 keys)
+constexpr int kR2Cand = 4096;       // candidates kept in LDS
+
+struct R2Smem {
+  RowSmem row;
+  uint32_t ck[kR2Cand];
+  uint32_t cj[kR2Cand];
+  uint32_t bm[kR2Words];
+  uint32_t misc[4];
+};
+
+// Resolve the candidate list (keys ck, indices cj, n_cand of them) that holds
+// the remaining R slots; sets the selected bits in bm. Returns false when the
+// band is too wide for the short list (caller redoes the row).
+template <int T>
+SP_DEV bool resolve_candidates(const TopkParams& p, RowCtx& c, RowSmem& rs, uint32_t* ck, uint32_t* cj,
+                               uint32_t* bm, uint32_t n_cand, uint32_t R, uint32_t wlo, uint32_t whi) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int bits = 32 - __builtin_clz((whi - wlo) | 1u);
+  uint32_t t, above;
+  radix_select<T>((int)n_cand, R, [&](int i, uint32_t& k) { k = ck[i]; return true; }, rs.hist, rs.sc, t, above,
+                  wlo, bits);
+  const float tf = order_key_f32(t);
+  uint32_t klo, khi;
+  band_limits(p, c, tf, tf, tf, klo, khi);
+  uint32_t n_in = 0;
+  if (tid == 0) rs.run[0] = 0;
+  __syncthreads();
+  for (uint32_t i = tid; i < n_cand; i += T) {
+    const uint32_t ks = ck[i];
+    if (ks > khi) {
+      atomicOr(&bm[cj[i] >> 5], 1u << (cj[i] & 31));
+      ++n_in;
+    } else if (ks >= klo) {
+      const uint32_t slot = atomicAdd(&rs.run[0], 1u);
+      if (slot < (uint32_t)kBandCap) {
+        rs.band_j[slot] = cj[i];
+        rs.band_k[slot] = ks;
+      }
+    }
+  }
+  uint32_t tot_in;
+  block_scan_sum<T>(n_in, rs.sc, tot_in);
+  const uint32_t nb = rs.run[0];
+  if (nb > (uint32_t)kBandCap) return false;
+  const uint32_t R2 = R - tot_in;
+  if (p.certified) {
+    for (uint32_t e = tid >> 6; e < nb; e += T / 64) {
+      const float key = wave_exact_key(c.ir, rs.band_j[e]);
+      if (lane == 0) rs.band_k[e] = f32_order_key(key);
+    }
+    __syncthreads();
+  }
+  for (uint32_t e = tid; e < nb; e += T) {
+    const uint32_t ke = rs.band_k[e], je = rs.band_j[e];
+    uint32_t rank = 0;
+    for (uint32_t f = 0; f < nb; ++f) {
+      const uint32_t kf = rs.band_k[f];
+      rank += (kf > ke || (kf == ke && rs.band_j[f] < je)) ? 1u : 0u;
+    }
+    if (rank < R2) atomicOr(&bm[je >> 5], 1u << (je & 31));
+  }
+  __syncthreads();
+  return true;
+}
+
+// Write the set bits of bm (nwords words) as ascending indices, pad with -1.
+template <int T>
+SP_DEV void emit_bitmap(const TopkParams& p, const RowCtx& c, RowSmem& rs, const uint32_t* bm, int nwords) {
+  const int tid = threadIdx.x;
+  const int perw = (nwords + T - 1) / T;
+  const int w0 = tid * perw, w1 = min(nwords, w0 + perw);
+  uint32_t cnt = 0;
+  for (int i = w0; i < w1; ++i) cnt += __popc(bm[i]);
+  uint32_t total;
+  uint32_t pos = block_scan_sum<T>(cnt, rs.sc, total);
+  for (int i = w0; i < w1; ++i) {
+    uint32_t m = bm[i];
+    while (m) {
+      const int bit = __ffs(m) - 1;
+      m &= m - 1;
+      if (pos < (uint32_t)p.K) c.out[pos] = i * 32 + bit;
+      ++pos;
+    }
+  }
+  for (int i = (int)total + tid; i < p.K; i += T) c.out[i] = -1;
+  if (p.count && tid == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = (int)min(total, (uint32_t)p.K);
+}
+
+__global__ __launch_bounds__(kTkThreads) void topk_row2_kernel(TopkParams p) {
+  constexpr int T = kTkThreads;
+  __shared__ R2Smem sm;
+  RowCtx c = row_ctx(p, blockIdx.x);
+  const int tid = threadIdx.x;
+  if (c.n <= p.K) return write_all(p, c, T);
+  const int n = c.n;
+  // pass 1: histogram of the top 12 bits
+  for (int i = tid; i < 4096; i += T) sm.row.hist[i] = 0;
+  const int nwords = (n + 31) >> 5;
+  for (int i = tid; i < nwords; i += T) sm.bm[i] = 0;
+  if (tid == 0) sm.misc[0] = 0;
+  __syncthreads();
+  for_each_key<T, 16>(c.s, n, [&](int j, uint32_t ks) { atomicAdd(&sm.row.hist[ks >> 20], 1u); });
+  __syncthreads();
+  uint32_t bin;
+  {
+    constexpr int per = 4096 / T;
+    const int lo = tid * per;
+    uint32_t mine = 0;
+    for (int q = 0; q < per; ++q) mine += sm.row.hist[lo + q];
+    uint32_t tot;
+    const uint32_t below = block_scan_sum<T>(mine, sm.row.sc, tot);
+    uint32_t cum = tot - below - mine;
+    const uint32_t K = (uint32_t)p.K;
+    if (cum < K && cum + mine >= K) {
+      for (int q = per - 1; q >= 0; --q) {
+        if (cum + sm.row.hist[lo + q] >= K) {
+          sm.misc[1] = (uint32_t)(lo + q);
+          break;
+        }
+        cum += sm.row.hist[lo + q];
+      }
+    }
+    __syncthreads();
+    bin = sm.misc[1];
+  }
+  uint32_t wlo, whi;
+  {
+    const float lo_b = order_key_f32(bin << 20), hi_b = order_key_f32((bin << 20) | 0xFFFFFu);
+    band_limits(p, c, 0.f, lo_b, hi_b, wlo, whi);
+  }
+  // pass 2: bitmap of keys above the window, list of keys inside it
+  uint32_t n_above = 0;
+  for_each_key<T, 16>(c.s, n, [&](int j, uint32_t ks) {
+    if (ks > whi) {
+      atomicOr(&sm.bm[j >> 5], 1u << (j & 31));
+      ++n_above;
+    } else if (ks >= wlo) {
+      const uint32_t slot = atomicAdd(&sm.misc[0], 1u);
+      if (slot < (uint32_t)kR2Cand) {
+        sm.ck[slot] = ks;
+        sm.cj[slot] = j;
+      }
+    }
+  });
+  uint32_t tot_above;
+  block_scan_sum<T>(n_above, sm.row.sc, tot_above);
+  const uint32_t n_cand = sm.misc[0];
+  bool ok = n_cand <= (uint32_t)kR2Cand;
+  if (ok) ok = resolve_candidates<T>(p, c, sm.row, sm.ck, sm.cj, sm.bm, n_cand, (uint32_t)p.K - tot_above, wlo, whi);
+  if (!ok) {   // too many keys near the threshold: the ordered single-pass routine
+    __syncthreads();
+    row_topk_single<T>(p, c, sm.row, [&](int i) { return c.s[i]; });
+    if (p.count && tid == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = p.K;
+    return;
+  }
+  emit_bitmap<T>(p, c, sm.row, sm.bm, nwords);
+}
+
 // ---------------------------------------------------------------- multi-workgroup schedule
 // Workgroups of one row communicate only across kernel boundaries (no
 // device-scope fences or returning atomics inside a kernel): histogram
@@ -239,7 +421,7 @@ __global__ __launch_bounds__(kMtThreads) void mt_hist_kernel(TopkParams p, MtWs 
   if (c.n <= p.K || j0 >= j1) return;
   for (int i = tid; i < 4096; i += kMtThreads) h[i] = 0;
   __syncthreads();
-  for (int j = j0 + tid; j < j1; j += kMtThreads) atomicAdd(&h[f32_order_key(c.s[j]) >> 20], 1u);
+  for_each_key<kMtThreads, 16>(c.s + j0, j1 - j0, [&](int, uint32_t ks) { atomicAdd(&h[ks >> 20], 1u); });
   __syncthreads();
   uint32_t* gh = w.hist + (int64_t)row * 4096;
   for (int i = tid; i < 4096; i += kMtThreads)
@@ -805,7 +987,10 @@ size_t topk_ws_bytes(const TopkParams& p) {
 hipError_t launch_topk(const TopkParams& p, hipStream_t st) {
   const int rows = p.B * p.G * p.Nq;
   if (!use_multi(p)) {
-    hipLaunchKernelGGL(topk_row_kernel, dim3(rows), dim3(kTkThreads), 0, st, p);
+    if (p.ctx <= 32 * kR2Words)
+      hipLaunchKernelGGL(topk_row2_kernel, dim3(rows), dim3(kTkThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL(topk_row_kernel, dim3(rows), dim3(kTkThreads), 0, st, p);
     return hipGetLastError();
   }
   MtWs w;

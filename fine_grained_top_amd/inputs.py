@@ -232,6 +232,7 @@ DECODE = _add(Workload("dsa_decode", "dsa_decode", B=8, Hq=32, Hkv=8, N=131072, 
 _add(dataclasses.replace(TINY, name="tiny_topk_f32_small", N=300, Nq=300, needles=3))
 _add(dataclasses.replace(WINDOW, name="window_global_small", Hq=2, Hkv=2, N=1000,
                          Nq=1000, window=96, n_global=5))
+_add(Workload("dense_small", "dense", B=2, Hq=4, Hkv=2, N=700, Nq=700, d=128, dtype="bf16", seed=6))
 _add(dataclasses.replace(BLOCKS, name="block_sparse_small", Hq=2, Hkv=2, N=1500,
                          Nq=1500, top_blocks=4, window=100))
 _add(dataclasses.replace(PREFILL, name="dsa_prefill_small", Hq=16, N=1200, Nq=1200,

@@ -308,3 +308,38 @@ def test_fused_falls_back_when_the_sample_misleads():
     rows = _all_rows(wl, inp)
     res = oracle_rows(wl, inp, rows)
     check_sets(hp, res, rows, wl)
+
+
+# ---------------------------------------------------------------- modes agree
+def test_dense_mode_small():
+    wl = gen.WORKLOADS["dense_small"]
+    inp = gen.generate(wl)
+    hp = run(wl, inp)
+    rows = _all_rows(wl, inp)
+    res = oracle_rows(wl, inp, rows)
+    check_out(hp, res, rows, 2e-3)
+
+
+def test_index_mode_equals_window_global_mode():
+    """Index mode fed the expanded window/global lists reproduces the
+    window/global mode ('A Guide to Sparse Attention', index-based vs fixed
+    patterns): the two kernels agree to float32 rounding."""
+    import oracle as orc
+    sp = S()
+    wl = gen.WORKLOADS["window_global_small"]
+    inp = gen.generate(wl)
+    hp = run(wl, inp)                                   # window/global mode
+    o_pattern = hp.o.clone()
+    width = wl.window + wl.n_global
+    lists = np.full((wl.B, 1, wl.Nq, width), -1, np.int32)
+    for r in range(wl.Nq):
+        p = wl.N - wl.Nq + r
+        sset = sorted(set(range(max(0, p - wl.window + 1), p + 1)) | set(range(min(wl.n_global, p + 1))))
+        lists[0, 0, r, : len(sset)] = sset
+    idx = torch.from_numpy(lists).cuda()
+    o = torch.empty_like(hp.o)
+    sp.spattn_sparse_attn_fwd(hp.q, hp.k, hp.v, hp.ctx_len, 0.0, sp.selection(sp.SEL_INDEX, idx), o)
+    torch.cuda.synchronize()
+    diff = float((o - o_pattern).abs().max())
+    say(f"  index vs pattern max diff {diff:.3e}")
+    assert diff <= 2e-3
