@@ -2,22 +2,20 @@
 //
 //  pool:  ksum[b,hk,beta,c] = sum_{t<bs} k[b,hk,bs*beta+t,c]   (float32)
 //         amax[b,hk,beta]   = max_c sum_t |k[..]|               (error-bound input)
-//  select (one workgroup per (b, h, r)): the eligible blocks are the complete
-//         past ones; score~(beta) = (q . ksum[beta]) / bs in float32; the
-//         nb-th largest score t and a rigorous bound eps give the band
-//         |score~ - t| <= 2 eps whose members are rescored exactly (the
-//         float32 nearest to the exact mean of q.k over the block) by one
-//         wave each; the best blocks by (exact key desc, block asc) are kept
-//         and written in ascending block order.
+//         ksum64, the same sums in float64 with an exactness flag per block
+//  select: the eligible blocks are the complete past ones; score~(beta) =
+//         (q . ksum[beta]) / bs in float32; the nb-th largest score t and a
+//         rigorous bound eps give the band |score~ - t| <= 2 eps whose members
+//         are rescored exactly (the float32 nearest to the exact mean of q.k
+//         over the block); the best blocks by (exact key desc, block asc) are
+//         kept and written in ascending block order.
 #include "common.h"
 #include "exact.h"
 #include "internal.h"
-#include "rowselect.h"
 
 namespace sp {
 
 constexpr int kBsThreads = 256;
-constexpr int kMaxBlocks = 2048;
 
 __global__ __launch_bounds__(128) void pool_kernel(BlockSelectParams p) {
   const int nbk = p.ctx / p.bs;
@@ -26,6 +24,8 @@ __global__ __launch_bounds__(128) void pool_kernel(BlockSelectParams p) {
   const int b = blockIdx.x / (nbk * p.Hkv);
   const int c = threadIdx.x;
   float s = 0.f, sa = 0.f;
+  double s64 = 0.0;
+  bool exact = true;
   if (c < p.d) {
     const int64_t base = b * p.k.s[0] + hk * p.k.s[1] + (int64_t)beta * p.bs * p.k.s[2] + c;
     for (int t = 0; t < p.bs; ++t) {
@@ -33,14 +33,31 @@ __global__ __launch_bounds__(128) void pool_kernel(BlockSelectParams p) {
                                         : bf16_to_f32(((const uint16_t*)p.k.p)[base + t * p.k.s[2]]);
       s += x;
       sa += fabsf(x);
+      // error-free transformation (TwoSum): the float64 sum is exact while every error term is 0
+      const double xs = (double)x, sn = s64 + xs;
+      const double bb = sn - s64;
+      const double err = (s64 - (sn - bb)) + (xs - bb);
+      exact &= err == 0.0;
+      s64 = sn;
     }
-    p.kbar[(((int64_t)b * p.Hkv + hk) * nbk + beta) * p.d + c] = s;
+    const int64_t o = (((int64_t)b * p.Hkv + hk) * nbk + beta) * p.d + c;
+    p.kbar[o] = s;
+    p.kbar64[o] = s64;
   }
   __shared__ float red[2];
+  __shared__ int ex[2];
   float m = wave_max(c < p.d ? sa : 0.f);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  const bool allx = __all(exact);
+  if ((threadIdx.x & 63) == 0) {
+    red[threadIdx.x >> 6] = m;
+    ex[threadIdx.x >> 6] = allx ? 1 : 0;
+  }
   __syncthreads();
-  if (threadIdx.x == 0) p.kabs[((int64_t)b * p.Hkv + hk) * nbk + beta] = fmaxf(red[0], red[1]);
+  if (threadIdx.x == 0) {
+    const int64_t ob = ((int64_t)b * p.Hkv + hk) * nbk + beta;
+    p.kabs[ob] = fmaxf(red[0], red[1]);
+    p.kexact[ob] = (ex[0] && ex[1]) ? 1u : 0u;
+  }
 }
 
 // exact block key computed by one wave: float64 partial sums over the lanes,
@@ -70,152 +87,224 @@ SP_DEV float wave_block_key(const BlockSelectParams& p, const void* qrow, const 
   return __shfl(slow, 0, 64);
 }
 
-__global__ __launch_bounds__(kBsThreads) void block_select_kernel(BlockSelectParams p) {
-  constexpr int T = kBsThreads;
-  __shared__ uint32_t keys[kMaxBlocks];
-  __shared__ uint32_t hist[4096];
-  __shared__ uint32_t band_b[kMaxBlocks];
-  __shared__ uint32_t band_k[kMaxBlocks];
-  __shared__ float qs[128];
-  __shared__ uint32_t sc[16];
-  __shared__ uint32_t run[4];
-  __shared__ float fred[8];
+// The same key from the block's exact float64 key sums: (1/bs) * q . ksum,
+// d products per candidate instead of bs * d; certified, else the full sum.
+SP_DEV float wave_block_key_sums(const BlockSelectParams& p, const void* qrow, const double* ks64, bool exact,
+                                 const void* kblock) {
+  if (exact) {
+    const int lane = threadIdx.x & 63;
+    double y = 0.0, A = 0.0;
+    for (int c = lane; c < p.d; c += 64) {
+      const double v = load_f64(qrow, p.q.dt, c) * ks64[c];
+      y += v;
+      A += fabs(v);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      y += __shfl_xor(y, o, 64);
+      A += __shfl_xor(A, o, 64);
+    }
+    const double g52 = 2.220446049250313e-16;
+    const double e = 2.0 * (p.d + 72) * g52 * A + 1e-300;
+    float key;
+    if (certify(ldexp(y, -p.log2bs), ldexp(e, -p.log2bs), key)) return key;
+  }
+  return wave_block_key(p, qrow, kblock);
+}
 
-  const int row = blockIdx.x;
-  const int r = row % p.Nq;
-  const int h = (row / p.Nq) % p.Hq;
-  const int b = row / (p.Nq * p.Hq);
+// Select, one workgroup per tile of RB consecutive query rows of one (b, h):
+//  phase 1: score~[rr][beta] = (q_rr . ksum[beta]) / bs for every block any row
+//           of the tile may see; each thread owns one block and reuses its key
+//           sum across the RB rows (q broadcast from LDS);
+//  phase 2: one wave per row: the nb-th largest score (bisection over the
+//           order key, counts by ballot), the band, exact keys of the band,
+//           the R best of the band, ordered output.
+template <int KPL>
+__global__ __launch_bounds__(kBsThreads) void block_select_kernel(BlockSelectParams p, int ntile) {
+  constexpr int RB = 128 / KPL;   // rows per tile: 16, 8, 4 for up to 512, 1024, 2048 blocks
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int nbk = p.ctx / p.bs;
+  f32x4* qs = (f32x4*)smem;                                   // [RB][d/4]
+  uint32_t* sk = (uint32_t*)(smem + RB * p.d * 4);            // [RB][nbk]
+  __shared__ float qn[RB];
+  __shared__ float fred[4];
+
+  // blockIdx -> tile: a contiguous range of tiles per XCD (dispatch round-robins
+  // workgroups over the 8 XCDs), so one XCD's L2 holds few heads' key sums
+  const int nwg = gridDim.x;
+  int wg = blockIdx.x;
+  if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
+  const int tile = wg % ntile;
+  const int h = (wg / ntile) % p.Hq;
+  const int b = wg / (ntile * p.Hq);
+  const int r0 = tile * RB;
+  const int nrows = min(RB, p.Nq - r0);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int hk = h / (p.Hq / p.Hkv);
   const int L = min(p.ctx_len ? p.ctx_len[b] : p.ctx, p.ctx);
-  const int pos = L - p.Nq + r;
-  const int nbk = p.ctx / p.bs;
-  const int ne = pos >= 0 ? min((pos + 1) / p.bs, nbk) : 0;
+  auto ne_of = [&](int rr) {
+    const int pos = L - p.Nq + r0 + rr;
+    return pos >= 0 ? min((pos + 1) / p.bs, nbk) : 0;
+  };
+  const int neMax = ne_of(nrows - 1);
   const int nb = p.nb;
-  int32_t* out = p.out + b * p.os[0] + h * p.os[1] + r * p.os[2];
-
-  if (ne <= nb) {
-    for (int i = tid; i < nb; i += T) out[i] = i < ne ? i : -1;
-    if (p.count && tid == 0) p.count[((int64_t)b * p.Hq + h) * p.Nq + r] = ne;
-    return;
-  }
   const int esz = p.q.dt == DT_F32 ? 4 : 2;
-  const char* qrow = (const char*)p.q.p + (b * p.q.s[0] + h * p.q.s[1] + r * p.q.s[2]) * esz;
-  float qa = 0.f;
-  for (int c = tid; c < p.d; c += T) {
-    const float x = p.q.dt == DT_F32 ? ((const float*)qrow)[c] : bf16_to_f32(((const uint16_t*)qrow)[c]);
-    qs[c] = x;
-    qa += fabsf(x);
-  }
-  qa = wave_sum(qa);
-  if (lane == 0) fred[wid] = qa;
-  __syncthreads();
-  const float qnorm1 = fred[0] + fred[1] + fred[2] + fred[3];
-  __syncthreads();
+  const int d4 = p.d >> 2;
 
-  const float* kb = p.kbar + ((int64_t)b * p.Hkv + hk) * nbk * p.d;
-  const float* ka = p.kabs + ((int64_t)b * p.Hkv + hk) * nbk;
-  const float inv = ldexpf(1.0f, -p.log2bs);
-  float amax = 0.f;
-  for (int beta = tid; beta < ne; beta += T) {
-    const f32x4* kr = (const f32x4*)(kb + (int64_t)beta * p.d);   // rows of d floats, 16-byte aligned
-    float s = 0.f;
-    for (int c4 = 0; c4 < p.d / 4; c4 += 8) {
-      f32x4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = kr[c4 + u];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s = fmaf(qs[4 * (c4 + u) + e], v[u][e], s);
+  if (neMax > nb) {
+    // q rows of the tile -> LDS, with their 1-norms
+    for (int rr = wid; rr < RB; rr += 4) {
+      const char* qrow = (const char*)p.q.p + (b * p.q.s[0] + h * p.q.s[1] + (int64_t)(r0 + rr) * p.q.s[2]) * esz;
+      float a = 0.f;
+      for (int c = lane; c < p.d; c += 64) {
+        float x = 0.f;
+        if (rr < nrows)
+          x = p.q.dt == DT_F32 ? ((const float*)qrow)[c] : bf16_to_f32(((const uint16_t*)qrow)[c]);
+        ((float*)qs)[rr * p.d + c] = x;
+        a += fabsf(x);
+      }
+      a = wave_sum(a);
+      if (lane == 0) qn[rr] = a;
     }
-    keys[beta] = f32_order_key(s * inv);
-    amax = fmaxf(amax, ka[beta]);
-  }
-  amax = wave_max(amax);
-  if (lane == 0) fred[wid] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(fred[0], fred[1]), fmaxf(fred[2], fred[3]));
-
-  uint32_t t, above;
-  radix_select<T>(ne, (uint32_t)nb, [&](int i, uint32_t& k) { k = keys[i]; return true; }, hist, sc, t,
-                  above);
-  // rigorous bound on |score~ - key|
-  const double u = 1.0 / 8388608.0;
-  auto gam = [&](double n) { return n * u / (1.0 - n * u); };
-  const double C = 1.25 * (gam(p.bs + 2) + gam(p.d + 2) * (1.0 + gam(p.bs + 2)) + u);
-  const float eps = (float)(C * (double)qnorm1 * (double)amax * (double)inv * (1 + 1e-6) + 1e-30);
-  const float tf = order_key_f32(t);
-  const float E = 2.0f * eps * 1.0001f + 1e-30f;
-  const uint32_t klo = f32_order_key(nextafterf(tf - E, -INFINITY));
-  const uint32_t khi = f32_order_key(nextafterf(tf + E, INFINITY));
-
-  // ordered pass: count blocks above the band, list the band (ascending)
-  if (tid == 0) { run[0] = 0; run[1] = 0; }
-  __syncthreads();
-  for (int base = 0; base < ne; base += T) {
-    const int i = base + tid;
-    bool in = false, bd = false;
-    if (i < ne) {
-      in = keys[i] > khi;
-      bd = keys[i] >= klo && keys[i] <= khi;
+    __syncthreads();
+    const float* kb = p.kbar + ((int64_t)b * p.Hkv + hk) * nbk * p.d;
+    const float* ka = p.kabs + ((int64_t)b * p.Hkv + hk) * nbk;
+    const float inv = ldexpf(1.0f, -p.log2bs);
+    float amax = 0.f;
+    for (int beta = tid; beta < neMax; beta += kBsThreads) {
+      const f32x4* kr = (const f32x4*)(kb + (int64_t)beta * p.d);
+      float acc[RB];
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) acc[rr] = 0.f;
+      for (int c4 = 0; c4 < d4; c4 += 4) {
+        f32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = kr[c4 + u];
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const f32x4 qv = qs[rr * d4 + c4 + u];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[rr] = fmaf(qv[e], v[u][e], acc[rr]);
+          }
+      }
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) sk[rr * nbk + beta] = f32_order_key(acc[rr] * inv);
+      amax = fmaxf(amax, ka[beta]);
     }
-    uint32_t nin, nbd;
-    const uint32_t bpos = block_prefix<T>(bd, sc, nbd);
-    block_prefix<T>(in, sc, nin);
-    if (bd) band_b[run[1] + bpos] = i;
-    __syncthreads();
-    if (tid == 0) { run[0] += nin; run[1] += nbd; }
-    __syncthreads();
+    amax = wave_max(amax);
+    if (lane == 0) fred[wid] = amax;
+  } else if (lane == 0) {
+    fred[wid] = 0.f;
   }
-  const uint32_t n_in = run[0], n_band = run[1];
-  // exact keys of the band, one wave per block
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(fred[0], fred[1]), fmaxf(fred[2], fred[3]));
+  // rigorous bound on |score~ - key| per unit of |q|_1 (amax covers every block of the tile)
+  const double uu = 1.0 / 8388608.0;
+  auto gam = [&](double n) { return n * uu / (1.0 - n * uu); };
+  const double C = 1.25 * (gam(p.bs + 2) + gam(p.d + 2) * (1.0 + gam(p.bs + 2)) + uu);
   const int ksz = p.k.dt == DT_F32 ? 4 : 2;
-  for (uint32_t e = wid; e < n_band; e += T / 64) {
-    const int beta = band_b[e];
-    const char* kblk = (const char*)p.k.p +
-                       (b * p.k.s[0] + hk * p.k.s[1] + (int64_t)beta * p.bs * p.k.s[2]) * ksz;
-    const float key = wave_block_key(p, qrow, kblk);
-    if (lane == 0) band_k[e] = f32_order_key(key);
-  }
-  __syncthreads();
-  // keep the R best of the band by (exact key desc, block asc): rank by counting
-  const uint32_t R = (uint32_t)nb - n_in;
-  for (uint32_t e = tid; e < n_band; e += T) {
-    const uint32_t ke = band_k[e];
-    uint32_t rank = 0;
-    for (uint32_t f = 0; f < n_band; ++f) {
-      const uint32_t kf = band_k[f];
-      rank += (kf > ke || (kf == ke && f < e)) ? 1u : 0u;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  for (int rr = wid; rr < nrows; rr += 4) {
+    const int r = r0 + rr;
+    const int ne = ne_of(rr);
+    int32_t* out = p.out + b * p.os[0] + h * p.os[1] + (int64_t)r * p.os[2];
+    const int64_t crow = ((int64_t)b * p.Hq + h) * p.Nq + r;
+    if (ne <= nb) {
+      for (int i = lane; i < nb; i += 64) out[i] = i < ne ? i : -1;
+      if (p.count && lane == 0) p.count[crow] = ne;
+      continue;
     }
-    if (rank < R) band_b[e] |= 0x80000000u;
-  }
-  __syncthreads();
-  // ordered output
-  if (tid == 0) { run[0] = 0; run[1] = 0; }
-  __syncthreads();
-  for (int base = 0; base < ne; base += T) {
-    const int i = base + tid;
-    bool sel = false, bd = false;
-    if (i < ne) {
-      sel = keys[i] > khi;
-      bd = keys[i] >= klo && keys[i] <= khi;
+    const uint32_t* srow = sk + rr * nbk;
+    uint32_t kr[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int i = j * 64 + lane;
+      kr[j] = i < ne ? srow[i] : 0u;
     }
-    uint32_t nbd, nsel;
-    const uint32_t brank = run[1] + block_prefix<T>(bd, sc, nbd);
-    if (bd) sel = (band_b[brank] & 0x80000000u) != 0;
-    const uint32_t opos = run[0] + block_prefix<T>(sel, sc, nsel);
-    if (sel && opos < (uint32_t)nb) out[opos] = i;
-    __syncthreads();
-    if (tid == 0) { run[0] += nsel; run[1] += nbd; }
-    __syncthreads();
+    // t = nb-th largest order key: the largest v with #{key >= v} >= nb
+    uint32_t t = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = t | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j)
+        if (j * 64 < ne) cnt += __popcll(ballot(kr[j] >= cand));
+      if (cnt >= nb) t = cand;
+    }
+    const float eps = (float)(C * (double)qn[rr] * (double)amax * ldexp(1.0, -p.log2bs) * (1 + 1e-6) + 1e-30);
+    const float tf = order_key_f32(t);
+    const float E = 2.0f * eps * 1.0001f + 1e-30f;
+    const uint32_t klo = f32_order_key(nextafterf(tf - E, -INFINITY));
+    const uint32_t khi = f32_order_key(nextafterf(tf + E, INFINITY));
+    uint64_t bm[KPL];
+    int n_in = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const bool v = j * 64 + lane < ne;
+      bm[j] = ballot(v && kr[j] >= klo && kr[j] <= khi);
+      n_in += __popcll(ballot(v && kr[j] > khi));
+    }
+    // exact keys of the band, written over the scores in LDS by every lane
+    const char* qrow = (const char*)p.q.p + (b * p.q.s[0] + h * p.q.s[1] + (int64_t)r * p.q.s[2]) * esz;
+    uint32_t* wrow = sk + rr * nbk;
+    for (int j = 0; j * 64 < ne; ++j) {
+      const int i = j * 64 + lane;
+      const uint32_t kk = i < ne ? wrow[i] : 0u;
+      uint64_t m = ballot(i < ne && kk >= klo && kk <= khi);
+      while (m) {
+        const int beta = j * 64 + __builtin_ctzll(m);
+        m &= m - 1;
+        const char* kblk = (const char*)p.k.p + (b * p.k.s[0] + hk * p.k.s[1] + (int64_t)beta * p.bs * p.k.s[2]) * ksz;
+        const int64_t ob = ((int64_t)b * p.Hkv + hk) * nbk + beta;
+        float key = wave_block_key_sums(p, qrow, p.kbar64 + ob * p.d, p.kexact[ob] != 0, kblk);
+        key = __shfl(key, 0, 64);
+        wrow[beta] = f32_order_key(key);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KPL; ++j)
+      if ((bm[j] >> lane) & 1) kr[j] = wrow[j * 64 + lane];
+    // the R best of the band: tb = R-th largest exact key, ties at tb by block index
+    const int R = nb - n_in;
+    uint32_t tb = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tb | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j)
+        if (j * 64 < ne) cnt += __popcll(ballot(((bm[j] >> lane) & 1) && kr[j] >= cand));
+      if (cnt >= R) tb = cand;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) gt += __popcll(ballot(((bm[j] >> lane) & 1) && kr[j] > tb));
+    const int need = R - gt;
+    int opos = 0, ties = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      if (j * 64 >= ne) break;
+      const int i = j * 64 + lane;
+      const bool band = (bm[j] >> lane) & 1;
+      const bool tie = band && kr[j] == tb;
+      const uint64_t tm = ballot(tie);
+      const int trank = ties + __popcll(tm & below);
+      const bool sel = i < ne && (band ? (kr[j] > tb || (tie && trank < need)) : kr[j] > khi);
+      const uint64_t smk = ballot(sel);
+      const int o = opos + __popcll(smk & below);
+      if (sel && o < nb) out[o] = i;
+      opos += __popcll(smk);
+      ties += __popcll(tm);
+    }
+    if (p.count && lane == 0) p.count[crow] = nb;
   }
-  if (p.count && tid == 0) p.count[((int64_t)b * p.Hq + h) * p.Nq + r] = nb;
 }
 
 size_t block_select_ws_bytes(int B, int Hkv, int ctx, int d, int bs) {
   const size_t nbk = ctx / bs;
-  return (size_t)B * Hkv * nbk * (d + 1) * sizeof(float);
+  return (size_t)B * Hkv * nbk * (3 * d + 2) * sizeof(float);   // kbar, kabs, kbar64 (2 floats each), kexact
 }
 
 hipError_t launch_block_select(const BlockSelectParams& p, hipStream_t st) {
@@ -223,7 +312,17 @@ hipError_t launch_block_select(const BlockSelectParams& p, hipStream_t st) {
   hipLaunchKernelGGL(pool_kernel, dim3(p.B * p.Hkv * nbk), dim3(128), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(block_select_kernel, dim3(p.B * p.Hq * p.Nq), dim3(kBsThreads), 0, st, p);
+  const int kpl = nbk <= 512 ? 8 : nbk <= 1024 ? 16 : 32;
+  const int rb = 128 / kpl;
+  const int ntile = (p.Nq + rb - 1) / rb;
+  const size_t lds = (size_t)rb * p.d * 4 + (size_t)rb * nbk * 4;
+  const dim3 grid(p.B * p.Hq * ntile);
+  if (kpl == 8)
+    hipLaunchKernelGGL(block_select_kernel<8>, grid, dim3(kBsThreads), lds, st, p, ntile);
+  else if (kpl == 16)
+    hipLaunchKernelGGL(block_select_kernel<16>, grid, dim3(kBsThreads), lds, st, p, ntile);
+  else
+    hipLaunchKernelGGL(block_select_kernel<32>, grid, dim3(kBsThreads), lds, st, p, ntile);
   return hipGetLastError();
 }
 

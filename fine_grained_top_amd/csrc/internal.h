@@ -67,8 +67,10 @@ struct BlockSelectParams {
   int32_t* out;            // [B, Hq, Nq, nb]
   int64_t os[4];
   int32_t* count;
-  float* kbar;             // workspace [B, Hkv, ctx/bs, d] f32
-  float* kabs;             // workspace [B, Hkv, ctx/bs] f32: max_t,c |k| per block
+  float* kbar;             // workspace [B, Hkv, ctx/bs, d] f32: per-block key sums
+  float* kabs;             // workspace [B, Hkv, ctx/bs] f32: max_c sum_t |k| per block
+  double* kbar64;          // workspace [B, Hkv, ctx/bs, d] f64: the same sums in float64
+  uint32_t* kexact;        // workspace [B, Hkv, ctx/bs]: 1 when every float64 sum is exact
 };
 size_t block_select_ws_bytes(int B, int Hkv, int ctx, int d, int bs);
 hipError_t launch_block_select(const BlockSelectParams& p, hipStream_t st);

@@ -353,8 +353,11 @@ SPATTN_API int spattn_block_select(const spattn_tensor* q, const spattn_tensor* 
   for (int i = 0; i < 4; ++i) p.os[i] = blk_idx_out->stride[i];
   p.count = blk_count_out;
   const size_t nbk = p.ctx / p.bs;
-  p.kbar = (float*)ws;
-  p.kabs = p.kbar + (size_t)p.B * p.Hkv * nbk * p.d;
+  const size_t nblk = (size_t)p.B * p.Hkv * nbk;
+  p.kbar64 = (double*)ws;                                 // 8-byte aligned first
+  p.kbar = (float*)(p.kbar64 + nblk * p.d);
+  p.kabs = p.kbar + nblk * p.d;
+  p.kexact = (uint32_t*)(p.kabs + nblk);
   return launched(sp::launch_block_select(p, (hipStream_t)stream));
 }
 

@@ -235,6 +235,63 @@ def test_certified_selection_at_rounding_midpoints():
         assert np.array_equal(idx.cpu().numpy()[0, 0, 0], want), K
 
 
+def _block_select_case(q, k, ctx_len, bs, nb):
+    """Run block selection on the GPU and compare every row with the oracle."""
+    import oracle as orc
+    sp = S()
+    B, Hq, Nq, d = q.shape
+    Hkv, ctx = k.shape[1], k.shape[2]
+    qt, kt = q.cuda(), k.cuda()
+    idx = torch.full((B, Hq, Nq, nb), 7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B, Hq, Nq), 7, dtype=torch.int32, device="cuda")
+    cl = torch.tensor(ctx_len, dtype=torch.int32, device="cuda")
+    sp.spattn_block_select(qt, kt, cl, bs, nb, idx, cnt)
+    torch.cuda.synchronize()
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    q64, k64 = q.double().numpy(), k.double().numpy()
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // (Hq // Hkv)
+            for r in range(Nq):
+                p = ctx_len[b] - Nq + r
+                want = orc.block_select(q64[b, h, r], k64[b, hk], p, bs, nb) if p >= 0 else np.zeros(0, np.int64)
+                assert cnt[b, h, r] == len(want), (b, h, r)
+                assert np.array_equal(idx[b, h, r, : len(want)], want), (b, h, r, nb)
+                assert np.all(idx[b, h, r, len(want):] == -1)
+
+
+@pytest.mark.parametrize("case", ["f32_1000_blocks", "bf16_2048_blocks", "bf16_64_blocks_ragged"])
+def test_block_select_edges(case):
+    """Block routing at every supported block count (per-lane key slots 8/16/32),
+    exact ties (duplicate and all-zero blocks), ragged lengths and row tiles."""
+    say(f"[gpu] block select {case}")
+    g = torch.Generator().manual_seed(11)
+    if case == "f32_1000_blocks":
+        B, Hq, Hkv, Nq, d, ctx, bs = 2, 2, 1, 24, 64, 2000, 2
+        q = torch.randn(B, Hq, Nq, d, generator=g)
+        k = torch.randn(B, Hkv, ctx, d, generator=g)
+        for src, dst in ((5, 9), (5, 700), (11, 12)):            # tied keys: identical blocks
+            k[:, :, dst * bs:(dst + 1) * bs] = k[:, :, src * bs:(src + 1) * bs]
+        k[1, :, 100 * bs:400 * bs] = 0.0                          # a run of exact-zero keys
+        for nb in (1, 37, 999):
+            _block_select_case(q, k, [2000, 1337], bs, nb)
+    elif case == "bf16_2048_blocks":
+        B, Hq, Hkv, Nq, d, ctx, bs = 1, 2, 2, 9, 128, 2048, 1
+        q = torch.randn(B, Hq, Nq, d, generator=g).bfloat16()
+        k = torch.randn(B, Hkv, ctx, d, generator=g).bfloat16()
+        k[0, 1] = 0.0                                              # head 1: every key ties at 0
+        k[0, 0, 1000:1010] = k[0, 0, 3]
+        for nb in (100, 2047):
+            _block_select_case(q, k, [2048], bs, nb)
+    else:
+        B, Hq, Hkv, Nq, d, ctx, bs = 2, 4, 2, 70, 128, 4096, 64
+        q = torch.randn(B, Hq, Nq, d, generator=g).bfloat16()
+        k = torch.randn(B, Hkv, ctx, d, generator=g).bfloat16()
+        k[:, :, 64 * 10:64 * 11] += 1.5                           # a strongly preferred block
+        for nb in (3, 16, 63):
+            _block_select_case(q, k, [4096, 1000], bs, nb)
+
+
 # ---------------------------------------------------------------- full-size workloads
 def test_decode_full_every_row():
     wl = gen.WORKLOADS["dsa_decode"]
