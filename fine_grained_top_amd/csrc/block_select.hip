@@ -66,17 +66,15 @@ SP_DEV float wave_block_key(const BlockSelectParams& p, const void* qrow, const 
   const int lane = threadIdx.x & 63;
   const int n = p.bs * p.d;
   double y = 0.0, A = 0.0;
+  bool x = true;
   for (int e = lane; e < n; e += 64) {
     const int t = e / p.d, c = e % p.d;
-    const double v = load_f64(qrow, p.q.dt, c) * load_f64(kblock, p.k.dt, t * p.k.s[2] + c);
-    y += v;
+    const double v = load_f64(qrow, p.q.dt, c) * load_f64(kblock, p.k.dt, t * p.k.s[2] + c);   // exact
+    xadd(y, x, v);
     A += fabs(v);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    y += __shfl_xor(y, o, 64);
-    A += __shfl_xor(A, o, 64);
-  }
+  wave_xreduce(y, x, A);
+  if (x) return key_of_exact(ldexp(y, -p.log2bs));
   const double g52 = 2.220446049250313e-16;
   const double e = 2.0 * (n + 72) * g52 * A + 1e-300;
   float key;
@@ -88,28 +86,74 @@ SP_DEV float wave_block_key(const BlockSelectParams& p, const void* qrow, const 
 }
 
 // The same key from the block's exact float64 key sums: (1/bs) * q . ksum,
-// d products per candidate instead of bs * d; certified, else the full sum.
+// d products per candidate instead of bs * d; exact or certified, else the
+// full sum.
 SP_DEV float wave_block_key_sums(const BlockSelectParams& p, const void* qrow, const double* ks64, bool exact,
                                  const void* kblock) {
+#pragma clang fp contract(off)
   if (exact) {
     const int lane = threadIdx.x & 63;
     double y = 0.0, A = 0.0;
+    bool x = true;
     for (int c = lane; c < p.d; c += 64) {
-      const double v = load_f64(qrow, p.q.dt, c) * ks64[c];
-      y += v;
-      A += fabs(v);
+      const double qv = load_f64(qrow, p.q.dt, c), kv = ks64[c];
+      xadd_prod(y, x, qv, kv);
+      A += fabs(qv * kv);
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      y += __shfl_xor(y, o, 64);
-      A += __shfl_xor(A, o, 64);
-    }
+    wave_xreduce(y, x, A);
+    if (x) return key_of_exact(ldexp(y, -p.log2bs));
     const double g52 = 2.220446049250313e-16;
-    const double e = 2.0 * (p.d + 72) * g52 * A + 1e-300;
+    const double e = 2.0 * (2 * p.d + 72) * g52 * A + 1e-300;
     float key;
     if (certify(ldexp(y, -p.log2bs), ldexp(e, -p.log2bs), key)) return key;
   }
   return wave_block_key(p, qrow, kblock);
+}
+
+// want-th largest (want >= 1) of the keys k[j] on lanes set in vm[j]
+// (slot j of lane l holds element 64 j + l; the set must have >= want
+// members): radix select, 8 bits a pass, on a per-wave LDS histogram of 256
+// bins. Wave-uniform result.
+template <int KPL>
+SP_DEV uint32_t wave_kth_largest(const uint32_t (&k)[KPL], const uint64_t (&vm)[KPL], int n, uint32_t want,
+                                 uint32_t* hist) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0;
+#pragma unroll
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    *(u32x4*)(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      if (j * 64 >= n) break;
+      if (((vm[j] >> lane) & 1) && (k[j] & hmask) == prefix) atomicAdd(&hist[(k[j] >> shift) & 255u], 1u);
+    }
+    __builtin_amdgcn_wave_barrier();
+    const u32x4 hv = *(const u32x4*)(hist + 4 * lane);
+    const uint32_t c = hv[0] + hv[1] + hv[2] + hv[3];
+    // members with a digit in a higher lane's bins
+    uint32_t incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t v = __shfl_down(incl, o, 64);
+      if (lane + o < 64) incl += v;
+    }
+    const uint32_t above0 = incl - c;
+    // the bin where the count from the top reaches want
+    uint32_t dg = 0, above = 0;
+    if (above0 + hv[3] >= want) { dg = 3; above = above0; }
+    else if (above0 + hv[3] + hv[2] >= want) { dg = 2; above = above0 + hv[3]; }
+    else if (above0 + hv[3] + hv[2] + hv[1] >= want) { dg = 1; above = above0 + hv[3] + hv[2]; }
+    else { dg = 0; above = above0 + hv[3] + hv[2] + hv[1]; }
+    const uint64_t hit = ballot(above0 < want && want <= above0 + c);
+    const int src = (int)__builtin_ctzll(hit);
+    const uint32_t digit = 4u * (uint32_t)src + (uint32_t)__shfl((int)dg, src, 64);
+    want -= (uint32_t)__shfl((int)above, src, 64);
+    prefix |= digit << shift;
+    __builtin_amdgcn_wave_barrier();
+  }
+  return prefix;
 }
 
 // Select, one workgroup per tile of RB consecutive query rows of one (b, h):
@@ -128,6 +172,9 @@ __global__ __launch_bounds__(kBsThreads) void block_select_kernel(BlockSelectPar
   uint32_t* sk = (uint32_t*)(smem + RB * p.d * 4);            // [RB][nbk]
   __shared__ float qn[RB];
   __shared__ float fred[4];
+  __shared__ __align__(16) uint32_t whist[4][256];
+  __shared__ uint32_t wband_i[4][64];
+  __shared__ uint32_t wband_k[4][64];
 
   // blockIdx -> tile: a contiguous range of tiles per XCD (dispatch round-robins
   // workgroups over the 8 XCDs), so one XCD's L2 holds few heads' key sums
@@ -139,7 +186,8 @@ __global__ __launch_bounds__(kBsThreads) void block_select_kernel(BlockSelectPar
   const int b = wg / (ntile * p.Hq);
   const int r0 = tile * RB;
   const int nrows = min(RB, p.Nq - r0);
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hk = h / (p.Hq / p.Hkv);
   const int L = min(p.ctx_len ? p.ctx_len[b] : p.ctx, p.ctx);
   auto ne_of = [&](int rr) {
@@ -207,9 +255,12 @@ __global__ __launch_bounds__(kBsThreads) void block_select_kernel(BlockSelectPar
   const int ksz = p.k.dt == DT_F32 ? 4 : 2;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
+  uint32_t* hist = whist[wid];
+  uint32_t* bl_i = wband_i[wid];
+  uint32_t* bl_k = wband_k[wid];
   for (int rr = wid; rr < nrows; rr += 4) {
     const int r = r0 + rr;
-    const int ne = ne_of(rr);
+    const int ne = __builtin_amdgcn_readfirstlane(ne_of(rr));
     int32_t* out = p.out + b * p.os[0] + h * p.os[1] + (int64_t)r * p.os[2];
     const int64_t crow = ((int64_t)b * p.Hq + h) * p.Nq + r;
     if (ne <= nb) {
@@ -217,39 +268,33 @@ __global__ __launch_bounds__(kBsThreads) void block_select_kernel(BlockSelectPar
       if (p.count && lane == 0) p.count[crow] = ne;
       continue;
     }
-    const uint32_t* srow = sk + rr * nbk;
+    uint32_t* wrow = sk + rr * nbk;
     uint32_t kr[KPL];
+    uint64_t vm[KPL];
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
       const int i = j * 64 + lane;
-      kr[j] = i < ne ? srow[i] : 0u;
+      kr[j] = i < ne ? wrow[i] : 0u;
+      vm[j] = ballot(i < ne);
     }
-    // t = nb-th largest order key: the largest v with #{key >= v} >= nb
-    uint32_t t = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = t | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int j = 0; j < KPL; ++j)
-        if (j * 64 < ne) cnt += __popcll(ballot(kr[j] >= cand));
-      if (cnt >= nb) t = cand;
-    }
+    const uint32_t t = wave_kth_largest<KPL>(kr, vm, ne, (uint32_t)nb, hist);
     const float eps = (float)(C * (double)qn[rr] * (double)amax * ldexp(1.0, -p.log2bs) * (1 + 1e-6) + 1e-30);
     const float tf = order_key_f32(t);
     const float E = 2.0f * eps * 1.0001f + 1e-30f;
     const uint32_t klo = f32_order_key(nextafterf(tf - E, -INFINITY));
     const uint32_t khi = f32_order_key(nextafterf(tf + E, INFINITY));
     uint64_t bm[KPL];
-    int n_in = 0;
+    int n_in = 0, nbd = 0;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
-      const bool v = j * 64 + lane < ne;
-      bm[j] = ballot(v && kr[j] >= klo && kr[j] <= khi);
-      n_in += __popcll(ballot(v && kr[j] > khi));
+      bm[j] = vm[j] & ballot(kr[j] >= klo && kr[j] <= khi);
+      n_in += __popcll(vm[j] & ballot(kr[j] > khi));
+      nbd += __popcll(bm[j]);
     }
-    // exact keys of the band, written over the scores in LDS by every lane
+    // exact keys of the band (ascending block order), written over the scores
+    // in LDS by every lane; the first 64 also into the wave's band list
     const char* qrow = (const char*)p.q.p + (b * p.q.s[0] + h * p.q.s[1] + (int64_t)r * p.q.s[2]) * esz;
-    uint32_t* wrow = sk + rr * nbk;
+    int e = 0;
     for (int j = 0; j * 64 < ne; ++j) {
       const int i = j * 64 + lane;
       const uint32_t kk = i < ne ? wrow[i] : 0u;
@@ -260,43 +305,60 @@ __global__ __launch_bounds__(kBsThreads) void block_select_kernel(BlockSelectPar
         const char* kblk = (const char*)p.k.p + (b * p.k.s[0] + hk * p.k.s[1] + (int64_t)beta * p.bs * p.k.s[2]) * ksz;
         const int64_t ob = ((int64_t)b * p.Hkv + hk) * nbk + beta;
         float key = wave_block_key_sums(p, qrow, p.kbar64 + ob * p.d, p.kexact[ob] != 0, kblk);
-        key = __shfl(key, 0, 64);
-        wrow[beta] = f32_order_key(key);
+        const uint32_t ok = f32_order_key(__shfl(key, 0, 64));
+        wrow[beta] = ok;
+        if (e < 64 && lane == 0) {
+          bl_i[e] = beta;
+          bl_k[e] = ok;
+        }
+        ++e;
       }
     }
-#pragma unroll
-    for (int j = 0; j < KPL; ++j)
-      if ((bm[j] >> lane) & 1) kr[j] = wrow[j * 64 + lane];
-    // the R best of the band: tb = R-th largest exact key, ties at tb by block index
+    __builtin_amdgcn_wave_barrier();
+    // the R best of the band by (exact key desc, block asc) get the mark ~0,
+    // the others 0: afterwards "selected" is "mark or score above the band"
     const int R = nb - n_in;
-    uint32_t tb = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = tb | (1u << bit);
-      int cnt = 0;
+    if (nbd <= 64) {
+      const uint32_t ke = lane < nbd ? bl_k[lane] : 0u;
+      int rank = 0;
+      for (int f = 0; f < nbd; ++f) {
+        const uint32_t kf = bl_k[f];
+        rank += (kf > ke || (kf == ke && f < lane)) ? 1 : 0;
+      }
+      if (lane < nbd) wrow[bl_i[lane]] = rank < R ? ~0u : 0u;
+    } else {
+      uint32_t ex[KPL];
 #pragma unroll
-      for (int j = 0; j < KPL; ++j)
-        if (j * 64 < ne) cnt += __popcll(ballot(((bm[j] >> lane) & 1) && kr[j] >= cand));
-      if (cnt >= R) tb = cand;
+      for (int j = 0; j < KPL; ++j) ex[j] = ((bm[j] >> lane) & 1) ? wrow[j * 64 + lane] : 0u;
+      const uint32_t tb = wave_kth_largest<KPL>(ex, bm, ne, (uint32_t)R, hist);
+      int gt = 0;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) gt += __popcll(bm[j] & ballot(ex[j] > tb));
+      const int need = R - gt;
+      int ties = 0;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        if (j * 64 >= ne) break;
+        const bool band = (bm[j] >> lane) & 1;
+        const uint64_t tm = bm[j] & ballot(ex[j] == tb);
+        const int trank = ties + (int)lanes_below(tm);
+        if (band) wrow[j * 64 + lane] = (ex[j] > tb || (ex[j] == tb && trank < need)) ? ~0u : 0u;
+        ties += __popcll(tm);
+      }
     }
-    int gt = 0;
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) gt += __popcll(ballot(((bm[j] >> lane) & 1) && kr[j] > tb));
-    const int need = R - gt;
-    int opos = 0, ties = 0;
+    __builtin_amdgcn_wave_barrier();
+    // ordered output
+    int opos = 0;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
       if (j * 64 >= ne) break;
       const int i = j * 64 + lane;
-      const bool band = (bm[j] >> lane) & 1;
-      const bool tie = band && kr[j] == tb;
-      const uint64_t tm = ballot(tie);
-      const int trank = ties + __popcll(tm & below);
-      const bool sel = i < ne && (band ? (kr[j] > tb || (tie && trank < need)) : kr[j] > khi);
+      const uint32_t kk = ((bm[j] >> lane) & 1) ? wrow[i] : kr[j];
+      const bool sel = i < ne && kk > khi;
       const uint64_t smk = ballot(sel);
-      const int o = opos + __popcll(smk & below);
+      const int o = opos + (int)lanes_below(smk);
       if (sel && o < nb) out[o] = i;
       opos += __popcll(smk);
-      ties += __popcll(tm);
     }
     if (p.count && lane == 0) p.count[crow] = nb;
   }

@@ -9,14 +9,53 @@
 // Evaluation: float64 with a rigorous error bound first (products of inputs
 // with <= 24-bit significands are exact in float64; an n-term float64 sum in
 // any order is within n * 2^-53 * sum|terms| of the exact sum). When the whole
-// error interval rounds to one float32 that value is the key. Otherwise (the
-// exact value sits next to a float32 rounding boundary) the sum is formed
-// exactly in a wide two's-complement fixed-point accumulator and rounded by
-// hand. Input significands are at most 24 bits, exponents within float32's.
+// error interval rounds to one float32 that value is the key. Alongside, every
+// float64 addition is checked with an error-free transformation (TwoSum;
+// TwoProduct by fma for products that need not be exact): when no addition
+// rounded, the float64 result is the exact value and one float32 rounding
+// gives the key, also when it sits exactly on a rounding boundary (common
+// for bf16 data, whose sums are short). Otherwise (the exact value sits next
+// to a float32 rounding boundary) the sum is formed exactly in a wide two's-
+// complement fixed-point accumulator and rounded by hand. Input significands
+// are at most 24 bits, exponents within float32's.
 #pragma once
 #include "common.h"
 
 namespace sp {
+
+// s += t with exactness tracking: exact stays true while no addition rounded
+// (TwoSum recovers the rounding error of s + t exactly).
+SP_DEV void xadd(double& s, bool& exact, double t) {
+#pragma clang fp contract(off)
+  const double n = s + t;
+  const double bb = n - s;
+  const double err = (s - (n - bb)) + (t - bb);
+  exact = exact && err == 0.0;
+  s = n;
+}
+
+// s += a * b exactly tracked: the product's rounding error (fma) is added too.
+SP_DEV void xadd_prod(double& s, bool& exact, double a, double b) {
+#pragma clang fp contract(off)
+  const double p = a * b;
+  const double pe = fma(a, b, -p);
+  xadd(s, exact, p);
+  if (pe != 0.0) xadd(s, exact, pe);
+}
+
+// Wave all-reduce of a tracked sum and of its magnitude sum; the butterfly
+// gives every lane the same value, and exact becomes wave-uniform.
+SP_DEV void wave_xreduce(double& y, bool& exact, double& A) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    xadd(y, exact, __shfl_xor(y, o, 64));
+    A += __shfl_xor(A, o, 64);
+  }
+  exact = __all(exact);
+}
+
+// float32 key of an exact float64 value (-0 read as +0)
+SP_DEV float key_of_exact(double y) { return (float)y + 0.0f; }
 
 SP_DEV double load_f64(const void* p, int dtype, int64_t i) {
   if (dtype == DT_F32) return (double)((const float*)p)[i];
@@ -200,26 +239,31 @@ SP_DEV float exact_key(const IndexerRow& r, int64_t j) {
   int64_t koff = j * r.k_stride;
   if (!r.relu) {
     double y = 0.0, A = 0.0;
+    bool x = true;
     for (int c = 0; c < r.d; ++c) {
-      double t = load_f64(r.q, r.qt, c) * load_f64(r.k, r.kt, koff + c);
-      y += t;
+      double t = load_f64(r.q, r.qt, c) * load_f64(r.k, r.kt, koff + c);   // exact product
+      xadd(y, x, t);
       A += fabs(t);
     }
+    if (x) return key_of_exact(y);
     float key;
     if (certify(y, 2.0 * (r.d + 4) * g52 * A + 1e-300, key)) return key;
     return exact_key_slow(r, j);
   }
-  double s = 0.0, Es = 0.0, Ar = 0.0;
-  bool ok = true;
+  double s = 0.0, Es = 0.0, Ar = 0.0, sx = 0.0;
+  bool ok = true, xall = true;
   for (int h = 0; h < r.H; ++h) {
     double y = 0.0, A = 0.0;
+    bool x = true;
     for (int c = 0; c < r.d; ++c) {
       double t = load_f64(r.q, r.qt, h * r.qh_stride + c) * load_f64(r.k, r.kt, koff + c);
-      y += t;
+      xadd(y, x, t);
       A += fabs(t);
     }
     double E = 2.0 * (r.d + 4) * g52 * A + 1e-300;
     double w = (double)r.w[h * r.w_stride];
+    if (!x) xall = false;
+    else if (y > 0.0 && w != 0.0) xadd_prod(sx, xall, w, y);
     if (y > E) {
       s += w * y;
       Es += fabs(w) * E;
@@ -228,6 +272,7 @@ SP_DEV float exact_key(const IndexerRow& r, int64_t j) {
       ok = false;
     }
   }
+  if (xall) return key_of_exact(sx);
   float key;
   if (ok && certify(s, Es + 2.0 * (r.H + 4) * g52 * Ar + 1e-300, key)) return key;
   return exact_key_slow(r, j);
@@ -240,38 +285,37 @@ SP_DEV float wave_exact_key(const IndexerRow& r, int64_t j) {
   const double g52 = 2.220446049250313e-16;
   const int lane = threadIdx.x & 63;
   const int64_t koff = j * r.k_stride;
-  double s = 0.0, Es = 0.0, Ar = 0.0;
-  bool ok = true;
+  double s = 0.0, Es = 0.0, Ar = 0.0, sx = 0.0;
+  bool ok = true, xall = true;
   for (int h0 = 0; h0 < r.H; h0 += 4) {
     double y[4] = {0.0, 0.0, 0.0, 0.0}, A[4] = {0.0, 0.0, 0.0, 0.0};
+    bool x[4] = {true, true, true, true};
     for (int c = lane; c < r.d; c += 64) {
       const double kv = load_f64(r.k, r.kt, koff + c);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         if (h0 + u < r.H) {
-          const double t = load_f64(r.q, r.qt, (h0 + u) * r.qh_stride + c) * kv;
-          y[u] += t;
+          const double t = load_f64(r.q, r.qt, (h0 + u) * r.qh_stride + c) * kv;   // exact product
+          xadd(y[u], x[u], t);
           A[u] += fabs(t);
         }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        y[u] += __shfl_xor(y[u], o, 64);
-        A[u] += __shfl_xor(A[u], o, 64);
-      }
+    for (int u = 0; u < 4; ++u) wave_xreduce(y[u], x[u], A[u]);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (h0 + u >= r.H) break;
       const double E = 2.0 * (r.d + 70) * g52 * A[u] + 1e-300;
       if (!r.relu) {
+        if (x[u]) return key_of_exact(y[u]);
         float key;
         if (certify(y[u], E, key)) return key;
         ok = false;
         break;
       }
       const double w = (double)r.w[(h0 + u) * r.w_stride];
+      if (!x[u]) xall = false;
+      else if (y[u] > 0.0 && w != 0.0) xadd_prod(sx, xall, w, y[u]);
       if (y[u] > E) {
         s += w * y[u];
         Es += fabs(w) * E;
@@ -282,6 +326,7 @@ SP_DEV float wave_exact_key(const IndexerRow& r, int64_t j) {
     }
     if (!r.relu) break;
   }
+  if (r.relu && xall) return key_of_exact(sx);
   float key = 0.f;
   if (r.relu && ok && certify(s, Es + 2.0 * (r.H + 4) * g52 * Ar + 1e-300, key)) return key;
   float slow = 0.f;
@@ -294,12 +339,14 @@ SP_DEV float exact_block_key(const void* q, int qt, const void* k, int kt, int64
                              int bs, int log2bs, int d) {
   const double g52 = 2.220446049250313e-16;
   double y = 0.0, A = 0.0;
+  bool x = true;
   for (int t = 0; t < bs; ++t)
     for (int c = 0; c < d; ++c) {
-      double v = load_f64(q, qt, c) * load_f64(k, kt, t * k_stride + c);
-      y += v;
+      double v = load_f64(q, qt, c) * load_f64(k, kt, t * k_stride + c);   // exact product
+      xadd(y, x, v);
       A += fabs(v);
     }
+  if (x) return key_of_exact(ldexp(y, -log2bs));
   double e = 2.0 * (bs * d + 8) * g52 * A + 1e-300;
   float key;
   if (certify(ldexp(y, -log2bs), ldexp(e, -log2bs), key)) return key;
