@@ -43,16 +43,22 @@ SP_DEV void xadd_prod(double& s, bool& exact, double a, double b) {
   if (pe != 0.0) xadd(s, exact, pe);
 }
 
-// Wave all-reduce of a tracked sum and of its magnitude sum; the butterfly
-// gives every lane the same value, and exact becomes wave-uniform.
-SP_DEV void wave_xreduce(double& y, bool& exact, double& A) {
+// All-reduce of a tracked sum and of its magnitude sum over a group of W
+// aligned lanes (W = 64: the wave; 32: a half-wave); the butterfly gives every
+// lane of the group the same value, and exact becomes group-uniform.
+template <int W>
+SP_DEV void group_xreduce(double& y, bool& exact, double& A) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
+  for (int o = W / 2; o > 0; o >>= 1) {
     xadd(y, exact, __shfl_xor(y, o, 64));
     A += __shfl_xor(A, o, 64);
   }
-  exact = __all(exact);
+  const uint64_t bad = ballot(!exact);
+  const int base = (threadIdx.x & 63) & ~(W - 1);
+  const uint64_t gm = W == 64 ? ~0ull : ((1ull << W) - 1) << base;
+  exact = (bad & gm) == 0;
 }
+SP_DEV void wave_xreduce(double& y, bool& exact, double& A) { group_xreduce<64>(y, exact, A); }
 
 // float32 key of an exact float64 value (-0 read as +0)
 SP_DEV float key_of_exact(double y) { return (float)y + 0.0f; }
@@ -278,19 +284,27 @@ SP_DEV float exact_key(const IndexerRow& r, int64_t j) {
   return exact_key_slow(r, j);
 }
 
-// The same key computed by a whole wave for one candidate j (wave-uniform):
-// lanes split the dimensions; every load of a group of four heads is issued
-// before any reduction, and per-head sums are reduced across the wave.
-SP_DEV float wave_exact_key(const IndexerRow& r, int64_t j) {
+// The same key computed by a group of W aligned lanes (a wave, or a half-wave
+// so that two candidates are scored at once) for one candidate j (group-
+// uniform): lanes split the dimensions; every load of a group of four heads
+// (operands and weights) is issued before any reduction, and per-head sums
+// are reduced across the group.
+template <int W>
+SP_DEV float group_exact_key(const IndexerRow& r, int64_t j) {
   const double g52 = 2.220446049250313e-16;
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & (W - 1);
+  const int base = (threadIdx.x & 63) & ~(W - 1);
   const int64_t koff = j * r.k_stride;
   double s = 0.0, Es = 0.0, Ar = 0.0, sx = 0.0;
   bool ok = true, xall = true;
   for (int h0 = 0; h0 < r.H; h0 += 4) {
     double y[4] = {0.0, 0.0, 0.0, 0.0}, A[4] = {0.0, 0.0, 0.0, 0.0};
     bool x[4] = {true, true, true, true};
-    for (int c = lane; c < r.d; c += 64) {
+    double wv[4] = {0.0, 0.0, 0.0, 0.0};      // loaded with the operands, used after the reduction
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (r.relu && h0 + u < r.H) wv[u] = (double)r.w[(h0 + u) * r.w_stride];
+    for (int c = lane; c < r.d; c += W) {
       const double kv = load_f64(r.k, r.kt, koff + c);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -301,11 +315,11 @@ SP_DEV float wave_exact_key(const IndexerRow& r, int64_t j) {
         }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) wave_xreduce(y[u], x[u], A[u]);
+    for (int u = 0; u < 4; ++u) group_xreduce<W>(y[u], x[u], A[u]);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (h0 + u >= r.H) break;
-      const double E = 2.0 * (r.d + 70) * g52 * A[u] + 1e-300;
+      const double E = 2.0 * (r.d + 70) * g52 * A[u] + 1e-300;   // r.d / W + log2 W terms per path
       if (!r.relu) {
         if (x[u]) return key_of_exact(y[u]);
         float key;
@@ -313,7 +327,7 @@ SP_DEV float wave_exact_key(const IndexerRow& r, int64_t j) {
         ok = false;
         break;
       }
-      const double w = (double)r.w[(h0 + u) * r.w_stride];
+      const double w = wv[u];
       if (!x[u]) xall = false;
       else if (y[u] > 0.0 && w != 0.0) xadd_prod(sx, xall, w, y[u]);
       if (y[u] > E) {
@@ -331,8 +345,9 @@ SP_DEV float wave_exact_key(const IndexerRow& r, int64_t j) {
   if (r.relu && ok && certify(s, Es + 2.0 * (r.H + 4) * g52 * Ar + 1e-300, key)) return key;
   float slow = 0.f;
   if (lane == 0) slow = exact_key_slow(r, j);
-  return __shfl(slow, 0, 64);
+  return __shfl(slow, base, 64);
 }
+SP_DEV float wave_exact_key(const IndexerRow& r, int64_t j) { return group_exact_key<64>(r, j); }
 
 // Block key: float32 nearest to (1/bs) * sum_{t<bs} q . k[t]; bs a power of two.
 SP_DEV float exact_block_key(const void* q, int qt, const void* k, int kt, int64_t k_stride,

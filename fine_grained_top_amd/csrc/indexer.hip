@@ -45,12 +45,15 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
   }
   __shared__ uint32_t lcount[128];
   __shared__ float wsl[128];
+  __shared__ float tsl[128];          // filter threshold of each slot's selection row
   for (int i = threadIdx.x; i < 128; i += 256) {
     if (FILTER) lcount[i] = 0;
-    float wv = 0.f;
+    float wv = 0.f, tv = INFINITY;
     const int ms = mbase + i;
     if (RELU && ms < M) wv = p.w[b * p.ws_[0] + (ms >> hshift) * p.ws_[1] + (ms & (p.H_I - 1)) * p.ws_[2]];
+    if (FILTER && ms < M) tv = p.tau[(b * p.G_sel + (ms & (p.H_I - 1)) / HPG) * p.Nq + (ms >> hshift)];
     wsl[i] = wv;
+    tsl[i] = tv;
   }
   __syncthreads();
 
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
               p.scores[b * p.ss[0] + g * p.ss[1] + r * p.ss[2] + j] = sc;
             } else {
               const int row = (b * p.G_sel + g) * p.Nq + r;
-              if (sc >= p.tau[row]) {
+              if (sc >= tsl[m0 - mbase]) {
                 const int lrow = g * p.Nq + r;   // fused path: all slots in one block
                 const uint32_t slot = atomicAdd(&lcount[lrow], 1u);
                 if (slot < (uint32_t)p.cap) {

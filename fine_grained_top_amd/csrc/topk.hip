@@ -721,84 +721,167 @@ SP_DEV float row_eps(const TopkParams& p, const RowCtx& c, const float* kmax, in
   return (float)e * (1.0f + 1e-6f);
 }
 
-__global__ __launch_bounds__(kTkThreads) void fz_pilot_kernel(TopkParams p, float* tau) {
+// Pilot, stage 1: one thread per (sampled key, selection row): the row's
+// heads score the key in float32; a key the row cannot see (after its
+// position) gets the order key 0, which no finite score has.
+constexpr int kPsThreads = 256;
+__global__ __launch_bounds__(kPsThreads) void fz_pilot_score_kernel(TopkParams p, uint32_t* skeys, int slots) {
+  const IndexerParams& x = p.ix;
+  const int b = blockIdx.y;
+  const int rowl = blockIdx.z;                      // (g, r) within the request
+  const int g = rowl / x.Nq, r = rowl % x.Nq;
+  const int i = blockIdx.x * kPsThreads + threadIdx.x;
+  __shared__ float qs[4 * 64];                      // <= 4 heads per group, d_I = 64
+  __shared__ float wsh[4];
+  for (int e = threadIdx.x; e < x.hpg * 64; e += kPsThreads) {
+    const int h = g * x.hpg + (e >> 6);
+    qs[e] = (float)load_f64(x.q.p, x.q.dt, b * x.q.s[0] + r * x.q.s[1] + h * x.q.s[2] + (e & 63));
+  }
+  if ((int)threadIdx.x < x.hpg)
+    wsh[threadIdx.x] = x.relu ? x.w[b * x.ws_[0] + r * x.ws_[1] + (g * x.hpg + threadIdx.x) * x.ws_[2]] : 1.f;
+  __syncthreads();
+  if (i >= slots) return;
+  const int L = min(p.ctx_len ? p.ctx_len[b] : p.ctx, p.ctx);
+  const int j = (i / kPilotRun) * kPilotStride + (i % kPilotRun);
+  uint32_t key = 0u;
+  if (j <= L - x.Nq + r) {
+    float kv[64];
+    if (x.k.dt == DT_FP8) {
+      const u32x4* kp = (const u32x4*)((const uint8_t*)x.k.p + b * x.k.s[0] + (int64_t)j * x.k.s[1]);
+      u32x4 raw[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) raw[u] = kp[u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u][v], false);
+          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u][v], true);
+          kv[16 * u + 4 * v + 0] = lo[0];
+          kv[16 * u + 4 * v + 1] = lo[1];
+          kv[16 * u + 4 * v + 2] = hi[0];
+          kv[16 * u + 4 * v + 3] = hi[1];
+        }
+    } else {
+      const u32x4* kp = (const u32x4*)((const uint16_t*)x.k.p + b * x.k.s[0] + (int64_t)j * x.k.s[1]);
+      u32x4 raw[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) raw[u] = kp[u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          kv[8 * u + 2 * v] = __uint_as_float(raw[u][v] << 16);
+          kv[8 * u + 2 * v + 1] = __uint_as_float(raw[u][v] & 0xFFFF0000u);
+        }
+    }
+    float sc = 0.f;
+    for (int h = 0; h < x.hpg; ++h) {
+      const f32x4* qh = (const f32x4*)(qs + h * 64);
+      float d = 0.f;
+#pragma unroll
+      for (int c4 = 0; c4 < 16; ++c4) {
+        const f32x4 qv = qh[c4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d = fmaf(qv[e], kv[4 * c4 + e], d);
+      }
+      sc = x.relu ? fmaf(wsh[h], fmaxf(d, 0.f), sc) : d;
+    }
+    key = f32_order_key(sc);
+  }
+  skeys[((int64_t)(b * x.G_sel + g) * x.Nq + r) * slots + i] = key;
+}
+
+// Pilot, stage 2: per row, tau = a score with at least about 1.5 K sampled
+// survivors in proportion (sample count scaled to the row's length): one
+// histogram pass of 4096 bins over the range of the sampled order keys; tau
+// is the lower edge of the bin where the count from the top reaches that
+// number. Any tau is correct (the final stage checks and can fall back);
+// this one only has to leave a little over 1.5 K keys.
+__global__ __launch_bounds__(kTkThreads) void fz_pilot_select_kernel(TopkParams p, const uint32_t* skeys,
+                                                                     int slots, float* tau) {
   constexpr int T = kTkThreads;
-  __shared__ uint32_t skey[kPilotCap];
+  constexpr int NW = T / 64;
   __shared__ uint32_t hist[4096];
   __shared__ uint32_t sc[16];
-  __shared__ float qs[4 * 64];       // the fused path has d_I = 64 and <= 4 heads per group
-  __shared__ float wsh[4];
-  const int row = blockIdx.x, tid = threadIdx.x;
+  __shared__ uint32_t red[2 * NW + 2];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   RowCtx c = row_ctx(p, row);
   if (c.n <= p.K) {
     if (tid == 0) tau[row] = INFINITY;   // every key is selected; nothing to filter
     return;
   }
-  const IndexerRow& ir = c.ir;
-  for (int e = tid; e < ir.H * 64; e += T) qs[e] = (float)load_f64(ir.q, ir.qt, (e >> 6) * ir.qh_stride + (e & 63));
-  if (tid < ir.H) wsh[tid] = ir.relu ? ir.w[tid * ir.w_stride] : 1.f;
-  __syncthreads();
-  const int nsb = (c.n + kPilotStride - 1) / kPilotStride;
-  const int slots = nsb * kPilotRun;
-  int m = 0;
-  for (int i = tid; i < slots; i += T) {
-    const int j = (i / kPilotRun) * kPilotStride + (i % kPilotRun);
-    uint32_t key = 0u;
-    if (j < c.n) {
-      float kv[64];
-      if (ir.kt == DT_FP8) {
-        const u32x4* kp = (const u32x4*)((const uint8_t*)ir.k + (int64_t)j * ir.k_stride);
-        u32x4 raw[4];
+  const uint32_t* src = skeys + (int64_t)row * slots;
+  constexpr int U = kPilotCap / T;
+  uint32_t v[U];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) raw[u] = kp[u];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u][v], false);
-            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u][v], true);
-            kv[16 * u + 4 * v + 0] = lo[0];
-            kv[16 * u + 4 * v + 1] = lo[1];
-            kv[16 * u + 4 * v + 2] = hi[0];
-            kv[16 * u + 4 * v + 3] = hi[1];
-          }
-      } else {
-        const u32x4* kp = (const u32x4*)((const uint16_t*)ir.k + (int64_t)j * ir.k_stride);
-        u32x4 raw[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) raw[u] = kp[u];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            kv[8 * u + 2 * v] = __uint_as_float(raw[u][v] << 16);
-            kv[8 * u + 2 * v + 1] = __uint_as_float(raw[u][v] & 0xFFFF0000u);
-          }
-      }
-      float sc2 = 0.f;
-      for (int h = 0; h < ir.H; ++h) {
-        float d = 0.f;
-#pragma unroll
-        for (int cc = 0; cc < 64; ++cc) d = fmaf(qs[h * 64 + cc], kv[cc], d);
-        sc2 = ir.relu ? fmaf(wsh[h], fmaxf(d, 0.f), sc2) : d;
-      }
-      key = f32_order_key(sc2);
-      ++m;
-    }
-    skey[i] = key;
+  for (int u = 0; u < U; ++u) {
+    const int i = tid + u * T;
+    v[u] = i < slots ? src[i] : 0u;
   }
-  uint32_t mt;
-  block_scan_sum<T>((uint32_t)m, sc, mt);
+  for (int i = tid; i < 4096; i += T) hist[i] = 0u;
+  uint32_t m = 0, kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (v[u] != 0u) {
+      ++m;
+      kmin = min(kmin, v[u]);
+      kmax = max(kmax, v[u]);
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    m += (uint32_t)__shfl_xor((int)m, o, 64);
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  }
+  if (lane == 0) {
+    red[wid] = kmin;
+    red[NW + wid] = kmax;
+    sc[wid] = m;
+  }
+  __syncthreads();
+  uint32_t mt = 0;
+  kmin = 0xFFFFFFFFu;
+  kmax = 0u;
+  for (int w = 0; w < NW; ++w) {
+    mt += sc[w];
+    kmin = min(kmin, red[w]);
+    kmax = max(kmax, red[NW + w]);
+  }
   const uint64_t want = ((uint64_t)3 * p.K * mt + 2ull * c.n - 1) / (2ull * c.n) + 16;   // ~1.5 K survivors
   const uint32_t R = (uint32_t)min((uint64_t)mt, want);
-  uint32_t t, above;
-  radix_select<T>(slots, R,
-                  [&](int i, uint32_t& k) {
-                    k = skey[i];
-                    return ((i / kPilotRun) * kPilotStride + (i % kPilotRun)) < c.n;
-                  },
-                  hist, sc, t, above);
-  if (tid == 0) tau[row] = order_key_f32(t);
+  if (R == 0) {
+    if (tid == 0) tau[row] = -INFINITY;
+    return;
+  }
+  const int bits = 32 - __builtin_clz((kmax - kmin) | 1u);
+  const int sh = bits > 12 ? bits - 12 : 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (v[u] != 0u) atomicAdd(&hist[(v[u] - kmin) >> sh], 1u);
+  __syncthreads();
+  // count from the top: thread tid owns bins [8 tid, 8 tid + 8)
+  uint32_t hb[8], cnt = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    hb[e] = hist[8 * tid + e];
+    cnt += hb[e];
+  }
+  uint32_t tot;
+  const uint32_t below = block_scan_sum<T>(cnt, sc, tot);   // members in lower threads' bins
+  const uint32_t above0 = tot - below - cnt;                // members in higher threads' bins
+  if (above0 < R && R <= above0 + cnt) {
+    uint32_t acc = above0;
+    int bin = 8 * tid;
+    for (int e = 7; e >= 0; --e) {
+      acc += hb[e];
+      if (acc >= R) {
+        bin = 8 * tid + e;
+        break;
+      }
+    }
+    tau[row] = order_key_f32(kmin + ((uint32_t)bin << sh));
+  }
 }
 
 struct FzWs {
@@ -845,16 +928,35 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
   if (tid == 0) sm.coff[nch] = n_cand;
   const bool any_over = __syncthreads_or(over) != 0;
   if (any_over || n_cand < (uint32_t)p.K || n_cand > (uint32_t)kCandCap) return fallback();
-  // compact into LDS: candidate e belongs to the chunk whose offset range holds it
-  for (uint32_t e = tid; e < n_cand; e += T) {
-    int lo = 0, hi = nch;                   // coff[lo] <= e < coff[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (sm.coff[mid] <= e) lo = mid; else hi = mid;
+  // compact into LDS: candidate e belongs to the chunk whose offset range holds
+  // it; the loads of 8 candidates per thread are in flight together
+  constexpr int CB = 8;
+  for (uint32_t e0 = 0; e0 < n_cand; e0 += CB * T) {
+    int64_t src[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const uint32_t e = e0 + u * T + tid;
+      int lo = 0, hi = nch;                 // coff[lo] <= e < coff[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sm.coff[mid] <= e) lo = mid; else hi = mid;
+      }
+      src[u] = e < n_cand ? ((int64_t)row * w.nchunk + lo) * w.cap + (e - sm.coff[lo]) : -1;
     }
-    const int64_t src = ((int64_t)row * w.nchunk + lo) * w.cap + (e - sm.coff[lo]);
-    sm.ck[e] = w.cand_k[src];
-    sm.cj[e] = w.cand_j[src];
+    uint32_t kk[CB], jj[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      kk[u] = src[u] >= 0 ? w.cand_k[src[u]] : 0u;
+      jj[u] = src[u] >= 0 ? w.cand_j[src[u]] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const uint32_t e = e0 + u * T + tid;
+      if (e < n_cand) {
+        sm.ck[e] = kk[u];
+        sm.cj[e] = jj[u];
+      }
+    }
   }
   const int nwords = (c.n + 31) >> 5;
   for (int i = tid; i < nwords; i += T) sm.bm[i] = 0u;
@@ -897,9 +999,9 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
   const uint32_t nb = sm.row.run[0];
   if (nb > (uint32_t)kBandCap) return fallback();
   const uint32_t R2 = (uint32_t)p.K - tot_in;
-  for (uint32_t e = tid >> 6; e < nb; e += T / 64) {
-    const float key = wave_exact_key(c.ir, sm.row.band_j[e]);
-    if (lane == 0) sm.row.band_k[e] = f32_order_key(key);
+  for (uint32_t e = tid >> 5; e < nb; e += T / 32) {   // a half-wave per band member
+    const float key = group_exact_key<32>(c.ir, sm.row.band_j[e]);
+    if ((lane & 31) == 0) sm.row.band_k[e] = f32_order_key(key);
   }
   __syncthreads();
   for (uint32_t e = tid; e < nb; e += T) {
@@ -941,7 +1043,8 @@ bool topk_fused_ok(const TopkParams& p) {
 size_t topk_fused_ws_bytes(const TopkParams& p) {
   const int64_t rows = (int64_t)p.B * p.G * p.Nq;
   const int64_t nchunk = (p.ctx + 511) / 512;
-  return (size_t)(rows + (int64_t)p.B * nchunk + rows * nchunk * (1 + 2 * kFzCap)) * 4;
+  const int64_t slots = (int64_t)(p.ctx + kPilotStride - 1) / kPilotStride * kPilotRun;
+  return (size_t)(rows + (int64_t)p.B * nchunk + rows * nchunk * (1 + 2 * kFzCap) + rows * slots) * 4;
 }
 
 hipError_t launch_topk_fused(const TopkParams& p, hipStream_t st) {
@@ -955,7 +1058,11 @@ hipError_t launch_topk_fused(const TopkParams& p, hipStream_t st) {
   w.cand_n = (uint32_t*)(w.kmax + (int64_t)p.B * w.nchunk);
   w.cand_k = w.cand_n + (int64_t)rows * w.nchunk;
   w.cand_j = w.cand_k + (int64_t)rows * w.nchunk * w.cap;
-  hipLaunchKernelGGL(fz_pilot_kernel, dim3(rows), dim3(kTkThreads), 0, st, p, w.tau);
+  const int slots = (p.ctx + kPilotStride - 1) / kPilotStride * kPilotRun;
+  uint32_t* skeys = w.cand_j + (int64_t)rows * w.nchunk * w.cap;
+  hipLaunchKernelGGL(fz_pilot_score_kernel, dim3((slots + kPsThreads - 1) / kPsThreads, p.B, p.G * p.Nq),
+                     dim3(kPsThreads), 0, st, p, skeys, slots);
+  hipLaunchKernelGGL(fz_pilot_select_kernel, dim3(rows), dim3(kTkThreads), 0, st, p, skeys, slots, w.tau);
   IndexerParams ix = p.ix;
   ix.kmax = w.kmax;
   ix.tau = w.tau;
