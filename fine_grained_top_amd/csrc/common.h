@@ -26,14 +26,13 @@ SP_DEV uint32_t f32_to_bf16_rne(float f) {
 
 enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
 
-// Two fp8 E4M3FN codes (bytes 2*HI, 2*HI+1 of w) -> packed bf16 pair (exact:
-// every E4M3FN value is a bf16 value).
+// Two fp8 E4M3FN codes (bytes 2*HI, 2*HI+1 of w) -> packed bf16 pair, exact
+// (every E4M3FN value, subnormals included, is a bf16 value): one gfx950
+// scaled conversion with unit scale.
 template <bool HI>
 SP_DEV uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  auto f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
-  uint32_t a = __float_as_uint(f[0]);
-  uint32_t b = __float_as_uint(f[1]);
-  return (a >> 16) | (b & 0xFFFF0000u);
+  const auto v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 SP_DEV float fp8_to_f32(uint32_t code) {

@@ -73,6 +73,31 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
     }
   }
 
+  // per (slot block, head group) constants of the filter, when they fit in
+  // registers: last visible key of the half-wave's slot row (-1: no row), its
+  // threshold, its LDS counter and the base of its output slots
+  constexpr int G4 = 16 / HPG;
+  constexpr bool HOIST = FILTER && NMB * G4 <= 8;
+  constexpr int NH = HOIST ? NMB * G4 : 1;
+  int hlim[NH], hlrow[NH];
+  float hthr[NH];
+  int64_t hbase[NH];
+  if constexpr (HOIST) {
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int gi = 0; gi < G4; ++gi) {
+        const int v0 = gi * HPG;
+        const int m0 = mbase + 32 * mb + 8 * (v0 >> 2) + 4 * half + (v0 & 3);
+        const int r = m0 >> hshift, g = (m0 & (p.H_I - 1)) / HPG;
+        const int e = mb * G4 + gi;
+        hlim[e] = m0 < M ? L - p.Nq + r : -1;
+        hthr[e] = tsl[(m0 - mbase) & 127];
+        hlrow[e] = g * p.Nq + r;
+        hbase[e] = ((int64_t)((b * p.G_sel + g) * p.Nq + r) * p.nchunk + blockIdx.x) * p.cap;
+      }
+  }
+
   u16x2 kmx = {0, 0};
   constexpr int TPW = kMfmaChunk / 32 / 4;   // tiles per wave
   // raw key bytes for all tiles of this wave
@@ -133,26 +158,45 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
         for (int t = 0; t < HPG; ++t) {
           const int v = gi * HPG + t;
           const float wv = RELU ? wsl[32 * mb + 8 * (v >> 2) + 4 * half + (v & 3)] : 0.f;
-          sc = RELU ? fmaf(wv, fmaxf(acc[v], 0.f), sc) : acc[v];
+          // ReLU on the bit pattern: a negative float is a negative int
+          const float rl = __int_as_float(max(__float_as_int(acc[v]), 0));
+          sc = RELU ? fmaf(wv, rl, sc) : acc[v];
         }
+        // every lane of a half-wave holds the same slot row (m0); keys differ
         const int v0 = gi * HPG;
         const int m0 = mbase + 32 * mb + 8 * (v0 >> 2) + 4 * half + (v0 & 3);
-        if (m0 < M) {
+        if constexpr (!FILTER) {
           const int r = m0 >> hshift, g = (m0 & (p.H_I - 1)) / HPG;
-          if (j <= L - p.Nq + r) {
-            if (!FILTER) {
-              p.scores[b * p.ss[0] + g * p.ss[1] + r * p.ss[2] + j] = sc;
-            } else {
-              const int row = (b * p.G_sel + g) * p.Nq + r;
-              if (sc >= tsl[m0 - mbase]) {
-                const int lrow = g * p.Nq + r;   // fused path: all slots in one block
-                const uint32_t slot = atomicAdd(&lcount[lrow], 1u);
-                if (slot < (uint32_t)p.cap) {
-                  const int64_t o = ((int64_t)row * p.nchunk + blockIdx.x) * p.cap + slot;
-                  p.cand_k[o] = f32_order_key(sc);
-                  p.cand_j[o] = j;
-                }
-              }
+          if (m0 < M && j <= L - p.Nq + r) p.scores[b * p.ss[0] + g * p.ss[1] + r * p.ss[2] + j] = sc;
+        } else {
+          int lim, lrow;
+          float thr;
+          int64_t obase;
+          if constexpr (HOIST) {
+            const int e = mb * G4 + gi;
+            lim = hlim[e];
+            thr = hthr[e];
+            lrow = hlrow[e];
+            obase = hbase[e];
+          } else {
+            const int r = m0 >> hshift, g = (m0 & (p.H_I - 1)) / HPG;
+            lim = m0 < M ? L - p.Nq + r : -1;
+            thr = tsl[(m0 - mbase) & 127];
+            lrow = g * p.Nq + r;
+            obase = ((int64_t)((b * p.G_sel + g) * p.Nq + r) * p.nchunk + blockIdx.x) * p.cap;
+          }
+          // append the half-wave's survivors with one LDS atomic per half-wave
+          const bool cand = j <= lim && sc >= thr;
+          const uint64_t bm = ballot(cand);
+          if (bm) {
+            const uint32_t mh = (uint32_t)(bm >> (32 * half));
+            uint32_t base = 0;
+            if (col == 0 && mh) base = atomicAdd(&lcount[lrow], (uint32_t)__popc(mh));
+            base = (uint32_t)__shfl((int)base, 32 * half, 64);
+            const uint32_t slot = base + (uint32_t)__popc(mh & ((1u << col) - 1u));
+            if (cand && slot < (uint32_t)p.cap) {
+              p.cand_k[obase + slot] = f32_order_key(sc);
+              p.cand_j[obase + slot] = j;
             }
           }
         }

@@ -908,53 +908,54 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   RowCtx c = row_ctx(p, row);
   if (c.n <= p.K) return write_all(p, c, T);
+  // candidate counts of the chunks covering keys 0..p (nch <= T), loaded
+  // together with the inputs of the error bound
+  const int nch = (c.n + 511) / 512;
+  uint32_t my = 0;
+  if (tid < nch) my = w.cand_n[(int64_t)row * w.nchunk + tid];
   c.eps = row_eps(p, c, w.kmax, w.nchunk, 512, sm.red);
   const float eps = c.eps;
   auto fallback = [&]() {
     row_topk_single<T>(p, c, sm.row, [&](int i) { return recompute_score(c.ir, i); });
     if (p.count && tid == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = p.K;
   };
-  // candidate counts of the chunks covering keys 0..p (nch <= T)
-  const int nch = (c.n + 511) / 512;
-  uint32_t my = 0;
-  bool over = false;
-  if (tid < nch) {
-    my = w.cand_n[(int64_t)row * w.nchunk + tid];
-    over = my > (uint32_t)w.cap;
-  }
+  const bool over = my > (uint32_t)w.cap;
   uint32_t n_cand;
   const uint32_t off = block_scan_sum<T>(my, sm.row.sc, n_cand);
   if (tid < nch) sm.coff[tid] = off;
   if (tid == 0) sm.coff[nch] = n_cand;
   const bool any_over = __syncthreads_or(over) != 0;
   if (any_over || n_cand < (uint32_t)p.K || n_cand > (uint32_t)kCandCap) return fallback();
-  // compact into LDS: candidate e belongs to the chunk whose offset range holds
-  // it; the loads of 8 candidates per thread are in flight together
-  constexpr int CB = 8;
-  for (uint32_t e0 = 0; e0 < n_cand; e0 += CB * T) {
-    int64_t src[CB];
+  // compact into LDS: wave w copies chunks w, w + NW, ... (lane l: slot l);
+  // the loads of 32 chunks are in flight together
+  {
+    constexpr int NW = T / 64, CPW = 32;
+    const int wid = tid >> 6;
+    for (int c0 = wid; c0 < nch; c0 += NW * CPW) {
+      uint32_t kk[CPW], jj[CPW];
 #pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      const uint32_t e = e0 + u * T + tid;
-      int lo = 0, hi = nch;                 // coff[lo] <= e < coff[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (sm.coff[mid] <= e) lo = mid; else hi = mid;
+      for (int u = 0; u < CPW; ++u) {
+        const int ch = c0 + u * NW;
+        const int n = ch < nch ? (int)(sm.coff[ch + 1] - sm.coff[ch]) : 0;
+        const int64_t src = ((int64_t)row * w.nchunk + ch) * w.cap + lane;
+        kk[u] = lane < n ? w.cand_k[src] : 0u;
+        jj[u] = lane < n ? w.cand_j[src] : 0u;
       }
-      src[u] = e < n_cand ? ((int64_t)row * w.nchunk + lo) * w.cap + (e - sm.coff[lo]) : -1;
-    }
-    uint32_t kk[CB], jj[CB];
 #pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      kk[u] = src[u] >= 0 ? w.cand_k[src[u]] : 0u;
-      jj[u] = src[u] >= 0 ? w.cand_j[src[u]] : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      const uint32_t e = e0 + u * T + tid;
-      if (e < n_cand) {
-        sm.ck[e] = kk[u];
-        sm.cj[e] = jj[u];
+      for (int u = 0; u < CPW; ++u) {
+        const int ch = c0 + u * NW;
+        if (ch < nch) {
+          const uint32_t o = sm.coff[ch], n = sm.coff[ch + 1] - o;
+          if ((uint32_t)lane < n) {
+            sm.ck[o + lane] = kk[u];
+            sm.cj[o + lane] = jj[u];
+          }
+          for (uint32_t e = lane + 64; e < n; e += 64) {   // more than 64 in a chunk: rare
+            const int64_t src = ((int64_t)row * w.nchunk + ch) * w.cap + e;
+            sm.ck[o + e] = w.cand_k[src];
+            sm.cj[o + e] = w.cand_j[src];
+          }
+        }
       }
     }
   }
@@ -999,9 +1000,9 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
   const uint32_t nb = sm.row.run[0];
   if (nb > (uint32_t)kBandCap) return fallback();
   const uint32_t R2 = (uint32_t)p.K - tot_in;
-  for (uint32_t e = tid >> 5; e < nb; e += T / 32) {   // a half-wave per band member
-    const float key = group_exact_key<32>(c.ir, sm.row.band_j[e]);
-    if ((lane & 31) == 0) sm.row.band_k[e] = f32_order_key(key);
+  for (uint32_t e = tid >> 4; e < nb; e += T / 16) {   // a quarter-wave per band member
+    const float key = group_exact_key<16>(c.ir, sm.row.band_j[e]);
+    if ((lane & 15) == 0) sm.row.band_k[e] = f32_order_key(key);
   }
   __syncthreads();
   for (uint32_t e = tid; e < nb; e += T) {
