@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
   constexpr int NH = HOIST ? NMB * G4 : 1;
   int hlim[NH], hlrow[NH];
   float hthr[NH];
-  int64_t hbase[NH];
+  int llrow = 0;   // leader lanes 2 e + hf (e = mb * G4 + gi): slot row of (mb, gi, half hf)
   if constexpr (HOIST) {
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
@@ -94,9 +94,16 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
         hlim[e] = m0 < M ? L - p.Nq + r : -1;
         hthr[e] = tsl[(m0 - mbase) & 127];
         hlrow[e] = g * p.Nq + r;
-        hbase[e] = ((int64_t)((b * p.G_sel + g) * p.Nq + r) * p.nchunk + blockIdx.x) * p.cap;
       }
+    const int e = lane >> 1, hf = lane & 1;
+    const int mb = e / G4, v0 = (e % G4) * HPG;
+    const int m0 = mbase + 32 * mb + 8 * (v0 >> 2) + 4 * hf + (v0 & 3);
+    llrow = (((m0 & (p.H_I - 1)) / HPG) * p.Nq + (m0 >> hshift)) & 127;
   }
+  // this workgroup's candidate slots: [selection row of the request][cap]
+  const int nrl = p.G_sel * p.Nq;
+  uint32_t* const ck_wg = FILTER ? p.cand_k + ((int64_t)b * p.nchunk + blockIdx.x) * nrl * p.cap : nullptr;
+  uint32_t* const cj_wg = FILTER ? p.cand_j + ((int64_t)b * p.nchunk + blockIdx.x) * nrl * p.cap : nullptr;
 
   u16x2 kmx = {0, 0};
   constexpr int TPW = kMfmaChunk / 32 / 4;   // tiles per wave
@@ -150,9 +157,11 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[mb][s], *(const bf16x8*)&Bw[s], acc, 0, 0, 0);
-      // epilogue: lane holds key j, slots 32*mb + 8*(v/4) + 4*half + v%4
+      // epilogue: lane holds key j, slots 32*mb + 8*(v/4) + 4*half + v%4;
+      // every lane of a half-wave holds the same slot row, keys differ
+      float scv[G4];
 #pragma unroll
-      for (int gi = 0; gi < 16 / HPG; ++gi) {
+      for (int gi = 0; gi < G4; ++gi) {
         float sc = 0.f;
 #pragma unroll
         for (int t = 0; t < HPG; ++t) {
@@ -162,31 +171,63 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
           const float rl = __int_as_float(max(__float_as_int(acc[v]), 0));
           sc = RELU ? fmaf(wv, rl, sc) : acc[v];
         }
-        // every lane of a half-wave holds the same slot row (m0); keys differ
-        const int v0 = gi * HPG;
-        const int m0 = mbase + 32 * mb + 8 * (v0 >> 2) + 4 * half + (v0 & 3);
-        if constexpr (!FILTER) {
+        scv[gi] = sc;
+      }
+      if constexpr (!FILTER) {
+#pragma unroll
+        for (int gi = 0; gi < G4; ++gi) {
+          const int v0 = gi * HPG;
+          const int m0 = mbase + 32 * mb + 8 * (v0 >> 2) + 4 * half + (v0 & 3);
           const int r = m0 >> hshift, g = (m0 & (p.H_I - 1)) / HPG;
-          if (m0 < M && j <= L - p.Nq + r) p.scores[b * p.ss[0] + g * p.ss[1] + r * p.ss[2] + j] = sc;
-        } else {
-          int lim, lrow;
-          float thr;
-          int64_t obase;
-          if constexpr (HOIST) {
+          if (m0 < M && j <= L - p.Nq + r) p.scores[b * p.ss[0] + g * p.ss[1] + r * p.ss[2] + j] = scv[gi];
+        }
+      } else if constexpr (HOIST) {
+        // survivors of all head groups at once: leader lane 2 e + hf reserves
+        // the slots of (group e, half hf) with one LDS atomic for all leaders
+        bool cdv[G4];
+        uint64_t bmv[G4], any = 0;
+#pragma unroll
+        for (int gi = 0; gi < G4; ++gi) {
+          const int e = mb * G4 + gi;
+          cdv[gi] = j <= hlim[e] && scv[gi] >= hthr[e];
+          bmv[gi] = ballot(cdv[gi]);
+          any |= bmv[gi];
+        }
+        if (any) {
+          uint32_t cnt = 0;
+#pragma unroll
+          for (int gi = 0; gi < G4; ++gi) {
             const int e = mb * G4 + gi;
-            lim = hlim[e];
-            thr = hthr[e];
-            lrow = hlrow[e];
-            obase = hbase[e];
-          } else {
-            const int r = m0 >> hshift, g = (m0 & (p.H_I - 1)) / HPG;
-            lim = m0 < M ? L - p.Nq + r : -1;
-            thr = tsl[(m0 - mbase) & 127];
-            lrow = g * p.Nq + r;
-            obase = ((int64_t)((b * p.G_sel + g) * p.Nq + r) * p.nchunk + blockIdx.x) * p.cap;
+            const uint32_t c0 = __popc((uint32_t)bmv[gi]), c1 = __popc((uint32_t)(bmv[gi] >> 32));
+            if ((lane >> 1) == e) cnt = (lane & 1) ? c1 : c0;
           }
-          // append the half-wave's survivors with one LDS atomic per half-wave
-          const bool cand = j <= lim && sc >= thr;
+          uint32_t base = 0;
+          if (cnt) base = atomicAdd(&lcount[llrow], cnt);
+#pragma unroll
+          for (int gi = 0; gi < G4; ++gi) {
+            if (!bmv[gi]) continue;
+            const int e = mb * G4 + gi;
+            const uint32_t b0 = __builtin_amdgcn_readlane(base, 2 * e);
+            const uint32_t b1 = __builtin_amdgcn_readlane(base, 2 * e + 1);
+            const uint32_t below = lanes_below(bmv[gi]) - (half ? (uint32_t)__popc((uint32_t)bmv[gi]) : 0u);
+            const uint32_t slot = (half ? b1 : b0) + below;
+            if (cdv[gi] && slot < (uint32_t)p.cap) {
+              const uint32_t o = (uint32_t)hlrow[e] * (uint32_t)p.cap + slot;
+              ck_wg[o] = f32_order_key(scv[gi]);
+              cj_wg[o] = j;
+            }
+          }
+        }
+      } else {
+        // many head groups: one half-wave append per group
+#pragma unroll
+        for (int gi = 0; gi < G4; ++gi) {
+          const int v0 = gi * HPG;
+          const int m0 = mbase + 32 * mb + 8 * (v0 >> 2) + 4 * half + (v0 & 3);
+          const int r = m0 >> hshift, g = (m0 & (p.H_I - 1)) / HPG;
+          const int lim = m0 < M ? L - p.Nq + r : -1;
+          const int lrow = g * p.Nq + r;
+          const bool cand = j <= lim && scv[gi] >= tsl[(m0 - mbase) & 127];
           const uint64_t bm = ballot(cand);
           if (bm) {
             const uint32_t mh = (uint32_t)(bm >> (32 * half));
@@ -195,8 +236,9 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
             base = (uint32_t)__shfl((int)base, 32 * half, 64);
             const uint32_t slot = base + (uint32_t)__popc(mh & ((1u << col) - 1u));
             if (cand && slot < (uint32_t)p.cap) {
-              p.cand_k[obase + slot] = f32_order_key(sc);
-              p.cand_j[obase + slot] = j;
+              const uint32_t o = (uint32_t)lrow * (uint32_t)p.cap + slot;
+              ck_wg[o] = f32_order_key(scv[gi]);
+              cj_wg[o] = j;
             }
           }
         }
@@ -216,11 +258,8 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
   }
   if (FILTER) {
     const int nrows = p.G_sel * p.Nq;
-    for (int i = threadIdx.x; i < nrows; i += 256) {
-      const int g = i / p.Nq, r = i % p.Nq;
-      const int row = (b * p.G_sel + g) * p.Nq + r;
-      p.cand_n[(int64_t)row * p.nchunk + blockIdx.x] = lcount[i];
-    }
+    for (int i = threadIdx.x; i < nrows; i += 256)
+      p.cand_n[((int64_t)b * p.nchunk + blockIdx.x) * nrows + i] = lcount[i];
   }
 }
 

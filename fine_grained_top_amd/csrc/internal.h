@@ -28,9 +28,9 @@ struct IndexerParams {
   int chunk, nchunk;
   // threshold filter (fused indexer + top-K): keep (key, index) pairs with score >= tau
   const float* tau;        // [B, G_sel, Nq] or null (store every score instead)
-  uint32_t* cand_k;        // [rows][nchunk][cap] order keys
-  uint32_t* cand_j;        // [rows][nchunk][cap] key positions
-  uint32_t* cand_n;        // [rows][nchunk] number found (may exceed cap)
+  uint32_t* cand_k;        // [B][nchunk][G_sel * Nq][cap] order keys
+  uint32_t* cand_j;        // [B][nchunk][G_sel * Nq][cap] key positions
+  uint32_t* cand_n;        // [B][nchunk][G_sel * Nq] number found (may exceed cap)
   int cap;
 };
 bool index_filter_ok(const IndexerParams& p);

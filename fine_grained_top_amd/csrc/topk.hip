@@ -912,7 +912,9 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
   // together with the inputs of the error bound
   const int nch = (c.n + 511) / 512;
   uint32_t my = 0;
-  if (tid < nch) my = w.cand_n[(int64_t)row * w.nchunk + tid];
+  // candidate arrays: [request][chunk][selection row of the request][cap]
+  const int nrl = p.G * p.Nq, rowl = c.g * p.Nq + c.r;
+  if (tid < nch) my = w.cand_n[((int64_t)c.b * w.nchunk + tid) * nrl + rowl];
   c.eps = row_eps(p, c, w.kmax, w.nchunk, 512, sm.red);
   const float eps = c.eps;
   auto fallback = [&]() {
@@ -937,7 +939,7 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
       for (int u = 0; u < CPW; ++u) {
         const int ch = c0 + u * NW;
         const int n = ch < nch ? (int)(sm.coff[ch + 1] - sm.coff[ch]) : 0;
-        const int64_t src = ((int64_t)row * w.nchunk + ch) * w.cap + lane;
+        const int64_t src = (((int64_t)c.b * w.nchunk + ch) * nrl + rowl) * w.cap + lane;
         kk[u] = lane < n ? w.cand_k[src] : 0u;
         jj[u] = lane < n ? w.cand_j[src] : 0u;
       }
@@ -951,7 +953,7 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
             sm.cj[o + lane] = jj[u];
           }
           for (uint32_t e = lane + 64; e < n; e += 64) {   // more than 64 in a chunk: rare
-            const int64_t src = ((int64_t)row * w.nchunk + ch) * w.cap + e;
+            const int64_t src = (((int64_t)c.b * w.nchunk + ch) * nrl + rowl) * w.cap + e;
             sm.ck[o + e] = w.cand_k[src];
             sm.cj[o + e] = w.cand_j[src];
           }
