@@ -140,8 +140,9 @@ constexpr int kVStride = 132;   // LDS row stride of staged V in 16-bit words (2
 struct SplitInfo {
   int nsplit, per;   // splits per row, list entries per split (multiple of 32)
 };
+constexpr int kMaxTilesPerWave = 16;   // 32-entry tiles per wave of one split
 
-template <bool PACKLO>
+template <bool PACKLO, bool PIPE>
 __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int Hg, SplitInfo si,
                                                               float* part) {
   const int split = blockIdx.x;
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int 
   const int t_end = min(a.K, t_begin + si.per);
 
   __shared__ __attribute__((aligned(16))) uint16_t vs[4][32 * kVStride];
-  __shared__ int idxs[4][32];
+  __shared__ int idxs[4][kMaxTilesPerWave * 32];
 
   // Q^T as the B operand: lane holds head c16, dims 32*qq + 8*ks + v
   bf16x8 Qb[4];
@@ -186,33 +187,41 @@ __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int 
   const uint16_t* kbase = (const uint16_t*)a.k.p + b * a.k.s[0] + kvh * a.k.s[1];
   const uint16_t* vbase = (const uint16_t*)a.v.p + b * a.v.s[0] + kvh * a.v.s[1];
 
-  for (int t0 = t_begin + 32 * wid; t0 < t_end; t0 += 128) {
-    // tile of 32 list entries
-    if (lane < 32) {
-      const int t = t0 + lane;
-      int j = t < t_end ? list[t] : -1;
-      if (j > pos) j = -1;
-      idxs[wid][lane] = j;
-    }
-    __builtin_amdgcn_wave_barrier();
-    // K rows for the two 16-key subtiles: row c16 (and 16 + c16), dims 32*qq..+32
-    u32x4 kr[2][4];
+  // this wave's tiles of 32 list entries: t_begin + 32 wid + 128 i; all their
+  // entries are loaded at once
+  const int first = t_begin + 32 * wid;
+  const int ntw = first < t_end ? (t_end - first + 127) / 128 : 0;
+  int* wix = idxs[wid];
+  for (int e = lane; e < ntw * 32; e += 64) {
+    const int t = first + 128 * (e >> 5) + (e & 31);
+    int j = t < t_end ? list[t] : -1;
+    if (j > pos) j = -1;
+    wix[e] = j;
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // K rows for the two 16-key subtiles (row c16 and 16 + c16, dims 32*qq..+32)
+  // and V rows (chunk u: key qq + 4u, 16-byte column c16) of tile i
+  auto issue = [&](int i, u32x4 (&kr)[2][4], u32x4 (&vr)[8]) {
+    const int* ix = wix + 32 * i;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      int j = idxs[wid][16 * st + c16];
+      int j = ix[16 * st + c16];
       j = j < 0 ? 0 : j;
       const uint16_t* kp = kbase + (int64_t)j * a.k.s[2] + 32 * qq;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) kr[st][ks] = *(const u32x4*)(kp + 8 * ks);
     }
-    // V rows: chunk u covers key qq + 4u, 16-byte column c16
-    u32x4 vr[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      int j = idxs[wid][qq + 4 * u];
+      int j = ix[qq + 4 * u];
       j = j < 0 ? 0 : j;
       vr[u] = *(const u32x4*)(vbase + (int64_t)j * a.v.s[2] + 8 * c16);
     }
+  };
+
+  auto compute = [&](int i, const u32x4 (&kr)[2][4], const u32x4 (&vr)[8]) {
+    const int* ix = wix + 32 * i;
     // S^T = K Q^T
     f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -224,8 +233,8 @@ __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int 
     float z[8];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      z[v] = idxs[wid][4 * qq + v] >= 0 ? S0[v] * c : -INFINITY;
-      z[4 + v] = idxs[wid][16 + 4 * qq + v] >= 0 ? S1[v] * c : -INFINITY;
+      z[v] = ix[4 * qq + v] >= 0 ? S0[v] * c : -INFINITY;
+      z[4 + v] = ix[16 + 4 * qq + v] >= 0 ? S1[v] * c : -INFINITY;
     }
     float tm = z[0];
 #pragma unroll
@@ -311,6 +320,27 @@ __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int 
         O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&Alo, *(const bf16x8*)&Bv, O[nt], 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
+  };
+
+  if constexpr (PIPE) {
+    // two register sets: the rows of tile i + 1 are in flight while tile i is
+    // computed (few rows: one workgroup per CU, latency hidden in the wave)
+    u32x4 kA[2][4], vA[8], kB[2][4], vB[8];
+    if (ntw > 0) issue(0, kA, vA);
+    for (int i = 0; i < ntw; i += 2) {
+      if (i + 1 < ntw) issue(i + 1, kB, vB);
+      compute(i, kA, vA);
+      if (i + 1 >= ntw) break;
+      if (i + 2 < ntw) issue(i + 2, kA, vA);
+      compute(i + 1, kB, vB);
+    }
+  } else {
+    // many rows: one register set, latency hidden by occupancy
+    u32x4 kA[2][4], vA[8];
+    for (int i = 0; i < ntw; ++i) {
+      issue(i, kA, vA);
+      compute(i, kA, vA);
+    }
   }
 
   // merge the 4 waves through LDS (reuses the V staging area)
@@ -412,14 +442,19 @@ static bool mfma_index_ok(const AttnParams& a) {
 }
 
 static SplitInfo pick_split(const AttnParams& a, int Hg) {
+  // Few rows (decode): enough splits for one workgroup per CU, but at least
+  // two tiles per wave so that loads overlap compute. Many rows: no split
+  // unless a split would exceed the tiles a wave can list.
   const int rows = a.B * a.Nq * (a.Hq / Hg);
   const int tiles = (a.K + 31) / 32;
-  int want = (2048 + rows - 1) / rows;            // aim for >= 2048 workgroups
-  int maxs = (tiles + 3) / 4;                     // at least 4 tiles (one per wave) per split
-  int ns = want < maxs ? want : maxs;
+  const int minsplit = (tiles + 4 * kMaxTilesPerWave - 1) / (4 * kMaxTilesPerWave);
+  int ns = (256 + rows - 1) / rows;
+  const int maxs = tiles / 8 > 1 ? tiles / 8 : 1;
+  if (ns > maxs) ns = maxs;
   if (ns > 64) ns = 64;
+  if (ns < minsplit) ns = minsplit;
   if (ns < 1) ns = 1;
-  int per_tiles = (tiles + ns - 1) / ns;
+  const int per_tiles = (tiles + ns - 1) / ns;
   SplitInfo si;
   si.per = per_tiles * 32;
   si.nsplit = (a.K + si.per - 1) / si.per;
@@ -442,10 +477,14 @@ hipError_t launch_attention(const AttnParams& a, hipStream_t st) {
     const int rows = a.B * a.Nq * (a.Hq / Hg);
     float* part = (float*)a.ws;
     dim3 grid(si.nsplit, rows);
-    if (Hg <= 8)
-      hipLaunchKernelGGL(attn_index_mfma_kernel<true>, grid, dim3(256), 0, st, a, Hg, si, part);
-    else
-      hipLaunchKernelGGL(attn_index_mfma_kernel<false>, grid, dim3(256), 0, st, a, Hg, si, part);
+    const bool pipe = (int64_t)rows * si.nsplit <= 1024;   // at most ~4 workgroups per CU
+    if (Hg <= 8) {
+      if (pipe) hipLaunchKernelGGL((attn_index_mfma_kernel<true, true>), grid, dim3(256), 0, st, a, Hg, si, part);
+      else hipLaunchKernelGGL((attn_index_mfma_kernel<true, false>), grid, dim3(256), 0, st, a, Hg, si, part);
+    } else {
+      if (pipe) hipLaunchKernelGGL((attn_index_mfma_kernel<false, true>), grid, dim3(256), 0, st, a, Hg, si, part);
+      else hipLaunchKernelGGL((attn_index_mfma_kernel<false, false>), grid, dim3(256), 0, st, a, Hg, si, part);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || si.nsplit == 1) return e;
     hipLaunchKernelGGL(attn_combine_kernel, dim3(rows, Hg), dim3(128), 0, st, a, Hg, si,
