@@ -93,6 +93,20 @@ def algorithmic(wl, inp, hp, fused):
     return out
 
 
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of a stage from the committed counter record of
+    this workload, or None when there is none or the kernels changed since."""
+    from fine_grained_top_amd import pmc_traffic
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("sources") != pmc_traffic.sources_hash() or stage not in rec.get("stages", {}):
+        return None
+    return rec["stages"][stage]["bytes"]
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -199,6 +213,7 @@ def main():
     if dom in alg:
         roof = roofline_of(alg[dom], stage_ms[dom])
         roof["kernel"] = dom
+        roof["traffic"] = measured_traffic(wl.name, dom)
     per_stage = {}
     for name, ms in stage_ms.items():
         e = {"ms": round(ms, 5)}
@@ -262,7 +277,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if wl.dtype == "f32" else "bf16",
         "data": "synthetic",
         "path": "fused indexer+top-K" if fused else "separate indexer and top-K calls",
         "config": {"workload": wl.name, "B": wl.B, "ctx_capacity": wl.N, "Nq": wl.Nq, "Hq": wl.Hq,
