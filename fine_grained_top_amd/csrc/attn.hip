@@ -462,6 +462,7 @@ static SplitInfo pick_split(const AttnParams& a, int Hg) {
 }
 
 size_t attn_ws_bytes(const AttnParams& a) {
+  if (attn_blocks_ok(a)) return attn_blocks_ws_bytes(a);
   if (!mfma_index_ok(a)) return 0;
   const int Hg = gather_group(a);
   const SplitInfo si = pick_split(a, Hg);
@@ -491,6 +492,7 @@ hipError_t launch_attention(const AttnParams& a, hipStream_t st) {
                        (const float*)part);
     return hipGetLastError();
   }
+  if (attn_blocks_ok(a)) return launch_attn_blocks(a, st);
   if (attn_tile_ok(a)) return launch_attn_tile(a, st);
   dim3 grid(a.Nq, a.Hq, a.B);
   hipLaunchKernelGGL(attn_generic_kernel, grid, dim3(64), 0, st, a);

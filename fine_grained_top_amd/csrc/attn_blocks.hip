@@ -1,0 +1,480 @@
+// Block-centric attention for per-row selected blocks (BLOCKS mode), bf16,
+// d = 128.
+//
+// With block choices that differ per row and head, the union of the blocks
+// of a few rows covers most of the context, so a query-tiled kernel would do
+// nearly dense work. Here the work is organized by key block instead: the
+// rows that chose a block are gathered and attend to that block once, and
+// each row's partial results are merged with its window part by their
+// softmax statistics (the decomposition MoBA uses: attention over a union of
+// disjoint key sets is the log-sum-exp merge of the parts).
+//
+//   count   per 256-row chunk: which (row, slot) entries contribute (valid,
+//           not a repeat of an earlier slot, some key before the row's window
+//           and not after the row), a per-block histogram and each entry's
+//           rank within its chunk's bin
+//   scan    per (request, head): per-chunk offsets of every block's list,
+//           list bases, 64-row work items per block and their prefix
+//   table   the flat list of work items (request-head, block, 64-row chunk)
+//   scatter each contributing (row, slot) into its block's row list
+//   attn    one workgroup per work item: the block's keys staged in LDS, the
+//           item's rows gathered, S^T = K Q^T and O += P V on MFMA, partial
+//           (m, l, O) per (row, slot)
+//   window  the tiled kernel in window mode (O and LSE of the window part)
+//   combine per row: merge the window part with the block partials
+//
+// Keys in both a chosen block and the row's window belong to the window part
+// only, so every visible key is counted once.
+#include "common.h"
+#include "internal.h"
+
+namespace sp {
+
+constexpr int kBcRows = 256;     // rows per count/scatter workgroup
+constexpr int kBcTM = 64;        // rows per attention work item
+constexpr int kBcMaxBlocks = 2048;
+constexpr int kBcKs = 136;       // K tile row stride in 16-bit words
+constexpr int kBcVs = 72;        // V^T row stride in 16-bit words
+constexpr float kBcLog2e = 1.4426950408889634f;
+constexpr float kBcLn2 = 0.6931471805599453f;
+
+struct BcWs {
+  int32_t* rank;      // [B*Hq][Nq][nb]: rank within the chunk's bin, -1 = no contribution
+  int32_t* hist;      // [B*Hq][nch][nbk]: chunk counts, then exclusive offsets over chunks
+  int32_t* tot;       // [B*Hq][nbk]: rows per block
+  int32_t* lbase;     // [B*Hq][nbk]: list base of each block
+  int32_t* ioff;      // [B*Hq][nbk]: first work item of each block within its (request, head)
+  int32_t* icnt;      // [B*Hq]: work items per (request, head)
+  int32_t* nitems;    // [1]: total work items
+  uint32_t* item_bk;  // [maxitems]: (request, head) * nbk + block
+  uint32_t* item_c;   // [maxitems]: 64-row chunk of the block's list
+  uint32_t* list;     // [B*Hq][Nq*nb]: row | slot << 24
+  float* part;        // [B*Hq][Nq][nb][130]: O (128), m, l
+  float* lse_w;       // [B*Hq][Nq]: LSE of the window part
+  int nch, nbk, maxitems;
+};
+
+static int bc_max_items(const AttnParams& a, int nbk) {
+  const int64_t bh = (int64_t)a.B * a.Hq;
+  return (int)(bh * (((int64_t)a.Nq * a.K + kBcTM - 1) / kBcTM + nbk));
+}
+
+static BcWs bc_layout(const AttnParams& a, void* base, size_t* bytes) {
+  BcWs w{};
+  w.nbk = (a.ctx + a.bs - 1) / a.bs;
+  w.nch = (a.Nq + kBcRows - 1) / kBcRows;
+  w.maxitems = bc_max_items(a, w.nbk);
+  const int64_t bh = (int64_t)a.B * a.Hq;
+  const int64_t ent = bh * a.Nq * a.K;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    char* p = (char*)base + off;
+    off += (n + 255) & ~(size_t)255;
+    return (void*)p;
+  };
+  w.part = (float*)take((size_t)ent * 130 * sizeof(float));
+  w.rank = (int32_t*)take((size_t)ent * 4);
+  w.list = (uint32_t*)take((size_t)ent * 4);
+  w.hist = (int32_t*)take((size_t)bh * w.nch * w.nbk * 4);
+  w.tot = (int32_t*)take((size_t)bh * w.nbk * 4);
+  w.lbase = (int32_t*)take((size_t)bh * w.nbk * 4);
+  w.ioff = (int32_t*)take((size_t)bh * w.nbk * 4);
+  w.icnt = (int32_t*)take((size_t)bh * 4);
+  w.nitems = (int32_t*)take(4);
+  w.item_bk = (uint32_t*)take((size_t)w.maxitems * 4);
+  w.item_c = (uint32_t*)take((size_t)w.maxitems * 4);
+  w.lse_w = (float*)take((size_t)bh * a.Nq * 4);
+  if (bytes) *bytes = off;
+  return w;
+}
+
+bool attn_blocks_ok(const AttnParams& a) {
+  return a.mode == 3 && attn_tile_ok(a) && (a.ctx + a.bs - 1) / a.bs <= kBcMaxBlocks && a.K <= 255 &&
+         a.Nq < (1 << 24);
+}
+
+size_t attn_blocks_ws_bytes(const AttnParams& a) {
+  size_t bytes = 0;
+  bc_layout(a, nullptr, &bytes);
+  return bytes;
+}
+
+// does slot s of a row contribute: a valid block, not a repeat of an earlier
+// slot, with some key at or before the row's position and before its window
+SP_DEV bool bc_contributes(const AttnParams& a, const int32_t* sel, int s, int nbk, int p, int wstart) {
+  const int blk = sel[s * a.sels[3]];
+  if (blk < 0 || blk >= nbk) return false;
+  for (int s2 = 0; s2 < s; ++s2)
+    if (sel[s2 * a.sels[3]] == blk) return false;
+  const int lo = blk * a.bs;
+  const int hi = min(min(lo + a.bs - 1, p), wstart - 1);
+  return hi >= lo;
+}
+
+__global__ __launch_bounds__(kBcRows) void bc_count_kernel(AttnParams a, BcWs w) {
+  __shared__ int hist[kBcMaxBlocks];
+  const int ch = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int bh = b * a.Hq + h;
+  for (int i = threadIdx.x; i < w.nbk; i += kBcRows) hist[i] = 0;
+  __syncthreads();
+  const int r = ch * kBcRows + threadIdx.x;
+  const int L = min(a.ctx_len ? a.ctx_len[b] : a.ctx, a.ctx);
+  if (r < a.Nq) {
+    const int p = L - a.Nq + r;
+    const int wstart = p - a.window + 1;
+    const int32_t* sel = a.sel + b * a.sels[0] + h * a.sels[1] + (int64_t)r * a.sels[2];
+    int32_t* rk = w.rank + ((int64_t)bh * a.Nq + r) * a.K;
+    for (int s = 0; s < a.K; ++s) {
+      int v = -1;
+      if (p >= 0 && bc_contributes(a, sel, s, w.nbk, p, wstart)) v = atomicAdd(&hist[sel[s * a.sels[3]]], 1);
+      rk[s] = v;
+    }
+  }
+  __syncthreads();
+  int32_t* hg = w.hist + ((int64_t)bh * w.nch + ch) * w.nbk;
+  for (int i = threadIdx.x; i < w.nbk; i += kBcRows) hg[i] = hist[i];
+}
+
+// per (request, head): chunk offsets per block, totals, list bases, work items
+__global__ __launch_bounds__(256) void bc_scan_kernel(AttnParams a, BcWs w) {
+  constexpr int T = 256;
+  __shared__ int sc[T];
+  __shared__ int sci[T];
+  const int bh = blockIdx.x;
+  const int per = (w.nbk + T - 1) / T;           // <= 8 blocks per thread
+  int tot[8], items[8];
+  int st = 0, si = 0;
+  for (int u = 0; u < per; ++u) {
+    const int blk = threadIdx.x * per + u;
+    int run = 0;
+    if (blk < w.nbk) {
+      for (int c = 0; c < w.nch; ++c) {
+        int32_t* hp = w.hist + ((int64_t)bh * w.nch + c) * w.nbk + blk;
+        const int v = *hp;
+        *hp = run;
+        run += v;
+      }
+    }
+    tot[u] = run;
+    items[u] = (run + kBcTM - 1) / kBcTM;
+    st += run;
+    si += items[u];
+  }
+  sc[threadIdx.x] = st;
+  sci[threadIdx.x] = si;
+  __syncthreads();
+  // exclusive prefix over threads (256 entries; one thread does it)
+  if (threadIdx.x == 0) {
+    int r0 = 0, r1 = 0;
+    for (int t = 0; t < T; ++t) {
+      const int v0 = sc[t], v1 = sci[t];
+      sc[t] = r0;
+      sci[t] = r1;
+      r0 += v0;
+      r1 += v1;
+    }
+    w.icnt[bh] = r1;
+  }
+  __syncthreads();
+  int lb = sc[threadIdx.x], io = sci[threadIdx.x];
+  for (int u = 0; u < per; ++u) {
+    const int blk = threadIdx.x * per + u;
+    if (blk < w.nbk) {
+      w.tot[(int64_t)bh * w.nbk + blk] = tot[u];
+      w.lbase[(int64_t)bh * w.nbk + blk] = lb;
+      w.ioff[(int64_t)bh * w.nbk + blk] = io;
+    }
+    lb += tot[u];
+    io += items[u];
+  }
+}
+
+// the flat work-item table; every (request, head) adds the items before it
+__global__ __launch_bounds__(256) void bc_table_kernel(AttnParams a, BcWs w) {
+  __shared__ int base;
+  const int bh = blockIdx.x;
+  if (threadIdx.x == 0) {
+    int s = 0;
+    for (int i = 0; i < bh; ++i) s += w.icnt[i];
+    base = s;
+    if (bh == (int)gridDim.x - 1) *w.nitems = s + w.icnt[bh];
+  }
+  __syncthreads();
+  for (int blk = threadIdx.x; blk < w.nbk; blk += 256) {
+    const int n = (w.tot[(int64_t)bh * w.nbk + blk] + kBcTM - 1) / kBcTM;
+    const int o = base + w.ioff[(int64_t)bh * w.nbk + blk];
+    for (int c = 0; c < n; ++c) {
+      w.item_bk[o + c] = (uint32_t)(bh * w.nbk + blk);
+      w.item_c[o + c] = (uint32_t)c;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBcRows) void bc_scatter_kernel(AttnParams a, BcWs w) {
+  const int ch = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int bh = b * a.Hq + h;
+  const int r = ch * kBcRows + threadIdx.x;
+  if (r >= a.Nq) return;
+  const int32_t* sel = a.sel + b * a.sels[0] + h * a.sels[1] + (int64_t)r * a.sels[2];
+  const int32_t* rk = w.rank + ((int64_t)bh * a.Nq + r) * a.K;
+  const int32_t* hg = w.hist + ((int64_t)bh * w.nch + ch) * w.nbk;
+  uint32_t* lst = w.list + (int64_t)bh * a.Nq * a.K;
+  for (int s = 0; s < a.K; ++s) {
+    const int v = rk[s];
+    if (v < 0) continue;
+    const int blk = sel[s * a.sels[3]];
+    const int pos = w.lbase[(int64_t)bh * w.nbk + blk] + hg[blk] + v;
+    lst[pos] = (uint32_t)r | ((uint32_t)s << 24);
+  }
+}
+
+struct BcSmem {
+  uint16_t ks[64 * kBcKs];
+  uint16_t vt[128 * kBcVs];
+};
+
+// One work item: up to 64 rows that chose block blk of (request, head) bh.
+// Wave wv holds rows 16 wv .. 16 wv + 15 of the item (lane column c16).
+__global__ __launch_bounds__(256) void bc_attn_kernel(AttnParams a, BcWs w) {
+  if ((int)blockIdx.x >= *w.nitems) return;
+  __shared__ __attribute__((aligned(16))) BcSmem sm;
+  const uint32_t bk = w.item_bk[blockIdx.x];
+  const int c = (int)w.item_c[blockIdx.x];
+  const int bh = bk / w.nbk, blk = bk % w.nbk;
+  const int b = bh / a.Hq, h = bh % a.Hq;
+  const int kvh = h / (a.Hq / a.Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int qq = lane >> 4, c16 = lane & 15;
+  const int L = min(a.ctx_len ? a.ctx_len[b] : a.ctx, a.ctx);
+  const int nrow = min(kBcTM, w.tot[bk] - kBcTM * c);
+  const uint32_t* lst = w.list + (int64_t)bh * a.Nq * a.K + w.lbase[bk] + kBcTM * c;
+
+  // this lane's row
+  const int ri = 16 * wid + c16;
+  const bool rvalid = ri < nrow;
+  const uint32_t ent = rvalid ? lst[ri] : 0u;
+  const int r = (int)(ent & 0xFFFFFFu);
+  const int p = L - a.Nq + r;
+  const int wstart = p - a.window + 1;
+  bf16x8 Qb[4];
+  if (rvalid) {
+    const uint16_t* qp = (const uint16_t*)a.q.p + b * a.q.s[0] + h * a.q.s[1] + (int64_t)r * a.q.s[2] + 32 * qq;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) Qb[s] = *(const bf16x8*)(qp + 8 * s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) Qb[s] = (bf16x8){};
+  }
+  const float cs = a.scale * kBcLog2e;
+  float m = -INFINITY, l = 0.f;
+  f32x4 O[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) O[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const uint16_t* kbase = (const uint16_t*)a.k.p + b * a.k.s[0] + kvh * a.k.s[1];
+  const uint16_t* vbase = (const uint16_t*)a.v.p + b * a.v.s[0] + kvh * a.v.s[1];
+  const int klo = blk * a.bs, khi = min(klo + a.bs, L);   // keys [klo, khi) of the block
+
+  for (int j0 = klo; j0 < khi; j0 += 64) {
+    // stage 64 keys: chunk cc = tid + 256u -> key cc/16, 16-byte column cc%16
+    u32x4 pk[4], pv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int cc = tid + 256 * u;
+      int j = j0 + (cc >> 4);
+      j = j < khi ? j : khi - 1;
+      pk[u] = *(const u32x4*)(kbase + (int64_t)j * a.k.s[2] + 8 * (cc & 15));
+      pv[u] = *(const u32x4*)(vbase + (int64_t)j * a.v.s[2] + 8 * (cc & 15));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int cc = tid + 256 * u;
+      const int key = cc >> 4, col = cc & 15;
+      *(u32x4*)&sm.ks[key * kBcKs + 8 * col] = pk[u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sm.vt[(8 * col + 2 * e) * kBcVs + key] = (uint16_t)(pv[u][e] & 0xFFFFu);
+        sm.vt[(8 * col + 2 * e + 1) * kBcVs + key] = (uint16_t)(pv[u][e] >> 16);
+      }
+    }
+    __syncthreads();
+    if (__ballot(rvalid)) {
+      f32x4 S[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        S[st] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        const uint16_t* kr = &sm.ks[(16 * st + c16) * kBcKs + 32 * qq];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          S[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(kr + 8 * s), Qb[s], S[st], 0, 0, 0);
+      }
+      // lane's keys j = j0 + 16 st + 4 qq + v for its row (column c16): in the
+      // block, at or before the row, before its window
+      float z[16];
+      float tm = -INFINITY;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int j = j0 + 16 * st + 4 * qq + v;
+          const bool vis = rvalid && j < khi && j <= p && j < wstart;
+          const float zz = vis ? S[st][v] * cs : -INFINITY;
+          z[4 * st + v] = zz;
+          tm = fmaxf(tm, zz);
+        }
+      tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
+      tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+      const float mn = fmaxf(m, tm);
+      float alpha = 1.f, ps = 0.f;
+      if (mn > -INFINITY) {
+        alpha = exp2f(m - mn);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          z[i] = exp2f(z[i] - mn);
+          ps += z[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z[i] = 0.f;
+      }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      l = l * alpha + ps;
+      m = mn;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float av = __shfl(alpha, 4 * qq + v, 64);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) O[nt][v] *= av;
+      }
+      // O += P V, two halves of 32 keys; k = 8 qq + v <-> keys 4 qq + v (v < 4), 16 + 4 qq + (v - 4)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        u32x4 Ahi, Alo;
+#pragma unroll
+        for (int v2 = 0; v2 < 4; ++v2) {
+          const int i0 = (v2 < 2) ? (8 * hf + 2 * v2) : (8 * hf + 4 + 2 * (v2 - 2));
+          const float x0 = z[i0], x1 = z[i0 + 1];
+          const uint32_t h0b = f32_to_bf16_rne(x0), h1b = f32_to_bf16_rne(x1);
+          Ahi[v2] = h0b | (h1b << 16);
+          Alo[v2] = f32_to_bf16_rne(x0 - bf16_to_f32(h0b)) | (f32_to_bf16_rne(x1 - bf16_to_f32(h1b)) << 16);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const uint16_t* vr = &sm.vt[(16 * nt + c16) * kBcVs + 32 * hf + 4 * qq];
+          const u32x2 lo4 = *(const u32x2*)vr;
+          const u32x2 hi4 = *(const u32x2*)(vr + 16);
+          const u32x4 Bv = (u32x4){lo4[0], lo4[1], hi4[0], hi4[1]};
+          O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&Ahi, *(const bf16x8*)&Bv, O[nt], 0, 0, 0);
+          O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&Alo, *(const bf16x8*)&Bv, O[nt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // partial (O, m, l) of each row: lane holds dims 16 nt + c16 of rows 4 qq + v of this wave
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int rr = 4 * qq + v;                   // row within the wave (lane column rr holds its state)
+    const float lr = __shfl(l, rr, 64);
+    const float mr = __shfl(m, rr, 64);
+    const uint32_t er = (uint32_t)__shfl((int)ent, rr, 64);
+    if (16 * wid + rr >= nrow) continue;
+    const int rw = (int)(er & 0xFFFFFFu), sw = (int)(er >> 24);
+    float* pp = w.part + (((int64_t)bh * a.Nq + rw) * a.K + sw) * 130;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) pp[16 * nt + c16] = O[nt][v];
+    if (c16 == 0) {
+      pp[128] = mr;
+      pp[129] = lr;
+    }
+  }
+}
+
+// per row (128 threads, two rows per workgroup): merge the window part (O
+// normalized, LSE) with the block partials; the partials' statistics are
+// loaded by one thread per slot, the output columns by one thread per column
+// with 16 slots' loads in flight
+__global__ __launch_bounds__(256) void bc_combine_kernel(AttnParams a, BcWs w) {
+  __shared__ float sm_m[2][256], sm_l[2][256];
+  const int half = threadIdx.x >> 7;
+  const int64_t row = (int64_t)blockIdx.x * 2 + half;
+  const int dd = threadIdx.x & 127;
+  const int64_t nrows = (int64_t)a.B * a.Hq * a.Nq;
+  const bool live = row < nrows;
+  const int K = a.K;
+  if (live)
+    for (int s = dd; s < K; s += 128) {
+      float ms = -INFINITY, ls = 0.f;
+      if (w.rank[row * K + s] >= 0) {
+        const float* pp = w.part + (row * K + s) * 130;
+        ms = pp[128];
+        ls = pp[129];
+      }
+      sm_m[half][s] = ms;
+      sm_l[half][s] = ls;
+    }
+  __syncthreads();
+  if (!live) return;
+  const int r = (int)(row % a.Nq), bh = (int)(row / a.Nq);
+  const int h = bh % a.Hq, b = bh / a.Hq;
+  float* o = a.o + b * a.os[0] + h * a.os[1] + (int64_t)r * a.os[2];
+  const float lw = w.lse_w[row];
+  // window part as (m, l, O) in base-2 units: m = LSE / ln 2, l = 1, O normalized
+  const float mw = lw > -INFINITY ? lw * kBcLog2e : -INFINITY;
+  float M = mw;
+  for (int s = 0; s < K; ++s) M = fmaxf(M, sm_m[half][s]);
+  float Ls = 0.f, Os = 0.f;
+  if (M > -INFINITY) {
+    if (mw > -INFINITY) {
+      const float f = exp2f(mw - M);
+      Ls = f;
+      Os = o[dd] * f;
+    }
+    const float* base = w.part + row * K * 130 + dd;
+    for (int s0 = 0; s0 < K; s0 += 16) {
+      float x[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int s = s0 + u;
+        x[u] = (s < K && sm_m[half][s] > -INFINITY) ? base[(int64_t)s * 130] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int s = s0 + u;
+        if (s < K && sm_m[half][s] > -INFINITY) {
+          const float f = exp2f(sm_m[half][s] - M);
+          Ls += sm_l[half][s] * f;
+          Os += x[u] * f;
+        }
+      }
+    }
+  }
+  o[dd] = Ls > 0.f ? Os / Ls : 0.f;
+  if (a.lse && dd == 0) a.lse[row] = Ls > 0.f ? (M + log2f(Ls)) * kBcLn2 : -INFINITY;
+}
+
+hipError_t launch_attn_blocks(const AttnParams& a0, hipStream_t st) {
+  AttnParams a = a0;
+  size_t need = 0;
+  BcWs w = bc_layout(a, a.ws, &need);
+  const dim3 gc(w.nch, a.Hq, a.B);
+  const int bh = a.B * a.Hq;
+  hipLaunchKernelGGL(bc_count_kernel, gc, dim3(kBcRows), 0, st, a, w);
+  hipLaunchKernelGGL(bc_scan_kernel, dim3(bh), dim3(256), 0, st, a, w);
+  hipLaunchKernelGGL(bc_table_kernel, dim3(bh), dim3(256), 0, st, a, w);
+  hipLaunchKernelGGL(bc_scatter_kernel, gc, dim3(kBcRows), 0, st, a, w);
+  hipLaunchKernelGGL(bc_attn_kernel, dim3(w.maxitems), dim3(256), 0, st, a, w);
+  // window part: the tiled kernel, its LSE into the workspace
+  AttnParams aw = a;
+  aw.mode = 2;
+  aw.n_global = 0;
+  aw.lse = w.lse_w;
+  hipError_t e = launch_attn_tile(aw, st);
+  if (e != hipSuccess) return e;
+  const int64_t nrows = (int64_t)bh * a.Nq;
+  hipLaunchKernelGGL(bc_combine_kernel, dim3((unsigned)((nrows + 1) / 2)), dim3(256), 0, st, a, w);
+  return hipGetLastError();
+}
+
+}  // namespace sp

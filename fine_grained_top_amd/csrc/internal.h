@@ -97,5 +97,8 @@ size_t attn_ws_bytes(const AttnParams& p);
 hipError_t launch_attention(const AttnParams& p, hipStream_t st);
 bool attn_tile_ok(const AttnParams& p);
 hipError_t launch_attn_tile(const AttnParams& p, hipStream_t st);
+bool attn_blocks_ok(const AttnParams& p);
+size_t attn_blocks_ws_bytes(const AttnParams& p);
+hipError_t launch_attn_blocks(const AttnParams& p, hipStream_t st);
 
 }  // namespace sp

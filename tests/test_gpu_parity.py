@@ -400,3 +400,52 @@ def test_index_mode_equals_window_global_mode():
     diff = float((o - o_pattern).abs().max())
     say(f"  index vs pattern max diff {diff:.3e}")
     assert diff <= 2e-3
+
+
+@pytest.mark.parametrize("bs", [64, 32, 128])
+def test_blocks_attention_edge_lists(bs):
+    """BLOCKS mode with hand-made lists: repeated blocks, padding, blocks after
+    the row, blocks inside the window, rows whose blocks all lie in the window,
+    ragged lengths, several requests and heads; every row against the oracle's
+    masked attention over the union of the blocks and the window."""
+    import oracle as orc
+    sp = S()
+    say(f"[gpu] blocks attention edge lists bs={bs}")
+    g = torch.Generator().manual_seed(21)
+    B, Hq, Hkv, Nq, d, ctx, nb, w = 2, 4, 2, 300, 128, 1200, 6, 100
+    q = torch.randn(B, Hq, Nq, d, generator=g).bfloat16()
+    k = torch.randn(B, Hkv, ctx, d, generator=g).bfloat16()
+    v = torch.randn(B, Hkv, ctx, d, generator=g).bfloat16()
+    ctx_len = [1200, 777]
+    nbk = ctx // bs
+    rng = np.random.default_rng(22)
+    blk = rng.integers(-1, nbk, size=(B, Hq, Nq, nb)).astype(np.int32)
+    blk[..., 1] = blk[..., 0]                                  # a repeated block
+    blk[0, 0, :, :] = nbk - 1                                   # after most rows' positions
+    blk[1, 1, ::3, 2:] = -1                                     # padding
+    for r in range(Nq):                                         # blocks inside the window
+        p = ctx_len[1] - Nq + r
+        blk[1, 2, r, 3] = max(0, p // bs)
+    qt, kt, vt = q.cuda(), k.cuda(), v.cuda()
+    o = torch.empty(B, Hq, Nq, d, device="cuda")
+    lse = torch.empty(B, Hq, Nq, device="cuda")
+    cl = torch.tensor(ctx_len, dtype=torch.int32, device="cuda")
+    sel = sp.selection(sp.SEL_BLOCKS, torch.from_numpy(blk).cuda(), window=w, block_size=bs)
+    sp.spattn_sparse_attn_fwd(qt, kt, vt, cl, 0.0, sel, o, lse)
+    torch.cuda.synchronize()
+    O, LS = o.cpu().numpy(), lse.cpu().numpy()
+    q64, k64, v64 = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    worst = 0.0
+    for b in range(B):
+        L = ctx_len[b]
+        for h in range(Hq):
+            kvh = h // (Hq // Hkv)
+            for r in range(Nq):
+                p = L - Nq + r
+                blocks = [int(x) for x in blk[b, h, r] if 0 <= x < nbk]
+                S_ = orc.blocks_set(blocks, p, bs, w)
+                Oo, Lo = orc.masked_attention(q64[b, h, r][None], k64[b, kvh, : p + 1], v64[b, kvh, : p + 1], S_,
+                                              1.0 / math.sqrt(d))
+                worst = max(worst, float(np.abs(O[b, h, r] - Oo[0]).max()), abs(float(LS[b, h, r] - Lo[0])))
+    say(f"  max |O - O_oracle|, |LSE - LSE_oracle| = {worst:.3e}")
+    assert worst <= 2e-3
