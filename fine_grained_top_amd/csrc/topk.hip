@@ -247,12 +247,14 @@ struct R2Smem {
 // band is too wide for the short list (caller redoes the row).
 template <int T>
 SP_DEV bool resolve_candidates(const TopkParams& p, RowCtx& c, RowSmem& rs, uint32_t* ck, uint32_t* cj,
-                               uint32_t* bm, uint32_t n_cand, uint32_t R, uint32_t wlo, uint32_t whi) {
+                               uint32_t* bm, uint32_t n_cand, uint32_t R, uint32_t wlo, uint32_t whi,
+                               uint32_t tlo = 0u, uint32_t thi = 0xFFFFFFFFu) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int bits = 32 - __builtin_clz((whi - wlo) | 1u);
   uint32_t t, above;
   radix_select<T>((int)n_cand, R, [&](int i, uint32_t& k) { k = ck[i]; return true; }, rs.hist, rs.sc, t, above,
                   wlo, bits);
+  if (t < tlo || t > thi) return false;   // the band might reach past the window
   const float tf = order_key_f32(t);
   uint32_t klo, khi;
   band_limits(p, c, tf, tf, tf, klo, khi);
@@ -278,9 +280,9 @@ SP_DEV bool resolve_candidates(const TopkParams& p, RowCtx& c, RowSmem& rs, uint
   if (nb > (uint32_t)kBandCap) return false;
   const uint32_t R2 = R - tot_in;
   if (p.certified) {
-    for (uint32_t e = tid >> 6; e < nb; e += T / 64) {
-      const float key = wave_exact_key(c.ir, rs.band_j[e]);
-      if (lane == 0) rs.band_k[e] = f32_order_key(key);
+    for (uint32_t e = tid >> 4; e < nb; e += T / 16) {   // a quarter-wave per band member
+      const float key = group_exact_key<16>(c.ir, rs.band_j[e]);
+      if ((lane & 15) == 0) rs.band_k[e] = f32_order_key(key);
     }
     __syncthreads();
   }
@@ -320,6 +322,76 @@ SP_DEV void emit_bitmap(const TopkParams& p, const RowCtx& c, RowSmem& rs, const
   if (p.count && tid == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = (int)min(total, (uint32_t)p.K);
 }
 
+// Order-key window [tlo, thi] that holds the rhi-th and the rlo-th largest of
+// the valid keys in k[0..m) (order key 0 marks an unused slot; rhi <= rlo <=
+// number of valid keys): one pass of a 4096-bin histogram over the keys'
+// range; thi is the upper edge of the bin of rank rhi, tlo the lower edge of
+// the bin of rank rlo.
+template <int T>
+SP_DEV void sample_window(const uint32_t* k, int m, uint32_t rhi, uint32_t rlo, uint32_t* hist, uint32_t* sc,
+                          uint32_t& tlo, uint32_t& thi) {
+  constexpr int NW = T / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int i = tid; i < m; i += T) {
+    const uint32_t v = k[i];
+    if (v != 0u) {
+      kmin = min(kmin, v);
+      kmax = max(kmax, v);
+    }
+  }
+  for (int i = tid; i < 4096; i += T) hist[i] = 0u;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  }
+  if (lane == 0) {
+    sc[wid] = kmin;
+    sc[NW + wid] = kmax;
+  }
+  __syncthreads();
+  kmin = 0xFFFFFFFFu;
+  kmax = 0u;
+  for (int w = 0; w < NW; ++w) {
+    kmin = min(kmin, sc[w]);
+    kmax = max(kmax, sc[NW + w]);
+  }
+  const int bits = 32 - __builtin_clz((kmax - kmin) | 1u);
+  const int sh = bits > 12 ? bits - 12 : 0;
+  for (int i = tid; i < m; i += T) {
+    const uint32_t v = k[i];
+    if (v != 0u) atomicAdd(&hist[(v - kmin) >> sh], 1u);
+  }
+  __syncthreads();
+  // counts from the top: thread tid owns bins [8 tid, 8 tid + 8)
+  constexpr int per = 4096 / T;
+  uint32_t hb[per], cnt = 0;
+#pragma unroll
+  for (int e = 0; e < per; ++e) {
+    hb[e] = hist[per * tid + e];
+    cnt += hb[e];
+  }
+  uint32_t tot;
+  const uint32_t below = block_scan_sum<T>(cnt, sc, tot);
+  const uint32_t above0 = tot - below - cnt;
+  uint32_t* res = hist;   // the two results, after everyone has read the bins
+  __syncthreads();
+  uint32_t acc = above0;
+#pragma unroll
+  for (int e = per - 1; e >= 0; --e) {
+    const uint32_t nxt = acc + hb[e];
+    const uint32_t bin = (uint32_t)(per * tid + e);
+    if (acc < rhi && rhi <= nxt) res[0] = (uint32_t)min((uint64_t)kmax, (uint64_t)kmin + (((uint64_t)bin + 1) << sh) - 1);
+    if (acc < rlo && rlo <= nxt) res[1] = kmin + (bin << sh);
+    acc = nxt;
+  }
+  __syncthreads();
+  thi = res[0];
+  tlo = res[1];
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(kTkThreads) void topk_row2_kernel(TopkParams p) {
   constexpr int T = kTkThreads;
   __shared__ R2Smem sm;
@@ -327,11 +399,85 @@ __global__ __launch_bounds__(kTkThreads) void topk_row2_kernel(TopkParams p) {
   const int tid = threadIdx.x;
   if (c.n <= p.K) return write_all(p, c, T);
   const int n = c.n;
-  // pass 1: histogram of the top 12 bits
-  for (int i = tid; i < 4096; i += T) sm.row.hist[i] = 0;
   const int nwords = (n + 31) >> 5;
-  for (int i = tid; i < nwords; i += T) sm.bm[i] = 0;
-  if (tid == 0) sm.misc[0] = 0;
+  const uint32_t K = (uint32_t)p.K;
+
+  // pass 2 for a window [wlo, whi] (order keys, already widened by the band):
+  // bitmap of the keys above it, short list of the keys inside it, exact
+  // resolution; false when the window does not hold the threshold with its
+  // band (t must lie in [tlo, thi]) or the list overflows
+  auto pass2 = [&](uint32_t wlo, uint32_t whi, uint32_t tlo, uint32_t thi) -> bool {
+    for (int i = tid; i < nwords; i += T) sm.bm[i] = 0;
+    if (tid == 0) sm.misc[0] = 0;
+    __syncthreads();
+    uint32_t n_above = 0;
+    for_each_key<T, 16>(c.s, n, [&](int j, uint32_t ks) {
+      if (ks > whi) {
+        atomicOr(&sm.bm[j >> 5], 1u << (j & 31));
+        ++n_above;
+      } else if (ks >= wlo) {
+        const uint32_t slot = atomicAdd(&sm.misc[0], 1u);
+        if (slot < (uint32_t)kR2Cand) {
+          sm.ck[slot] = ks;
+          sm.cj[slot] = j;
+        }
+      }
+    });
+    uint32_t tot_above;
+    block_scan_sum<T>(n_above, sm.row.sc, tot_above);
+    const uint32_t n_cand = sm.misc[0];
+    if (n_cand > (uint32_t)kR2Cand || tot_above >= K || tot_above + n_cand < K) return false;
+    return resolve_candidates<T>(p, c, sm.row, sm.ck, sm.cj, sm.bm, n_cand, K - tot_above, wlo, whi, tlo, thi);
+  };
+
+  // pass 1, sampled: runs of 64 keys every S (all keys when n <= 4096); the
+  // window is the sample's order statistics around the expected rank of the
+  // K-th key, with a margin of four standard deviations
+  {
+    const int S = 64 * ((n + 4095) / 4096);
+    const int nruns = (n + S - 1) / S;
+    const int m_all = nruns * 64;                  // <= 4096 slots
+    uint32_t mloc = 0;
+    for (int e0 = 0; e0 < m_all; e0 += 8 * T) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * T + tid;
+        const int j = (e >> 6) * S + (e & 63);
+        v[u] = (e < m_all && j < n) ? c.s[j] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * T + tid;
+        const int j = (e >> 6) * S + (e & 63);
+        const bool ok = e < m_all && j < n;
+        if (e < m_all) sm.ck[e] = ok ? f32_order_key(v[u]) : 0u;
+        mloc += ok ? 1u : 0u;
+      }
+    }
+    uint32_t m;
+    block_scan_sum<T>(mloc, sm.row.sc, m);        // (its barriers also publish the samples)
+    uint32_t rhi, rlo;
+    if ((int)m == n) {
+      rhi = rlo = K;                              // the sample is the row: exact ranks
+    } else {
+      const float r = (float)K * (float)m / (float)n;
+      const float dlt = 4.f * sqrtf(r) + 4.f;
+      rhi = (uint32_t)fmaxf(1.f, floorf(r - dlt));
+      rlo = (uint32_t)fminf((float)m, ceilf(r + dlt));
+    }
+    uint32_t thi, tlo;
+    sample_window<T>(sm.ck, m_all, rhi, rlo, sm.row.hist, sm.row.sc, tlo, thi);
+    uint32_t wlo, whi;
+    band_limits(p, c, 0.f, order_key_f32(tlo), order_key_f32(thi), wlo, whi);
+    __syncthreads();
+    if (pass2(wlo, whi, tlo, thi)) return emit_bitmap<T>(p, c, sm.row, sm.bm, nwords);
+    __syncthreads();
+  }
+
+  // pass 1, full: histogram of the top 12 bits; the window is the bin of the
+  // K-th key widened by the band
+  for (int i = tid; i < 4096; i += T) sm.row.hist[i] = 0;
   __syncthreads();
   for_each_key<T, 16>(c.s, n, [&](int j, uint32_t ks) { atomicAdd(&sm.row.hist[ks >> 20], 1u); });
   __syncthreads();
@@ -344,7 +490,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_row2_kernel(TopkParams p) {
     uint32_t tot;
     const uint32_t below = block_scan_sum<T>(mine, sm.row.sc, tot);
     uint32_t cum = tot - below - mine;
-    const uint32_t K = (uint32_t)p.K;
     if (cum < K && cum + mine >= K) {
       for (int q = per - 1; q >= 0; --q) {
         if (cum + sm.row.hist[lo + q] >= K) {
@@ -362,26 +507,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_row2_kernel(TopkParams p) {
     const float lo_b = order_key_f32(bin << 20), hi_b = order_key_f32((bin << 20) | 0xFFFFFu);
     band_limits(p, c, 0.f, lo_b, hi_b, wlo, whi);
   }
-  // pass 2: bitmap of keys above the window, list of keys inside it
-  uint32_t n_above = 0;
-  for_each_key<T, 16>(c.s, n, [&](int j, uint32_t ks) {
-    if (ks > whi) {
-      atomicOr(&sm.bm[j >> 5], 1u << (j & 31));
-      ++n_above;
-    } else if (ks >= wlo) {
-      const uint32_t slot = atomicAdd(&sm.misc[0], 1u);
-      if (slot < (uint32_t)kR2Cand) {
-        sm.ck[slot] = ks;
-        sm.cj[slot] = j;
-      }
-    }
-  });
-  uint32_t tot_above;
-  block_scan_sum<T>(n_above, sm.row.sc, tot_above);
-  const uint32_t n_cand = sm.misc[0];
-  bool ok = n_cand <= (uint32_t)kR2Cand;
-  if (ok) ok = resolve_candidates<T>(p, c, sm.row, sm.ck, sm.cj, sm.bm, n_cand, (uint32_t)p.K - tot_above, wlo, whi);
-  if (!ok) {   // too many keys near the threshold: the ordered single-pass routine
+  __syncthreads();
+  if (!pass2(wlo, whi, bin << 20, (bin << 20) | 0xFFFFFu)) {
+    // too many keys near the threshold: the ordered single-pass routine
     __syncthreads();
     row_topk_single<T>(p, c, sm.row, [&](int i) { return c.s[i]; });
     if (p.count && tid == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = p.K;
