@@ -42,6 +42,20 @@ struct RowSmem {
   uint32_t run[4];
 };
 
+// The same for the two-pass kernel, compact: the band lists reuse the
+// histogram's storage (the histogram is dead once the threshold is known).
+struct RowSmemC {
+  union {
+    uint32_t hist[4096];
+    struct {
+      uint32_t band_j[2048];
+      uint32_t band_k[2048];
+    };
+  };
+  uint32_t sc[16];
+  uint32_t run[4];
+};
+
 struct RowCtx {
   int b, g, r, n;
   const float* s;
@@ -232,21 +246,28 @@ SP_DEV void for_each_key(const float* s, int n, F f) {
 // above that bin (plus the certification margin) and lists the keys inside it;
 // the short list is resolved exactly and the bitmap is written out in order.
 constexpr int kR2Words = 2048;      // bitmap words (65536 keys)
-constexpr int kR2Cand = 4096;       // candidates kept in LDS
+constexpr int kR2Cand = 2000;       // candidates (and samples) kept in LDS
 
-struct R2Smem {
-  RowSmem row;
+// 40 KB, so that four rows run on a CU at once; the rare fallback reuses the
+// storage for the single-pass routine's layout
+struct R2Main {
+  RowSmemC row;
   uint32_t ck[kR2Cand];
   uint32_t cj[kR2Cand];
   uint32_t bm[kR2Words];
   uint32_t misc[4];
 };
+union R2Smem {
+  R2Main m;
+  RowSmem full;
+};
+static_assert(sizeof(R2Smem) <= 40960, "two-pass top-K shared memory must allow four workgroups per CU");
 
 // Resolve the candidate list (keys ck, indices cj, n_cand of them) that holds
 // the remaining R slots; sets the selected bits in bm. Returns false when the
 // band is too wide for the short list (caller redoes the row).
-template <int T>
-SP_DEV bool resolve_candidates(const TopkParams& p, RowCtx& c, RowSmem& rs, uint32_t* ck, uint32_t* cj,
+template <int T, typename SM>
+SP_DEV bool resolve_candidates(const TopkParams& p, RowCtx& c, SM& rs, uint32_t* ck, uint32_t* cj,
                                uint32_t* bm, uint32_t n_cand, uint32_t R, uint32_t wlo, uint32_t whi,
                                uint32_t tlo = 0u, uint32_t thi = 0xFFFFFFFFu) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -268,7 +289,7 @@ SP_DEV bool resolve_candidates(const TopkParams& p, RowCtx& c, RowSmem& rs, uint
       ++n_in;
     } else if (ks >= klo) {
       const uint32_t slot = atomicAdd(&rs.run[0], 1u);
-      if (slot < (uint32_t)kBandCap) {
+      if (slot < (uint32_t)(sizeof(rs.band_j) / sizeof(uint32_t))) {
         rs.band_j[slot] = cj[i];
         rs.band_k[slot] = ks;
       }
@@ -277,7 +298,7 @@ SP_DEV bool resolve_candidates(const TopkParams& p, RowCtx& c, RowSmem& rs, uint
   uint32_t tot_in;
   block_scan_sum<T>(n_in, rs.sc, tot_in);
   const uint32_t nb = rs.run[0];
-  if (nb > (uint32_t)kBandCap) return false;
+  if (nb > (uint32_t)(sizeof(rs.band_j) / sizeof(uint32_t))) return false;
   const uint32_t R2 = R - tot_in;
   if (p.certified) {
     for (uint32_t e = tid >> 4; e < nb; e += T / 16) {   // a quarter-wave per band member
@@ -300,8 +321,8 @@ SP_DEV bool resolve_candidates(const TopkParams& p, RowCtx& c, RowSmem& rs, uint
 }
 
 // Write the set bits of bm (nwords words) as ascending indices, pad with -1.
-template <int T>
-SP_DEV void emit_bitmap(const TopkParams& p, const RowCtx& c, RowSmem& rs, const uint32_t* bm, int nwords) {
+template <int T, typename SM>
+SP_DEV void emit_bitmap(const TopkParams& p, const RowCtx& c, SM& rs, const uint32_t* bm, int nwords) {
   const int tid = threadIdx.x;
   const int perw = (nwords + T - 1) / T;
   const int w0 = tid * perw, w1 = min(nwords, w0 + perw);
@@ -392,9 +413,13 @@ SP_DEV void sample_window(const uint32_t* k, int m, uint32_t rhi, uint32_t rlo, 
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kTkThreads) void topk_row2_kernel(TopkParams p) {
-  constexpr int T = kTkThreads;
-  __shared__ R2Smem sm;
+// 256 threads held to 128 registers, 40 KB of LDS: four rows per CU (the
+// exact-key paths are cold)
+constexpr int kR2Threads = 256;
+__global__ __launch_bounds__(kR2Threads) __attribute__((amdgpu_waves_per_eu(4))) void topk_row2_kernel(TopkParams p) {
+  constexpr int T = kR2Threads;
+  __shared__ R2Smem smu;
+  R2Main& sm = smu.m;
   RowCtx c = row_ctx(p, blockIdx.x);
   const int tid = threadIdx.x;
   if (c.n <= p.K) return write_all(p, c, T);
@@ -430,13 +455,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_row2_kernel(TopkParams p) {
     return resolve_candidates<T>(p, c, sm.row, sm.ck, sm.cj, sm.bm, n_cand, K - tot_above, wlo, whi, tlo, thi);
   };
 
-  // pass 1, sampled: runs of 64 keys every S (all keys when n <= 4096); the
+  // pass 1, sampled: runs of 64 keys every S (all keys when n <= 1984); the
   // window is the sample's order statistics around the expected rank of the
   // K-th key, with a margin of four standard deviations
   {
-    const int S = 64 * ((n + 4095) / 4096);
+    const int S = 64 * ((n + 1983) / 1984);
     const int nruns = (n + S - 1) / S;
-    const int m_all = nruns * 64;                  // <= 4096 slots
+    const int m_all = nruns * 64;                  // <= 1984 slots
     uint32_t mloc = 0;
     for (int e0 = 0; e0 < m_all; e0 += 8 * T) {
       float v[8];
@@ -511,7 +536,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_row2_kernel(TopkParams p) {
   if (!pass2(wlo, whi, bin << 20, (bin << 20) | 0xFFFFFu)) {
     // too many keys near the threshold: the ordered single-pass routine
     __syncthreads();
-    row_topk_single<T>(p, c, sm.row, [&](int i) { return c.s[i]; });
+    row_topk_single<T>(p, c, smu.full, [&](int i) { return c.s[i]; });
     if (p.count && tid == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = p.K;
     return;
   }
@@ -1226,7 +1251,7 @@ hipError_t launch_topk(const TopkParams& p, hipStream_t st) {
   const int rows = p.B * p.G * p.Nq;
   if (!use_multi(p)) {
     if (p.ctx <= 32 * kR2Words)
-      hipLaunchKernelGGL(topk_row2_kernel, dim3(rows), dim3(kTkThreads), 0, st, p);
+      hipLaunchKernelGGL(topk_row2_kernel, dim3(rows), dim3(kR2Threads), 0, st, p);
     else
       hipLaunchKernelGGL(topk_row_kernel, dim3(rows), dim3(kTkThreads), 0, st, p);
     return hipGetLastError();
