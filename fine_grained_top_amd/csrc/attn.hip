@@ -135,7 +135,8 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnParams a) {
 }
 
 // ---------------------------------------------------------------- MFMA gather
-constexpr int kVStride = 132;   // LDS row stride of staged V in 16-bit words (264 B)
+constexpr int kVStride = 132;   // per-wave staging area: 32 rows of 264 B (rows are used at 256 B)
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 struct SplitInfo {
   int nsplit, per;   // splits per row, list entries per split (multiple of 32)
@@ -294,27 +295,35 @@ __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int 
         Alo[v2] = pl[v2];
       }
     }
-    // stage V rows in LDS: row = key, 16-byte column c16
+    // stage V rows in LDS row-major (256 B per key row), 16-byte chunk c of
+    // row r at chunk c ^ (r mod 16), so that the rows read together by the
+    // transposed reads below spread over the banks
+    uint16_t* vw = &vs[wid][0];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      uint16_t* dst = &vs[wid][(qq + 4 * u) * kVStride + 8 * c16];
-      *(u32x2*)dst = (u32x2){vr[u][0], vr[u][1]};
-      *(u32x2*)(dst + 4) = (u32x2){vr[u][2], vr[u][3]};
+      const int row = qq + 4 * u;
+      *(u32x4*)&vw[row * 128 + 8 * (c16 ^ (row & 15))] = vr[u];
     }
     __builtin_amdgcn_wave_barrier();
-    // B operand: column dim 16*nt + c16, k = 8*qq + v -> keys
+    // B operand (column dim 16 nt + c16, k = 8 qq + v <-> keys 4 qq + v and
+    // 16 + 4 qq + v - 4) by two LDS transposed reads per nt: lane (qq, j) of
+    // a 16-lane group points at key row 4 qq + j / 4 (+16), dims 16 nt +
+    // 4 (j mod 4) .. +3, and receives dim 16 nt + j of the group's four rows
+    const int trow = 4 * qq + (c16 >> 2);
+    const int tsub = 4 * (c16 & 3);                 // dim offset within the 16-dim slab
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
-      uint16_t bv[8];
-      const int dcol = 16 * nt + c16;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        bv[v] = vs[wid][(4 * qq + v) * kVStride + dcol];
-        bv[4 + v] = vs[wid][(16 + 4 * qq + v) * kVStride + dcol];
-      }
+      const int lchunk = 2 * nt + (tsub >> 3);      // logical 16-byte chunk of the row
+      const int within = tsub & 7;                  // 16-bit words into the chunk
+      const uint16_t* p0 = &vw[trow * 128 + 8 * (lchunk ^ (trow & 15)) + within];
+      const uint16_t* p1 = &vw[(trow + 16) * 128 + 8 * (lchunk ^ ((trow + 16) & 15)) + within];
+      const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p0);
+      const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p1);
       u32x4 Bv;
-#pragma unroll
-      for (int v2 = 0; v2 < 4; ++v2) Bv[v2] = (uint32_t)bv[2 * v2] | ((uint32_t)bv[2 * v2 + 1] << 16);
+      Bv[0] = (uint32_t)(uint16_t)r0[0] | ((uint32_t)(uint16_t)r0[1] << 16);
+      Bv[1] = (uint32_t)(uint16_t)r0[2] | ((uint32_t)(uint16_t)r0[3] << 16);
+      Bv[2] = (uint32_t)(uint16_t)r1[0] | ((uint32_t)(uint16_t)r1[1] << 16);
+      Bv[3] = (uint32_t)(uint16_t)r1[2] | ((uint32_t)(uint16_t)r1[3] << 16);
       O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&Ahi, *(const bf16x8*)&Bv, O[nt], 0, 0, 0);
       if (!PACKLO)
         O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&Alo, *(const bf16x8*)&Bv, O[nt], 0, 0, 0);
