@@ -28,13 +28,14 @@
 #include "common.h"
 #include "internal.h"
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
 namespace sp {
 
 constexpr int kBcRows = 256;     // rows per count/scatter workgroup
 constexpr int kBcTM = 64;        // rows per attention work item
 constexpr int kBcMaxBlocks = 2048;
 constexpr int kBcKs = 136;       // K tile row stride in 16-bit words
-constexpr int kBcVs = 72;        // V^T row stride in 16-bit words
 constexpr float kBcLog2e = 1.4426950408889634f;
 constexpr float kBcLn2 = 0.6931471805599453f;
 
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(kBcRows) void bc_scatter_kernel(AttnParams a, BcWs 
 
 struct BcSmem {
   uint16_t ks[64 * kBcKs];
-  uint16_t vt[128 * kBcVs];
+  uint16_t vt[64 * 128];    // V tile row-major, XOR-swizzled 16-byte chunks
 };
 
 // One work item: up to 64 rows that chose block blk of (request, head) bh.
@@ -291,11 +292,8 @@ __global__ __launch_bounds__(256) void bc_attn_kernel(AttnParams a, BcWs w) {
       const int cc = tid + 256 * u;
       const int key = cc >> 4, col = cc & 15;
       *(u32x4*)&sm.ks[key * kBcKs + 8 * col] = pk[u];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sm.vt[(8 * col + 2 * e) * kBcVs + key] = (uint16_t)(pv[u][e] & 0xFFFFu);
-        sm.vt[(8 * col + 2 * e + 1) * kBcVs + key] = (uint16_t)(pv[u][e] >> 16);
-      }
+      // V row-major, 16-byte chunk col of row key at col ^ (key mod 16)
+      *(u32x4*)&sm.vt[key * 128 + 8 * (col ^ (key & 15))] = pv[u];
     }
     __syncthreads();
     if (__ballot(rvalid)) {
@@ -361,10 +359,20 @@ __global__ __launch_bounds__(256) void bc_attn_kernel(AttnParams a, BcWs w) {
         }
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
-          const uint16_t* vr = &sm.vt[(16 * nt + c16) * kBcVs + 32 * hf + 4 * qq];
-          const u32x2 lo4 = *(const u32x2*)vr;
-          const u32x2 hi4 = *(const u32x2*)(vr + 16);
-          const u32x4 Bv = (u32x4){lo4[0], lo4[1], hi4[0], hi4[1]};
+          // B operand by two LDS transposed reads: lane (qq, j) points at key
+          // row 32 hf + 4 qq + j / 4 (+16), dims 16 nt + 4 (j mod 4) .. +3, and
+          // receives dim 16 nt + j of its group's four rows
+          const int tr0 = 32 * hf + 4 * qq + (c16 >> 2), tr1 = tr0 + 16;
+          const int lch = 2 * nt + ((4 * (c16 & 3)) >> 3), wth = (4 * (c16 & 3)) & 7;
+          const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)&sm.vt[tr0 * 128 + 8 * (lch ^ (tr0 & 15)) + wth]);
+          const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)&sm.vt[tr1 * 128 + 8 * (lch ^ (tr1 & 15)) + wth]);
+          u32x4 Bv;
+          Bv[0] = (uint32_t)(uint16_t)a0[0] | ((uint32_t)(uint16_t)a0[1] << 16);
+          Bv[1] = (uint32_t)(uint16_t)a0[2] | ((uint32_t)(uint16_t)a0[3] << 16);
+          Bv[2] = (uint32_t)(uint16_t)a1[0] | ((uint32_t)(uint16_t)a1[1] << 16);
+          Bv[3] = (uint32_t)(uint16_t)a1[2] | ((uint32_t)(uint16_t)a1[3] << 16);
           O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&Ahi, *(const bf16x8*)&Bv, O[nt], 0, 0, 0);
           O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&Alo, *(const bf16x8*)&Bv, O[nt], 0, 0, 0);
         }

@@ -5,9 +5,10 @@
 // 16w..16w+15. Key tiles of 64 keys are visited in increasing order: the
 // global tiles and the band of the window (WINDOW_GLOBAL), every past tile
 // (DENSE), or the union of the rows' selected blocks and windows (BLOCKS,
-// from an LDS tile bitmap). K tiles are staged row-major and V tiles
-// transposed in LDS; the next tile is prefetched into registers while the
-// current one is consumed. Per wave and tile: S^T = K Q^T on
+// from an LDS tile bitmap). K and V tiles are staged row-major in LDS (V
+// with XOR-swizzled 16-byte chunks, read as the MFMA operand by transposed
+// LDS reads); the next tile is prefetched into registers while the current
+// one is consumed. Per wave and tile: S^T = K Q^T on
 // v_mfma_f32_16x16x32_bf16 (lane = query row, 4 keys per 16-key subtile),
 // per-element masks from the row's visible set, online softmax in float32
 // (exp2), and O += P V with P as a bf16 hi/lo pair. In BLOCKS mode a wave
@@ -15,18 +16,19 @@
 #include "common.h"
 #include "internal.h"
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
 namespace sp {
 
 constexpr int kTQ = 64, kTK = 64;
 constexpr int kKs = 136;       // K tile row stride in 16-bit words (272 B)
-constexpr int kVs = 72;        // V^T row stride in 16-bit words (144 B)
 constexpr int kMaxBlkWords = 64;   // per-row block bitmap words (<= 2048 blocks)
 constexpr float kLog2eT = 1.4426950408889634f;
 constexpr float kLn2T = 0.6931471805599453f;
 
 struct TileSmem {
   uint16_t ks[kTK * kKs];
-  uint16_t vt[128 * kVs];
+  uint16_t vt[64 * 128];    // V tile row-major, XOR-swizzled 16-byte chunks
   uint32_t tiles[64];                    // tile bitmap (<= 2048 tiles)
   uint32_t rowblk[kTQ * kMaxBlkWords];   // BLOCKS: per-row selected-block bitmaps
 };
@@ -131,11 +133,8 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
       const int c = tid + 256 * u;
       const int key = c >> 4, col = c & 15;
       *(u32x4*)&sm.ks[key * kKs + 8 * col] = pk[u];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sm.vt[(8 * col + 2 * e) * kVs + key] = (uint16_t)(pv[u][e] & 0xFFFFu);
-        sm.vt[(8 * col + 2 * e + 1) * kVs + key] = (uint16_t)(pv[u][e] >> 16);
-      }
+      // V row-major, 16-byte chunk col of row key at col ^ (key mod 16)
+      *(u32x4*)&sm.vt[key * 128 + 8 * (col ^ (key & 15))] = pv[u];
     }
     __syncthreads();
     const int tn = next_tile(t);
@@ -222,10 +221,20 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
         }
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
-          const uint16_t* vr = &sm.vt[(16 * nt + c16) * kVs + 32 * hf + 4 * qq];
-          const u32x2 lo4 = *(const u32x2*)vr;          // keys 32hf + 4qq .. +3
-          const u32x2 hi4 = *(const u32x2*)(vr + 16);   // keys 32hf + 16 + 4qq .. +3
-          const u32x4 Bv = (u32x4){lo4[0], lo4[1], hi4[0], hi4[1]};
+          // B operand by two LDS transposed reads: lane (qq, j) points at key
+          // row 32 hf + 4 qq + j / 4 (+16), dims 16 nt + 4 (j mod 4) .. +3, and
+          // receives dim 16 nt + j of its group's four rows
+          const int tr0 = 32 * hf + 4 * qq + (c16 >> 2), tr1 = tr0 + 16;
+          const int lch = 2 * nt + ((4 * (c16 & 3)) >> 3), wth = (4 * (c16 & 3)) & 7;
+          const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)&sm.vt[tr0 * 128 + 8 * (lch ^ (tr0 & 15)) + wth]);
+          const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)&sm.vt[tr1 * 128 + 8 * (lch ^ (tr1 & 15)) + wth]);
+          u32x4 Bv;
+          Bv[0] = (uint32_t)(uint16_t)a0[0] | ((uint32_t)(uint16_t)a0[1] << 16);
+          Bv[1] = (uint32_t)(uint16_t)a0[2] | ((uint32_t)(uint16_t)a0[3] << 16);
+          Bv[2] = (uint32_t)(uint16_t)a1[0] | ((uint32_t)(uint16_t)a1[1] << 16);
+          Bv[3] = (uint32_t)(uint16_t)a1[2] | ((uint32_t)(uint16_t)a1[3] << 16);
           O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&Ahi, *(const bf16x8*)&Bv, O[nt], 0, 0, 0);
           O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&Alo, *(const bf16x8*)&Bv, O[nt], 0, 0, 0);
         }
