@@ -290,7 +290,9 @@ SP_DEV float exact_key(const IndexerRow& r, int64_t j) {
 // (operands and weights) is issued before any reduction, and per-head sums
 // are reduced across the group.
 template <int W>
-SP_DEV float group_exact_key(const IndexerRow& r, int64_t j) {
+SP_DEV float group_exact_key(const IndexerRow& r, int64_t j, const float* qs = nullptr, const float* wsg = nullptr) {
+  // qs/wsg (optional): the row's queries [H][d] and weights [H] already in
+  // LDS as float (exact copies of the bf16/f32 inputs)
   const double g52 = 2.220446049250313e-16;
   const int lane = threadIdx.x & (W - 1);
   const int base = (threadIdx.x & 63) & ~(W - 1);
@@ -303,16 +305,27 @@ SP_DEV float group_exact_key(const IndexerRow& r, int64_t j) {
     double wv[4] = {0.0, 0.0, 0.0, 0.0};      // loaded with the operands, used after the reduction
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (r.relu && h0 + u < r.H) wv[u] = (double)r.w[(h0 + u) * r.w_stride];
-    for (int c = lane; c < r.d; c += W) {
-      const double kv = load_f64(r.k, r.kt, koff + c);
+      if (r.relu && h0 + u < r.H) wv[u] = wsg ? (double)wsg[h0 + u] : (double)r.w[(h0 + u) * r.w_stride];
+    for (int c0 = 0; c0 < r.d; c0 += 8 * W) {
+      double kv[8];                            // the key's elements of this lane, loads in flight together
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (h0 + u < r.H) {
-          const double t = load_f64(r.q, r.qt, (h0 + u) * r.qh_stride + c) * kv;   // exact product
-          xadd(y[u], x[u], t);
-          A[u] += fabs(t);
-        }
+      for (int i = 0; i < 8; ++i) {
+        const int c = c0 + lane + W * i;
+        kv[i] = c < r.d ? load_f64(r.k, r.kt, koff + c) : 0.0;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = c0 + lane + W * i;
+        if (c >= r.d) break;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (h0 + u < r.H) {
+            const double qv = qs ? (double)qs[(h0 + u) * r.d + c] : load_f64(r.q, r.qt, (h0 + u) * r.qh_stride + c);
+            const double t = qv * kv[i];       // exact product
+            xadd(y[u], x[u], t);
+            A[u] += fabs(t);
+          }
+      }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) group_xreduce<W>(y[u], x[u], A[u]);

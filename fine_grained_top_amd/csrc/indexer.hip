@@ -102,8 +102,7 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
   }
   // this workgroup's candidate slots: [selection row of the request][cap]
   const int nrl = p.G_sel * p.Nq;
-  uint32_t* const ck_wg = FILTER ? p.cand_k + ((int64_t)b * p.nchunk + blockIdx.x) * nrl * p.cap : nullptr;
-  uint32_t* const cj_wg = FILTER ? p.cand_j + ((int64_t)b * p.nchunk + blockIdx.x) * nrl * p.cap : nullptr;
+  u32x2* const cw = FILTER ? (u32x2*)p.cand + ((int64_t)b * p.nchunk + blockIdx.x) * nrl * p.cap : nullptr;
 
   u16x2 kmx = {0, 0};
   constexpr int TPW = kMfmaChunk / 32 / 4;   // tiles per wave
@@ -213,8 +212,7 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
             const uint32_t slot = (half ? b1 : b0) + below;
             if (cdv[gi] && slot < (uint32_t)p.cap) {
               const uint32_t o = (uint32_t)hlrow[e] * (uint32_t)p.cap + slot;
-              ck_wg[o] = f32_order_key(scv[gi]);
-              cj_wg[o] = j;
+              cw[o] = u32x2{f32_order_key(scv[gi]), (uint32_t)j};
             }
           }
         }
@@ -237,8 +235,7 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
             const uint32_t slot = base + (uint32_t)__popc(mh & ((1u << col) - 1u));
             if (cand && slot < (uint32_t)p.cap) {
               const uint32_t o = (uint32_t)lrow * (uint32_t)p.cap + slot;
-              ck_wg[o] = f32_order_key(scv[gi]);
-              cj_wg[o] = j;
+              cw[o] = u32x2{f32_order_key(scv[gi]), (uint32_t)j};
             }
           }
         }

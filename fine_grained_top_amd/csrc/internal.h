@@ -28,8 +28,7 @@ struct IndexerParams {
   int chunk, nchunk;
   // threshold filter (fused indexer + top-K): keep (key, index) pairs with score >= tau
   const float* tau;        // [B, G_sel, Nq] or null (store every score instead)
-  uint32_t* cand_k;        // [B][nchunk][G_sel * Nq][cap] order keys
-  uint32_t* cand_j;        // [B][nchunk][G_sel * Nq][cap] key positions
+  uint32_t* cand;          // [B][nchunk][G_sel * Nq][cap][2]: (order key, key position), 8-byte aligned
   uint32_t* cand_n;        // [B][nchunk][G_sel * Nq] number found (may exceed cap)
   int cap;
 };

@@ -1041,12 +1041,13 @@ struct FzWs {
   float* tau;
   float* kmax;
   uint32_t* cand_n;
-  uint32_t* cand_k;
-  uint32_t* cand_j;
+  u32x2* cand;             // (order key, key position) pairs
   int nchunk, cap;
 };
 
 struct FzSmem {
+  float qs[4 * 64];       // the row's indexer queries (<= 4 heads, d_I = 64) and weights
+  float wsg[4];
   RowSmem row;
   uint32_t ck[kCandCap];
   uint32_t cj[kCandCap];
@@ -1061,6 +1062,10 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   RowCtx c = row_ctx(p, row);
   if (c.n <= p.K) return write_all(p, c, T);
+  // the row's queries and weights into LDS for the exact band keys
+  for (int e = tid; e < c.ir.H * c.ir.d; e += T)
+    sm.qs[e] = (float)load_f64(c.ir.q, c.ir.qt, (e / c.ir.d) * c.ir.qh_stride + e % c.ir.d);
+  if (tid < c.ir.H) sm.wsg[tid] = c.ir.relu ? c.ir.w[tid * c.ir.w_stride] : 1.f;
   // candidate counts of the chunks covering keys 0..p (nch <= T), loaded
   // together with the inputs of the error bound
   const int nch = (c.n + 511) / 512;
@@ -1093,8 +1098,9 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
         const int ch = c0 + u * NW;
         const int n = ch < nch ? (int)(sm.coff[ch + 1] - sm.coff[ch]) : 0;
         const int64_t src = (((int64_t)c.b * w.nchunk + ch) * nrl + rowl) * w.cap + lane;
-        kk[u] = lane < n ? w.cand_k[src] : 0u;
-        jj[u] = lane < n ? w.cand_j[src] : 0u;
+        const u32x2 cv = lane < n ? w.cand[src] : u32x2{0u, 0u};
+        kk[u] = cv[0];
+        jj[u] = cv[1];
       }
 #pragma unroll
       for (int u = 0; u < CPW; ++u) {
@@ -1107,8 +1113,9 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
           }
           for (uint32_t e = lane + 64; e < n; e += 64) {   // more than 64 in a chunk: rare
             const int64_t src = (((int64_t)c.b * w.nchunk + ch) * nrl + rowl) * w.cap + e;
-            sm.ck[o + e] = w.cand_k[src];
-            sm.cj[o + e] = w.cand_j[src];
+            const u32x2 cv = w.cand[src];
+            sm.ck[o + e] = cv[0];
+            sm.cj[o + e] = cv[1];
           }
         }
       }
@@ -1156,7 +1163,7 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
   if (nb > (uint32_t)kBandCap) return fallback();
   const uint32_t R2 = (uint32_t)p.K - tot_in;
   for (uint32_t e = tid >> 4; e < nb; e += T / 16) {   // a quarter-wave per band member
-    const float key = group_exact_key<16>(c.ir, sm.row.band_j[e]);
+    const float key = group_exact_key<16>(c.ir, sm.row.band_j[e], sm.qs, sm.wsg);
     if ((lane & 15) == 0) sm.row.band_k[e] = f32_order_key(key);
   }
   __syncthreads();
@@ -1208,22 +1215,19 @@ hipError_t launch_topk_fused(const TopkParams& p, hipStream_t st) {
   FzWs w;
   w.nchunk = (p.ctx + 511) / 512;
   w.cap = kFzCap;
-  float* base = (float*)p.ws;
-  w.tau = base;
+  w.cand = (u32x2*)p.ws;                                  // first: 8-byte aligned
+  w.tau = (float*)(w.cand + (int64_t)rows * w.nchunk * w.cap);
   w.kmax = w.tau + rows;
   w.cand_n = (uint32_t*)(w.kmax + (int64_t)p.B * w.nchunk);
-  w.cand_k = w.cand_n + (int64_t)rows * w.nchunk;
-  w.cand_j = w.cand_k + (int64_t)rows * w.nchunk * w.cap;
   const int slots = (p.ctx + kPilotStride - 1) / kPilotStride * kPilotRun;
-  uint32_t* skeys = w.cand_j + (int64_t)rows * w.nchunk * w.cap;
+  uint32_t* skeys = w.cand_n + (int64_t)rows * w.nchunk;
   hipLaunchKernelGGL(fz_pilot_score_kernel, dim3((slots + kPsThreads - 1) / kPsThreads, p.B, p.G * p.Nq),
                      dim3(kPsThreads), 0, st, p, skeys, slots);
   hipLaunchKernelGGL(fz_pilot_select_kernel, dim3(rows), dim3(kTkThreads), 0, st, p, skeys, slots, w.tau);
   IndexerParams ix = p.ix;
   ix.kmax = w.kmax;
   ix.tau = w.tau;
-  ix.cand_k = w.cand_k;
-  ix.cand_j = w.cand_j;
+  ix.cand = (uint32_t*)w.cand;
   ix.cand_n = w.cand_n;
   ix.cap = w.cap;
   ix.err = nullptr;
