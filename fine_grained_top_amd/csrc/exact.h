@@ -306,15 +306,16 @@ SP_DEV float group_exact_key(const IndexerRow& r, int64_t j, const float* qs = n
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       if (r.relu && h0 + u < r.H) wv[u] = wsg ? (double)wsg[h0 + u] : (double)r.w[(h0 + u) * r.w_stride];
-    for (int c0 = 0; c0 < r.d; c0 += 8 * W) {
-      double kv[8];                            // the key's elements of this lane, loads in flight together
+    constexpr int NK = 64 / W;                 // the lane's elements per 64 dimensions
+    for (int c0 = 0; c0 < r.d; c0 += 64) {
+      double kv[NK];                           // loads in flight together
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < NK; ++i) {
         const int c = c0 + lane + W * i;
         kv[i] = c < r.d ? load_f64(r.k, r.kt, koff + c) : 0.0;
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < NK; ++i) {
         const int c = c0 + lane + W * i;
         if (c >= r.d) break;
 #pragma unroll

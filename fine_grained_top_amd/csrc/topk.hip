@@ -246,12 +246,14 @@ SP_DEV void for_each_key(const float* s, int n, F f) {
 // above that bin (plus the certification margin) and lists the keys inside it;
 // the short list is resolved exactly and the bitmap is written out in order.
 constexpr int kR2Words = 2048;      // bitmap words (65536 keys)
-constexpr int kR2Cand = 2000;       // candidates (and samples) kept in LDS
+constexpr int kR2Cand = 1860;       // candidates (and samples) kept in LDS
 
 // 40 KB, so that four rows run on a CU at once; the rare fallback reuses the
 // storage for the single-pass routine's layout
 struct R2Main {
   RowSmemC row;
+  float qs[4 * 64];     // certified rows with <= 4 heads of <= 64 dims: queries and weights
+  float wsg[4];
   uint32_t ck[kR2Cand];
   uint32_t cj[kR2Cand];
   uint32_t bm[kR2Words];
@@ -269,7 +271,8 @@ static_assert(sizeof(R2Smem) <= 40960, "two-pass top-K shared memory must allow 
 template <int T, typename SM>
 SP_DEV bool resolve_candidates(const TopkParams& p, RowCtx& c, SM& rs, uint32_t* ck, uint32_t* cj,
                                uint32_t* bm, uint32_t n_cand, uint32_t R, uint32_t wlo, uint32_t whi,
-                               uint32_t tlo = 0u, uint32_t thi = 0xFFFFFFFFu) {
+                               uint32_t tlo = 0u, uint32_t thi = 0xFFFFFFFFu, const float* qs = nullptr,
+                               const float* wsg = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int bits = 32 - __builtin_clz((whi - wlo) | 1u);
   uint32_t t, above;
@@ -302,7 +305,7 @@ SP_DEV bool resolve_candidates(const TopkParams& p, RowCtx& c, SM& rs, uint32_t*
   const uint32_t R2 = R - tot_in;
   if (p.certified) {
     for (uint32_t e = tid >> 4; e < nb; e += T / 16) {   // a quarter-wave per band member
-      const float key = group_exact_key<16>(c.ir, rs.band_j[e]);
+      const float key = group_exact_key<16>(c.ir, rs.band_j[e], qs, wsg);
       if ((lane & 15) == 0) rs.band_k[e] = f32_order_key(key);
     }
     __syncthreads();
@@ -345,13 +348,16 @@ SP_DEV void emit_bitmap(const TopkParams& p, const RowCtx& c, SM& rs, const uint
 
 // Order-key window [tlo, thi] that holds the rhi-th and the rlo-th largest of
 // the valid keys in k[0..m) (order key 0 marks an unused slot; rhi <= rlo <=
-// number of valid keys): one pass of a 4096-bin histogram over the keys'
-// range; thi is the upper edge of the bin of rank rhi, tlo the lower edge of
-// the bin of rank rlo.
+// number of valid keys). A 4096-bin histogram over the keys' range gives the
+// bins of the two ranks; a second histogram over the span of those bins
+// refines them (a wide range, e.g. with ReLU zeros, would otherwise leave
+// bins far coarser than the rank window). thi is the upper edge of the final
+// bin of rank rhi, tlo the lower edge of the final bin of rank rlo.
 template <int T>
 SP_DEV void sample_window(const uint32_t* k, int m, uint32_t rhi, uint32_t rlo, uint32_t* hist, uint32_t* sc,
                           uint32_t& tlo, uint32_t& thi) {
   constexpr int NW = T / 64;
+  constexpr int per = 4096 / T;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   for (int i = tid; i < m; i += T) {
@@ -361,7 +367,6 @@ SP_DEV void sample_window(const uint32_t* k, int m, uint32_t rhi, uint32_t rlo, 
       kmax = max(kmax, v);
     }
   }
-  for (int i = tid; i < 4096; i += T) hist[i] = 0u;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
@@ -372,44 +377,57 @@ SP_DEV void sample_window(const uint32_t* k, int m, uint32_t rhi, uint32_t rlo, 
     sc[NW + wid] = kmax;
   }
   __syncthreads();
-  kmin = 0xFFFFFFFFu;
-  kmax = 0u;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
   for (int w = 0; w < NW; ++w) {
-    kmin = min(kmin, sc[w]);
-    kmax = max(kmax, sc[NW + w]);
+    lo = min(lo, sc[w]);
+    hi = max(hi, sc[NW + w]);
   }
-  const int bits = 32 - __builtin_clz((kmax - kmin) | 1u);
-  const int sh = bits > 12 ? bits - 12 : 0;
-  for (int i = tid; i < m; i += T) {
-    const uint32_t v = k[i];
-    if (v != 0u) atomicAdd(&hist[(v - kmin) >> sh], 1u);
-  }
-  __syncthreads();
-  // counts from the top: thread tid owns bins [8 tid, 8 tid + 8)
-  constexpr int per = 4096 / T;
-  uint32_t hb[per], cnt = 0;
+  uint32_t above = 0;      // valid keys above hi (none at the first level)
+  for (int level = 0; level < 2; ++level) {
+    __syncthreads();
+    for (int i = tid; i < 4096; i += T) hist[i] = 0u;
+    __syncthreads();
+    const int bits = 32 - __builtin_clz((hi - lo) | 1u);
+    const int sh = bits > 12 ? bits - 12 : 0;
+    for (int i = tid; i < m; i += T) {
+      const uint32_t v = k[i];
+      if (v != 0u && v >= lo && v <= hi) atomicAdd(&hist[(v - lo) >> sh], 1u);
+    }
+    __syncthreads();
+    // counts from the top: thread tid owns bins [per tid, per tid + per)
+    uint32_t hb[per], cnt = 0;
 #pragma unroll
-  for (int e = 0; e < per; ++e) {
-    hb[e] = hist[per * tid + e];
-    cnt += hb[e];
-  }
-  uint32_t tot;
-  const uint32_t below = block_scan_sum<T>(cnt, sc, tot);
-  const uint32_t above0 = tot - below - cnt;
-  uint32_t* res = hist;   // the two results, after everyone has read the bins
-  __syncthreads();
-  uint32_t acc = above0;
+    for (int e = 0; e < per; ++e) {
+      hb[e] = hist[per * tid + e];
+      cnt += hb[e];
+    }
+    uint32_t tot;
+    const uint32_t below = block_scan_sum<T>(cnt, sc, tot);
+    uint32_t acc = above + tot - below - cnt;
+    uint32_t* res = hist;   // results, once every thread has read its bins
+    __syncthreads();
 #pragma unroll
-  for (int e = per - 1; e >= 0; --e) {
-    const uint32_t nxt = acc + hb[e];
-    const uint32_t bin = (uint32_t)(per * tid + e);
-    if (acc < rhi && rhi <= nxt) res[0] = (uint32_t)min((uint64_t)kmax, (uint64_t)kmin + (((uint64_t)bin + 1) << sh) - 1);
-    if (acc < rlo && rlo <= nxt) res[1] = kmin + (bin << sh);
-    acc = nxt;
+    for (int e = per - 1; e >= 0; --e) {
+      const uint32_t nxt = acc + hb[e];
+      const uint32_t bin = (uint32_t)(per * tid + e);
+      if (acc < rhi && rhi <= nxt) {
+        res[0] = (uint32_t)min((uint64_t)hi, (uint64_t)lo + (((uint64_t)bin + 1) << sh) - 1);
+        res[2] = acc;                          // keys above that bin
+      }
+      if (acc < rlo && rlo <= nxt) res[1] = lo + (bin << sh);
+      acc = nxt;
+    }
+    __syncthreads();
+    const uint32_t nhi = res[0], nlo = res[1], nab = res[2];
+    if (sh == 0 || level == 1) {
+      thi = nhi;
+      tlo = nlo;
+      break;
+    }
+    hi = nhi;
+    lo = nlo;
+    above = nab;
   }
-  __syncthreads();
-  thi = res[0];
-  tlo = res[1];
   __syncthreads();
 }
 
@@ -426,6 +444,15 @@ __global__ __launch_bounds__(kR2Threads) __attribute__((amdgpu_waves_per_eu(4)))
   const int n = c.n;
   const int nwords = (n + 31) >> 5;
   const uint32_t K = (uint32_t)p.K;
+  // certified rows: the row's queries and weights into LDS for the exact band keys
+  const bool staged = p.certified && c.ir.H <= 4 && c.ir.d <= 64;
+  if (staged) {
+    for (int e = tid; e < c.ir.H * c.ir.d; e += T)
+      sm.qs[e] = (float)load_f64(c.ir.q, c.ir.qt, (e / c.ir.d) * c.ir.qh_stride + e % c.ir.d);
+    if (tid < c.ir.H) sm.wsg[tid] = c.ir.relu ? c.ir.w[tid * c.ir.w_stride] : 1.f;
+  }
+  const float* qsp = staged ? sm.qs : nullptr;
+  const float* wsp = staged ? sm.wsg : nullptr;
 
   // pass 2 for a window [wlo, whi] (order keys, already widened by the band):
   // bitmap of the keys above it, short list of the keys inside it, exact
@@ -452,16 +479,17 @@ __global__ __launch_bounds__(kR2Threads) __attribute__((amdgpu_waves_per_eu(4)))
     block_scan_sum<T>(n_above, sm.row.sc, tot_above);
     const uint32_t n_cand = sm.misc[0];
     if (n_cand > (uint32_t)kR2Cand || tot_above >= K || tot_above + n_cand < K) return false;
-    return resolve_candidates<T>(p, c, sm.row, sm.ck, sm.cj, sm.bm, n_cand, K - tot_above, wlo, whi, tlo, thi);
+    return resolve_candidates<T>(p, c, sm.row, sm.ck, sm.cj, sm.bm, n_cand, K - tot_above, wlo, whi, tlo, thi,
+                                 qsp, wsp);
   };
 
-  // pass 1, sampled: runs of 64 keys every S (all keys when n <= 1984); the
+  // pass 1, sampled: runs of 64 keys every S (all keys when n <= 1856); the
   // window is the sample's order statistics around the expected rank of the
-  // K-th key, with a margin of four standard deviations
+  // K-th key, with a margin of a few standard deviations
   {
-    const int S = 64 * ((n + 1983) / 1984);
+    const int S = 64 * ((n + 1855) / 1856);
     const int nruns = (n + S - 1) / S;
-    const int m_all = nruns * 64;                  // <= 1984 slots
+    const int m_all = nruns * 64;                  // <= 1856 slots
     uint32_t mloc = 0;
     for (int e0 = 0; e0 < m_all; e0 += 8 * T) {
       float v[8];
@@ -486,8 +514,10 @@ __global__ __launch_bounds__(kR2Threads) __attribute__((amdgpu_waves_per_eu(4)))
     if ((int)m == n) {
       rhi = rlo = K;                              // the sample is the row: exact ranks
     } else {
+      // 2.5 standard deviations of the sample rank, but no wider than what
+      // keeps the expected number of candidates at 70 % of the list
       const float r = (float)K * (float)m / (float)n;
-      const float dlt = 4.f * sqrtf(r) + 4.f;
+      const float dlt = fminf(2.5f * sqrtf(r) + 2.f, 0.35f * (float)kR2Cand * (float)m / (float)n);
       rhi = (uint32_t)fmaxf(1.f, floorf(r - dlt));
       rlo = (uint32_t)fminf((float)m, ceilf(r + dlt));
     }
