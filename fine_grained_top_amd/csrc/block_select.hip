@@ -43,6 +43,15 @@ __global__ __launch_bounds__(128) void pool_kernel(BlockSelectParams p) {
     const int64_t o = (((int64_t)b * p.Hkv + hk) * nbk + beta) * p.d + c;
     p.kbar[o] = s;
     p.kbar64[o] = s64;
+    // s = hi + mid + lo + r with |r| <= 2^-24 |s| (each part the nearest bf16 of what is left)
+    const uint32_t hi = f32_to_bf16_rne(s);
+    const float r1 = s - bf16_to_f32(hi);
+    const uint32_t mid = f32_to_bf16_rne(r1);
+    const uint32_t lo = f32_to_bf16_rne(r1 - bf16_to_f32(mid));
+    const int64_t nall = (int64_t)p.B * p.Hkv * nbk * p.d;
+    p.kb3[o] = (uint16_t)hi;
+    p.kb3[nall + o] = (uint16_t)mid;
+    p.kb3[2 * nall + o] = (uint16_t)lo;
   }
   __shared__ float red[2];
   __shared__ int ex[2];
@@ -163,7 +172,7 @@ SP_DEV uint32_t wave_kth_largest(const uint32_t (&k)[KPL], const uint64_t (&vm)[
 //  phase 2: one wave per row: the nb-th largest score (bisection over the
 //           order key, counts by ballot), the band, exact keys of the band,
 //           the R best of the band, ordered output.
-template <int KPL>
+template <int KPL, bool MFMA>
 __global__ __launch_bounds__(kBsThreads) void block_select_kernel(BlockSelectParams p, int ntile) {
   constexpr int RB = 128 / KPL;   // rows per tile: 16, 8, 4 for up to 512, 1024, 2048 blocks
   extern __shared__ __align__(16) unsigned char smem[];
@@ -219,7 +228,47 @@ __global__ __launch_bounds__(kBsThreads) void block_select_kernel(BlockSelectPar
     const float* ka = p.kabs + ((int64_t)b * p.Hkv + hk) * nbk;
     const float inv = ldexpf(1.0f, -p.log2bs);
     float amax = 0.f;
-    for (int beta = tid; beta < neMax; beta += kBsThreads) {
+    if (MFMA) {
+      // S[16 rows][16 blocks] = Q K^T on v_mfma_f32_16x16x32_bf16, K the three
+      // bf16 parts of the block sums: A = q rows (lane: row l%16, dims 8(l/16)..),
+      // B = parts (lane: block l%16, same dims), D: lane block l%16, rows 4(l/16)+v
+      const int64_t nall = (int64_t)p.B * p.Hkv * nbk * p.d;
+      const uint16_t* kp = p.kb3 + ((int64_t)b * p.Hkv + hk) * nbk * p.d;
+      const int m16 = lane & 15, kg = lane >> 4;
+      bf16x8 Aq[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        bf16x8 a = (bf16x8){};
+        if (32 * st < p.d) {
+          const float* qr = (const float*)qs + m16 * p.d + 32 * st + 8 * kg;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[e] = (__bf16)qr[e];      // exact: q is bf16
+        }
+        Aq[st] = a;
+      }
+      for (int bt = wid; 16 * bt < neMax; bt += 4) {
+        const int blk = 16 * bt + m16;
+        const int bc = blk < neMax ? blk : neMax - 1;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          if (32 * st >= p.d) break;
+          const int64_t off = (int64_t)bc * p.d + 32 * st + 8 * kg;
+          const bf16x8 bh = *(const bf16x8*)(kp + off);
+          const bf16x8 bm = *(const bf16x8*)(kp + nall + off);
+          const bf16x8 bl = *(const bf16x8*)(kp + 2 * nall + off);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aq[st], bh, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aq[st], bm, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aq[st], bl, acc, 0, 0, 0);
+        }
+        if (blk < neMax) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sk[(4 * kg + v) * nbk + blk] = f32_order_key(acc[v] * inv);
+        }
+      }
+      for (int beta = tid; beta < neMax; beta += kBsThreads) amax = fmaxf(amax, ka[beta]);
+    }
+    for (int beta = tid; !MFMA && beta < neMax; beta += kBsThreads) {
       const f32x4* kr = (const f32x4*)(kb + (int64_t)beta * p.d);
       float acc[RB];
 #pragma unroll
@@ -251,9 +300,11 @@ __global__ __launch_bounds__(kBsThreads) void block_select_kernel(BlockSelectPar
   // rigorous bound on |score~ - key| per unit of |q|_1 (amax covers every block of the tile)
   const double uu = 1.0 / 8388608.0;
   auto gam = [&](double n) { return n * uu / (1.0 - n * uu); };
-  const double C = 1.25 * (gam(p.bs + 2) + gam(p.d + 2) * (1.0 + gam(p.bs + 2)) + uu);
+  // float32 sums (bs terms), then either FMA chains of d products or MFMA
+  // accumulation of 3 d exact bf16 products with the 2^-24 split remainder
+  const double C = MFMA ? 1.25 * (gam(p.bs + 2) + uu * (1.0 + gam(p.bs + 2)) + gam(3 * p.d + 2) * (1.0 + gam(p.bs + 2)) + uu)
+                        : 1.25 * (gam(p.bs + 2) + gam(p.d + 2) * (1.0 + gam(p.bs + 2)) + uu);
   const int ksz = p.k.dt == DT_F32 ? 4 : 2;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
   uint32_t* hist = whist[wid];
   uint32_t* bl_i = wband_i[wid];
@@ -366,7 +417,8 @@ __global__ __launch_bounds__(kBsThreads) void block_select_kernel(BlockSelectPar
 
 size_t block_select_ws_bytes(int B, int Hkv, int ctx, int d, int bs) {
   const size_t nbk = ctx / bs;
-  return (size_t)B * Hkv * nbk * (3 * d + 2) * sizeof(float);   // kbar, kabs, kbar64 (2 floats each), kexact
+  // kbar64 (2 floats each), kbar, kabs, kexact, then the three bf16 parts (256-byte aligned)
+  return (size_t)B * Hkv * nbk * (3 * d + 2) * sizeof(float) + 256 + (size_t)B * Hkv * nbk * d * 3 * 2;
 }
 
 hipError_t launch_block_select(const BlockSelectParams& p, hipStream_t st) {
@@ -379,12 +431,14 @@ hipError_t launch_block_select(const BlockSelectParams& p, hipStream_t st) {
   const int ntile = (p.Nq + rb - 1) / rb;
   const size_t lds = (size_t)rb * p.d * 4 + (size_t)rb * nbk * 4;
   const dim3 grid(p.B * p.Hq * ntile);
-  if (kpl == 8)
-    hipLaunchKernelGGL(block_select_kernel<8>, grid, dim3(kBsThreads), lds, st, p, ntile);
+  if (kpl == 8 && p.q.dt == DT_BF16)
+    hipLaunchKernelGGL((block_select_kernel<8, true>), grid, dim3(kBsThreads), lds, st, p, ntile);
+  else if (kpl == 8)
+    hipLaunchKernelGGL((block_select_kernel<8, false>), grid, dim3(kBsThreads), lds, st, p, ntile);
   else if (kpl == 16)
-    hipLaunchKernelGGL(block_select_kernel<16>, grid, dim3(kBsThreads), lds, st, p, ntile);
+    hipLaunchKernelGGL((block_select_kernel<16, false>), grid, dim3(kBsThreads), lds, st, p, ntile);
   else
-    hipLaunchKernelGGL(block_select_kernel<32>, grid, dim3(kBsThreads), lds, st, p, ntile);
+    hipLaunchKernelGGL((block_select_kernel<32, false>), grid, dim3(kBsThreads), lds, st, p, ntile);
   return hipGetLastError();
 }
 
