@@ -43,15 +43,12 @@ __global__ __launch_bounds__(128) void pool_kernel(BlockSelectParams p) {
     const int64_t o = (((int64_t)b * p.Hkv + hk) * nbk + beta) * p.d + c;
     p.kbar[o] = s;
     p.kbar64[o] = s64;
-    // s = hi + mid + lo + r with |r| <= 2^-24 |s| (each part the nearest bf16 of what is left)
+    // s = hi + mid + r with |r| <= 2^-16 |s| (each part the nearest bf16 of what is left)
     const uint32_t hi = f32_to_bf16_rne(s);
-    const float r1 = s - bf16_to_f32(hi);
-    const uint32_t mid = f32_to_bf16_rne(r1);
-    const uint32_t lo = f32_to_bf16_rne(r1 - bf16_to_f32(mid));
+    const uint32_t mid = f32_to_bf16_rne(s - bf16_to_f32(hi));
     const int64_t nall = (int64_t)p.B * p.Hkv * nbk * p.d;
-    p.kb3[o] = (uint16_t)hi;
-    p.kb3[nall + o] = (uint16_t)mid;
-    p.kb3[2 * nall + o] = (uint16_t)lo;
+    p.kb2[o] = (uint16_t)hi;
+    p.kb2[nall + o] = (uint16_t)mid;
   }
   __shared__ float red[2];
   __shared__ int ex[2];
@@ -70,15 +67,16 @@ __global__ __launch_bounds__(128) void pool_kernel(BlockSelectParams p) {
 }
 
 // exact block key computed by one wave: float64 partial sums over the lanes,
-// certified, else the exact accumulator on lane 0.
-SP_DEV float wave_block_key(const BlockSelectParams& p, const void* qrow, const void* kblock) {
+// certified, else the exact accumulator on lane 0. qrow holds the query row
+// in type qdt (the caller's LDS copy, exact).
+SP_DEV float wave_block_key(const BlockSelectParams& p, const void* qrow, int qdt, const void* kblock) {
   const int lane = threadIdx.x & 63;
   const int n = p.bs * p.d;
   double y = 0.0, A = 0.0;
   bool x = true;
   for (int e = lane; e < n; e += 64) {
     const int t = e / p.d, c = e % p.d;
-    const double v = load_f64(qrow, p.q.dt, c) * load_f64(kblock, p.k.dt, t * p.k.s[2] + c);   // exact
+    const double v = load_f64(qrow, qdt, c) * load_f64(kblock, p.k.dt, t * p.k.s[2] + c);   // exact
     xadd(y, x, v);
     A += fabs(v);
   }
@@ -90,24 +88,29 @@ SP_DEV float wave_block_key(const BlockSelectParams& p, const void* qrow, const 
   const bool ok = certify(ldexp(y, -p.log2bs), ldexp(e, -p.log2bs), key);
   if (ok) return key;
   float slow = 0.f;
-  if (lane == 0) slow = exact_block_key(qrow, p.q.dt, kblock, p.k.dt, p.k.s[2], p.bs, p.log2bs, p.d);
+  if (lane == 0) slow = exact_block_key(qrow, qdt, kblock, p.k.dt, p.k.s[2], p.bs, p.log2bs, p.d);
   return __shfl(slow, 0, 64);
 }
 
 // The same key from the block's exact float64 key sums: (1/bs) * q . ksum,
 // d products per candidate instead of bs * d; exact or certified, else the
-// full sum.
-SP_DEV float wave_block_key_sums(const BlockSelectParams& p, const void* qrow, const double* ks64, bool exact,
-                                 const void* kblock) {
+// full sum. The flag and the sums (d <= 128: two per lane) load together.
+SP_DEV float wave_block_key_sums(const BlockSelectParams& p, const void* qrow, int qdt, const double* ks64,
+                                 const uint32_t* kx, const void* kblock) {
 #pragma clang fp contract(off)
-  if (exact) {
-    const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63;
+  const double k0 = ks64[lane];
+  const double k1 = lane + 64 < p.d ? ks64[lane + 64] : 0.0;
+  if (*kx != 0) {
     double y = 0.0, A = 0.0;
     bool x = true;
-    for (int c = lane; c < p.d; c += 64) {
-      const double qv = load_f64(qrow, p.q.dt, c), kv = ks64[c];
-      xadd_prod(y, x, qv, kv);
-      A += fabs(qv * kv);
+    const double q0 = load_f64(qrow, qdt, lane);
+    xadd_prod(y, x, q0, k0);
+    A += fabs(q0 * k0);
+    if (lane + 64 < p.d) {
+      const double q1 = load_f64(qrow, qdt, lane + 64);
+      xadd_prod(y, x, q1, k1);
+      A += fabs(q1 * k1);
     }
     wave_xreduce(y, x, A);
     if (x) return key_of_exact(ldexp(y, -p.log2bs));
@@ -116,13 +119,14 @@ SP_DEV float wave_block_key_sums(const BlockSelectParams& p, const void* qrow, c
     float key;
     if (certify(ldexp(y, -p.log2bs), ldexp(e, -p.log2bs), key)) return key;
   }
-  return wave_block_key(p, qrow, kblock);
+  return wave_block_key(p, qrow, qdt, kblock);
 }
 
 // want-th largest (want >= 1) of the keys k[j] on lanes set in vm[j]
 // (slot j of lane l holds element 64 j + l; the set must have >= want
 // members): radix select, 8 bits a pass, on a per-wave LDS histogram of 256
-// bins. Wave-uniform result.
+// 16-bit bins packed two to a word (128 words; counts stay below 2^16).
+// Wave-uniform result.
 template <int KPL>
 SP_DEV uint32_t wave_kth_largest(const uint32_t (&k)[KPL], const uint64_t (&vm)[KPL], int n, uint32_t want,
                                  uint32_t* hist) {
@@ -130,35 +134,35 @@ SP_DEV uint32_t wave_kth_largest(const uint32_t (&k)[KPL], const uint64_t (&vm)[
   uint32_t prefix = 0;
 #pragma unroll
   for (int shift = 24; shift >= 0; shift -= 8) {
-    *(u32x4*)(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+    *(u32x2*)(hist + 2 * lane) = u32x2{0u, 0u};
     __builtin_amdgcn_wave_barrier();
     const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
       if (j * 64 >= n) break;
-      if (((vm[j] >> lane) & 1) && (k[j] & hmask) == prefix) atomicAdd(&hist[(k[j] >> shift) & 255u], 1u);
+      if (((vm[j] >> lane) & 1) && (k[j] & hmask) == prefix) {
+        const uint32_t dgt = (k[j] >> shift) & 255u;
+        atomicAdd(&hist[dgt >> 1], 1u << ((dgt & 1u) << 4));
+      }
     }
     __builtin_amdgcn_wave_barrier();
-    const u32x4 hv = *(const u32x4*)(hist + 4 * lane);
-    const uint32_t c = hv[0] + hv[1] + hv[2] + hv[3];
+    // lane l owns bins 4l .. 4l+3
+    const u32x2 hw = *(const u32x2*)(hist + 2 * lane);
+    const uint32_t h0 = hw[0] & 0xFFFFu, h1 = hw[0] >> 16, h2 = hw[1] & 0xFFFFu, h3 = hw[1] >> 16;
+    const uint32_t c = h0 + h1 + h2 + h3;
     // members with a digit in a higher lane's bins
-    uint32_t incl = c;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t v = __shfl_down(incl, o, 64);
-      if (lane + o < 64) incl += v;
-    }
-    const uint32_t above0 = incl - c;
+    const uint32_t pin = wave_prefix_incl_u32(c);
+    const uint32_t above0 = (uint32_t)__builtin_amdgcn_readlane((int)pin, 63) - pin;
     // the bin where the count from the top reaches want
     uint32_t dg = 0, above = 0;
-    if (above0 + hv[3] >= want) { dg = 3; above = above0; }
-    else if (above0 + hv[3] + hv[2] >= want) { dg = 2; above = above0 + hv[3]; }
-    else if (above0 + hv[3] + hv[2] + hv[1] >= want) { dg = 1; above = above0 + hv[3] + hv[2]; }
-    else { dg = 0; above = above0 + hv[3] + hv[2] + hv[1]; }
+    if (above0 + h3 >= want) { dg = 3; above = above0; }
+    else if (above0 + h3 + h2 >= want) { dg = 2; above = above0 + h3; }
+    else if (above0 + h3 + h2 + h1 >= want) { dg = 1; above = above0 + h3 + h2; }
+    else { dg = 0; above = above0 + h3 + h2 + h1; }
     const uint64_t hit = ballot(above0 < want && want <= above0 + c);
     const int src = (int)__builtin_ctzll(hit);
-    const uint32_t digit = 4u * (uint32_t)src + (uint32_t)__shfl((int)dg, src, 64);
-    want -= (uint32_t)__shfl((int)above, src, 64);
+    const uint32_t digit = 4u * (uint32_t)src + (uint32_t)__builtin_amdgcn_readlane((int)dg, src);
+    want -= (uint32_t)__builtin_amdgcn_readlane((int)above, src);
     prefix |= digit << shift;
     __builtin_amdgcn_wave_barrier();
   }
@@ -167,23 +171,25 @@ SP_DEV uint32_t wave_kth_largest(const uint32_t (&k)[KPL], const uint64_t (&vm)[
 
 // Select, one workgroup per tile of RB consecutive query rows of one (b, h):
 //  phase 1: score~[rr][beta] = (q_rr . ksum[beta]) / bs for every block any row
-//           of the tile may see; each thread owns one block and reuses its key
-//           sum across the RB rows (q broadcast from LDS);
-//  phase 2: one wave per row: the nb-th largest score (bisection over the
-//           order key, counts by ballot), the band, exact keys of the band,
-//           the R best of the band, ordered output.
+//           of the tile may see, into LDS as order keys. bf16 q: MFMA tiles of
+//           16 rows x 16 blocks, the key sums as two bf16 parts, the q tile in
+//           registers (and copied to LDS for phase 2); float32 q: one thread
+//           per block reusing its key sum across the RB rows;
+//  phase 2: one wave per row: the nb-th largest score (radix select), the
+//           band, exact keys of the band, the R best of the band, ordered output.
 template <int KPL, bool MFMA>
-__global__ __launch_bounds__(kBsThreads) void block_select_kernel(BlockSelectParams p, int ntile) {
+__global__ __launch_bounds__(kBsThreads) __attribute__((amdgpu_waves_per_eu(4))) void block_select_kernel(BlockSelectParams p, int ntile) {
   constexpr int RB = 128 / KPL;   // rows per tile: 16, 8, 4 for up to 512, 1024, 2048 blocks
   extern __shared__ __align__(16) unsigned char smem[];
   const int nbk = p.ctx / p.bs;
-  f32x4* qs = (f32x4*)smem;                                   // [RB][d/4]
-  uint32_t* sk = (uint32_t*)(smem + RB * p.d * 4);            // [RB][nbk]
+  // q rows of the tile: [RB][d] bf16 (MFMA) or float32
+  f32x4* qs = (f32x4*)smem;
+  uint16_t* qb = (uint16_t*)smem;
+  uint32_t* sk = (uint32_t*)(smem + RB * p.d * (MFMA ? 2 : 4));   // [RB][nbk]
   __shared__ float qn[RB];
   __shared__ float fred[4];
-  __shared__ __align__(16) uint32_t whist[4][256];
-  __shared__ uint32_t wband_i[4][64];
-  __shared__ uint32_t wband_k[4][64];
+  // per wave: the radix histogram, which the band lists (64 indices, 64 keys) reuse
+  __shared__ __align__(16) uint32_t whist[4][128];
 
   // blockIdx -> tile: a contiguous range of tiles per XCD (dispatch round-robins
   // workgroups over the 8 XCDs), so one XCD's L2 holds few heads' key sums
@@ -209,86 +215,125 @@ __global__ __launch_bounds__(kBsThreads) void block_select_kernel(BlockSelectPar
   const int d4 = p.d >> 2;
 
   if (neMax > nb) {
-    // q rows of the tile -> LDS, with their 1-norms
-    for (int rr = wid; rr < RB; rr += 4) {
-      const char* qrow = (const char*)p.q.p + (b * p.q.s[0] + h * p.q.s[1] + (int64_t)(r0 + rr) * p.q.s[2]) * esz;
-      float a = 0.f;
-      for (int c = lane; c < p.d; c += 64) {
-        float x = 0.f;
-        if (rr < nrows)
-          x = p.q.dt == DT_F32 ? ((const float*)qrow)[c] : bf16_to_f32(((const uint16_t*)qrow)[c]);
-        ((float*)qs)[rr * p.d + c] = x;
-        a += fabsf(x);
-      }
-      a = wave_sum(a);
-      if (lane == 0) qn[rr] = a;
-    }
-    __syncthreads();
-    const float* kb = p.kbar + ((int64_t)b * p.Hkv + hk) * nbk * p.d;
     const float* ka = p.kabs + ((int64_t)b * p.Hkv + hk) * nbk;
     const float inv = ldexpf(1.0f, -p.log2bs);
     float amax = 0.f;
     if (MFMA) {
-      // S[16 rows][16 blocks] = Q K^T on v_mfma_f32_16x16x32_bf16, K the three
-      // bf16 parts of the block sums: A = q rows (lane: row l%16, dims 8(l/16)..),
-      // B = parts (lane: block l%16, same dims), D: lane block l%16, rows 4(l/16)+v
+      // S[16 rows][16 blocks] = Q K^T on v_mfma_f32_16x16x32_bf16 over the two
+      // bf16 parts of the block sums: A = q rows (lane: row l%16, dims
+      // 32 st + 8(l/16) ..+7), B = parts (lane: block l%16, same dims),
+      // D: lane block l%16, rows 4(l/16)+v
       const int64_t nall = (int64_t)p.B * p.Hkv * nbk * p.d;
-      const uint16_t* kp = p.kb3 + ((int64_t)b * p.Hkv + hk) * nbk * p.d;
+      const uint16_t* kp = p.kb2 + ((int64_t)b * p.Hkv + hk) * nbk * p.d;
       const int m16 = lane & 15, kg = lane >> 4;
-      bf16x8 Aq[4];
+      const int nst = p.d >> 5;
+      // block 1-norm bounds: issued first, consumed after the tiles (nbk <= 512)
+      const float ka0 = tid < neMax ? ka[tid] : 0.f;
+      const float ka1 = tid + kBsThreads < neMax ? ka[tid + kBsThreads] : 0.f;
+      u32x4 qa[4];
+      {
+        const uint16_t* qr = (const uint16_t*)p.q.p + b * p.q.s[0] + h * p.q.s[1] +
+                             (int64_t)(r0 + min(m16, nrows - 1)) * p.q.s[2] + 8 * kg;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (st < nst) v = *(const u32x4*)(qr + 32 * st);   // rows are 16-byte aligned (checked at the boundary)
+          if (m16 >= nrows) v = u32x4{0u, 0u, 0u, 0u};
+          qa[st] = v;
+        }
+      }
+      u32x4 Bc[2][4], Bn[2][4];
+      auto loadB = [&](u32x4 (&Bt)[2][4], int bt) {
+        const int blk = 16 * bt + m16;
+        const uint16_t* src = kp + (int64_t)(blk < neMax ? blk : neMax - 1) * p.d + 8 * kg;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          if (st < nst) {
+            Bt[0][st] = *(const u32x4*)(src + 32 * st);
+            Bt[1][st] = *(const u32x4*)(src + nall + 32 * st);
+          }
+        }
+      };
+      if (16 * wid < neMax) loadB(Bc, wid);
+      // the q tile to LDS for phase 2 (wave 0) and the row 1-norms
+      float a1 = 0.f;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        bf16x8 a = (bf16x8){};
-        if (32 * st < p.d) {
-          const float* qr = (const float*)qs + m16 * p.d + 32 * st + 8 * kg;
+        if (st < nst) {
+          if (wid == 0) *(u32x4*)(qb + m16 * p.d + 32 * st + 8 * kg) = qa[st];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) a[e] = (__bf16)qr[e];      // exact: q is bf16
+          for (int e = 0; e < 4; ++e)
+            a1 += fabsf(bf16_to_f32(qa[st][e] & 0xFFFFu)) + fabsf(bf16_to_f32(qa[st][e] >> 16));
         }
-        Aq[st] = a;
       }
+      a1 += __shfl_xor(a1, 16, 64);
+      a1 += __shfl_xor(a1, 32, 64);
+      if (wid == 0 && lane < RB) qn[lane] = a1;
       for (int bt = wid; 16 * bt < neMax; bt += 4) {
-        const int blk = 16 * bt + m16;
-        const int bc = blk < neMax ? blk : neMax - 1;
+        const bool more = 16 * (bt + 4) < neMax;
+        if (more) loadB(Bn, bt + 4);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-          if (32 * st >= p.d) break;
-          const int64_t off = (int64_t)bc * p.d + 32 * st + 8 * kg;
-          const bf16x8 bh = *(const bf16x8*)(kp + off);
-          const bf16x8 bm = *(const bf16x8*)(kp + nall + off);
-          const bf16x8 bl = *(const bf16x8*)(kp + 2 * nall + off);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aq[st], bh, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aq[st], bm, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aq[st], bl, acc, 0, 0, 0);
+          if (st < nst) {
+            const bf16x8 A = __builtin_bit_cast(bf16x8, qa[st]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, Bc[0][st]), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, Bc[1][st]), acc, 0, 0, 0);
+          }
         }
+        const int blk = 16 * bt + m16;
         if (blk < neMax) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) sk[(4 * kg + v) * nbk + blk] = f32_order_key(acc[v] * inv);
         }
-      }
-      for (int beta = tid; beta < neMax; beta += kBsThreads) amax = fmaxf(amax, ka[beta]);
-    }
-    for (int beta = tid; !MFMA && beta < neMax; beta += kBsThreads) {
-      const f32x4* kr = (const f32x4*)(kb + (int64_t)beta * p.d);
-      float acc[RB];
+        if (more) {
 #pragma unroll
-      for (int rr = 0; rr < RB; ++rr) acc[rr] = 0.f;
-      for (int c4 = 0; c4 < d4; c4 += 4) {
-        f32x4 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = kr[c4 + u];
-#pragma unroll
-        for (int rr = 0; rr < RB; ++rr)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const f32x4 qv = qs[rr * d4 + c4 + u];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[rr] = fmaf(qv[e], v[u][e], acc[rr]);
+          for (int st = 0; st < 4; ++st) {
+            Bc[0][st] = Bn[0][st];
+            Bc[1][st] = Bn[1][st];
           }
+        }
       }
+      amax = fmaxf(ka0, ka1);
+    } else {
+      // q rows of the tile -> LDS, with their 1-norms
+      for (int rr = wid; rr < RB; rr += 4) {
+        const char* qrow = (const char*)p.q.p + (b * p.q.s[0] + h * p.q.s[1] + (int64_t)(r0 + rr) * p.q.s[2]) * esz;
+        float a = 0.f;
+        for (int c = lane; c < p.d; c += 64) {
+          float x = 0.f;
+          if (rr < nrows)
+            x = p.q.dt == DT_F32 ? ((const float*)qrow)[c] : bf16_to_f32(((const uint16_t*)qrow)[c]);
+          ((float*)qs)[rr * p.d + c] = x;
+          a += fabsf(x);
+        }
+        a = wave_sum(a);
+        if (lane == 0) qn[rr] = a;
+      }
+      __syncthreads();
+      const float* kb = p.kbar + ((int64_t)b * p.Hkv + hk) * nbk * p.d;
+      for (int beta = tid; beta < neMax; beta += kBsThreads) {
+        const f32x4* kr = (const f32x4*)(kb + (int64_t)beta * p.d);
+        float acc[RB];
 #pragma unroll
-      for (int rr = 0; rr < RB; ++rr) sk[rr * nbk + beta] = f32_order_key(acc[rr] * inv);
-      amax = fmaxf(amax, ka[beta]);
+        for (int rr = 0; rr < RB; ++rr) acc[rr] = 0.f;
+        for (int c4 = 0; c4 < d4; c4 += 4) {
+          f32x4 v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = kr[c4 + u];
+#pragma unroll
+          for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const f32x4 qv = qs[rr * d4 + c4 + u];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[rr] = fmaf(qv[e], v[u][e], acc[rr]);
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) sk[rr * nbk + beta] = f32_order_key(acc[rr] * inv);
+        amax = fmaxf(amax, ka[beta]);
+      }
     }
     amax = wave_max(amax);
     if (lane == 0) fred[wid] = amax;
@@ -300,15 +345,17 @@ __global__ __launch_bounds__(kBsThreads) void block_select_kernel(BlockSelectPar
   // rigorous bound on |score~ - key| per unit of |q|_1 (amax covers every block of the tile)
   const double uu = 1.0 / 8388608.0;
   auto gam = [&](double n) { return n * uu / (1.0 - n * uu); };
-  // float32 sums (bs terms), then either FMA chains of d products or MFMA
-  // accumulation of 3 d exact bf16 products with the 2^-24 split remainder
-  const double C = MFMA ? 1.25 * (gam(p.bs + 2) + uu * (1.0 + gam(p.bs + 2)) + gam(3 * p.d + 2) * (1.0 + gam(p.bs + 2)) + uu)
-                        : 1.25 * (gam(p.bs + 2) + gam(p.d + 2) * (1.0 + gam(p.bs + 2)) + uu);
+  // float32 sums (bs terms), then either FMA chains of d products, or MFMA
+  // accumulation of the 2 d exact products with the bf16 parts hi + mid of
+  // each sum (|hi| + |mid| <= (1 + 2^-6) |sum|, the remainder below 2^-16 |sum|)
+  const double gb = 1.0 + gam(p.bs + 2);
+  const double C = MFMA ? 1.25 * (gam(p.bs + 2) + gb / 65536.0 + gam(2 * p.d + 2) * (1.0 + 1.0 / 64.0) * gb + uu)
+                        : 1.25 * (gam(p.bs + 2) + gam(p.d + 2) * gb + uu);
   const int ksz = p.k.dt == DT_F32 ? 4 : 2;
 
   uint32_t* hist = whist[wid];
-  uint32_t* bl_i = wband_i[wid];
-  uint32_t* bl_k = wband_k[wid];
+  uint32_t* bl_i = hist;        // band lists: used only while no radix select runs
+  uint32_t* bl_k = hist + 64;
   for (int rr = wid; rr < nrows; rr += 4) {
     const int r = r0 + rr;
     const int ne = __builtin_amdgcn_readfirstlane(ne_of(rr));
@@ -344,7 +391,8 @@ __global__ __launch_bounds__(kBsThreads) void block_select_kernel(BlockSelectPar
     }
     // exact keys of the band (ascending block order), written over the scores
     // in LDS by every lane; the first 64 also into the wave's band list
-    const char* qrow = (const char*)p.q.p + (b * p.q.s[0] + h * p.q.s[1] + (int64_t)r * p.q.s[2]) * esz;
+    const void* qrow = MFMA ? (const void*)(qb + rr * p.d) : (const void*)((const float*)qs + rr * p.d);
+    const int qdt = MFMA ? DT_BF16 : DT_F32;
     int e = 0;
     for (int j = 0; j * 64 < ne; ++j) {
       const int i = j * 64 + lane;
@@ -355,8 +403,8 @@ __global__ __launch_bounds__(kBsThreads) void block_select_kernel(BlockSelectPar
         m &= m - 1;
         const char* kblk = (const char*)p.k.p + (b * p.k.s[0] + hk * p.k.s[1] + (int64_t)beta * p.bs * p.k.s[2]) * ksz;
         const int64_t ob = ((int64_t)b * p.Hkv + hk) * nbk + beta;
-        float key = wave_block_key_sums(p, qrow, p.kbar64 + ob * p.d, p.kexact[ob] != 0, kblk);
-        const uint32_t ok = f32_order_key(__shfl(key, 0, 64));
+        const float key = wave_block_key_sums(p, qrow, qdt, p.kbar64 + ob * p.d, p.kexact + ob, kblk);
+        const uint32_t ok = f32_order_key(__builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, key))));
         wrow[beta] = ok;
         if (e < 64 && lane == 0) {
           bl_i[e] = beta;
@@ -417,8 +465,8 @@ __global__ __launch_bounds__(kBsThreads) void block_select_kernel(BlockSelectPar
 
 size_t block_select_ws_bytes(int B, int Hkv, int ctx, int d, int bs) {
   const size_t nbk = ctx / bs;
-  // kbar64 (2 floats each), kbar, kabs, kexact, then the three bf16 parts (256-byte aligned)
-  return (size_t)B * Hkv * nbk * (3 * d + 2) * sizeof(float) + 256 + (size_t)B * Hkv * nbk * d * 3 * 2;
+  // kbar64 (2 floats each), kbar, kabs, kexact, then the two bf16 parts (256-byte aligned)
+  return (size_t)B * Hkv * nbk * (3 * d + 2) * sizeof(float) + 256 + (size_t)B * Hkv * nbk * d * 2 * 2;
 }
 
 hipError_t launch_block_select(const BlockSelectParams& p, hipStream_t st) {
@@ -429,9 +477,10 @@ hipError_t launch_block_select(const BlockSelectParams& p, hipStream_t st) {
   const int kpl = nbk <= 512 ? 8 : nbk <= 1024 ? 16 : 32;
   const int rb = 128 / kpl;
   const int ntile = (p.Nq + rb - 1) / rb;
-  const size_t lds = (size_t)rb * p.d * 4 + (size_t)rb * nbk * 4;
+  const bool mfma = kpl == 8 && p.q.dt == DT_BF16;
+  const size_t lds = (size_t)rb * p.d * (mfma ? 2 : 4) + (size_t)rb * nbk * 4;
   const dim3 grid(p.B * p.Hq * ntile);
-  if (kpl == 8 && p.q.dt == DT_BF16)
+  if (mfma)
     hipLaunchKernelGGL((block_select_kernel<8, true>), grid, dim3(kBsThreads), lds, st, p, ntile);
   else if (kpl == 8)
     hipLaunchKernelGGL((block_select_kernel<8, false>), grid, dim3(kBsThreads), lds, st, p, ntile);

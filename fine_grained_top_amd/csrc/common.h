@@ -68,6 +68,20 @@ SP_DEV uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// Inclusive prefix sum over the 64 lanes (lane l gets the sum of lanes 0..l)
+// on DPP moves: shifts of 1, 2, 4, 8 inside each 16-lane row (lanes shifted
+// in from outside the row read 0), then lane 15 of rows 0 and 2 added to
+// rows 1 and 3, then lane 31 added to rows 2 and 3. Every lane must be active.
+SP_DEV uint32_t wave_prefix_incl_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
 // Number of active lanes below this one whose predicate is set.
 SP_DEV uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

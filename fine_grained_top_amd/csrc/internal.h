@@ -70,8 +70,8 @@ struct BlockSelectParams {
   float* kabs;             // workspace [B, Hkv, ctx/bs] f32: max_c sum_t |k| per block
   double* kbar64;          // workspace [B, Hkv, ctx/bs, d] f64: the same sums in float64
   uint32_t* kexact;        // workspace [B, Hkv, ctx/bs]: 1 when every float64 sum is exact
-  uint16_t* kb3;           // workspace [3][B, Hkv, ctx/bs, d] bf16: the float32 sums split in three
-                           // (hi + mid + lo within 2^-24 relative), the operands of the MFMA scoring
+  uint16_t* kb2;           // workspace [2][B, Hkv, ctx/bs, d] bf16: the float32 sums split in two
+                           // (hi + mid within 2^-16 relative), the operands of the MFMA scoring
 };
 size_t block_select_ws_bytes(int B, int Hkv, int ctx, int d, int bs);
 hipError_t launch_block_select(const BlockSelectParams& p, hipStream_t st);

@@ -358,8 +358,8 @@ SPATTN_API int spattn_block_select(const spattn_tensor* q, const spattn_tensor* 
   p.kbar = (float*)(p.kbar64 + nblk * p.d);
   p.kabs = p.kbar + nblk * p.d;
   p.kexact = (uint32_t*)(p.kabs + nblk);
-  const uintptr_t kb3 = ((uintptr_t)(p.kexact + nblk) + 255) & ~(uintptr_t)255;
-  p.kb3 = (uint16_t*)kb3;
+  const uintptr_t kb2 = ((uintptr_t)(p.kexact + nblk) + 255) & ~(uintptr_t)255;
+  p.kb2 = (uint16_t*)kb2;
   return launched(sp::launch_block_select(p, (hipStream_t)stream));
 }
 
