@@ -421,7 +421,7 @@ __global__ __launch_bounds__(kBsThreads) __attribute__((amdgpu_waves_per_eu(4)))
       const uint32_t ke = lane < nbd ? bl_k[lane] : 0u;
       int rank = 0;
       for (int f = 0; f < nbd; ++f) {
-        const uint32_t kf = bl_k[f];
+        const uint32_t kf = (uint32_t)__builtin_amdgcn_readlane((int)ke, f);
         rank += (kf > ke || (kf == ke && f < lane)) ? 1 : 0;
       }
       if (lane < nbd) wrow[bl_i[lane]] = rank < R ? ~0u : 0u;

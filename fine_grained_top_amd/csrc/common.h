@@ -82,6 +82,46 @@ SP_DEV uint32_t wave_prefix_incl_u32(uint32_t v) {
   return v;
 }
 
+// Sum and maxima over the 64 lanes with the same DPP pattern, the result
+// read from lane 63 (wave-uniform). For the maxima a lane with no source lane
+// keeps its own value. Every lane must be active.
+SP_DEV float wave_sum_dpp(float v) {
+#define SP_DPP_ADD(ctrl, rm, bc) \
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, rm, 0xf, bc))
+  SP_DPP_ADD(0x111, 0xf, true);
+  SP_DPP_ADD(0x112, 0xf, true);
+  SP_DPP_ADD(0x114, 0xf, true);
+  SP_DPP_ADD(0x118, 0xf, true);
+  SP_DPP_ADD(0x142, 0xa, false);
+  SP_DPP_ADD(0x143, 0xc, false);
+#undef SP_DPP_ADD
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+SP_DEV float wave_max_dpp(float v) {
+#define SP_DPP_MAX(ctrl, rm)                                                                     \
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), \
+                                                                      __builtin_bit_cast(int, v), ctrl, rm, 0xf, false)))
+  SP_DPP_MAX(0x111, 0xf);
+  SP_DPP_MAX(0x112, 0xf);
+  SP_DPP_MAX(0x114, 0xf);
+  SP_DPP_MAX(0x118, 0xf);
+  SP_DPP_MAX(0x142, 0xa);
+  SP_DPP_MAX(0x143, 0xc);
+#undef SP_DPP_MAX
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+SP_DEV uint32_t wave_max_u32_dpp(uint32_t v) {
+#define SP_DPP_UMAX(ctrl, rm) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, ctrl, rm, 0xf, false))
+  SP_DPP_UMAX(0x111, 0xf);
+  SP_DPP_UMAX(0x112, 0xf);
+  SP_DPP_UMAX(0x114, 0xf);
+  SP_DPP_UMAX(0x118, 0xf);
+  SP_DPP_UMAX(0x142, 0xa);
+  SP_DPP_UMAX(0x143, 0xc);
+#undef SP_DPP_UMAX
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Number of active lanes below this one whose predicate is set.
 SP_DEV uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

@@ -69,6 +69,42 @@ SP_DEV double load_f64(const void* p, int dtype, int64_t i) {
   return (double)fp8_to_f32(((const uint8_t*)p)[i]);
 }
 
+// out[e] = element i + e of a row of type dtype as float64 (exact), 0 from
+// element i + avail on. A whole run of four is one vector load: rows start
+// 16-byte aligned and i is a multiple of four, so the run is aligned to its
+// own size.
+template <int N>
+SP_DEV void load_run_f64(const void* p, int dtype, int64_t i, int avail, double (&out)[N]) {
+  if constexpr (N == 4) {
+    if (avail >= 4) {
+      if (dtype == DT_FP8) {
+        const uint32_t w = *(const uint32_t*)((const uint8_t*)p + i);
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+        out[0] = lo[0];
+        out[1] = lo[1];
+        out[2] = hi[0];
+        out[3] = hi[1];
+      } else if (dtype == DT_BF16) {
+        const u32x2 w = *(const u32x2*)((const uint16_t*)p + i);
+        out[0] = bf16_to_f32(w[0] & 0xFFFFu);
+        out[1] = bf16_to_f32(w[0] >> 16);
+        out[2] = bf16_to_f32(w[1] & 0xFFFFu);
+        out[3] = bf16_to_f32(w[1] >> 16);
+      } else {
+        const f32x4 w = *(const f32x4*)((const float*)p + i);
+        out[0] = w[0];
+        out[1] = w[1];
+        out[2] = w[2];
+        out[3] = w[3];
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < N; ++e) out[e] = e < avail ? load_f64(p, dtype, i + e) : 0.0;
+}
+
 // value = m * 2^e with m an integer of at most 24 bits (exact for our formats).
 SP_DEV void split24(double v, int64_t& m, int& e, bool& neg) {
   neg = v < 0;
@@ -306,17 +342,13 @@ SP_DEV float group_exact_key(const IndexerRow& r, int64_t j, const float* qs = n
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       if (r.relu && h0 + u < r.H) wv[u] = wsg ? (double)wsg[h0 + u] : (double)r.w[(h0 + u) * r.w_stride];
-    constexpr int NK = 64 / W;                 // the lane's elements per 64 dimensions
+    constexpr int NK = 64 / W;                 // the lane's elements per 64 dimensions: a contiguous run
     for (int c0 = 0; c0 < r.d; c0 += 64) {
-      double kv[NK];                           // loads in flight together
+      double kv[NK];                           // one vector load where the run is whole
+      load_run_f64<NK>(r.k, r.kt, koff + c0 + NK * lane, r.d - c0 - NK * lane, kv);
 #pragma unroll
       for (int i = 0; i < NK; ++i) {
-        const int c = c0 + lane + W * i;
-        kv[i] = c < r.d ? load_f64(r.k, r.kt, koff + c) : 0.0;
-      }
-#pragma unroll
-      for (int i = 0; i < NK; ++i) {
-        const int c = c0 + lane + W * i;
+        const int c = c0 + NK * lane + i;
         if (c >= r.d) break;
 #pragma unroll
         for (int u = 0; u < 4; ++u)

@@ -37,12 +37,7 @@ template <int T>
 SP_DEV uint32_t block_scan_sum(uint32_t v, uint32_t* scratch, uint32_t& total) {
   constexpr int NW = T / 64;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t u = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += u;
-  }
+  const uint32_t incl = wave_prefix_incl_u32(v);
   if (lane == 63) scratch[wid] = incl;
   __syncthreads();
   uint32_t base = 0, tot = 0;
@@ -91,13 +86,9 @@ SP_DEV void radix_select(int n, uint32_t R, Get get, uint32_t* hist, uint32_t* s
     uint32_t mine = 0;
     if (lo < nb)
       for (int q = 0; q < per; ++q) mine += hist[lo + q];
-    // inclusive suffix scan within the wave (higher lanes own higher bins)
-    uint32_t v = mine;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t u = __shfl_down(v, o, 64);
-      if (lane + o < 64) v += u;
-    }
+    // inclusive suffix sum within the wave (higher lanes own higher bins)
+    const uint32_t pin = wave_prefix_incl_u32(mine);
+    const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)pin, 63) - pin + mine;
     if (lane == 0) sc[wid] = v;   // wave total
     __syncthreads();
     uint32_t higher_waves = 0;

@@ -265,6 +265,37 @@ union R2Smem {
 };
 static_assert(sizeof(R2Smem) <= 40960, "two-pass top-K shared memory must allow four workgroups per CU");
 
+// Mark in bm the R2 best band members by (exact key desc, position asc). A
+// band of at most 64 is ranked by wave 0 from registers (readlane), a larger
+// one by every thread from LDS. The caller synchronizes afterwards.
+template <int T>
+SP_DEV void band_mark(const uint32_t* band_k, const uint32_t* band_j, uint32_t nb, uint32_t R2, uint32_t* bm) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (nb <= 64) {
+    if (tid < 64) {
+      const uint32_t ke = (uint32_t)lane < nb ? band_k[lane] : 0u;
+      const uint32_t je = (uint32_t)lane < nb ? band_j[lane] : 0u;
+      uint32_t rank = 0;
+      for (uint32_t f = 0; f < nb; ++f) {
+        const uint32_t kf = (uint32_t)__builtin_amdgcn_readlane((int)ke, (int)f);
+        const uint32_t jf = (uint32_t)__builtin_amdgcn_readlane((int)je, (int)f);
+        rank += (kf > ke || (kf == ke && jf < je)) ? 1u : 0u;
+      }
+      if ((uint32_t)lane < nb && rank < R2) atomicOr(&bm[je >> 5], 1u << (je & 31));
+    }
+    return;
+  }
+  for (uint32_t e = tid; e < nb; e += T) {
+    const uint32_t ke = band_k[e], je = band_j[e];
+    uint32_t rank = 0;
+    for (uint32_t f = 0; f < nb; ++f) {
+      const uint32_t kf = band_k[f];
+      rank += (kf > ke || (kf == ke && band_j[f] < je)) ? 1u : 0u;
+    }
+    if (rank < R2) atomicOr(&bm[je >> 5], 1u << (je & 31));
+  }
+}
+
 // Resolve the candidate list (keys ck, indices cj, n_cand of them) that holds
 // the remaining R slots; sets the selected bits in bm. Returns false when the
 // band is too wide for the short list (caller redoes the row).
@@ -310,35 +341,35 @@ SP_DEV bool resolve_candidates(const TopkParams& p, RowCtx& c, SM& rs, uint32_t*
     }
     __syncthreads();
   }
-  for (uint32_t e = tid; e < nb; e += T) {
-    const uint32_t ke = rs.band_k[e], je = rs.band_j[e];
-    uint32_t rank = 0;
-    for (uint32_t f = 0; f < nb; ++f) {
-      const uint32_t kf = rs.band_k[f];
-      rank += (kf > ke || (kf == ke && rs.band_j[f] < je)) ? 1u : 0u;
-    }
-    if (rank < R2) atomicOr(&bm[je >> 5], 1u << (je & 31));
-  }
+  band_mark<T>(rs.band_k, rs.band_j, nb, R2, bm);
   __syncthreads();
   return true;
 }
 
-// Write the set bits of bm (nwords words) as ascending indices, pad with -1.
-template <int T, typename SM>
+// Write the set bits of bm (nwords <= MAXW words) as ascending indices, pad
+// with -1. Thread t owns a contiguous run of words, read from LDS once.
+template <int T, int MAXW, typename SM>
 SP_DEV void emit_bitmap(const TopkParams& p, const RowCtx& c, SM& rs, const uint32_t* bm, int nwords) {
+  constexpr int PW = (MAXW + T - 1) / T;
   const int tid = threadIdx.x;
   const int perw = (nwords + T - 1) / T;
-  const int w0 = tid * perw, w1 = min(nwords, w0 + perw);
+  const int w0 = tid * perw;
+  uint32_t wv[PW];
   uint32_t cnt = 0;
-  for (int i = w0; i < w1; ++i) cnt += __popc(bm[i]);
+#pragma unroll
+  for (int q = 0; q < PW; ++q) {
+    wv[q] = (q < perw && w0 + q < nwords) ? bm[w0 + q] : 0u;
+    cnt += __popc(wv[q]);
+  }
   uint32_t total;
   uint32_t pos = block_scan_sum<T>(cnt, rs.sc, total);
-  for (int i = w0; i < w1; ++i) {
-    uint32_t m = bm[i];
+#pragma unroll
+  for (int q = 0; q < PW; ++q) {
+    uint32_t m = wv[q];
     while (m) {
       const int bit = __ffs(m) - 1;
       m &= m - 1;
-      if (pos < (uint32_t)p.K) c.out[pos] = i * 32 + bit;
+      if (pos < (uint32_t)p.K) c.out[pos] = (w0 + q) * 32 + bit;
       ++pos;
     }
   }
@@ -526,7 +557,7 @@ __global__ __launch_bounds__(kR2Threads) __attribute__((amdgpu_waves_per_eu(4)))
     uint32_t wlo, whi;
     band_limits(p, c, 0.f, order_key_f32(tlo), order_key_f32(thi), wlo, whi);
     __syncthreads();
-    if (pass2(wlo, whi, tlo, thi)) return emit_bitmap<T>(p, c, sm.row, sm.bm, nwords);
+    if (pass2(wlo, whi, tlo, thi)) return emit_bitmap<T, kR2Words>(p, c, sm.row, sm.bm, nwords);
     __syncthreads();
   }
 
@@ -570,7 +601,7 @@ __global__ __launch_bounds__(kR2Threads) __attribute__((amdgpu_waves_per_eu(4)))
     if (p.count && tid == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = p.K;
     return;
   }
-  emit_bitmap<T>(p, c, sm.row, sm.bm, nwords);
+  emit_bitmap<T, kR2Words>(p, c, sm.row, sm.bm, nwords);
 }
 
 // ---------------------------------------------------------------- multi-workgroup schedule
@@ -867,6 +898,17 @@ SP_DEV float recompute_score(const IndexerRow& r, int64_t j) {
   return s;
 }
 
+// the bound from its inputs: CO = sum over the group's heads and dims of
+// |w_h q_hc| (summed in float32 in any order), KM = max |k| over the row's keys
+SP_DEV float eps_of(const IndexerParams& x, float CO, float KM) {
+  const double u = 1.0 / 8388608.0;
+  auto gam = [&](double n) { return n * u / (1.0 - n * u); };
+  const double C = 1.25 * (gam(x.d_I + 2) + gam(x.hpg + 2) * (1.0 + gam(x.d_I + 2)) + u);
+  // CO was summed in float32: inflate by its own rounding bound
+  const double e = C * (double)CO * (1.0 + gam(x.hpg * x.d_I + 2)) * (double)KM * (1.0 + 1e-6) + 1e-30;
+  return (float)e * (1.0f + 1e-6f);
+}
+
 // rigorous |score~ - key| bound of a row, as computed by the indexer
 SP_DEV float row_eps(const TopkParams& p, const RowCtx& c, const float* kmax, int nchunk, int chunk,
                      float* red) {
@@ -896,12 +938,7 @@ SP_DEV float row_eps(const TopkParams& p, const RowCtx& c, const float* kmax, in
     CO += red[16 + w];
   }
   __syncthreads();
-  const double u = 1.0 / 8388608.0;
-  auto gam = [&](double n) { return n * u / (1.0 - n * u); };
-  const double C = 1.25 * (gam(x.d_I + 2) + gam(x.hpg + 2) * (1.0 + gam(x.d_I + 2)) + u);
-  // coef was summed in float32: inflate by its own rounding bound
-  const double e = C * (double)CO * (1.0 + gam(x.hpg * x.d_I + 2)) * (double)KM * (1.0 + 1e-6) + 1e-30;
-  return (float)e * (1.0f + 1e-6f);
+  return eps_of(x, CO, KM);
 }
 
 // Pilot, stage 1: one thread per (sampled key, selection row): the row's
@@ -1083,7 +1120,7 @@ struct FzSmem {
   uint32_t cj[kCandCap];
   uint32_t bm[kMaxWords];
   uint32_t coff[kTkThreads + 1];
-  float red[32];
+  float red[5 * (kTkThreads / 64)];   // per-wave partials: key bound, 1-norm, count, overflow, largest key
 };
 
 __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs w) {
@@ -1092,76 +1129,111 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   RowCtx c = row_ctx(p, row);
   if (c.n <= p.K) return write_all(p, c, T);
-  // the row's queries and weights into LDS for the exact band keys
-  for (int e = tid; e < c.ir.H * c.ir.d; e += T)
-    sm.qs[e] = (float)load_f64(c.ir.q, c.ir.qt, (e / c.ir.d) * c.ir.qh_stride + e % c.ir.d);
-  if (tid < c.ir.H) sm.wsg[tid] = c.ir.relu ? c.ir.w[tid * c.ir.w_stride] : 1.f;
-  // candidate counts of the chunks covering keys 0..p (nch <= T), loaded
-  // together with the inputs of the error bound
+  // one pass over the inputs: the row's queries and weights (into LDS for the
+  // exact band keys, and the weighted 1-norm of the queries for the error
+  // bound), the key bounds of the request's chunks, the candidate counts of
+  // the chunks covering keys 0..p (nch <= T) and the pilot threshold; one
+  // barrier publishes the per-wave partials
+  constexpr int NW = T / 64;
+  const int wid = tid >> 6;
   const int nch = (c.n + 511) / 512;
-  uint32_t my = 0;
+  const int L = min(p.ctx_len ? p.ctx_len[c.b] : p.ctx, p.ctx);
+  const int nch_k = min(w.nchunk, (L + 511) / 512);
   // candidate arrays: [request][chunk][selection row of the request][cap]
   const int nrl = p.G * p.Nq, rowl = c.g * p.Nq + c.r;
-  if (tid < nch) my = w.cand_n[((int64_t)c.b * w.nchunk + tid) * nrl + rowl];
-  c.eps = row_eps(p, c, w.kmax, w.nchunk, 512, sm.red);
+  const uint32_t my = tid < nch ? w.cand_n[((int64_t)c.b * w.nchunk + tid) * nrl + rowl] : 0u;
+  float km = 0.f, coef = 0.f;
+  for (int i = tid; i < nch_k; i += T) km = fmaxf(km, w.kmax[(int64_t)c.b * w.nchunk + i]);
+  const float tau = w.tau[row];
+  for (int e = tid; e < c.ir.H * c.ir.d; e += T) {
+    const int hh = e / c.ir.d;
+    const float qv = (float)load_f64(c.ir.q, c.ir.qt, hh * c.ir.qh_stride + e % c.ir.d);
+    sm.qs[e] = qv;
+    coef = fmaf(c.ir.relu ? fabsf(c.ir.w[hh * c.ir.w_stride]) : 1.f, fabsf(qv), coef);
+  }
+  if (tid < c.ir.H) sm.wsg[tid] = c.ir.relu ? c.ir.w[tid * c.ir.w_stride] : 1.f;
+  const uint32_t incl = wave_prefix_incl_u32(my);
+  km = wave_max_dpp(km);
+  coef = wave_sum_dpp(coef);
+  const bool wover = __any(my > (uint32_t)w.cap);
+  if (lane == 63) {
+    sm.red[wid] = km;
+    sm.red[NW + wid] = coef;
+    sm.red[2 * NW + wid] = __uint_as_float(incl);
+    sm.red[3 * NW + wid] = wover ? 1.f : 0.f;
+  }
+  __syncthreads();
+  float KM = 0.f, CO = 0.f;
+  uint32_t wbase = 0, n_cand = 0;
+  bool any_over = false;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    KM = fmaxf(KM, sm.red[v]);
+    CO += sm.red[NW + v];
+    const uint32_t tv = __float_as_uint(sm.red[2 * NW + v]);
+    wbase += v < wid ? tv : 0u;
+    n_cand += tv;
+    any_over |= sm.red[3 * NW + v] != 0.f;
+  }
+  c.eps = eps_of(p.ix, CO, KM);
   const float eps = c.eps;
   auto fallback = [&]() {
     row_topk_single<T>(p, c, sm.row, [&](int i) { return recompute_score(c.ir, i); });
     if (p.count && tid == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = p.K;
   };
-  const bool over = my > (uint32_t)w.cap;
-  uint32_t n_cand;
-  const uint32_t off = block_scan_sum<T>(my, sm.row.sc, n_cand);
-  if (tid < nch) sm.coff[tid] = off;
-  if (tid == 0) sm.coff[nch] = n_cand;
-  const bool any_over = __syncthreads_or(over) != 0;
   if (any_over || n_cand < (uint32_t)p.K || n_cand > (uint32_t)kCandCap) return fallback();
+  if (tid < nch) sm.coff[tid] = wbase + incl - my;
+  if (tid == 0) sm.coff[nch] = n_cand;
+  __syncthreads();
   // compact into LDS: wave w copies chunks w, w + NW, ... (lane l: slot l);
-  // the loads of 32 chunks are in flight together
+  // lane u first reads the offset and count of the batch's chunk u, which
+  // the loops take with readlane, so the loads of 32 chunks issue back to back
+  uint32_t kmx = 0;      // the largest candidate key, from the copied keys
   {
-    constexpr int NW = T / 64, CPW = 32;
-    const int wid = tid >> 6;
+    constexpr int CPW = 32;
     for (int c0 = wid; c0 < nch; c0 += NW * CPW) {
+      const int chl = c0 + (lane & (CPW - 1)) * NW;
+      const uint32_t ol = chl < nch ? sm.coff[chl] : 0u;
+      const uint32_t nl = chl < nch ? sm.coff[chl + 1] - ol : 0u;
       uint32_t kk[CPW], jj[CPW];
 #pragma unroll
       for (int u = 0; u < CPW; ++u) {
         const int ch = c0 + u * NW;
-        const int n = ch < nch ? (int)(sm.coff[ch + 1] - sm.coff[ch]) : 0;
+        const int n = __builtin_amdgcn_readlane((int)nl, u);
         const int64_t src = (((int64_t)c.b * w.nchunk + ch) * nrl + rowl) * w.cap + lane;
         const u32x2 cv = lane < n ? w.cand[src] : u32x2{0u, 0u};
         kk[u] = cv[0];
         jj[u] = cv[1];
       }
 #pragma unroll
+      for (int u = 0; u < CPW; ++u) kmx = max(kmx, kk[u]);
+#pragma unroll
       for (int u = 0; u < CPW; ++u) {
         const int ch = c0 + u * NW;
-        if (ch < nch) {
-          const uint32_t o = sm.coff[ch], n = sm.coff[ch + 1] - o;
-          if ((uint32_t)lane < n) {
-            sm.ck[o + lane] = kk[u];
-            sm.cj[o + lane] = jj[u];
-          }
-          for (uint32_t e = lane + 64; e < n; e += 64) {   // more than 64 in a chunk: rare
-            const int64_t src = (((int64_t)c.b * w.nchunk + ch) * nrl + rowl) * w.cap + e;
-            const u32x2 cv = w.cand[src];
-            sm.ck[o + e] = cv[0];
-            sm.cj[o + e] = cv[1];
-          }
+        const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)ol, u);
+        const uint32_t n = (uint32_t)__builtin_amdgcn_readlane((int)nl, u);
+        if ((uint32_t)lane < n) {
+          sm.ck[o + lane] = kk[u];
+          sm.cj[o + lane] = jj[u];
+        }
+        for (uint32_t e = lane + 64; e < n; e += 64) {   // more than 64 in a chunk: rare
+          const int64_t src = (((int64_t)c.b * w.nchunk + ch) * nrl + rowl) * w.cap + e;
+          const u32x2 cv = w.cand[src];
+          sm.ck[o + e] = cv[0];
+          sm.cj[o + e] = cv[1];
+          kmx = max(kmx, cv[0]);
         }
       }
     }
   }
+  kmx = wave_max_u32_dpp(kmx);
+  if (lane == 63) sm.red[4 * NW + wid] = __uint_as_float(kmx);
   const int nwords = (c.n + 31) >> 5;
   for (int i = tid; i < nwords; i += T) sm.bm[i] = 0u;
   __syncthreads();
-  const uint32_t base = f32_order_key(w.tau[row]);
-  uint32_t kmx = 0;
-  for (uint32_t i = tid; i < n_cand; i += T) kmx = max(kmx, sm.ck[i]);
-  kmx = wave_max_u32(kmx);
-  if (lane == 0) sm.row.sc[tid >> 6] = kmx;
-  __syncthreads();
-  for (int i = 0; i < T / 64; ++i) kmx = max(kmx, sm.row.sc[i]);
-  __syncthreads();
+  const uint32_t base = f32_order_key(tau);
+#pragma unroll
+  for (int v = 0; v < NW; ++v) kmx = max(kmx, __float_as_uint(sm.red[4 * NW + v]));
   const int bits = 32 - __builtin_clz((kmx - base) | 1u);
   uint32_t t, above;
   radix_select<T>((int)n_cand, (uint32_t)p.K, [&](int i, uint32_t& k) { k = sm.ck[i]; return true; },
@@ -1197,33 +1269,9 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
     if ((lane & 15) == 0) sm.row.band_k[e] = f32_order_key(key);
   }
   __syncthreads();
-  for (uint32_t e = tid; e < nb; e += T) {
-    const uint32_t ke = sm.row.band_k[e], je = sm.row.band_j[e];
-    uint32_t rank = 0;
-    for (uint32_t f = 0; f < nb; ++f) {
-      const uint32_t kf = sm.row.band_k[f];
-      rank += (kf > ke || (kf == ke && sm.row.band_j[f] < je)) ? 1u : 0u;
-    }
-    if (rank < R2) atomicOr(&sm.bm[je >> 5], 1u << (je & 31));
-  }
+  band_mark<T>(sm.row.band_k, sm.row.band_j, nb, R2, sm.bm);
   __syncthreads();
-  const int perw = (nwords + T - 1) / T;
-  const int w0 = tid * perw, w1 = min(nwords, w0 + perw);
-  uint32_t cnt = 0;
-  for (int i = w0; i < w1; ++i) cnt += __popc(sm.bm[i]);
-  uint32_t total;
-  uint32_t pos = block_scan_sum<T>(cnt, sm.row.sc, total);
-  for (int i = w0; i < w1; ++i) {
-    uint32_t m = sm.bm[i];
-    while (m) {
-      const int bit = __ffs(m) - 1;
-      m &= m - 1;
-      if (pos < (uint32_t)p.K) c.out[pos] = i * 32 + bit;
-      ++pos;
-    }
-  }
-  for (int i = (int)total + tid; i < p.K; i += T) c.out[i] = -1;
-  if (p.count && tid == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = (int)min(total, (uint32_t)p.K);
+  emit_bitmap<T, kMaxWords>(p, c, sm.row, sm.bm, nwords);
 }
 
 static constexpr int kFzCap = 512;   // = keys per indexer chunk: a chunk can never overflow
