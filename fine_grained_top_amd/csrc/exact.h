@@ -58,6 +58,37 @@ SP_DEV void group_xreduce(double& y, bool& exact, double& A) {
   const uint64_t gm = W == 64 ? ~0ull : ((1ull << W) - 1) << base;
   exact = (bad & gm) == 0;
 }
+
+// A float64 rotated by N lanes within each 16-lane row (DPP row_ror; every
+// source lane is valid).
+template <int N>
+SP_DEV double row_ror_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, 0x120 + N, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), 0x120 + N, 0xf, 0xf, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// group_xreduce<16> of NH independent sums at once: rotations by 8, 4, 2, 1
+// within the 16-lane row, the sums interleaved level by level. Lanes add the
+// same pairs in swapped order (commutative, so every lane ends with the same
+// bits, and both see the same rounding).
+template <int NH>
+SP_DEV void row16_xreduce(double (&y)[NH], bool (&exact)[NH], double (&A)[NH]) {
+#define SP_ROR_STEP(N)                                   \
+  _Pragma("unroll") for (int u = 0; u < NH; ++u) {       \
+    xadd(y[u], exact[u], row_ror_f64<N>(y[u]));          \
+    A[u] += row_ror_f64<N>(A[u]);                        \
+  }
+  SP_ROR_STEP(8)
+  SP_ROR_STEP(4)
+  SP_ROR_STEP(2)
+  SP_ROR_STEP(1)
+#undef SP_ROR_STEP
+  const uint64_t gm = 0xFFFFull << ((threadIdx.x & 63) & ~15);
+#pragma unroll
+  for (int u = 0; u < NH; ++u) exact[u] = (ballot(!exact[u]) & gm) == 0;
+}
 SP_DEV void wave_xreduce(double& y, bool& exact, double& A) { group_xreduce<64>(y, exact, A); }
 
 // float32 key of an exact float64 value (-0 read as +0)
@@ -320,16 +351,19 @@ SP_DEV float exact_key(const IndexerRow& r, int64_t j) {
   return exact_key_slow(r, j);
 }
 
-// The same key computed by a group of W aligned lanes (a wave, or a half-wave
-// so that two candidates are scored at once) for one candidate j (group-
-// uniform): lanes split the dimensions; every load of a group of four heads
-// (operands and weights) is issued before any reduction, and per-head sums
-// are reduced across the group.
-template <int W>
-SP_DEV float group_exact_key(const IndexerRow& r, int64_t j, const float* qs = nullptr, const float* wsg = nullptr) {
-  // qs/wsg (optional): the row's queries [H][d] and weights [H] already in
-  // LDS as float (exact copies of the bf16/f32 inputs)
+// The same key computed by a group of W aligned lanes (a wave, or a quarter-
+// wave so that several candidates are scored at once) for one candidate j
+// (group-uniform): lane l takes a contiguous run of 64 / W dimensions of
+// every 64 (one vector load of the key row; zeros past d add nothing), heads
+// go four at a time with all their operands loaded before the reduction, and
+// the per-head sums are reduced across the group. QL: the row's queries and
+// weights are in LDS (qs [H][d], wsg [H], exact float copies); otherwise they
+// are read from the inputs. The code is straight-line apart from uniform
+// branches on H and on the score mode.
+template <int W, bool QL>
+SP_DEV float group_exact_key_impl(const IndexerRow& r, int64_t j, const float* qs, const float* wsg) {
   const double g52 = 2.220446049250313e-16;
+  constexpr int NK = 64 / W;
   const int lane = threadIdx.x & (W - 1);
   const int base = (threadIdx.x & 63) & ~(W - 1);
   const int64_t koff = j * r.k_stride;
@@ -341,50 +375,59 @@ SP_DEV float group_exact_key(const IndexerRow& r, int64_t j, const float* qs = n
     double wv[4] = {0.0, 0.0, 0.0, 0.0};      // loaded with the operands, used after the reduction
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (r.relu && h0 + u < r.H) wv[u] = wsg ? (double)wsg[h0 + u] : (double)r.w[(h0 + u) * r.w_stride];
-    constexpr int NK = 64 / W;                 // the lane's elements per 64 dimensions: a contiguous run
+      if (r.relu && h0 + u < r.H) wv[u] = QL ? (double)wsg[h0 + u] : (double)r.w[(h0 + u) * r.w_stride];
     for (int c0 = 0; c0 < r.d; c0 += 64) {
-      double kv[NK];                           // one vector load where the run is whole
-      load_run_f64<NK>(r.k, r.kt, koff + c0 + NK * lane, r.d - c0 - NK * lane, kv);
+      const int cb = c0 + NK * lane;
+      double kv[NK];
+      load_run_f64<NK>(r.k, r.kt, koff + cb, r.d - cb, kv);
 #pragma unroll
-      for (int i = 0; i < NK; ++i) {
-        const int c = c0 + NK * lane + i;
-        if (c >= r.d) break;
+      for (int u = 0; u < 4; ++u) {
+        if (h0 + u < r.H) {
+          double qv[NK];
+          if constexpr (QL) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (h0 + u < r.H) {
-            const double qv = qs ? (double)qs[(h0 + u) * r.d + c] : load_f64(r.q, r.qt, (h0 + u) * r.qh_stride + c);
-            const double t = qv * kv[i];       // exact product
+            for (int i = 0; i < NK; ++i) qv[i] = cb + i < r.d ? (double)qs[(h0 + u) * r.d + cb + i] : 0.0;
+          } else {
+            load_run_f64<NK>(r.q, r.qt, (h0 + u) * r.qh_stride + cb, r.d - cb, qv);
+          }
+#pragma unroll
+          for (int i = 0; i < NK; ++i) {
+            const double t = qv[i] * kv[i];   // exact product
             xadd(y[u], x[u], t);
             A[u] += fabs(t);
           }
+        }
       }
     }
+    if constexpr (W == 16) {
+      row16_xreduce<4>(y, x, A);
+    } else {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) group_xreduce<W>(y[u], x[u], A[u]);
+      for (int u = 0; u < 4; ++u) group_xreduce<W>(y[u], x[u], A[u]);
+    }
+    if (!r.relu) {                             // plain dot: one head
+      if (x[0]) return key_of_exact(y[0]);
+      float key;
+      if (certify(y[0], 2.0 * (r.d + 70) * g52 * A[0] + 1e-300, key)) return key;
+      ok = false;
+      break;
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (h0 + u >= r.H) break;
-      const double E = 2.0 * (r.d + 70) * g52 * A[u] + 1e-300;   // r.d / W + log2 W terms per path
-      if (!r.relu) {
-        if (x[u]) return key_of_exact(y[u]);
-        float key;
-        if (certify(y[u], E, key)) return key;
-        ok = false;
-        break;
-      }
-      const double w = wv[u];
-      if (!x[u]) xall = false;
-      else if (y[u] > 0.0 && w != 0.0) xadd_prod(sx, xall, w, y[u]);
-      if (y[u] > E) {
-        s += w * y[u];
-        Es += fabs(w) * E;
-        Ar += fabs(w * y[u]);
-      } else if (!(y[u] < -E) && w != 0.0) {
-        ok = false;
+      if (h0 + u < r.H) {
+        const double E = 2.0 * (r.d + 70) * g52 * A[u] + 1e-300;   // r.d / W + log2 W terms per path
+        const double w = wv[u];
+        if (!x[u]) xall = false;
+        else if (y[u] > 0.0 && w != 0.0) xadd_prod(sx, xall, w, y[u]);
+        if (y[u] > E) {
+          s += w * y[u];
+          Es += fabs(w) * E;
+          Ar += fabs(w * y[u]);
+        } else if (!(y[u] < -E) && w != 0.0) {
+          ok = false;
+        }
       }
     }
-    if (!r.relu) break;
   }
   if (r.relu && xall) return key_of_exact(sx);
   float key = 0.f;
@@ -392,6 +435,13 @@ SP_DEV float group_exact_key(const IndexerRow& r, int64_t j, const float* qs = n
   float slow = 0.f;
   if (lane == 0) slow = exact_key_slow(r, j);
   return __shfl(slow, base, 64);
+}
+
+// qs/wsg (optional, together): the row's queries [H][d] and weights [H]
+// already in LDS as float (exact copies of the bf16/f32 inputs)
+template <int W>
+SP_DEV float group_exact_key(const IndexerRow& r, int64_t j, const float* qs = nullptr, const float* wsg = nullptr) {
+  return qs ? group_exact_key_impl<W, true>(r, j, qs, wsg) : group_exact_key_impl<W, false>(r, j, nullptr, nullptr);
 }
 SP_DEV float wave_exact_key(const IndexerRow& r, int64_t j) { return group_exact_key<64>(r, j); }
 

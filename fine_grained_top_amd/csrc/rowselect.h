@@ -57,9 +57,14 @@ SP_DEV uint32_t block_scan_sum(uint32_t v, uint32_t* scratch, uint32_t& total) {
 // to `base` and must lie in [base, base + 2^bits) for included elements; the
 // bits are consumed from the top in digits of at most 12. On return: t = that
 // key (absolute), above = number of included elements with key > t.
+// With thi given, the passes may stop early, once the keys left in the chosen
+// bin span at most tol as floats (order keys of finite floats): then t and
+// *thi are the ends of that bin (the R-th largest lies in [t, *thi]) and
+// above counts the elements above the bin; otherwise *thi = t.
 template <int T, typename Get>
 SP_DEV void radix_select(int n, uint32_t R, Get get, uint32_t* hist, uint32_t* sc,
-                         uint32_t& t, uint32_t& above, uint32_t base = 0u, int bits = 32) {
+                         uint32_t& t, uint32_t& above, uint32_t base = 0u, int bits = 32,
+                         uint32_t* thi = nullptr, float tol = -1.f) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   constexpr int NW = T / 64;
   uint32_t prefix = 0, pmask = 0, acc_above = 0, need = R;
@@ -114,8 +119,14 @@ SP_DEV void radix_select(int n, uint32_t R, Get get, uint32_t* hist, uint32_t* s
     prefix |= bin << sh;
     pmask |= dmask << sh;
     left = sh;
+    if (thi && left > 0) {
+      const float flo = order_key_f32(base + prefix);
+      const float fhi = order_key_f32(base + (prefix | ((1u << left) - 1u)));
+      if (fhi - flo <= tol) break;          // false for a non-finite end: keep refining
+    }
   }
   t = prefix + base;
+  if (thi) *thi = base + (prefix | (left > 0 ? (1u << left) - 1u : 0u));
   above = acc_above;
 }
 

@@ -1185,43 +1185,47 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
   if (tid < nch) sm.coff[tid] = wbase + incl - my;
   if (tid == 0) sm.coff[nch] = n_cand;
   __syncthreads();
-  // compact into LDS: wave w copies chunks w, w + NW, ... (lane l: slot l);
-  // lane u first reads the offset and count of the batch's chunk u, which
-  // the loops take with readlane, so the loads of 32 chunks issue back to back
+  // compact into LDS: wave w copies chunks w, w + NW, ..., two chunks per
+  // load instruction (32 lanes each, lane l: slot l mod 32) and 32 chunks per
+  // batch, whose offsets and counts are read first; candidate offsets within
+  // the request's arrays fit 32 bits (checked at launch)
   uint32_t kmx = 0;      // the largest candidate key, from the copied keys
   {
-    constexpr int CPW = 32;
-    for (int c0 = wid; c0 < nch; c0 += NW * CPW) {
-      const int chl = c0 + (lane & (CPW - 1)) * NW;
-      const uint32_t ol = chl < nch ? sm.coff[chl] : 0u;
-      const uint32_t nl = chl < nch ? sm.coff[chl + 1] - ol : 0u;
-      uint32_t kk[CPW], jj[CPW];
+    constexpr int CPI = 2, IT = 16;
+    const int sub = lane >> 5;
+    const uint32_t sl = (uint32_t)(lane & 31);
+    const u32x2* cb = w.cand + (int64_t)c.b * w.nchunk * nrl * w.cap + (int64_t)rowl * w.cap;
+    const uint32_t cstep = (uint32_t)(nrl * w.cap);     // pairs between a row's slots of consecutive chunks
+    for (int c0 = wid; c0 < nch; c0 += NW * CPI * IT) {
+      uint32_t oo[IT], nn[IT];
 #pragma unroll
-      for (int u = 0; u < CPW; ++u) {
-        const int ch = c0 + u * NW;
-        const int n = __builtin_amdgcn_readlane((int)nl, u);
-        const int64_t src = (((int64_t)c.b * w.nchunk + ch) * nrl + rowl) * w.cap + lane;
-        const u32x2 cv = lane < n ? w.cand[src] : u32x2{0u, 0u};
-        kk[u] = cv[0];
-        jj[u] = cv[1];
+      for (int it = 0; it < IT; ++it) {
+        const int ch = c0 + NW * (CPI * it + sub);
+        oo[it] = ch < nch ? sm.coff[ch] : 0u;
+        nn[it] = ch < nch ? sm.coff[ch + 1] - oo[it] : 0u;
+      }
+      u32x2 cv[IT];
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const uint32_t ch = (uint32_t)(c0 + NW * (CPI * it + sub));
+        cv[it] = sl < nn[it] ? cb[ch * cstep + sl] : u32x2{0u, 0u};
       }
 #pragma unroll
-      for (int u = 0; u < CPW; ++u) kmx = max(kmx, kk[u]);
-#pragma unroll
-      for (int u = 0; u < CPW; ++u) {
-        const int ch = c0 + u * NW;
-        const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)ol, u);
-        const uint32_t n = (uint32_t)__builtin_amdgcn_readlane((int)nl, u);
-        if ((uint32_t)lane < n) {
-          sm.ck[o + lane] = kk[u];
-          sm.cj[o + lane] = jj[u];
+      for (int it = 0; it < IT; ++it) {
+        if (sl < nn[it]) {
+          sm.ck[oo[it] + sl] = cv[it][0];
+          sm.cj[oo[it] + sl] = cv[it][1];
+          kmx = max(kmx, cv[it][0]);
         }
-        for (uint32_t e = lane + 64; e < n; e += 64) {   // more than 64 in a chunk: rare
-          const int64_t src = (((int64_t)c.b * w.nchunk + ch) * nrl + rowl) * w.cap + e;
-          const u32x2 cv = w.cand[src];
-          sm.ck[o + e] = cv[0];
-          sm.cj[o + e] = cv[1];
-          kmx = max(kmx, cv[0]);
+      }
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const uint32_t ch = (uint32_t)(c0 + NW * (CPI * it + sub));
+        for (uint32_t e = sl + 32; e < nn[it]; e += 32) {   // more than 32 in a chunk
+          const u32x2 v = cb[ch * cstep + e];
+          sm.ck[oo[it] + e] = v[0];
+          sm.cj[oo[it] + e] = v[1];
+          kmx = max(kmx, v[0]);
         }
       }
     }
@@ -1235,13 +1239,14 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
 #pragma unroll
   for (int v = 0; v < NW; ++v) kmx = max(kmx, __float_as_uint(sm.red[4 * NW + v]));
   const int bits = 32 - __builtin_clz((kmx - base) | 1u);
-  uint32_t t, above;
-  radix_select<T>((int)n_cand, (uint32_t)p.K, [&](int i, uint32_t& k) { k = sm.ck[i]; return true; },
-                  sm.row.hist, sm.row.sc, t, above, base, bits);
-  const float tf = order_key_f32(t);
+  // the K-th largest key lies in [t, thi]; the radix passes stop once that
+  // bin spans at most E as floats (the band below grows by at most that)
   const float E = 2.0f * eps * 1.0001f + 1e-30f;
-  const uint32_t klo = f32_order_key(nextafterf(tf - E, -INFINITY));
-  const uint32_t khi = f32_order_key(nextafterf(tf + E, INFINITY));
+  uint32_t t, thi, above;
+  radix_select<T>((int)n_cand, (uint32_t)p.K, [&](int i, uint32_t& k) { k = sm.ck[i]; return true; },
+                  sm.row.hist, sm.row.sc, t, above, base, bits, &thi, E);
+  const uint32_t klo = f32_order_key(nextafterf(order_key_f32(t) - E, -INFINITY));
+  const uint32_t khi = f32_order_key(nextafterf(order_key_f32(thi) + E, INFINITY));
   if (klo < base) return fallback();        // part of the band may lie below tau
   uint32_t n_in = 0;
   if (tid == 0) sm.row.run[0] = 0;
@@ -1277,8 +1282,10 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
 static constexpr int kFzCap = 512;   // = keys per indexer chunk: a chunk can never overflow
 
 bool topk_fused_ok(const TopkParams& p) {
+  const int64_t nchunk = (p.ctx + 511) / 512;
   return index_filter_ok(p.ix) && p.ctx <= kPilotCap / kPilotRun * kPilotStride &&
-         (p.ctx + 31) / 32 <= kMaxWords && (p.ctx + 511) / 512 <= kTkThreads;
+         (p.ctx + 31) / 32 <= kMaxWords && nchunk <= kTkThreads &&
+         nchunk * p.G * p.Nq * kFzCap < ((int64_t)1 << 31);   // 32-bit candidate offsets per request
 }
 
 size_t topk_fused_ws_bytes(const TopkParams& p) {
