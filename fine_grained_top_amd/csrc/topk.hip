@@ -953,6 +953,23 @@ __global__ __launch_bounds__(kPsThreads) void fz_pilot_score_kernel(TopkParams p
   const int i = blockIdx.x * kPsThreads + threadIdx.x;
   __shared__ float qs[4 * 64];                      // <= 4 heads per group, d_I = 64
   __shared__ float wsh[4];
+  // the sampled key's bytes are requested first, so that their latency
+  // overlaps the staging of the group's queries
+  const int L = min(p.ctx_len ? p.ctx_len[b] : p.ctx, p.ctx);
+  const int j = (i / kPilotRun) * kPilotStride + (i % kPilotRun);
+  const bool vis = i < slots && j <= L - x.Nq + r;
+  u32x4 raw[8];
+  if (vis) {
+    if (x.k.dt == DT_FP8) {
+      const u32x4* kp = (const u32x4*)((const uint8_t*)x.k.p + b * x.k.s[0] + (int64_t)j * x.k.s[1]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) raw[u] = kp[u];
+    } else {
+      const u32x4* kp = (const u32x4*)((const uint16_t*)x.k.p + b * x.k.s[0] + (int64_t)j * x.k.s[1]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) raw[u] = kp[u];
+    }
+  }
   for (int e = threadIdx.x; e < x.hpg * 64; e += kPsThreads) {
     const int h = g * x.hpg + (e >> 6);
     qs[e] = (float)load_f64(x.q.p, x.q.dt, b * x.q.s[0] + r * x.q.s[1] + h * x.q.s[2] + (e & 63));
@@ -961,16 +978,10 @@ __global__ __launch_bounds__(kPsThreads) void fz_pilot_score_kernel(TopkParams p
     wsh[threadIdx.x] = x.relu ? x.w[b * x.ws_[0] + r * x.ws_[1] + (g * x.hpg + threadIdx.x) * x.ws_[2]] : 1.f;
   __syncthreads();
   if (i >= slots) return;
-  const int L = min(p.ctx_len ? p.ctx_len[b] : p.ctx, p.ctx);
-  const int j = (i / kPilotRun) * kPilotStride + (i % kPilotRun);
   uint32_t key = 0u;
-  if (j <= L - x.Nq + r) {
+  if (vis) {
     float kv[64];
     if (x.k.dt == DT_FP8) {
-      const u32x4* kp = (const u32x4*)((const uint8_t*)x.k.p + b * x.k.s[0] + (int64_t)j * x.k.s[1]);
-      u32x4 raw[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) raw[u] = kp[u];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -983,10 +994,6 @@ __global__ __launch_bounds__(kPsThreads) void fz_pilot_score_kernel(TopkParams p
           kv[16 * u + 4 * v + 3] = hi[1];
         }
     } else {
-      const u32x4* kp = (const u32x4*)((const uint16_t*)x.k.p + b * x.k.s[0] + (int64_t)j * x.k.s[1]);
-      u32x4 raw[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) raw[u] = kp[u];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
 #pragma unroll
@@ -1048,12 +1055,9 @@ __global__ __launch_bounds__(kTkThreads) void fz_pilot_select_kernel(TopkParams 
       kmin = min(kmin, v[u]);
       kmax = max(kmax, v[u]);
     }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    m += (uint32_t)__shfl_xor((int)m, o, 64);
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-  }
+  m = (uint32_t)__builtin_amdgcn_readlane((int)wave_prefix_incl_u32(m), 63);
+  kmin = ~wave_max_u32_dpp(~kmin);
+  kmax = wave_max_u32_dpp(kmax);
   if (lane == 0) {
     red[wid] = kmin;
     red[NW + wid] = kmax;
