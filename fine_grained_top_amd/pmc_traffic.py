@@ -29,7 +29,8 @@ STAGES = {
     "index_scores": ["false>(sp::IndexerParams)", "idx_generic", "idx_err"],
     "topk": ["topk_row", "mt_zero", "mt_hist", "mt_collect", "mt_finalize"],
     "block_select": ["pool_kernel", "block_select_kernel"],
-    "attention": ["attn_index_mfma", "attn_combine", "attn_tile", "attn_generic"],
+    "attention": ["attn_index_mfma", "attn_combine", "attn_tile", "attn_generic", "bc_count", "bc_scan", "bc_table",
+                  "bc_scatter", "bc_attn", "bc_combine"],
 }
 CALIB_BYTES = 1 << 30
 
