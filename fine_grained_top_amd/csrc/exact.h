@@ -355,12 +355,12 @@ SP_DEV float exact_key(const IndexerRow& r, int64_t j) {
 // wave so that several candidates are scored at once) for one candidate j
 // (group-uniform): lane l takes a contiguous run of 64 / W dimensions of
 // every 64 (one vector load of the key row; zeros past d add nothing), heads
-// go four at a time with all their operands loaded before the reduction, and
+// go HB at a time with all their operands loaded before the reduction, and
 // the per-head sums are reduced across the group. QL: the row's queries and
 // weights are in LDS (qs [H][d], wsg [H], exact float copies); otherwise they
 // are read from the inputs. The code is straight-line apart from uniform
 // branches on H and on the score mode.
-template <int W, bool QL>
+template <int W, bool QL, int HB, bool SLOW>
 SP_DEV float group_exact_key_impl(const IndexerRow& r, int64_t j, const float* qs, const float* wsg) {
   const double g52 = 2.220446049250313e-16;
   constexpr int NK = 64 / W;
@@ -369,19 +369,23 @@ SP_DEV float group_exact_key_impl(const IndexerRow& r, int64_t j, const float* q
   const int64_t koff = j * r.k_stride;
   double s = 0.0, Es = 0.0, Ar = 0.0, sx = 0.0;
   bool ok = true, xall = true;
-  for (int h0 = 0; h0 < r.H; h0 += 4) {
-    double y[4] = {0.0, 0.0, 0.0, 0.0}, A[4] = {0.0, 0.0, 0.0, 0.0};
-    bool x[4] = {true, true, true, true};
-    double wv[4] = {0.0, 0.0, 0.0, 0.0};      // loaded with the operands, used after the reduction
+  for (int h0 = 0; h0 < r.H; h0 += HB) {
+    double y[HB], A[HB], wv[HB];              // wv: loaded with the operands, used after the reduction
+    bool x[HB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < HB; ++u) {
+      y[u] = A[u] = wv[u] = 0.0;
+      x[u] = true;
+    }
+#pragma unroll
+    for (int u = 0; u < HB; ++u)
       if (r.relu && h0 + u < r.H) wv[u] = QL ? (double)wsg[h0 + u] : (double)r.w[(h0 + u) * r.w_stride];
     for (int c0 = 0; c0 < r.d; c0 += 64) {
       const int cb = c0 + NK * lane;
       double kv[NK];
       load_run_f64<NK>(r.k, r.kt, koff + cb, r.d - cb, kv);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < HB; ++u) {
         if (h0 + u < r.H) {
           double qv[NK];
           if constexpr (QL) {
@@ -400,10 +404,10 @@ SP_DEV float group_exact_key_impl(const IndexerRow& r, int64_t j, const float* q
       }
     }
     if constexpr (W == 16) {
-      row16_xreduce<4>(y, x, A);
+      row16_xreduce<HB>(y, x, A);
     } else {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) group_xreduce<W>(y[u], x[u], A[u]);
+      for (int u = 0; u < HB; ++u) group_xreduce<W>(y[u], x[u], A[u]);
     }
     if (!r.relu) {                             // plain dot: one head
       if (x[0]) return key_of_exact(y[0]);
@@ -413,7 +417,7 @@ SP_DEV float group_exact_key_impl(const IndexerRow& r, int64_t j, const float* q
       break;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < HB; ++u) {
       if (h0 + u < r.H) {
         const double E = 2.0 * (r.d + 70) * g52 * A[u] + 1e-300;   // r.d / W + log2 W terms per path
         const double w = wv[u];
@@ -432,16 +436,22 @@ SP_DEV float group_exact_key_impl(const IndexerRow& r, int64_t j, const float* q
   if (r.relu && xall) return key_of_exact(sx);
   float key = 0.f;
   if (r.relu && ok && certify(s, Es + 2.0 * (r.H + 4) * g52 * Ar + 1e-300, key)) return key;
+  if constexpr (!SLOW) return __builtin_nanf("");   // the caller redoes the row
   float slow = 0.f;
   if (lane == 0) slow = exact_key_slow(r, j);
   return __shfl(slow, base, 64);
 }
 
 // qs/wsg (optional, together): the row's queries [H][d] and weights [H]
-// already in LDS as float (exact copies of the bf16/f32 inputs)
-template <int W>
+// already in LDS as float (exact copies of the bf16/f32 inputs). HB heads
+// are tracked at once (fewer registers with a smaller batch, more latency).
+// SLOW = false: a key that neither the exact path nor the bound settles is
+// returned as NaN instead of being formed in the wide accumulator (kept out
+// of register-tight kernels; the caller then redoes the row elsewhere).
+template <int W, int HB = 4, bool SLOW = true>
 SP_DEV float group_exact_key(const IndexerRow& r, int64_t j, const float* qs = nullptr, const float* wsg = nullptr) {
-  return qs ? group_exact_key_impl<W, true>(r, j, qs, wsg) : group_exact_key_impl<W, false>(r, j, nullptr, nullptr);
+  return qs ? group_exact_key_impl<W, true, HB, SLOW>(r, j, qs, wsg)
+            : group_exact_key_impl<W, false, HB, SLOW>(r, j, nullptr, nullptr);
 }
 SP_DEV float wave_exact_key(const IndexerRow& r, int64_t j) { return group_exact_key<64>(r, j); }
 

@@ -247,9 +247,9 @@ SP_DEV void for_each_key(const float* s, int n, F f) {
 // the short list is resolved exactly and the bitmap is written out in order.
 constexpr int kR2Words = 2048;      // bitmap words (65536 keys)
 constexpr int kR2Cand = 1860;       // candidates (and samples) kept in LDS
+constexpr int kR2Heads = 1;         // indexer heads tracked at once in the exact band keys
 
-// 40 KB, so that four rows run on a CU at once; the rare fallback reuses the
-// storage for the single-pass routine's layout
+// 40 KB, so that four rows run on a CU at once
 struct R2Main {
   RowSmemC row;
   float qs[4 * 64];     // certified rows with <= 4 heads of <= 64 dims: queries and weights
@@ -259,11 +259,7 @@ struct R2Main {
   uint32_t bm[kR2Words];
   uint32_t misc[4];
 };
-union R2Smem {
-  R2Main m;
-  RowSmem full;
-};
-static_assert(sizeof(R2Smem) <= 40960, "two-pass top-K shared memory must allow four workgroups per CU");
+static_assert(sizeof(R2Main) <= 40960, "two-pass top-K shared memory must allow four workgroups per CU");
 
 // Mark in bm the R2 best band members by (exact key desc, position asc). A
 // band of at most 64 is ranked by wave 0 from registers (readlane), a larger
@@ -298,8 +294,9 @@ SP_DEV void band_mark(const uint32_t* band_k, const uint32_t* band_j, uint32_t n
 
 // Resolve the candidate list (keys ck, indices cj, n_cand of them) that holds
 // the remaining R slots; sets the selected bits in bm. Returns false when the
-// band is too wide for the short list (caller redoes the row).
-template <int T, typename SM>
+// band is too wide for the short list or an exact band key needs the wide
+// accumulator (caller redoes the row).
+template <int T, typename SM, int HB = 4, bool SLOW = false>
 SP_DEV bool resolve_candidates(const TopkParams& p, RowCtx& c, SM& rs, uint32_t* ck, uint32_t* cj,
                                uint32_t* bm, uint32_t n_cand, uint32_t R, uint32_t wlo, uint32_t whi,
                                uint32_t tlo = 0u, uint32_t thi = 0xFFFFFFFFu, const float* qs = nullptr,
@@ -335,11 +332,17 @@ SP_DEV bool resolve_candidates(const TopkParams& p, RowCtx& c, SM& rs, uint32_t*
   if (nb > (uint32_t)(sizeof(rs.band_j) / sizeof(uint32_t))) return false;
   const uint32_t R2 = R - tot_in;
   if (p.certified) {
+    if (tid == 0) rs.run[1] = 0;
+    __syncthreads();
     for (uint32_t e = tid >> 4; e < nb; e += T / 16) {   // a quarter-wave per band member
-      const float key = group_exact_key<16>(c.ir, rs.band_j[e], qs, wsg);
-      if ((lane & 15) == 0) rs.band_k[e] = f32_order_key(key);
+      const float key = group_exact_key<16, HB, SLOW>(c.ir, rs.band_j[e], qs, wsg);
+      if ((lane & 15) == 0) {
+        rs.band_k[e] = f32_order_key(key);
+        if (key != key) rs.run[1] = 1u;             // not settled without the wide accumulator
+      }
     }
     __syncthreads();
+    if (rs.run[1]) return false;
   }
   band_mark<T>(rs.band_k, rs.band_j, nb, R2, bm);
   __syncthreads();
@@ -462,16 +465,22 @@ SP_DEV void sample_window(const uint32_t* k, int m, uint32_t rhi, uint32_t rlo, 
   __syncthreads();
 }
 
-// 256 threads held to 128 registers, 40 KB of LDS: four rows per CU (the
-// exact-key paths are cold)
 constexpr int kR2Threads = 256;
-__global__ __launch_bounds__(kR2Threads) __attribute__((amdgpu_waves_per_eu(4))) void topk_row2_kernel(TopkParams p) {
+
+// One row of up to 65536 keys (see above). SLOW = false keeps the function
+// within 128 registers (four rows per CU): exact band keys one indexer head at
+// a time, no wide accumulator (a key it would need fails the row). Returns
+// false when the row needs the ordered single-pass routine (a window that
+// misses the threshold, too many keys near it, or such a key).
+template <bool SLOW>
+SP_DEV bool row2_select(const TopkParams& p, int row, R2Main& sm) {
   constexpr int T = kR2Threads;
-  __shared__ R2Smem smu;
-  R2Main& sm = smu.m;
-  RowCtx c = row_ctx(p, blockIdx.x);
+  RowCtx c = row_ctx(p, row);
   const int tid = threadIdx.x;
-  if (c.n <= p.K) return write_all(p, c, T);
+  if (c.n <= p.K) {
+    write_all(p, c, T);
+    return true;
+  }
   const int n = c.n;
   const int nwords = (n + 31) >> 5;
   const uint32_t K = (uint32_t)p.K;
@@ -510,8 +519,10 @@ __global__ __launch_bounds__(kR2Threads) __attribute__((amdgpu_waves_per_eu(4)))
     block_scan_sum<T>(n_above, sm.row.sc, tot_above);
     const uint32_t n_cand = sm.misc[0];
     if (n_cand > (uint32_t)kR2Cand || tot_above >= K || tot_above + n_cand < K) return false;
-    return resolve_candidates<T>(p, c, sm.row, sm.ck, sm.cj, sm.bm, n_cand, K - tot_above, wlo, whi, tlo, thi,
-                                 qsp, wsp);
+    // one indexer head at a time in the exact band keys: the kernel stays
+    // within 128 registers (four rows per CU) without spilling
+    return resolve_candidates<T, RowSmemC, SLOW ? 4 : kR2Heads, SLOW>(p, c, sm.row, sm.ck, sm.cj, sm.bm, n_cand,
+                                                                       K - tot_above, wlo, whi, tlo, thi, qsp, wsp);
   };
 
   // pass 1, sampled: runs of 64 keys every S (all keys when n <= 1856); the
@@ -557,7 +568,10 @@ __global__ __launch_bounds__(kR2Threads) __attribute__((amdgpu_waves_per_eu(4)))
     uint32_t wlo, whi;
     band_limits(p, c, 0.f, order_key_f32(tlo), order_key_f32(thi), wlo, whi);
     __syncthreads();
-    if (pass2(wlo, whi, tlo, thi)) return emit_bitmap<T, kR2Words>(p, c, sm.row, sm.bm, nwords);
+    if (pass2(wlo, whi, tlo, thi)) {
+      emit_bitmap<T, kR2Words>(p, c, sm.row, sm.bm, nwords);
+      return true;
+    }
     __syncthreads();
   }
 
@@ -594,15 +608,55 @@ __global__ __launch_bounds__(kR2Threads) __attribute__((amdgpu_waves_per_eu(4)))
     band_limits(p, c, 0.f, lo_b, hi_b, wlo, whi);
   }
   __syncthreads();
-  if (!pass2(wlo, whi, bin << 20, (bin << 20) | 0xFFFFFu)) {
-    // too many keys near the threshold: the ordered single-pass routine
-    __syncthreads();
-    row_topk_single<T>(p, c, smu.full, [&](int i) { return c.s[i]; });
-    if (p.count && tid == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = p.K;
-    return;
-  }
+  if (!pass2(wlo, whi, bin << 20, (bin << 20) | 0xFFFFFu)) return false;
   emit_bitmap<T, kR2Words>(p, c, sm.row, sm.bm, nwords);
+  return true;
 }
+
+// Rows of up to 65536 keys, one workgroup each: 256 threads held to 128
+// registers, 40 KB of LDS, four rows per CU. A row that this kernel cannot
+// finish is only flagged in redo[row] (the rare paths would cost every row
+// registers); topk_redo_kernel finishes it.
+__global__ __launch_bounds__(kR2Threads) __attribute__((amdgpu_waves_per_eu(4))) void topk_row2_kernel(TopkParams p,
+                                                                                                      uint32_t* redo) {
+  __shared__ R2Main sm;
+  const bool done = row2_select<false>(p, blockIdx.x, sm);
+  if (threadIdx.x == 0) redo[blockIdx.x] = done ? 0u : 1u;
+}
+
+// Rows flagged by topk_row2_kernel: each workgroup takes blocks of kR2Threads
+// rows, reads their flags with one load per thread, lists the flagged ones in
+// LDS and redoes each with the wide exact accumulator available, then, if
+// that fails too, with the ordered single-pass routine.
+union R2Redo {
+  R2Main m;
+  RowSmem full;
+};
+constexpr int kRedoGrid = 256;
+__global__ __launch_bounds__(kR2Threads) void topk_redo_kernel(TopkParams p, const uint32_t* redo, int rows) {
+  __shared__ R2Redo smu;
+  __shared__ uint32_t list[kR2Threads];
+  __shared__ uint32_t nlist;
+  for (int r0 = blockIdx.x * kR2Threads; r0 < rows; r0 += gridDim.x * kR2Threads) {
+    if (threadIdx.x == 0) nlist = 0u;
+    __syncthreads();
+    const int row = r0 + (int)threadIdx.x;
+    if (row < rows && redo[row] != 0u) list[atomicAdd(&nlist, 1u)] = (uint32_t)row;
+    __syncthreads();
+    const uint32_t nl = nlist;
+    for (uint32_t q = 0; q < nl; ++q) {
+      const int rq = (int)list[q];
+      if (!row2_select<true>(p, rq, smu.m)) {
+        __syncthreads();
+        RowCtx c = row_ctx(p, rq);
+        row_topk_single<kR2Threads>(p, c, smu.full, [&](int i) { return c.s[i]; });
+        if (p.count && threadIdx.x == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = p.K;
+      }
+      __syncthreads();
+    }
+  }
+}
+
 
 // ---------------------------------------------------------------- multi-workgroup schedule
 // Workgroups of one row communicate only across kernel boundaries (no
@@ -1333,7 +1387,7 @@ static bool use_multi(const TopkParams& p) {
 }
 
 size_t topk_ws_bytes(const TopkParams& p) {
-  if (!use_multi(p)) return 0;
+  if (!use_multi(p)) return p.ctx <= 32 * kR2Words ? (size_t)p.B * p.G * p.Nq * sizeof(uint32_t) : 0;   // redo flags
   const int64_t rows = (int64_t)p.B * p.G * p.Nq;
   const int64_t words = (p.ctx + 31) / 32;
   const int64_t nchunk = (p.ctx + kMtChunk - 1) / kMtChunk;
@@ -1343,9 +1397,12 @@ size_t topk_ws_bytes(const TopkParams& p) {
 hipError_t launch_topk(const TopkParams& p, hipStream_t st) {
   const int rows = p.B * p.G * p.Nq;
   if (!use_multi(p)) {
-    if (p.ctx <= 32 * kR2Words)
-      hipLaunchKernelGGL(topk_row2_kernel, dim3(rows), dim3(kR2Threads), 0, st, p);
-    else
+    if (p.ctx <= 32 * kR2Words) {
+      uint32_t* redo = (uint32_t*)p.ws;
+      hipLaunchKernelGGL(topk_row2_kernel, dim3(rows), dim3(kR2Threads), 0, st, p, redo);
+      hipLaunchKernelGGL(topk_redo_kernel, dim3(min((rows + kR2Threads - 1) / kR2Threads, kRedoGrid)), dim3(kR2Threads),
+                         0, st, p, redo, rows);
+    } else
       hipLaunchKernelGGL(topk_row_kernel, dim3(rows), dim3(kTkThreads), 0, st, p);
     return hipGetLastError();
   }
