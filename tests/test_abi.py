@@ -74,11 +74,17 @@ def test_topk_validation():
     sc = torch.zeros(1, 1, 4, 64)
     io = torch.zeros(1, 1, 4, 8, dtype=torch.int32)
 
-    def call(k, flags, idx=io, err=None, ix=None):
+    need = S.LIB.spattn_topk_workspace(ctypes.byref(S.tensor(sc)), None, 8, 0)
+    assert 0 < need < (1 << 20)                 # the row kernels' per-row flags
+    ws = torch.zeros(need, dtype=torch.uint8)
+
+    def call(k, flags, idx=io, err=None, ix=None, ws_bytes=need):
         s, o = S.tensor(sc), S.tensor(idx)
-        return S.LIB.spattn_topk(ctypes.byref(s), err, ix, None, k, flags, ctypes.byref(o), None, None, 0, None)
+        return S.LIB.spattn_topk(ctypes.byref(s), err, ix, None, k, flags, ctypes.byref(o), None,
+                                 ws.data_ptr(), ws_bytes, None)
 
     assert call(8, 0) == 4                      # valid: reaches the device check
+    assert call(8, 0, ws_bytes=need - 1) == 3   # workspace too small
     assert call(0, 0) == 1                      # K must be >= 1
     assert call(8, 0, idx=torch.zeros(1, 1, 4, 7, dtype=torch.int32)) == 1
     assert call(8, S.TOPK_CERTIFIED) == 1       # certified needs err + indexer
