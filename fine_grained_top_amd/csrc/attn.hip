@@ -240,8 +240,7 @@ __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int 
     float tm = z[0];
 #pragma unroll
     for (int v = 1; v < 8; ++v) tm = fmaxf(tm, z[v]);
-    tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
-    tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+    tm = rows4_max(tm);
     const float mn = fmaxf(m, tm);
     float alpha = 1.f, ps = 0.f;
     float pv[8];
@@ -256,16 +255,24 @@ __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int 
 #pragma unroll
       for (int v = 0; v < 8; ++v) pv[v] = 0.f;
     }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
+    ps = rows4_sum(ps);
     l = l * alpha + ps;
     m = mn;
-    // rescale O: lane holds rows (heads) 4*qq + v; alpha of head hh lives in lane hh
+    // rescale O: lane holds rows (heads) 4*qq + v; alpha of head hh lives in
+    // lane hh (read with readlane, then picked by the lane's row group; with
+    // PACKLO rows 8..15 repeat heads 0..7)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      int hrow = 4 * qq + v;
-      if (PACKLO) hrow &= 7;
-      const float av = __shfl(alpha, hrow, 64);
+      const float a0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), v));
+      const float a1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), 4 + v));
+      float av;
+      if (PACKLO) {
+        av = (qq & 1) ? a1 : a0;
+      } else {
+        const float a2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), 8 + v));
+        const float a3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), 12 + v));
+        av = qq == 0 ? a0 : qq == 1 ? a1 : qq == 2 ? a2 : a3;
+      }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) O[nt][v] *= av;
     }
@@ -282,10 +289,12 @@ __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int 
     // pv[0..3] are keys 4qq+0..3 (k = 8qq+0..3), pv[4..7] keys 16+4qq+0..3 (k = 8qq+4..7)
     u32x4 Ahi, Alo;
     if (PACKLO) {
-      // rows 0..7: hi of heads 0..7; rows 8..15: lo of heads 0..7 (fetched from lane - 8)
+      // rows 0..7: hi of heads 0..7; rows 8..15: lo of heads 0..7 (from lane - 8
+      // of the same 16-lane row: DPP row_shr:8)
       uint32_t plo_src[4];
 #pragma unroll
-      for (int v2 = 0; v2 < 4; ++v2) plo_src[v2] = __shfl(pl[v2], (lane & ~15) | (c16 & 7), 64);
+      for (int v2 = 0; v2 < 4; ++v2)
+        plo_src[v2] = (uint32_t)__builtin_amdgcn_update_dpp((int)pl[v2], (int)pl[v2], 0x118, 0xf, 0xf, false);
 #pragma unroll
       for (int v2 = 0; v2 < 4; ++v2) Ahi[v2] = c16 < 8 ? ph[v2] : plo_src[v2];
     } else {

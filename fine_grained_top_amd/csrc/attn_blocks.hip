@@ -320,8 +320,7 @@ __global__ __launch_bounds__(256) void bc_attn_kernel(AttnParams a, BcWs w) {
           z[4 * st + v] = zz;
           tm = fmaxf(tm, zz);
         }
-      tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
-      tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+      tm = rows4_max(tm);
       const float mn = fmaxf(m, tm);
       float alpha = 1.f, ps = 0.f;
       if (mn > -INFINITY) {
@@ -335,13 +334,18 @@ __global__ __launch_bounds__(256) void bc_attn_kernel(AttnParams a, BcWs w) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) z[i] = 0.f;
       }
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
+      ps = rows4_sum(ps);
       l = l * alpha + ps;
       m = mn;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float av = __shfl(alpha, 4 * qq + v, 64);
+        // alpha of row r lives in lane r: four readlanes, picked by the lane's row group
+        const int ai = __builtin_bit_cast(int, alpha);
+        const float a0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ai, v));
+        const float a1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ai, 4 + v));
+        const float a2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ai, 8 + v));
+        const float a3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ai, 12 + v));
+        const float av = qq == 0 ? a0 : qq == 1 ? a1 : qq == 2 ? a2 : a3;
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) O[nt][v] *= av;
       }

@@ -122,6 +122,24 @@ SP_DEV uint32_t wave_max_u32_dpp(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// Maximum and sum over the lanes l, l^16, l^32, l^48 (the same position in
+// the four 16-lane rows) with the gfx950 lane swaps: permlane16_swap of a
+// value with itself gives every lane the row-0/row-1 (row-2/row-3) pair's two
+// values, permlane32_swap the two halves'. Each lane combines the same two
+// operands in the same order, so all four lanes end with identical bits.
+SP_DEV float rows4_max(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+SP_DEV float rows4_sum(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Number of active lanes below this one whose predicate is set.
 SP_DEV uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
