@@ -235,6 +235,56 @@ def test_certified_selection_at_rounding_midpoints():
         assert np.array_equal(idx.cpu().numpy()[0, 0, 0], want), K
 
 
+def test_certified_selection_needs_wide_accumulator():
+    """Exact scores a hair off a float32 halfway point: (1 + 2^-12)^2 is the
+    midpoint 1 + 2^-11 + 2^-24, and a second product of +-2^-70 decides the
+    rounding. The float64 sum rounds (the tracked sum is inexact) and its error
+    interval holds the midpoint, so only the wide fixed-point accumulation
+    settles these keys: in the row kernels a flagged row is finished by the
+    redo kernel with that accumulator."""
+    import oracle as orc
+    sp = S()
+    say("[gpu] certified keys needing the wide accumulator")
+    d, ctx, Nq = 8, 96, 4
+    a = np.float32(1.0 + 2.0 ** -12)
+    t = np.float32(2.0 ** -35)
+    q = np.zeros((1, Nq, 1, d), np.float32)
+    q[0, :, 0, 0] = a
+    q[0, :, 0, 1] = t
+    k = np.zeros((1, ctx, 1, d), np.float32)
+    for j in range(ctx):
+        kind = j % 6
+        if kind == 0:
+            k[0, j, 0, 0] = np.float32(1.0 + 2.0 ** -10)     # clearly above the midpoint group
+        elif kind == 1:
+            k[0, j, 0, 0] = np.float32(1.0)                  # clearly below
+        else:
+            k[0, j, 0, 0] = a
+            k[0, j, 0, 1] = [t, -t, np.float32(0.0), t][kind - 2]   # up, down, exactly the midpoint, up
+    assert (q.astype(np.float64)[0, 0, 0] @ k.astype(np.float64)[0, 2, 0]) == 1 + 2.0 ** -11 + 2.0 ** -24
+    for K in (20, 40, 60):
+        qt = torch.from_numpy(q).cuda()
+        kt = torch.from_numpy(k).cuda()
+        ix = sp.indexer(qt, kt, None, sp.SCORE_DOT, 1)
+        scores = torch.empty(1, 1, Nq, ctx, device="cuda")
+        err = torch.empty(1, 1, Nq, device="cuda")
+        sp.spattn_index_scores(ix, None, scores, err)
+        idx = torch.full((1, 1, Nq, K), 7, dtype=torch.int32, device="cuda")
+        need = sp.LIB.spattn_topk_workspace(sp.ctypes.byref(sp.tensor(scores)), sp.ctypes.byref(ix), K,
+                                            sp.TOPK_CERTIFIED)
+        ws = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
+        sp.spattn_topk(scores, err, ix, None, K, sp.TOPK_CERTIFIED, idx, ws=ws)
+        torch.cuda.synchronize()
+        # the row kernel handed these rows on (one flag word per row at the start of its workspace)
+        assert int(ws[: 4 * Nq].view(torch.int32).cpu().count_nonzero()) > 0
+        got = idx.cpu().numpy()[0, 0]
+        for r in range(Nq):
+            p = ctx - Nq + r
+            keys = orc.keys_dot(q[0, r, 0].astype(np.float64), k[0, : p + 1, 0].astype(np.float64))
+            want = orc.topk(keys, K)
+            assert np.array_equal(got[r, : len(want)], want), (K, r)
+
+
 def _block_select_case(q, k, ctx_len, bs, nb):
     """Run block selection on the GPU and compare every row with the oracle."""
     import oracle as orc
