@@ -222,20 +222,30 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(TopkParams p) {
   if (p.count && threadIdx.x == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = p.K;
 }
 
-// Visit s[0..n) as (j, order key) with U independent loads in flight per thread.
+// Visit s[0..n) as (j, order key), U loads per thread a batch; the next
+// batch is in flight while the current one is visited.
 template <int T, int U, typename F>
 SP_DEV void for_each_key(const float* s, int n, F f) {
-  for (int base = 0; base < n; base += T * U) {
-    float v[U];
+  float v[U], w[U];
+  auto load = [&](float (&x)[U], int base) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = base + u * T + (int)threadIdx.x;
-      v[u] = j < n ? s[j] : 0.f;
+      x[u] = j < n ? s[j] : 0.f;
     }
+  };
+  load(v, 0);
+  for (int base = 0; base < n; base += T * U) {
+    const bool more = base + T * U < n;
+    if (more) load(w, base + T * U);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = base + u * T + (int)threadIdx.x;
       if (j < n) f(j, f32_order_key(v[u]));
+    }
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = w[u];
     }
   }
 }
@@ -503,7 +513,7 @@ SP_DEV bool row2_select(const TopkParams& p, int row, R2Main& sm) {
     if (tid == 0) sm.misc[0] = 0;
     __syncthreads();
     uint32_t n_above = 0;
-    for_each_key<T, 16>(c.s, n, [&](int j, uint32_t ks) {
+    for_each_key<T, 8>(c.s, n, [&](int j, uint32_t ks) {
       if (ks > whi) {
         atomicOr(&sm.bm[j >> 5], 1u << (j & 31));
         ++n_above;
@@ -579,7 +589,7 @@ SP_DEV bool row2_select(const TopkParams& p, int row, R2Main& sm) {
   // K-th key widened by the band
   for (int i = tid; i < 4096; i += T) sm.row.hist[i] = 0;
   __syncthreads();
-  for_each_key<T, 16>(c.s, n, [&](int j, uint32_t ks) { atomicAdd(&sm.row.hist[ks >> 20], 1u); });
+  for_each_key<T, 8>(c.s, n, [&](int j, uint32_t ks) { atomicAdd(&sm.row.hist[ks >> 20], 1u); });
   __syncthreads();
   uint32_t bin;
   {
