@@ -411,11 +411,8 @@ SP_DEV void sample_window(const uint32_t* k, int m, uint32_t rhi, uint32_t rlo, 
       kmax = max(kmax, v);
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-  }
+  kmin = ~wave_max_u32_dpp(~kmin);
+  kmax = wave_max_u32_dpp(kmax);
   if (lane == 0) {
     sc[wid] = kmin;
     sc[NW + wid] = kmax;
