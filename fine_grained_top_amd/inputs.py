@@ -18,7 +18,11 @@ Recipe (stated once, used everywhere):
   * the block-sparse workload shifts every key element of 4% of the 64-token
     blocks by +2.0 (two standard deviations) before rounding, the same blocks
     for every head;
-  * decode lengths are drawn uniformly from an inclusive integer range.
+  * decode lengths are drawn uniformly from an inclusive integer range;
+  * paged workloads also store K and V as a pool of P-token pages: the
+    B * ceil(N/P) logical pages are placed at the physical slots of one seeded
+    permutation (page_table[b, page] = slot), so consecutive pages of a
+    request are scattered over the pool.
 """
 from __future__ import annotations
 
@@ -32,7 +36,7 @@ import numpy as np
 CHUNK = 1 << 22
 
 # tensor ids used in the seed sequence
-TID = dict(q=1, k=2, v=3, q_idx=4, k_idx=5, w=6, lengths=7, needles=8, shift=9)
+TID = dict(q=1, k=2, v=3, q_idx=4, k_idx=5, w=6, lengths=7, needles=8, shift=9, pages=10)
 
 
 def _threads() -> int:
@@ -168,7 +172,7 @@ def uniform01(seed: int, tid: int, shape) -> np.ndarray:
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # topk | window_global | blocks | dsa_prefill | dsa_decode
+    kind: str                 # topk | window_global | blocks | dsa_prefill | dsa_decode | dsa_pages
     B: int
     Hq: int
     Hkv: int
@@ -194,6 +198,10 @@ class Workload:
     top_blocks: int = 0
     shift_frac: float = 0.0
     shift: float = 0.0
+    # page-granular selection over a paged KV cache (dsa_pages)
+    page_size: int = 0
+    top_pages: int = 0
+    n_local: int = 0
     # decode lengths (inclusive range); None = every request has N keys
     len_range: Optional[Tuple[int, int]] = None
 
@@ -239,6 +247,16 @@ _add(dataclasses.replace(PREFILL, name="dsa_prefill_small", Hq=16, N=1200, Nq=12
                          topk=128, needles=12))
 _add(dataclasses.replace(DECODE, name="dsa_decode_small", B=3, N=9000,
                          topk=512, len_range=(6000, 9000)))
+
+# Page-granular selection over a paged KV cache: the decode shape above with
+# 64-token pages, the 30 best pages plus the 2 most recent (2048 tokens read).
+PAGED = _add(dataclasses.replace(DECODE, name="dsa_paged_decode", kind="dsa_pages", seed=7,
+                                 topk=0, page_size=64, top_pages=30, n_local=2))
+_add(dataclasses.replace(PAGED, name="dsa_paged_decode_small", B=3, N=9000, top_pages=6,
+                         len_range=(6000, 9000)))
+_add(dataclasses.replace(PAGED, name="dsa_paged_prefill_small", B=1, Hq=8, Hkv=2, N=700, Nq=700,
+                         H_I=4, G_sel=2, idx_k_dtype="bf16", page_size=16, top_pages=5,
+                         n_local=1, len_range=None))
 
 
 def lengths(w: Workload) -> np.ndarray:
@@ -290,7 +308,29 @@ def generate(w: Workload) -> Dict[str, np.ndarray]:
         else:
             out["w"] = np.ones(w.H_I, dtype=np.float32)
         out["needles"] = _plant_needles(w, out)
+    if w.page_size:
+        out["page_table"], out["k_pages"], out["v_pages"] = paged_kv(w, out["k"], out["v"])
     return out
+
+
+def paged_kv(w: Workload, k: np.ndarray, v: np.ndarray):
+    """page_table int32 [B, ceil(N/P)] and the pools [B*ceil(N/P), Hkv, P, d]."""
+    P = w.page_size
+    npr = (w.N + P - 1) // P
+    slots = _rng(w.seed, TID["pages"]).permutation(w.B * npr).astype(np.int32)
+    table = slots.reshape(w.B, npr)
+    pad = npr * P - w.N
+
+    def pool(x: np.ndarray) -> np.ndarray:
+        if pad:
+            x = np.concatenate([x, np.zeros(x.shape[:2] + (pad, x.shape[3]), x.dtype)], axis=2)
+        # [B, Hkv, npr, P, d] -> [B*npr, Hkv, P, d] in logical order, then placed at the slots
+        logical = x.reshape(w.B, w.Hkv, npr, P, w.d).transpose(0, 2, 1, 3, 4).reshape(w.B * npr, w.Hkv, P, w.d)
+        out = np.empty_like(logical)
+        out[slots] = logical
+        return out
+
+    return table, pool(k), pool(v)
 
 
 def _plant_needles(w: Workload, t: Dict[str, np.ndarray]) -> np.ndarray:

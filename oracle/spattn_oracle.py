@@ -31,6 +31,13 @@ What is computed (sources are the five pages on sparse attention):
   "Sparse Attention in 2026", DSA paragraph): score s(i,j) is either
   q_I . k_I,j or sum_h w_h * ReLU(q_I,h . k_I,j), the indexer carries no
   positional encoding, and the K highest scoring past keys are kept.
+* Page-granular selection ("Sparse Attention in 2026: Why It Finally Had to
+  Be Native", the DSA list: the indexer rates every 64-token KV page, the
+  attention reads the best pages plus the mandatory recent pages, whole).
+  The page does not say how token scores become a page rating; it is read
+  here as the largest key among the page's visible tokens. The recent pages
+  are the n_local pages ending with the one that holds the query position;
+  every earlier page competes by (page key descending, page index ascending).
 
 Selection keys. The pages fix no precision for the scores. Selection is made
 on key(j) = the float32 nearest (ties to even) to the exact real-valued score,
@@ -243,6 +250,41 @@ def blocks_set(blocks: Sequence[int], p: int, bs: int, w: int) -> np.ndarray:
     return s[s <= p].astype(np.int32)
 
 
+def page_keys(keys: np.ndarray, P: int, n_pages: int) -> np.ndarray:
+    """key(page) = the largest key among the page's tokens.
+
+    ``keys`` holds the keys of the visible tokens 0..p; page pi covers tokens
+    pi*P .. pi*P+P-1, cut at p ("Sparse Attention in 2026", DSA list: one
+    rating per 64-token page).
+    """
+    out = np.empty(n_pages, dtype=np.float32)
+    for pi in range(n_pages):
+        out[pi] = keys[pi * P:min((pi + 1) * P, keys.shape[0])].max()
+    return out
+
+
+def page_select(keys: np.ndarray, p: int, P: int, top_pages: int, n_local: int) -> np.ndarray:
+    """Pages read by the query at position p, ascending.
+
+    The n_local most recent pages (the page holding p and the ones before it)
+    are always read; among the earlier pages the min(top_pages, count) best by
+    (page key descending, page index ascending) are added ("Sparse Attention
+    in 2026", DSA list: top-k relevant pages plus mandatory recent/local pages).
+    """
+    last = p // P
+    n_cand = max(0, last + 1 - n_local)
+    chosen = topk(page_keys(keys[:p + 1], P, n_cand), top_pages) if n_cand else np.zeros(0, np.int32)
+    local = np.arange(n_cand, last + 1)
+    return np.concatenate([chosen, local]).astype(np.int32)
+
+
+def pages_set(pages: Sequence[int], p: int, P: int) -> np.ndarray:
+    """Every token of the listed pages, within 0..p (pages are read whole)."""
+    parts = [np.arange(P * pg, P * pg + P) for pg in pages]
+    s = np.unique(np.concatenate(parts)) if len(parts) else np.zeros(0, np.int64)
+    return s[s <= p].astype(np.int32)
+
+
 # --------------------------------------------------------------------------
 # attention
 # --------------------------------------------------------------------------
@@ -287,7 +329,7 @@ class Rows:
     def __init__(self) -> None:
         self.sets: Dict[Tuple[int, int, int], np.ndarray] = {}      # (b, group, r) -> S
         self.keys: Dict[Tuple[int, int, int], np.ndarray] = {}      # token/block keys
-        self.blocks: Dict[Tuple[int, int, int], np.ndarray] = {}    # (b, head, r) -> blocks
+        self.blocks: Dict[Tuple[int, int, int], np.ndarray] = {}    # (b, head or group, r) -> blocks or pages
         self.O: Dict[Tuple[int, int], np.ndarray] = {}              # (b, r) -> [Hq, d]
         self.lse: Dict[Tuple[int, int], np.ndarray] = {}
         self.pairs = 0
@@ -315,7 +357,7 @@ def run(wl, inp: Dict[str, np.ndarray], rows: Iterable[Tuple[int, int]],
         Kb = [decode(Kst[b, h, :n], wl.dtype) for h in range(wl.Hkv)]
         # visible set per query head
         S_of_head: List[np.ndarray] = [None] * wl.Hq
-        if wl.kind in ("topk", "dsa_prefill", "dsa_decode"):
+        if wl.kind in ("topk", "dsa_prefill", "dsa_decode", "dsa_pages"):
             qi = decode(inp["q_idx"][b, r], wl.idx_q_dtype)            # [H_I, d_I]
             hpg = wl.H_I // wl.G_sel
             w = np.asarray(inp["w"], dtype=np.float32).astype(np.float64)
@@ -326,7 +368,12 @@ def run(wl, inp: Dict[str, np.ndarray], rows: Iterable[Tuple[int, int]],
                     keys = keys_dot(qi[g * hpg], Ki)
                 else:
                     keys = keys_weighted_relu(qi[g * hpg:(g + 1) * hpg], w[g * hpg:(g + 1) * hpg], Ki)
-                S = topk(keys, wl.topk)
+                if wl.kind == "dsa_pages":
+                    pg = page_select(keys, p, wl.page_size, wl.top_pages, wl.n_local)
+                    res.blocks[(b, g, r)] = pg
+                    S = pages_set(pg, p, wl.page_size)
+                else:
+                    S = topk(keys, wl.topk)
                 res.sets[(b, g, r)] = S
                 if keep_keys:
                     res.keys[(b, g, r)] = keys

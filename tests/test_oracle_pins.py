@@ -380,3 +380,82 @@ def test_generator_is_deterministic():
     b = gen.generate(wl)
     for key in a:
         assert np.array_equal(a[key], b[key]), key
+
+
+# ---------------------------------------------------------------- page-granular selection
+def test_page_select_hand_worked():
+    g = _gold("page_select_hand.json")
+    keys = np.asarray(g["keys"], dtype=np.float32)
+    for c in g["select_cases"]:
+        got = orc.page_select(keys, c["p"], c["P"], c["top"], c["local"])
+        assert list(got) == c["pages"], c
+    for c in g["set_cases"]:
+        assert list(orc.pages_set(c["pages"], c["p"], c["P"])) == c["tokens"], c
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_page_select_one_token_pages_is_token_topk(seed):
+    """With 1-token pages and no mandatory pages, page selection is token top-K."""
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(5, 50))
+    keys = rng.integers(-3, 4, size=n).astype(np.float32)
+    for p in (0, n // 3, n - 1):
+        for K in (1, 4, p + 1, p + 3):
+            assert list(orc.page_select(keys, p, 1, K, 0)) == _brute_topk(list(keys[:p + 1]), K)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_page_select_brute_force(seed):
+    """Page maxima by explicit loops, ranking by brute force, recent pages always kept."""
+    rng = np.random.default_rng(200 + seed)
+    n = int(rng.integers(1, 70))
+    keys = rng.integers(-4, 5, size=n).astype(np.float32)       # many ties
+    for P in (1, 2, 4, 8):
+        for n_local in (0, 1, 2, 3):
+            for top in (1, 2, 5):
+                for p in sorted({0, n // 2, n - 1}):
+                    last = p // P
+                    cands = list(range(max(0, last + 1 - n_local)))
+                    pk = []
+                    for pg in cands:
+                        m = None
+                        for j in range(pg * P, pg * P + P):
+                            if j <= p and (m is None or keys[j] > m):
+                                m = keys[j]
+                        pk.append(m)
+                    want = _brute_topk(pk, top) + list(range(len(cands), last + 1))
+                    got = orc.page_select(keys, p, P, top, n_local)
+                    assert list(got) == want, (P, n_local, top, p)
+                    assert len(got) == min(top, len(cands)) + (last + 1 - len(cands))
+
+
+def test_pages_full_coverage_is_causal():
+    """Enough pages for every row: every past token is read, which is causal SDPA."""
+    import dataclasses
+    wl = dataclasses.replace(gen.WORKLOADS["dsa_paged_prefill_small"], N=150, Nq=150, Hq=2, Hkv=1,
+                             G_sel=1, H_I=2, top_pages=100)
+    inp = gen.generate(wl)
+    res = orc.run(wl, inp, [(0, r) for r in range(0, 150, 11)])
+    q = orc.decode(inp["q"][0], "bf16")
+    k = orc.decode(inp["k"][0], "bf16")
+    v = orc.decode(inp["v"][0], "bf16")
+    ref = _sdpa_causal(q, np.repeat(k, 2, axis=0), np.repeat(v, 2, axis=0))
+    for r in range(0, 150, 11):
+        assert np.array_equal(res.sets[(0, 0, r)], np.arange(r + 1))
+        for h in range(2):
+            assert np.max(np.abs(res.O[(0, r)][h] - ref[h, r])) < 1e-12
+
+
+def test_paged_pool_holds_the_logical_cache():
+    """The generator's page pool, read through the page table, is the logical K/V."""
+    wl = gen.WORKLOADS["dsa_paged_decode_small"]
+    inp = gen.generate(wl)
+    P = wl.page_size
+    T = inp["page_table"]
+    assert sorted(T.ravel().tolist()) == list(range(T.size))
+    for b in range(wl.B):
+        n = int(inp["ctx_len"][b])
+        for name in ("k", "v"):
+            pool = inp[name + "_pages"]
+            rebuilt = np.concatenate([pool[T[b, pg]] for pg in range((n + P - 1) // P)], axis=1)[:, :n]
+            assert np.array_equal(rebuilt, inp[name][b, :, :n])
