@@ -13,6 +13,10 @@
 //    attn_combine with their (max, sum) pairs.
 //  * attn_generic: any mode, f32 or bf16, d <= 128; one wave per (row, head):
 //    lanes score 64 candidates at a time, then sweep them over the dims.
+//  * Page lists (mode 4) are read as one token slot per (listed page, offset).
+//    Paged K/V storage (pools of pages and a page table) is translated where
+//    a key's row address is formed: logical token j of request b is row
+//    j mod P of pool page table[b][j / P].
 #include "common.h"
 #include "internal.h"
 
@@ -25,9 +29,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Enumerates the visible set of one query row: t -> key position or -1.
 struct Visible {
   int mode, p, count;
-  const int32_t* list;   // index list (mode 1) or block list (mode 3)
+  const int32_t* list;   // index list (mode 1), block list (mode 3) or page list (mode 4)
   int K;                 // list length
-  int g_end, w_start, bs, nb_keys;
+  int g_end, w_start, bs, nb_keys, lgbs;
 
   SP_DEV void init(const AttnParams& a, int b, int h, int r, int pos) {
     mode = a.mode;
@@ -39,6 +43,11 @@ struct Visible {
     } else if (mode == 1) {
       const int gsel = h / (a.Hq / a.G_sel);
       list = a.sel + b * a.sels[0] + gsel * a.sels[1] + r * a.sels[2];
+      count = K;
+    } else if (mode == 4) {
+      const int gsel = h / (a.Hq / a.G_sel);
+      list = a.sel + b * a.sels[0] + gsel * a.sels[1] + r * a.sels[2];
+      lgbs = a.lgbs;
       count = K;
     } else if (mode == 2) {
       g_end = min(a.n_global, p + 1);
@@ -59,6 +68,12 @@ struct Visible {
       const int j = list[t];
       return (j >= 0 && j <= p) ? j : -1;
     }
+    if (mode == 4) {
+      const int pg = list[t >> lgbs];
+      if (pg < 0) return -1;
+      const int j = (pg << lgbs) + (t & ((1 << lgbs) - 1));
+      return j <= p ? j : -1;
+    }
     if (mode == 2) return t < g_end ? t : w_start + (t - g_end);
     if (t < nb_keys) {
       const int blk = list[t / bs];
@@ -72,6 +87,15 @@ struct Visible {
 
 SP_DEV float ldv(const void* p, int dt, int64_t i) {
   return dt == DT_F32 ? ((const float*)p)[i] : bf16_to_f32(((const uint16_t*)p)[i]);
+}
+
+// Element offset of key j's row of KV head kvh of request b in tensor t.
+SP_DEV int64_t kv_row(const AttnParams& a, const View4& t, int b, int kvh, int j) {
+  if (a.ptab) {
+    const int64_t pg = a.ptab[b * a.pts + (j >> a.lgP)];
+    return pg * t.s[0] + kvh * t.s[1] + (int64_t)(j & ((1 << a.lgP) - 1)) * t.s[2];
+  }
+  return b * t.s[0] + kvh * t.s[1] + (int64_t)j * t.s[2];
 }
 
 // ---------------------------------------------------------------- generic
@@ -89,8 +113,6 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnParams a) {
   const int64_t qb = b * a.q.s[0] + h * a.q.s[1] + r * a.q.s[2];
   for (int c = lane; c < a.d; c += 64) qs[c] = ldv(a.q.p, a.q.dt, qb + c);
   __syncthreads();
-  const int64_t kb = b * a.k.s[0] + kvh * a.k.s[1];
-  const int64_t vb = b * a.v.s[0] + kvh * a.v.s[1];
   float m = -INFINITY, l = 0.f, acc0 = 0.f, acc1 = 0.f;
   for (int t0 = 0; t0 < vis.count; t0 += 64) {
     const int t = t0 + lane;
@@ -98,7 +120,7 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnParams a) {
     float z = -INFINITY;
     if (j >= 0) {
       float s = 0.f;
-      const int64_t kr = kb + (int64_t)j * a.k.s[2];
+      const int64_t kr = kv_row(a, a.k, b, kvh, j);
       for (int c = 0; c < a.d; ++c) s = fmaf(qs[c], ldv(a.k.p, a.k.dt, kr + c), s);
       z = s * a.scale;
     }
@@ -121,7 +143,7 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnParams a) {
       const int ju = js[u];
       if (ju < 0) continue;
       const float pu = ps[u];
-      const int64_t vr = vb + (int64_t)ju * a.v.s[2];
+      const int64_t vr = kv_row(a, a.v, b, kvh, ju);
       if (lane < a.d) acc0 = fmaf(pu, ldv(a.v.p, a.v.dt, vr + lane), acc0);
       if (lane + 64 < a.d) acc1 = fmaf(pu, ldv(a.v.p, a.v.dt, vr + lane + 64), acc1);
     }
@@ -143,7 +165,7 @@ struct SplitInfo {
 };
 constexpr int kMaxTilesPerWave = 16;   // 32-entry tiles per wave of one split
 
-template <bool PACKLO, bool PIPE>
+template <bool PACKLO, bool PIPE, bool PAGED>
 __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int Hg, SplitInfo si,
                                                               float* part) {
   const int split = blockIdx.x;
@@ -185,8 +207,17 @@ __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int 
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) O[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  const uint16_t* kbase = (const uint16_t*)a.k.p + b * a.k.s[0] + kvh * a.k.s[1];
-  const uint16_t* vbase = (const uint16_t*)a.v.p + b * a.v.s[0] + kvh * a.v.s[1];
+  // key rows: list entries become logical tokens j (page lists: one entry per
+  // token slot), then, with paged storage, pool tokens (pool page << lgP | row)
+  const uint16_t* kbase = (const uint16_t*)a.k.p + (PAGED ? 0 : b * a.k.s[0]) + kvh * a.k.s[1];
+  const uint16_t* vbase = (const uint16_t*)a.v.p + (PAGED ? 0 : b * a.v.s[0]) + kvh * a.v.s[1];
+  const int pmask = (1 << a.lgP) - 1;
+  auto krow = [&](int j) -> int64_t {
+    return PAGED ? (int64_t)(j >> a.lgP) * a.k.s[0] + (int64_t)(j & pmask) * a.k.s[2] : (int64_t)j * a.k.s[2];
+  };
+  auto vrow = [&](int j) -> int64_t {
+    return PAGED ? (int64_t)(j >> a.lgP) * a.v.s[0] + (int64_t)(j & pmask) * a.v.s[2] : (int64_t)j * a.v.s[2];
+  };
 
   // this wave's tiles of 32 list entries: t_begin + 32 wid + 128 i; all their
   // entries are loaded at once
@@ -195,8 +226,17 @@ __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int 
   int* wix = idxs[wid];
   for (int e = lane; e < ntw * 32; e += 64) {
     const int t = first + 128 * (e >> 5) + (e & 31);
-    int j = t < t_end ? list[t] : -1;
+    int j = -1;
+    if (t < t_end) {
+      if (a.mode == 4) {
+        const int pg = list[t >> a.lgbs];
+        j = pg < 0 ? -1 : (pg << a.lgbs) + (t & ((1 << a.lgbs) - 1));
+      } else {
+        j = list[t];
+      }
+    }
     if (j > pos) j = -1;
+    if (PAGED && j >= 0) j = (a.ptab[b * a.pts + (j >> a.lgP)] << a.lgP) | (j & pmask);
     wix[e] = j;
   }
   __builtin_amdgcn_wave_barrier();
@@ -209,7 +249,7 @@ __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int 
     for (int st = 0; st < 2; ++st) {
       int j = ix[16 * st + c16];
       j = j < 0 ? 0 : j;
-      const uint16_t* kp = kbase + (int64_t)j * a.k.s[2] + 32 * qq;
+      const uint16_t* kp = kbase + krow(j) + 32 * qq;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) kr[st][ks] = *(const u32x4*)(kp + 8 * ks);
     }
@@ -217,7 +257,7 @@ __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int 
     for (int u = 0; u < 8; ++u) {
       int j = ix[qq + 4 * u];
       j = j < 0 ? 0 : j;
-      vr[u] = *(const u32x4*)(vbase + (int64_t)j * a.v.s[2] + 8 * c16);
+      vr[u] = *(const u32x4*)(vbase + vrow(j) + 8 * c16);
     }
   };
 
@@ -456,7 +496,7 @@ static int gather_group(const AttnParams& a) {
 }
 
 static bool mfma_index_ok(const AttnParams& a) {
-  return a.mode == 1 && a.q.dt == DT_BF16 && a.d == 128 && gather_group(a) <= 16;
+  return (a.mode == 1 || a.mode == 4) && a.q.dt == DT_BF16 && a.d == 128 && gather_group(a) <= 16;
 }
 
 static SplitInfo pick_split(const AttnParams& a, int Hg) {
@@ -497,13 +537,17 @@ hipError_t launch_attention(const AttnParams& a, hipStream_t st) {
     float* part = (float*)a.ws;
     dim3 grid(si.nsplit, rows);
     const bool pipe = (int64_t)rows * si.nsplit <= 1024;   // at most ~4 workgroups per CU
+#define SP_ATTN_MFMA(PL, PI, PG) \
+  hipLaunchKernelGGL((attn_index_mfma_kernel<PL, PI, PG>), grid, dim3(256), 0, st, a, Hg, si, part)
+    const bool paged = a.ptab != nullptr;
     if (Hg <= 8) {
-      if (pipe) hipLaunchKernelGGL((attn_index_mfma_kernel<true, true>), grid, dim3(256), 0, st, a, Hg, si, part);
-      else hipLaunchKernelGGL((attn_index_mfma_kernel<true, false>), grid, dim3(256), 0, st, a, Hg, si, part);
+      if (pipe) { if (paged) SP_ATTN_MFMA(true, true, true); else SP_ATTN_MFMA(true, true, false); }
+      else { if (paged) SP_ATTN_MFMA(true, false, true); else SP_ATTN_MFMA(true, false, false); }
     } else {
-      if (pipe) hipLaunchKernelGGL((attn_index_mfma_kernel<false, true>), grid, dim3(256), 0, st, a, Hg, si, part);
-      else hipLaunchKernelGGL((attn_index_mfma_kernel<false, false>), grid, dim3(256), 0, st, a, Hg, si, part);
+      if (pipe) { if (paged) SP_ATTN_MFMA(false, true, true); else SP_ATTN_MFMA(false, true, false); }
+      else { if (paged) SP_ATTN_MFMA(false, false, true); else SP_ATTN_MFMA(false, false, false); }
     }
+#undef SP_ATTN_MFMA
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || si.nsplit == 1) return e;
     hipLaunchKernelGGL(attn_combine_kernel, dim3(rows, Hg), dim3(128), 0, st, a, Hg, si,

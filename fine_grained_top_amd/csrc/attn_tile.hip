@@ -265,7 +265,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
 }
 
 bool attn_tile_ok(const AttnParams& a) {
-  if (a.q.dt != DT_BF16 || a.d != 128 || a.mode == 1) return false;
+  if (a.q.dt != DT_BF16 || a.d != 128 || a.mode == 1 || a.mode == 4 || a.ptab) return false;
   if ((a.ctx + kTK - 1) / kTK > 2048) return false;
   if (a.mode == 3 && ((a.ctx + a.bs - 1) / a.bs > 32 * kMaxBlkWords)) return false;
   return true;

@@ -20,6 +20,7 @@
 // are at most 24 bits, exponents within float32's.
 #pragma once
 #include "common.h"
+#include "internal.h"
 
 namespace sp {
 
@@ -273,6 +274,27 @@ struct IndexerRow {        // one query row of one selection group
   int d;                   // indexer head dim
   int relu;                // 1 = weighted ReLU, 0 = plain dot
 };
+
+// The indexer row of query row r of request b, selection group g.
+SP_DEV IndexerRow indexer_row(const IndexerParams& x, int b, int g, int r) {
+  IndexerRow ir;
+  const int hpg = x.hpg;
+  const int kg = x.G_k == 1 ? 0 : g;
+  const int esz = x.q.dt == DT_F32 ? 4 : 2;
+  const int ksz = x.k.dt == DT_F32 ? 4 : (x.k.dt == DT_BF16 ? 2 : 1);
+  ir.q = (const char*)x.q.p + (b * x.q.s[0] + r * x.q.s[1] + (int64_t)g * hpg * x.q.s[2]) * esz;
+  ir.qt = x.q.dt;
+  ir.qh_stride = x.q.s[2];
+  ir.k = (const char*)x.k.p + (b * x.k.s[0] + kg * x.k.s[2]) * ksz;
+  ir.kt = x.k.dt;
+  ir.k_stride = x.k.s[1];
+  ir.w = x.relu ? x.w + b * x.ws_[0] + r * x.ws_[1] + (int64_t)g * hpg * x.ws_[2] : nullptr;
+  ir.w_stride = x.ws_[2];
+  ir.H = hpg;
+  ir.d = x.d_I;
+  ir.relu = x.relu;
+  return ir;
+}
 
 SP_DEV float exact_key_slow(const IndexerRow& r, int64_t j) {
   int64_t koff = j * r.k_stride;

@@ -57,6 +57,15 @@ bool topk_fused_ok(const TopkParams& p);
 size_t topk_fused_ws_bytes(const TopkParams& p);
 hipError_t launch_topk_fused(const TopkParams& p, hipStream_t st);
 
+// ---------------------------------------------------------------- page select
+constexpr int kMaxPages = 16384;   // candidate pages per row held in LDS
+struct PageSelParams {
+  TopkParams t;            // scores, err, indexer (certified), shapes; t.K = top_pages;
+                           // t.idx / t.is: page list [B, G, Nq, width]; t.count
+  int lgP, n_local, width; // log2 page size, mandatory recent pages, list width
+};
+hipError_t launch_page_select(const PageSelParams& p, hipStream_t st);
+
 // ---------------------------------------------------------------- block select
 struct BlockSelectParams {
   View4 q;                 // [B, Hq, Nq, d]
@@ -83,11 +92,18 @@ struct AttnParams {
   int B, Hq, Hkv, Nq, ctx, d;
   const int32_t* ctx_len;
   float scale;
-  int mode;                // 0 dense, 1 index, 2 window/global, 3 blocks
-  const int32_t* sel;      // index list or block list
+  int mode;                // 0 dense, 1 index, 2 window/global, 3 blocks, 4 pages
+  const int32_t* sel;      // index list, block list or page list
   int64_t sels[4];
-  int G_sel, K;            // index list groups and width (or number of blocks)
+  int G_sel, K;            // list groups and width (index: keys; blocks: blocks; pages: page
+                           // slots times the page size, i.e. one entry per token slot)
   int window, n_global, bs;
+  int lgbs;                // pages: log2 of the tokens per listed page
+  // paged K/V storage: k, v are pools [n_pages, Hkv, 1 << lgP, d]; logical page
+  // pg of request b lives in pool page ptab[b * pts + pg]
+  const int32_t* ptab;
+  int64_t pts;
+  int lgP;
   float* o;                // [B, Hq, Nq, d] f32
   int64_t os[4];
   float* lse;              // [B, Hq, Nq] or null

@@ -296,6 +296,68 @@ SPATTN_API int spattn_topk(const spattn_tensor* scores, const float* err, const 
   return launched(fused ? sp::launch_topk_fused(p, (hipStream_t)stream) : sp::launch_topk(p, (hipStream_t)stream));
 }
 
+// ------------------------------------------------------------------ page select
+static int log2_pow2(int32_t v, int32_t hi) {   // log2 of a power of two in 1..hi, else -1
+  if (v < 1 || v > hi || (v & (v - 1))) return -1;
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+static int page_select_setup(const spattn_tensor* scores, const float* err, const spattn_indexer* ix,
+                             const int32_t* ctx_len, int32_t page_size, int32_t top_pages, int32_t n_local,
+                             uint32_t flags, const spattn_tensor* pg_idx_out, sp::PageSelParams& q) {
+  int rc;
+  q = sp::PageSelParams{};
+  if (flags & ~SPATTN_TOPK_CERTIFIED) return fail(SPATTN_ERR_INVALID_ARG, "unknown flags");
+  q.lgP = log2_pow2(page_size, 4096);
+  if (q.lgP < 0) return fail(SPATTN_ERR_INVALID_ARG, "page_size must be a power of two in 1..4096");
+  if (top_pages < 0 || n_local < 0 || (int64_t)top_pages + n_local < 1)
+    return fail(SPATTN_ERR_INVALID_ARG, "need top_pages >= 0, n_local >= 0 and top_pages + n_local >= 1");
+  if (top_pages > 16384 || n_local > 16384) return fail(SPATTN_ERR_UNSUPPORTED, "top_pages and n_local must be <= 16384");
+  if (!scores) return fail(SPATTN_ERR_INVALID_ARG, "scores: null tensor");
+  if ((rc = topk_setup(scores, err, ix, ctx_len, 1, flags, nullptr, q.t))) return rc;
+  const int64_t npages = ((int64_t)q.t.ctx + page_size - 1) / page_size;
+  if (npages > sp::kMaxPages) return fail(SPATTN_ERR_UNSUPPORTED, "more than %d pages per request", sp::kMaxPages);
+  q.t.K = top_pages;
+  q.n_local = n_local;
+  q.width = top_pages + n_local;
+  if (pg_idx_out) {
+    if ((rc = check_tensor(pg_idx_out, "pg_idx_out", 4, false))) return rc;
+    if (pg_idx_out->dtype != SPATTN_I32) return fail(SPATTN_ERR_INVALID_ARG, "pg_idx_out must be int32");
+    if (pg_idx_out->shape[0] != q.t.B || pg_idx_out->shape[1] != q.t.G || pg_idx_out->shape[2] != q.t.Nq ||
+        pg_idx_out->shape[3] != q.width)
+      return fail(SPATTN_ERR_INVALID_ARG, "pg_idx_out must be [B, G, Nq, top_pages + n_local]");
+    q.t.idx = (int32_t*)pg_idx_out->data;
+    for (int i = 0; i < 4; ++i) q.t.is[i] = pg_idx_out->stride[i];
+  }
+  return SPATTN_OK;
+}
+
+SPATTN_API size_t spattn_page_select_workspace(const spattn_tensor* scores, int32_t page_size, int32_t top_pages,
+                                               int32_t n_local) {
+  sp::PageSelParams q;
+  if (page_select_setup(scores, nullptr, nullptr, nullptr, page_size, top_pages, n_local, 0u, nullptr, q))
+    return (size_t)-1;
+  return 0;
+}
+
+SPATTN_API int spattn_page_select(const spattn_tensor* scores, const float* err, const spattn_indexer* ix,
+                                  const int32_t* ctx_len, int32_t page_size, int32_t top_pages, int32_t n_local,
+                                  uint32_t flags, const spattn_tensor* pg_idx_out, int32_t* pg_count_out, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  sp::PageSelParams q;
+  int rc;
+  (void)ws;
+  (void)ws_bytes;
+  if (!pg_idx_out) return fail(SPATTN_ERR_INVALID_ARG, "pg_idx_out: null tensor");
+  if ((rc = page_select_setup(scores, err, ix, ctx_len, page_size, top_pages, n_local, flags, pg_idx_out, q)))
+    return rc;
+  q.t.count = pg_count_out;
+  if ((rc = device_ok())) return rc;
+  return launched(sp::launch_page_select(q, (hipStream_t)stream));
+}
+
 // ------------------------------------------------------------------ block select
 static int check_qk(const spattn_tensor* q, const spattn_tensor* k) {
   int rc;
@@ -364,10 +426,45 @@ SPATTN_API int spattn_block_select(const spattn_tensor* q, const spattn_tensor* 
 }
 
 // ------------------------------------------------------------------ attention
-static int attn_setup(const spattn_tensor* q, const spattn_tensor* k, const spattn_tensor* v,
-                      const spattn_selection* sel, sp::AttnParams& p, bool need_v) {
+// q [B, H_q, Nq, d] against a page pool [n_pages, H_kv, P, d] and its table
+static int check_q_pool(const spattn_tensor* q, const spattn_tensor* k, const spattn_kv_pages* pg, int& lgP,
+                        int64_t& ctx) {
   int rc;
-  if ((rc = check_qk(q, k))) return rc;
+  if ((rc = check_tensor(q, "q", 4, true))) return rc;
+  if ((rc = check_tensor(k, "k_pool", 4, true))) return rc;
+  if (q->dtype != k->dtype) return fail(SPATTN_ERR_INVALID_ARG, "q and k_pool dtypes differ");
+  if (q->dtype != SPATTN_F32 && q->dtype != SPATTN_BF16)
+    return fail(SPATTN_ERR_UNSUPPORTED, "q/k dtype must be f32 or bf16");
+  if (q->shape[3] != k->shape[3]) return fail(SPATTN_ERR_INVALID_ARG, "q/k_pool head dim mismatch");
+  if (k->shape[1] < 1 || q->shape[1] % k->shape[1])
+    return fail(SPATTN_ERR_INVALID_ARG, "KV heads must divide query heads");
+  if (q->shape[3] != 64 && q->shape[3] != 128) return fail(SPATTN_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  lgP = log2_pow2(pg->page_size, 4096);
+  if (lgP < 0) return fail(SPATTN_ERR_INVALID_ARG, "page_size must be a power of two in 1..4096");
+  if (k->shape[2] != pg->page_size) return fail(SPATTN_ERR_INVALID_ARG, "k_pool must be [n_pages, H_kv, page_size, d]");
+  if (k->shape[0] < 1 || k->shape[0] * (int64_t)pg->page_size >= ((int64_t)1 << 31))
+    return fail(SPATTN_ERR_UNSUPPORTED, "need 1 <= n_pages and n_pages * page_size < 2^31");
+  if ((rc = check_tensor(&pg->page_table, "page_table", 2, false))) return rc;
+  if (pg->page_table.dtype != SPATTN_I32) return fail(SPATTN_ERR_INVALID_ARG, "page_table must be int32");
+  if (pg->page_table.shape[0] != q->shape[0] || pg->page_table.shape[1] < 1)
+    return fail(SPATTN_ERR_INVALID_ARG, "page_table must be [B, max_pages]");
+  ctx = pg->page_table.shape[1] * (int64_t)pg->page_size;
+  if (ctx >= ((int64_t)1 << 31)) return fail(SPATTN_ERR_UNSUPPORTED, "max_pages * page_size must be < 2^31");
+  if (q->shape[2] < 1 || q->shape[2] > ctx) return fail(SPATTN_ERR_INVALID_ARG, "need 1 <= Nq <= ctx");
+  return SPATTN_OK;
+}
+
+static int attn_setup(const spattn_tensor* q, const spattn_tensor* k, const spattn_tensor* v,
+                      const spattn_selection* sel, sp::AttnParams& p, bool need_v,
+                      const spattn_kv_pages* pages = nullptr) {
+  int rc;
+  int lgP = 0;
+  int64_t pctx = 0;
+  if (pages) {
+    if ((rc = check_q_pool(q, k, pages, lgP, pctx))) return rc;
+  } else if ((rc = check_qk(q, k))) {
+    return rc;
+  }
   if (need_v) {
     if ((rc = check_tensor(v, "v", 4, true))) return rc;
     if (v->dtype != k->dtype) return fail(SPATTN_ERR_INVALID_ARG, "v dtype differs from k");
@@ -384,7 +481,12 @@ static int attn_setup(const spattn_tensor* q, const spattn_tensor* k, const spat
   p.Nq = (int)q->shape[2];
   p.d = (int)q->shape[3];
   p.Hkv = (int)k->shape[1];
-  p.ctx = (int)k->shape[2];
+  p.ctx = pages ? (int)pctx : (int)k->shape[2];
+  if (pages) {
+    p.ptab = (const int32_t*)pages->page_table.data;
+    p.pts = pages->page_table.stride[0];
+    p.lgP = lgP;
+  }
   p.mode = sel->mode;
   p.G_sel = 1;
   switch (sel->mode) {
@@ -421,6 +523,26 @@ static int attn_setup(const spattn_tensor* q, const spattn_tensor* k, const spat
       p.window = sel->window;
       break;
     }
+    case SPATTN_SEL_PAGES: {
+      if ((rc = check_tensor(&sel->idx, "sel.idx", 4, false))) return rc;
+      if (sel->idx.dtype != SPATTN_I32) return fail(SPATTN_ERR_INVALID_ARG, "sel.idx must be int32");
+      const int64_t G = sel->idx.shape[1];
+      if (sel->idx.shape[0] != p.B || sel->idx.shape[2] != p.Nq || G < 1 || p.Hq % G)
+        return fail(SPATTN_ERR_INVALID_ARG, "page list must be [B, G_sel, Nq, np] with G_sel | H_q");
+      if ((G % p.Hkv) && (p.Hkv % G))
+        return fail(SPATTN_ERR_INVALID_ARG, "G_sel and H_kv must divide one another");
+      const int lg = log2_pow2(sel->block_size, 4096);
+      if (lg < 0) return fail(SPATTN_ERR_INVALID_ARG, "PAGES: block_size must be a power of two in 1..4096");
+      const int64_t slots = sel->idx.shape[3] << lg;
+      if (slots >= ((int64_t)1 << 31)) return fail(SPATTN_ERR_UNSUPPORTED, "page list covers too many tokens");
+      p.G_sel = (int)G;
+      p.K = (int)slots;
+      p.bs = sel->block_size;
+      p.lgbs = lg;
+      p.sel = (const int32_t*)sel->idx.data;
+      for (int i = 0; i < 4; ++i) p.sels[i] = sel->idx.stride[i];
+      break;
+    }
     default: return fail(SPATTN_ERR_INVALID_ARG, "unknown selection mode %d", sel->mode);
   }
   return SPATTN_OK;
@@ -433,13 +555,12 @@ SPATTN_API size_t spattn_sparse_attn_fwd_workspace(const spattn_tensor* q, const
   return sp::attn_ws_bytes(p);
 }
 
-SPATTN_API int spattn_sparse_attn_fwd(const spattn_tensor* q, const spattn_tensor* k, const spattn_tensor* v,
-                                      const int32_t* ctx_len, float scale, const spattn_selection* sel,
-                                      const spattn_tensor* o_out, float* lse_out, void* ws, size_t ws_bytes,
-                                      void* stream) {
+static int attn_fwd(const spattn_tensor* q, const spattn_tensor* k, const spattn_tensor* v,
+                    const spattn_kv_pages* pages, const int32_t* ctx_len, float scale, const spattn_selection* sel,
+                    const spattn_tensor* o_out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
   sp::AttnParams p;
   int rc;
-  if ((rc = attn_setup(q, k, v, sel, p, true))) return rc;
+  if ((rc = attn_setup(q, k, v, sel, p, true, pages))) return rc;
   if ((rc = check_tensor(o_out, "o_out", 4, false))) return rc;
   if (o_out->dtype != SPATTN_F32) return fail(SPATTN_ERR_INVALID_ARG, "o_out must be f32");
   for (int i = 0; i < 4; ++i)
@@ -456,6 +577,29 @@ SPATTN_API int spattn_sparse_attn_fwd(const spattn_tensor* q, const spattn_tenso
   p.ws_bytes = ws_bytes;
   if ((rc = device_ok())) return rc;
   return launched(sp::launch_attention(p, (hipStream_t)stream));
+}
+
+SPATTN_API int spattn_sparse_attn_fwd(const spattn_tensor* q, const spattn_tensor* k, const spattn_tensor* v,
+                                      const int32_t* ctx_len, float scale, const spattn_selection* sel,
+                                      const spattn_tensor* o_out, float* lse_out, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  return attn_fwd(q, k, v, nullptr, ctx_len, scale, sel, o_out, lse_out, ws, ws_bytes, stream);
+}
+
+SPATTN_API size_t spattn_sparse_attn_fwd_paged_workspace(const spattn_tensor* q, const spattn_tensor* k_pool,
+                                                         const spattn_kv_pages* pages, const spattn_selection* sel) {
+  sp::AttnParams p;
+  if (!pages || attn_setup(q, k_pool, nullptr, sel, p, false, pages)) return (size_t)-1;
+  return sp::attn_ws_bytes(p);
+}
+
+SPATTN_API int spattn_sparse_attn_fwd_paged(const spattn_tensor* q, const spattn_tensor* k_pool,
+                                            const spattn_tensor* v_pool, const spattn_kv_pages* pages,
+                                            const int32_t* ctx_len, float scale, const spattn_selection* sel,
+                                            const spattn_tensor* o_out, float* lse_out, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  if (!pages) return fail(SPATTN_ERR_INVALID_ARG, "pages: null");
+  return attn_fwd(q, k_pool, v_pool, pages, ctx_len, scale, sel, o_out, lse_out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

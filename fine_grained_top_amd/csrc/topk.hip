@@ -75,24 +75,7 @@ SP_DEV RowCtx row_ctx(const TopkParams& p, int row) {
   c.s = p.scores + c.b * p.ss[0] + c.g * p.ss[1] + c.r * p.ss[2];
   c.ir = IndexerRow{};
   c.eps = (p.certified && p.err) ? p.err[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] : 0.f;
-  if (p.certified) {
-    const IndexerParams& x = p.ix;
-    const int hpg = x.hpg;
-    const int kg = x.G_k == 1 ? 0 : c.g;
-    const int esz = x.q.dt == DT_F32 ? 4 : 2;
-    const int ksz = x.k.dt == DT_F32 ? 4 : (x.k.dt == DT_BF16 ? 2 : 1);
-    c.ir.q = (const char*)x.q.p + (c.b * x.q.s[0] + c.r * x.q.s[1] + (int64_t)c.g * hpg * x.q.s[2]) * esz;
-    c.ir.qt = x.q.dt;
-    c.ir.qh_stride = x.q.s[2];
-    c.ir.k = (const char*)x.k.p + (c.b * x.k.s[0] + kg * x.k.s[2]) * ksz;
-    c.ir.kt = x.k.dt;
-    c.ir.k_stride = x.k.s[1];
-    c.ir.w = x.relu ? x.w + c.b * x.ws_[0] + c.r * x.ws_[1] + (int64_t)c.g * hpg * x.ws_[2] : nullptr;
-    c.ir.w_stride = x.ws_[2];
-    c.ir.H = hpg;
-    c.ir.d = x.d_I;
-    c.ir.relu = x.relu;
-  }
+  if (p.certified) c.ir = indexer_row(p.ix, c.b, c.g, c.r);
   return c;
 }
 

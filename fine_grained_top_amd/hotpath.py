@@ -2,8 +2,10 @@
 
 Orchestration only: it moves the seeded inputs to the device, owns the output
 and workspace buffers, and calls the libspattn entry points in order
-(indexer scores -> certified top-K -> sparse attention; block selection ->
-block-sparse attention; or a fixed window + global pattern).
+(indexer scores -> certified top-K -> sparse attention; indexer scores ->
+certified page selection -> attention over the pages of a paged KV cache;
+block selection -> block-sparse attention; or a fixed window + global
+pattern).
 """
 from __future__ import annotations
 
@@ -33,8 +35,16 @@ class HotPath:
         self.fused = fused
         dt = wl.dtype
         self.q = to_device(inp["q"], dt, device)
-        self.k = to_device(inp["k"], dt, device)
-        self.v = to_device(inp["v"], dt, device)
+        self.pages = None
+        if wl.page_size:
+            # paged KV cache: pools of pages and the page table (the logical K/V are not uploaded)
+            self.k = to_device(inp["k_pages"], dt, device)
+            self.v = to_device(inp["v_pages"], dt, device)
+            self.page_table = torch.from_numpy(inp["page_table"].astype(np.int32)).to(device)
+            self.pages = S.kv_pages(self.page_table, wl.page_size)
+        else:
+            self.k = to_device(inp["k"], dt, device)
+            self.v = to_device(inp["v"], dt, device)
         self.ctx_len = torch.from_numpy(inp["ctx_len"].astype(np.int32)).to(device)
         self.o = torch.empty(wl.B, wl.Hq, wl.Nq, wl.d, dtype=torch.float32, device=device)
         self.lse = torch.empty(wl.B, wl.Hq, wl.Nq, dtype=torch.float32, device=device)
@@ -50,9 +60,14 @@ class HotPath:
                                 mode, wl.heads_per_group)
             self.scores = torch.empty(wl.B, wl.G_sel, wl.Nq, wl.N, dtype=torch.float32, device=device)
             self.err = torch.empty(wl.B, wl.G_sel, wl.Nq, dtype=torch.float32, device=device)
-            self.idx = torch.empty(wl.B, wl.G_sel, wl.Nq, wl.topk, dtype=torch.int32, device=device)
+            width = wl.top_pages + wl.n_local if wl.kind == "dsa_pages" else wl.topk
+            self.idx = torch.empty(wl.B, wl.G_sel, wl.Nq, width, dtype=torch.int32, device=device)
             self.count = torch.empty(wl.B, wl.G_sel, wl.Nq, dtype=torch.int32, device=device)
-            self.sel = S.selection(S.SEL_INDEX, self.idx)
+            if wl.kind == "dsa_pages":
+                self.sel = S.selection(S.SEL_PAGES, self.idx, block_size=wl.page_size)
+                self.fused = False          # page selection reads the score matrix
+            else:
+                self.sel = S.selection(S.SEL_INDEX, self.idx)
             if self.fused and S.LIB.spattn_topk_workspace(None, S.ctypes.byref(self.ix), wl.topk,
                                                           S.TOPK_FUSED_INDEX) == S.SIZE_MAX:
                 self.fused = False          # this indexer shape has no fused kernel: separate calls
@@ -75,14 +90,22 @@ class HotPath:
         if self.wl.H_I:
             q.append(S.LIB.spattn_index_scores_workspace(byref(self.ix)))
             ts = S.tensor(self.scores)
-            q.append(S.LIB.spattn_topk_workspace(byref(ts), byref(self.ix), self.wl.topk, S.TOPK_CERTIFIED))
+            if self.wl.kind == "dsa_pages":
+                q.append(S.LIB.spattn_page_select_workspace(byref(ts), self.wl.page_size, self.wl.top_pages,
+                                                            self.wl.n_local))
+            else:
+                q.append(S.LIB.spattn_topk_workspace(byref(ts), byref(self.ix), self.wl.topk, S.TOPK_CERTIFIED))
             if self.fused:
                 q.append(S.LIB.spattn_topk_workspace(None, byref(self.ix), self.wl.topk, S.TOPK_FUSED_INDEX))
         tq, tk = S.tensor(self.q), S.tensor(self.k)
         if self.wl.kind == "blocks":
             q.append(S.LIB.spattn_block_select_workspace(byref(tq), byref(tk), self.wl.block_size,
                                                          self.wl.top_blocks))
-        q.append(S.LIB.spattn_sparse_attn_fwd_workspace(byref(tq), byref(tk), byref(self.sel)))
+        if self.pages is not None:
+            q.append(S.LIB.spattn_sparse_attn_fwd_paged_workspace(byref(tq), byref(tk), byref(self.pages),
+                                                                  byref(self.sel)))
+        else:
+            q.append(S.LIB.spattn_sparse_attn_fwd_workspace(byref(tq), byref(tk), byref(self.sel)))
         return q
 
     # the individual stages
@@ -97,20 +120,31 @@ class HotPath:
         S.spattn_topk(None, None, self.ix, self.ctx_len, self.wl.topk, S.TOPK_FUSED_INDEX,
                       self.idx, self.count, self.ws, stream)
 
+    def page_select(self, stream=None):
+        S.spattn_page_select(self.scores, self.err, self.ix, self.ctx_len, self.wl.page_size, self.wl.top_pages,
+                             self.wl.n_local, S.TOPK_CERTIFIED, self.idx, self.count, self.ws, stream)
+
     def block_select(self, stream=None):
         S.spattn_block_select(self.q, self.k, self.ctx_len, self.wl.block_size, self.wl.top_blocks,
                               self.idx, self.count, self.ws, stream)
 
     def attention(self, stream=None):
-        S.spattn_sparse_attn_fwd(self.q, self.k, self.v, self.ctx_len, 0.0, self.sel, self.o, self.lse,
-                                 self.ws, stream)
+        if self.pages is not None:
+            S.spattn_sparse_attn_fwd_paged(self.q, self.k, self.v, self.pages, self.ctx_len, 0.0, self.sel, self.o,
+                                           self.lse, self.ws, stream)
+        else:
+            S.spattn_sparse_attn_fwd(self.q, self.k, self.v, self.ctx_len, 0.0, self.sel, self.o, self.lse,
+                                     self.ws, stream)
 
     def step(self, stream=None):
         if self.wl.H_I and self.fused:
             self.topk_fused(stream)
         elif self.wl.H_I:
             self.index_scores(stream)
-            self.topk(stream)
+            if self.wl.kind == "dsa_pages":
+                self.page_select(stream)
+            else:
+                self.topk(stream)
         elif self.wl.kind == "blocks":
             self.block_select(stream)
         self.attention(stream)

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libspattn.so")
 
 F32, BF16, FP8_E4M3, I32 = 0, 1, 2, 3
 SCORE_DOT, SCORE_WEIGHTED_RELU = 0, 1
-SEL_DENSE, SEL_INDEX, SEL_WINDOW_GLOBAL, SEL_BLOCKS = 0, 1, 2, 3
+SEL_DENSE, SEL_INDEX, SEL_WINDOW_GLOBAL, SEL_BLOCKS, SEL_PAGES = 0, 1, 2, 3, 4
 TOPK_CERTIFIED, TOPK_FUSED_INDEX = 1, 2
 
 SIZE_MAX = ctypes.c_size_t(-1).value
@@ -48,6 +48,10 @@ class Selection(ctypes.Structure):
                 ("n_global", ctypes.c_int32), ("block_size", ctypes.c_int32)]
 
 
+class KvPages(ctypes.Structure):
+    _fields_ = [("page_table", Tensor), ("page_size", ctypes.c_int32)]
+
+
 def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built; run __graft_entry__.build() first")
@@ -59,11 +63,17 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "spattn_index_scores": (ctypes.c_int, [P(Indexer), vp, P(Tensor), vp, vp, sz, vp]),
         "spattn_topk_workspace": (sz, [P(Tensor), P(Indexer), i32, u32]),
         "spattn_topk": (ctypes.c_int, [P(Tensor), vp, P(Indexer), vp, i32, u32, P(Tensor), vp, vp, sz, vp]),
+        "spattn_page_select_workspace": (sz, [P(Tensor), i32, i32, i32]),
+        "spattn_page_select": (ctypes.c_int, [P(Tensor), vp, P(Indexer), vp, i32, i32, i32, u32, P(Tensor), vp,
+                                              vp, sz, vp]),
         "spattn_block_select_workspace": (sz, [P(Tensor), P(Tensor), i32, i32]),
         "spattn_block_select": (ctypes.c_int, [P(Tensor), P(Tensor), vp, i32, i32, P(Tensor), vp, vp, sz, vp]),
         "spattn_sparse_attn_fwd_workspace": (sz, [P(Tensor), P(Tensor), P(Selection)]),
         "spattn_sparse_attn_fwd": (ctypes.c_int, [P(Tensor), P(Tensor), P(Tensor), vp, ctypes.c_float,
                                                   P(Selection), P(Tensor), vp, vp, sz, vp]),
+        "spattn_sparse_attn_fwd_paged_workspace": (sz, [P(Tensor), P(Tensor), P(KvPages), P(Selection)]),
+        "spattn_sparse_attn_fwd_paged": (ctypes.c_int, [P(Tensor), P(Tensor), P(Tensor), P(KvPages), vp,
+                                                        ctypes.c_float, P(Selection), P(Tensor), vp, vp, sz, vp]),
         "spattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "spattn_version": (ctypes.c_char_p, []),
         "spattn_last_error_message": (ctypes.c_char_p, []),
@@ -128,6 +138,7 @@ def indexer(q_idx: torch.Tensor, k_idx: torch.Tensor, w: Optional[torch.Tensor],
     ix.w = tensor(w)
     ix.score_mode = score_mode
     ix.heads_per_group = heads_per_group
+    ix._keep = (q_idx, k_idx, w)        # the struct holds raw pointers: keep the tensors alive with it
     return ix
 
 
@@ -139,7 +150,16 @@ def selection(mode: int, idx: Optional[torch.Tensor] = None, window: int = 0, n_
     s.window = window
     s.n_global = n_global
     s.block_size = block_size
+    s._keep = idx
     return s
+
+
+def kv_pages(page_table: torch.Tensor, page_size: int) -> KvPages:
+    kp = KvPages()
+    kp.page_table = tensor(page_table)
+    kp.page_size = page_size
+    kp._keep = page_table
+    return kp
 
 
 # ---------------------------------------------------------------- entry points
@@ -169,6 +189,21 @@ def spattn_topk(scores: Optional[torch.Tensor], err: Optional[torch.Tensor], ix:
                            _ptr(count_out), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
 
 
+def spattn_page_select(scores: torch.Tensor, err: Optional[torch.Tensor], ix: Optional[Indexer],
+                       ctx_len: Optional[torch.Tensor], page_size: int, top_pages: int, n_local: int, flags: int,
+                       pg_idx_out: torch.Tensor, pg_count_out: Optional[torch.Tensor] = None,
+                       ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    sc, io = tensor(scores), tensor(pg_idx_out)
+    need = LIB.spattn_page_select_workspace(ctypes.byref(sc), page_size, top_pages, n_local)
+    if need == SIZE_MAX:
+        raise SpattnError(1, LIB.spattn_last_error_message().decode())
+    ws = _workspace(need, scores.device, ws)
+    ixp = ctypes.byref(ix) if ix is not None else None
+    _check(LIB.spattn_page_select(ctypes.byref(sc), _ptr(err), ixp, _ptr(ctx_len), page_size, top_pages, n_local,
+                                  flags, ctypes.byref(io), _ptr(pg_count_out), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(stream)))
+
+
 def spattn_block_select(q: torch.Tensor, k: torch.Tensor, ctx_len: Optional[torch.Tensor], block_size: int,
                         top_blocks: int, blk_idx_out: torch.Tensor, blk_count_out: Optional[torch.Tensor] = None,
                         ws: Optional[torch.Tensor] = None, stream=None) -> None:
@@ -194,6 +229,22 @@ def spattn_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ct
     _check(LIB.spattn_sparse_attn_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), _ptr(ctx_len),
                                       scale, ctypes.byref(sel), ctypes.byref(to), _ptr(lse_out), _ptr(ws),
                                       0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def spattn_sparse_attn_fwd_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, pages: KvPages,
+                                 ctx_len: Optional[torch.Tensor], scale: float, sel: Selection,
+                                 o_out: torch.Tensor, lse_out: Optional[torch.Tensor] = None,
+                                 ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    tq, tk, tv, to = tensor(q), tensor(k_pool), tensor(v_pool), tensor(o_out)
+    need = LIB.spattn_sparse_attn_fwd_paged_workspace(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(pages),
+                                                      ctypes.byref(sel))
+    if need == SIZE_MAX:
+        raise SpattnError(1, LIB.spattn_last_error_message().decode())
+    ws = _workspace(need, q.device, ws)
+    _check(LIB.spattn_sparse_attn_fwd_paged(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv),
+                                            ctypes.byref(pages), _ptr(ctx_len), scale, ctypes.byref(sel),
+                                            ctypes.byref(to), _ptr(lse_out), _ptr(ws),
+                                            0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def spattn_version() -> str:

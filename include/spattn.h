@@ -18,7 +18,10 @@
  *  - "Sparse Attention Is Reshaping Production AI", fixed patterns and
  *    learned block routing (mean-pooled block keys, top-k blocks);
  *  - "Sparse Attention" (completesystemdesign.dev), sliding window + global
- *    tokens and block-sparse patterns.
+ *    tokens and block-sparse patterns;
+ *  - "Sparse Attention in 2026", DSA list (page-granular selection: the
+ *    indexer rates every KV page, attention reads the best pages plus the
+ *    mandatory recent pages).
  *
  * Conventions shared by every call
  *  - All tensors are caller-owned device buffers described by spattn_tensor
@@ -99,18 +102,33 @@ enum spattn_sel_mode {
   SPATTN_SEL_DENSE = 0,          /* S = all keys 0..p (the conservative fallback) */
   SPATTN_SEL_INDEX = 1,          /* S = explicit index list (e.g. from spattn_topk) */
   SPATTN_SEL_WINDOW_GLOBAL = 2,  /* S = {p-window+1..p} U {0..n_global-1}, within 0..p */
-  SPATTN_SEL_BLOCKS = 3          /* S = selected blocks U {p-window+1..p}, within 0..p */
+  SPATTN_SEL_BLOCKS = 3,         /* S = selected blocks U {p-window+1..p}, within 0..p */
+  SPATTN_SEL_PAGES = 4           /* S = every token of the listed pages, within 0..p */
 };
 
 typedef struct spattn_selection {
   int32_t mode;          /* enum spattn_sel_mode */
   spattn_tensor idx;     /* INDEX: int32 [B, G_sel, Nq, K], ascending key positions, -1
                             padded; G_sel divides H_q and G_sel | H_kv or H_kv | G_sel.
-                            BLOCKS: int32 [B, H_q, Nq, nb] block ids, -1 padded. */
+                            BLOCKS: int32 [B, H_q, Nq, nb] block ids, -1 padded.
+                            PAGES: int32 [B, G_sel, Nq, np] page ids (page pg = tokens
+                            pg*block_size .. pg*block_size+block_size-1), ascending, -1
+                            padded (e.g. from spattn_page_select); G_sel as for INDEX. */
   int32_t window;        /* keys in the sliding window, the query itself included */
   int32_t n_global;      /* WINDOW_GLOBAL: tokens 0..n_global-1 are visible to all rows */
-  int32_t block_size;    /* BLOCKS: tokens per block */
+  int32_t block_size;    /* BLOCKS: tokens per block; PAGES: tokens per page (power of two) */
 } spattn_selection;
+
+/* Paged K/V storage: the keys and values of all requests live in a pool of
+ * fixed-size pages, and a page table maps each request's logical pages to pool
+ * pages. Logical token j of request b is row j mod page_size of pool page
+ * page_table[b, j / page_size]. */
+typedef struct spattn_kv_pages {
+  spattn_tensor page_table;   /* int32 [B, max_pages]; entries of pages that hold tokens
+                                 0..ctx_len[b]-1 must lie in [0, n_pages) (read on the
+                                 device, not checked by the host); others are not read */
+  int32_t page_size;          /* tokens per page: a power of two in 1..4096 */
+} spattn_kv_pages;
 
 /* ------------------------------------------------------------------------
  * spattn_index_scores — indexer scores for every (query row, past key).
@@ -163,6 +181,41 @@ SPATTN_API int spattn_topk(const spattn_tensor* scores, const float* err,
                            void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * spattn_page_select — page-granular selection.
+ * Source: "Sparse Attention in 2026: Why It Finally Had to Be Native", DSA
+ * list (the indexer rates every KV page; attention reads the top-rated
+ * pages plus the mandatory recent/local pages, whole, without compression).
+ *
+ * Row (b,g,r) at position p: page pg covers tokens pg*P .. pg*P+P-1. The
+ * n_local most recent pages (the one holding p and those before it) are
+ * always read. Every earlier page is a candidate keyed by the largest
+ * selection key among its tokens within 0..p (the page does not say how
+ * token ratings combine; this is the reading the library takes), and the
+ * min(top_pages, #candidates) best by (key descending, page ascending) are
+ * added. pg_idx_out int32 [B, G, Nq, top_pages + n_local] receives the page
+ * ids ascending, -1 padded; pg_count_out int32 [B, G, Nq] (optional) the
+ * number of pages.
+ *
+ *  scores: f32 [B, G, Nq, ctx] token scores (entries past p are not read).
+ *  flags = 0: keys are the float32 scores as given.
+ *  flags = SPATTN_TOPK_CERTIFIED: scores and err come from
+ *      spattn_index_scores on indexer ix; keys are the exact token keys (the
+ *      float32 nearest to the exact score), near-ties rescored exactly, so
+ *      the page list equals exhaustive selection on exact keys.
+ *  Limits: P a power of two in 1..4096; ceil(ctx / P) <= 16384;
+ *  top_pages, n_local >= 0 with top_pages + n_local >= 1; top_pages <= 16384.
+ *  No workspace is needed (the query returns 0).
+ * ---------------------------------------------------------------------- */
+SPATTN_API size_t spattn_page_select_workspace(const spattn_tensor* scores, int32_t page_size,
+                                               int32_t top_pages, int32_t n_local);
+SPATTN_API int spattn_page_select(const spattn_tensor* scores, const float* err,
+                                  const spattn_indexer* ix, const int32_t* ctx_len,
+                                  int32_t page_size, int32_t top_pages, int32_t n_local,
+                                  uint32_t flags, const spattn_tensor* pg_idx_out,
+                                  int32_t* pg_count_out, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/* ------------------------------------------------------------------------
  * spattn_block_select — block routing for block-sparse attention.
  * Source: "Sparse Attention Is Reshaping Production AI", Learned Block
  * Routing (keys mean-pooled per block, unscaled dot product with the query,
@@ -206,6 +259,31 @@ SPATTN_API int spattn_sparse_attn_fwd(const spattn_tensor* q, const spattn_tenso
                                       float scale, const spattn_selection* sel,
                                       const spattn_tensor* o_out, float* lse_out, void* ws,
                                       size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * spattn_sparse_attn_fwd_paged — the same attention over paged K/V storage
+ * (the serving layout in which the pages of "Sparse Attention in 2026", DSA
+ * list, are the unit of selection and of reading).
+ *
+ *  k_pool, v_pool: [n_pages, H_kv, page_size, d], same dtype as q (bf16 or
+ *     f32), d in {64, 128}, rows 16-byte aligned; n_pages * page_size < 2^31.
+ *  pages: the page table and page size; the logical capacity is
+ *     ctx = max_pages * page_size and ctx_len values must lie in [Nq, ctx].
+ *  Every selection mode is accepted; INDEX and PAGES lists with bf16, d = 128
+ *  take the gather kernel, the others a generic kernel. Everything else as
+ *  spattn_sparse_attn_fwd.
+ * ---------------------------------------------------------------------- */
+SPATTN_API size_t spattn_sparse_attn_fwd_paged_workspace(const spattn_tensor* q,
+                                                         const spattn_tensor* k_pool,
+                                                         const spattn_kv_pages* pages,
+                                                         const spattn_selection* sel);
+SPATTN_API int spattn_sparse_attn_fwd_paged(const spattn_tensor* q, const spattn_tensor* k_pool,
+                                            const spattn_tensor* v_pool,
+                                            const spattn_kv_pages* pages,
+                                            const int32_t* ctx_len, float scale,
+                                            const spattn_selection* sel,
+                                            const spattn_tensor* o_out, float* lse_out,
+                                            void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ helpers */
 SPATTN_API const char* spattn_status_string(int status);

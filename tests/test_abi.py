@@ -135,3 +135,58 @@ def test_block_select_validation():
     assert call(16, 0) == 1
     assert call(16, 2, ws_bytes=8) == 3
     assert call(16, 3) == 1                      # output width must equal top_blocks
+
+
+def test_page_select_validation():
+    sc = torch.zeros(1, 2, 4, 256)
+    io = torch.zeros(1, 2, 4, 5, dtype=torch.int32)
+
+    def call(P, top, loc, flags=0, idx=io, scores=sc):
+        s, o = S.tensor(scores), S.tensor(idx)
+        return S.LIB.spattn_page_select(ctypes.byref(s), None, None, None, P, top, loc, flags, ctypes.byref(o),
+                                        None, None, 0, None)
+
+    assert S.LIB.spattn_page_select_workspace(ctypes.byref(S.tensor(sc)), 64, 3, 2) == 0
+    assert call(64, 3, 2) == 4                  # valid: reaches the device check
+    assert call(16, 5, 0) == 4
+    assert call(48, 3, 2) == 1                  # page size not a power of two
+    assert call(8192, 3, 2) == 1                # page size above 4096
+    assert call(64, 0, 0, idx=torch.zeros(1, 2, 4, 0, dtype=torch.int32)) == 1
+    assert call(64, -1, 6) == 1
+    assert call(64, 3, 1) == 1                  # width must be top_pages + n_local
+    assert call(64, 3, 2, flags=S.TOPK_CERTIFIED) == 1   # certified needs err + indexer
+    assert call(64, 3, 2, flags=S.TOPK_FUSED_INDEX) == 1  # no fused variant
+    assert call(1, 3, 2, scores=torch.zeros(1, 2, 4, 20000)) == 2   # more than 16384 pages
+    assert "pages" in S.spattn_last_error_message()
+
+
+def test_paged_attention_validation():
+    q = torch.zeros(2, 4, 1, 128, dtype=torch.bfloat16)
+    pool = torch.zeros(6, 2, 16, 128, dtype=torch.bfloat16)
+    table = torch.zeros(2, 3, dtype=torch.int32)
+    o = torch.zeros(2, 4, 1, 128)
+    pidx = torch.zeros(2, 2, 1, 3, dtype=torch.int32)
+
+    def call(sel, kk=pool, vv=pool, tab=table, P=16, oo=o):
+        tq, tk, tv, to = S.tensor(q), S.tensor(kk), S.tensor(vv), S.tensor(oo)
+        pg = S.kv_pages(tab, P)
+        ws = torch.zeros(1 << 20, dtype=torch.uint8)
+        return S.LIB.spattn_sparse_attn_fwd_paged(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv),
+                                                  ctypes.byref(pg), None, 0.0, ctypes.byref(sel), ctypes.byref(to),
+                                                  None, ws.data_ptr(), ws.numel(), None)
+
+    assert call(S.selection(S.SEL_PAGES, pidx, block_size=16)) == 4
+    assert call(S.selection(S.SEL_INDEX, torch.zeros(2, 2, 1, 8, dtype=torch.int32))) == 4
+    assert call(S.selection(S.SEL_DENSE)) == 4
+    assert call(S.selection(S.SEL_PAGES, pidx, block_size=12)) == 1            # not a power of two
+    assert call(S.selection(S.SEL_PAGES, pidx, block_size=16), P=8) == 1       # pool pages hold 16 tokens
+    assert call(S.selection(S.SEL_DENSE), tab=torch.zeros(3, 3, dtype=torch.int32)) == 1   # one row per request
+    assert call(S.selection(S.SEL_DENSE), tab=torch.zeros(2, 3)) == 1          # table must be int32
+    assert call(S.selection(S.SEL_DENSE), vv=torch.zeros(6, 2, 16, 64, dtype=torch.bfloat16)) == 1
+    # the plain entry point is unchanged by the page-list mode
+    tq, tk, to = S.tensor(q), S.tensor(torch.zeros(2, 2, 48, 128, dtype=torch.bfloat16)), S.tensor(o)
+    sel = S.selection(S.SEL_PAGES, pidx, block_size=16)
+    ws = torch.zeros(1 << 20, dtype=torch.uint8)
+    assert S.LIB.spattn_sparse_attn_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tk), None, 0.0,
+                                        ctypes.byref(sel), ctypes.byref(to), None, ws.data_ptr(), ws.numel(),
+                                        None) == 4

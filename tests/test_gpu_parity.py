@@ -48,10 +48,11 @@ def check_sets(hp, res, rows, wl):
     idx = hp.idx.cpu().numpy()
     cnt = hp.count.cpu().numpy()
     groups = wl.Hq if wl.kind == "blocks" else wl.G_sel
+    listed = wl.kind in ("blocks", "dsa_pages")          # block or page lists, not token sets
     bad = 0
     for (b, r) in rows:
         for g in range(groups):
-            want = res.blocks[(b, g, r)] if wl.kind == "blocks" else res.sets[(b, g, r)]
+            want = res.blocks[(b, g, r)] if listed else res.sets[(b, g, r)]
             got = idx[b, g, r]
             ok = cnt[b, g, r] == len(want) and np.array_equal(got[:len(want)], want) and np.all(got[len(want):] == -1)
             if not ok:
@@ -130,7 +131,8 @@ def test_tiny_fp32_full():
 
 
 @pytest.mark.parametrize("name", ["dsa_decode_small", "dsa_prefill_small", "window_global_small",
-                                  "block_sparse_small", "tiny_topk_f32_small"])
+                                  "block_sparse_small", "tiny_topk_f32_small", "dsa_paged_decode_small",
+                                  "dsa_paged_prefill_small"])
 def test_small_workload(name):
     wl = gen.WORKLOADS[name]
     inp = gen.generate(wl)
@@ -499,3 +501,201 @@ def test_blocks_attention_edge_lists(bs):
                 worst = max(worst, float(np.abs(O[b, h, r] - Oo[0]).max()), abs(float(LS[b, h, r] - Lo[0])))
     say(f"  max |O - O_oracle|, |LSE - LSE_oracle| = {worst:.3e}")
     assert worst <= 2e-3
+
+
+# ---------------------------------------------------------------- page-granular selection, paged KV
+def _page_select_on(sc, P, top, n_local, ctx_len):
+    sp = S()
+    B, G, nq, ctx = sc.shape
+    idx = torch.full((B, G, nq, top + n_local), 7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B, G, nq), 7, dtype=torch.int32, device="cuda")
+    cl = torch.tensor(ctx_len, dtype=torch.int32, device="cuda")
+    sp.spattn_page_select(sc, None, None, cl, P, top, n_local, 0, idx, cnt)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), cnt.cpu().numpy()
+
+
+def _check_pages(idx, cnt, keys_of, ctx_len, Nq, P, top, n_local):
+    import oracle as orc
+    B, G = idx.shape[:2]
+    for b in range(B):
+        for g in range(G):
+            for r in range(Nq):
+                p = ctx_len[b] - Nq + r
+                want = orc.page_select(keys_of(b, g, r, p), p, P, top, n_local)
+                assert cnt[b, g, r] == len(want), (P, top, n_local, b, g, r)
+                assert np.array_equal(idx[b, g, r, : len(want)], want), (P, top, n_local, b, g, r)
+                assert np.all(idx[b, g, r, len(want):] == -1)
+
+
+@pytest.mark.parametrize("ctx", [3000, 3001])
+def test_page_select_ties_and_edges(ctx):
+    """Uncertified page selection on integer scores (many tied page keys), +-0,
+    a row of equal scores, ragged lengths, page sizes from 1 to 512, rows that
+    are and are not 16-byte aligned (odd row length), and top_pages from 0 to
+    more than the candidate pages."""
+    say(f"[gpu] page select ties/edges ctx={ctx}")
+    rng = np.random.default_rng(31)
+    B, G, Nq = 2, 2, 12
+    sc = rng.integers(-6, 7, size=(B, G, Nq, ctx)).astype(np.float32)
+    sc[0, 0, 3] = 1.0
+    sc[1, 1, :, ::3] = -0.0
+    sc[1, 1, :, 1::3] = 0.0
+    ctx_len = [ctx, 1777]
+    dev = torch.from_numpy(sc).cuda()
+    for P, top, n_local in [(1, 40, 0), (1, 5, 3), (4, 7, 1), (16, 5, 2), (16, 0, 3), (64, 6, 2), (64, 1, 0),
+                            (128, 3, 1), (512, 1, 1), (64, 1000, 2), (4096, 1, 0)]:
+        idx, cnt = _page_select_on(dev, P, top, n_local, ctx_len)
+        _check_pages(idx, cnt, lambda b, g, r, p: sc[b, g, r, : p + 1], ctx_len, Nq, P, top, n_local)
+
+
+def _dot_page_case(q, k, P, top, n_local, Nq):
+    """Certified page selection from indexer scores (DOT, f32) against the
+    oracle's exact keys."""
+    import oracle as orc
+    sp = S()
+    ctx = k.shape[1]
+    qt = torch.from_numpy(q).cuda()
+    kt = torch.from_numpy(k).cuda()
+    ix = sp.indexer(qt, kt, None, sp.SCORE_DOT, 1)
+    scores = torch.empty(1, 1, Nq, ctx, device="cuda")
+    err = torch.empty(1, 1, Nq, device="cuda")
+    sp.spattn_index_scores(ix, None, scores, err)
+    idx = torch.full((1, 1, Nq, top + n_local), 7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((1, 1, Nq), 7, dtype=torch.int32, device="cuda")
+    sp.spattn_page_select(scores, err, ix, None, P, top, n_local, sp.TOPK_CERTIFIED, idx, cnt)
+    torch.cuda.synchronize()
+    keys = lambda b, g, r, p: orc.keys_dot(q[0, r, 0].astype(np.float64), k[0, : p + 1, 0].astype(np.float64))
+    _check_pages(idx.cpu().numpy(), cnt.cpu().numpy(), keys, [ctx], Nq, P, top, n_local)
+
+
+def test_page_select_certified_near_ties():
+    """Token scores at and a hair off float32 halfway points (the second
+    product of +-2^-70 needs the wide fixed-point accumulation): page keys tie
+    in float32 and only the exact keys order the pages."""
+    say("[gpu] certified page select near ties")
+    d, ctx, Nq = 8, 96, 4
+    a = np.float32(1.0 + 2.0 ** -12)
+    t = np.float32(2.0 ** -35)
+    q = np.zeros((1, Nq, 1, d), np.float32)
+    q[0, :, 0, 0] = a
+    q[0, :, 0, 1] = t
+    k = np.zeros((1, ctx, 1, d), np.float32)
+    for j in range(ctx):
+        kind = j % 6
+        if kind == 0:
+            k[0, j, 0, 0] = np.float32(1.0 + 2.0 ** -10)
+        elif kind == 1:
+            k[0, j, 0, 0] = np.float32(1.0)
+        else:
+            k[0, j, 0, 0] = a
+            k[0, j, 0, 1] = [t, -t, np.float32(0.0), t][kind - 2]
+    for P, top, n_local in [(1, 20, 0), (1, 40, 2), (2, 12, 1), (4, 5, 0), (8, 3, 1)]:
+        _dot_page_case(q, k, P, top, n_local, Nq)
+    # pages whose best tokens sit at rounding midpoints of the plain dot product
+    q2 = np.zeros((1, 2, 1, d), np.float32)
+    q2[0, :, 0, :2] = 1.0
+    k2 = np.zeros((1, 64, 1, d), np.float32)
+    k2[0, :, 0, 0] = 1.0
+    tiny = np.float32(2.0 ** -24)
+    pattern = [tiny, tiny + np.float32(2.0 ** -40), 0.0, 3 * tiny]
+    for j in range(64):
+        k2[0, j, 0, 1] = pattern[j % 4] if j % 5 else np.float32(-1.0)
+    for P, top, n_local in [(1, 10, 0), (2, 6, 1), (4, 3, 2)]:
+        _dot_page_case(q2, k2, P, top, n_local, 2)
+
+
+def test_paged_decode_full_every_row():
+    wl = gen.WORKLOADS["dsa_paged_decode"]
+    say("[gpu] generating dsa_paged_decode inputs")
+    inp = gen.generate(wl)
+    hp = run(wl, inp)
+    rows = _all_rows(wl, inp)
+    res = oracle_rows(wl, inp, rows)
+    check_sets(hp, res, rows, wl)
+    check_out(hp, res, rows, 2e-3)
+
+
+def _pool(x, table, P):
+    """[B, Hkv, ctx, d] -> a page pool [B * npr, Hkv, P, d] laid out by the page table."""
+    B, Hkv, ctx, d = x.shape
+    npr = table.shape[1]
+    pad = npr * P - ctx
+    xp = torch.cat([x, torch.zeros(B, Hkv, pad, d, dtype=x.dtype)], dim=2) if pad else x
+    logical = xp.reshape(B, Hkv, npr, P, d).permute(0, 2, 1, 3, 4).reshape(B * npr, Hkv, P, d)
+    pool = torch.empty_like(logical)
+    pool[torch.from_numpy(table.reshape(-1)).long()] = logical
+    return pool.contiguous()
+
+
+@pytest.mark.parametrize("dtype,d,Nq", [("bf16", 128, 1), ("bf16", 128, 40), ("f32", 64, 40)])
+def test_paged_storage_matches_contiguous(dtype, d, Nq):
+    """Attention over a paged pool reads the same keys as over the contiguous
+    cache: with the same kernel the outputs agree bit for bit, for index lists
+    and for page lists; page lists also agree bit for bit with the index lists
+    they expand to, and every row matches the oracle."""
+    import oracle as orc
+    sp = S()
+    say(f"[gpu] paged vs contiguous {dtype} d={d} Nq={Nq}")
+    g = torch.Generator().manual_seed(41)
+    B, Hq, Hkv, ctx, P, npg = 3, 8, 2, 1000, 16, 9
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = torch.randn(B, Hq, Nq, d, generator=g).to(tdt)
+    k = torch.randn(B, Hkv, ctx, d, generator=g).to(tdt)
+    v = torch.randn(B, Hkv, ctx, d, generator=g).to(tdt)
+    ctx_len = [1000, 777, 513]
+    npr = (ctx + P - 1) // P
+    table = np.random.default_rng(42).permutation(B * npr).astype(np.int32).reshape(B, npr)
+    kp, vp = _pool(k, table, P), _pool(v, table, P)
+    rng = np.random.default_rng(43)
+    plist = np.full((B, Hkv, Nq, npg), -1, np.int32)
+    tlist = np.full((B, Hkv, Nq, npg * P), -1, np.int32)
+    for b in range(B):
+        for gg in range(Hkv):
+            for r in range(Nq):
+                p = ctx_len[b] - Nq + r
+                last = p // P
+                n = int(rng.integers(1, npg + 1))
+                pages = np.sort(rng.choice(np.arange(last + 2), size=min(n, last + 2), replace=False))
+                plist[b, gg, r, : len(pages)] = pages             # may include the page after p
+                toks = np.concatenate([np.arange(P * x, P * x + P) for x in pages])
+                tlist[b, gg, r, : len(toks)] = toks
+    cl = torch.tensor(ctx_len, dtype=torch.int32, device="cuda")
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    kpd, vpd = kp.cuda(), vp.cuda()
+    tab = torch.from_numpy(table).cuda()
+    pages = sp.kv_pages(tab, P)
+    pld, tld = torch.from_numpy(plist).cuda(), torch.from_numpy(tlist).cuda()
+    outs = {}
+    for name, sel in [("pages", sp.selection(sp.SEL_PAGES, pld, block_size=P)),
+                      ("index", sp.selection(sp.SEL_INDEX, tld))]:
+        for paged in (False, True):
+            o = torch.empty(B, Hq, Nq, d, device="cuda")
+            lse = torch.empty(B, Hq, Nq, device="cuda")
+            if paged:
+                sp.spattn_sparse_attn_fwd_paged(qd, kpd, vpd, pages, cl, 0.0, sel, o, lse)
+            else:
+                sp.spattn_sparse_attn_fwd(qd, kd, vd, cl, 0.0, sel, o, lse)
+            torch.cuda.synchronize()
+            outs[(name, paged)] = (o.cpu(), lse.cpu())
+    ref_o, ref_l = outs[("index", False)]
+    for key, (o, l) in outs.items():
+        assert torch.equal(o, ref_o) and torch.equal(l, ref_l), key
+    q64, k64, v64 = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    worst = 0.0
+    for b in range(B):
+        for h in range(Hq):
+            kvh = h // (Hq // Hkv)
+            for r in range(Nq):
+                p = ctx_len[b] - Nq + r
+                S_ = orc.pages_set([x for x in plist[b, kvh, r] if x >= 0], p, P)
+                if len(S_) == 0:                                  # only the page after p was listed
+                    assert torch.all(ref_o[b, h, r] == 0) and float(ref_l[b, h, r]) == -math.inf
+                    continue
+                o, l = orc.masked_attention(q64[b, h, r][None], k64[b, kvh, : p + 1], v64[b, kvh, : p + 1], S_,
+                                            1.0 / math.sqrt(d))
+                worst = max(worst, float(np.abs(ref_o[b, h, r].double().numpy() - o[0]).max()),
+                            abs(float(ref_l[b, h, r]) - float(l[0])))
+    tol = 1e-5 if dtype == "f32" else 2e-3
+    say(f"  max diff vs oracle {worst:.3e} (tol {tol})")
+    assert worst <= tol
