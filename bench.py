@@ -70,6 +70,20 @@ def algorithmic(wl, inp, hp, fused):
         flops_att = 4.0 * pairs * wl.d
         out["attention"] = {"bytes": gath + qkv_out, "flops": flops_att,
                             "bound": "hbm" if wl.Nq == 1 else "mfma"}
+        if wl.kind == "dsa_pages":
+            # page lists: every listed page is read whole (cut at the query position)
+            P = wl.page_size
+            width = wl.top_pages + wl.n_local
+            out["page_select"] = {"bytes": score_bytes + wl.B * wl.G_sel * wl.Nq * width * 4,
+                                  "rows": wl.B * wl.G_sel * wl.Nq}
+            pg = hp.idx.cpu().numpy().astype(np.int64)                      # [B, G, Nq, width]
+            pos = np.stack([L - wl.Nq + np.arange(wl.Nq) for L in lens])[:, None, :, None]
+            tok = np.clip(np.minimum(pg * P + P, pos + 1) - pg * P, 0, None) * (pg >= 0)
+            sel_g = float(tok.sum())                                         # sum over (b, g, r) of |S|
+            per_sel = (wl.Hq // max(wl.Hq // wl.G_sel, wl.Hq // wl.Hkv)) // wl.G_sel   # gathers per group
+            out["attention"] = {"bytes": sel_g * per_sel * wl.d * e * 2 + qkv_out,
+                                "flops": 4.0 * sel_g * (wl.Hq // wl.G_sel) * wl.d,
+                                "bound": "hbm" if wl.Nq == 1 else "mfma"}
     elif wl.kind == "window_global":
         pairs = float(metrics.window_global_pairs(wl.N, wl.window, wl.n_global)) * wl.Hq * wl.B
         kv = wl.B * wl.Hkv * wl.N * wl.d * e * 2
@@ -157,6 +171,9 @@ def main():
     stages = []
     if wl.H_I and fused:
         stages = [("index_topk_fused", lambda hp: hp.topk_fused()), ("attention", lambda hp: hp.attention())]
+    elif wl.H_I and wl.kind == "dsa_pages":
+        stages = [("index_scores", lambda hp: hp.index_scores()), ("page_select", lambda hp: hp.page_select()),
+                  ("attention", lambda hp: hp.attention())]
     elif wl.H_I:
         stages = [("index_scores", lambda hp: hp.index_scores()), ("topk", lambda hp: hp.topk()),
                   ("attention", lambda hp: hp.attention())]
@@ -255,7 +272,7 @@ def main():
             ok &= err <= (1e-5 if wl.dtype == "f32" else 2e-3)
             if idx is not None and wl.kind != "blocks":
                 for g in range(wl.G_sel):
-                    want = res.sets[(b, g, r)]
+                    want = res.blocks[(b, g, r)] if wl.kind == "dsa_pages" else res.sets[(b, g, r)]
                     ok &= bool(np.array_equal(idx[b, g, r, : len(want)], want))
             if time.perf_counter() - t0 > args.cpu_seconds:
                 break
@@ -279,7 +296,9 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if wl.dtype == "f32" else "bf16",
         "data": "synthetic",
-        "path": "fused indexer+top-K" if fused else "separate indexer and top-K calls",
+        "path": ("indexer scores, certified page selection, attention over a paged KV cache"
+                 if wl.kind == "dsa_pages" else
+                 "fused indexer+top-K" if fused else "separate indexer and top-K calls"),
         "config": {"workload": wl.name, "B": wl.B, "ctx_capacity": wl.N, "Nq": wl.Nq, "Hq": wl.Hq,
                    "Hkv": wl.Hkv, "d": wl.d, "H_I": wl.H_I, "d_I": wl.d_I, "topk": wl.topk,
                    "idx_k_dtype": wl.idx_k_dtype, "len_range": wl.len_range, "replicas": args.replicas},
@@ -289,6 +308,8 @@ def main():
         "oracle_spot_parity": parity,
         "kv_cache_gb_per_layer": round(metrics.kv_cache_memory_gb(wl.B, wl.N, wl.Hkv * wl.d, 1), 3),
     }
+    if wl.page_size:
+        out["config"].update({"page_size": wl.page_size, "top_pages": wl.top_pages, "n_local": wl.n_local})
     print(json.dumps(out), flush=True)
 
 

@@ -63,7 +63,9 @@ struct PageSelParams {
   TopkParams t;            // scores, err, indexer (certified), shapes; t.K = top_pages;
                            // t.idx / t.is: page list [B, G, Nq, width]; t.count
   int lgP, n_local, width; // log2 page size, mandatory recent pages, list width
+  void* ws;                // workspace (page keys of every row, when rows are few)
 };
+size_t page_select_ws_bytes(const PageSelParams& p);
 hipError_t launch_page_select(const PageSelParams& p, hipStream_t st);
 
 // ---------------------------------------------------------------- block select

@@ -12,7 +12,9 @@
 //  1. page keys: the row's scores are read once, coalesced (four tokens per
 //     lane when the row is 16-byte aligned), and folded per page by lane
 //     shuffles; pages wider than a wave's sweep are merged by LDS atomics.
-//     Keys stay in LDS (up to kMaxPages candidates).
+//     Keys stay in LDS (up to kMaxPages candidates). With few rows (decode)
+//     this pass is spread over many workgroups per row instead (page_keys
+//     kernel, kPkChunk tokens each), which leave the keys in the workspace.
 //  2. radix select of the top_pages-th largest page key t.
 //  3. uncertified: pages above t are in, pages equal to t go in by index.
 //     Certified (scores within eps of the exact keys): pages whose computed key
@@ -32,6 +34,9 @@ namespace sp {
 
 constexpr int kPsThreads = 512;
 constexpr int kPsBandCap = 2048;
+constexpr int kPkThreads = 256;
+constexpr int kPkChunk = 8192;      // tokens per page-key workgroup (a multiple of every page size)
+constexpr int kPsFewRows = 512;     // up to this many rows the page keys get their own kernel
 
 struct PsSmem {
   uint32_t pk[kMaxPages];        // order keys of the candidate pages
@@ -90,7 +95,32 @@ SP_DEV void page_keys(const float* s, int ntok, int lgP, int npc, uint32_t* pk) 
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kPsThreads) void page_select_kernel(PageSelParams q) {
+// Keys of the candidate pages of one row in the token range of one
+// workgroup, written to pkg[row * npmax + page].
+__global__ __launch_bounds__(kPkThreads) void page_keys_kernel(PageSelParams q, uint32_t* pkg, int npmax) {
+  __shared__ uint32_t pk[kPkChunk];
+  const TopkParams& p = q.t;
+  const int row = blockIdx.y;
+  const int r = row % p.Nq, g = (row / p.Nq) % p.G, b = row / (p.Nq * p.G);
+  const int L = min(p.ctx_len ? p.ctx_len[b] : p.ctx, p.ctx);
+  const int pos = L - p.Nq + r;
+  if (pos < 0) return;
+  const int npc = max(0, (pos >> q.lgP) + 1 - q.n_local);
+  if (npc <= p.K || p.K == 0) return;              // the selection kernel needs no keys for this row
+  const int ntok = min(npc << q.lgP, pos + 1);
+  const int t0 = blockIdx.x * kPkChunk;
+  if (t0 >= ntok) return;
+  const int t1 = min(t0 + kPkChunk, ntok);
+  const int n = (t1 - t0 + (1 << q.lgP) - 1) >> q.lgP;
+  const float* s = p.scores + b * p.ss[0] + g * p.ss[1] + r * p.ss[2];
+  page_keys<kPkThreads>(s + t0, t1 - t0, q.lgP, n, pk);
+  uint32_t* dst = pkg + (int64_t)row * npmax + (t0 >> q.lgP);
+  for (int i = threadIdx.x; i < n; i += kPkThreads) dst[i] = pk[i];
+}
+
+// pkg: page keys from page_keys_kernel (row stride npmax), or null to
+// compute them here.
+__global__ __launch_bounds__(kPsThreads) void page_select_kernel(PageSelParams q, const uint32_t* pkg, int npmax) {
   constexpr int T = kPsThreads;
   __shared__ PsSmem sm;
   const TopkParams& p = q.t;
@@ -122,7 +152,13 @@ __global__ __launch_bounds__(kPsThreads) void page_select_kernel(PageSelParams q
   if (K == 0) return;
 
   const float* s = p.scores + b * p.ss[0] + g * p.ss[1] + r * p.ss[2];
-  page_keys<T>(s, min(npc << lgP, pos + 1), lgP, npc, sm.pk);
+  if (pkg) {
+    const uint32_t* src = pkg + (int64_t)row * npmax;
+    for (int i = tid; i < npc; i += T) sm.pk[i] = src[i];
+    __syncthreads();
+  } else {
+    page_keys<T>(s, min(npc << lgP, pos + 1), lgP, npc, sm.pk);
+  }
 
   const uint32_t R = (uint32_t)K;
   uint32_t t, above;
@@ -138,34 +174,46 @@ __global__ __launch_bounds__(kPsThreads) void page_select_kernel(PageSelParams q
     ir = indexer_row(p.ix, b, g, r);
   }
 
-  // ordered pass 1: pages above the band, the band cached in page order
-  if (tid == 0) { sm.run[0] = 0; sm.run[1] = 0; }
-  __syncthreads();
-  for (int base = 0; base < npc; base += T) {
-    const int i = base + tid;
-    const uint32_t k = i < npc ? sm.pk[i] : 0u;
-    const bool in = i < npc && k > khi;
-    const bool bd = i < npc && k >= klo && k <= khi;
-    uint32_t nin, nbd;
-    const uint32_t bpos = block_prefix<T>(bd, sm.sc, nbd);
-    block_prefix<T>(in, sm.sc, nin);
-    const uint32_t bslot = sm.run[1] + bpos;
-    if (bd && bslot < (uint32_t)kPsBandCap) {
-      sm.band_j[bslot] = (uint32_t)i;
-      sm.band_k[bslot] = k;
-    }
-    __syncthreads();
-    if (tid == 0) { sm.run[0] += nin; sm.run[1] += nbd; }
-    __syncthreads();
-  }
-  const uint32_t n_in = sm.run[0], n_band = sm.run[1];
-  const uint32_t R2 = R - n_in;                    // >= 1: at most R-1 keys exceed t
-  const bool cached = n_band <= (uint32_t)kPsBandCap;
   const int P = 1 << lgP;
-
   // lowest computed score a token may have and still hold the page's exact key
   auto tok_floor = [&](uint32_t ck) { return nextafterf(order_key_f32(ck) - E, -INFINITY); };
-  // exact page key by one thread (the uncached fallback)
+
+  // word pass: bits of the pages above the band (hist[w]) and in it (hist[512 + w]),
+  // 64 pages per wave step
+  static_assert(kMaxPages <= 32 * T && kMaxPages / 32 <= 512, "one bitmap word per thread");
+  const int nwords = (npc + 31) >> 5;
+  for (int c = (tid >> 6); 64 * c < npc; c += T / 64) {
+    const int i = 64 * c + lane;
+    const uint32_t k = i < npc ? sm.pk[i] : 0u;
+    const uint64_t min_ = ballot(i < npc && k > khi);
+    const uint64_t mbd = ballot(i < npc && k >= klo && k <= khi);
+    if (lane == 0) {
+      sm.hist[2 * c] = (uint32_t)min_;
+      sm.hist[512 + 2 * c] = (uint32_t)mbd;
+    } else if (lane == 1 && 2 * c + 1 < nwords) {
+      sm.hist[2 * c + 1] = (uint32_t)(min_ >> 32);
+      sm.hist[512 + 2 * c + 1] = (uint32_t)(mbd >> 32);
+    }
+  }
+  __syncthreads();
+  const uint32_t win = tid < nwords ? sm.hist[tid] : 0u;
+  const uint32_t wbd = tid < nwords ? sm.hist[512 + tid] : 0u;
+  uint32_t tot;
+  const uint32_t pre = block_scan_sum<T>(((uint32_t)__popc(wbd) << 16) | (uint32_t)__popc(win), sm.sc, tot);
+  const uint32_t n_in = tot & 0xFFFFu, n_band = tot >> 16;
+  const uint32_t R2 = R - n_in;                    // >= 1: at most R-1 keys exceed t
+  const bool cached = n_band <= (uint32_t)kPsBandCap;
+  if (cached) {                                    // the band in page order
+    uint32_t slot = pre >> 16;
+    for (uint32_t m = wbd; m; m &= m - 1, ++slot) {
+      const int i = 32 * tid + __ffs(m) - 1;
+      sm.band_j[slot] = (uint32_t)i;
+      sm.band_k[slot] = sm.pk[i];
+    }
+  }
+  __syncthreads();
+
+  // exact page key by one thread (the fallback beyond the band cache)
   auto exkey_thread = [&](int pg, uint32_t ck) -> uint32_t {
     if (!p.certified) return ck;
     const float lo = tok_floor(ck);
@@ -176,31 +224,10 @@ __global__ __launch_bounds__(kPsThreads) void page_select_kernel(PageSelParams q
     return bk;
   };
 
-  if (cached && p.certified) {                     // one wave per band page
-    for (uint32_t e = tid >> 6; e < n_band; e += T / 64) {
-      const int pg = (int)sm.band_j[e];
-      const float lo = tok_floor(sm.band_k[e]);
-      const int j0 = pg << lgP, j1 = min(j0 + P, pos + 1);
-      uint32_t bk = 0u;
-      for (int jb = j0; jb < j1; jb += 64) {
-        const int j = jb + lane;
-        uint64_t m = ballot(j < j1 && s[j] >= lo);
-        while (m) {
-          const int bit = __builtin_ctzll(m);
-          m &= m - 1;
-          bk = max(bk, f32_order_key(wave_exact_key(ir, jb + bit)));
-        }
-      }
-      if (lane == 0) sm.band_k[e] = bk;
-    }
-    __syncthreads();
-  }
-
-  uint32_t t2, above2;
-  if (cached) {
-    radix_select<T>((int)n_band, R2, [&](int i, uint32_t& k) { k = sm.band_k[i]; return true; }, sm.hist, sm.sc,
-                    t2, above2);
-  } else {
+  if (!cached) {
+    // rare (a band wider than the cache): exact keys recomputed by each thread
+    // in an ordered pass over all pages
+    uint32_t t2, above2;
     radix_select<T>(npc, R2,
                     [&](int i, uint32_t& k) {
                       const uint32_t ck = sm.pk[i];
@@ -209,43 +236,138 @@ __global__ __launch_bounds__(kPsThreads) void page_select_kernel(PageSelParams q
                       return true;
                     },
                     sm.hist, sm.sc, t2, above2);
+    const uint32_t need_eq = R2 - above2;
+    if (tid == 0) { sm.run[0] = 0; sm.run[2] = 0; }
+    __syncthreads();
+    for (int base = 0; base < npc; base += T) {
+      const int i = base + tid;
+      bool sel = false, eq = false;
+      if (i < npc) {
+        const uint32_t ck = sm.pk[i];
+        sel = ck > khi;
+        if (ck >= klo && ck <= khi) {
+          const uint32_t ex = exkey_thread(i, ck);
+          eq = ex == t2;
+          sel = ex > t2;
+        }
+      }
+      uint32_t neq;
+      const uint32_t erank = sm.run[2] + block_prefix<T>(eq, sm.sc, neq);
+      if (eq && erank < need_eq) sel = true;
+      uint32_t nsel;
+      const uint32_t opos = sm.run[0] + block_prefix<T>(sel, sm.sc, nsel);
+      if (sel && opos < R) out[opos] = i;
+      __syncthreads();
+      if (tid == 0) { sm.run[0] += nsel; sm.run[2] += neq; }
+      __syncthreads();
+    }
+    return;
   }
+
+  if (p.certified) {
+    // (band page, token) pairs whose token may hold the page's exact key,
+    // listed in hist (tokens, then band slots); each pair is rescored by a
+    // quarter-wave and folded into its page by an LDS maximum
+    constexpr int kQCap = 2048;
+    if (tid == 0) sm.run[2] = 0;
+    __syncthreads();
+    for (uint32_t e = tid >> 6; e < n_band; e += T / 64) {
+      const float lo = tok_floor(sm.band_k[e]);
+      const int j0 = (int)sm.band_j[e] << lgP, j1 = min(j0 + P, pos + 1);
+      for (int jb = j0; jb < j1; jb += 64) {
+        const int j = jb + lane;
+        const uint64_t m = ballot(j < j1 && s[j] >= lo);
+        uint32_t base = 0u;
+        if (lane == 0) base = atomicAdd(&sm.run[2], (uint32_t)__popcll(m));
+        base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+        if ((m >> lane) & 1u) {
+          const uint32_t slot = base + lanes_below(m);
+          if (slot < (uint32_t)kQCap) {
+            sm.hist[slot] = (uint32_t)j;
+            sm.hist[kQCap + slot] = e;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t nq = sm.run[2];
+    if (nq <= (uint32_t)kQCap) {
+      for (uint32_t e = tid; e < n_band; e += T) sm.band_k[e] = 0u;
+      __syncthreads();
+      for (uint32_t x = tid >> 4; x < nq; x += T / 16) {
+        const float key = group_exact_key<16, 4, true>(ir, sm.hist[x]);
+        if ((lane & 15) == 0) atomicMax(&sm.band_k[sm.hist[kQCap + x]], f32_order_key(key));
+      }
+    } else {                                       // many near-tied tokens: one wave per band page
+      for (uint32_t e = tid >> 6; e < n_band; e += T / 64) {
+        const float lo = tok_floor(sm.band_k[e]);
+        const int j0 = (int)sm.band_j[e] << lgP, j1 = min(j0 + P, pos + 1);
+        uint32_t bk = 0u;
+        for (int jb = j0; jb < j1; jb += 64) {
+          const int j = jb + lane;
+          uint64_t m = ballot(j < j1 && s[j] >= lo);
+          while (m) {
+            const int bit = __builtin_ctzll(m);
+            m &= m - 1;
+            bk = max(bk, f32_order_key(wave_exact_key(ir, jb + bit)));
+          }
+        }
+        if (lane == 0) sm.band_k[e] = bk;
+      }
+    }
+    __syncthreads();
+  }
+
+  uint32_t t2, above2;
+  radix_select<T>((int)n_band, R2, [&](int i, uint32_t& k) { k = sm.band_k[i]; return true; }, sm.hist, sm.sc,
+                  t2, above2);
   const uint32_t need_eq = R2 - above2;
 
-  // ordered pass 2: the selected candidates in ascending page order
-  if (tid == 0) { sm.run[0] = 0; sm.run[1] = 0; sm.run[2] = 0; }
+  // selection bitmap (in pk, whose keys are no longer needed): the pages above
+  // the band, then the band's winners in page order
+  sm.pk[tid] = win;
   __syncthreads();
-  for (int base = 0; base < npc; base += T) {
-    const int i = base + tid;
-    bool sel = false, bd = false, eq = false;
-    uint32_t ck = 0u;
-    if (i < npc) {
-      ck = sm.pk[i];
-      sel = ck > khi;
-      bd = ck >= klo && ck <= khi;
-    }
-    uint32_t nbd;
-    const uint32_t brank = sm.run[1] + block_prefix<T>(bd, sm.sc, nbd);
-    if (bd) {
-      const uint32_t ex = cached ? sm.band_k[brank] : exkey_thread(i, ck);
-      eq = ex == t2;
-      if (ex > t2) sel = true;
-    }
+  uint32_t run_eq = 0;
+  for (uint32_t base = 0; base < n_band; base += T) {
+    const uint32_t e = base + tid;
+    const uint32_t ex = e < n_band ? sm.band_k[e] : 0u;
+    const bool eq = e < n_band && ex == t2;
     uint32_t neq;
-    const uint32_t erank = sm.run[2] + block_prefix<T>(eq, sm.sc, neq);
-    if (eq && erank < need_eq) sel = true;
-    uint32_t nsel;
-    const uint32_t opos = sm.run[0] + block_prefix<T>(sel, sm.sc, nsel);
-    if (sel && opos < R) out[opos] = i;
-    __syncthreads();
-    if (tid == 0) { sm.run[0] += nsel; sm.run[1] += nbd; sm.run[2] += neq; }
-    __syncthreads();
+    const uint32_t er = run_eq + block_prefix<T>(eq, sm.sc, neq);
+    run_eq += neq;
+    if (e < n_band && (ex > t2 || (eq && er < need_eq))) {
+      const uint32_t i = sm.band_j[e];
+      atomicOr(&sm.pk[i >> 5], 1u << (i & 31));
+    }
   }
+  __syncthreads();
+  const uint32_t wsel = tid < nwords ? sm.pk[tid] : 0u;
+  uint32_t nsel;
+  uint32_t opos = block_scan_sum<T>((uint32_t)__popc(wsel), sm.sc, nsel);
+  for (uint32_t m = wsel; m; m &= m - 1, ++opos)
+    if (opos < R) out[opos] = 32 * tid + __ffs(m) - 1;
+}
+
+static int page_rows(const PageSelParams& p) { return p.t.B * p.t.G * p.t.Nq; }
+static int page_cap(const PageSelParams& p) { return (p.t.ctx + (1 << p.lgP) - 1) >> p.lgP; }
+
+size_t page_select_ws_bytes(const PageSelParams& p) {
+  const int rows = page_rows(p);
+  return rows <= kPsFewRows ? (size_t)rows * page_cap(p) * sizeof(uint32_t) : 0;
 }
 
 hipError_t launch_page_select(const PageSelParams& p, hipStream_t st) {
-  const int rows = p.t.B * p.t.G * p.t.Nq;
-  hipLaunchKernelGGL(page_select_kernel, dim3(rows), dim3(kPsThreads), 0, st, p);
+  const int rows = page_rows(p);
+  uint32_t* pkg = nullptr;
+  const int npmax = page_cap(p);
+  if (page_select_ws_bytes(p)) {
+    pkg = (uint32_t*)p.ws;
+    const int chunks = (p.t.ctx + kPkChunk - 1) / kPkChunk;
+    hipLaunchKernelGGL(page_keys_kernel, dim3(chunks, rows), dim3(kPkThreads), 0, st, p, pkg, npmax);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(page_select_kernel, dim3(rows), dim3(kPsThreads), 0, st, p, (const uint32_t*)pkg, npmax);
   return hipGetLastError();
 }
 

@@ -339,7 +339,7 @@ SPATTN_API size_t spattn_page_select_workspace(const spattn_tensor* scores, int3
   sp::PageSelParams q;
   if (page_select_setup(scores, nullptr, nullptr, nullptr, page_size, top_pages, n_local, 0u, nullptr, q))
     return (size_t)-1;
-  return 0;
+  return sp::page_select_ws_bytes(q);
 }
 
 SPATTN_API int spattn_page_select(const spattn_tensor* scores, const float* err, const spattn_indexer* ix,
@@ -348,12 +348,13 @@ SPATTN_API int spattn_page_select(const spattn_tensor* scores, const float* err,
                                   size_t ws_bytes, void* stream) {
   sp::PageSelParams q;
   int rc;
-  (void)ws;
-  (void)ws_bytes;
   if (!pg_idx_out) return fail(SPATTN_ERR_INVALID_ARG, "pg_idx_out: null tensor");
   if ((rc = page_select_setup(scores, err, ix, ctx_len, page_size, top_pages, n_local, flags, pg_idx_out, q)))
     return rc;
   q.t.count = pg_count_out;
+  const size_t need = sp::page_select_ws_bytes(q);
+  if (ws_bytes < need || (need && !ws)) return fail(SPATTN_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  q.ws = ws;
   if ((rc = device_ok())) return rc;
   return launched(sp::launch_page_select(q, (hipStream_t)stream));
 }

@@ -27,7 +27,8 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 STAGES = {
     "index_topk_fused": ["fz_pilot_score", "fz_pilot_select", "true>(sp::IndexerParams)", "fz_final"],
     "index_scores": ["false>(sp::IndexerParams)", "idx_generic", "idx_err"],
-    "topk": ["topk_row", "mt_zero", "mt_hist", "mt_collect", "mt_finalize"],
+    "topk": ["topk_row", "topk_redo", "mt_zero", "mt_hist", "mt_collect", "mt_finalize"],
+    "page_select": ["page_select_kernel"],
     "block_select": ["pool_kernel", "block_select_kernel"],
     "attention": ["attn_index_mfma", "attn_combine", "attn_tile", "attn_generic", "bc_count", "bc_scan", "bc_table",
                   "bc_scatter", "bc_attn", "bc_combine"],

@@ -204,7 +204,9 @@ SPATTN_API int spattn_topk(const spattn_tensor* scores, const float* err,
  *      the page list equals exhaustive selection on exact keys.
  *  Limits: P a power of two in 1..4096; ceil(ctx / P) <= 16384;
  *  top_pages, n_local >= 0 with top_pages + n_local >= 1; top_pages <= 16384.
- *  No workspace is needed (the query returns 0).
+ *  Workspace: with at most 512 rows (B * G * Nq) the page keys of every row
+ *  are staged there, rows * ceil(ctx / P) * 4 bytes; otherwise none (the
+ *  query returns 0).
  * ---------------------------------------------------------------------- */
 SPATTN_API size_t spattn_page_select_workspace(const spattn_tensor* scores, int32_t page_size,
                                                int32_t top_pages, int32_t n_local);

@@ -141,13 +141,20 @@ def test_page_select_validation():
     sc = torch.zeros(1, 2, 4, 256)
     io = torch.zeros(1, 2, 4, 5, dtype=torch.int32)
 
-    def call(P, top, loc, flags=0, idx=io, scores=sc):
+    ws = torch.zeros(1 << 20, dtype=torch.uint8)
+
+    def call(P, top, loc, flags=0, idx=io, scores=sc, ws_bytes=1 << 20):
         s, o = S.tensor(scores), S.tensor(idx)
         return S.LIB.spattn_page_select(ctypes.byref(s), None, None, None, P, top, loc, flags, ctypes.byref(o),
-                                        None, None, 0, None)
+                                        None, ws.data_ptr(), ws_bytes, None)
 
-    assert S.LIB.spattn_page_select_workspace(ctypes.byref(S.tensor(sc)), 64, 3, 2) == 0
+    # few rows: the page keys of every row are staged in the workspace
+    need = S.LIB.spattn_page_select_workspace(ctypes.byref(S.tensor(sc)), 64, 3, 2)
+    assert need == 8 * 4 * 4
     assert call(64, 3, 2) == 4                  # valid: reaches the device check
+    assert call(64, 3, 2, ws_bytes=need - 1) == 3
+    many = torch.zeros(1, 1, 600, 700)          # many rows: one pass per row, no workspace
+    assert S.LIB.spattn_page_select_workspace(ctypes.byref(S.tensor(many)), 64, 3, 2) == 0
     assert call(16, 5, 0) == 4
     assert call(48, 3, 2) == 1                  # page size not a power of two
     assert call(8192, 3, 2) == 1                # page size above 4096
