@@ -76,6 +76,8 @@ def algorithmic(wl, inp, hp, fused):
             width = wl.top_pages + wl.n_local
             out["page_select"] = {"bytes": score_bytes + wl.B * wl.G_sel * wl.Nq * width * 4,
                                   "rows": wl.B * wl.G_sel * wl.Nq}
+            out["index_page_fused"] = {"bytes": keys_read + wl.B * wl.G_sel * wl.Nq * width * 4, "flops": flops_idx,
+                                       "rows": wl.B * wl.G_sel * wl.Nq, "bound": "hbm" if wl.Nq == 1 else "mfma"}
             pg = hp.idx.cpu().numpy().astype(np.int64)                      # [B, G, Nq, width]
             pos = np.stack([L - wl.Nq + np.arange(wl.Nq) for L in lens])[:, None, :, None]
             tok = np.clip(np.minimum(pg * P + P, pos + 1) - pg * P, 0, None) * (pg >= 0)
@@ -169,7 +171,9 @@ def main():
 
     stream = torch.cuda.current_stream()
     stages = []
-    if wl.H_I and fused:
+    if wl.H_I and fused and wl.kind == "dsa_pages":
+        stages = [("index_page_fused", lambda hp: hp.page_select_fused()), ("attention", lambda hp: hp.attention())]
+    elif wl.H_I and fused:
         stages = [("index_topk_fused", lambda hp: hp.topk_fused()), ("attention", lambda hp: hp.attention())]
     elif wl.H_I and wl.kind == "dsa_pages":
         stages = [("index_scores", lambda hp: hp.index_scores()), ("page_select", lambda hp: hp.page_select()),
@@ -296,8 +300,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if wl.dtype == "f32" else "bf16",
         "data": "synthetic",
-        "path": ("indexer scores, certified page selection, attention over a paged KV cache"
-                 if wl.kind == "dsa_pages" else
+        "path": (("fused indexer+page selection" if fused else "indexer scores, certified page selection")
+                 + ", attention over a paged KV cache" if wl.kind == "dsa_pages" else
                  "fused indexer+top-K" if fused else "separate indexer and top-K calls"),
         "config": {"workload": wl.name, "B": wl.B, "ctx_capacity": wl.N, "Nq": wl.Nq, "Hq": wl.Hq,
                    "Hkv": wl.Hkv, "d": wl.d, "H_I": wl.H_I, "d_I": wl.d_I, "topk": wl.topk,

@@ -477,6 +477,51 @@ SP_DEV float group_exact_key(const IndexerRow& r, int64_t j, const float* qs = n
 }
 SP_DEV float wave_exact_key(const IndexerRow& r, int64_t j) { return group_exact_key<64>(r, j); }
 
+// Rigorous bound on |score~ - key| for a row scored by the indexer kernels
+// from its inputs: CO = sum over the group's heads and dims of |w_h q_hc|
+// (summed in float32 in any order), KM = max |k| over the row's keys.
+SP_DEV float eps_of(const IndexerParams& x, float CO, float KM) {
+  const double u = 1.0 / 8388608.0;
+  auto gam = [&](double n) { return n * u / (1.0 - n * u); };
+  const double C = 1.25 * (gam(x.d_I + 2) + gam(x.hpg + 2) * (1.0 + gam(x.d_I + 2)) + u);
+  // CO was summed in float32: inflate by its own rounding bound
+  const double e = C * (double)CO * (1.0 + gam(x.hpg * x.d_I + 2)) * (double)KM * (1.0 + 1e-6) + 1e-30;
+  return (float)e * (1.0f + 1e-6f);
+}
+
+// The same bound for one row by a whole workgroup: KM from the indexer's
+// per-chunk maxima x.kmax[(b * G_k + kg) * nchunk + c] over the chunks that
+// hold keys 0..L-1, CO from the row's query and weights. Every thread calls
+// it; red holds >= 32 floats; two barriers.
+SP_DEV float row_eps(const IndexerParams& x, const IndexerRow& ir, int b, int kg, int L, float* red) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nch = min(x.nchunk, (L + x.chunk - 1) / x.chunk);
+  const float* km_row = x.kmax + ((int64_t)b * x.G_k + kg) * x.nchunk;
+  float km = 0.f;
+  for (int i = tid; i < nch; i += blockDim.x) km = fmaxf(km, km_row[i]);
+  float coef = 0.f;
+  for (int e = tid; e < ir.H * ir.d; e += blockDim.x) {
+    const int h = e / ir.d, cc = e % ir.d;
+    const float qv = fabsf((float)load_f64(ir.q, ir.qt, h * ir.qh_stride + cc));
+    const float wv = ir.relu ? fabsf(ir.w[h * ir.w_stride]) : 1.f;
+    coef = fmaf(wv, qv, coef);
+  }
+  km = wave_max(km);
+  coef = wave_sum(coef);
+  if (lane == 0) {
+    red[wid] = km;
+    red[16 + wid] = coef;
+  }
+  __syncthreads();
+  float KM = 0.f, CO = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+    KM = fmaxf(KM, red[w]);
+    CO += red[16 + w];
+  }
+  __syncthreads();
+  return eps_of(x, CO, KM);
+}
+
 // Block key: float32 nearest to (1/bs) * sum_{t<bs} q . k[t]; bs a power of two.
 SP_DEV float exact_block_key(const void* q, int qt, const void* k, int kt, int64_t k_stride,
                              int bs, int log2bs, int d) {

@@ -7,6 +7,10 @@
 //    turns 32 keys into a 32x32x16 bf16 MFMA B operand (fp8 upconverted to
 //    bf16 exactly) against the resident query slots, and reduces the heads
 //    of a group in-lane in the epilogue.
+//    With page keys requested (pages of 32..512 keys), the epilogue also
+//    folds each tile's scores per selection row (DPP rotations inside 16-lane
+//    rows and a row swap give the maximum over the half-wave's 32 keys) and
+//    merges them per page in LDS: the largest score of every (row, page).
 //  * idx_generic: any supported dtype/shape, one key per thread, FMA chain.
 // Both record, per 512/256-key chunk, the largest |k| element, from which
 // idx_err derives each row's rigorous bound |score - key|.
@@ -27,8 +31,11 @@ SP_DEV float load_val(const void* p, int dt, int64_t i) {
 }
 
 // ----------------------------------------------------------------------------
-template <int KT, int NMB, int HPG, bool RELU, bool FILTER>
+// MODE: 0 scores, 1 threshold filter (candidate lists), 2 scores and page keys
+template <int KT, int NMB, int HPG, bool RELU, int MODE>
 __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
+  constexpr bool FILTER = MODE == 1;
+  constexpr bool PM = MODE == 2;
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
@@ -46,6 +53,9 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
   __shared__ uint32_t lcount[128];
   __shared__ float wsl[128];
   __shared__ float tsl[128];          // filter threshold of each slot's selection row
+  __shared__ uint32_t pml[PM ? 128 * 16 : 1];   // page keys: [slot][page of the chunk]
+  if (PM)
+    for (int i = threadIdx.x; i < 128 * 16; i += 256) pml[i] = 0u;
   for (int i = threadIdx.x; i < 128; i += 256) {
     if (FILTER) lcount[i] = 0;
     float wv = 0.f, tv = INFINITY;
@@ -180,6 +190,24 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
           const int r = m0 >> hshift, g = (m0 & (p.H_I - 1)) / HPG;
           if (m0 < M && j <= L - p.Nq + r) p.scores[b * p.ss[0] + g * p.ss[1] + r * p.ss[2] + j] = scv[gi];
         }
+        if constexpr (PM) {
+          // page keys: maximum over the half-wave's 32 keys of each slot row,
+          // merged into the tile's page
+          const int pl = ((wid + 4 * i) * 32) >> p.pk_lgP;
+#pragma unroll
+          for (int gi = 0; gi < G4; ++gi) {
+            const int v0 = gi * HPG;
+            const int m0 = mbase + 32 * mb + 8 * (v0 >> 2) + 4 * half + (v0 & 3);
+            uint32_t kk = (m0 < M && j <= L - p.Nq + (m0 >> hshift)) ? f32_order_key(scv[gi]) : 0u;
+            kk = max(kk, (uint32_t)__builtin_amdgcn_update_dpp((int)kk, (int)kk, 0x128, 0xf, 0xf, false));
+            kk = max(kk, (uint32_t)__builtin_amdgcn_update_dpp((int)kk, (int)kk, 0x124, 0xf, 0xf, false));
+            kk = max(kk, (uint32_t)__builtin_amdgcn_update_dpp((int)kk, (int)kk, 0x122, 0xf, 0xf, false));
+            kk = max(kk, (uint32_t)__builtin_amdgcn_update_dpp((int)kk, (int)kk, 0x121, 0xf, 0xf, false));
+            const auto sw = __builtin_amdgcn_permlane16_swap(kk, kk, false, false);
+            kk = max((uint32_t)sw[0], (uint32_t)sw[1]);
+            if (col == 0 && kk) atomicMax(&pml[((m0 - mbase) & 127) * 16 + pl], kk);
+          }
+        }
       } else if constexpr (HOIST) {
         // survivors of all head groups at once: leader lane 2 e + hf reserves
         // the slots of (group e, half hf) with one LDS atomic for all leaders
@@ -252,6 +280,20 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
   if (threadIdx.x == 0) {
     const uint32_t m4 = max(max(red[0], red[1]), max(red[2], red[3]));
     p.kmax[(int64_t)b * p.nchunk + blockIdx.x] = bf16_to_f32(m4);
+  }
+  if (PM) {
+    // one key per (selection row, page of the chunk), from the row's first slot
+    const int npl = kMfmaChunk >> p.pk_lgP;
+    for (int e = threadIdx.x; e < 128 * npl; e += 256) {
+      const int sl = e / npl, pl = e - sl * npl;
+      const int m = mbase + sl;
+      const int h = m & (p.H_I - 1);
+      if (m >= M || h % HPG) continue;
+      const int r = m >> hshift, g = h / HPG;
+      const int64_t row = ((int64_t)b * p.G_sel + g) * p.Nq + r;
+      const int page = (j0 >> p.pk_lgP) + pl;
+      if (page < p.pk_stride) p.pkeys[row * p.pk_stride + page] = pml[sl * 16 + pl];
+    }
   }
   if (FILTER) {
     const int nrows = p.G_sel * p.Nq;
@@ -347,26 +389,26 @@ size_t indexer_ws_bytes(int B, int G_k, int ctx) {
   return (size_t)B * G_k * nchunk * sizeof(float);
 }
 
-template <int KT, int NMB, int HPG, bool RELU, bool FILTER>
+template <int KT, int NMB, int HPG, bool RELU, int MODE>
 static void launch_mfma(const IndexerParams& p, hipStream_t st) {
   dim3 grid((p.ctx + kMfmaChunk - 1) / kMfmaChunk, p.B, (p.Nq * p.H_I + 127) / 128);
-  hipLaunchKernelGGL((idx_mfma64_kernel<KT, NMB, HPG, RELU, FILTER>), grid, dim3(256), 0, st, p);
+  hipLaunchKernelGGL((idx_mfma64_kernel<KT, NMB, HPG, RELU, MODE>), grid, dim3(256), 0, st, p);
 }
 
-template <int KT, int NMB, bool FILTER>
+template <int KT, int NMB, int MODE>
 static void dispatch_hpg(const IndexerParams& p, hipStream_t st) {
-  if (!p.relu) return launch_mfma<KT, NMB, 1, false, FILTER>(p, st);
-  if (p.hpg == 1) return launch_mfma<KT, NMB, 1, true, FILTER>(p, st);
-  if (p.hpg == 2) return launch_mfma<KT, NMB, 2, true, FILTER>(p, st);
-  return launch_mfma<KT, NMB, 4, true, FILTER>(p, st);
+  if (!p.relu) return launch_mfma<KT, NMB, 1, false, MODE>(p, st);
+  if (p.hpg == 1) return launch_mfma<KT, NMB, 1, true, MODE>(p, st);
+  if (p.hpg == 2) return launch_mfma<KT, NMB, 2, true, MODE>(p, st);
+  return launch_mfma<KT, NMB, 4, true, MODE>(p, st);
 }
 
-template <int KT, bool FILTER>
+template <int KT, int MODE>
 static void dispatch_nmb(const IndexerParams& p, hipStream_t st) {
   const int M = p.Nq * p.H_I;
-  if (M <= 32) return dispatch_hpg<KT, 1, FILTER>(p, st);
-  if (M <= 64) return dispatch_hpg<KT, 2, FILTER>(p, st);
-  return dispatch_hpg<KT, 4, FILTER>(p, st);
+  if (M <= 32) return dispatch_hpg<KT, 1, MODE>(p, st);
+  if (M <= 64) return dispatch_hpg<KT, 2, MODE>(p, st);
+  return dispatch_hpg<KT, 4, MODE>(p, st);
 }
 
 // MFMA path: d_I = 64, bf16 queries, bf16/fp8 keys shared by every group,
@@ -378,13 +420,23 @@ static bool mfma_ok(const IndexerParams& p) {
          (int64_t)p.Nq * p.H_I <= (int64_t)128 * 65535;
 }
 
+bool index_pagekeys_ok(const IndexerParams& p, int lgP) { return mfma_ok(p) && lgP >= 5 && lgP <= 9; }
+
+int index_chunk(const IndexerParams& p) { return mfma_ok(p) ? kMfmaChunk : kGenChunk; }
+
 hipError_t launch_index_scores(const IndexerParams& p0, hipStream_t st) {
   IndexerParams p = p0;
   if (mfma_ok(p)) {
     p.chunk = kMfmaChunk;
     p.nchunk = (p.ctx + kMfmaChunk - 1) / kMfmaChunk;
-    if (p.k.dt == DT_FP8) dispatch_nmb<DT_FP8, false>(p, st);
-    else dispatch_nmb<DT_BF16, false>(p, st);
+    const bool pm = p.pkeys != nullptr;
+    if (p.k.dt == DT_FP8) {
+      if (pm) dispatch_nmb<DT_FP8, 2>(p, st);
+      else dispatch_nmb<DT_FP8, 0>(p, st);
+    } else {
+      if (pm) dispatch_nmb<DT_BF16, 2>(p, st);
+      else dispatch_nmb<DT_BF16, 0>(p, st);
+    }
   } else {
     p.chunk = kGenChunk;
     p.nchunk = (p.ctx + kGenChunk - 1) / kGenChunk;
@@ -404,8 +456,8 @@ hipError_t launch_index_filter(const IndexerParams& p0, hipStream_t st) {
   IndexerParams p = p0;
   p.chunk = kMfmaChunk;
   p.nchunk = (p.ctx + kMfmaChunk - 1) / kMfmaChunk;
-  if (p.k.dt == DT_FP8) dispatch_nmb<DT_FP8, true>(p, st);
-  else dispatch_nmb<DT_BF16, true>(p, st);
+  if (p.k.dt == DT_FP8) dispatch_nmb<DT_FP8, 1>(p, st);
+  else dispatch_nmb<DT_BF16, 1>(p, st);
   return hipGetLastError();
 }
 

@@ -31,7 +31,14 @@ struct IndexerParams {
   uint32_t* cand;          // [B][nchunk][G_sel * Nq][cap][2]: (order key, key position), 8-byte aligned
   uint32_t* cand_n;        // [B][nchunk][G_sel * Nq] number found (may exceed cap)
   int cap;
+  // page keys (MFMA path only): the largest score of each (selection row, page)
+  // as an order key, [B * G_sel * Nq][pk_stride], pages of 1 << pk_lgP keys
+  uint32_t* pkeys;
+  int64_t pk_stride;
+  int pk_lgP;
 };
+bool index_pagekeys_ok(const IndexerParams& p, int lgP);   // pages of 32..512 keys
+int index_chunk(const IndexerParams& p);   // keys per chunk of the chunk maxima (kmax)
 bool index_filter_ok(const IndexerParams& p);
 hipError_t launch_index_filter(const IndexerParams& p, hipStream_t st);   // chunk = 512
 size_t indexer_ws_bytes(int B, int G_k, int ctx);
@@ -63,7 +70,8 @@ struct PageSelParams {
   TopkParams t;            // scores, err, indexer (certified), shapes; t.K = top_pages;
                            // t.idx / t.is: page list [B, G, Nq, width]; t.count
   int lgP, n_local, width; // log2 page size, mandatory recent pages, list width
-  void* ws;                // workspace (page keys of every row, when rows are few)
+  void* ws;                // workspace: fused scores and error bounds, staged page keys
+  bool fused;              // scores computed here from t.ix (no score matrix given)
 };
 size_t page_select_ws_bytes(const PageSelParams& p);
 hipError_t launch_page_select(const PageSelParams& p, hipStream_t st);

@@ -14,7 +14,8 @@
 //     shuffles; pages wider than a wave's sweep are merged by LDS atomics.
 //     Keys stay in LDS (up to kMaxPages candidates). With few rows (decode)
 //     this pass is spread over many workgroups per row instead (page_keys
-//     kernel, kPkChunk tokens each), which leave the keys in the workspace.
+//     kernel, kPkChunk tokens each), which leave the keys in the workspace;
+//     in the fused call the MFMA indexer writes them from its epilogue.
 //  2. radix select of the top_pages-th largest page key t.
 //  3. uncertified: pages above t are in, pages equal to t go in by index.
 //     Certified (scores within eps of the exact keys): pages whose computed key
@@ -45,6 +46,7 @@ struct PsSmem {
   uint32_t band_k[kPsBandCap];
   uint32_t sc[16];
   uint32_t run[4];
+  float red[32];
 };
 
 // Keys of pages 0..npc-1 from the scores of tokens 0..ntok-1 (ntok covers the
@@ -168,10 +170,13 @@ __global__ __launch_bounds__(kPsThreads) void page_select_kernel(PageSelParams q
   IndexerRow ir{};
   if (p.certified) {
     const float tf = order_key_f32(t);
-    E = 2.0f * p.err[((int64_t)b * p.G + g) * p.Nq + r] * 1.0001f + 1e-30f;
+    ir = indexer_row(p.ix, b, g, r);
+    // the row's bound: given, or (fused call) from the indexer's chunk maxima
+    const float eps = p.err ? p.err[((int64_t)b * p.G + g) * p.Nq + r]
+                            : row_eps(p.ix, ir, b, p.ix.G_k == 1 ? 0 : g, L, sm.red);
+    E = 2.0f * eps * 1.0001f + 1e-30f;
     klo = f32_order_key(nextafterf(tf - E, -INFINITY));
     khi = f32_order_key(nextafterf(tf + E, INFINITY));
-    ir = indexer_row(p.ix, b, g, r);
   }
 
   const int P = 1 << lgP;
@@ -350,22 +355,72 @@ __global__ __launch_bounds__(kPsThreads) void page_select_kernel(PageSelParams q
 
 static int page_rows(const PageSelParams& p) { return p.t.B * p.t.G * p.t.Nq; }
 static int page_cap(const PageSelParams& p) { return (p.t.ctx + (1 << p.lgP) - 1) >> p.lgP; }
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t page_select_ws_bytes(const PageSelParams& p) {
-  const int rows = page_rows(p);
-  return rows <= kPsFewRows ? (size_t)rows * page_cap(p) * sizeof(uint32_t) : 0;
+// Workspace layout. Fused: scores [B, G, Nq, ctx] f32 | the indexer's chunk
+// maxima of |k| | page keys [rows][pages]. Otherwise the page
+// keys only, and only for few rows.
+struct PsLayout {
+  size_t scores, kmax, keys, total;
+  bool staged;             // page keys staged in the workspace
+  bool epilogue;           // ... by the indexer itself
+};
+
+static PsLayout ps_layout(const PageSelParams& p) {
+  PsLayout l{};
+  const size_t rows = (size_t)page_rows(p);
+  size_t off = 0;
+  if (p.fused) {
+    l.scores = off;
+    off += align256(rows * p.t.ctx * sizeof(float));
+    l.kmax = off;
+    off += align256(indexer_ws_bytes(p.t.ix.B, p.t.ix.G_k, p.t.ix.ctx));
+    l.epilogue = index_pagekeys_ok(p.t.ix, p.lgP);
+  }
+  l.staged = l.epilogue || rows <= (size_t)kPsFewRows;
+  l.keys = off;
+  if (l.staged) off += rows * page_cap(p) * sizeof(uint32_t);
+  l.total = off;
+  return l;
 }
 
-hipError_t launch_page_select(const PageSelParams& p, hipStream_t st) {
+size_t page_select_ws_bytes(const PageSelParams& p) { return ps_layout(p).total; }
+
+hipError_t launch_page_select(const PageSelParams& p0, hipStream_t st) {
+  PageSelParams p = p0;
   const int rows = page_rows(p);
-  uint32_t* pkg = nullptr;
   const int npmax = page_cap(p);
-  if (page_select_ws_bytes(p)) {
-    pkg = (uint32_t*)p.ws;
+  const PsLayout l = ps_layout(p);
+  char* w = (char*)p.ws;
+  uint32_t* pkg = l.staged ? (uint32_t*)(w + l.keys) : nullptr;
+  hipError_t e;
+  if (p.fused) {
+    IndexerParams x = p.t.ix;
+    x.scores = (float*)(w + l.scores);
+    x.ss[3] = 1;
+    x.ss[2] = p.t.ctx;
+    x.ss[1] = (int64_t)p.t.Nq * p.t.ctx;
+    x.ss[0] = (int64_t)p.t.G * p.t.Nq * p.t.ctx;
+    x.err = nullptr;                  // the selection kernel bounds each row itself
+    x.kmax = (float*)(w + l.kmax);
+    x.chunk = index_chunk(x);
+    x.nchunk = (x.ctx + x.chunk - 1) / x.chunk;
+    if (l.epilogue) {
+      x.pkeys = pkg;
+      x.pk_stride = npmax;
+      x.pk_lgP = p.lgP;
+    }
+    if ((e = launch_index_scores(x, st)) != hipSuccess) return e;
+    p.t.scores = x.scores;
+    for (int i = 0; i < 4; ++i) p.t.ss[i] = x.ss[i];
+    p.t.err = nullptr;
+    p.t.certified = true;
+    p.t.ix = x;
+  }
+  if (pkg && !l.epilogue) {
     const int chunks = (p.t.ctx + kPkChunk - 1) / kPkChunk;
     hipLaunchKernelGGL(page_keys_kernel, dim3(chunks, rows), dim3(kPkThreads), 0, st, p, pkg, npmax);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(page_select_kernel, dim3(rows), dim3(kPsThreads), 0, st, p, (const uint32_t*)pkg, npmax);
   return hipGetLastError();

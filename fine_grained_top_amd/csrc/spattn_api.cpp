@@ -309,14 +309,28 @@ static int page_select_setup(const spattn_tensor* scores, const float* err, cons
                              uint32_t flags, const spattn_tensor* pg_idx_out, sp::PageSelParams& q) {
   int rc;
   q = sp::PageSelParams{};
-  if (flags & ~SPATTN_TOPK_CERTIFIED) return fail(SPATTN_ERR_INVALID_ARG, "unknown flags");
+  if (flags & ~(SPATTN_TOPK_CERTIFIED | SPATTN_TOPK_FUSED_INDEX)) return fail(SPATTN_ERR_INVALID_ARG, "unknown flags");
   q.lgP = log2_pow2(page_size, 4096);
   if (q.lgP < 0) return fail(SPATTN_ERR_INVALID_ARG, "page_size must be a power of two in 1..4096");
   if (top_pages < 0 || n_local < 0 || (int64_t)top_pages + n_local < 1)
     return fail(SPATTN_ERR_INVALID_ARG, "need top_pages >= 0, n_local >= 0 and top_pages + n_local >= 1");
   if (top_pages > 16384 || n_local > 16384) return fail(SPATTN_ERR_UNSUPPORTED, "top_pages and n_local must be <= 16384");
-  if (!scores) return fail(SPATTN_ERR_INVALID_ARG, "scores: null tensor");
-  if ((rc = topk_setup(scores, err, ix, ctx_len, 1, flags, nullptr, q.t))) return rc;
+  if (flags & SPATTN_TOPK_FUSED_INDEX) {
+    if (scores || err) return fail(SPATTN_ERR_INVALID_ARG, "fused selection takes no scores or err");
+    int64_t B, Nq, ctx, G;
+    if ((rc = check_indexer(ix, &B, &Nq, &ctx, &G))) return rc;
+    q.t.certified = true;
+    q.t.ix = indexer_params(ix, ctx_len);
+    q.t.B = (int)B;
+    q.t.G = (int)G;
+    q.t.Nq = (int)Nq;
+    q.t.ctx = (int)ctx;
+    q.t.ctx_len = ctx_len;
+    q.fused = true;
+  } else {
+    if (!scores) return fail(SPATTN_ERR_INVALID_ARG, "scores: null tensor");
+    if ((rc = topk_setup(scores, err, ix, ctx_len, 1, flags, nullptr, q.t))) return rc;
+  }
   const int64_t npages = ((int64_t)q.t.ctx + page_size - 1) / page_size;
   if (npages > sp::kMaxPages) return fail(SPATTN_ERR_UNSUPPORTED, "more than %d pages per request", sp::kMaxPages);
   q.t.K = top_pages;
@@ -334,10 +348,12 @@ static int page_select_setup(const spattn_tensor* scores, const float* err, cons
   return SPATTN_OK;
 }
 
-SPATTN_API size_t spattn_page_select_workspace(const spattn_tensor* scores, int32_t page_size, int32_t top_pages,
-                                               int32_t n_local) {
+SPATTN_API size_t spattn_page_select_workspace(const spattn_tensor* scores, const spattn_indexer* ix,
+                                               int32_t page_size, int32_t top_pages, int32_t n_local,
+                                               uint32_t flags) {
   sp::PageSelParams q;
-  if (page_select_setup(scores, nullptr, nullptr, nullptr, page_size, top_pages, n_local, 0u, nullptr, q))
+  if (page_select_setup(scores, nullptr, ix, nullptr, page_size, top_pages, n_local,
+                        flags & ~SPATTN_TOPK_CERTIFIED, nullptr, q))
     return (size_t)-1;
   return sp::page_select_ws_bytes(q);
 }

@@ -942,49 +942,6 @@ SP_DEV float recompute_score(const IndexerRow& r, int64_t j) {
   return s;
 }
 
-// the bound from its inputs: CO = sum over the group's heads and dims of
-// |w_h q_hc| (summed in float32 in any order), KM = max |k| over the row's keys
-SP_DEV float eps_of(const IndexerParams& x, float CO, float KM) {
-  const double u = 1.0 / 8388608.0;
-  auto gam = [&](double n) { return n * u / (1.0 - n * u); };
-  const double C = 1.25 * (gam(x.d_I + 2) + gam(x.hpg + 2) * (1.0 + gam(x.d_I + 2)) + u);
-  // CO was summed in float32: inflate by its own rounding bound
-  const double e = C * (double)CO * (1.0 + gam(x.hpg * x.d_I + 2)) * (double)KM * (1.0 + 1e-6) + 1e-30;
-  return (float)e * (1.0f + 1e-6f);
-}
-
-// rigorous |score~ - key| bound of a row, as computed by the indexer
-SP_DEV float row_eps(const TopkParams& p, const RowCtx& c, const float* kmax, int nchunk, int chunk,
-                     float* red) {
-  const IndexerParams& x = p.ix;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int L = min(p.ctx_len ? p.ctx_len[c.b] : p.ctx, p.ctx);
-  const int nch = min(nchunk, (L + chunk - 1) / chunk);
-  float km = 0.f;
-  for (int i = tid; i < nch; i += blockDim.x) km = fmaxf(km, kmax[(int64_t)c.b * nchunk + i]);
-  float coef = 0.f;
-  for (int e = tid; e < c.ir.H * c.ir.d; e += blockDim.x) {
-    const int h = e / c.ir.d, cc = e % c.ir.d;
-    const float qv = fabsf((float)load_f64(c.ir.q, c.ir.qt, h * c.ir.qh_stride + cc));
-    const float wv = c.ir.relu ? fabsf(c.ir.w[h * c.ir.w_stride]) : 1.f;
-    coef = fmaf(wv, qv, coef);
-  }
-  km = wave_max(km);
-  coef = wave_sum(coef);
-  if (lane == 0) {
-    red[wid] = km;
-    red[16 + wid] = coef;
-  }
-  __syncthreads();
-  float KM = 0.f, CO = 0.f;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-    KM = fmaxf(KM, red[w]);
-    CO += red[16 + w];
-  }
-  __syncthreads();
-  return eps_of(x, CO, KM);
-}
-
 // Pilot, stage 1: one thread per (sampled key, selection row): the row's
 // heads score the key in float32; a key the row cannot see (after its
 // position) gets the order key 0, which no finite score has.

@@ -65,12 +65,11 @@ class HotPath:
             self.count = torch.empty(wl.B, wl.G_sel, wl.Nq, dtype=torch.int32, device=device)
             if wl.kind == "dsa_pages":
                 self.sel = S.selection(S.SEL_PAGES, self.idx, block_size=wl.page_size)
-                self.fused = False          # page selection reads the score matrix
             else:
                 self.sel = S.selection(S.SEL_INDEX, self.idx)
-            if self.fused and S.LIB.spattn_topk_workspace(None, S.ctypes.byref(self.ix), wl.topk,
-                                                          S.TOPK_FUSED_INDEX) == S.SIZE_MAX:
-                self.fused = False          # this indexer shape has no fused kernel: separate calls
+                if self.fused and S.LIB.spattn_topk_workspace(None, S.ctypes.byref(self.ix), wl.topk,
+                                                              S.TOPK_FUSED_INDEX) == S.SIZE_MAX:
+                    self.fused = False      # this indexer shape has no fused kernel: separate calls
         elif wl.kind == "blocks":
             self.idx = torch.empty(wl.B, wl.Hq, wl.Nq, wl.top_blocks, dtype=torch.int32, device=device)
             self.count = torch.empty(wl.B, wl.Hq, wl.Nq, dtype=torch.int32, device=device)
@@ -90,13 +89,17 @@ class HotPath:
         if self.wl.H_I:
             q.append(S.LIB.spattn_index_scores_workspace(byref(self.ix)))
             ts = S.tensor(self.scores)
-            if self.wl.kind == "dsa_pages":
-                q.append(S.LIB.spattn_page_select_workspace(byref(ts), self.wl.page_size, self.wl.top_pages,
-                                                            self.wl.n_local))
+            wl = self.wl
+            if wl.kind == "dsa_pages":
+                q.append(S.LIB.spattn_page_select_workspace(byref(ts), byref(self.ix), wl.page_size, wl.top_pages,
+                                                            wl.n_local, S.TOPK_CERTIFIED))
+                if self.fused:
+                    q.append(S.LIB.spattn_page_select_workspace(None, byref(self.ix), wl.page_size, wl.top_pages,
+                                                                wl.n_local, S.TOPK_FUSED_INDEX))
             else:
-                q.append(S.LIB.spattn_topk_workspace(byref(ts), byref(self.ix), self.wl.topk, S.TOPK_CERTIFIED))
-            if self.fused:
-                q.append(S.LIB.spattn_topk_workspace(None, byref(self.ix), self.wl.topk, S.TOPK_FUSED_INDEX))
+                q.append(S.LIB.spattn_topk_workspace(byref(ts), byref(self.ix), wl.topk, S.TOPK_CERTIFIED))
+                if self.fused:
+                    q.append(S.LIB.spattn_topk_workspace(None, byref(self.ix), wl.topk, S.TOPK_FUSED_INDEX))
         tq, tk = S.tensor(self.q), S.tensor(self.k)
         if self.wl.kind == "blocks":
             q.append(S.LIB.spattn_block_select_workspace(byref(tq), byref(tk), self.wl.block_size,
@@ -124,6 +127,10 @@ class HotPath:
         S.spattn_page_select(self.scores, self.err, self.ix, self.ctx_len, self.wl.page_size, self.wl.top_pages,
                              self.wl.n_local, S.TOPK_CERTIFIED, self.idx, self.count, self.ws, stream)
 
+    def page_select_fused(self, stream=None):
+        S.spattn_page_select(None, None, self.ix, self.ctx_len, self.wl.page_size, self.wl.top_pages,
+                             self.wl.n_local, S.TOPK_FUSED_INDEX, self.idx, self.count, self.ws, stream)
+
     def block_select(self, stream=None):
         S.spattn_block_select(self.q, self.k, self.ctx_len, self.wl.block_size, self.wl.top_blocks,
                               self.idx, self.count, self.ws, stream)
@@ -137,7 +144,9 @@ class HotPath:
                                      self.ws, stream)
 
     def step(self, stream=None):
-        if self.wl.H_I and self.fused:
+        if self.wl.H_I and self.fused and self.wl.kind == "dsa_pages":
+            self.page_select_fused(stream)
+        elif self.wl.H_I and self.fused:
             self.topk_fused(stream)
         elif self.wl.H_I:
             self.index_scores(stream)

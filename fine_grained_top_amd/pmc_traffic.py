@@ -22,13 +22,14 @@ import sqlite3
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
-# kernels of each stage, by name fragment; the fused and the plain indexer are
-# one template whose last argument tells them apart
+# kernels of each stage, by name fragment; the plain, filtering and page-key
+# indexer are one template whose last argument (0, 1, 2) tells them apart
 STAGES = {
-    "index_topk_fused": ["fz_pilot_score", "fz_pilot_select", "true>(sp::IndexerParams)", "fz_final"],
-    "index_scores": ["false>(sp::IndexerParams)", "idx_generic", "idx_err"],
+    "index_topk_fused": ["fz_pilot_score", "fz_pilot_select", "1>(sp::IndexerParams)", "fz_final"],
+    "index_scores": ["0>(sp::IndexerParams)", "idx_generic", "idx_err"],
+    "index_page_fused": ["2>(sp::IndexerParams)", "idx_err", "page_keys", "page_select"],
     "topk": ["topk_row", "topk_redo", "mt_zero", "mt_hist", "mt_collect", "mt_finalize"],
-    "page_select": ["page_select_kernel"],
+    "page_select": ["page_keys_kernel", "page_select_kernel"],
     "block_select": ["pool_kernel", "block_select_kernel"],
     "attention": ["attn_index_mfma", "attn_combine", "attn_tile", "attn_generic", "bc_count", "bc_scan", "bc_table",
                   "bc_scatter", "bc_attn", "bc_combine"],

@@ -63,7 +63,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "spattn_index_scores": (ctypes.c_int, [P(Indexer), vp, P(Tensor), vp, vp, sz, vp]),
         "spattn_topk_workspace": (sz, [P(Tensor), P(Indexer), i32, u32]),
         "spattn_topk": (ctypes.c_int, [P(Tensor), vp, P(Indexer), vp, i32, u32, P(Tensor), vp, vp, sz, vp]),
-        "spattn_page_select_workspace": (sz, [P(Tensor), i32, i32, i32]),
+        "spattn_page_select_workspace": (sz, [P(Tensor), P(Indexer), i32, i32, i32, u32]),
         "spattn_page_select": (ctypes.c_int, [P(Tensor), vp, P(Indexer), vp, i32, i32, i32, u32, P(Tensor), vp,
                                               vp, sz, vp]),
         "spattn_block_select_workspace": (sz, [P(Tensor), P(Tensor), i32, i32]),
@@ -189,17 +189,19 @@ def spattn_topk(scores: Optional[torch.Tensor], err: Optional[torch.Tensor], ix:
                            _ptr(count_out), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
 
 
-def spattn_page_select(scores: torch.Tensor, err: Optional[torch.Tensor], ix: Optional[Indexer],
+def spattn_page_select(scores: Optional[torch.Tensor], err: Optional[torch.Tensor], ix: Optional[Indexer],
                        ctx_len: Optional[torch.Tensor], page_size: int, top_pages: int, n_local: int, flags: int,
                        pg_idx_out: torch.Tensor, pg_count_out: Optional[torch.Tensor] = None,
                        ws: Optional[torch.Tensor] = None, stream=None) -> None:
-    sc, io = tensor(scores), tensor(pg_idx_out)
-    need = LIB.spattn_page_select_workspace(ctypes.byref(sc), page_size, top_pages, n_local)
+    sc = tensor(scores) if scores is not None else None
+    io = tensor(pg_idx_out)
+    scp = ctypes.byref(sc) if sc is not None else None
+    ixp = ctypes.byref(ix) if ix is not None else None
+    need = LIB.spattn_page_select_workspace(scp, ixp, page_size, top_pages, n_local, flags)
     if need == SIZE_MAX:
         raise SpattnError(1, LIB.spattn_last_error_message().decode())
-    ws = _workspace(need, scores.device, ws)
-    ixp = ctypes.byref(ix) if ix is not None else None
-    _check(LIB.spattn_page_select(ctypes.byref(sc), _ptr(err), ixp, _ptr(ctx_len), page_size, top_pages, n_local,
+    ws = _workspace(need, pg_idx_out.device, ws)
+    _check(LIB.spattn_page_select(scp, _ptr(err), ixp, _ptr(ctx_len), page_size, top_pages, n_local,
                                   flags, ctypes.byref(io), _ptr(pg_count_out), _ptr(ws),
                                   0 if ws is None else ws.numel(), _stream(stream)))
 

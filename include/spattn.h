@@ -202,14 +202,21 @@ SPATTN_API int spattn_topk(const spattn_tensor* scores, const float* err,
  *      spattn_index_scores on indexer ix; keys are the exact token keys (the
  *      float32 nearest to the exact score), near-ties rescored exactly, so
  *      the page list equals exhaustive selection on exact keys.
+ *  flags = SPATTN_TOPK_FUSED_INDEX: scores and err are NULL; the call scores
+ *      the tokens from ix itself (into the workspace, with the page keys
+ *      taken in the indexer's epilogue where its MFMA kernel applies and P is
+ *      32..512) and selects as with SPATTN_TOPK_CERTIFIED.
  *  Limits: P a power of two in 1..4096; ceil(ctx / P) <= 16384;
  *  top_pages, n_local >= 0 with top_pages + n_local >= 1; top_pages <= 16384.
- *  Workspace: with at most 512 rows (B * G * Nq) the page keys of every row
- *  are staged there, rows * ceil(ctx / P) * 4 bytes; otherwise none (the
- *  query returns 0).
+ *  Workspace (the query takes the same scores or indexer and flags): fused,
+ *  the scores [B, G, Nq, ctx] f32 and the indexer's per-chunk maxima of |k|,
+ *  plus the page keys;
+ *  otherwise the page keys of every row when there are at most 512 rows
+ *  (B * G * Nq), rows * ceil(ctx / P) * 4 bytes, else nothing.
  * ---------------------------------------------------------------------- */
-SPATTN_API size_t spattn_page_select_workspace(const spattn_tensor* scores, int32_t page_size,
-                                               int32_t top_pages, int32_t n_local);
+SPATTN_API size_t spattn_page_select_workspace(const spattn_tensor* scores, const spattn_indexer* ix,
+                                               int32_t page_size, int32_t top_pages, int32_t n_local,
+                                               uint32_t flags);
 SPATTN_API int spattn_page_select(const spattn_tensor* scores, const float* err,
                                   const spattn_indexer* ix, const int32_t* ctx_len,
                                   int32_t page_size, int32_t top_pages, int32_t n_local,

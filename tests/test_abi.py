@@ -149,12 +149,12 @@ def test_page_select_validation():
                                         None, ws.data_ptr(), ws_bytes, None)
 
     # few rows: the page keys of every row are staged in the workspace
-    need = S.LIB.spattn_page_select_workspace(ctypes.byref(S.tensor(sc)), 64, 3, 2)
+    need = S.LIB.spattn_page_select_workspace(ctypes.byref(S.tensor(sc)), None, 64, 3, 2, 0)
     assert need == 8 * 4 * 4
     assert call(64, 3, 2) == 4                  # valid: reaches the device check
     assert call(64, 3, 2, ws_bytes=need - 1) == 3
     many = torch.zeros(1, 1, 600, 700)          # many rows: one pass per row, no workspace
-    assert S.LIB.spattn_page_select_workspace(ctypes.byref(S.tensor(many)), 64, 3, 2) == 0
+    assert S.LIB.spattn_page_select_workspace(ctypes.byref(S.tensor(many)), None, 64, 3, 2, 0) == 0
     assert call(16, 5, 0) == 4
     assert call(48, 3, 2) == 1                  # page size not a power of two
     assert call(8192, 3, 2) == 1                # page size above 4096
@@ -162,7 +162,7 @@ def test_page_select_validation():
     assert call(64, -1, 6) == 1
     assert call(64, 3, 1) == 1                  # width must be top_pages + n_local
     assert call(64, 3, 2, flags=S.TOPK_CERTIFIED) == 1   # certified needs err + indexer
-    assert call(64, 3, 2, flags=S.TOPK_FUSED_INDEX) == 1  # no fused variant
+    assert call(64, 3, 2, flags=S.TOPK_FUSED_INDEX) == 1  # fused takes no scores
     assert call(1, 3, 2, scores=torch.zeros(1, 2, 4, 20000)) == 2   # more than 16384 pages
     assert "pages" in S.spattn_last_error_message()
 
@@ -197,3 +197,25 @@ def test_paged_attention_validation():
     assert S.LIB.spattn_sparse_attn_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tk), None, 0.0,
                                         ctypes.byref(sel), ctypes.byref(to), None, ws.data_ptr(), ws.numel(),
                                         None) == 4
+
+
+def test_page_select_fused_validation():
+    q = torch.zeros(2, 1, 32, 64, dtype=torch.bfloat16)
+    k = torch.zeros(2, 4096, 1, 64, dtype=torch.uint8)
+    w = torch.zeros(2, 1, 32)
+    ix = S.indexer(q, k, w, S.SCORE_WEIGHTED_RELU, 4)
+    io = torch.zeros(2, 8, 1, 5, dtype=torch.int32)
+    need = S.LIB.spattn_page_select_workspace(None, ctypes.byref(ix), 64, 3, 2, S.TOPK_FUSED_INDEX)
+    rows = 2 * 8
+    assert need >= rows * 4096 * 4 + rows * (4096 // 64) * 4   # scores and page keys
+    ws = torch.zeros(need, dtype=torch.uint8)
+
+    def call(flags=S.TOPK_FUSED_INDEX, scores=None, ws_bytes=need, idx=io):
+        sp_ = ctypes.byref(S.tensor(scores)) if scores is not None else None
+        return S.LIB.spattn_page_select(sp_, None, ctypes.byref(ix), None, 64, 3, 2, flags,
+                                        ctypes.byref(S.tensor(idx)), None, ws.data_ptr(), ws_bytes, None)
+
+    assert call() == 4                                          # valid: reaches the device check
+    assert call(ws_bytes=need - 1) == 3
+    assert call(scores=torch.zeros(2, 8, 1, 4096)) == 1         # fused takes no scores
+    assert call(idx=torch.zeros(2, 8, 1, 4, dtype=torch.int32)) == 1

@@ -699,3 +699,26 @@ def test_paged_storage_matches_contiguous(dtype, d, Nq):
     tol = 1e-5 if dtype == "f32" else 2e-3
     say(f"  max diff vs oracle {worst:.3e} (tol {tol})")
     assert worst <= tol
+
+
+@pytest.mark.parametrize("name,P,top", [("dsa_paged_decode_small", 64, 6), ("dsa_paged_decode_small", 32, 9),
+                                        ("dsa_paged_decode_small", 512, 1), ("dsa_paged_decode_small", 16, 20),
+                                        ("dsa_paged_prefill_small", 16, 5), ("dsa_paged_prefill_small", 128, 1),
+                                        ("dsa_paged_decode", 64, 30)])
+def test_fused_page_select(name, P, top):
+    """Page selection from the indexer inputs in one call: the page keys come
+    from the indexer's epilogue (pages of 32..512 keys on its MFMA path) or
+    from the separate page-key pass; page lists equal the oracle's and the
+    two-call path's bit for bit, and the attention over them matches."""
+    wl = dataclasses.replace(gen.WORKLOADS[name], page_size=P, top_pages=top)
+    inp = gen.generate(wl)
+    hp = run_fused(wl, inp)
+    rows = _all_rows(wl, inp) if wl.Nq == 1 else [(0, r) for r in range(0, wl.Nq, 7)] + [(0, wl.Nq - 1)]
+    res = oracle_rows(wl, inp, rows)
+    check_sets(hp, res, rows, wl)
+    check_out(hp, res, rows, 2e-3)
+    fused_idx = hp.idx.clone()
+    hp.index_scores()
+    hp.page_select()
+    torch.cuda.synchronize()
+    assert torch.equal(hp.idx, fused_idx)
