@@ -87,7 +87,7 @@ def algorithmic(wl, inp, hp, fused):
                                 "flops": 4.0 * sel_g * (wl.Hq // wl.G_sel) * wl.d,
                                 "bound": "hbm" if wl.Nq == 1 else "mfma"}
     elif wl.kind == "window_global":
-        pairs = float(metrics.window_global_pairs(wl.N, wl.window, wl.n_global)) * wl.Hq * wl.B
+        pairs = float(metrics.window_stride_pairs(wl.N, wl.window, wl.n_global, wl.stride)) * wl.Hq * wl.B
         kv = wl.B * wl.Hkv * wl.N * wl.d * e * 2
         out["attention"] = {"bytes": kv + qkv_out, "flops": 4.0 * pairs * wl.d, "bound": "hbm"}
     elif wl.kind == "blocks":

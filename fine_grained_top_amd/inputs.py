@@ -194,6 +194,7 @@ class Workload:
     # fixed patterns
     window: int = 0
     n_global: int = 0
+    stride: int = 0           # dilated stride: every stride-th token is visible too
     block_size: int = 0
     top_blocks: int = 0
     shift_frac: float = 0.0
@@ -240,6 +241,11 @@ DECODE = _add(Workload("dsa_decode", "dsa_decode", B=8, Hq=32, Hkv=8, N=131072, 
 _add(dataclasses.replace(TINY, name="tiny_topk_f32_small", N=300, Nq=300, needles=3))
 _add(dataclasses.replace(WINDOW, name="window_global_small", Hq=2, Hkv=2, N=1000,
                          Nq=1000, window=96, n_global=5))
+# Local window plus dilated stride (the fixed pattern's defaults: 64 positions
+# back, i.e. 65 keys with the query, and every 8th token).
+STRIDED = _add(dataclasses.replace(WINDOW, name="window_stride", seed=8, window=65, n_global=0, stride=8))
+_add(dataclasses.replace(STRIDED, name="window_stride_small", Hq=2, Hkv=2, N=1000, Nq=1000, stride=24,
+                         n_global=3))
 _add(Workload("dense_small", "dense", B=2, Hq=4, Hkv=2, N=700, Nq=700, d=128, dtype="bf16", seed=6))
 _add(dataclasses.replace(BLOCKS, name="block_sparse_small", Hq=2, Hkv=2, N=1500,
                          Nq=1500, top_blocks=4, window=100))

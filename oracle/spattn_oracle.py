@@ -20,7 +20,9 @@ What is computed (sources are the five pages on sparse attention):
   lower-triangular dense pattern, cost N^2/2).
 * Sliding window of w keys including the query itself, plus g global tokens
   at positions 0..g-1 ("Sparse Attention", sliding window + global figure,
-  cost N*w + N*g; "A Guide ...", section 2 pattern list).
+  cost N*w + N*g; "A Guide ...", section 2 pattern list), plus, with a stride
+  R > 0, every past token at a multiple of R ("Sparse Attention Is Reshaping
+  Production AI", Fixed Patterns: local window plus dilated stride).
 * Block-sparse selection: keys pooled by mean over 64-token blocks, each
   query scores blocks by an unscaled dot product with the pooled key and keeps
   the top blocks ("Sparse Attention Is Reshaping Production AI", "Learned
@@ -225,11 +227,15 @@ def topk(keys: np.ndarray, K: int) -> np.ndarray:
     return np.sort(order[:kk]).astype(np.int32)
 
 
-def window_global_set(p: int, w: int, g: int) -> np.ndarray:
-    """Keys j <= p with j >= p - w + 1 (window incl. self) or j < g (global)."""
+def window_global_set(p: int, w: int, g: int, stride: int = 0) -> np.ndarray:
+    """Keys j <= p with j >= p - w + 1 (window incl. self), j < g (global) or,
+    when stride > 0, j a multiple of stride (dilated stride)."""
     win = np.arange(max(0, p - w + 1), p + 1)
     glob = np.arange(0, min(g, p + 1))
-    return np.union1d(win, glob).astype(np.int32)
+    s = np.union1d(win, glob)
+    if stride > 0:
+        s = np.union1d(s, np.arange(0, p + 1, stride))
+    return s.astype(np.int32)
 
 
 def eligible_blocks(p: int, bs: int) -> int:
@@ -381,7 +387,7 @@ def run(wl, inp: Dict[str, np.ndarray], rows: Iterable[Tuple[int, int]],
                     if h // (wl.Hq // wl.G_sel) == g:
                         S_of_head[h] = S
         elif wl.kind == "window_global":
-            S = window_global_set(p, wl.window, wl.n_global)
+            S = window_global_set(p, wl.window, wl.n_global, wl.stride)
             res.sets[(b, 0, r)] = S
             S_of_head = [S] * wl.Hq
         elif wl.kind == "blocks":

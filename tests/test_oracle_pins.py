@@ -237,7 +237,8 @@ def test_window_global_pair_counts():
     g = _gold("pages_arithmetic.json")["window_global_counts"]
     for n, w, gg, expect in g["cases"]:
         assert metrics.window_global_pairs(n, w, gg) == expect
-    for n, w, gg in [(12, 2, 2), (40, 7, 3), (33, 33, 0), (50, 10, 10), (16384, 512, 16)]:
+    for n, w, gg in [(12, 2, 2), (40, 7, 3), (33, 33, 0), (50, 10, 10), (16384, 512, 16), (33, 33, 2),
+                     (10, 9, 5), (6, 20, 3)]:
         tot = sum(len(orc.window_global_set(p, w, gg)) for p in range(n))
         assert tot == metrics.window_global_pairs(n, w, gg)
         if n <= 50:
@@ -459,3 +460,35 @@ def test_paged_pool_holds_the_logical_cache():
             pool = inp[name + "_pages"]
             rebuilt = np.concatenate([pool[T[b, pg]] for pg in range((n + P - 1) // P)], axis=1)[:, :n]
             assert np.array_equal(rebuilt, inp[name][b, :, :n])
+
+
+
+# ---------------------------------------------------------------- dilated stride
+@pytest.mark.parametrize("stride", [1, 3, 8, 13])
+def test_window_stride_is_the_pages_fixed_mask(stride):
+    """Window of w keys (incl. self) plus every stride-th token == the fixed
+    local + dilated mask of 'Sparse Attention Is Reshaping Production AI' with
+    window w - 1; attention under it equals torch SDPA with that mask."""
+    n, w, d = 60, 6, 16
+    rng = np.random.default_rng(12)
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    mask = _fixed_pattern_mask(n, w - 1, stride)
+    for i in range(n):
+        S = orc.window_global_set(i, w, 0, stride)
+        assert np.array_equal(S, np.nonzero(mask[i])[0])
+        if i % 7 == 0:
+            o, _ = orc.masked_attention(q[i:i + 1], k[: i + 1], v[: i + 1], S, 1 / math.sqrt(d))
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q[i:i + 1]), torch.from_numpy(k[: i + 1]), torch.from_numpy(v[: i + 1]),
+                attn_mask=torch.from_numpy(mask[i, : i + 1][None, :])).numpy()
+            assert np.max(np.abs(o - ref)) < 1e-12
+
+
+def test_window_stride_pair_counts():
+    """Sum of |S(i)| with window, globals and stride: oracle sets, brute force
+    and the benchmark's count agree."""
+    for n, w, g, s in [(40, 7, 3, 5), (64, 8, 0, 8), (50, 10, 12, 4), (33, 33, 2, 3), (45, 1, 0, 1)]:
+        tot = sum(len(orc.window_global_set(p, w, g, s)) for p in range(n))
+        brute = sum(1 for i in range(n) for j in range(i + 1) if j >= i - w + 1 or j < g or j % s == 0)
+        assert tot == brute == metrics.window_stride_pairs(n, w, g, s)
+    assert metrics.window_stride_pairs(16384, 512, 16, 0) == metrics.window_global_pairs(16384, 512, 16)
