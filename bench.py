@@ -89,7 +89,9 @@ def algorithmic(wl, inp, hp, fused):
     elif wl.kind == "window_global":
         pairs = float(metrics.window_stride_pairs(wl.N, wl.window, wl.n_global, wl.stride)) * wl.Hq * wl.B
         kv = wl.B * wl.Hkv * wl.N * wl.d * e * 2
-        out["attention"] = {"bytes": kv + qkv_out, "flops": 4.0 * pairs * wl.d, "bound": "hbm"}
+        # a dilated stride makes every row see ~p/stride keys: the products, not the bytes, bound it
+        out["attention"] = {"bytes": kv + qkv_out, "flops": 4.0 * pairs * wl.d,
+                            "bound": "mfma" if wl.stride else "hbm"}
     elif wl.kind == "blocks":
         blk = hp.idx.cpu().numpy()                       # [B, Hq, Nq, nb]
         p = np.arange(wl.Nq)[None, None, :]

@@ -32,6 +32,7 @@ struct Visible {
   const int32_t* list;   // index list (mode 1), block list (mode 3) or page list (mode 4)
   int K;                 // list length
   int g_end, w_start, bs, nb_keys, lgbs;
+  int n_wg, stride, m0;    // window/global: keys before the strided ones, stride, first multiple
 
   SP_DEV void init(const AttnParams& a, int b, int h, int r, int pos) {
     mode = a.mode;
@@ -53,6 +54,14 @@ struct Visible {
       g_end = min(a.n_global, p + 1);
       w_start = max(max(0, p - a.window + 1), g_end);
       count = g_end + max(0, p - w_start + 1);
+      // dilated stride: the multiples of stride in [g_end, w_start)
+      n_wg = count;
+      stride = a.stride;
+      m0 = 0;
+      if (stride > 0 && w_start > 0) {
+        m0 = (g_end + stride - 1) / stride;
+        count += max(0, (w_start - 1) / stride - m0 + 1);
+      }
     } else {
       list = a.sel + b * a.sels[0] + h * a.sels[1] + r * a.sels[2];
       bs = a.bs;
@@ -74,7 +83,7 @@ struct Visible {
       const int j = (pg << lgbs) + (t & ((1 << lgbs) - 1));
       return j <= p ? j : -1;
     }
-    if (mode == 2) return t < g_end ? t : w_start + (t - g_end);
+    if (mode == 2) return t < g_end ? t : t < n_wg ? w_start + (t - g_end) : (m0 + (t - n_wg)) * stride;
     if (t < nb_keys) {
       const int blk = list[t / bs];
       if (blk < 0) return -1;

@@ -5,7 +5,9 @@
 // 16w..16w+15. Key tiles of 64 keys are visited in increasing order: the
 // global tiles and the band of the window (WINDOW_GLOBAL), every past tile
 // (DENSE), or the union of the rows' selected blocks and windows (BLOCKS,
-// from an LDS tile bitmap). K and V tiles are staged row-major in LDS (V
+// from an LDS tile bitmap). A dilated stride adds tiles of 64 consecutive
+// multiples of the stride (K/V rows read at that stride), masked to the keys
+// outside each row's window and global prefix, which the first stream covers. K and V tiles are staged row-major in LDS (V
 // with XOR-swizzled 16-byte chunks, read as the MFMA operand by transposed
 // LDS reads); the next tile is prefetched into registers while the current
 // one is consumed. Per wave and tile: S^T = K Q^T on
@@ -54,6 +56,17 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
     for (int i = tid; i < kTQ * bwords; i += 256) sm.rowblk[i] = 0;
   __syncthreads();
   const int last_tile = prow_last >= 0 ? min(ntiles_all - 1, prow_last / kTK) : -1;
+  // dilated stride: multiples m * stride, m in [m_lo, m_hi], below the latest
+  // window start of the tile and outside the global prefix, as nvt virtual
+  // tiles numbered from ntiles_all
+  const int NT = ntiles_all;
+  const int sd = a.mode == 2 ? a.stride : 0;
+  int m_lo = 0, nvt = 0;
+  if (sd > 0 && prow_last - a.window >= 0) {
+    m_lo = (a.n_global + sd - 1) / sd;
+    const int m_hi = (prow_last - a.window) / sd;
+    if (m_hi >= m_lo) nvt = (m_hi - m_lo + kTK) / kTK;
+  }
   if (a.mode == 0) {
     for (int t = tid; t <= last_tile; t += 256) atomicOr(&sm.tiles[t >> 5], 1u << (t & 31));
   } else if (a.mode == 2) {
@@ -112,19 +125,25 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
     }
     return -1;
   };
+  // next tile of either stream
+  auto next_any = [&](int t) -> int {
+    if (t >= NT) return t + 1 < NT + nvt ? t + 1 : -1;
+    const int n = t < last_tile ? next_tile(t) : -1;
+    return n >= 0 ? n : (nvt > 0 ? NT : -1);
+  };
   // prefetch of one tile: chunk c = tid + 256u -> key c/16, 16-byte column c%16
   u32x4 pk[4], pv[4];
   auto load_tile = [&](int t) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int c = tid + 256 * u;
-      int j = t * kTK + (c >> 4);
+      int j = t < NT ? t * kTK + (c >> 4) : (m_lo + (t - NT) * kTK + (c >> 4)) * sd;
       j = j < L ? j : L - 1;
       pk[u] = *(const u32x4*)(kbase + (int64_t)j * a.k.s[2] + 8 * (c & 15));
       pv[u] = *(const u32x4*)(vbase + (int64_t)j * a.v.s[2] + 8 * (c & 15));
     }
   };
-  int t = last_tile >= 0 ? next_tile(-1) : -1;
+  int t = next_any(-1);
   if (t >= 0) load_tile(t);
   while (t >= 0) {
     // stage the prefetched tile
@@ -137,13 +156,16 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
       *(u32x4*)&sm.vt[key * 128 + 8 * (col ^ (key & 15))] = pv[u];
     }
     __syncthreads();
-    const int tn = next_tile(t);
+    const int tn = next_any(t);
     if (tn >= 0) load_tile(tn);
 
-    const int j0 = t * kTK;
+    const bool sv = t >= NT;                       // a tile of stride multiples
+    const int j0 = sv ? 0 : t * kTK;
+    const int mb0 = sv ? m_lo + (t - NT) * kTK : 0;
     // does any row of this wave see this tile?
     bool see = rvalid && prow >= j0;
-    if (see && a.mode == 2) see = (j0 + kTK - 1 >= wstart) || (j0 < a.n_global);
+    if (sv) see = rvalid && mb0 * sd <= prow && mb0 * sd < wstart;
+    else if (see && a.mode == 2) see = (j0 + kTK - 1 >= wstart) || (j0 < a.n_global);
     if (see && a.mode == 3) {
       bool any = j0 + kTK - 1 >= wstart;
       if (!any) {
@@ -171,9 +193,10 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int j = j0 + 16 * st + 4 * qq + v;
+          const int j = sv ? (mb0 + 16 * st + 4 * qq + v) * sd : j0 + 16 * st + 4 * qq + v;
           bool vis = rvalid && j <= prow;
-          if (vis && a.mode == 2) vis = j >= wstart || j < a.n_global;
+          if (sv) vis = vis && j < wstart && j >= a.n_global;
+          else if (vis && a.mode == 2) vis = j >= wstart || j < a.n_global;
           if (vis && a.mode == 3) {
             const int bb = j / a.bs;
             vis = j >= wstart || ((sm.rowblk[rloc * bwords + (bb >> 5)] >> (bb & 31)) & 1u);

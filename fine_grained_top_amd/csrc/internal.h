@@ -108,6 +108,7 @@ struct AttnParams {
   int G_sel, K;            // list groups and width (index: keys; blocks: blocks; pages: page
                            // slots times the page size, i.e. one entry per token slot)
   int window, n_global, bs;
+  int stride;              // window/global: every stride-th token is visible too (0: none)
   int lgbs;                // pages: log2 of the tokens per listed page
   // paged K/V storage: k, v are pools [n_pages, Hkv, 1 << lgP, d]; logical page
   // pg of request b lives in pool page ptab[b * pts + pg]

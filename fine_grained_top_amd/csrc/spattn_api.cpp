@@ -524,8 +524,11 @@ static int attn_setup(const spattn_tensor* q, const spattn_tensor* k, const spat
     }
     case SPATTN_SEL_WINDOW_GLOBAL:
       if (sel->window < 0 || sel->n_global < 0) return fail(SPATTN_ERR_INVALID_ARG, "window/n_global must be >= 0");
+      if (sel->stride < 0 || sel->stride > (1 << 24))
+        return fail(SPATTN_ERR_INVALID_ARG, "stride must be in 0..2^24");
       p.window = sel->window;
       p.n_global = sel->n_global;
+      p.stride = sel->stride;
       break;
     case SPATTN_SEL_BLOCKS: {
       if ((rc = check_tensor(&sel->idx, "sel.idx", 4, false))) return rc;

@@ -75,7 +75,7 @@ class HotPath:
             self.count = torch.empty(wl.B, wl.Hq, wl.Nq, dtype=torch.int32, device=device)
             self.sel = S.selection(S.SEL_BLOCKS, self.idx, window=wl.window, block_size=wl.block_size)
         elif wl.kind == "window_global":
-            self.sel = S.selection(S.SEL_WINDOW_GLOBAL, window=wl.window, n_global=wl.n_global)
+            self.sel = S.selection(S.SEL_WINDOW_GLOBAL, window=wl.window, n_global=wl.n_global, stride=wl.stride)
         else:
             self.sel = S.selection(S.SEL_DENSE)
         self.ws = torch.empty(self.ws_bytes(), dtype=torch.uint8, device=device)

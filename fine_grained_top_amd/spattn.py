@@ -45,7 +45,7 @@ class Indexer(ctypes.Structure):
 
 class Selection(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("idx", Tensor), ("window", ctypes.c_int32),
-                ("n_global", ctypes.c_int32), ("block_size", ctypes.c_int32)]
+                ("n_global", ctypes.c_int32), ("block_size", ctypes.c_int32), ("stride", ctypes.c_int32)]
 
 
 class KvPages(ctypes.Structure):
@@ -143,13 +143,14 @@ def indexer(q_idx: torch.Tensor, k_idx: torch.Tensor, w: Optional[torch.Tensor],
 
 
 def selection(mode: int, idx: Optional[torch.Tensor] = None, window: int = 0, n_global: int = 0,
-              block_size: int = 0) -> Selection:
+              block_size: int = 0, stride: int = 0) -> Selection:
     s = Selection()
     s.mode = mode
     s.idx = tensor(idx)
     s.window = window
     s.n_global = n_global
     s.block_size = block_size
+    s.stride = stride
     s._keep = idx
     return s
 

@@ -101,7 +101,8 @@ typedef struct spattn_indexer {
 enum spattn_sel_mode {
   SPATTN_SEL_DENSE = 0,          /* S = all keys 0..p (the conservative fallback) */
   SPATTN_SEL_INDEX = 1,          /* S = explicit index list (e.g. from spattn_topk) */
-  SPATTN_SEL_WINDOW_GLOBAL = 2,  /* S = {p-window+1..p} U {0..n_global-1}, within 0..p */
+  SPATTN_SEL_WINDOW_GLOBAL = 2,  /* S = {p-window+1..p} U {0..n_global-1} U {multiples of
+                                    stride}, within 0..p */
   SPATTN_SEL_BLOCKS = 3,         /* S = selected blocks U {p-window+1..p}, within 0..p */
   SPATTN_SEL_PAGES = 4           /* S = every token of the listed pages, within 0..p */
 };
@@ -117,6 +118,9 @@ typedef struct spattn_selection {
   int32_t window;        /* keys in the sliding window, the query itself included */
   int32_t n_global;      /* WINDOW_GLOBAL: tokens 0..n_global-1 are visible to all rows */
   int32_t block_size;    /* BLOCKS: tokens per block; PAGES: tokens per page (power of two) */
+  int32_t stride;        /* WINDOW_GLOBAL: when > 0 every token at a multiple of stride is
+                            visible too (local window plus dilated stride, "Sparse Attention
+                            Is Reshaping Production AI", Fixed Patterns); 0 = none */
 } spattn_selection;
 
 /* Paged K/V storage: the keys and values of all requests live in a pool of

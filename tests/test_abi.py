@@ -107,6 +107,8 @@ def test_attention_validation():
 
     assert call(S.selection(S.SEL_INDEX, idx)) == 4
     assert call(S.selection(S.SEL_WINDOW_GLOBAL, window=8, n_global=2)) == 4
+    assert call(S.selection(S.SEL_WINDOW_GLOBAL, window=8, n_global=2, stride=4)) == 4
+    assert call(S.selection(S.SEL_WINDOW_GLOBAL, window=8, stride=-1)) == 1
     assert call(S.selection(S.SEL_DENSE)) == 4
     assert call(S.selection(7)) == 1
     assert call(S.selection(S.SEL_INDEX, idx.float())) == 1

@@ -132,7 +132,7 @@ def test_tiny_fp32_full():
 
 @pytest.mark.parametrize("name", ["dsa_decode_small", "dsa_prefill_small", "window_global_small",
                                   "block_sparse_small", "tiny_topk_f32_small", "dsa_paged_decode_small",
-                                  "dsa_paged_prefill_small"])
+                                  "dsa_paged_prefill_small", "window_stride_small"])
 def test_small_workload(name):
     wl = gen.WORKLOADS[name]
     inp = gen.generate(wl)
@@ -364,7 +364,8 @@ def _sample_rows(wl, n, seed):
     return [(0, r) for r in sorted(rows)]
 
 
-@pytest.mark.parametrize("name,n", [("window_global", 48), ("block_sparse", 24), ("dsa_prefill", 24)])
+@pytest.mark.parametrize("name,n", [("window_global", 48), ("block_sparse", 24), ("dsa_prefill", 24),
+                                    ("window_stride", 48)])
 def test_full_size_sampled_rows(name, n):
     wl = gen.WORKLOADS[name]
     say(f"[gpu] generating {name} inputs")
@@ -722,3 +723,54 @@ def test_fused_page_select(name, P, top):
     hp.page_select()
     torch.cuda.synchronize()
     assert torch.equal(hp.idx, fused_idx)
+
+
+@pytest.mark.parametrize("stride,g,w,dtype", [(8, 0, 65, "bf16"), (64, 5, 100, "bf16"), (100, 3, 40, "bf16"),
+                                              (1, 0, 10, "bf16"), (7, 2, 30, "f32")])
+def test_window_stride_modes_agree(stride, g, w, dtype):
+    """The strided window/global pattern against index lists that spell out
+    the same visible sets (the tiled kernel, or the generic one for f32,
+    against the gather kernel), and every row against the oracle."""
+    import oracle as orc
+    sp = S()
+    say(f"[gpu] window+stride s={stride} g={g} w={w} {dtype}")
+    g_ = torch.Generator().manual_seed(51)
+    B, H, Nq, ctx, d = 2, 2, 300, 700, 128
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = torch.randn(B, H, Nq, d, generator=g_).to(tdt)
+    k = torch.randn(B, H, ctx, d, generator=g_).to(tdt)
+    v = torch.randn(B, H, ctx, d, generator=g_).to(tdt)
+    ctx_len = [700, 455]
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    cl = torch.tensor(ctx_len, dtype=torch.int32, device="cuda")
+    o_pat = torch.empty(B, H, Nq, d, device="cuda")
+    l_pat = torch.empty(B, H, Nq, device="cuda")
+    sp.spattn_sparse_attn_fwd(qd, kd, vd, cl, 0.0, sp.selection(sp.SEL_WINDOW_GLOBAL, window=w, n_global=g,
+                                                                 stride=stride), o_pat, l_pat)
+    sets = {}
+    width = 0
+    for b in range(B):
+        for r in range(Nq):
+            p = ctx_len[b] - Nq + r
+            sets[(b, r)] = orc.window_global_set(p, w, g, stride)
+            width = max(width, len(sets[(b, r)]))
+    lists = np.full((B, 1, Nq, width), -1, np.int32)
+    for (b, r), S_ in sets.items():
+        lists[b, 0, r, : len(S_)] = S_
+    ld = torch.from_numpy(lists).cuda()
+    o_idx = torch.empty_like(o_pat)
+    sp.spattn_sparse_attn_fwd(qd, kd, vd, cl, 0.0, sp.selection(sp.SEL_INDEX, ld), o_idx)
+    torch.cuda.synchronize()
+    diff = float((o_idx - o_pat).abs().max())
+    q64, k64, v64 = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    O, LSE = o_pat.cpu().numpy(), l_pat.cpu().numpy()
+    worst = 0.0
+    for (b, r), S_ in sets.items():
+        p = ctx_len[b] - Nq + r
+        for h in range(H):
+            o, l = orc.masked_attention(q64[b, h, r][None], k64[b, h, : p + 1], v64[b, h, : p + 1], S_,
+                                        1.0 / math.sqrt(d))
+            worst = max(worst, float(np.abs(O[b, h, r] - o[0]).max()), abs(float(LSE[b, h, r]) - float(l[0])))
+    tol = 1e-5 if dtype == "f32" else 2e-3
+    say(f"  pattern vs index lists {diff:.3e}; pattern vs oracle {worst:.3e} (tol {tol})")
+    assert worst <= tol and diff <= tol
