@@ -35,6 +35,8 @@ struct TileSmem {
   uint32_t rowblk[kTQ * kMaxBlkWords];   // BLOCKS: per-row selected-block bitmaps
 };
 
+// STRIDE: window/global mode with a dilated stride (the second key stream)
+template <bool STRIDE>
 __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
   __shared__ __attribute__((aligned(16))) TileSmem sm;
   const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -60,9 +62,9 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
   // window start of the tile and outside the global prefix, as nvt virtual
   // tiles numbered from ntiles_all
   const int NT = ntiles_all;
-  const int sd = a.mode == 2 ? a.stride : 0;
+  const int sd = STRIDE ? a.stride : 0;
   int m_lo = 0, nvt = 0;
-  if (sd > 0 && prow_last - a.window >= 0) {
+  if (STRIDE && prow_last - a.window >= 0) {
     m_lo = (a.n_global + sd - 1) / sd;
     const int m_hi = (prow_last - a.window) / sd;
     if (m_hi >= m_lo) nvt = (m_hi - m_lo + kTK) / kTK;
@@ -127,9 +129,9 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
   };
   // next tile of either stream
   auto next_any = [&](int t) -> int {
-    if (t >= NT) return t + 1 < NT + nvt ? t + 1 : -1;
+    if (STRIDE && t >= NT) return t + 1 < NT + nvt ? t + 1 : -1;
     const int n = t < last_tile ? next_tile(t) : -1;
-    return n >= 0 ? n : (nvt > 0 ? NT : -1);
+    return n >= 0 ? n : (STRIDE && nvt > 0 ? NT : -1);
   };
   // prefetch of one tile: chunk c = tid + 256u -> key c/16, 16-byte column c%16
   u32x4 pk[4], pv[4];
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int c = tid + 256 * u;
-      int j = t < NT ? t * kTK + (c >> 4) : (m_lo + (t - NT) * kTK + (c >> 4)) * sd;
+      int j = (!STRIDE || t < NT) ? t * kTK + (c >> 4) : (m_lo + (t - NT) * kTK + (c >> 4)) * sd;
       j = j < L ? j : L - 1;
       pk[u] = *(const u32x4*)(kbase + (int64_t)j * a.k.s[2] + 8 * (c & 15));
       pv[u] = *(const u32x4*)(vbase + (int64_t)j * a.v.s[2] + 8 * (c & 15));
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
     const int tn = next_any(t);
     if (tn >= 0) load_tile(tn);
 
-    const bool sv = t >= NT;                       // a tile of stride multiples
+    const bool sv = STRIDE && t >= NT;             // a tile of stride multiples
     const int j0 = sv ? 0 : t * kTK;
     const int mb0 = sv ? m_lo + (t - NT) * kTK : 0;
     // does any row of this wave see this tile?
@@ -186,25 +188,38 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
         for (int s = 0; s < 4; ++s)
           S[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(kr + 8 * s), Qb[s], S[st], 0, 0, 0);
       }
-      // masks: lane's keys j = j0 + 16*st + 4*qq + v for its row (column c16)
+      // masks: lane's keys j = j0 + 16*st + 4*qq + v for its row (column c16);
+      // in a stride tile the keys are multiples (mb0 + 16*st + 4*qq + v) * stride
       float z[16];
       float tm = -INFINITY;
+      if (!sv) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
+        for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int j = sv ? (mb0 + 16 * st + 4 * qq + v) * sd : j0 + 16 * st + 4 * qq + v;
-          bool vis = rvalid && j <= prow;
-          if (sv) vis = vis && j < wstart && j >= a.n_global;
-          else if (vis && a.mode == 2) vis = j >= wstart || j < a.n_global;
-          if (vis && a.mode == 3) {
-            const int bb = j / a.bs;
-            vis = j >= wstart || ((sm.rowblk[rloc * bwords + (bb >> 5)] >> (bb & 31)) & 1u);
+          for (int v = 0; v < 4; ++v) {
+            const int j = j0 + 16 * st + 4 * qq + v;
+            bool vis = rvalid && j <= prow;
+            if (vis && a.mode == 2) vis = j >= wstart || j < a.n_global;
+            if (vis && a.mode == 3) {
+              const int bb = j / a.bs;
+              vis = j >= wstart || ((sm.rowblk[rloc * bwords + (bb >> 5)] >> (bb & 31)) & 1u);
+            }
+            const float zz = vis ? S[st][v] * cs : -INFINITY;
+            z[4 * st + v] = zz;
+            tm = fmaxf(tm, zz);
           }
-          const float zz = vis ? S[st][v] * cs : -INFINITY;
-          z[4 * st + v] = zz;
-          tm = fmaxf(tm, zz);
-        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int j = (mb0 + 16 * st + 4 * qq + v) * sd;
+            const bool vis = rvalid && j <= prow && j < wstart && j >= a.n_global;
+            const float zz = vis ? S[st][v] * cs : -INFINITY;
+            z[4 * st + v] = zz;
+            tm = fmaxf(tm, zz);
+          }
+      }
       tm = rows4_max(tm);
       const float mn = fmaxf(m, tm);
       float alpha = 1.f, ps = 0.f;
@@ -296,7 +311,8 @@ bool attn_tile_ok(const AttnParams& a) {
 
 hipError_t launch_attn_tile(const AttnParams& a, hipStream_t st) {
   dim3 grid((a.Nq + kTQ - 1) / kTQ, a.Hq, a.B);
-  hipLaunchKernelGGL(attn_tile_kernel, grid, dim3(256), 0, st, a);
+  if (a.mode == 2 && a.stride > 0) hipLaunchKernelGGL(attn_tile_kernel<true>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(attn_tile_kernel<false>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
