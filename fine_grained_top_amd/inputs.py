@@ -17,7 +17,8 @@ Recipe (stated once, used everywhere):
     (for several indexer heads: the head with the largest weight);
   * the block-sparse workload shifts every key element of 4% of the 64-token
     blocks by +2.0 (two standard deviations) before rounding, the same blocks
-    for every head;
+    for every head (the NSA workload too);
+  * NSA branch gates are U(0,1) draws, one per (request, head, row, branch);
   * decode lengths are drawn uniformly from an inclusive integer range;
   * paged workloads also store K and V as a pool of P-token pages: the
     B * ceil(N/P) logical pages are placed at the physical slots of one seeded
@@ -36,7 +37,7 @@ import numpy as np
 CHUNK = 1 << 22
 
 # tensor ids used in the seed sequence
-TID = dict(q=1, k=2, v=3, q_idx=4, k_idx=5, w=6, lengths=7, needles=8, shift=9, pages=10)
+TID = dict(q=1, k=2, v=3, q_idx=4, k_idx=5, w=6, lengths=7, needles=8, shift=9, pages=10, gates=11)
 
 
 def _threads() -> int:
@@ -172,7 +173,7 @@ def uniform01(seed: int, tid: int, shape) -> np.ndarray:
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # topk | window_global | blocks | dsa_prefill | dsa_decode | dsa_pages
+    kind: str                 # topk | window_global | blocks | nsa | dsa_prefill | dsa_decode | dsa_pages
     B: int
     Hq: int
     Hkv: int
@@ -249,6 +250,11 @@ _add(dataclasses.replace(STRIDED, name="window_stride_small", Hq=2, Hkv=2, N=100
 _add(Workload("dense_small", "dense", B=2, Hq=4, Hkv=2, N=700, Nq=700, d=128, dtype="bf16", seed=6))
 _add(dataclasses.replace(BLOCKS, name="block_sparse_small", Hq=2, Hkv=2, N=1500,
                          Nq=1500, top_blocks=4, window=100))
+# Three-branch NSA attention on the block-sparse shapes: compression over the
+# mean-pooled 64-token blocks, selection of the top-16 blocks, a 512-token
+# window, and one gate value per branch for every (row, head).
+NSA = _add(dataclasses.replace(BLOCKS, name="nsa_blocks", kind="nsa", seed=9))
+_add(dataclasses.replace(NSA, name="nsa_blocks_small", Hq=4, Hkv=2, N=1500, Nq=1500, top_blocks=4, window=100))
 _add(dataclasses.replace(PREFILL, name="dsa_prefill_small", Hq=16, N=1200, Nq=1200,
                          topk=128, needles=12))
 _add(dataclasses.replace(DECODE, name="dsa_decode_small", B=3, N=9000,
@@ -301,7 +307,7 @@ def generate(w: Workload) -> Dict[str, np.ndarray]:
     out["ctx_len"] = lengths(w)
     out["q"] = normal(w.seed, TID["q"], (w.B, w.Hq, w.Nq, w.d), w.dtype)
     shift_fn = None
-    if w.kind == "blocks" and w.shift_frac > 0:
+    if w.kind in ("blocks", "nsa") and w.shift_frac > 0:
         blocks, shift_fn = _shift_blocks(w)
         out["shifted_blocks"] = blocks.astype(np.int64)
     out["k"] = normal(w.seed, TID["k"], (w.B, w.Hkv, w.N, w.d), w.dtype, shift_fn)
@@ -316,6 +322,8 @@ def generate(w: Workload) -> Dict[str, np.ndarray]:
         out["needles"] = _plant_needles(w, out)
     if w.page_size:
         out["page_table"], out["k_pages"], out["v_pages"] = paged_kv(w, out["k"], out["v"])
+    if w.kind == "nsa":
+        out["gates"] = uniform01(w.seed, TID["gates"], (w.B, w.Hq, w.Nq, 3))   # compression, selection, window
     return out
 
 

@@ -33,6 +33,14 @@ What is computed (sources are the five pages on sparse attention):
   "Sparse Attention in 2026", DSA paragraph): score s(i,j) is either
   q_I . k_I,j or sum_h w_h * ReLU(q_I,h . k_I,j), the indexer carries no
   positional encoding, and the K highest scoring past keys are kept.
+* Three-branch NSA attention ("Sparse Attention in 2026", NSA paragraph;
+  "Sparse Attention" (completesystemdesign.dev), three parallel paths): a
+  compression branch attends over the key and value blocks mean-pooled into
+  single entries (complete past blocks), a selection branch over the tokens of
+  the top blocks chosen by the compression branch's own scores (the pooled-key
+  dot products above), and a window branch; each branch has its own softmax
+  and a gate weighs them: o = g_cmp o_cmp + g_sel o_sel + g_win o_win. A branch
+  with no visible entry contributes 0.
 * Page-granular selection ("Sparse Attention in 2026: Why It Finally Had to
   Be Native", the DSA list: the indexer rates every 64-token KV page, the
   attention reads the best pages plus the mandatory recent pages, whole).
@@ -291,6 +299,30 @@ def pages_set(pages: Sequence[int], p: int, P: int) -> np.ndarray:
     return s[s <= p].astype(np.int32)
 
 
+def pooled_blocks(X: np.ndarray, bs: int, n_blocks: int) -> np.ndarray:
+    """Mean of each complete block of bs rows: the compressed entries."""
+    return X[: n_blocks * bs].reshape(n_blocks, bs, X.shape[1]).mean(axis=1)
+
+
+def nsa_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, p: int, bs: int, blocks: Sequence[int], w: int,
+                  gates: np.ndarray, scale: float) -> np.ndarray:
+    """Gated sum of the compression, selection and window branches for one
+    query head q [d] at position p (keys K, V [>= p+1, d]); gates [3]."""
+    out = np.zeros(K.shape[1])
+    nc = eligible_blocks(p, bs)
+    branches = []
+    if nc:
+        branches.append((0, pooled_blocks(K, bs, nc), pooled_blocks(V, bs, nc), np.arange(nc)))
+    sel = blocks_set(blocks, p, bs, 0)
+    if len(sel):
+        branches.append((1, K[: p + 1], V[: p + 1], sel))
+    branches.append((2, K[: p + 1], V[: p + 1], window_global_set(p, w, 0)))
+    for gi, Kx, Vx, S in branches:
+        o, _ = masked_attention(q[None, :], Kx, Vx, S, scale)
+        out += gates[gi] * o[0]
+    return out
+
+
 # --------------------------------------------------------------------------
 # attention
 # --------------------------------------------------------------------------
@@ -390,7 +422,7 @@ def run(wl, inp: Dict[str, np.ndarray], rows: Iterable[Tuple[int, int]],
             S = window_global_set(p, wl.window, wl.n_global, wl.stride)
             res.sets[(b, 0, r)] = S
             S_of_head = [S] * wl.Hq
-        elif wl.kind == "blocks":
+        elif wl.kind in ("blocks", "nsa"):
             for h in range(wl.Hq):
                 qh = decode(Q[b, h, r], wl.dtype)
                 ne = eligible_blocks(p, wl.block_size)
@@ -399,7 +431,7 @@ def run(wl, inp: Dict[str, np.ndarray], rows: Iterable[Tuple[int, int]],
                 res.blocks[(b, h, r)] = blk
                 if keep_keys:
                     res.keys[(b, h, r)] = keys
-                S = blocks_set(blk, p, wl.block_size, wl.window)
+                S = blocks_set(blk, p, wl.block_size, 0 if wl.kind == "nsa" else wl.window)
                 res.sets[(b, h, r)] = S
                 S_of_head[h] = S
         elif wl.kind == "dense":
@@ -410,7 +442,17 @@ def run(wl, inp: Dict[str, np.ndarray], rows: Iterable[Tuple[int, int]],
             raise ValueError(wl.kind)
         res.candidates += n * wl.Hq
         res.pairs += sum(len(s) for s in S_of_head)
-        if attention:
+        if attention and wl.kind == "nsa":
+            O = np.zeros((wl.Hq, wl.d))
+            gates = np.asarray(inp["gates"], dtype=np.float32).astype(np.float64)
+            for h in range(wl.Hq):
+                qh = decode(Q[b, h, r], wl.dtype)
+                kvh = h // qpk
+                Vh = decode(Vst[b, kvh, :n], wl.dtype)
+                O[h] = nsa_attention(qh, Kb[kvh], Vh, p, wl.block_size, res.blocks[(b, h, r)], wl.window,
+                                     gates[b, h, r], scale)
+            res.O[(b, r)] = O
+        elif attention:
             O = np.zeros((wl.Hq, wl.d))
             lse = np.zeros(wl.Hq)
             for h in range(wl.Hq):

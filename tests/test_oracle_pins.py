@@ -492,3 +492,57 @@ def test_window_stride_pair_counts():
         brute = sum(1 for i in range(n) for j in range(i + 1) if j >= i - w + 1 or j < g or j % s == 0)
         assert tot == brute == metrics.window_stride_pairs(n, w, g, s)
     assert metrics.window_stride_pairs(16384, 512, 16, 0) == metrics.window_global_pairs(16384, 512, 16)
+
+
+# ---------------------------------------------------------------- NSA branches
+def _nsa_case(seed=14, n=40, d=8, bs=4):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal(d), rng.standard_normal((n, d)), rng.standard_normal((n, d))
+
+
+def test_nsa_compression_of_one_token_blocks_is_causal_sdpa():
+    """With one-token blocks the mean-pooled entries are the tokens, so the
+    compression branch alone (gates 1, 0, 0) is causal attention."""
+    q, K, V = _nsa_case()
+    Q = np.random.default_rng(15).standard_normal((K.shape[0], K.shape[1]))
+    ref = _sdpa_causal(Q[None], K[None], V[None])[0]
+    for p in (0, 5, 39):
+        o = orc.nsa_attention(Q[p], K, V, p, 1, [], 3, np.array([1.0, 0.0, 0.0]), 1 / math.sqrt(K.shape[1]))
+        assert np.max(np.abs(o - ref[p])) < 1e-12
+
+
+def test_nsa_pooling_is_the_block_mean():
+    """Compressed entries by explicit sums over each complete block."""
+    _, K, _ = _nsa_case()
+    P = orc.pooled_blocks(K, 4, 9)
+    for blk in range(9):
+        want = [sum(K[4 * blk + t][c] for t in range(4)) / 4 for c in range(K.shape[1])]
+        assert np.allclose(P[blk], want, rtol=0, atol=1e-15)
+    # a block of identical rows compresses to that row
+    K2 = np.repeat(K[:1], 8, axis=0)
+    assert np.allclose(orc.pooled_blocks(K2, 8, 1)[0], K[0], rtol=0, atol=1e-15)
+
+
+def test_nsa_gates_pick_branches():
+    """Each one-hot gate returns its branch alone: window attention, attention
+    over the chosen blocks' tokens, compression over pooled blocks; and the
+    gated sum is linear in the gates (an empty branch adds nothing)."""
+    q, K, V = _nsa_case()
+    sc = 1 / math.sqrt(K.shape[1])
+    p, bs, w, blocks = 30, 4, 6, [1, 3, 5]
+    win, _ = orc.masked_attention(q[None], K[: p + 1], V[: p + 1], np.arange(p - w + 1, p + 1), sc)
+    sel_set = np.concatenate([np.arange(4 * x, 4 * x + 4) for x in blocks])
+    sel, _ = orc.masked_attention(q[None], K[: p + 1], V[: p + 1], sel_set, sc)
+    nc = (p + 1) // bs
+    Kc = np.stack([K[4 * x: 4 * x + 4].mean(axis=0) for x in range(nc)])
+    Vc = np.stack([V[4 * x: 4 * x + 4].mean(axis=0) for x in range(nc)])
+    cmp_, _ = orc.masked_attention(q[None], Kc, Vc, np.arange(nc), sc)
+    for g, want in (([0, 0, 1], win[0]), ([0, 1, 0], sel[0]), ([1, 0, 0], cmp_[0])):
+        assert np.max(np.abs(orc.nsa_attention(q, K, V, p, bs, blocks, w, np.array(g, float), sc) - want)) < 1e-12
+    g = np.array([0.2, 0.3, 0.5])
+    mix = orc.nsa_attention(q, K, V, p, bs, blocks, w, g, sc)
+    assert np.max(np.abs(mix - (0.2 * cmp_[0] + 0.3 * sel[0] + 0.5 * win[0]))) < 1e-12
+    # before the first complete block only the window contributes
+    early = orc.nsa_attention(q, K, V, 2, bs, [], w, g, sc)
+    w0, _ = orc.masked_attention(q[None], K[:3], V[:3], np.arange(0, 3), sc)
+    assert np.max(np.abs(early - 0.5 * w0[0])) < 1e-12
