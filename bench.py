@@ -92,6 +92,22 @@ def algorithmic(wl, inp, hp, fused):
         # a dilated stride makes every row see ~p/stride keys: the products, not the bytes, bound it
         out["attention"] = {"bytes": kv + qkv_out, "flops": 4.0 * pairs * wl.d,
                             "bound": "mfma" if wl.stride else "hbm"}
+    elif wl.kind == "nsa":
+        # three branches: pooled entries of complete blocks, the chosen blocks' tokens, the window
+        blk = hp.idx.cpu().numpy().astype(np.int64)          # [B, Hq, Nq, nb]
+        p = np.arange(wl.Nq)[None, None, :, None]
+        tok = np.clip(np.minimum(blk * wl.block_size + wl.block_size, p + 1) - blk * wl.block_size, 0, None)
+        sel_pairs = float((tok * (blk >= 0)).sum())
+        pos = np.arange(wl.Nq)
+        win_pairs = float(np.minimum(pos + 1, wl.window).sum()) * wl.Hq * wl.B
+        cmp_pairs = float(((pos + 1) // wl.block_size).sum()) * wl.Hq * wl.B
+        kv = wl.B * wl.Hkv * wl.N * wl.d * e * 2
+        out["attention"] = {"bytes": kv + qkv_out, "flops": 4.0 * (sel_pairs + win_pairs + cmp_pairs) * wl.d,
+                            "bound": "mfma"}
+        nbk = wl.N // wl.block_size
+        elig = float(np.sum(np.minimum((np.arange(wl.Nq) + 1) // wl.block_size, nbk))) * wl.Hq * wl.B
+        out["block_select"] = {"bytes": wl.B * wl.Hkv * wl.N * wl.d * e + wl.B * wl.Hq * wl.Nq * wl.d * e
+                               + blk.size * 4, "flops": 2.0 * elig * wl.d, "rows": wl.B * wl.Hq * wl.Nq}
     elif wl.kind == "blocks":
         blk = hp.idx.cpu().numpy()                       # [B, Hq, Nq, nb]
         p = np.arange(wl.Nq)[None, None, :]
@@ -183,7 +199,7 @@ def main():
     elif wl.H_I:
         stages = [("index_scores", lambda hp: hp.index_scores()), ("topk", lambda hp: hp.topk()),
                   ("attention", lambda hp: hp.attention())]
-    elif wl.kind == "blocks":
+    elif wl.kind in ("blocks", "nsa"):
         stages = [("block_select", lambda hp: hp.block_select()), ("attention", lambda hp: hp.attention())]
     else:
         stages = [("attention", lambda hp: hp.attention())]
@@ -276,7 +292,7 @@ def main():
             done += 1
             err = float(np.abs(O[b, :, r] - res.O[(b, r)]).max())
             ok &= err <= (1e-5 if wl.dtype == "f32" else 2e-3)
-            if idx is not None and wl.kind != "blocks":
+            if idx is not None and wl.kind not in ("blocks", "nsa"):
                 for g in range(wl.G_sel):
                     want = res.blocks[(b, g, r)] if wl.kind == "dsa_pages" else res.sets[(b, g, r)]
                     ok &= bool(np.array_equal(idx[b, g, r, : len(want)], want))

@@ -41,6 +41,8 @@ struct Visible {
     K = a.K;
     if (mode == 0) {
       count = p + 1;
+    } else if (mode == 5) {
+      count = (p + 1) / a.bs;               // compressed entries of the complete blocks
     } else if (mode == 1) {
       const int gsel = h / (a.Hq / a.G_sel);
       list = a.sel + b * a.sels[0] + gsel * a.sels[1] + r * a.sels[2];
@@ -72,7 +74,7 @@ struct Visible {
     if (p < 0) count = 0;
   }
   SP_DEV int key(int t) const {
-    if (mode == 0) return t;
+    if (mode == 0 || mode == 5) return t;
     if (mode == 1) {
       const int j = list[t];
       return (j >= 0 && j <= p) ? j : -1;

@@ -48,7 +48,10 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
   const int pbase = L - a.Nq;                      // position of row 0
   const int prow_first = pbase + q0;
   const int prow_last = pbase + min(q0 + kTQ, a.Nq) - 1;
-  const int ntiles_all = (L + kTK - 1) / kTK;
+  // mode 5 (compressed entries): key rows are the request's complete blocks,
+  // entry c visible at position p when c <= (p + 1) / bs - 1
+  const int Lk = a.mode == 5 ? L / a.bs : L;
+  const int ntiles_all = (Lk + kTK - 1) / kTK;
   const int nbk = a.mode == 3 ? (a.ctx + a.bs - 1) / a.bs : 0;
   const int bwords = (nbk + 31) >> 5;
 
@@ -57,7 +60,8 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
   if (a.mode == 3)
     for (int i = tid; i < kTQ * bwords; i += 256) sm.rowblk[i] = 0;
   __syncthreads();
-  const int last_tile = prow_last >= 0 ? min(ntiles_all - 1, prow_last / kTK) : -1;
+  const int plast_v = a.mode == 5 ? (prow_last + 1) / a.bs - 1 : prow_last;
+  const int last_tile = plast_v >= 0 ? min(ntiles_all - 1, plast_v / kTK) : -1;
   // dilated stride: multiples m * stride, m in [m_lo, m_hi], below the latest
   // window start of the tile and outside the global prefix, as nvt virtual
   // tiles numbered from ntiles_all
@@ -69,7 +73,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
     const int m_hi = (prow_last - a.window) / sd;
     if (m_hi >= m_lo) nvt = (m_hi - m_lo + kTK) / kTK;
   }
-  if (a.mode == 0) {
+  if (a.mode == 0 || a.mode == 5) {
     for (int t = tid; t <= last_tile; t += 256) atomicOr(&sm.tiles[t >> 5], 1u << (t & 31));
   } else if (a.mode == 2) {
     const int gt = (min(a.n_global, L) + kTK - 1) / kTK;
@@ -96,6 +100,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
   const int rq = q0 + rloc;
   const bool rvalid = rq < a.Nq;
   const int prow = pbase + rq;
+  const int prow_v = a.mode == 5 ? (prow + 1) / a.bs - 1 : prow;   // last visible key row
   const int wstart = prow - a.window + 1;
   bf16x8 Qb[4];
   if (rvalid) {
@@ -140,7 +145,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
     for (int u = 0; u < 4; ++u) {
       const int c = tid + 256 * u;
       int j = (!STRIDE || t < NT) ? t * kTK + (c >> 4) : (m_lo + (t - NT) * kTK + (c >> 4)) * sd;
-      j = j < L ? j : L - 1;
+      j = j < Lk ? j : Lk - 1;
       pk[u] = *(const u32x4*)(kbase + (int64_t)j * a.k.s[2] + 8 * (c & 15));
       pv[u] = *(const u32x4*)(vbase + (int64_t)j * a.v.s[2] + 8 * (c & 15));
     }
@@ -165,7 +170,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
     const int j0 = sv ? 0 : t * kTK;
     const int mb0 = sv ? m_lo + (t - NT) * kTK : 0;
     // does any row of this wave see this tile?
-    bool see = rvalid && prow >= j0;
+    bool see = rvalid && prow_v >= j0;
     if (sv) see = rvalid && mb0 * sd <= prow && mb0 * sd < wstart;
     else if (see && a.mode == 2) see = (j0 + kTK - 1 >= wstart) || (j0 < a.n_global);
     if (see && a.mode == 3) {
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int j = j0 + 16 * st + 4 * qq + v;
-            bool vis = rvalid && j <= prow;
+            bool vis = rvalid && j <= prow_v;
             if (vis && a.mode == 2) vis = j >= wstart || j < a.n_global;
             if (vis && a.mode == 3) {
               const int bb = j / a.bs;

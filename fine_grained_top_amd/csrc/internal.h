@@ -102,7 +102,8 @@ struct AttnParams {
   int B, Hq, Hkv, Nq, ctx, d;
   const int32_t* ctx_len;
   float scale;
-  int mode;                // 0 dense, 1 index, 2 window/global, 3 blocks, 4 pages
+  int mode;                // 0 dense, 1 index, 2 window/global, 3 blocks, 4 pages,
+                           // 5 compressed entries (k, v: per-block means; bs: block size)
   const int32_t* sel;      // index list, block list or page list
   int64_t sels[4];
   int G_sel, K;            // list groups and width (index: keys; blocks: blocks; pages: page
@@ -122,6 +123,18 @@ struct AttnParams {
   size_t ws_bytes;
 };
 size_t attn_ws_bytes(const AttnParams& p);
+// three-branch NSA attention: compression (mode 5 over the pooled blocks),
+// selection (mode 3 without window), window (mode 2), combined by gates
+struct NsaParams {
+  AttnParams a;            // q, k, v, ctx_len, scale, shapes; sel/sels/K: block lists [B, Hq, Nq, nb]
+  const float* gates;      // [B, Hq, Nq, 3] f32: compression, selection, window
+  int64_t gs[4];
+  float* o;                // [B, Hq, Nq, d] f32
+  int64_t os[4];
+  void* ws;
+};
+size_t nsa_ws_bytes(const NsaParams& p);
+hipError_t launch_nsa(const NsaParams& p, hipStream_t st);
 hipError_t launch_attention(const AttnParams& p, hipStream_t st);
 bool attn_tile_ok(const AttnParams& p);
 hipError_t launch_attn_tile(const AttnParams& p, hipStream_t st);

@@ -606,6 +606,60 @@ SPATTN_API int spattn_sparse_attn_fwd(const spattn_tensor* q, const spattn_tenso
   return attn_fwd(q, k, v, nullptr, ctx_len, scale, sel, o_out, lse_out, ws, ws_bytes, stream);
 }
 
+// ------------------------------------------------------------------ NSA
+static int nsa_setup(const spattn_tensor* q, const spattn_tensor* k, const spattn_tensor* v, int32_t block_size,
+                     const spattn_tensor* blk_idx, int32_t window, sp::NsaParams& p, bool need_v) {
+  int rc;
+  p = sp::NsaParams{};
+  if (!blk_idx) return fail(SPATTN_ERR_INVALID_ARG, "blk_idx: null tensor");
+  if (log2_pow2(block_size, 4096) < 0) return fail(SPATTN_ERR_INVALID_ARG, "block_size must be a power of two in 1..4096");
+  if (window < 0) return fail(SPATTN_ERR_INVALID_ARG, "window must be >= 0");
+  spattn_selection sel{};
+  sel.mode = SPATTN_SEL_BLOCKS;
+  sel.idx = *blk_idx;
+  sel.block_size = block_size;
+  if ((rc = attn_setup(q, k, v, &sel, p.a, need_v))) return rc;
+  p.a.window = window;
+  return SPATTN_OK;
+}
+
+SPATTN_API size_t spattn_nsa_fwd_workspace(const spattn_tensor* q, const spattn_tensor* k, int32_t block_size,
+                                           const spattn_tensor* blk_idx, int32_t window) {
+  sp::NsaParams p;
+  if (nsa_setup(q, k, nullptr, block_size, blk_idx, window, p, false)) return (size_t)-1;
+  return sp::nsa_ws_bytes(p);
+}
+
+SPATTN_API int spattn_nsa_fwd(const spattn_tensor* q, const spattn_tensor* k, const spattn_tensor* v,
+                              const int32_t* ctx_len, float scale, int32_t block_size, const spattn_tensor* blk_idx,
+                              int32_t window, const spattn_tensor* gates, const spattn_tensor* o_out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  sp::NsaParams p;
+  int rc;
+  if ((rc = nsa_setup(q, k, v, block_size, blk_idx, window, p, true))) return rc;
+  if ((rc = check_tensor(gates, "gates", 4, false))) return rc;
+  if (gates->dtype != SPATTN_F32) return fail(SPATTN_ERR_INVALID_ARG, "gates must be f32");
+  if (gates->shape[0] != q->shape[0] || gates->shape[1] != q->shape[1] || gates->shape[2] != q->shape[2] ||
+      gates->shape[3] != 3)
+    return fail(SPATTN_ERR_INVALID_ARG, "gates must be [B, H_q, Nq, 3]");
+  if ((rc = check_tensor(o_out, "o_out", 4, false))) return rc;
+  if (o_out->dtype != SPATTN_F32) return fail(SPATTN_ERR_INVALID_ARG, "o_out must be f32");
+  for (int i = 0; i < 4; ++i)
+    if (o_out->shape[i] != q->shape[i]) return fail(SPATTN_ERR_INVALID_ARG, "o_out shape must equal q's");
+  if (!(scale >= 0.f) || std::isinf(scale)) return fail(SPATTN_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  p.a.scale = scale == 0.f ? 1.0f / std::sqrt((float)p.a.d) : scale;
+  p.a.ctx_len = ctx_len;
+  p.gates = (const float*)gates->data;
+  for (int i = 0; i < 4; ++i) p.gs[i] = gates->stride[i];
+  p.o = (float*)o_out->data;
+  for (int i = 0; i < 4; ++i) p.os[i] = o_out->stride[i];
+  const size_t need = sp::nsa_ws_bytes(p);
+  if (ws_bytes < need || !ws) return fail(SPATTN_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  p.ws = ws;
+  if ((rc = device_ok())) return rc;
+  return launched(sp::launch_nsa(p, (hipStream_t)stream));
+}
+
 SPATTN_API size_t spattn_sparse_attn_fwd_paged_workspace(const spattn_tensor* q, const spattn_tensor* k_pool,
                                                          const spattn_kv_pages* pages, const spattn_selection* sel) {
   sp::AttnParams p;

@@ -4,8 +4,8 @@ Orchestration only: it moves the seeded inputs to the device, owns the output
 and workspace buffers, and calls the libspattn entry points in order
 (indexer scores -> certified top-K -> sparse attention; indexer scores ->
 certified page selection -> attention over the pages of a paged KV cache;
-block selection -> block-sparse attention; or a fixed window + global
-pattern).
+block selection -> block-sparse attention; block selection -> three-branch
+NSA attention; or a fixed window + global pattern).
 """
 from __future__ import annotations
 
@@ -70,10 +70,12 @@ class HotPath:
                 if self.fused and S.LIB.spattn_topk_workspace(None, S.ctypes.byref(self.ix), wl.topk,
                                                               S.TOPK_FUSED_INDEX) == S.SIZE_MAX:
                     self.fused = False      # this indexer shape has no fused kernel: separate calls
-        elif wl.kind == "blocks":
+        elif wl.kind in ("blocks", "nsa"):
             self.idx = torch.empty(wl.B, wl.Hq, wl.Nq, wl.top_blocks, dtype=torch.int32, device=device)
             self.count = torch.empty(wl.B, wl.Hq, wl.Nq, dtype=torch.int32, device=device)
             self.sel = S.selection(S.SEL_BLOCKS, self.idx, window=wl.window, block_size=wl.block_size)
+            if wl.kind == "nsa":
+                self.gates = torch.from_numpy(inp["gates"].astype(np.float32)).to(device)
         elif wl.kind == "window_global":
             self.sel = S.selection(S.SEL_WINDOW_GLOBAL, window=wl.window, n_global=wl.n_global, stride=wl.stride)
         else:
@@ -101,10 +103,13 @@ class HotPath:
                 if self.fused:
                     q.append(S.LIB.spattn_topk_workspace(None, byref(self.ix), wl.topk, S.TOPK_FUSED_INDEX))
         tq, tk = S.tensor(self.q), S.tensor(self.k)
-        if self.wl.kind == "blocks":
+        if self.wl.kind in ("blocks", "nsa"):
             q.append(S.LIB.spattn_block_select_workspace(byref(tq), byref(tk), self.wl.block_size,
                                                          self.wl.top_blocks))
-        if self.pages is not None:
+        if self.wl.kind == "nsa":
+            q.append(S.LIB.spattn_nsa_fwd_workspace(byref(tq), byref(tk), self.wl.block_size,
+                                                    byref(S.tensor(self.idx)), self.wl.window))
+        elif self.pages is not None:
             q.append(S.LIB.spattn_sparse_attn_fwd_paged_workspace(byref(tq), byref(tk), byref(self.pages),
                                                                   byref(self.sel)))
         else:
@@ -136,7 +141,10 @@ class HotPath:
                               self.idx, self.count, self.ws, stream)
 
     def attention(self, stream=None):
-        if self.pages is not None:
+        if self.wl.kind == "nsa":
+            S.spattn_nsa_fwd(self.q, self.k, self.v, self.ctx_len, 0.0, self.wl.block_size, self.idx, self.wl.window,
+                             self.gates, self.o, self.ws, stream)
+        elif self.pages is not None:
             S.spattn_sparse_attn_fwd_paged(self.q, self.k, self.v, self.pages, self.ctx_len, 0.0, self.sel, self.o,
                                            self.lse, self.ws, stream)
         else:
@@ -154,6 +162,6 @@ class HotPath:
                 self.page_select(stream)
             else:
                 self.topk(stream)
-        elif self.wl.kind == "blocks":
+        elif self.wl.kind in ("blocks", "nsa"):
             self.block_select(stream)
         self.attention(stream)

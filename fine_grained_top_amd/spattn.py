@@ -74,6 +74,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "spattn_sparse_attn_fwd_paged_workspace": (sz, [P(Tensor), P(Tensor), P(KvPages), P(Selection)]),
         "spattn_sparse_attn_fwd_paged": (ctypes.c_int, [P(Tensor), P(Tensor), P(Tensor), P(KvPages), vp,
                                                         ctypes.c_float, P(Selection), P(Tensor), vp, vp, sz, vp]),
+        "spattn_nsa_fwd_workspace": (sz, [P(Tensor), P(Tensor), i32, P(Tensor), i32]),
+        "spattn_nsa_fwd": (ctypes.c_int, [P(Tensor), P(Tensor), P(Tensor), vp, ctypes.c_float, i32, P(Tensor), i32,
+                                          P(Tensor), P(Tensor), vp, sz, vp]),
         "spattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "spattn_version": (ctypes.c_char_p, []),
         "spattn_last_error_message": (ctypes.c_char_p, []),
@@ -248,6 +251,19 @@ def spattn_sparse_attn_fwd_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: 
                                             ctypes.byref(pages), _ptr(ctx_len), scale, ctypes.byref(sel),
                                             ctypes.byref(to), _ptr(lse_out), _ptr(ws),
                                             0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def spattn_nsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ctx_len: Optional[torch.Tensor], scale: float,
+                   block_size: int, blk_idx: torch.Tensor, window: int, gates: torch.Tensor, o_out: torch.Tensor,
+                   ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    tq, tk, tv, tb, tg, to = tensor(q), tensor(k), tensor(v), tensor(blk_idx), tensor(gates), tensor(o_out)
+    need = LIB.spattn_nsa_fwd_workspace(ctypes.byref(tq), ctypes.byref(tk), block_size, ctypes.byref(tb), window)
+    if need == SIZE_MAX:
+        raise SpattnError(1, LIB.spattn_last_error_message().decode())
+    ws = _workspace(need, q.device, ws)
+    _check(LIB.spattn_nsa_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), _ptr(ctx_len), scale, block_size,
+                              ctypes.byref(tb), window, ctypes.byref(tg), ctypes.byref(to), _ptr(ws),
+                              0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def spattn_version() -> str:

@@ -298,6 +298,36 @@ SPATTN_API int spattn_sparse_attn_fwd_paged(const spattn_tensor* q, const spattn
                                             const spattn_tensor* o_out, float* lse_out,
                                             void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * spattn_nsa_fwd — three-branch NSA attention.
+ * Source: "Sparse Attention in 2026: Why It Finally Had to Be Native", NSA
+ * paragraph (coarse compression of token blocks mean-pooled into single
+ * entries, fine-grained selection of the top blocks by the compression
+ * branch's own scores, a sliding window, all feeding a learned gate);
+ * "Sparse Attention" (completesystemdesign.dev), three parallel paths.
+ *
+ * For query row (b,h,r) at position p, with each branch's own softmax:
+ *  o_cmp: attention over the per-block means of K and V of the complete past
+ *         blocks {beta : block_size*beta + block_size - 1 <= p} (the means
+ *         are formed here and kept in the cache dtype);
+ *  o_sel: attention over the tokens of the blocks listed in blk_idx
+ *         int32 [B, H_q, Nq, nb] (e.g. from spattn_block_select, whose scores
+ *         q . mean(k) are the compression branch's logits), within 0..p;
+ *  o_win: attention over the keys p-window+1..p;
+ *  o_out f32 [B, H_q, Nq, d] = g0 o_cmp + g1 o_sel + g2 o_win with
+ *  gates f32 [B, H_q, Nq, 3] (the learned gate's outputs, given). A branch
+ *  with nothing visible contributes 0.
+ *  q, k, v as for spattn_sparse_attn_fwd; block_size a power of two.
+ *  Workspace: the pooled K and V, the three branch outputs and the block
+ *  attention's scratch (the query gives the size).
+ * ---------------------------------------------------------------------- */
+SPATTN_API size_t spattn_nsa_fwd_workspace(const spattn_tensor* q, const spattn_tensor* k, int32_t block_size,
+                                           const spattn_tensor* blk_idx, int32_t window);
+SPATTN_API int spattn_nsa_fwd(const spattn_tensor* q, const spattn_tensor* k, const spattn_tensor* v,
+                              const int32_t* ctx_len, float scale, int32_t block_size,
+                              const spattn_tensor* blk_idx, int32_t window, const spattn_tensor* gates,
+                              const spattn_tensor* o_out, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ helpers */
 SPATTN_API const char* spattn_status_string(int status);
 SPATTN_API const char* spattn_version(void);

@@ -40,7 +40,9 @@ What is computed (sources are the five pages on sparse attention):
   the top blocks chosen by the compression branch's own scores (the pooled-key
   dot products above), and a window branch; each branch has its own softmax
   and a gate weighs them: o = g_cmp o_cmp + g_sel o_sel + g_win o_win. A branch
-  with no visible entry contributes 0.
+  with no visible entry contributes 0. The pages do not fix the precision of
+  the compressed entries; they are read as stored in the cache's format: the
+  exact block mean rounded to nearest-even bf16 (or float32).
 * Page-granular selection ("Sparse Attention in 2026: Why It Finally Had to
   Be Native", the DSA list: the indexer rates every 64-token KV page, the
   attention reads the best pages plus the mandatory recent pages, whole).
@@ -299,20 +301,43 @@ def pages_set(pages: Sequence[int], p: int, P: int) -> np.ndarray:
     return s[s <= p].astype(np.int32)
 
 
-def pooled_blocks(X: np.ndarray, bs: int, n_blocks: int) -> np.ndarray:
-    """Mean of each complete block of bs rows: the compressed entries."""
-    return X[: n_blocks * bs].reshape(n_blocks, bs, X.shape[1]).mean(axis=1)
+def round_to_format(x: np.ndarray, fmt: Optional[str]) -> np.ndarray:
+    """float64 values rounded to nearest-even bf16 or float32 (returned as float64)."""
+    if fmt is None:
+        return x
+    if fmt == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    # bf16 keeps 7 of the 52 stored significand bits: round the float64 bit
+    # pattern at bit 45, ties to even (finite values in bf16's normal range)
+    bits = np.ascontiguousarray(x, dtype=np.float64).view(np.uint64)
+    lsb = (bits >> np.uint64(45)) & np.uint64(1)
+    bits = (bits + np.uint64((1 << 44) - 1) + lsb) & ~np.uint64((1 << 45) - 1)
+    return bits.view(np.float64)
+
+
+def pooled_blocks(X: np.ndarray, bs: int, n_blocks: int, fmt: Optional[str] = None) -> np.ndarray:
+    """Mean of each complete block of bs rows (the compressed entries), summed
+    with math.fsum (correctly rounded) and, with fmt, rounded to that format."""
+    out = np.empty((n_blocks, X.shape[1]))
+    for b in range(n_blocks):
+        for c in range(X.shape[1]):
+            out[b, c] = math.fsum(X[b * bs:(b + 1) * bs, c]) / bs
+    return round_to_format(out, fmt)
 
 
 def nsa_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, p: int, bs: int, blocks: Sequence[int], w: int,
-                  gates: np.ndarray, scale: float) -> np.ndarray:
+                  gates: np.ndarray, scale: float, fmt: Optional[str] = None,
+                  pooled: Optional[Tuple[np.ndarray, np.ndarray]] = None) -> np.ndarray:
     """Gated sum of the compression, selection and window branches for one
-    query head q [d] at position p (keys K, V [>= p+1, d]); gates [3]."""
+    query head q [d] at position p (keys K, V [>= p+1, d]); gates [3]; fmt:
+    the format the compressed entries are kept in; pooled: those entries
+    already formed (of at least the complete blocks up to p)."""
     out = np.zeros(K.shape[1])
     nc = eligible_blocks(p, bs)
     branches = []
     if nc:
-        branches.append((0, pooled_blocks(K, bs, nc), pooled_blocks(V, bs, nc), np.arange(nc)))
+        Kc, Vc = pooled if pooled is not None else (pooled_blocks(K, bs, nc, fmt), pooled_blocks(V, bs, nc, fmt))
+        branches.append((0, Kc[:nc], Vc[:nc], np.arange(nc)))
     sel = blocks_set(blocks, p, bs, 0)
     if len(sel):
         branches.append((1, K[: p + 1], V[: p + 1], sel))
@@ -445,12 +470,15 @@ def run(wl, inp: Dict[str, np.ndarray], rows: Iterable[Tuple[int, int]],
         if attention and wl.kind == "nsa":
             O = np.zeros((wl.Hq, wl.d))
             gates = np.asarray(inp["gates"], dtype=np.float32).astype(np.float64)
-            for h in range(wl.Hq):
-                qh = decode(Q[b, h, r], wl.dtype)
-                kvh = h // qpk
+            nc = eligible_blocks(p, wl.block_size)
+            for kvh in range(wl.Hkv):
                 Vh = decode(Vst[b, kvh, :n], wl.dtype)
-                O[h] = nsa_attention(qh, Kb[kvh], Vh, p, wl.block_size, res.blocks[(b, h, r)], wl.window,
-                                     gates[b, h, r], scale)
+                pooled = (pooled_blocks(Kb[kvh], wl.block_size, nc, wl.dtype),
+                          pooled_blocks(Vh, wl.block_size, nc, wl.dtype))
+                for h in range(kvh * qpk, (kvh + 1) * qpk):
+                    qh = decode(Q[b, h, r], wl.dtype)
+                    O[h] = nsa_attention(qh, Kb[kvh], Vh, p, wl.block_size, res.blocks[(b, h, r)], wl.window,
+                                         gates[b, h, r], scale, pooled=pooled)
             res.O[(b, r)] = O
         elif attention:
             O = np.zeros((wl.Hq, wl.d))

@@ -221,3 +221,29 @@ def test_page_select_fused_validation():
     assert call(ws_bytes=need - 1) == 3
     assert call(scores=torch.zeros(2, 8, 1, 4096)) == 1         # fused takes no scores
     assert call(idx=torch.zeros(2, 8, 1, 4, dtype=torch.int32)) == 1
+
+
+
+def test_nsa_validation():
+    q = torch.zeros(1, 2, 64, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 256, 128, dtype=torch.bfloat16)
+    blk = torch.zeros(1, 2, 64, 4, dtype=torch.int32)
+    gates = torch.zeros(1, 2, 64, 3)
+    o = torch.zeros(1, 2, 64, 128)
+    need = S.LIB.spattn_nsa_fwd_workspace(ctypes.byref(S.tensor(q)), ctypes.byref(S.tensor(k)), 64,
+                                          ctypes.byref(S.tensor(blk)), 32)
+    assert need >= 2 * 2 * 4 * 128 * 2 + 3 * 2 * 64 * 128 * 4    # pooled K, V and three branch outputs
+    ws = torch.zeros(need, dtype=torch.uint8)
+
+    def call(bs=64, b=blk, g=gates, w=32, ws_bytes=need, oo=o):
+        t = [S.tensor(x) for x in (q, k, k, b, g, oo)]
+        return S.LIB.spattn_nsa_fwd(ctypes.byref(t[0]), ctypes.byref(t[1]), ctypes.byref(t[2]), None, 0.0, bs,
+                                    ctypes.byref(t[3]), w, ctypes.byref(t[4]), ctypes.byref(t[5]), ws.data_ptr(),
+                                    ws_bytes, None)
+
+    assert call() == 4
+    assert call(bs=48) == 1                       # not a power of two
+    assert call(w=-1) == 1
+    assert call(g=torch.zeros(1, 2, 64, 2)) == 1  # three gates per row
+    assert call(b=torch.zeros(1, 1, 64, 4, dtype=torch.int32)) == 1
+    assert call(ws_bytes=need - 1) == 3

@@ -518,9 +518,25 @@ def test_nsa_pooling_is_the_block_mean():
     for blk in range(9):
         want = [sum(K[4 * blk + t][c] for t in range(4)) / 4 for c in range(K.shape[1])]
         assert np.allclose(P[blk], want, rtol=0, atol=1e-15)
-    # a block of identical rows compresses to that row
+    # a block of identical rows compresses to that row (fsum is exact here)
     K2 = np.repeat(K[:1], 8, axis=0)
-    assert np.allclose(orc.pooled_blocks(K2, 8, 1)[0], K[0], rtol=0, atol=1e-15)
+    assert np.array_equal(orc.pooled_blocks(K2, 8, 1)[0], K[0])
+
+
+def test_nsa_entries_round_like_torch():
+    """Compressed entries kept in bf16 / float32: nearest-even rounding of the
+    exact means, checked against torch's casts from float64 (a cast that does
+    not round twice) on values at and near bf16 halfway points."""
+    rng = np.random.default_rng(16)
+    x = rng.standard_normal(4000)
+    # exact bf16 halfway points and their float64 neighbours
+    base = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(rng.standard_normal(200).astype(np.float32))).astype(np.float64)
+    half = base + np.abs(base) * 2.0 ** -8
+    x = np.concatenate([x, half, np.nextafter(half, np.inf), np.nextafter(half, -np.inf)])
+    for fmt, tdt in (("bf16", torch.bfloat16), ("f32", torch.float32)):
+        got = orc.round_to_format(x.copy(), fmt)
+        ref = torch.from_numpy(x).to(tdt).to(torch.float64).numpy()
+        assert np.array_equal(got, ref), fmt
 
 
 def test_nsa_gates_pick_branches():
