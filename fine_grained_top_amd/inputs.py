@@ -173,7 +173,8 @@ def uniform01(seed: int, tid: int, shape) -> np.ndarray:
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # topk | window_global | blocks | nsa | dsa_prefill | dsa_decode | dsa_pages
+    kind: str                 # topk | window_global | blocks | nsa | dsa_prefill | dsa_decode | dsa_pages |
+                              # dsa_two_level
     B: int
     Hq: int
     Hkv: int
@@ -266,6 +267,14 @@ PAGED = _add(dataclasses.replace(DECODE, name="dsa_paged_decode", kind="dsa_page
                                  topk=0, page_size=64, top_pages=30, n_local=2))
 _add(dataclasses.replace(PAGED, name="dsa_paged_decode_small", B=3, N=9000, top_pages=6,
                          len_range=(6000, 9000)))
+# Two-level selection on the decode shapes: the 64 best 64-token blocks by
+# their mean indexer key (about 4K candidate tokens), then the top-2048 tokens.
+TWO = _add(dataclasses.replace(DECODE, name="dsa_two_level_decode", kind="dsa_two_level", seed=10,
+                               block_size=64, top_blocks=64))
+_add(dataclasses.replace(TWO, name="dsa_two_level_decode_small", B=3, N=9000, topk=512, top_blocks=16,
+                         len_range=(6000, 9000)))
+_add(dataclasses.replace(TWO, name="dsa_two_level_prefill_small", B=1, Hq=8, Hkv=2, N=700, Nq=700, H_I=4,
+                         G_sel=2, idx_k_dtype="bf16", block_size=16, top_blocks=6, topk=40, len_range=None))
 _add(dataclasses.replace(PAGED, name="dsa_paged_prefill_small", B=1, Hq=8, Hkv=2, N=700, Nq=700,
                          H_I=4, G_sel=2, idx_k_dtype="bf16", page_size=16, top_pages=5,
                          n_local=1, len_range=None))

@@ -43,6 +43,15 @@ What is computed (sources are the five pages on sparse attention):
   with no visible entry contributes 0. The pages do not fix the precision of
   the compressed entries; they are read as stored in the cache's format: the
   exact block mean rounded to nearest-even bf16 (or float32).
+* Two-level selection ("Sparse Attention Is Reshaping Production AI",
+  per-token routing: a coarse block pass finds candidate regions, a fine pass
+  picks the top-K tokens inside them). Read as: each complete block's indexer
+  key is the mean of its tokens' indexer keys, kept in float32 (a per-block
+  cache); the coarse pass scores blocks with the indexer's own score on those
+  keys and keeps the top_blocks complete past blocks by (key desc, block asc);
+  the candidates are the chosen blocks' tokens plus the query's own
+  incomplete block, and the fine pass keeps the K best candidates by (token
+  key desc, position asc).
 * Page-granular selection ("Sparse Attention in 2026: Why It Finally Had to
   Be Native", the DSA list: the indexer rates every 64-token KV page, the
   attention reads the best pages plus the mandatory recent pages, whole).
@@ -294,6 +303,20 @@ def page_select(keys: np.ndarray, p: int, P: int, top_pages: int, n_local: int) 
     return np.concatenate([chosen, local]).astype(np.int32)
 
 
+def two_level_select(block_keys: np.ndarray, token_keys: np.ndarray, p: int, bs: int, top_blocks: int,
+                     K: int) -> np.ndarray:
+    """Positions chosen by the two-level selection at query position p, ascending.
+
+    block_keys: keys of the complete blocks 0..(p+1)//bs - 1; token_keys: keys
+    of the tokens 0..p."""
+    nbe = (p + 1) // bs
+    blocks = topk(block_keys[:nbe], top_blocks)
+    cand = np.concatenate([np.arange(bs * b, bs * b + bs) for b in blocks] + [np.arange(nbe * bs, p + 1)])
+    cand = np.sort(cand).astype(np.int64)
+    chosen = topk(token_keys[cand], K)               # indices into cand, ascending = positions ascending
+    return cand[chosen].astype(np.int32)
+
+
 def pages_set(pages: Sequence[int], p: int, P: int) -> np.ndarray:
     """Every token of the listed pages, within 0..p (pages are read whole)."""
     parts = [np.arange(P * pg, P * pg + P) for pg in pages]
@@ -420,7 +443,7 @@ def run(wl, inp: Dict[str, np.ndarray], rows: Iterable[Tuple[int, int]],
         Kb = [decode(Kst[b, h, :n], wl.dtype) for h in range(wl.Hkv)]
         # visible set per query head
         S_of_head: List[np.ndarray] = [None] * wl.Hq
-        if wl.kind in ("topk", "dsa_prefill", "dsa_decode", "dsa_pages"):
+        if wl.kind in ("topk", "dsa_prefill", "dsa_decode", "dsa_pages", "dsa_two_level"):
             qi = decode(inp["q_idx"][b, r], wl.idx_q_dtype)            # [H_I, d_I]
             hpg = wl.H_I // wl.G_sel
             w = np.asarray(inp["w"], dtype=np.float32).astype(np.float64)
@@ -435,6 +458,14 @@ def run(wl, inp: Dict[str, np.ndarray], rows: Iterable[Tuple[int, int]],
                     pg = page_select(keys, p, wl.page_size, wl.top_pages, wl.n_local)
                     res.blocks[(b, g, r)] = pg
                     S = pages_set(pg, p, wl.page_size)
+                elif wl.kind == "dsa_two_level":
+                    nbe = n // wl.block_size
+                    Kp = pooled_blocks(Ki, wl.block_size, nbe, "f32")
+                    if wl.score_mode == "dot":
+                        bkeys = keys_dot(qi[g * hpg], Kp)
+                    else:
+                        bkeys = keys_weighted_relu(qi[g * hpg:(g + 1) * hpg], w[g * hpg:(g + 1) * hpg], Kp)
+                    S = two_level_select(bkeys, keys, p, wl.block_size, wl.top_blocks, wl.topk)
                 else:
                     S = topk(keys, wl.topk)
                 res.sets[(b, g, r)] = S

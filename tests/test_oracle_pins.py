@@ -562,3 +562,42 @@ def test_nsa_gates_pick_branches():
     early = orc.nsa_attention(q, K, V, 2, bs, [], w, g, sc)
     w0, _ = orc.masked_attention(q[None], K[:3], V[:3], np.arange(0, 3), sc)
     assert np.max(np.abs(early - 0.5 * w0[0])) < 1e-12
+
+
+
+# ---------------------------------------------------------------- two-level selection
+@pytest.mark.parametrize("seed", range(4))
+def test_two_level_brute_force(seed):
+    """Blocks ranked by brute force, candidates listed by hand, tokens ranked
+    by brute force; every chosen token is a candidate."""
+    rng = np.random.default_rng(300 + seed)
+    n = int(rng.integers(5, 80))
+    tk = rng.integers(-4, 5, size=n).astype(np.float32)
+    for bs in (1, 4, 8):
+        for p in sorted({0, n // 2, n - 1}):
+            nbe = (p + 1) // bs
+            bk = rng.integers(-3, 4, size=nbe).astype(np.float32)
+            for nb, K in ((1, 3), (2, 5), (50, 200)):
+                blocks = _brute_topk(list(bk), nb)
+                cand = sorted([j for b in blocks for j in range(bs * b, bs * b + bs)] + list(range(nbe * bs, p + 1)))
+                order = sorted(cand, key=lambda j: (-float(tk[j]), j))[:K]
+                got = orc.two_level_select(bk, tk[: p + 1], p, bs, nb, K)
+                assert list(got) == sorted(order), (bs, p, nb, K)
+
+
+def test_two_level_with_every_block_is_token_topk():
+    """With at least as many blocks as exist the candidates are all tokens:
+    two-level selection equals token top-K."""
+    rng = np.random.default_rng(310)
+    tk = rng.standard_normal(300).astype(np.float32)
+    for p in (0, 63, 64, 200, 299):
+        bk = rng.standard_normal((p + 1) // 64).astype(np.float32)
+        assert np.array_equal(orc.two_level_select(bk, tk[: p + 1], p, 64, 100, 37), orc.topk(tk[: p + 1], 37))
+
+
+def test_two_level_hand_worked():
+    """p = 9, blocks of 4 (complete: 0 and 1, tokens 8..9 in the open block),
+    block keys [5, 7]: one block keeps block 1; candidates 4..7 and 8, 9."""
+    tk = np.array([9, 9, 9, 9, 1, 3, 2, 3, 0, 2], dtype=np.float32)
+    got = orc.two_level_select(np.array([5, 7], np.float32), tk, 9, 4, 1, 3)
+    assert list(got) == [5, 6, 7]          # keys 3, 3, then the tie of 2 at 6 and 9 goes to 6
