@@ -70,6 +70,13 @@ def algorithmic(wl, inp, hp, fused):
         flops_att = 4.0 * pairs * wl.d
         out["attention"] = {"bytes": gath + qkv_out, "flops": flops_att,
                             "bound": "hbm" if wl.Nq == 1 else "mfma"}
+        if wl.kind == "dsa_two_level":
+            # block keys of the complete blocks, then the candidates' token keys
+            nbe = np.stack([(L - wl.Nq + np.arange(wl.Nq) + 1) // wl.block_size for L in lens])   # [B, Nq]
+            nopen = np.stack([L - wl.Nq + np.arange(wl.Nq) + 1 for L in lens]) - nbe * wl.block_size
+            ncand = np.minimum(nbe, wl.top_blocks) * wl.block_size + nopen
+            rd = float((nbe * wl.d_I * 4 + ncand * wl.d_I * kb).sum()) * wl.G_sel
+            out["two_level_select"] = {"bytes": rd + idx_bytes, "rows": wl.B * wl.G_sel * wl.Nq}
         if wl.kind == "dsa_pages":
             # page lists: every listed page is read whole (cut at the query position)
             P = wl.page_size
@@ -193,6 +200,8 @@ def main():
         stages = [("index_page_fused", lambda hp: hp.page_select_fused()), ("attention", lambda hp: hp.attention())]
     elif wl.H_I and fused:
         stages = [("index_topk_fused", lambda hp: hp.topk_fused()), ("attention", lambda hp: hp.attention())]
+    elif wl.H_I and wl.kind == "dsa_two_level":
+        stages = [("two_level_select", lambda hp: hp.topk_two_level()), ("attention", lambda hp: hp.attention())]
     elif wl.H_I and wl.kind == "dsa_pages":
         stages = [("index_scores", lambda hp: hp.index_scores()), ("page_select", lambda hp: hp.page_select()),
                   ("attention", lambda hp: hp.attention())]
@@ -320,6 +329,8 @@ def main():
         "data": "synthetic",
         "path": (("fused indexer+page selection" if fused else "indexer scores, certified page selection")
                  + ", attention over a paged KV cache" if wl.kind == "dsa_pages" else
+                 "two-level block-then-token selection (block-key cache formed before timing)"
+                 if wl.kind == "dsa_two_level" else
                  "fused indexer+top-K" if fused else "separate indexer and top-K calls"),
         "config": {"workload": wl.name, "B": wl.B, "ctx_capacity": wl.N, "Nq": wl.Nq, "Hq": wl.Hq,
                    "Hkv": wl.Hkv, "d": wl.d, "H_I": wl.H_I, "d_I": wl.d_I, "topk": wl.topk,
@@ -332,6 +343,8 @@ def main():
     }
     if wl.page_size:
         out["config"].update({"page_size": wl.page_size, "top_pages": wl.top_pages, "n_local": wl.n_local})
+    if wl.kind in ("dsa_two_level", "nsa"):
+        out["config"].update({"block_size": wl.block_size, "top_blocks": wl.top_blocks})
     print(json.dumps(out), flush=True)
 
 

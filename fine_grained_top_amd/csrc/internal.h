@@ -76,6 +76,17 @@ struct PageSelParams {
 size_t page_select_ws_bytes(const PageSelParams& p);
 hipError_t launch_page_select(const PageSelParams& p, hipStream_t st);
 
+// ---------------------------------------------------------------- two-level selection
+constexpr int kTlMaxCand = 8192;   // blocks per row, and candidate tokens per row
+struct TwoLevelParams {
+  TopkParams t;            // token indexer (t.ix), shapes, ctx_len, output list [B, G, Nq, K], counts
+  float* kp;               // block indexer keys [B, ctx >> lgbs, G_k, d_I] f32
+  int64_t kps[4];
+  int lgbs, nb;            // log2 block size, blocks kept by the first pick
+};
+hipError_t launch_pool_index_keys(const TwoLevelParams& p, hipStream_t st);
+hipError_t launch_two_level(const TwoLevelParams& p, hipStream_t st);
+
 // ---------------------------------------------------------------- block select
 struct BlockSelectParams {
   View4 q;                 // [B, Hq, Nq, d]

@@ -375,6 +375,73 @@ SPATTN_API int spattn_page_select(const spattn_tensor* scores, const float* err,
   return launched(sp::launch_page_select(q, (hipStream_t)stream));
 }
 
+// ------------------------------------------------------------------ two-level selection
+static int two_level_setup(const spattn_indexer* ix, const spattn_tensor* kp, const int32_t* ctx_len,
+                           int32_t block_size, sp::TwoLevelParams& q) {
+  int rc;
+  q = sp::TwoLevelParams{};
+  int64_t B, Nq, ctx, G;
+  if ((rc = check_indexer(ix, &B, &Nq, &ctx, &G))) return rc;
+  q.lgbs = log2_pow2(block_size, 4096);
+  if (q.lgbs < 0) return fail(SPATTN_ERR_INVALID_ARG, "block_size must be a power of two in 1..4096");
+  if ((ctx >> q.lgbs) > sp::kTlMaxCand) return fail(SPATTN_ERR_UNSUPPORTED, "more than %d blocks per request", sp::kTlMaxCand);
+  if ((rc = check_tensor(kp, "k_blocks", 4, true))) return rc;
+  if (kp->dtype != SPATTN_F32) return fail(SPATTN_ERR_INVALID_ARG, "k_blocks must be f32");
+  if (kp->shape[0] != B || kp->shape[1] < (ctx >> q.lgbs) || kp->shape[2] != ix->k_idx.shape[2] ||
+      kp->shape[3] != ix->k_idx.shape[3])
+    return fail(SPATTN_ERR_INVALID_ARG, "k_blocks must be [B, ctx / block_size, G_k, d_I]");
+  q.t.ix = indexer_params(ix, ctx_len);
+  q.t.certified = true;
+  q.t.B = (int)B;
+  q.t.G = (int)G;
+  q.t.Nq = (int)Nq;
+  q.t.ctx = (int)ctx;
+  q.t.ctx_len = ctx_len;
+  q.kp = (float*)kp->data;
+  for (int i = 0; i < 4; ++i) q.kps[i] = kp->stride[i];
+  return SPATTN_OK;
+}
+
+SPATTN_API int spattn_pool_index_keys(const spattn_indexer* ix, const int32_t* ctx_len, int32_t block_size,
+                                      const spattn_tensor* k_blocks_out, void* stream) {
+  sp::TwoLevelParams q;
+  int rc;
+  if ((rc = two_level_setup(ix, k_blocks_out, ctx_len, block_size, q))) return rc;
+  if ((rc = device_ok())) return rc;
+  return launched(sp::launch_pool_index_keys(q, (hipStream_t)stream));
+}
+
+SPATTN_API size_t spattn_topk_two_level_workspace(const spattn_indexer* ix, const spattn_tensor* k_blocks,
+                                                  int32_t block_size, int32_t top_blocks, int32_t k) {
+  sp::TwoLevelParams q;
+  if (two_level_setup(ix, k_blocks, nullptr, block_size, q) || top_blocks < 1 || k < 1) return (size_t)-1;
+  return 0;
+}
+
+SPATTN_API int spattn_topk_two_level(const spattn_indexer* ix, const spattn_tensor* k_blocks, const int32_t* ctx_len,
+                                     int32_t block_size, int32_t top_blocks, int32_t k, const spattn_tensor* idx_out,
+                                     int32_t* count_out, void* ws, size_t ws_bytes, void* stream) {
+  sp::TwoLevelParams q;
+  int rc;
+  (void)ws;
+  (void)ws_bytes;
+  if ((rc = two_level_setup(ix, k_blocks, ctx_len, block_size, q))) return rc;
+  if (top_blocks < 1 || k < 1 || k > 16384) return fail(SPATTN_ERR_INVALID_ARG, "need top_blocks >= 1 and 1 <= k <= 16384");
+  if (((int64_t)top_blocks + 1) << q.lgbs > sp::kTlMaxCand)
+    return fail(SPATTN_ERR_UNSUPPORTED, "(top_blocks + 1) * block_size must be <= %d", sp::kTlMaxCand);
+  if ((rc = check_tensor(idx_out, "idx_out", 4, false))) return rc;
+  if (idx_out->dtype != SPATTN_I32) return fail(SPATTN_ERR_INVALID_ARG, "idx_out must be int32");
+  if (idx_out->shape[0] != q.t.B || idx_out->shape[1] != q.t.G || idx_out->shape[2] != q.t.Nq || idx_out->shape[3] != k)
+    return fail(SPATTN_ERR_INVALID_ARG, "idx_out must be [B, G, Nq, k]");
+  q.t.idx = (int32_t*)idx_out->data;
+  for (int i = 0; i < 4; ++i) q.t.is[i] = idx_out->stride[i];
+  q.t.count = count_out;
+  q.t.K = k;
+  q.nb = top_blocks;
+  if ((rc = device_ok())) return rc;
+  return launched(sp::launch_two_level(q, (hipStream_t)stream));
+}
+
 // ------------------------------------------------------------------ block select
 static int check_qk(const spattn_tensor* q, const spattn_tensor* k) {
   int rc;

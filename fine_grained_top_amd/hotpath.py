@@ -4,6 +4,7 @@ Orchestration only: it moves the seeded inputs to the device, owns the output
 and workspace buffers, and calls the libspattn entry points in order
 (indexer scores -> certified top-K -> sparse attention; indexer scores ->
 certified page selection -> attention over the pages of a paged KV cache;
+block keys -> two-level block-then-token selection -> sparse attention;
 block selection -> block-sparse attention; block selection -> three-branch
 NSA attention; or a fixed window + global pattern).
 """
@@ -65,6 +66,13 @@ class HotPath:
             self.count = torch.empty(wl.B, wl.G_sel, wl.Nq, dtype=torch.int32, device=device)
             if wl.kind == "dsa_pages":
                 self.sel = S.selection(S.SEL_PAGES, self.idx, block_size=wl.page_size)
+            elif wl.kind == "dsa_two_level":
+                self.sel = S.selection(S.SEL_INDEX, self.idx)
+                self.fused = False
+                # the block-key cache, formed once (a decode loop extends it a block at a time)
+                self.k_blocks = torch.empty(wl.B, wl.N // wl.block_size, wl.G_k, wl.d_I, dtype=torch.float32,
+                                            device=device)
+                S.spattn_pool_index_keys(self.ix, self.ctx_len, wl.block_size, self.k_blocks)
             else:
                 self.sel = S.selection(S.SEL_INDEX, self.idx)
                 if self.fused and S.LIB.spattn_topk_workspace(None, S.ctypes.byref(self.ix), wl.topk,
@@ -128,6 +136,13 @@ class HotPath:
         S.spattn_topk(None, None, self.ix, self.ctx_len, self.wl.topk, S.TOPK_FUSED_INDEX,
                       self.idx, self.count, self.ws, stream)
 
+    def pool_blocks(self, stream=None):
+        S.spattn_pool_index_keys(self.ix, self.ctx_len, self.wl.block_size, self.k_blocks, stream)
+
+    def topk_two_level(self, stream=None):
+        S.spattn_topk_two_level(self.ix, self.k_blocks, self.ctx_len, self.wl.block_size, self.wl.top_blocks,
+                                self.wl.topk, self.idx, self.count, None, stream)
+
     def page_select(self, stream=None):
         S.spattn_page_select(self.scores, self.err, self.ix, self.ctx_len, self.wl.page_size, self.wl.top_pages,
                              self.wl.n_local, S.TOPK_CERTIFIED, self.idx, self.count, self.ws, stream)
@@ -156,6 +171,8 @@ class HotPath:
             self.page_select_fused(stream)
         elif self.wl.H_I and self.fused:
             self.topk_fused(stream)
+        elif self.wl.H_I and self.wl.kind == "dsa_two_level":
+            self.topk_two_level(stream)
         elif self.wl.H_I:
             self.index_scores(stream)
             if self.wl.kind == "dsa_pages":

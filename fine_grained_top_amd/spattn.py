@@ -66,6 +66,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "spattn_page_select_workspace": (sz, [P(Tensor), P(Indexer), i32, i32, i32, u32]),
         "spattn_page_select": (ctypes.c_int, [P(Tensor), vp, P(Indexer), vp, i32, i32, i32, u32, P(Tensor), vp,
                                               vp, sz, vp]),
+        "spattn_pool_index_keys": (ctypes.c_int, [P(Indexer), vp, i32, P(Tensor), vp]),
+        "spattn_topk_two_level_workspace": (sz, [P(Indexer), P(Tensor), i32, i32, i32]),
+        "spattn_topk_two_level": (ctypes.c_int, [P(Indexer), P(Tensor), vp, i32, i32, i32, P(Tensor), vp, vp, sz,
+                                                 vp]),
         "spattn_block_select_workspace": (sz, [P(Tensor), P(Tensor), i32, i32]),
         "spattn_block_select": (ctypes.c_int, [P(Tensor), P(Tensor), vp, i32, i32, P(Tensor), vp, vp, sz, vp]),
         "spattn_sparse_attn_fwd_workspace": (sz, [P(Tensor), P(Tensor), P(Selection)]),
@@ -208,6 +212,21 @@ def spattn_page_select(scores: Optional[torch.Tensor], err: Optional[torch.Tenso
     _check(LIB.spattn_page_select(scp, _ptr(err), ixp, _ptr(ctx_len), page_size, top_pages, n_local,
                                   flags, ctypes.byref(io), _ptr(pg_count_out), _ptr(ws),
                                   0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def spattn_pool_index_keys(ix: Indexer, ctx_len: Optional[torch.Tensor], block_size: int,
+                           k_blocks_out: torch.Tensor, stream=None) -> None:
+    _check(LIB.spattn_pool_index_keys(ctypes.byref(ix), _ptr(ctx_len), block_size, ctypes.byref(tensor(k_blocks_out)),
+                                      _stream(stream)))
+
+
+def spattn_topk_two_level(ix: Indexer, k_blocks: torch.Tensor, ctx_len: Optional[torch.Tensor], block_size: int,
+                          top_blocks: int, k: int, idx_out: torch.Tensor, count_out: Optional[torch.Tensor] = None,
+                          ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    tb, io = tensor(k_blocks), tensor(idx_out)
+    _check(LIB.spattn_topk_two_level(ctypes.byref(ix), ctypes.byref(tb), _ptr(ctx_len), block_size, top_blocks, k,
+                                     ctypes.byref(io), _ptr(count_out), _ptr(ws), 0 if ws is None else ws.numel(),
+                                     _stream(stream)))
 
 
 def spattn_block_select(q: torch.Tensor, k: torch.Tensor, ctx_len: Optional[torch.Tensor], block_size: int,

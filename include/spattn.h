@@ -229,6 +229,38 @@ SPATTN_API int spattn_page_select(const spattn_tensor* scores, const float* err,
                                   void* stream);
 
 /* ------------------------------------------------------------------------
+ * Two-level selection.
+ * Source: "Sparse Attention Is Reshaping Production AI", per-token routing
+ * (a coarse block pass identifies candidate regions cheaply, a fine pass
+ * picks the top-K tokens from within them; together they beat either alone).
+ *
+ * spattn_pool_index_keys: k_blocks_out f32 [B, ctx / block_size, G_k, d_I]
+ *   receives, for every complete block of each request, the mean of its
+ *   tokens' indexer keys (summed in float64, rounded once to float32). A
+ *   decode loop keeps this cache and extends it one block at a time.
+ * spattn_topk_two_level: row (b,g,r) at position p scores its complete past
+ *   blocks {beta : block_size*beta + block_size - 1 <= p} with the indexer's
+ *   own score (ix's queries and weights on k_blocks) and keeps the
+ *   min(top_blocks, #blocks) best by (key desc, block asc); the candidates are
+ *   their tokens plus the tokens of p's own incomplete block; the min(k,
+ *   #candidates) best candidates by (token key desc, position asc) are written
+ *   ascending to idx_out int32 [B, G, Nq, k], -1 padded (counts optional).
+ *   Keys are exact as for SPATTN_TOPK_CERTIFIED (float32 nearest to the exact
+ *   score; near-ties rescored exactly), so the result equals exhaustive
+ *   two-level selection on exact keys.
+ *  Limits: block_size a power of two; ctx / block_size <= 8192;
+ *  (top_blocks + 1) * block_size <= 8192; k <= 16384. No workspace.
+ * ---------------------------------------------------------------------- */
+SPATTN_API int spattn_pool_index_keys(const spattn_indexer* ix, const int32_t* ctx_len, int32_t block_size,
+                                      const spattn_tensor* k_blocks_out, void* stream);
+SPATTN_API size_t spattn_topk_two_level_workspace(const spattn_indexer* ix, const spattn_tensor* k_blocks,
+                                                  int32_t block_size, int32_t top_blocks, int32_t k);
+SPATTN_API int spattn_topk_two_level(const spattn_indexer* ix, const spattn_tensor* k_blocks,
+                                     const int32_t* ctx_len, int32_t block_size, int32_t top_blocks,
+                                     int32_t k, const spattn_tensor* idx_out, int32_t* count_out,
+                                     void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * spattn_block_select — block routing for block-sparse attention.
  * Source: "Sparse Attention Is Reshaping Production AI", Learned Block
  * Routing (keys mean-pooled per block, unscaled dot product with the query,

@@ -247,3 +247,27 @@ def test_nsa_validation():
     assert call(g=torch.zeros(1, 2, 64, 2)) == 1  # three gates per row
     assert call(b=torch.zeros(1, 1, 64, 4, dtype=torch.int32)) == 1
     assert call(ws_bytes=need - 1) == 3
+
+
+
+def test_two_level_validation():
+    q = torch.zeros(2, 1, 32, 64, dtype=torch.bfloat16)
+    k = torch.zeros(2, 4096, 1, 64, dtype=torch.uint8)
+    w = torch.zeros(2, 1, 32)
+    ix = S.indexer(q, k, w, S.SCORE_WEIGHTED_RELU, 4)
+    kb = torch.zeros(2, 64, 1, 64)
+    io = torch.zeros(2, 8, 1, 100, dtype=torch.int32)
+
+    def call(bs=64, nb=8, K=100, blocks=kb, idx=io):
+        return S.LIB.spattn_topk_two_level(ctypes.byref(ix), ctypes.byref(S.tensor(blocks)), None, bs, nb, K,
+                                           ctypes.byref(S.tensor(idx)), None, None, 0, None)
+
+    assert S.LIB.spattn_topk_two_level_workspace(ctypes.byref(ix), ctypes.byref(S.tensor(kb)), 64, 8, 100) == 0
+    assert call() == 4                                    # valid: reaches the device check
+    assert call(bs=48) == 1
+    assert call(nb=0) == 1
+    assert call(nb=200) == 2                              # (top_blocks + 1) * block_size > 8192
+    assert call(blocks=torch.zeros(2, 63, 1, 64)) == 1    # fewer block rows than ctx / block_size
+    assert call(blocks=kb.to(torch.bfloat16)) == 1        # block keys are f32
+    assert call(idx=torch.zeros(2, 8, 1, 99, dtype=torch.int32)) == 1
+    assert S.LIB.spattn_pool_index_keys(ctypes.byref(ix), None, 64, ctypes.byref(S.tensor(kb)), None) == 4

@@ -133,7 +133,8 @@ def test_tiny_fp32_full():
 
 @pytest.mark.parametrize("name", ["dsa_decode_small", "dsa_prefill_small", "window_global_small",
                                   "block_sparse_small", "tiny_topk_f32_small", "dsa_paged_decode_small",
-                                  "dsa_paged_prefill_small", "window_stride_small", "nsa_blocks_small"])
+                                  "dsa_paged_prefill_small", "window_stride_small", "nsa_blocks_small",
+                                  "dsa_two_level_decode_small", "dsa_two_level_prefill_small"])
 def test_small_workload(name):
     wl = gen.WORKLOADS[name]
     inp = gen.generate(wl)
@@ -820,3 +821,61 @@ def test_nsa_branches_one_at_a_time():
             worst = max(worst, float(np.abs(got - want).max()))
     say(f"  compression branch vs oracle {worst:.3e}")
     assert worst <= 2e-3
+
+
+def test_two_level_decode_full_every_row():
+    wl = gen.WORKLOADS["dsa_two_level_decode"]
+    say("[gpu] generating dsa_two_level_decode inputs")
+    inp = gen.generate(wl)
+    hp = run(wl, inp)
+    rows = _all_rows(wl, inp)
+    res = oracle_rows(wl, inp, rows)
+    check_sets(hp, res, rows, wl)
+    check_out(hp, res, rows, 2e-3)
+
+
+@pytest.mark.parametrize("bs,nb,K", [(4, 3, 10), (4, 30, 50), (8, 2, 7), (1, 12, 12), (16, 1, 40)])
+def test_two_level_certified_near_ties(bs, nb, K):
+    """Token and block keys at and a hair off float32 halfway points (the
+    second product of +-2^-70 needs the wide accumulator), f32 DOT indexer:
+    both picks against the oracle's exact keys; also top_blocks beyond the
+    blocks and K beyond the candidates."""
+    import oracle as orc
+    sp = S()
+    say(f"[gpu] two-level near ties bs={bs} nb={nb} K={K}")
+    d, ctx, Nq = 8, 96, 4
+    a = np.float32(1.0 + 2.0 ** -12)
+    t = np.float32(2.0 ** -35)
+    q = np.zeros((1, Nq, 1, d), np.float32)
+    q[0, :, 0, 0] = a
+    q[0, :, 0, 1] = t
+    k = np.zeros((1, ctx, 1, d), np.float32)
+    for j in range(ctx):
+        kind = (j * 7) % 6
+        if kind == 0:
+            k[0, j, 0, 0] = np.float32(1.0 + 2.0 ** -10)
+        elif kind == 1:
+            k[0, j, 0, 0] = np.float32(1.0)
+        else:
+            k[0, j, 0, 0] = a
+            k[0, j, 0, 1] = [t, -t, np.float32(0.0), t][kind - 2]
+    qt, kt = torch.from_numpy(q).cuda(), torch.from_numpy(k).cuda()
+    ix = sp.indexer(qt, kt, None, sp.SCORE_DOT, 1)
+    kb = torch.empty(1, ctx // bs, 1, d, device="cuda")
+    sp.spattn_pool_index_keys(ix, None, bs, kb)
+    idx = torch.full((1, 1, Nq, K), 7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((1, 1, Nq), 7, dtype=torch.int32, device="cuda")
+    sp.spattn_topk_two_level(ix, kb, None, bs, nb, K, idx, cnt)
+    torch.cuda.synchronize()
+    got, gc = idx.cpu().numpy()[0, 0], cnt.cpu().numpy()[0, 0]
+    k64 = k[0, :, 0].astype(np.float64)
+    for r in range(Nq):
+        p = ctx - Nq + r
+        q64 = q[0, r, 0].astype(np.float64)
+        tk = orc.keys_dot(q64, k64[: p + 1])
+        nbe = (p + 1) // bs
+        bk = orc.keys_dot(q64, orc.pooled_blocks(k64, bs, nbe, "f32"))
+        want = orc.two_level_select(bk, tk, p, bs, nb, K)
+        assert gc[r] == len(want), (r, gc[r], len(want))
+        assert np.array_equal(got[r, : len(want)], want), r
+        assert np.all(got[r, len(want):] == -1)
