@@ -394,6 +394,33 @@ def masked_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, S: np.ndarray,
     return O, lse
 
 
+def masked_attention_grads(q: np.ndarray, K: np.ndarray, V: np.ndarray, S: np.ndarray, scale: float,
+                           dO: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of sum(dO * O) for O = masked_attention(q, K, V, S).
+
+    q, dO [H, d] (heads that share K and V and the visible set); K, V [n, d].
+    With P the masked softmax: dV = P^T dO, dP = dO V^T, D = rowsum(dO * O),
+    dS = P * (dP - D), dq = scale dS K, dK = scale dS^T q ("Sparse Attention
+    in 2026", natively trainable sparsity: the backward runs over the same
+    visible set). An empty visible set has zero gradients.
+    """
+    H, n = q.shape[0], K.shape[0]
+    if len(S) == 0:
+        return np.zeros_like(q), np.zeros((n, K.shape[1])), np.zeros((n, V.shape[1]))
+    z = (q @ K.T) * scale
+    mask = np.zeros(n, dtype=bool)
+    mask[S] = True
+    z = np.where(mask[None, :], z, -np.inf)
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    P = e / e.sum(axis=1, keepdims=True)
+    O = P @ V
+    dV = P.T @ dO
+    dP = dO @ V.T
+    D = (dO * O).sum(axis=1, keepdims=True)
+    dS = P * (dP - D)
+    return scale * dS @ K, scale * dS.T @ q, dV
+
+
 def softmax_rows(q: np.ndarray, K: np.ndarray, S: np.ndarray, scale: float) -> np.ndarray:
     """The masked softmax probabilities (for checking that rows sum to one)."""
     z = (q @ K.T) * scale

@@ -601,3 +601,34 @@ def test_two_level_hand_worked():
     tk = np.array([9, 9, 9, 9, 1, 3, 2, 3, 0, 2], dtype=np.float32)
     got = orc.two_level_select(np.array([5, 7], np.float32), tk, 9, 4, 1, 3)
     assert list(got) == [5, 6, 7]          # keys 3, 3, then the tie of 2 at 6 and 9 goes to 6
+
+
+
+# ---------------------------------------------------------------- backward
+@pytest.mark.parametrize("seed", range(3))
+def test_attention_grads_match_torch_autograd(seed):
+    """dq, dK, dV of the masked attention against torch autograd in float64
+    (softmax over the visible set, everything else masked), including a
+    visible set of one key and an empty one."""
+    rng = np.random.default_rng(400 + seed)
+    H, n, d = 3, 37, 16
+    q, dO = rng.standard_normal((H, d)), rng.standard_normal((H, d))
+    K, V = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    scale = 1 / math.sqrt(d)
+    for S in (np.sort(rng.choice(n, 11, replace=False)), np.arange(n), np.array([5]), np.array([], dtype=np.int64)):
+        dq, dK, dV = orc.masked_attention_grads(q, K, V, S, scale, dO)
+        if len(S) == 0:
+            assert not dq.any() and not dK.any() and not dV.any()
+            continue
+        tq, tK, tV = (torch.tensor(x, requires_grad=True) for x in (q, K, V))
+        mask = torch.zeros(n, dtype=torch.bool)
+        mask[torch.from_numpy(S)] = True
+        o = torch.nn.functional.scaled_dot_product_attention(tq[None], tK[None], tV[None], attn_mask=mask[None, None, :],
+                                                             scale=scale)[0]
+        (o * torch.from_numpy(dO)).sum().backward()
+        assert np.max(np.abs(dq - tq.grad.numpy())) < 1e-12
+        assert np.max(np.abs(dK - tK.grad.numpy())) < 1e-12
+        assert np.max(np.abs(dV - tV.grad.numpy())) < 1e-12
+        # keys outside the visible set get no gradient
+        outside = np.setdiff1d(np.arange(n), S)
+        assert not dK[outside].any() and not dV[outside].any()
