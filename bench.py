@@ -99,6 +99,10 @@ def algorithmic(wl, inp, hp, fused):
         # a dilated stride makes every row see ~p/stride keys: the products, not the bytes, bound it
         out["attention"] = {"bytes": kv + qkv_out, "flops": 4.0 * pairs * wl.d,
                             "bound": "mfma" if wl.stride else "hbm"}
+        if wl.backward:
+            # q, k, v, O, dO read once; dq, dk, dv written once; 8 flops per (pair, dim): s, dp, dq, dk, dv
+            gbytes = wl.B * (wl.Hq * wl.Nq * wl.d * (e + 4 + 4 + 4 + 4) + wl.Hkv * wl.N * wl.d * (2 * e + 8))
+            out["attention_bwd"] = {"bytes": gbytes, "flops": 8.0 * pairs * wl.d, "bound": "mfma"}
     elif wl.kind == "nsa":
         # three branches: pooled entries of complete blocks, the chosen blocks' tokens, the window
         blk = hp.idx.cpu().numpy().astype(np.int64)          # [B, Hq, Nq, nb]
@@ -212,6 +216,8 @@ def main():
         stages = [("block_select", lambda hp: hp.block_select()), ("attention", lambda hp: hp.attention())]
     else:
         stages = [("attention", lambda hp: hp.attention())]
+    if wl.backward:
+        stages.append(("attention_bwd", lambda hp: hp.attention_bwd()))
 
     def step(i, ev=None):
         hp = paths[i % len(paths)]

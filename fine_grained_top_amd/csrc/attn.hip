@@ -167,6 +167,99 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnParams a) {
   if (a.lse && lane == 0) a.lse[((int64_t)b * a.Hq + h) * a.Nq + r] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
+// ---------------------------------------------------------------- backward
+// Gradients of sum(dO * O) over the same visible set, float32 (any mode):
+// one wave per (row, head) walks the row's visible keys 64 at a time; lanes
+// score them (s = q.k, dp = dO.v), form p = exp(s * scale - lse) and
+// ds = p (dp - D) with D = dO.O; then, key by key, the lanes (one per
+// dimension) add ds * scale * k to dq and add the key's dk and dv shares
+// (ds * scale * q and p * dO) with float atomics, since a key's gradient
+// gathers contributions from every row and head that sees it.
+__global__ __launch_bounds__(256) void attn_bwd_zero_kernel(AttnParams a, AttnBwd g) {
+  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  for (int c = threadIdx.x; c < a.d; c += blockDim.x) {
+    g.dk[b * g.dks[0] + h * g.dks[1] + (int64_t)j * g.dks[2] + c] = 0.f;
+    g.dv[b * g.dvs[0] + h * g.dvs[1] + (int64_t)j * g.dvs[2] + c] = 0.f;
+  }
+}
+
+__global__ __launch_bounds__(64) void attn_bwd_generic_kernel(AttnParams a, AttnBwd g) {
+  const int r = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int L = min(a.ctx_len ? a.ctx_len[b] : a.ctx, a.ctx);
+  const int pos = L - a.Nq + r;
+  const int kvh = h / (a.Hq / a.Hkv);
+  Visible vis;
+  vis.init(a, b, h, r, pos);
+  __shared__ float qs[128], dos[128], ps[64], dss[64];
+  __shared__ int js[64];
+  const int64_t qb = b * a.q.s[0] + h * a.q.s[1] + r * a.q.s[2];
+  const float* dOr = g.dO + b * g.dos[0] + h * g.dos[1] + r * g.dos[2];
+  const float* Or = g.o + b * g.os[0] + h * g.os[1] + r * g.os[2];
+  float dd = 0.f;
+  for (int c = lane; c < a.d; c += 64) {
+    qs[c] = ldv(a.q.p, a.q.dt, qb + c);
+    dos[c] = dOr[c];
+    dd = fmaf(dOr[c], Or[c], dd);
+  }
+  const float D = wave_sum(dd);
+  const float lse = g.lse[((int64_t)b * a.Hq + h) * a.Nq + r];
+  __syncthreads();
+  float acc0 = 0.f, acc1 = 0.f;
+  const int64_t dkb = b * g.dks[0] + kvh * g.dks[1];
+  const int64_t dvb = b * g.dvs[0] + kvh * g.dvs[1];
+  if (lse > -INFINITY) {
+    for (int t0 = 0; t0 < vis.count; t0 += 64) {
+      const int t = t0 + lane;
+      const int j = t < vis.count ? vis.key(t) : -1;
+      float p = 0.f, ds = 0.f;
+      if (j >= 0) {
+        const int64_t kr = kv_row(a, a.k, b, kvh, j), vr = kv_row(a, a.v, b, kvh, j);
+        float sdot = 0.f, dp = 0.f;
+        for (int c = 0; c < a.d; ++c) {
+          sdot = fmaf(qs[c], ldv(a.k.p, a.k.dt, kr + c), sdot);
+          dp = fmaf(dos[c], ldv(a.v.p, a.v.dt, vr + c), dp);
+        }
+        p = expf(sdot * a.scale - lse);
+        ds = p * (dp - D) * a.scale;
+      }
+      ps[lane] = p;
+      dss[lane] = ds;
+      js[lane] = j;
+      __syncthreads();
+      const int nt = min(64, vis.count - t0);
+      for (int u = 0; u < nt; ++u) {
+        const int ju = js[u];
+        if (ju < 0) continue;
+        const float pu = ps[u], dsu = dss[u];
+        const int64_t kr = kv_row(a, a.k, b, kvh, ju);
+        if (lane < a.d) {
+          acc0 = fmaf(dsu, ldv(a.k.p, a.k.dt, kr + lane), acc0);
+          atomicAdd(&g.dk[dkb + (int64_t)ju * g.dks[2] + lane], dsu * qs[lane]);
+          atomicAdd(&g.dv[dvb + (int64_t)ju * g.dvs[2] + lane], pu * dos[lane]);
+        }
+        if (lane + 64 < a.d) {
+          acc1 = fmaf(dsu, ldv(a.k.p, a.k.dt, kr + lane + 64), acc1);
+          atomicAdd(&g.dk[dkb + (int64_t)ju * g.dks[2] + lane + 64], dsu * qs[lane + 64]);
+          atomicAdd(&g.dv[dvb + (int64_t)ju * g.dvs[2] + lane + 64], pu * dos[lane + 64]);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  float* dq = g.dq + b * g.dqs[0] + h * g.dqs[1] + r * g.dqs[2];
+  if (lane < a.d) dq[lane] = acc0;
+  if (lane + 64 < a.d) dq[lane + 64] = acc1;
+}
+
+hipError_t launch_attention_bwd(const AttnParams& a, const AttnBwd& g, hipStream_t st) {
+  hipLaunchKernelGGL(attn_bwd_zero_kernel, dim3(a.ctx, a.Hkv, a.B), dim3(128), 0, st, a, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_generic_kernel, dim3(a.Nq, a.Hq, a.B), dim3(64), 0, st, a, g);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- MFMA gather
 constexpr int kVStride = 132;   // per-wave staging area: 32 rows of 264 B (rows are used at 256 B)
 typedef short v4i16 __attribute__((ext_vector_type(4)));

@@ -134,6 +134,21 @@ struct AttnParams {
   size_t ws_bytes;
 };
 size_t attn_ws_bytes(const AttnParams& p);
+// backward over the same visible sets: gradients of sum(dO * O)
+struct AttnBwd {
+  const float* o;          // forward output [B, Hq, Nq, d]
+  int64_t os[4];
+  const float* lse;        // forward LSE [B, Hq, Nq]
+  const float* dO;         // [B, Hq, Nq, d]
+  int64_t dos[4];
+  float* dq;               // [B, Hq, Nq, d]
+  int64_t dqs[4];
+  float* dk;               // [B, Hkv, ctx, d] (zeroed, then accumulated)
+  int64_t dks[4];
+  float* dv;
+  int64_t dvs[4];
+};
+hipError_t launch_attention_bwd(const AttnParams& a, const AttnBwd& g, hipStream_t st);
 // three-branch NSA attention: compression (mode 5 over the pooled blocks),
 // selection (mode 3 without window), window (mode 2), combined by gates
 struct NsaParams {

@@ -673,6 +673,51 @@ SPATTN_API int spattn_sparse_attn_fwd(const spattn_tensor* q, const spattn_tenso
   return attn_fwd(q, k, v, nullptr, ctx_len, scale, sel, o_out, lse_out, ws, ws_bytes, stream);
 }
 
+// ------------------------------------------------------------------ backward
+static int check_f32_like(const spattn_tensor* t, const char* name, const int64_t* shape) {
+  int rc;
+  if ((rc = check_tensor(t, name, 4, false))) return rc;
+  if (t->dtype != SPATTN_F32) return fail(SPATTN_ERR_INVALID_ARG, "%s must be f32", name);
+  for (int i = 0; i < 4; ++i)
+    if (t->shape[i] != shape[i]) return fail(SPATTN_ERR_INVALID_ARG, "%s has the wrong shape", name);
+  return SPATTN_OK;
+}
+
+SPATTN_API int spattn_sparse_attn_bwd(const spattn_tensor* q, const spattn_tensor* k, const spattn_tensor* v,
+                                      const int32_t* ctx_len, float scale, const spattn_selection* sel,
+                                      const spattn_tensor* o, const float* lse, const spattn_tensor* d_o,
+                                      const spattn_tensor* dq_out, const spattn_tensor* dk_out,
+                                      const spattn_tensor* dv_out, void* stream) {
+  sp::AttnParams p;
+  sp::AttnBwd g{};
+  int rc;
+  if ((rc = attn_setup(q, k, v, sel, p, true))) return rc;
+  if (!lse) return fail(SPATTN_ERR_INVALID_ARG, "lse: null (the forward's LSE is required)");
+  if ((rc = check_f32_like(o, "o", q->shape))) return rc;
+  if ((rc = check_f32_like(d_o, "d_o", q->shape))) return rc;
+  if ((rc = check_f32_like(dq_out, "dq_out", q->shape))) return rc;
+  if ((rc = check_f32_like(dk_out, "dk_out", k->shape))) return rc;
+  if ((rc = check_f32_like(dv_out, "dv_out", k->shape))) return rc;
+  if (!(scale >= 0.f) || std::isinf(scale)) return fail(SPATTN_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  p.scale = scale == 0.f ? 1.0f / std::sqrt((float)p.d) : scale;
+  p.ctx_len = ctx_len;
+  g.o = (const float*)o->data;
+  g.lse = lse;
+  g.dO = (const float*)d_o->data;
+  g.dq = (float*)dq_out->data;
+  g.dk = (float*)dk_out->data;
+  g.dv = (float*)dv_out->data;
+  for (int i = 0; i < 4; ++i) {
+    g.os[i] = o->stride[i];
+    g.dos[i] = d_o->stride[i];
+    g.dqs[i] = dq_out->stride[i];
+    g.dks[i] = dk_out->stride[i];
+    g.dvs[i] = dv_out->stride[i];
+  }
+  if ((rc = device_ok())) return rc;
+  return launched(sp::launch_attention_bwd(p, g, (hipStream_t)stream));
+}
+
 // ------------------------------------------------------------------ NSA
 static int nsa_setup(const spattn_tensor* q, const spattn_tensor* k, const spattn_tensor* v, int32_t block_size,
                      const spattn_tensor* blk_idx, int32_t window, sp::NsaParams& p, bool need_v) {

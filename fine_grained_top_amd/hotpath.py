@@ -88,6 +88,11 @@ class HotPath:
             self.sel = S.selection(S.SEL_WINDOW_GLOBAL, window=wl.window, n_global=wl.n_global, stride=wl.stride)
         else:
             self.sel = S.selection(S.SEL_DENSE)
+        if wl.backward:
+            self.d_o = torch.from_numpy(inp["d_o"].astype(np.float32)).to(device)
+            self.dq = torch.empty_like(self.o)
+            self.dk = torch.empty(self.k.shape, dtype=torch.float32, device=device)
+            self.dv = torch.empty(self.v.shape, dtype=torch.float32, device=device)
         self.ws = torch.empty(self.ws_bytes(), dtype=torch.uint8, device=device)
 
     def ws_bytes(self) -> int:
@@ -166,6 +171,10 @@ class HotPath:
             S.spattn_sparse_attn_fwd(self.q, self.k, self.v, self.ctx_len, 0.0, self.sel, self.o, self.lse,
                                      self.ws, stream)
 
+    def attention_bwd(self, stream=None):
+        S.spattn_sparse_attn_bwd(self.q, self.k, self.v, self.ctx_len, 0.0, self.sel, self.o, self.lse, self.d_o,
+                                 self.dq, self.dk, self.dv, stream)
+
     def step(self, stream=None):
         if self.wl.H_I and self.fused and self.wl.kind == "dsa_pages":
             self.page_select_fused(stream)
@@ -182,3 +191,5 @@ class HotPath:
         elif self.wl.kind in ("blocks", "nsa"):
             self.block_select(stream)
         self.attention(stream)
+        if self.wl.backward:
+            self.attention_bwd(stream)

@@ -37,7 +37,7 @@ import numpy as np
 CHUNK = 1 << 22
 
 # tensor ids used in the seed sequence
-TID = dict(q=1, k=2, v=3, q_idx=4, k_idx=5, w=6, lengths=7, needles=8, shift=9, pages=10, gates=11)
+TID = dict(q=1, k=2, v=3, q_idx=4, k_idx=5, w=6, lengths=7, needles=8, shift=9, pages=10, gates=11, d_o=12)
 
 
 def _threads() -> int:
@@ -205,6 +205,8 @@ class Workload:
     page_size: int = 0
     top_pages: int = 0
     n_local: int = 0
+    # backward: an upstream gradient dO is drawn and the gradients are computed
+    backward: bool = False
     # decode lengths (inclusive range); None = every request has N keys
     len_range: Optional[Tuple[int, int]] = None
 
@@ -246,6 +248,11 @@ _add(dataclasses.replace(WINDOW, name="window_global_small", Hq=2, Hkv=2, N=1000
 # Local window plus dilated stride (the fixed pattern's defaults: 64 positions
 # back, i.e. 65 keys with the query, and every 8th token).
 STRIDED = _add(dataclasses.replace(WINDOW, name="window_stride", seed=8, window=65, n_global=0, stride=8))
+# Backward over the window + global pattern (a training step's attention).
+_add(dataclasses.replace(WINDOW, name="window_global_bwd", seed=11, Hq=8, Hkv=8, N=4096, Nq=4096, window=256,
+                         n_global=16, backward=True))
+_add(dataclasses.replace(WINDOW, name="window_global_bwd_small", seed=11, Hq=4, Hkv=2, N=300, Nq=300, window=40,
+                         n_global=3, backward=True))
 _add(dataclasses.replace(STRIDED, name="window_stride_small", Hq=2, Hkv=2, N=1000, Nq=1000, stride=24,
                          n_global=3))
 _add(Workload("dense_small", "dense", B=2, Hq=4, Hkv=2, N=700, Nq=700, d=128, dtype="bf16", seed=6))
@@ -333,6 +340,8 @@ def generate(w: Workload) -> Dict[str, np.ndarray]:
         out["page_table"], out["k_pages"], out["v_pages"] = paged_kv(w, out["k"], out["v"])
     if w.kind == "nsa":
         out["gates"] = uniform01(w.seed, TID["gates"], (w.B, w.Hq, w.Nq, 3))   # compression, selection, window
+    if w.backward:
+        out["d_o"] = normal(w.seed, TID["d_o"], (w.B, w.Hq, w.Nq, w.d), "f32")
     return out
 
 

@@ -31,8 +31,9 @@ STAGES = {
     "topk": ["topk_row", "topk_redo", "mt_zero", "mt_hist", "mt_collect", "mt_finalize"],
     "page_select": ["page_keys_kernel", "page_select_kernel"],
     "two_level_select": ["two_level_kernel"],
+    "attention_bwd": ["attn_bwd_zero", "attn_bwd_generic"],
     "block_select": ["pool_kernel", "block_select_kernel"],
-    "attention": ["attn_index_mfma", "attn_combine", "attn_tile", "attn_generic", "bc_count", "bc_scan", "bc_table",
+    "attention": ["attn_index_mfma", "attn_combine", "attn_tile", "attn_generic_kernel", "bc_count", "bc_scan", "bc_table",
                   "bc_scatter", "bc_attn", "bc_combine"],
 }
 CALIB_BYTES = 1 << 30

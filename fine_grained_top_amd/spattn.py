@@ -78,6 +78,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "spattn_sparse_attn_fwd_paged_workspace": (sz, [P(Tensor), P(Tensor), P(KvPages), P(Selection)]),
         "spattn_sparse_attn_fwd_paged": (ctypes.c_int, [P(Tensor), P(Tensor), P(Tensor), P(KvPages), vp,
                                                         ctypes.c_float, P(Selection), P(Tensor), vp, vp, sz, vp]),
+        "spattn_sparse_attn_bwd": (ctypes.c_int, [P(Tensor), P(Tensor), P(Tensor), vp, ctypes.c_float, P(Selection),
+                                                  P(Tensor), vp, P(Tensor), P(Tensor), P(Tensor), P(Tensor), vp]),
         "spattn_nsa_fwd_workspace": (sz, [P(Tensor), P(Tensor), i32, P(Tensor), i32]),
         "spattn_nsa_fwd": (ctypes.c_int, [P(Tensor), P(Tensor), P(Tensor), vp, ctypes.c_float, i32, P(Tensor), i32,
                                           P(Tensor), P(Tensor), vp, sz, vp]),
@@ -270,6 +272,15 @@ def spattn_sparse_attn_fwd_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: 
                                             ctypes.byref(pages), _ptr(ctx_len), scale, ctypes.byref(sel),
                                             ctypes.byref(to), _ptr(lse_out), _ptr(ws),
                                             0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def spattn_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ctx_len: Optional[torch.Tensor],
+                           scale: float, sel: Selection, o: torch.Tensor, lse: torch.Tensor, d_o: torch.Tensor,
+                           dq_out: torch.Tensor, dk_out: torch.Tensor, dv_out: torch.Tensor, stream=None) -> None:
+    t = [tensor(x) for x in (q, k, v, o, d_o, dq_out, dk_out, dv_out)]
+    _check(LIB.spattn_sparse_attn_bwd(ctypes.byref(t[0]), ctypes.byref(t[1]), ctypes.byref(t[2]), _ptr(ctx_len), scale,
+                                      ctypes.byref(sel), ctypes.byref(t[3]), _ptr(lse), ctypes.byref(t[4]),
+                                      ctypes.byref(t[5]), ctypes.byref(t[6]), ctypes.byref(t[7]), _stream(stream)))
 
 
 def spattn_nsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ctx_len: Optional[torch.Tensor], scale: float,

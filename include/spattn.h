@@ -331,6 +331,30 @@ SPATTN_API int spattn_sparse_attn_fwd_paged(const spattn_tensor* q, const spattn
                                             void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * spattn_sparse_attn_bwd — gradients of the sparse attention over the same
+ * visible sets. Source: "Sparse Attention in 2026: Why It Finally Had to Be
+ * Native" (natively trainable sparsity: forward and backward run over the
+ * selected set; the speedup covers training, not only serving).
+ *
+ * For the forward O = spattn_sparse_attn_fwd(q, k, v, sel) and an upstream
+ * gradient d_o, writes dq = d(sum d_o*O)/dq, dk, dv (GQA: a KV head gathers
+ * the gradients of all its query heads): with P the softmax over S(i),
+ * dV = P^T dO, dS = P (dO V^T - rowsum(dO * O)), dq = scale dS K,
+ * dK = scale dS^T Q.
+ *  q, k, v, ctx_len, scale, sel: as passed to the forward (contiguous K/V,
+ *     every selection mode); o f32 [B, H_q, Nq, d] and lse f32 [B, H_q, Nq]:
+ *     the forward's outputs; d_o, dq_out f32 [B, H_q, Nq, d];
+ *     dk_out, dv_out f32 [B, H_kv, ctx, d] (overwritten).
+ *  float32 arithmetic; dk/dv are accumulated with float atomics, so their
+ *  low bits depend on the order in which rows finish. No workspace.
+ * ---------------------------------------------------------------------- */
+SPATTN_API int spattn_sparse_attn_bwd(const spattn_tensor* q, const spattn_tensor* k, const spattn_tensor* v,
+                                      const int32_t* ctx_len, float scale, const spattn_selection* sel,
+                                      const spattn_tensor* o, const float* lse, const spattn_tensor* d_o,
+                                      const spattn_tensor* dq_out, const spattn_tensor* dk_out,
+                                      const spattn_tensor* dv_out, void* stream);
+
+/* ------------------------------------------------------------------------
  * spattn_nsa_fwd — three-branch NSA attention.
  * Source: "Sparse Attention in 2026: Why It Finally Had to Be Native", NSA
  * paragraph (coarse compression of token blocks mean-pooled into single

@@ -271,3 +271,25 @@ def test_two_level_validation():
     assert call(blocks=kb.to(torch.bfloat16)) == 1        # block keys are f32
     assert call(idx=torch.zeros(2, 8, 1, 99, dtype=torch.int32)) == 1
     assert S.LIB.spattn_pool_index_keys(ctypes.byref(ix), None, 64, ctypes.byref(S.tensor(kb)), None) == 4
+
+
+
+def test_backward_validation():
+    q = torch.zeros(1, 4, 8, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 16, 128, dtype=torch.bfloat16)
+    o = torch.zeros(1, 4, 8, 128)
+    lse = torch.zeros(1, 4, 8)
+    dk = torch.zeros(1, 2, 16, 128)
+
+    def call(sel=S.selection(S.SEL_DENSE), oo=o, lp=lse, dkk=dk):
+        t = [S.tensor(x) for x in (q, k, k, oo, o, o, dkk, dk)]
+        return S.LIB.spattn_sparse_attn_bwd(ctypes.byref(t[0]), ctypes.byref(t[1]), ctypes.byref(t[2]), None, 0.0,
+                                            ctypes.byref(sel), ctypes.byref(t[3]), None if lp is None else lp.data_ptr(),
+                                            ctypes.byref(t[4]), ctypes.byref(t[5]), ctypes.byref(t[6]),
+                                            ctypes.byref(t[7]), None)
+
+    assert call() == 4
+    assert call(S.selection(S.SEL_WINDOW_GLOBAL, window=4, stride=2)) == 4
+    assert call(lp=None) == 1                                     # the forward's LSE is required
+    assert call(oo=torch.zeros(1, 4, 8, 64)) == 1
+    assert call(dkk=torch.zeros(1, 2, 16, 128, dtype=torch.bfloat16)) == 1

@@ -879,3 +879,98 @@ def test_two_level_certified_near_ties(bs, nb, K):
         assert gc[r] == len(want), (r, gc[r], len(want))
         assert np.array_equal(got[r, : len(want)], want), r
         assert np.all(got[r, len(want):] == -1)
+
+
+
+# ---------------------------------------------------------------- backward
+def _grads_oracle(q, k, v, dO, sets, ctx_len, Nq, scale):
+    """dq, dk, dv by the oracle: per (request, head, row) gradients of the
+    masked attention, the key gradients summed over rows and heads."""
+    import oracle as orc
+    B, Hq, _, d = q.shape
+    Hkv, ctx = k.shape[1], k.shape[2]
+    dq = np.zeros((B, Hq, Nq, d))
+    dk = np.zeros((B, Hkv, ctx, d))
+    dv = np.zeros((B, Hkv, ctx, d))
+    for b in range(B):
+        for h in range(Hq):
+            kvh = h // (Hq // Hkv)
+            for r in range(Nq):
+                p = ctx_len[b] - Nq + r
+                S_ = sets(b, h, r, p)
+                gq, gk, gv = orc.masked_attention_grads(q[b, h, r][None], k[b, kvh, : p + 1], v[b, kvh, : p + 1],
+                                                        S_, scale, dO[b, h, r][None])
+                dq[b, h, r] = gq[0]
+                dk[b, kvh, : p + 1] += gk
+                dv[b, kvh, : p + 1] += gv
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("mode,dtype", [("window", "bf16"), ("stride", "f32"), ("index", "bf16"), ("blocks", "bf16"),
+                                        ("dense", "f32")])
+def test_attention_backward(mode, dtype):
+    """dq, dk, dv over every selection mode, GQA, ragged lengths, against the
+    oracle's gradients (float32 accumulation with float atomics)."""
+    import oracle as orc
+    sp = S()
+    say(f"[gpu] backward {mode} {dtype}")
+    g_ = torch.Generator().manual_seed(61)
+    B, Hq, Hkv, Nq, ctx = 2, 4, 2, 96, 160
+    d = 128 if dtype == "bf16" else 64
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = torch.randn(B, Hq, Nq, d, generator=g_).to(tdt)
+    k = torch.randn(B, Hkv, ctx, d, generator=g_).to(tdt)
+    v = torch.randn(B, Hkv, ctx, d, generator=g_).to(tdt)
+    dO = torch.randn(B, Hq, Nq, d, generator=g_)
+    ctx_len = [160, 130]
+    rng = np.random.default_rng(62)
+    keep = []
+    if mode in ("window", "stride"):
+        w, gl, st = 20, 3, (7 if mode == "stride" else 0)
+        sel = sp.selection(sp.SEL_WINDOW_GLOBAL, window=w, n_global=gl, stride=st)
+        sets = lambda b, h, r, p: orc.window_global_set(p, w, gl, st)
+    elif mode == "index":
+        lists = np.full((B, Hkv, Nq, 24), -1, np.int32)
+        for b in range(B):
+            for g in range(Hkv):
+                for r in range(Nq):
+                    p = ctx_len[b] - Nq + r
+                    s_ = np.sort(rng.choice(p + 1, size=min(24, p + 1), replace=False))
+                    lists[b, g, r, : len(s_)] = s_
+        ld = torch.from_numpy(lists).cuda()
+        keep.append(ld)
+        sel = sp.selection(sp.SEL_INDEX, ld)
+        sets = lambda b, h, r, p: lists[b, h // (Hq // Hkv), r][lists[b, h // (Hq // Hkv), r] >= 0]
+    elif mode == "blocks":
+        bs, nb, w = 16, 3, 10
+        blk = np.full((B, Hq, Nq, nb), -1, np.int32)
+        for b in range(B):
+            for h in range(Hq):
+                for r in range(Nq):
+                    p = ctx_len[b] - Nq + r
+                    ne = (p + 1) // bs
+                    c = np.sort(rng.choice(ne, size=min(nb, ne), replace=False)) if ne else []
+                    blk[b, h, r, : len(c)] = c
+        bd = torch.from_numpy(blk).cuda()
+        keep.append(bd)
+        sel = sp.selection(sp.SEL_BLOCKS, bd, window=w, block_size=bs)
+        sets = lambda b, h, r, p: orc.blocks_set([x for x in blk[b, h, r] if x >= 0], p, bs, w)
+    else:
+        sel = sp.selection(sp.SEL_DENSE)
+        sets = lambda b, h, r, p: np.arange(p + 1)
+    qd, kd, vd, dOd = q.cuda(), k.cuda(), v.cuda(), dO.cuda()
+    cl = torch.tensor(ctx_len, dtype=torch.int32, device="cuda")
+    o = torch.empty(B, Hq, Nq, d, device="cuda")
+    lse = torch.empty(B, Hq, Nq, device="cuda")
+    sp.spattn_sparse_attn_fwd(qd, kd, vd, cl, 0.0, sel, o, lse)
+    dq = torch.empty(B, Hq, Nq, d, device="cuda")
+    dk = torch.full((B, Hkv, ctx, d), float("nan"), device="cuda")
+    dv = torch.full((B, Hkv, ctx, d), float("nan"), device="cuda")
+    sp.spattn_sparse_attn_bwd(qd, kd, vd, cl, 0.0, sel, o, lse, dOd, dq, dk, dv)
+    torch.cuda.synchronize()
+    rq, rk, rv = _grads_oracle(q.double().numpy(), k.double().numpy(), v.double().numpy(), dO.double().numpy(),
+                               sets, ctx_len, Nq, 1.0 / math.sqrt(d))
+    errs = [float(np.abs(got.cpu().numpy() - ref).max()) / max(1.0, float(np.abs(ref).max()))
+            for got, ref in ((dq, rq), (dk, rk), (dv, rv))]
+    say(f"  relative max errors dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}")
+    assert max(errs) <= 1e-4
