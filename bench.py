@@ -32,6 +32,11 @@ F32_PEAK_TFS = 157.3         # fp32 vector
 
 def roofline_of(a, ms):
     """Roofline entry for one stage from its algorithmic bytes/flops and time."""
+    if a.get("bound") == "alu":
+        ach = a["flops"] / (ms * 1e-3) / 1e12
+        return {"bound": "alu", "achieved": round(ach, 2), "peak": F32_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(ach / F32_PEAK_TFS, 4), "traffic": None, "alg_flops_per_launch": a["flops"],
+                "launch_ms": round(ms, 5)}
     if a.get("bound") == "mfma":
         ach = a["flops"] / (ms * 1e-3) / 1e12
         return {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_PEAK_TFS, "unit": "TFLOP/s",
@@ -100,9 +105,11 @@ def algorithmic(wl, inp, hp, fused):
         out["attention"] = {"bytes": kv + qkv_out, "flops": 4.0 * pairs * wl.d,
                             "bound": "mfma" if wl.stride else "hbm"}
         if wl.backward:
-            # q, k, v, O, dO read once; dq, dk, dv written once; 8 flops per (pair, dim): s, dp, dq, dk, dv
+            # q, k, v, O, dO read once; dq, dk, dv written once; five products of 2 flops per
+            # (pair, dim): s = q.k, dp = dO.v, dq += ds k, dk += ds q, dv += p dO; computed by
+            # float32 FMAs, so the vector float32 peak bounds it
             gbytes = wl.B * (wl.Hq * wl.Nq * wl.d * (e + 4 + 4 + 4 + 4) + wl.Hkv * wl.N * wl.d * (2 * e + 8))
-            out["attention_bwd"] = {"bytes": gbytes, "flops": 8.0 * pairs * wl.d, "bound": "mfma"}
+            out["attention_bwd"] = {"bytes": gbytes, "flops": 10.0 * pairs * wl.d, "bound": "alu"}
     elif wl.kind == "nsa":
         # three branches: pooled entries of complete blocks, the chosen blocks' tokens, the window
         blk = hp.idx.cpu().numpy().astype(np.int64)          # [B, Hq, Nq, nb]
@@ -278,7 +285,8 @@ def main():
             e["hbm_frac"] = round(e["GB_s"] / HBM_PEAK_GBS, 4)
             if a.get("flops"):
                 e["TFLOP_s"] = round(a["flops"] / (ms * 1e-3) / 1e12, 3)
-                e["mfma_frac"] = round(e["TFLOP_s"] / (MFMA_PEAK_TFS if wl.dtype == "bf16" else F32_PEAK_TFS), 4)
+                vec = a.get("bound") == "alu" or wl.dtype != "bf16"
+                e["mfma_frac" if not vec else "alu_frac"] = round(e["TFLOP_s"] / (F32_PEAK_TFS if vec else MFMA_PEAK_TFS), 4)
             if a.get("rows"):
                 e["rows_per_s"] = round(a["rows"] / (ms * 1e-3), 1)
         per_stage[name] = e

@@ -256,6 +256,7 @@ hipError_t launch_attention_bwd(const AttnParams& a, const AttnBwd& g, hipStream
   hipLaunchKernelGGL(attn_bwd_zero_kernel, dim3(a.ctx, a.Hkv, a.B), dim3(128), 0, st, a, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (attn_bwd_tile_ok(a)) return launch_attn_bwd_tile(a, g, st);
   hipLaunchKernelGGL(attn_bwd_generic_kernel, dim3(a.Nq, a.Hq, a.B), dim3(64), 0, st, a, g);
   return hipGetLastError();
 }

@@ -149,6 +149,9 @@ struct AttnBwd {
   int64_t dvs[4];
 };
 hipError_t launch_attention_bwd(const AttnParams& a, const AttnBwd& g, hipStream_t st);
+// tiled backward of the dense and window/global patterns (bf16, d = 128)
+bool attn_bwd_tile_ok(const AttnParams& a);
+hipError_t launch_attn_bwd_tile(const AttnParams& a, const AttnBwd& g, hipStream_t st);
 // three-branch NSA attention: compression (mode 5 over the pooled blocks),
 // selection (mode 3 without window), window (mode 2), combined by gates
 struct NsaParams {

@@ -906,11 +906,13 @@ def _grads_oracle(q, k, v, dO, sets, ctx_len, Nq, scale):
     return dq, dk, dv
 
 
-@pytest.mark.parametrize("mode,dtype", [("window", "bf16"), ("stride", "f32"), ("index", "bf16"), ("blocks", "bf16"),
-                                        ("dense", "f32")])
+@pytest.mark.parametrize("mode,dtype", [("window", "bf16"), ("window_wide", "bf16"), ("stride", "f32"),
+                                        ("index", "bf16"), ("blocks", "bf16"), ("dense", "f32"), ("dense", "bf16")])
 def test_attention_backward(mode, dtype):
     """dq, dk, dv over every selection mode, GQA, ragged lengths, against the
-    oracle's gradients (float32 accumulation with float atomics)."""
+    oracle's gradients (float32 accumulation with float atomics). The bf16
+    dense and window cases run the tiled kernel (query tiles of 64 rows, one
+    full and one ragged, over ragged key tiles), the others the per-row one."""
     import oracle as orc
     sp = S()
     say(f"[gpu] backward {mode} {dtype}")
@@ -925,8 +927,8 @@ def test_attention_backward(mode, dtype):
     ctx_len = [160, 130]
     rng = np.random.default_rng(62)
     keep = []
-    if mode in ("window", "stride"):
-        w, gl, st = 20, 3, (7 if mode == "stride" else 0)
+    if mode in ("window", "window_wide", "stride"):
+        w, gl, st = (70, 17, 0) if mode == "window_wide" else (20, 3, (7 if mode == "stride" else 0))
         sel = sp.selection(sp.SEL_WINDOW_GLOBAL, window=w, n_global=gl, stride=st)
         sets = lambda b, h, r, p: orc.window_global_set(p, w, gl, st)
     elif mode == "index":
