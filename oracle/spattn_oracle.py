@@ -59,6 +59,15 @@ What is computed (sources are the five pages on sparse attention):
   here as the largest key among the page's visible tokens. The recent pages
   are the n_local pages ending with the one that holds the query position;
   every earlier page competes by (page key descending, page index ascending).
+* Query-aware page selection without a trained indexer ("Sparse Attention"
+  (completesystemdesign.dev), inference-only alternatives: Quest-style
+  page-wise KV selection). The page names no criterion; Quest's published one
+  (Tang et al., 2024) is taken: each complete page keeps the channel-wise
+  minimum m and maximum M of its keys, and a selection group's key for the
+  page is the float32 nearest to the exact sum over the group's query heads h
+  and channels c of max(q_hc m_c, q_hc M_c) (the largest q . x over the box
+  [m, M]). The n_local >= 1 most recent pages are always read and the others
+  ranked by (key descending, page ascending).
 
 Selection keys. The pages fix no precision for the scores. Selection is made
 on key(j) = the float32 nearest (ties to even) to the exact real-valued score,
@@ -317,6 +326,55 @@ def two_level_select(block_keys: np.ndarray, token_keys: np.ndarray, p: int, bs:
     return cand[chosen].astype(np.int32)
 
 
+def quest_bounds(K: np.ndarray, P: int, n_pages: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Channel-wise minimum and maximum of the keys of pages 0..n_pages-1
+    (each page the P rows pi*P .. pi*P+P-1 of K), each [n_pages, d]."""
+    Kp = K[: n_pages * P].reshape(n_pages, P, K.shape[1])
+    return Kp.min(axis=1), Kp.max(axis=1)
+
+
+def exact_quest_key(Q: np.ndarray, mn: np.ndarray, mx: np.ndarray) -> np.float32:
+    """Nearest float32 of sum_h sum_c max(Q[h,c] mn[c], Q[h,c] mx[c]), exact rationals."""
+    total = Fraction(0)
+    for h in range(Q.shape[0]):
+        for c in range(Q.shape[1]):
+            a = _frac(Q[h, c])
+            total += max(a * _frac(mn[c]), a * _frac(mx[c]))
+    return f32_nearest(total)
+
+
+def quest_page_keys(Q: np.ndarray, K: np.ndarray, P: int, n_pages: int) -> np.ndarray:
+    """key(page) for the query heads Q [H, d] of one selection group over the
+    complete pages 0..n_pages-1 of K: the float32 nearest to the exact bound
+    (products of bf16/f32 values are exact in float64; the float64 sum is
+    certified against its rounding bound, else summed exactly)."""
+    if n_pages == 0:
+        return np.zeros(0, np.float32)
+    mn, mx = quest_bounds(K, P, n_pages)
+    T = np.maximum(Q[None, :, :] * mn[:, None, :], Q[None, :, :] * mx[:, None, :])    # [pages, H, d]
+    T = T.reshape(n_pages, -1)
+    y = T.sum(axis=1)
+    A = np.abs(T).sum(axis=1)
+    e = 2.0 * (T.shape[1] + 4) * U52 * A + 1e-300
+    keys, ok = _certify(y, e)
+    for i in np.nonzero(~ok)[0]:
+        keys[i] = exact_quest_key(Q, mn[i], mx[i])
+    return keys
+
+
+def quest_select(Q: np.ndarray, K: np.ndarray, p: int, P: int, top_pages: int, n_local: int) -> np.ndarray:
+    """Pages read by the query heads Q [H, d] of one group at position p, ascending:
+    the n_local (>= 1) most recent pages, and among the earlier (complete)
+    pages the min(top_pages, count) best by (bound key descending, page
+    ascending)."""
+    assert n_local >= 1
+    last = p // P
+    n_cand = max(0, last + 1 - n_local)
+    chosen = topk(quest_page_keys(Q, K[:p + 1], P, n_cand), top_pages) if n_cand else np.zeros(0, np.int32)
+    local = np.arange(n_cand, last + 1)
+    return np.concatenate([chosen, local]).astype(np.int32)
+
+
 def pages_set(pages: Sequence[int], p: int, P: int) -> np.ndarray:
     """Every token of the listed pages, within 0..p (pages are read whole)."""
     parts = [np.arange(P * pg, P * pg + P) for pg in pages]
@@ -501,6 +559,16 @@ def run(wl, inp: Dict[str, np.ndarray], rows: Iterable[Tuple[int, int]],
                 for h in range(wl.Hq):
                     if h // (wl.Hq // wl.G_sel) == g:
                         S_of_head[h] = S
+        elif wl.kind == "quest":
+            hg = wl.Hq // wl.G_sel
+            for g in range(wl.G_sel):
+                Qg = np.stack([decode(Q[b, h, r], wl.dtype) for h in range(g * hg, (g + 1) * hg)])
+                pg = quest_select(Qg, Kb[(g * hg) // qpk], p, wl.page_size, wl.top_pages, wl.n_local)
+                res.blocks[(b, g, r)] = pg
+                S = pages_set(pg, p, wl.page_size)
+                res.sets[(b, g, r)] = S
+                for h in range(g * hg, (g + 1) * hg):
+                    S_of_head[h] = S
         elif wl.kind == "window_global":
             S = window_global_set(p, wl.window, wl.n_global, wl.stride)
             res.sets[(b, 0, r)] = S

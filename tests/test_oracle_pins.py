@@ -632,3 +632,70 @@ def test_attention_grads_match_torch_autograd(seed):
         # keys outside the visible set get no gradient
         outside = np.setdiff1d(np.arange(n), S)
         assert not dK[outside].any() and not dV[outside].any()
+
+
+# ---------------------------------------------------------------- Quest page selection
+def test_quest_hand_worked():
+    """Bounds and page lists worked out by hand (tests/golden/quest_hand.json)."""
+    with open(os.path.join(GOLD, "quest_hand.json")) as f:
+        g = json.load(f)
+    K = np.array(g["keys"], dtype=np.float64)
+    heads = {k: np.array(v, dtype=np.float64) for k, v in g["heads"].items()}
+    for c in g["bounds"]:
+        n = K.shape[0] // c["P"]
+        got = orc.quest_page_keys(heads[c["heads"]], K, c["P"], n)
+        assert got.tolist() == c["keys"], c
+    for c in g["select_cases"]:
+        got = orc.quest_select(heads[c["heads"]], K, c["p"], c["P"], c["top"], c["local"])
+        assert got.tolist() == c["pages"], c
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_quest_bound_is_the_box_maximum(seed):
+    """A page's bound is, summed over the group's heads, the largest value each
+    head's score takes at any corner of the box the page's keys span (a linear
+    function peaks at a corner of a box), found here by enumerating all 2^d
+    corners in exact arithmetic; and no token of the page scores above it."""
+    rng = np.random.default_rng(seed)
+    d, H, P, n = 6, 2, 3, 4
+    Q = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(rng.standard_normal((H, d)).astype(np.float32))).astype(np.float64)
+    K = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(rng.standard_normal((n * P, d)).astype(np.float32))).astype(np.float64)
+    keys = orc.quest_page_keys(Q, K, P, n)
+    qsum = [sum(Fraction(float(Q[h, c])) for h in range(H)) for c in range(d)]
+    for pg in range(n):
+        rows = K[pg * P:(pg + 1) * P]
+        lo, hi = rows.min(axis=0), rows.max(axis=0)
+        best = None
+        for mask in range(1 << d):
+            x = [hi[c] if (mask >> c) & 1 else lo[c] for c in range(d)]
+            vh = [sum(Fraction(float(Q[h, c])) * Fraction(float(x[c])) for c in range(d)) for h in range(H)]
+            best = vh if best is None else [max(a, b) for a, b in zip(best, vh)]
+        assert keys[pg] == orc.f32_nearest(sum(best))
+        for t in range(P):
+            s = sum(qsum[c] * Fraction(float(rows[t, c])) for c in range(d))
+            assert s <= sum(best)
+
+
+@pytest.mark.parametrize("seed", [3, 4])
+def test_quest_one_token_pages_is_token_topk(seed):
+    """With one-token pages the box is the key itself: the bound is the summed
+    score (sum_h q_h) . k_j, and Quest selection is token top-K over tokens
+    0..p-1 plus the query's own token."""
+    rng = np.random.default_rng(seed)
+    d, H, n, K_ = 16, 3, 40, 7
+    Q = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(rng.standard_normal((H, d)).astype(np.float32))).astype(np.float64)
+    K = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(rng.standard_normal((n, d)).astype(np.float32))).astype(np.float64)
+    qsum = Q.sum(axis=0)          # exact: three bf16 values of similar size
+    for p in (5, 20, 39):
+        got = orc.quest_select(Q, K, p, 1, K_, 1)
+        want = np.sort(np.concatenate([orc.topk(orc.keys_dot(qsum, K[:p]), K_), [p]]))
+        assert got.tolist() == want.tolist()
+
+
+def test_quest_key_rounds_exact_midpoints_to_even():
+    """Bounds at a float32 midpoint take the exact path and round to even."""
+    Q = np.array([[1.0, 1.0]])
+    for tail, want in ((2.0 ** -24, 1.0), (3 * 2.0 ** -24, 1.0 + 2.0 ** -22), (-(2.0 ** -25), 1.0), (-3 * 2.0 ** -25, 1.0 - 2.0 ** -23)):
+        K = np.array([[1.0, tail], [1.0, tail]])
+        got = orc.quest_page_keys(Q, K, 2, 1)
+        assert got[0] == np.float32(want), (tail, got[0], want)
