@@ -48,6 +48,19 @@ def roofline_of(a, ms):
             "launch_ms": round(ms, 5)}
 
 
+def _paged_attention(wl, hp, lens, e, qkv_out):
+    """Attention over page lists: every listed page is read whole (cut at the query position)."""
+    import numpy as np
+    P = wl.page_size
+    pg = hp.idx.cpu().numpy().astype(np.int64)                      # [B, G, Nq, width]
+    pos = np.stack([L - wl.Nq + np.arange(wl.Nq) for L in lens])[:, None, :, None]
+    tok = np.clip(np.minimum(pg * P + P, pos + 1) - pg * P, 0, None) * (pg >= 0)
+    sel_g = float(tok.sum())                                         # sum over (b, g, r) of |S|
+    per_sel = max(1, wl.Hkv // wl.G_sel)                             # KV heads each list is gathered for
+    return {"bytes": sel_g * per_sel * wl.d * e * 2 + qkv_out, "flops": 4.0 * sel_g * (wl.Hq // wl.G_sel) * wl.d,
+            "bound": "hbm" if wl.Nq == 1 else "mfma"}
+
+
 def algorithmic(wl, inp, hp, fused):
     """Algorithmic bytes (compulsory HBM traffic) and flops of one call of each stage."""
     import numpy as np
@@ -90,14 +103,16 @@ def algorithmic(wl, inp, hp, fused):
                                   "rows": wl.B * wl.G_sel * wl.Nq}
             out["index_page_fused"] = {"bytes": keys_read + wl.B * wl.G_sel * wl.Nq * width * 4, "flops": flops_idx,
                                        "rows": wl.B * wl.G_sel * wl.Nq, "bound": "hbm" if wl.Nq == 1 else "mfma"}
-            pg = hp.idx.cpu().numpy().astype(np.int64)                      # [B, G, Nq, width]
-            pos = np.stack([L - wl.Nq + np.arange(wl.Nq) for L in lens])[:, None, :, None]
-            tok = np.clip(np.minimum(pg * P + P, pos + 1) - pg * P, 0, None) * (pg >= 0)
-            sel_g = float(tok.sum())                                         # sum over (b, g, r) of |S|
-            per_sel = (wl.Hq // max(wl.Hq // wl.G_sel, wl.Hq // wl.Hkv)) // wl.G_sel   # gathers per group
-            out["attention"] = {"bytes": sel_g * per_sel * wl.d * e * 2 + qkv_out,
-                                "flops": 4.0 * sel_g * (wl.Hq // wl.G_sel) * wl.d,
-                                "bound": "hbm" if wl.Nq == 1 else "mfma"}
+            out["attention"] = _paged_attention(wl, hp, lens, e, qkv_out)
+    elif wl.kind == "quest":
+        # the bounds (min and max rows) of every candidate page of rows that rank pages, q in, page lists out
+        pos = np.stack([L - wl.Nq + np.arange(wl.Nq) for L in lens])              # [B, Nq]
+        npc = np.maximum(0, pos // wl.page_size + 1 - wl.n_local)
+        rows = wl.B * wl.G_sel * wl.Nq
+        bnd = float(np.where(npc > wl.top_pages, npc, 0).sum()) * wl.G_sel * 2 * wl.d * e
+        out["quest_select"] = {"bytes": bnd + wl.B * wl.Hq * wl.Nq * wl.d * e
+                               + rows * (wl.top_pages + wl.n_local) * 4, "rows": rows}
+        out["attention"] = _paged_attention(wl, hp, lens, e, qkv_out)
     elif wl.kind == "window_global":
         pairs = float(metrics.window_stride_pairs(wl.N, wl.window, wl.n_global, wl.stride)) * wl.Hq * wl.B
         kv = wl.B * wl.Hkv * wl.N * wl.d * e * 2
@@ -221,6 +236,8 @@ def main():
                   ("attention", lambda hp: hp.attention())]
     elif wl.kind in ("blocks", "nsa"):
         stages = [("block_select", lambda hp: hp.block_select()), ("attention", lambda hp: hp.attention())]
+    elif wl.kind == "quest":
+        stages = [("quest_select", lambda hp: hp.quest_select()), ("attention", lambda hp: hp.attention())]
     else:
         stages = [("attention", lambda hp: hp.attention())]
     if wl.backward:
@@ -317,7 +334,7 @@ def main():
             ok &= err <= (1e-5 if wl.dtype == "f32" else 2e-3)
             if idx is not None and wl.kind not in ("blocks", "nsa"):
                 for g in range(wl.G_sel):
-                    want = res.blocks[(b, g, r)] if wl.kind == "dsa_pages" else res.sets[(b, g, r)]
+                    want = res.blocks[(b, g, r)] if wl.kind in ("dsa_pages", "quest") else res.sets[(b, g, r)]
                     ok &= bool(np.array_equal(idx[b, g, r, : len(want)], want))
             if time.perf_counter() - t0 > args.cpu_seconds:
                 break
@@ -343,6 +360,8 @@ def main():
         "data": "synthetic",
         "path": (("fused indexer+page selection" if fused else "indexer scores, certified page selection")
                  + ", attention over a paged KV cache" if wl.kind == "dsa_pages" else
+                 "Quest page selection from per-page key bounds (bounds formed before timing), attention over "
+                 "a paged KV cache" if wl.kind == "quest" else
                  "two-level block-then-token selection (block-key cache formed before timing)"
                  if wl.kind == "dsa_two_level" else
                  "fused indexer+top-K" if fused else "separate indexer and top-K calls"),

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 OUT = os.path.join(PKG, "libspattn.so")
 OBJ = os.path.join(ROOT, "_build")
 
-SOURCES = ["spattn_api.cpp", "indexer.hip", "topk.hip", "block_select.hip", "attn.hip", "attn_tile.hip", "attn_blocks.hip", "attn_bwd.hip", "pages.hip", "nsa.hip", "twolevel.hip"]
+SOURCES = ["spattn_api.cpp", "indexer.hip", "topk.hip", "block_select.hip", "attn.hip", "attn_tile.hip", "attn_blocks.hip", "attn_bwd.hip", "pages.hip", "nsa.hip", "twolevel.hip", "quest.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

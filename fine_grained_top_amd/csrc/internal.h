@@ -75,6 +75,26 @@ struct PageSelParams {
 };
 size_t page_select_ws_bytes(const PageSelParams& p);
 hipError_t launch_page_select(const PageSelParams& p, hipStream_t st);
+// selection on page keys given as order keys in pkg[row * npmax + page]
+// (every candidate page of every row with more candidates than p.t.K),
+// taken as they are (p.t.certified false, no scores)
+hipError_t launch_page_select_keys(const PageSelParams& p, const uint32_t* pkg, int npmax, hipStream_t st);
+
+// ---------------------------------------------------------------- Quest page selection
+struct QuestParams {
+  View4 q;                 // [B, Hq, Nq, d]
+  View4 kp;                // key pool [n_pages, Hkv, P, d]
+  const int32_t* ptab;     // page table [B, maxp]
+  int64_t pts[2];
+  void* bnd;               // page bounds [B, maxp, Hkv, 2d] in the key dtype: min | max
+  int64_t bs[3];
+  int B, Hq, Hkv, Nq, d, dt, lgP, maxp, ctx;
+  const int32_t* ctx_len;
+  PageSelParams sel;       // selection groups, top_pages, n_local, outputs; ws: page keys
+};
+size_t quest_ws_bytes(const QuestParams& p);
+hipError_t launch_quest_bounds(const QuestParams& p, hipStream_t st);
+hipError_t launch_quest_select(const QuestParams& p, hipStream_t st);
 
 // ---------------------------------------------------------------- two-level selection
 constexpr int kTlMaxCand = 8192;   // blocks per row, and candidate tokens per row

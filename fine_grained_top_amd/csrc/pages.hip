@@ -426,4 +426,9 @@ hipError_t launch_page_select(const PageSelParams& p0, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_page_select_keys(const PageSelParams& p, const uint32_t* pkg, int npmax, hipStream_t st) {
+  hipLaunchKernelGGL(page_select_kernel, dim3(page_rows(p)), dim3(kPsThreads), 0, st, p, pkg, npmax);
+  return hipGetLastError();
+}
+
 }  // namespace sp

@@ -788,4 +788,140 @@ SPATTN_API int spattn_sparse_attn_fwd_paged(const spattn_tensor* q, const spattn
   return attn_fwd(q, k_pool, v_pool, pages, ctx_len, scale, sel, o_out, lse_out, ws, ws_bytes, stream);
 }
 
+// ------------------------------------------------------------------ Quest page selection
+static int check_bounds(const spattn_tensor* bnd, int64_t B, int64_t Hkv, int64_t d, int dt, int64_t& maxp) {
+  int rc;
+  if ((rc = check_tensor(bnd, "bounds", 4, true))) return rc;
+  if (bnd->dtype != dt) return fail(SPATTN_ERR_INVALID_ARG, "bounds must have the key dtype");
+  if (bnd->shape[0] != B || bnd->shape[2] != Hkv || bnd->shape[3] != 2 * d || bnd->shape[1] < 1)
+    return fail(SPATTN_ERR_INVALID_ARG, "bounds must be [B, max_pages, H_kv, 2d]");
+  maxp = bnd->shape[1];
+  return SPATTN_OK;
+}
+
+SPATTN_API int spattn_quest_page_bounds(const spattn_tensor* k_pool, const spattn_kv_pages* pages,
+                                        const int32_t* ctx_len, const spattn_tensor* bounds_out, void* stream) {
+  int rc;
+  if (!pages) return fail(SPATTN_ERR_INVALID_ARG, "pages: null");
+  if ((rc = check_tensor(k_pool, "k_pool", 4, true))) return rc;
+  if (k_pool->dtype != SPATTN_F32 && k_pool->dtype != SPATTN_BF16)
+    return fail(SPATTN_ERR_UNSUPPORTED, "k_pool dtype must be f32 or bf16");
+  const int64_t Hkv = k_pool->shape[1], d = k_pool->shape[3];
+  if (d != 64 && d != 128) return fail(SPATTN_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  const int lgP = log2_pow2(pages->page_size, 4096);
+  if (lgP < 0) return fail(SPATTN_ERR_INVALID_ARG, "page_size must be a power of two in 1..4096");
+  if (k_pool->shape[2] != pages->page_size || Hkv < 1 || k_pool->shape[0] < 1)
+    return fail(SPATTN_ERR_INVALID_ARG, "k_pool must be [n_pages, H_kv, page_size, d]");
+  if ((rc = check_tensor(&pages->page_table, "page_table", 2, false))) return rc;
+  if (pages->page_table.dtype != SPATTN_I32) return fail(SPATTN_ERR_INVALID_ARG, "page_table must be int32");
+  const int64_t B = pages->page_table.shape[0], tabp = pages->page_table.shape[1];
+  if (B < 1 || tabp < 1) return fail(SPATTN_ERR_INVALID_ARG, "page_table must be [B, max_pages]");
+  int64_t maxp;
+  if ((rc = check_bounds(bounds_out, B, Hkv, d, k_pool->dtype, maxp))) return rc;
+  if (maxp != tabp) return fail(SPATTN_ERR_INVALID_ARG, "bounds and page_table disagree on max_pages");
+  if (maxp * pages->page_size >= ((int64_t)1 << 31) || maxp > 65535)
+    return fail(SPATTN_ERR_UNSUPPORTED, "max_pages too large");
+  sp::QuestParams p{};
+  p.kp = view(k_pool);
+  p.ptab = (const int32_t*)pages->page_table.data;
+  p.pts[0] = pages->page_table.stride[0];
+  p.pts[1] = pages->page_table.stride[1];
+  p.bnd = bounds_out->data;
+  for (int i = 0; i < 3; ++i) p.bs[i] = bounds_out->stride[i];
+  p.B = (int)B;
+  p.Hkv = (int)Hkv;
+  p.d = (int)d;
+  p.dt = k_pool->dtype;
+  p.lgP = lgP;
+  p.maxp = (int)maxp;
+  p.ctx = (int)(maxp << lgP);
+  p.ctx_len = ctx_len;
+  if ((rc = device_ok())) return rc;
+  return launched(sp::launch_quest_bounds(p, (hipStream_t)stream));
+}
+
+static int quest_setup(const spattn_tensor* q, const spattn_tensor* bounds, const int32_t* ctx_len,
+                       int32_t page_size, int32_t top_pages, int32_t n_local, const spattn_tensor* pg_idx_out,
+                       sp::QuestParams& p) {
+  int rc;
+  p = sp::QuestParams{};
+  if ((rc = check_tensor(q, "q", 4, true))) return rc;
+  if (q->dtype != SPATTN_F32 && q->dtype != SPATTN_BF16) return fail(SPATTN_ERR_UNSUPPORTED, "q dtype must be f32 or bf16");
+  const int64_t B = q->shape[0], Hq = q->shape[1], Nq = q->shape[2], d = q->shape[3];
+  if (d != 64 && d != 128) return fail(SPATTN_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  if (!bounds) return fail(SPATTN_ERR_INVALID_ARG, "bounds: null tensor");
+  const int64_t Hkv = bounds->ndim == 4 ? bounds->shape[2] : 0;
+  if (Hkv < 1 || Hq % Hkv) return fail(SPATTN_ERR_INVALID_ARG, "KV heads must divide query heads");
+  int64_t maxp;
+  if ((rc = check_bounds(bounds, B, Hkv, d, q->dtype, maxp))) return rc;
+  const int lgP = log2_pow2(page_size, 4096);
+  if (lgP < 0) return fail(SPATTN_ERR_INVALID_ARG, "page_size must be a power of two in 1..4096");
+  if (maxp > sp::kMaxPages) return fail(SPATTN_ERR_UNSUPPORTED, "more than %d pages per request", sp::kMaxPages);
+  const int64_t ctx = maxp << lgP;
+  if (ctx >= ((int64_t)1 << 31)) return fail(SPATTN_ERR_UNSUPPORTED, "max_pages * page_size must be < 2^31");
+  if (Nq < 1 || Nq > ctx) return fail(SPATTN_ERR_INVALID_ARG, "need 1 <= Nq <= ctx");
+  if (top_pages < 0 || top_pages > 16384) return fail(SPATTN_ERR_INVALID_ARG, "top_pages must be in 0..16384");
+  if (n_local < 1 || n_local > 16384)
+    return fail(SPATTN_ERR_INVALID_ARG, "n_local must be in 1..16384 (the page holding the query is always read)");
+  if (!pg_idx_out) return fail(SPATTN_ERR_INVALID_ARG, "pg_idx_out: null tensor");
+  if ((rc = check_tensor(pg_idx_out, "pg_idx_out", 4, false))) return rc;
+  if (pg_idx_out->dtype != SPATTN_I32) return fail(SPATTN_ERR_INVALID_ARG, "pg_idx_out must be int32");
+  const int64_t G = pg_idx_out->shape[1];
+  if (pg_idx_out->shape[0] != B || pg_idx_out->shape[2] != Nq || pg_idx_out->shape[3] != (int64_t)top_pages + n_local)
+    return fail(SPATTN_ERR_INVALID_ARG, "pg_idx_out must be [B, G, Nq, top_pages + n_local]");
+  if (G < 1 || G % Hkv || Hq % G) return fail(SPATTN_ERR_INVALID_ARG, "selection groups G: H_kv | G | H_q");
+  if (Hq / G > 16) return fail(SPATTN_ERR_UNSUPPORTED, "at most 16 query heads per selection group");
+  if (B * G * Nq > 65535) return fail(SPATTN_ERR_UNSUPPORTED, "B * G * Nq must be <= 65535");
+  p.q = view(q);
+  p.bnd = bounds->data;
+  for (int i = 0; i < 3; ++i) p.bs[i] = bounds->stride[i];
+  p.B = (int)B;
+  p.Hq = (int)Hq;
+  p.Hkv = (int)Hkv;
+  p.Nq = (int)Nq;
+  p.d = (int)d;
+  p.dt = q->dtype;
+  p.lgP = lgP;
+  p.maxp = (int)maxp;
+  p.ctx = (int)ctx;
+  p.ctx_len = ctx_len;
+  sp::PageSelParams& s = p.sel;
+  s.t.B = (int)B;
+  s.t.G = (int)G;
+  s.t.Nq = (int)Nq;
+  s.t.ctx = (int)ctx;
+  s.t.K = top_pages;
+  s.t.ctx_len = ctx_len;
+  s.t.certified = false;
+  s.t.idx = (int32_t*)pg_idx_out->data;
+  for (int i = 0; i < 4; ++i) s.t.is[i] = pg_idx_out->stride[i];
+  s.lgP = lgP;
+  s.n_local = n_local;
+  s.width = top_pages + n_local;
+  return SPATTN_OK;
+}
+
+SPATTN_API size_t spattn_quest_select_workspace(const spattn_tensor* q, const spattn_tensor* bounds,
+                                                int32_t page_size, int32_t top_pages, int32_t n_local,
+                                                const spattn_tensor* pg_idx_out) {
+  sp::QuestParams p;
+  if (quest_setup(q, bounds, nullptr, page_size, top_pages, n_local, pg_idx_out, p)) return (size_t)-1;
+  return sp::quest_ws_bytes(p);
+}
+
+SPATTN_API int spattn_quest_select(const spattn_tensor* q, const spattn_tensor* bounds, const int32_t* ctx_len,
+                                   int32_t page_size, int32_t top_pages, int32_t n_local,
+                                   const spattn_tensor* pg_idx_out, int32_t* pg_count_out, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  sp::QuestParams p;
+  int rc;
+  if ((rc = quest_setup(q, bounds, ctx_len, page_size, top_pages, n_local, pg_idx_out, p))) return rc;
+  p.sel.t.count = pg_count_out;
+  const size_t need = sp::quest_ws_bytes(p);
+  if (ws_bytes < need || (need && !ws)) return fail(SPATTN_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  p.sel.ws = ws;
+  if ((rc = device_ok())) return rc;
+  return launched(sp::launch_quest_select(p, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -4,6 +4,7 @@ Orchestration only: it moves the seeded inputs to the device, owns the output
 and workspace buffers, and calls the libspattn entry points in order
 (indexer scores -> certified top-K -> sparse attention; indexer scores ->
 certified page selection -> attention over the pages of a paged KV cache;
+per-page key bounds -> Quest page selection -> attention over the chosen pages;
 block keys -> two-level block-then-token selection -> sparse attention;
 block selection -> block-sparse attention; block selection -> three-branch
 NSA attention; or a fixed window + global pattern).
@@ -78,6 +79,15 @@ class HotPath:
                 if self.fused and S.LIB.spattn_topk_workspace(None, S.ctypes.byref(self.ix), wl.topk,
                                                               S.TOPK_FUSED_INDEX) == S.SIZE_MAX:
                     self.fused = False      # this indexer shape has no fused kernel: separate calls
+        elif wl.kind == "quest":
+            width = wl.top_pages + wl.n_local
+            self.idx = torch.empty(wl.B, wl.G_sel, wl.Nq, width, dtype=torch.int32, device=device)
+            self.count = torch.empty(wl.B, wl.G_sel, wl.Nq, dtype=torch.int32, device=device)
+            self.sel = S.selection(S.SEL_PAGES, self.idx, block_size=wl.page_size)
+            # per-page key bounds, formed once (a decode loop refreshes a page's entry when it fills)
+            self.bounds = torch.empty(wl.B, self.page_table.shape[1], wl.Hkv, 2 * wl.d, dtype=self.k.dtype,
+                                      device=device)
+            S.spattn_quest_page_bounds(self.k, self.pages, self.ctx_len, self.bounds)
         elif wl.kind in ("blocks", "nsa"):
             self.idx = torch.empty(wl.B, wl.Hq, wl.Nq, wl.top_blocks, dtype=torch.int32, device=device)
             self.count = torch.empty(wl.B, wl.Hq, wl.Nq, dtype=torch.int32, device=device)
@@ -116,6 +126,10 @@ class HotPath:
                 if self.fused:
                     q.append(S.LIB.spattn_topk_workspace(None, byref(self.ix), wl.topk, S.TOPK_FUSED_INDEX))
         tq, tk = S.tensor(self.q), S.tensor(self.k)
+        if self.wl.kind == "quest":
+            q.append(S.LIB.spattn_quest_select_workspace(byref(tq), byref(S.tensor(self.bounds)), self.wl.page_size,
+                                                         self.wl.top_pages, self.wl.n_local,
+                                                         byref(S.tensor(self.idx))))
         if self.wl.kind in ("blocks", "nsa"):
             q.append(S.LIB.spattn_block_select_workspace(byref(tq), byref(tk), self.wl.block_size,
                                                          self.wl.top_blocks))
@@ -156,6 +170,10 @@ class HotPath:
         S.spattn_page_select(None, None, self.ix, self.ctx_len, self.wl.page_size, self.wl.top_pages,
                              self.wl.n_local, S.TOPK_FUSED_INDEX, self.idx, self.count, self.ws, stream)
 
+    def quest_select(self, stream=None):
+        S.spattn_quest_select(self.q, self.bounds, self.ctx_len, self.wl.page_size, self.wl.top_pages,
+                              self.wl.n_local, self.idx, self.count, self.ws, stream)
+
     def block_select(self, stream=None):
         S.spattn_block_select(self.q, self.k, self.ctx_len, self.wl.block_size, self.wl.top_blocks,
                               self.idx, self.count, self.ws, stream)
@@ -190,6 +208,8 @@ class HotPath:
                 self.topk(stream)
         elif self.wl.kind in ("blocks", "nsa"):
             self.block_select(stream)
+        elif self.wl.kind == "quest":
+            self.quest_select(stream)
         self.attention(stream)
         if self.wl.backward:
             self.attention_bwd(stream)

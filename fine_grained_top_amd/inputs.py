@@ -174,7 +174,7 @@ def uniform01(seed: int, tid: int, shape) -> np.ndarray:
 class Workload:
     name: str
     kind: str                 # topk | window_global | blocks | nsa | dsa_prefill | dsa_decode | dsa_pages |
-                              # dsa_two_level
+                              # dsa_two_level | quest
     B: int
     Hq: int
     Hkv: int
@@ -201,7 +201,8 @@ class Workload:
     top_blocks: int = 0
     shift_frac: float = 0.0
     shift: float = 0.0
-    # page-granular selection over a paged KV cache (dsa_pages)
+    # page-granular selection over a paged KV cache (dsa_pages, quest; for quest G_sel is
+    # the number of page lists per row, H_kv | G_sel | H_q)
     page_size: int = 0
     top_pages: int = 0
     n_local: int = 0
@@ -285,6 +286,14 @@ _add(dataclasses.replace(TWO, name="dsa_two_level_prefill_small", B=1, Hq=8, Hkv
 _add(dataclasses.replace(PAGED, name="dsa_paged_prefill_small", B=1, Hq=8, Hkv=2, N=700, Nq=700,
                          H_I=4, G_sel=2, idx_k_dtype="bf16", page_size=16, top_pages=5,
                          n_local=1, len_range=None))
+# Query-aware page selection with no indexer (Quest's bounds): the decode
+# shapes above, one page list per KV group from the group's four query heads,
+# the 31 best 64-token pages plus the page holding the query (2048 tokens).
+QUEST = _add(dataclasses.replace(DECODE, name="quest_decode", kind="quest", seed=12, H_I=0, d_I=0, G_sel=8,
+                                 topk=0, page_size=64, top_pages=31, n_local=1))
+_add(dataclasses.replace(QUEST, name="quest_decode_small", B=3, N=9000, top_pages=6, len_range=(6000, 9000)))
+_add(dataclasses.replace(QUEST, name="quest_prefill_small", B=1, Hq=8, Hkv=2, N=700, Nq=700, G_sel=8,
+                         page_size=16, top_pages=5, n_local=2, len_range=None))
 
 
 def lengths(w: Workload) -> np.ndarray:

@@ -83,6 +83,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "spattn_nsa_fwd_workspace": (sz, [P(Tensor), P(Tensor), i32, P(Tensor), i32]),
         "spattn_nsa_fwd": (ctypes.c_int, [P(Tensor), P(Tensor), P(Tensor), vp, ctypes.c_float, i32, P(Tensor), i32,
                                           P(Tensor), P(Tensor), vp, sz, vp]),
+        "spattn_quest_page_bounds": (ctypes.c_int, [P(Tensor), P(KvPages), vp, P(Tensor), vp]),
+        "spattn_quest_select_workspace": (sz, [P(Tensor), P(Tensor), i32, i32, i32, P(Tensor)]),
+        "spattn_quest_select": (ctypes.c_int, [P(Tensor), P(Tensor), vp, i32, i32, i32, P(Tensor), vp, vp, sz,
+                                               vp]),
         "spattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "spattn_version": (ctypes.c_char_p, []),
         "spattn_last_error_message": (ctypes.c_char_p, []),
@@ -214,6 +218,27 @@ def spattn_page_select(scores: Optional[torch.Tensor], err: Optional[torch.Tenso
     _check(LIB.spattn_page_select(scp, _ptr(err), ixp, _ptr(ctx_len), page_size, top_pages, n_local,
                                   flags, ctypes.byref(io), _ptr(pg_count_out), _ptr(ws),
                                   0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def spattn_quest_page_bounds(k_pool: torch.Tensor, pages: KvPages, ctx_len: Optional[torch.Tensor],
+                             bounds_out: torch.Tensor, stream=None) -> None:
+    _check(LIB.spattn_quest_page_bounds(ctypes.byref(tensor(k_pool)), ctypes.byref(pages), _ptr(ctx_len),
+                                        ctypes.byref(tensor(bounds_out)), _stream(stream)))
+
+
+def spattn_quest_select(q: torch.Tensor, bounds: torch.Tensor, ctx_len: Optional[torch.Tensor], page_size: int,
+                        top_pages: int, n_local: int, pg_idx_out: torch.Tensor,
+                        pg_count_out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                        stream=None) -> None:
+    tq, tb, io = tensor(q), tensor(bounds), tensor(pg_idx_out)
+    need = LIB.spattn_quest_select_workspace(ctypes.byref(tq), ctypes.byref(tb), page_size, top_pages, n_local,
+                                             ctypes.byref(io))
+    if need == SIZE_MAX:
+        raise SpattnError(1, LIB.spattn_last_error_message().decode())
+    ws = _workspace(need, q.device, ws)
+    _check(LIB.spattn_quest_select(ctypes.byref(tq), ctypes.byref(tb), _ptr(ctx_len), page_size, top_pages, n_local,
+                                   ctypes.byref(io), _ptr(pg_count_out), _ptr(ws), 0 if ws is None else ws.numel(),
+                                   _stream(stream)))
 
 
 def spattn_pool_index_keys(ix: Indexer, ctx_len: Optional[torch.Tensor], block_size: int,

@@ -384,6 +384,51 @@ SPATTN_API int spattn_nsa_fwd(const spattn_tensor* q, const spattn_tensor* k, co
                               const spattn_tensor* blk_idx, int32_t window, const spattn_tensor* gates,
                               const spattn_tensor* o_out, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * spattn_quest_page_bounds / spattn_quest_select — query-aware page selection
+ * without a trained indexer.
+ * Source: "Sparse Attention" (completesystemdesign.dev), inference-only
+ * alternatives (Quest-style page-wise KV selection: the page idea of DSA at
+ * serving time, no retraining). The page names no criterion; the library
+ * takes Quest's published one (Tang et al., 2024): per page and channel the
+ * smallest and largest key of the page's tokens, and for a query the bound
+ * sum_c max(q_c min_c, q_c max_c), the largest q . x over the box the keys
+ * span, so no token of the page scores above it.
+ *
+ * spattn_quest_page_bounds: for every complete page pg < ctx_len[b] / P of
+ *  every request, bounds_out[b, pg, h, 0:d] = channel-wise minimum and
+ *  bounds_out[b, pg, h, d:2d] = maximum of the keys of that page's P tokens
+ *  (KV head h). Exact (no rounding). Entries of other pages are not written.
+ *  k_pool [n_pages, H_kv, P, d] and pages as for spattn_sparse_attn_fwd_paged;
+ *  bounds_out [B, max_pages, H_kv, 2d] in k_pool's dtype, rows 16-byte
+ *  aligned. A decode loop refreshes a page's entry once the page is full.
+ *
+ * spattn_quest_select: row (b, g, r) at position p = ctx_len[b] - Nq + r.
+ *  Selection group g of G (H_kv divides G, G divides H_q, H_q / G <= 16)
+ *  serves query heads g*H_q/G .. (g+1)*H_q/G - 1. The n_local >= 1 most
+ *  recent pages (the one holding p and those before it, so every candidate
+ *  page is complete) are always read. Each earlier page is a candidate whose
+ *  key is the float32 nearest to the exact sum over the group's heads of
+ *  their bounds for that page (bf16/f32 products exact in float64, the sum
+ *  certified, an exact wide sum near a rounding boundary), and the
+ *  min(top_pages, #candidates) best by (key descending, page ascending)
+ *  are added. pg_idx_out int32 [B, G, Nq, top_pages + n_local]: logical page
+ *  ids ascending, -1 padded (feed to spattn_sparse_attn_fwd_paged with
+ *  SPATTN_SEL_PAGES); pg_count_out int32 [B, G, Nq] (optional).
+ *  q [B, H_q, Nq, d] in the bounds' dtype (f32 or bf16), d 64 or 128.
+ *  Limits: P a power of two in 1..4096; max_pages <= 16384; top_pages <= 16384.
+ *  Workspace: B * G * Nq * max_pages * 4 bytes (the page keys).
+ * ---------------------------------------------------------------------- */
+SPATTN_API int spattn_quest_page_bounds(const spattn_tensor* k_pool, const spattn_kv_pages* pages,
+                                        const int32_t* ctx_len, const spattn_tensor* bounds_out, void* stream);
+SPATTN_API size_t spattn_quest_select_workspace(const spattn_tensor* q, const spattn_tensor* bounds,
+                                                int32_t page_size, int32_t top_pages, int32_t n_local,
+                                                const spattn_tensor* pg_idx_out);
+SPATTN_API int spattn_quest_select(const spattn_tensor* q, const spattn_tensor* bounds, const int32_t* ctx_len,
+                                   int32_t page_size, int32_t top_pages, int32_t n_local,
+                                   const spattn_tensor* pg_idx_out, int32_t* pg_count_out, void* ws,
+                                   size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ helpers */
 SPATTN_API const char* spattn_status_string(int status);
 SPATTN_API const char* spattn_version(void);

@@ -293,3 +293,49 @@ def test_backward_validation():
     assert call(lp=None) == 1                                     # the forward's LSE is required
     assert call(oo=torch.zeros(1, 4, 8, 64)) == 1
     assert call(dkk=torch.zeros(1, 2, 16, 128, dtype=torch.bfloat16)) == 1
+
+
+def test_quest_validation():
+    B, Hq, Hkv, Nq, d, maxp, P = 2, 8, 2, 1, 128, 5, 16
+    q = torch.zeros(B, Hq, Nq, d, dtype=torch.bfloat16)
+    bnd = torch.zeros(B, maxp, Hkv, 2 * d, dtype=torch.bfloat16)
+    io = torch.zeros(B, Hkv, Nq, 4, dtype=torch.int32)
+    ws = torch.zeros(1 << 20, dtype=torch.uint8)
+
+    def sel(top=3, loc=1, P_=P, qq=q, bb=bnd, idx=io, ws_bytes=1 << 20):
+        tq, tb, to = S.tensor(qq), S.tensor(bb), S.tensor(idx)
+        return S.LIB.spattn_quest_select(ctypes.byref(tq), ctypes.byref(tb), None, P_, top, loc, ctypes.byref(to),
+                                         None, ws.data_ptr(), ws_bytes, None)
+
+    need = S.LIB.spattn_quest_select_workspace(ctypes.byref(S.tensor(q)), ctypes.byref(S.tensor(bnd)), P, 3, 1,
+                                               ctypes.byref(S.tensor(io)))
+    assert need == B * Hkv * Nq * maxp * 4
+    assert sel() == 4                                        # valid: reaches the device check
+    assert sel(idx=torch.zeros(B, Hq, Nq, 4, dtype=torch.int32)) == 4    # one list per query head
+    assert sel(ws_bytes=need - 1) == 3
+    assert sel(loc=0, top=4) == 1                            # the query's own page must be read
+    assert "n_local" in S.spattn_last_error_message()
+    assert sel(top=2) == 1                                   # width must be top_pages + n_local
+    assert sel(idx=torch.zeros(B, 3, Nq, 4, dtype=torch.int32)) == 1     # H_kv must divide G
+    assert sel(P_=24) == 1                                   # page size not a power of two
+    assert sel(bb=torch.zeros(B, maxp, Hkv, d, dtype=torch.bfloat16)) == 1   # bounds need 2d
+    assert sel(bb=bnd.float()) == 1                          # bounds in q's dtype
+    assert sel(qq=torch.zeros(B, Hq, Nq, 96, dtype=torch.bfloat16),
+               bb=torch.zeros(B, maxp, Hkv, 192, dtype=torch.bfloat16)) == 2   # head dim 96
+    big = torch.zeros(1, 64, 1, d, dtype=torch.bfloat16)
+    assert sel(qq=big, bb=torch.zeros(1, maxp, 2, 2 * d, dtype=torch.bfloat16),
+               idx=torch.zeros(1, 2, 1, 4, dtype=torch.int32)) == 2            # 32 heads per group
+
+    pool = torch.zeros(7, Hkv, P, d, dtype=torch.bfloat16)
+    table = torch.zeros(B, maxp, dtype=torch.int32)
+
+    def bounds(kk=pool, tab=table, P_=P, bb=bnd):
+        pg = S.kv_pages(tab, P_)
+        return S.LIB.spattn_quest_page_bounds(ctypes.byref(S.tensor(kk)), ctypes.byref(pg), None,
+                                              ctypes.byref(S.tensor(bb)), None)
+
+    assert bounds() == 4
+    assert bounds(tab=torch.zeros(B, maxp + 1, dtype=torch.int32)) == 1      # max_pages disagree
+    assert bounds(P_=32) == 1                                                 # pool rows are pages of 16
+    assert bounds(bb=bnd.float()) == 1                                        # bounds in the key dtype
+    assert bounds(bb=torch.zeros(B, maxp, 3, 2 * d, dtype=torch.bfloat16)) == 1   # KV heads disagree

@@ -48,7 +48,7 @@ def check_sets(hp, res, rows, wl):
     idx = hp.idx.cpu().numpy()
     cnt = hp.count.cpu().numpy()
     groups = wl.Hq if wl.kind in ("blocks", "nsa") else wl.G_sel
-    listed = wl.kind in ("blocks", "nsa", "dsa_pages")   # block or page lists, not token sets
+    listed = wl.kind in ("blocks", "nsa", "dsa_pages", "quest")   # block or page lists, not token sets
     bad = 0
     for (b, r) in rows:
         for g in range(groups):
@@ -134,7 +134,8 @@ def test_tiny_fp32_full():
 @pytest.mark.parametrize("name", ["dsa_decode_small", "dsa_prefill_small", "window_global_small",
                                   "block_sparse_small", "tiny_topk_f32_small", "dsa_paged_decode_small",
                                   "dsa_paged_prefill_small", "window_stride_small", "nsa_blocks_small",
-                                  "dsa_two_level_decode_small", "dsa_two_level_prefill_small"])
+                                  "dsa_two_level_decode_small", "dsa_two_level_prefill_small",
+                                  "quest_decode_small", "quest_prefill_small"])
 def test_small_workload(name):
     wl = gen.WORKLOADS[name]
     inp = gen.generate(wl)
@@ -976,3 +977,69 @@ def test_attention_backward(mode, dtype):
             for got, ref in ((dq, rq), (dk, rk), (dv, rv))]
     say(f"  relative max errors dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}")
     assert max(errs) <= 1e-4
+
+
+# ---------------------------------------------------------------- Quest page selection
+def _quest_case(dtype, d, tails):
+    """A paged cache whose page keys sit on float32 rounding midpoints and tie
+    often: query (1, 1, 0, ...), every key's channel 0 is 1 and channel 1 one
+    of `tails`, so a page's bound is 1 + its largest tail (one head)."""
+    B, Hkv, P, npg = 2, 2, 4, 40
+    ctx = P * npg
+    rng = np.random.default_rng(71)
+    K = np.zeros((B, Hkv, ctx, d), np.float64)
+    K[..., 0] = 1.0
+    K[..., 1] = np.array(tails)[rng.integers(0, len(tails), size=(B, Hkv, ctx))]
+    K[..., 2:] = rng.integers(-2, 3, size=(B, Hkv, ctx, d - 2))
+    q = np.zeros((B, Hkv, 1, d), np.float64)
+    q[..., 0] = 1.0
+    q[..., 1] = 1.0
+    return K, q, P, npg
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_quest_bounds_and_ties(dtype, d):
+    """Per-page bounds equal the exact channel minima and maxima; page lists
+    equal the oracle's where many bounds tie and sit on float32 midpoints (the
+    exact-sum path), with a partial last page and ragged lengths."""
+    import oracle as orc
+    sp = S()
+    say(f"[gpu] quest bounds and ties {dtype} d={d}")
+    tails = [0.0, 2.0 ** -24, 3 * 2.0 ** -24, -(2.0 ** -25), -3 * 2.0 ** -25, 2.0 ** -20]
+    K, q, P, npg = _quest_case(dtype, d, tails)
+    B, Hkv, ctx, _ = K.shape
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    # pool: logical page (b, pg) at slot perm[b * npg + pg]
+    perm = np.random.default_rng(72).permutation(B * npg)
+    pool = np.zeros((B * npg, Hkv, P, d))
+    table = np.zeros((B, npg), np.int32)
+    for b in range(B):
+        for pg in range(npg):
+            pool[perm[b * npg + pg]] = K[b, :, pg * P:(pg + 1) * P]
+            table[b, pg] = perm[b * npg + pg]
+    kp = torch.from_numpy(pool).to(tdt).cuda()
+    tab = torch.from_numpy(table).cuda()
+    pages = sp.kv_pages(tab, P)
+    lens = [ctx, ctx - 7]
+    cl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    bnd = torch.full((B, npg, Hkv, 2 * d), float("nan"), dtype=tdt, device="cuda")
+    sp.spattn_quest_page_bounds(kp, pages, cl, bnd)
+    qd = torch.from_numpy(q).to(tdt).cuda()
+    for top, loc in ((5, 1), (12, 2), (40, 1)):
+        io = torch.empty(B, Hkv, 1, top + loc, dtype=torch.int32, device="cuda")
+        cnt = torch.empty(B, Hkv, 1, dtype=torch.int32, device="cuda")
+        sp.spattn_quest_select(qd, bnd, cl, P, top, loc, io, cnt)
+        torch.cuda.synchronize()
+        got, gc = io.cpu().numpy(), cnt.cpu().numpy()
+        for b in range(B):
+            p = lens[b] - 1
+            for h in range(Hkv):
+                want = orc.quest_select(q[b, h], K[b, h], p, P, top, loc)
+                assert gc[b, h, 0] == len(want) and np.array_equal(got[b, h, 0, :len(want)], want), (b, h, top)
+                assert np.all(got[b, h, 0, len(want):] == -1)
+    bn = bnd.float().cpu().numpy()
+    for b in range(B):
+        for pg in range(lens[b] // P):
+            rows = K[b, :, pg * P:(pg + 1) * P]                # [Hkv, P, d]
+            assert np.array_equal(bn[b, pg, :, :d], rows.min(axis=1))
+            assert np.array_equal(bn[b, pg, :, d:], rows.max(axis=1))
