@@ -174,7 +174,7 @@ def uniform01(seed: int, tid: int, shape) -> np.ndarray:
 class Workload:
     name: str
     kind: str                 # topk | window_global | blocks | nsa | dsa_prefill | dsa_decode | dsa_pages |
-                              # dsa_two_level | quest
+                              # dsa_two_level | quest | msa
     B: int
     Hq: int
     Hkv: int
@@ -286,6 +286,19 @@ _add(dataclasses.replace(TWO, name="dsa_two_level_prefill_small", B=1, Hq=8, Hkv
 _add(dataclasses.replace(PAGED, name="dsa_paged_prefill_small", B=1, Hq=8, Hkv=2, N=700, Nq=700,
                          H_I=4, G_sel=2, idx_k_dtype="bf16", page_size=16, top_pages=5,
                          n_local=1, len_range=None))
+# Blockwise selection per GQA group (MSA-style) on the block-sparse prefill
+# shapes with four KV groups: an 8-head indexer (two heads per group) rates
+# each complete 64-token block by its mean indexer key, each group keeps its
+# 16 best blocks, and every head of the group attends over them plus a
+# 512-token window.
+MSA = _add(Workload("msa_prefill", "msa", B=1, Hq=16, Hkv=4, N=32768, Nq=32768, d=128, dtype="bf16", seed=13,
+                    H_I=8, d_I=64, G_sel=4, G_k=1, idx_q_dtype="bf16", idx_k_dtype="bf16",
+                    score_mode="weighted_relu", block_size=64, top_blocks=16, window=512))
+_add(dataclasses.replace(MSA, name="msa_prefill_small", Hq=4, Hkv=2, N=1500, Nq=1500, H_I=4, G_sel=2,
+                         top_blocks=4, window=100))
+_add(dataclasses.replace(MSA, name="msa_decode_small", B=3, Hq=8, Hkv=2, N=9000, Nq=1, H_I=4, G_sel=2,
+                         idx_k_dtype="fp8", top_blocks=8, window=64, len_range=(6000, 9000)))
+
 # Query-aware page selection with no indexer (Quest's bounds): the decode
 # shapes above, one page list per KV group from the group's four query heads,
 # the 31 best 64-token pages plus the page holding the query (2048 tokens).

@@ -59,6 +59,14 @@ What is computed (sources are the five pages on sparse attention):
   here as the largest key among the page's visible tokens. The recent pages
   are the n_local pages ending with the one that holds the query position;
   every earlier page competes by (page key descending, page index ascending).
+* Blockwise selection per GQA group ("Sparse Attention in 2026", MSA
+  paragraph: an index branch scores and picks the top-k KV blocks for each
+  GQA group and the main branch attends exactly over them). The page does
+  not say how the index branch rates a block; it is read as the indexer's own
+  score on the block's mean indexer key (kept in float32, as in the two-level
+  coarse pass), over complete past blocks, ranked by (key descending, block
+  ascending) with no softmax, and the query's local window is attended too
+  (as for the block-sparse pattern), so every row sees at least itself.
 * Query-aware page selection without a trained indexer ("Sparse Attention"
   (completesystemdesign.dev), inference-only alternatives: Quest-style
   page-wise KV selection). The page names no criterion; Quest's published one
@@ -375,6 +383,13 @@ def quest_select(Q: np.ndarray, K: np.ndarray, p: int, P: int, top_pages: int, n
     return np.concatenate([chosen, local]).astype(np.int32)
 
 
+def group_block_select(block_keys: np.ndarray, p: int, bs: int, top_blocks: int) -> np.ndarray:
+    """Blocks one GQA group reads at position p: the min(top_blocks, count)
+    complete past blocks best by (block key descending, block ascending),
+    ascending. block_keys: the keys of blocks 0..(p+1)//bs - 1 at least."""
+    return topk(block_keys[:(p + 1) // bs], top_blocks)
+
+
 def pages_set(pages: Sequence[int], p: int, P: int) -> np.ndarray:
     """Every token of the listed pages, within 0..p (pages are read whole)."""
     parts = [np.arange(P * pg, P * pg + P) for pg in pages]
@@ -528,7 +543,28 @@ def run(wl, inp: Dict[str, np.ndarray], rows: Iterable[Tuple[int, int]],
         Kb = [decode(Kst[b, h, :n], wl.dtype) for h in range(wl.Hkv)]
         # visible set per query head
         S_of_head: List[np.ndarray] = [None] * wl.Hq
-        if wl.kind in ("topk", "dsa_prefill", "dsa_decode", "dsa_pages", "dsa_two_level"):
+        if wl.kind == "msa":
+            qi = decode(inp["q_idx"][b, r], wl.idx_q_dtype)
+            hpg = wl.H_I // wl.G_sel
+            w = np.asarray(inp["w"], dtype=np.float32).astype(np.float64)
+            nbe = n // wl.block_size
+            for g in range(wl.G_sel):
+                kg = g if wl.G_k == wl.G_sel else 0
+                Kp = pooled_blocks(decode(inp["k_idx"][b, :nbe * wl.block_size, kg], wl.idx_k_dtype),
+                                   wl.block_size, nbe, "f32")
+                if wl.score_mode == "dot":
+                    bkeys = keys_dot(qi[g * hpg], Kp)
+                else:
+                    bkeys = keys_weighted_relu(qi[g * hpg:(g + 1) * hpg], w[g * hpg:(g + 1) * hpg], Kp)
+                blk = group_block_select(bkeys, p, wl.block_size, wl.top_blocks)
+                res.blocks[(b, g, r)] = blk
+                if keep_keys:
+                    res.keys[(b, g, r)] = bkeys
+                S = blocks_set(blk, p, wl.block_size, wl.window)
+                res.sets[(b, g, r)] = S
+                for h in range(g * (wl.Hq // wl.G_sel), (g + 1) * (wl.Hq // wl.G_sel)):
+                    S_of_head[h] = S
+        elif wl.kind in ("topk", "dsa_prefill", "dsa_decode", "dsa_pages", "dsa_two_level"):
             qi = decode(inp["q_idx"][b, r], wl.idx_q_dtype)            # [H_I, d_I]
             hpg = wl.H_I // wl.G_sel
             w = np.asarray(inp["w"], dtype=np.float32).astype(np.float64)

@@ -4,6 +4,7 @@ None of these compares the oracle with itself: each uses a library routine
 (torch SDPA, numpy's correctly rounded float casts, math.fsum), a hand-worked
 value, a closed form or a brute-force enumeration.
 """
+import dataclasses
 import json
 import math
 import os
@@ -699,3 +700,51 @@ def test_quest_key_rounds_exact_midpoints_to_even():
         K = np.array([[1.0, tail], [1.0, tail]])
         got = orc.quest_page_keys(Q, K, 2, 1)
         assert got[0] == np.float32(want), (tail, got[0], want)
+
+
+# ---------------------------------------------------------------- blocks per GQA group
+@pytest.mark.parametrize("seed", [0, 1])
+def test_group_block_select_brute_force(seed):
+    """Each group's blocks: the block mean of the indexer keys rounded once to
+    float32 (exact rational mean), the indexer's exact weighted-ReLU score on
+    it rounded once, then a full sort by (key desc, block asc) -- all in exact
+    arithmetic, against the oracle's certified path."""
+    rng = np.random.default_rng(seed)
+    d, H, bs, n = 8, 3, 4, 37
+    to_bf = lambda x: gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(x.astype(np.float32))).astype(np.float64)
+    Q = to_bf(rng.standard_normal((H, d)))
+    w = rng.random(H).astype(np.float32).astype(np.float64)
+    K = to_bf(rng.standard_normal((n, d)))
+    for p in (3, 4, 17, 36):
+        nbe = (p + 1) // bs
+        means = [[orc.f32_nearest(sum(Fraction(float(K[bi * bs + t, c])) for t in range(bs)) / bs)
+                  for c in range(d)] for bi in range(nbe)]
+        keys = []
+        for bi in range(nbe):
+            tot = Fraction(0)
+            for h in range(H):
+                dot = sum(Fraction(float(Q[h, c])) * Fraction(float(means[bi][c])) for c in range(d))
+                tot += Fraction(float(w[h])) * max(dot, Fraction(0))
+            keys.append(orc.f32_nearest(tot))
+        want = sorted(sorted(range(nbe), key=lambda i: (-float(keys[i]), i))[:5])
+        Kp = orc.pooled_blocks(K, bs, nbe, "f32")
+        got = orc.group_block_select(orc.keys_weighted_relu(Q, w, Kp), p, bs, 5)
+        assert got.tolist() == want, p
+
+
+def test_group_blocks_full_coverage_is_causal_gqa():
+    """Enough blocks and a window of one block: every head of every group sees
+    its whole causal prefix, so the output is causal attention (torch SDPA in
+    float64) with K/V shared within each group."""
+    wl = dataclasses.replace(gen.WORKLOADS["msa_prefill_small"], N=130, Nq=130, top_blocks=10, window=64)
+    inp = gen.generate(wl)
+    rows = [(0, r) for r in range(0, 130, 7)]
+    res = orc.run(wl, inp, rows)
+    q = torch.from_numpy(orc.decode(inp["q"][0], "bf16"))
+    k = torch.from_numpy(orc.decode(inp["k"][0], "bf16")).repeat_interleave(wl.Hq // wl.Hkv, dim=0)
+    v = torch.from_numpy(orc.decode(inp["v"][0], "bf16")).repeat_interleave(wl.Hq // wl.Hkv, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True).numpy()
+    for (b, r) in rows:
+        assert np.abs(res.O[(b, r)] - ref[:, r]).max() < 1e-12
+        for g in range(wl.G_sel):
+            assert res.sets[(b, g, r)].tolist() == list(range(r + 1))
