@@ -69,7 +69,23 @@ def algorithmic(wl, inp, hp, fused):
     lens = inp["ctx_len"].astype(np.int64)
     qkv_out = wl.B * wl.Hq * wl.Nq * wl.d * (e + 4) + wl.B * wl.Hq * wl.Nq * 4   # q in, O and LSE out
     out = {}
-    if wl.H_I:
+    if wl.kind == "msa":
+        # block lists per KV group, read by the group's query heads; blocks inside the window count once
+        blk = hp.idx.cpu().numpy()                                                # [B, G, Nq, nb]
+        pos = np.stack([L - wl.Nq + np.arange(wl.Nq) for L in lens])[:, None, :]  # [B, 1, Nq]
+        ws_ = np.maximum(0, pos - wl.window + 1)
+        valid = blk >= 0
+        lo = blk * wl.block_size
+        in_win = np.clip(np.minimum(lo + wl.block_size, pos[..., None] + 1) - np.maximum(lo, ws_[..., None]), 0, None)
+        size = (valid * wl.block_size).sum(-1) - (valid * in_win).sum(-1) + (pos - ws_ + 1)
+        pairs = float(size.sum()) * (wl.Hq // wl.G_sel)
+        kv = wl.B * wl.Hkv * wl.N * wl.d * e * 2
+        out["attention"] = {"bytes": kv + qkv_out, "flops": 4.0 * pairs * wl.d, "bound": "mfma", "pairs": pairs}
+        nbe = float(((pos[:, 0, :] + 1) // wl.block_size).sum())              # complete blocks over the rows
+        out["index_block_select"] = {"bytes": nbe * wl.G_sel * wl.d_I * 4 + blk.size * 4
+                                     + wl.B * wl.Nq * wl.H_I * wl.d_I * 2,
+                                     "flops": 2.0 * nbe * wl.H_I * wl.d_I, "rows": wl.B * wl.G_sel * wl.Nq}
+    elif wl.H_I:
         kb = {"fp8": 1, "bf16": 2, "f32": 4}[wl.idx_k_dtype]
         pos = np.concatenate([L - wl.Nq + np.arange(wl.Nq) for L in lens])
         cand = float(np.sum(pos + 1))                      # (row, key) pairs scored per group
@@ -222,7 +238,9 @@ def main():
 
     stream = torch.cuda.current_stream()
     stages = []
-    if wl.H_I and fused and wl.kind == "dsa_pages":
+    if wl.kind == "msa":
+        stages = [("index_block_select", lambda hp: hp.index_block_select()), ("attention", lambda hp: hp.attention())]
+    elif wl.H_I and fused and wl.kind == "dsa_pages":
         stages = [("index_page_fused", lambda hp: hp.page_select_fused()), ("attention", lambda hp: hp.attention())]
     elif wl.H_I and fused:
         stages = [("index_topk_fused", lambda hp: hp.topk_fused()), ("attention", lambda hp: hp.attention())]
@@ -334,7 +352,7 @@ def main():
             ok &= err <= (1e-5 if wl.dtype == "f32" else 2e-3)
             if idx is not None and wl.kind not in ("blocks", "nsa"):
                 for g in range(wl.G_sel):
-                    want = res.blocks[(b, g, r)] if wl.kind in ("dsa_pages", "quest") else res.sets[(b, g, r)]
+                    want = res.blocks[(b, g, r)] if wl.kind in ("dsa_pages", "quest", "msa") else res.sets[(b, g, r)]
                     ok &= bool(np.array_equal(idx[b, g, r, : len(want)], want))
             if time.perf_counter() - t0 > args.cpu_seconds:
                 break
@@ -362,6 +380,8 @@ def main():
                  + ", attention over a paged KV cache" if wl.kind == "dsa_pages" else
                  "Quest page selection from per-page key bounds (bounds formed before timing), attention over "
                  "a paged KV cache" if wl.kind == "quest" else
+                 "top blocks per GQA group by the indexer on block-mean keys (block-key cache formed before "
+                 "timing), block-sparse attention with the group's list" if wl.kind == "msa" else
                  "two-level block-then-token selection (block-key cache formed before timing)"
                  if wl.kind == "dsa_two_level" else
                  "fused indexer+top-K" if fused else "separate indexer and top-K calls"),
@@ -376,8 +396,10 @@ def main():
     }
     if wl.page_size:
         out["config"].update({"page_size": wl.page_size, "top_pages": wl.top_pages, "n_local": wl.n_local})
-    if wl.kind in ("dsa_two_level", "nsa"):
+    if wl.kind in ("dsa_two_level", "nsa", "msa"):
         out["config"].update({"block_size": wl.block_size, "top_blocks": wl.top_blocks})
+    if wl.kind in ("msa", "nsa"):
+        out["config"].update({"window": wl.window, "G_sel": wl.G_sel})
     print(json.dumps(out), flush=True)
 
 

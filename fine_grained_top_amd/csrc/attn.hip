@@ -65,7 +65,7 @@ struct Visible {
         count += max(0, (w_start - 1) / stride - m0 + 1);
       }
     } else {
-      list = a.sel + b * a.sels[0] + h * a.sels[1] + r * a.sels[2];
+      list = a.sel + b * a.sels[0] + (h / (a.Hq / a.G_sel)) * a.sels[1] + r * a.sels[2];
       bs = a.bs;
       w_start = max(0, p - a.window + 1);
       nb_keys = K * bs;

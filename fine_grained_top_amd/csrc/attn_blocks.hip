@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kBcRows) void bc_count_kernel(AttnParams a, BcWs w)
   if (r < a.Nq) {
     const int p = L - a.Nq + r;
     const int wstart = p - a.window + 1;
-    const int32_t* sel = a.sel + b * a.sels[0] + h * a.sels[1] + (int64_t)r * a.sels[2];
+    const int32_t* sel = a.sel + b * a.sels[0] + (h / (a.Hq / a.G_sel)) * a.sels[1] + (int64_t)r * a.sels[2];
     int32_t* rk = w.rank + ((int64_t)bh * a.Nq + r) * a.K;
     for (int s = 0; s < a.K; ++s) {
       int v = -1;
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kBcRows) void bc_scatter_kernel(AttnParams a, BcWs 
   const int bh = b * a.Hq + h;
   const int r = ch * kBcRows + threadIdx.x;
   if (r >= a.Nq) return;
-  const int32_t* sel = a.sel + b * a.sels[0] + h * a.sels[1] + (int64_t)r * a.sels[2];
+  const int32_t* sel = a.sel + b * a.sels[0] + (h / (a.Hq / a.G_sel)) * a.sels[1] + (int64_t)r * a.sels[2];
   const int32_t* rk = w.rank + ((int64_t)bh * a.Nq + r) * a.K;
   const int32_t* hg = w.hist + ((int64_t)bh * w.nch + ch) * w.nbk;
   uint32_t* lst = w.list + (int64_t)bh * a.Nq * a.K;

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
     for (int e = tid; e < kTQ * a.K; e += 256) {
       const int rr = e / a.K, slot = e % a.K;
       if (q0 + rr >= a.Nq) continue;
-      const int blk = a.sel[b * a.sels[0] + h * a.sels[1] + (int64_t)(q0 + rr) * a.sels[2] + slot];
+      const int blk = a.sel[b * a.sels[0] + (h / (a.Hq / a.G_sel)) * a.sels[1] + (int64_t)(q0 + rr) * a.sels[2] + slot];
       if (blk < 0 || blk >= nbk) continue;
       atomicOr(&sm.rowblk[rr * bwords + (blk >> 5)], 1u << (blk & 31));
       const int t0 = (blk * a.bs) / kTK, t1 = min(ntiles_all - 1, (blk * a.bs + a.bs - 1) / kTK);

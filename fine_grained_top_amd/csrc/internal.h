@@ -103,6 +103,7 @@ struct TwoLevelParams {
   float* kp;               // block indexer keys [B, ctx >> lgbs, G_k, d_I] f32
   int64_t kps[4];
   int lgbs, nb;            // log2 block size, blocks kept by the first pick
+  bool blocks_only;        // emit the first pick's blocks [B, G, Nq, nb] and stop
 };
 hipError_t launch_pool_index_keys(const TwoLevelParams& p, hipStream_t st);
 hipError_t launch_two_level(const TwoLevelParams& p, hipStream_t st);

@@ -442,6 +442,28 @@ SPATTN_API int spattn_topk_two_level(const spattn_indexer* ix, const spattn_tens
   return launched(sp::launch_two_level(q, (hipStream_t)stream));
 }
 
+SPATTN_API int spattn_index_block_select(const spattn_indexer* ix, const spattn_tensor* k_blocks,
+                                         const int32_t* ctx_len, int32_t block_size, int32_t top_blocks,
+                                         const spattn_tensor* blk_idx_out, int32_t* blk_count_out, void* stream) {
+  sp::TwoLevelParams q;
+  int rc;
+  if ((rc = two_level_setup(ix, k_blocks, ctx_len, block_size, q))) return rc;
+  if (top_blocks < 1 || top_blocks > 16384) return fail(SPATTN_ERR_INVALID_ARG, "need 1 <= top_blocks <= 16384");
+  if ((rc = check_tensor(blk_idx_out, "blk_idx_out", 4, false))) return rc;
+  if (blk_idx_out->dtype != SPATTN_I32) return fail(SPATTN_ERR_INVALID_ARG, "blk_idx_out must be int32");
+  if (blk_idx_out->shape[0] != q.t.B || blk_idx_out->shape[1] != q.t.G || blk_idx_out->shape[2] != q.t.Nq ||
+      blk_idx_out->shape[3] != top_blocks)
+    return fail(SPATTN_ERR_INVALID_ARG, "blk_idx_out must be [B, G, Nq, top_blocks]");
+  q.t.idx = (int32_t*)blk_idx_out->data;
+  for (int i = 0; i < 4; ++i) q.t.is[i] = blk_idx_out->stride[i];
+  q.t.count = blk_count_out;
+  q.t.K = top_blocks;
+  q.nb = top_blocks;
+  q.blocks_only = true;
+  if ((rc = device_ok())) return rc;
+  return launched(sp::launch_two_level(q, (hipStream_t)stream));
+}
+
 // ------------------------------------------------------------------ block select
 static int check_qk(const spattn_tensor* q, const spattn_tensor* k) {
   int rc;
@@ -600,9 +622,10 @@ static int attn_setup(const spattn_tensor* q, const spattn_tensor* k, const spat
     case SPATTN_SEL_BLOCKS: {
       if ((rc = check_tensor(&sel->idx, "sel.idx", 4, false))) return rc;
       if (sel->idx.dtype != SPATTN_I32) return fail(SPATTN_ERR_INVALID_ARG, "sel.idx must be int32");
-      if (sel->idx.shape[0] != p.B || sel->idx.shape[1] != p.Hq || sel->idx.shape[2] != p.Nq)
-        return fail(SPATTN_ERR_INVALID_ARG, "block list must be [B, H_q, Nq, nb]");
+      if (sel->idx.shape[0] != p.B || sel->idx.shape[1] < 1 || p.Hq % sel->idx.shape[1] || sel->idx.shape[2] != p.Nq)
+        return fail(SPATTN_ERR_INVALID_ARG, "block list must be [B, G_sel, Nq, nb] with G_sel | H_q");
       if (sel->block_size < 1 || sel->window < 0) return fail(SPATTN_ERR_INVALID_ARG, "bad block_size/window");
+      p.G_sel = (int)sel->idx.shape[1];
       p.K = (int)sel->idx.shape[3];
       p.sel = (const int32_t*)sel->idx.data;
       for (int i = 0; i < 4; ++i) p.sels[i] = sel->idx.stride[i];
@@ -731,6 +754,7 @@ static int nsa_setup(const spattn_tensor* q, const spattn_tensor* k, const spatt
   sel.idx = *blk_idx;
   sel.block_size = block_size;
   if ((rc = attn_setup(q, k, v, &sel, p.a, need_v))) return rc;
+  if (p.a.G_sel != p.a.Hq) return fail(SPATTN_ERR_INVALID_ARG, "blk_idx must be [B, H_q, Nq, nb]");
   p.a.window = window;
   return SPATTN_OK;
 }

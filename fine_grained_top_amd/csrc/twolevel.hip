@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kTlThreads) void two_level_kernel(TwoLevelParams q)
   const int pos = L - p.Nq + r;
   int32_t* out = p.idx + b * p.is[0] + g * p.is[1] + r * p.is[2];
   int32_t* cnt = p.count ? p.count + ((int64_t)b * p.G + g) * p.Nq + r : nullptr;
-  const int K = p.K;
+  const int K = q.blocks_only ? q.nb : p.K;
   if (pos < 0) {
     for (int i = tid; i < K; i += T) out[i] = -1;
     if (cnt && tid == 0) *cnt = 0;
@@ -300,6 +300,18 @@ __global__ __launch_bounds__(kTlThreads) void two_level_kernel(TwoLevelParams q)
       sm.bm[w] = lo >= nbe ? 0u : (nbe - lo >= 32 ? 0xFFFFFFFFu : (1u << (nbe - lo)) - 1u);
     }
     __syncthreads();
+  }
+
+  if (q.blocks_only) {                             // the chosen blocks, ascending
+    const int nwb = (nbe + 31) >> 5;
+    const uint32_t wv = tid < nwb ? sm.bm[tid] : 0u;
+    uint32_t nsel;
+    uint32_t opos = block_scan_sum<T>((uint32_t)__popc(wv), sm.sc, nsel);
+    for (uint32_t m = wv; m; m &= m - 1, ++opos)
+      if (opos < (uint32_t)K) out[opos] = 32 * tid + __ffs(m) - 1;
+    for (int i = (int)nsel + tid; i < K; i += T) out[i] = -1;
+    if (cnt && tid == 0) *cnt = min((int)nsel, K);
+    return;
   }
 
   // ---- candidates: the chosen blocks' tokens, ascending, then the open block

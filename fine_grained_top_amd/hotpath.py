@@ -6,6 +6,7 @@ and workspace buffers, and calls the libspattn entry points in order
 certified page selection -> attention over the pages of a paged KV cache;
 per-page key bounds -> Quest page selection -> attention over the chosen pages;
 block keys -> two-level block-then-token selection -> sparse attention;
+block keys -> top blocks per GQA group -> block-sparse attention;
 block selection -> block-sparse attention; block selection -> three-branch
 NSA attention; or a fixed window + global pattern).
 """
@@ -60,13 +61,23 @@ class HotPath:
             mode = S.SCORE_WEIGHTED_RELU if wl.score_mode == "weighted_relu" else S.SCORE_DOT
             self.ix = S.indexer(self.q_idx, self.k_idx, self.w if mode == S.SCORE_WEIGHTED_RELU else None,
                                 mode, wl.heads_per_group)
-            self.scores = torch.empty(wl.B, wl.G_sel, wl.Nq, wl.N, dtype=torch.float32, device=device)
+            # the score matrix of the separate indexer/top-K calls (block selection needs none)
+            self.scores = None if wl.kind == "msa" else \
+                torch.empty(wl.B, wl.G_sel, wl.Nq, wl.N, dtype=torch.float32, device=device)
             self.err = torch.empty(wl.B, wl.G_sel, wl.Nq, dtype=torch.float32, device=device)
             width = wl.top_pages + wl.n_local if wl.kind == "dsa_pages" else wl.topk
             self.idx = torch.empty(wl.B, wl.G_sel, wl.Nq, width, dtype=torch.int32, device=device)
             self.count = torch.empty(wl.B, wl.G_sel, wl.Nq, dtype=torch.int32, device=device)
             if wl.kind == "dsa_pages":
                 self.sel = S.selection(S.SEL_PAGES, self.idx, block_size=wl.page_size)
+            elif wl.kind == "msa":
+                # one block list per KV group, read by every query head of the group
+                self.idx = torch.empty(wl.B, wl.G_sel, wl.Nq, wl.top_blocks, dtype=torch.int32, device=device)
+                self.sel = S.selection(S.SEL_BLOCKS, self.idx, window=wl.window, block_size=wl.block_size)
+                self.fused = False
+                self.k_blocks = torch.empty(wl.B, wl.N // wl.block_size, wl.G_k, wl.d_I, dtype=torch.float32,
+                                            device=device)
+                S.spattn_pool_index_keys(self.ix, self.ctx_len, wl.block_size, self.k_blocks)
             elif wl.kind == "dsa_two_level":
                 self.sel = S.selection(S.SEL_INDEX, self.idx)
                 self.fused = False
@@ -115,7 +126,9 @@ class HotPath:
             q.append(S.LIB.spattn_index_scores_workspace(byref(self.ix)))
             ts = S.tensor(self.scores)
             wl = self.wl
-            if wl.kind == "dsa_pages":
+            if wl.kind == "msa":
+                pass
+            elif wl.kind == "dsa_pages":
                 q.append(S.LIB.spattn_page_select_workspace(byref(ts), byref(self.ix), wl.page_size, wl.top_pages,
                                                             wl.n_local, S.TOPK_CERTIFIED))
                 if self.fused:
@@ -162,6 +175,10 @@ class HotPath:
         S.spattn_topk_two_level(self.ix, self.k_blocks, self.ctx_len, self.wl.block_size, self.wl.top_blocks,
                                 self.wl.topk, self.idx, self.count, None, stream)
 
+    def index_block_select(self, stream=None):
+        S.spattn_index_block_select(self.ix, self.k_blocks, self.ctx_len, self.wl.block_size, self.wl.top_blocks,
+                                    self.idx, self.count, stream)
+
     def page_select(self, stream=None):
         S.spattn_page_select(self.scores, self.err, self.ix, self.ctx_len, self.wl.page_size, self.wl.top_pages,
                              self.wl.n_local, S.TOPK_CERTIFIED, self.idx, self.count, self.ws, stream)
@@ -200,6 +217,8 @@ class HotPath:
             self.topk_fused(stream)
         elif self.wl.H_I and self.wl.kind == "dsa_two_level":
             self.topk_two_level(stream)
+        elif self.wl.kind == "msa":
+            self.index_block_select(stream)
         elif self.wl.H_I:
             self.index_scores(stream)
             if self.wl.kind == "dsa_pages":

@@ -31,6 +31,7 @@ STAGES = {
     "topk": ["topk_row", "topk_redo", "mt_zero", "mt_hist", "mt_collect", "mt_finalize"],
     "page_select": ["page_keys_kernel", "page_select_kernel"],
     "two_level_select": ["two_level_kernel"],
+    "index_block_select": ["two_level_kernel"],
     "quest_select": ["quest_keys_kernel", "page_select_kernel"],
     "attention_bwd": ["attn_bwd_zero", "attn_bwd_generic", "attn_bwd_tile"],
     "block_select": ["pool_kernel", "block_select_kernel"],

@@ -83,6 +83,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "spattn_nsa_fwd_workspace": (sz, [P(Tensor), P(Tensor), i32, P(Tensor), i32]),
         "spattn_nsa_fwd": (ctypes.c_int, [P(Tensor), P(Tensor), P(Tensor), vp, ctypes.c_float, i32, P(Tensor), i32,
                                           P(Tensor), P(Tensor), vp, sz, vp]),
+        "spattn_index_block_select": (ctypes.c_int, [P(Indexer), P(Tensor), vp, i32, i32, P(Tensor), vp, vp]),
         "spattn_quest_page_bounds": (ctypes.c_int, [P(Tensor), P(KvPages), vp, P(Tensor), vp]),
         "spattn_quest_select_workspace": (sz, [P(Tensor), P(Tensor), i32, i32, i32, P(Tensor)]),
         "spattn_quest_select": (ctypes.c_int, [P(Tensor), P(Tensor), vp, i32, i32, i32, P(Tensor), vp, vp, sz,
@@ -254,6 +255,14 @@ def spattn_topk_two_level(ix: Indexer, k_blocks: torch.Tensor, ctx_len: Optional
     _check(LIB.spattn_topk_two_level(ctypes.byref(ix), ctypes.byref(tb), _ptr(ctx_len), block_size, top_blocks, k,
                                      ctypes.byref(io), _ptr(count_out), _ptr(ws), 0 if ws is None else ws.numel(),
                                      _stream(stream)))
+
+
+def spattn_index_block_select(ix: Indexer, k_blocks: torch.Tensor, ctx_len: Optional[torch.Tensor], block_size: int,
+                              top_blocks: int, blk_idx_out: torch.Tensor, blk_count_out: Optional[torch.Tensor] = None,
+                              stream=None) -> None:
+    _check(LIB.spattn_index_block_select(ctypes.byref(ix), ctypes.byref(tensor(k_blocks)), _ptr(ctx_len), block_size,
+                                         top_blocks, ctypes.byref(tensor(blk_idx_out)), _ptr(blk_count_out),
+                                         _stream(stream)))
 
 
 def spattn_block_select(q: torch.Tensor, k: torch.Tensor, ctx_len: Optional[torch.Tensor], block_size: int,

@@ -111,7 +111,9 @@ typedef struct spattn_selection {
   int32_t mode;          /* enum spattn_sel_mode */
   spattn_tensor idx;     /* INDEX: int32 [B, G_sel, Nq, K], ascending key positions, -1
                             padded; G_sel divides H_q and G_sel | H_kv or H_kv | G_sel.
-                            BLOCKS: int32 [B, H_q, Nq, nb] block ids, -1 padded.
+                            BLOCKS: int32 [B, G_sel, Nq, nb] block ids, -1 padded;
+                            G_sel divides H_q and query head h reads list
+                            h / (H_q / G_sel) (G_sel = H_q: one list per head).
                             PAGES: int32 [B, G_sel, Nq, np] page ids (page pg = tokens
                             pg*block_size .. pg*block_size+block_size-1), ascending, -1
                             padded (e.g. from spattn_page_select); G_sel as for INDEX. */
@@ -259,6 +261,28 @@ SPATTN_API int spattn_topk_two_level(const spattn_indexer* ix, const spattn_tens
                                      const int32_t* ctx_len, int32_t block_size, int32_t top_blocks,
                                      int32_t k, const spattn_tensor* idx_out, int32_t* count_out,
                                      void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * spattn_index_block_select — blockwise selection per GQA group.
+ * Source: "Sparse Attention in 2026: Why It Finally Had to Be Native", MSA
+ * paragraph (an index branch scores and picks the top-k KV blocks for each
+ * GQA group; the main branch attends exactly over them).
+ *
+ * Row (b,g,r) at position p: the coarse pass of spattn_topk_two_level alone.
+ * Every complete past block {beta : block_size*beta + block_size - 1 <= p}
+ * is keyed by the indexer's own score on its mean indexer key in k_blocks
+ * (from spattn_pool_index_keys), exact as for SPATTN_TOPK_CERTIFIED, and the
+ * min(top_blocks, #blocks) best by (key desc, block asc) are written
+ * ascending to blk_idx_out int32 [B, G, Nq, top_blocks], -1 padded; counts
+ * optional. G is the indexer's selection-group count: with one group per KV
+ * head the list serves every query head of that group, as a BLOCKS selection
+ * of spattn_sparse_attn_fwd (block lists [B, G, Nq, nb]).
+ *  Limits: block_size a power of two; ctx / block_size <= 8192;
+ *  top_blocks <= 16384. No workspace.
+ * ---------------------------------------------------------------------- */
+SPATTN_API int spattn_index_block_select(const spattn_indexer* ix, const spattn_tensor* k_blocks,
+                                         const int32_t* ctx_len, int32_t block_size, int32_t top_blocks,
+                                         const spattn_tensor* blk_idx_out, int32_t* blk_count_out, void* stream);
 
 /* ------------------------------------------------------------------------
  * spattn_block_select — block routing for block-sparse attention.

@@ -339,3 +339,42 @@ def test_quest_validation():
     assert bounds(P_=32) == 1                                                 # pool rows are pages of 16
     assert bounds(bb=bnd.float()) == 1                                        # bounds in the key dtype
     assert bounds(bb=torch.zeros(B, maxp, 3, 2 * d, dtype=torch.bfloat16)) == 1   # KV heads disagree
+
+
+def test_index_block_select_validation():
+    B, Nq, ctx, H_I, d_I, bs = 1, 4, 256, 4, 64, 16
+    q_idx = torch.zeros(B, Nq, H_I, d_I, dtype=torch.bfloat16)
+    k_idx = torch.zeros(B, ctx, 1, d_I, dtype=torch.bfloat16)
+    w = torch.zeros(B, Nq, H_I)
+    ix = S.indexer(q_idx, k_idx, w, S.SCORE_WEIGHTED_RELU, 2)            # two selection groups
+    kb = torch.zeros(B, ctx // bs, 1, d_I)
+
+    def call(top=3, out=None, P=bs, kbl=kb):
+        o = torch.zeros(B, 2, Nq, top, dtype=torch.int32) if out is None else out
+        return S.LIB.spattn_index_block_select(ctypes.byref(ix), ctypes.byref(S.tensor(kbl)), None, P, top,
+                                               ctypes.byref(S.tensor(o)), None, None)
+
+    assert call() == 4                                                   # valid: reaches the device check
+    assert call(top=0, out=torch.zeros(B, 2, Nq, 0, dtype=torch.int32)) == 1
+    assert call(out=torch.zeros(B, 1, Nq, 3, dtype=torch.int32)) == 1     # one list per selection group
+    assert call(out=torch.zeros(B, 2, Nq, 4, dtype=torch.int32)) == 1     # width must be top_blocks
+    assert call(P=24) == 1                                               # block size not a power of two
+    assert call(kbl=torch.zeros(B, ctx // bs, 1, d_I, dtype=torch.bfloat16)) == 1   # block keys are f32
+
+
+def test_blocks_selection_groups_validation():
+    q = torch.zeros(1, 8, 4, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 64, 128, dtype=torch.bfloat16)
+    o = torch.zeros(1, 8, 4, 128)
+
+    def call(G):
+        blk = torch.zeros(1, G, 4, 3, dtype=torch.int32)
+        sel = S.selection(S.SEL_BLOCKS, blk, window=8, block_size=16)
+        ws = torch.zeros(1 << 20, dtype=torch.uint8)
+        return S.LIB.spattn_sparse_attn_fwd(ctypes.byref(S.tensor(q)), ctypes.byref(S.tensor(k)),
+                                            ctypes.byref(S.tensor(k)), None, 0.0, ctypes.byref(sel),
+                                            ctypes.byref(S.tensor(o)), None, ws.data_ptr(), ws.numel(), None)
+
+    for G in (1, 2, 4, 8):
+        assert call(G) == 4, G                                           # G_sel divides H_q
+    assert call(3) == 1

@@ -48,7 +48,7 @@ def check_sets(hp, res, rows, wl):
     idx = hp.idx.cpu().numpy()
     cnt = hp.count.cpu().numpy()
     groups = wl.Hq if wl.kind in ("blocks", "nsa") else wl.G_sel
-    listed = wl.kind in ("blocks", "nsa", "dsa_pages", "quest")   # block or page lists, not token sets
+    listed = wl.kind in ("blocks", "nsa", "dsa_pages", "quest", "msa")   # block or page lists, not token sets
     bad = 0
     for (b, r) in rows:
         for g in range(groups):
@@ -135,7 +135,8 @@ def test_tiny_fp32_full():
                                   "block_sparse_small", "tiny_topk_f32_small", "dsa_paged_decode_small",
                                   "dsa_paged_prefill_small", "window_stride_small", "nsa_blocks_small",
                                   "dsa_two_level_decode_small", "dsa_two_level_prefill_small",
-                                  "quest_decode_small", "quest_prefill_small"])
+                                  "quest_decode_small", "quest_prefill_small", "msa_prefill_small",
+                                  "msa_decode_small"])
 def test_small_workload(name):
     wl = gen.WORKLOADS[name]
     inp = gen.generate(wl)
@@ -1043,3 +1044,22 @@ def test_quest_bounds_and_ties(dtype, d):
             rows = K[b, :, pg * P:(pg + 1) * P]                # [Hkv, P, d]
             assert np.array_equal(bn[b, pg, :, :d], rows.min(axis=1))
             assert np.array_equal(bn[b, pg, :, d:], rows.max(axis=1))
+
+
+# ---------------------------------------------------------------- blocks per GQA group
+def test_group_block_lists_equal_repeated_head_lists():
+    """A BLOCKS selection with one list per KV group gives the same output as
+    the same lists repeated for every query head (bitwise), on the block-sparse
+    small shapes with four query heads per group."""
+    sp = S()
+    wl = dataclasses.replace(gen.WORKLOADS["msa_prefill_small"], Hq=8, Hkv=2, H_I=4, G_sel=2)
+    say(f"[gpu] group block lists {wl.name} Hq={wl.Hq} G={wl.G_sel}")
+    inp = gen.generate(wl)
+    hp = run(wl, inp)
+    rep = hp.idx.repeat_interleave(wl.Hq // wl.G_sel, dim=1).contiguous()
+    sel = sp.selection(sp.SEL_BLOCKS, rep, window=wl.window, block_size=wl.block_size)
+    o2 = torch.empty_like(hp.o)
+    l2 = torch.empty_like(hp.lse)
+    sp.spattn_sparse_attn_fwd(hp.q, hp.k, hp.v, hp.ctx_len, 0.0, sel, o2, l2)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, hp.o) and torch.equal(l2, hp.lse)
