@@ -81,10 +81,13 @@ def algorithmic(wl, inp, hp, fused):
         pairs = float(size.sum()) * (wl.Hq // wl.G_sel)
         kv = wl.B * wl.Hkv * wl.N * wl.d * e * 2
         out["attention"] = {"bytes": kv + qkv_out, "flops": 4.0 * pairs * wl.d, "bound": "mfma", "pairs": pairs}
+        # block scores: float32 FMAs over (row, complete block, indexer head, dim); the compulsory
+        # bytes are the block-key cache once, the indexer queries and weights, and the lists
         nbe = float(((pos[:, 0, :] + 1) // wl.block_size).sum())              # complete blocks over the rows
-        out["index_block_select"] = {"bytes": nbe * wl.G_sel * wl.d_I * 4 + blk.size * 4
-                                     + wl.B * wl.Nq * wl.H_I * wl.d_I * 2,
-                                     "flops": 2.0 * nbe * wl.H_I * wl.d_I, "rows": wl.B * wl.G_sel * wl.Nq}
+        out["index_block_select"] = {"bytes": wl.B * (wl.N // wl.block_size) * wl.G_k * wl.d_I * 4 + blk.size * 4
+                                     + wl.B * wl.Nq * wl.H_I * (wl.d_I * 2 + 4),
+                                     "flops": 2.0 * nbe * wl.H_I * wl.d_I, "rows": wl.B * wl.G_sel * wl.Nq,
+                                     "bound": "alu"}
     elif wl.H_I:
         kb = {"fp8": 1, "bf16": 2, "f32": 4}[wl.idx_k_dtype]
         pos = np.concatenate([L - wl.Nq + np.arange(wl.Nq) for L in lens])
