@@ -366,6 +366,183 @@ __global__ __launch_bounds__(kTlThreads) void two_level_kernel(TwoLevelParams q)
   if (cnt && tid == 0) *cnt = K;
 }
 
+// ---------------------------------------------------------------- blocks only, one wave per row
+// The coarse pick alone for many rows (prefill): one wave per row, four rows
+// of one (request, group) per workgroup, which share every 64-block chunk of
+// the block-key cache staged in LDS (lane l scores block 64 c + l of chunk c,
+// so each lane holds the keys of blocks l, 64 + l, ..., 448 + l). The
+// R-th largest computed key t comes from removing the wave's maximum value
+// (all its copies) until R keys are out; keys above t + 2 eps are in the
+// exact selection, keys below t - 2 eps are out, and only when the band
+// between holds more keys than the free slots are its members rescored
+// exactly and ranked by (exact key desc, block asc).
+constexpr int kGbRows = 4;           // rows (waves) per workgroup
+constexpr int kGbSlots = 8;          // blocks per lane: up to 512 blocks per request
+constexpr int kGbStride = 65;        // LDS row stride of a staged block key (floats)
+
+__global__ __launch_bounds__(64 * kGbRows) void group_block_pick_kernel(TwoLevelParams q) {
+  __shared__ float kb[64 * kGbStride];
+  __shared__ float qsw[kGbRows][4 * 64];
+  const TopkParams& p = q.t;
+  const IndexerParams& x = p.ix;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int r = blockIdx.x * kGbRows + wid;
+  const int L = min(p.ctx_len ? p.ctx_len[b] : p.ctx, p.ctx);
+  const int rlast = min(blockIdx.x * kGbRows + kGbRows - 1, p.Nq - 1);
+  const int nbe_max = max(0, L - p.Nq + rlast + 1) >> q.lgbs;   // blocks any row of this workgroup sees
+  const bool live = r < p.Nq;
+  const int pos = L - p.Nq + r;
+  const int nbe = live && pos >= 0 ? (pos + 1) >> q.lgbs : 0;
+  const int R = q.nb;
+  const int kg = x.G_k == 1 ? 0 : g;
+  IndexerRow ir{};
+  float co = 0.f;
+  if (live) {
+    ir = indexer_row(x, b, g, r);
+    for (int e = lane; e < ir.H * 64; e += 64) {
+      const int h = e >> 6;
+      const float qv = (float)load_f64(ir.q, ir.qt, h * ir.qh_stride + (e & 63));
+      qsw[wid][e] = qv;
+      co = fmaf(ir.relu ? fabsf(ir.w[h * ir.w_stride]) : 1.f, fabsf(qv), co);
+    }
+  }
+  float wsg[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) wsg[h] = live && h < ir.H ? (ir.relu ? ir.w[h * ir.w_stride] : 1.f) : 0.f;
+  const float* kbase = q.kp + b * q.kps[0] + kg * q.kps[2];
+  uint32_t key[kGbSlots];
+  float kabs = 0.f;
+#pragma unroll
+  for (int c = 0; c < kGbSlots; ++c) {
+    key[c] = 0u;
+    if (64 * c >= nbe_max) continue;                // uniform over the workgroup
+    __syncthreads();                                // the previous chunk is consumed
+    for (int e = tid; e < 64 * 16; e += 64 * kGbRows) {
+      const int bl = e >> 4, c4 = (e & 15) * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (64 * c + bl < nbe_max) v = *(const float4*)(kbase + (int64_t)(64 * c + bl) * q.kps[1] + c4);
+      float* d = kb + bl * kGbStride + c4;
+      d[0] = v.x;
+      d[1] = v.y;
+      d[2] = v.z;
+      d[3] = v.w;
+    }
+    __syncthreads();
+    const int blk = 64 * c + lane;
+    if (live && blk < nbe) {
+      const float* kr = kb + lane * kGbStride;
+      float dd[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 64; ++e) {
+        const float kv = kr[e];
+        kabs = fmaxf(kabs, fabsf(kv));
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          if (h < ir.H) dd[h] = fmaf(qsw[wid][h * 64 + e], kv, dd[h]);
+      }
+      float sc = 0.f;
+      if (ir.relu) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          if (h < ir.H) sc = fmaf(wsg[h], fmaxf(dd[h], 0.f), sc);
+      } else {
+        sc = dd[0];
+      }
+      key[c] = f32_order_key(sc);                   // > 0 for every finite score
+    }
+  }
+  if (!live) return;                                // no barrier below
+  int32_t* out = p.idx + b * p.is[0] + g * p.is[1] + r * p.is[2];
+  int32_t* cnt = p.count ? p.count + ((int64_t)b * p.G + g) * p.Nq + r : nullptr;
+  if (nbe <= R) {                                   // every complete block (none when pos < 0)
+    for (int i = lane; i < R; i += 64) out[i] = i < nbe ? i : -1;
+    if (cnt && lane == 0) *cnt = nbe;
+    return;
+  }
+  // the R-th largest computed key
+  uint32_t wk[kGbSlots];
+#pragma unroll
+  for (int c = 0; c < kGbSlots; ++c) wk[c] = key[c];
+  uint32_t removed = 0, t = 0;
+  while (true) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int c = 0; c < kGbSlots; ++c) m = max(m, wk[c]);
+    m = wave_max_u32_dpp(m);
+    uint32_t n = 0;
+#pragma unroll
+    for (int c = 0; c < kGbSlots; ++c) n += (uint32_t)__popcll(ballot(wk[c] == m));
+    if (removed + n >= (uint32_t)R || m == 0u) {
+      t = m;
+      break;
+    }
+    removed += n;
+#pragma unroll
+    for (int c = 0; c < kGbSlots; ++c)
+      if (wk[c] == m) wk[c] = 0u;
+  }
+  // certified band around t
+  const float KM = wave_max_dpp(kabs);
+  const float CO = wave_sum_dpp(co);
+  const float E = 2.0f * eps_of(x, CO, KM) * 1.0001f + 1e-30f;
+  const float tf = order_key_f32(t);
+  const uint32_t klo = f32_order_key(nextafterf(tf - E, -INFINITY));
+  const uint32_t khi = f32_order_key(nextafterf(tf + E, INFINITY));
+  bool chosen[kGbSlots], band[kGbSlots];
+  uint32_t n_in = 0, n_band = 0;
+#pragma unroll
+  for (int c = 0; c < kGbSlots; ++c) {
+    chosen[c] = key[c] > khi;
+    band[c] = key[c] != 0u && key[c] >= klo && key[c] <= khi;
+    n_in += (uint32_t)__popcll(ballot(chosen[c]));
+    n_band += (uint32_t)__popcll(ballot(band[c]));
+  }
+  const uint32_t R2 = (uint32_t)R - n_in;           // n_in + n_band >= R (every key >= t is in or in the band)
+  if (n_band <= R2) {
+#pragma unroll
+    for (int c = 0; c < kGbSlots; ++c) chosen[c] = chosen[c] || band[c];
+  } else {
+    // exact keys of the band, ranked by (exact key desc, block asc)
+    IndexerRow irp = ir;
+    irp.k = kbase;
+    irp.kt = DT_F32;
+    irp.k_stride = q.kps[1];
+    uint32_t ex[kGbSlots];
+#pragma unroll
+    for (int c = 0; c < kGbSlots; ++c) ex[c] = band[c] ? f32_order_key(exact_key(irp, 64 * c + lane)) : 0u;
+    for (uint32_t k = 0; k < R2; ++k) {
+      uint32_t m = 0u;
+#pragma unroll
+      for (int c = 0; c < kGbSlots; ++c) m = max(m, ex[c]);
+      m = wave_max_u32_dpp(m);
+      uint32_t inv = 0u;                             // the lowest block holding m, as 0xFFFFFFFF - block
+#pragma unroll
+      for (int c = 0; c < kGbSlots; ++c)
+        if (m != 0u && ex[c] == m) inv = max(inv, 0xFFFFFFFFu - (uint32_t)(64 * c + lane));
+      const uint32_t win = 0xFFFFFFFFu - wave_max_u32_dpp(inv);
+#pragma unroll
+      for (int c = 0; c < kGbSlots; ++c)
+        if ((uint32_t)(64 * c + lane) == win) {
+          chosen[c] = true;
+          ex[c] = 0u;
+        }
+    }
+  }
+  uint32_t base = 0;
+#pragma unroll
+  for (int c = 0; c < kGbSlots; ++c) {
+    const uint64_t m = ballot(chosen[c]);
+    if (chosen[c]) out[base + lanes_below(m)] = 64 * c + lane;
+    base += (uint32_t)__popcll(m);
+  }
+  if (cnt && lane == 0) *cnt = R;
+}
+
+static bool group_block_pick_ok(const TwoLevelParams& q) {
+  const IndexerParams& x = q.t.ix;
+  return q.blocks_only && x.d_I == 64 && x.hpg <= 4 && (x.ctx >> q.lgbs) <= 64 * kGbSlots && q.nb <= 64;
+}
+
 hipError_t launch_pool_index_keys(const TwoLevelParams& q, hipStream_t st) {
   const IndexerParams& x = q.t.ix;
   const int nblk = x.ctx >> q.lgbs;
@@ -375,6 +552,11 @@ hipError_t launch_pool_index_keys(const TwoLevelParams& q, hipStream_t st) {
 }
 
 hipError_t launch_two_level(const TwoLevelParams& q, hipStream_t st) {
+  if (group_block_pick_ok(q)) {
+    hipLaunchKernelGGL(group_block_pick_kernel, dim3((q.t.Nq + kGbRows - 1) / kGbRows, q.t.G, q.t.B),
+                       dim3(64 * kGbRows), 0, st, q);
+    return hipGetLastError();
+  }
   const int rows = q.t.B * q.t.G * q.t.Nq;
   hipLaunchKernelGGL(two_level_kernel, dim3(rows), dim3(kTlThreads), 0, st, q);
   return hipGetLastError();

@@ -1063,3 +1063,54 @@ def test_group_block_lists_equal_repeated_head_lists():
     sp.spattn_sparse_attn_fwd(hp.q, hp.k, hp.v, hp.ctx_len, 0.0, sel, o2, l2)
     torch.cuda.synchronize()
     assert torch.equal(o2, hp.o) and torch.equal(l2, hp.lse)
+
+
+@pytest.mark.parametrize("R", [3, 16])
+def test_group_block_pick_ties(R):
+    """Per-group block selection where most blocks share one mean key (exact
+    ties, ranked by block index) and a few differ by one unit in the last
+    place, against the oracle's selection on the same pooled keys; many rows,
+    two groups of two indexer heads."""
+    import oracle as orc
+    from fine_grained_top_amd.hotpath import to_device
+    sp = S()
+    say(f"[gpu] group block pick ties R={R}")
+    B, Nq, ctx, H_I, G, d_I, bs = 2, 700, 1600, 4, 2, 64, 16
+    rng = np.random.default_rng(81 + R)
+    base_v = rng.standard_normal(d_I).astype(np.float32)
+    K = np.tile(base_v, (B, ctx, 1))
+    kst = gen.f32_to_bf16_bits(K.reshape(B, ctx, 1, d_I))
+    for bb in range(B):
+        for blk in rng.choice(ctx // bs, size=12, replace=False):       # a few blocks nudged by one bf16 unit
+            kst[bb, blk * bs, 0, blk % d_I] = int(kst[bb, blk * bs, 0, blk % d_I]) + (1 if blk % 2 else -1)
+    qst = gen.f32_to_bf16_bits(rng.standard_normal((B, Nq, H_I, d_I)).astype(np.float32))
+    w = rng.random(H_I).astype(np.float32)
+    q = to_device(qst, "bf16")
+    k = to_device(kst, "bf16")
+    wd = torch.from_numpy(w).cuda().view(1, 1, H_I).expand(B, Nq, H_I)
+    ix = sp.indexer(q, k, wd, sp.SCORE_WEIGHTED_RELU, H_I // G)
+    lens = [ctx, ctx - 37]
+    cl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    kb = torch.empty(B, ctx // bs, 1, d_I, device="cuda")
+    sp.spattn_pool_index_keys(ix, cl, bs, kb)
+    out = torch.empty(B, G, Nq, R, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(B, G, Nq, dtype=torch.int32, device="cuda")
+    sp.spattn_index_block_select(ix, kb, cl, bs, R, out, cnt)
+    torch.cuda.synchronize()
+    got, gc = out.cpu().numpy(), cnt.cpu().numpy()
+    Kd = gen.bf16_bits_to_f32(kst).astype(np.float64)[:, :, 0]
+    Qd = gen.bf16_bits_to_f32(qst).astype(np.float64)
+    bad = 0
+    for bb in range(B):
+        nbe_all = lens[bb] // bs
+        pooled = orc.pooled_blocks(Kd[bb], bs, nbe_all, "f32")
+        for g in range(G):
+            hs = slice(g * (H_I // G), (g + 1) * (H_I // G))
+            for r in range(0, Nq, 3):
+                p = lens[bb] - Nq + r
+                keys = orc.keys_weighted_relu(Qd[bb, r, hs], w[hs].astype(np.float64), pooled[: (p + 1) // bs])
+                want = orc.group_block_select(keys, p, bs, R)
+                ok = gc[bb, g, r] == len(want) and np.array_equal(got[bb, g, r, :len(want)], want) \
+                    and np.all(got[bb, g, r, len(want):] == -1)
+                bad += 0 if ok else 1
+    assert bad == 0, f"{bad} rows differ"
