@@ -1114,3 +1114,72 @@ def test_group_block_pick_ties(R):
                     and np.all(got[bb, g, r, len(want):] == -1)
                 bad += 0 if ok else 1
     assert bad == 0, f"{bad} rows differ"
+
+
+def test_quest_edge_cases():
+    """Quest selection at the edges: no top pages (local pages only), more
+    local pages than the context holds, contexts shorter than one page, one
+    list per query head, f32."""
+    import oracle as orc
+    sp = S()
+    say("[gpu] quest edge cases")
+    B, Hq, Hkv, d, P, npg = 3, 4, 2, 64, 8, 12
+    rng = np.random.default_rng(91)
+    K = rng.standard_normal((B, Hkv, P * npg, d)).astype(np.float32)
+    q = rng.standard_normal((B, Hq, 1, d)).astype(np.float32)
+    pool = np.ascontiguousarray(K.reshape(B, Hkv, npg, P, d).transpose(0, 2, 1, 3, 4).reshape(B * npg, Hkv, P, d))
+    table = np.arange(B * npg, dtype=np.int32).reshape(B, npg)
+    kp, tab = torch.from_numpy(pool).cuda(), torch.from_numpy(table).cuda()
+    pages = sp.kv_pages(tab, P)
+    lens = [5, P * npg, 3 * P + 1]
+    cl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    bnd = torch.empty(B, npg, Hkv, 2 * d, device="cuda")
+    sp.spattn_quest_page_bounds(kp, pages, cl, bnd)
+    qd = torch.from_numpy(q).cuda()
+    for G, top, loc in ((Hkv, 0, 1), (Hkv, 3, 20), (Hq, 2, 1), (Hq, 40, 2)):
+        io = torch.empty(B, G, 1, top + loc, dtype=torch.int32, device="cuda")
+        cnt = torch.empty(B, G, 1, dtype=torch.int32, device="cuda")
+        sp.spattn_quest_select(qd, bnd, cl, P, top, loc, io, cnt)
+        torch.cuda.synchronize()
+        got, gc = io.cpu().numpy(), cnt.cpu().numpy()
+        hg = Hq // G
+        for b in range(B):
+            p = lens[b] - 1
+            for g in range(G):
+                Qg = q[b, g * hg:(g + 1) * hg, 0].astype(np.float64)
+                want = orc.quest_select(Qg, K[b, (g * hg) // (Hq // Hkv)].astype(np.float64), p, P, top, loc)
+                assert gc[b, g, 0] == len(want), (G, top, loc, b, g)
+                assert np.array_equal(got[b, g, 0, :len(want)], want) and np.all(got[b, g, 0, len(want):] == -1)
+
+
+def test_group_block_select_wide_rows():
+    """Per-group block selection beyond the wave-per-row kernel's shape (more
+    than 512 blocks, 80 blocks kept): the per-row workgroup's coarse pick."""
+    import oracle as orc
+    from fine_grained_top_amd.hotpath import to_device
+    sp = S()
+    say("[gpu] group block select, 1024 blocks, R=80")
+    B, Nq, ctx, H_I, G, d_I, bs, R = 1, 40, 16384, 4, 2, 64, 16, 80
+    rng = np.random.default_rng(93)
+    kst = gen.f32_to_bf16_bits(rng.standard_normal((B, ctx, 1, d_I)).astype(np.float32))
+    qst = gen.f32_to_bf16_bits(rng.standard_normal((B, Nq, H_I, d_I)).astype(np.float32))
+    w = rng.random(H_I).astype(np.float32)
+    ix = sp.indexer(to_device(qst, "bf16"), to_device(kst, "bf16"),
+                    torch.from_numpy(w).cuda().view(1, 1, H_I).expand(B, Nq, H_I), sp.SCORE_WEIGHTED_RELU, H_I // G)
+    kb = torch.empty(B, ctx // bs, 1, d_I, device="cuda")
+    sp.spattn_pool_index_keys(ix, None, bs, kb)
+    out = torch.empty(B, G, Nq, R, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(B, G, Nq, dtype=torch.int32, device="cuda")
+    sp.spattn_index_block_select(ix, kb, None, bs, R, out, cnt)
+    torch.cuda.synchronize()
+    got, gc = out.cpu().numpy(), cnt.cpu().numpy()
+    Kd = gen.bf16_bits_to_f32(kst).astype(np.float64)[0, :, 0]
+    Qd = gen.bf16_bits_to_f32(qst).astype(np.float64)[0]
+    pooled = orc.pooled_blocks(Kd, bs, ctx // bs, "f32")
+    for g in range(G):
+        hs = slice(g * (H_I // G), (g + 1) * (H_I // G))
+        for r in range(0, Nq, 7):
+            p = ctx - Nq + r
+            want = orc.group_block_select(orc.keys_weighted_relu(Qd[r, hs], w[hs].astype(np.float64),
+                                                                 pooled[: (p + 1) // bs]), p, bs, R)
+            assert gc[0, g, r] == len(want) and np.array_equal(got[0, g, r], want), (g, r)
