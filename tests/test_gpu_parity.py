@@ -369,7 +369,7 @@ def _sample_rows(wl, n, seed):
 
 
 @pytest.mark.parametrize("name,n", [("window_global", 48), ("block_sparse", 24), ("dsa_prefill", 24),
-                                    ("window_stride", 48), ("nsa_blocks", 16)])
+                                    ("window_stride", 48), ("nsa_blocks", 16), ("msa_prefill", 16)])
 def test_full_size_sampled_rows(name, n):
     wl = gen.WORKLOADS[name]
     say(f"[gpu] generating {name} inputs")
@@ -1183,3 +1183,52 @@ def test_group_block_select_wide_rows():
             want = orc.group_block_select(orc.keys_weighted_relu(Qd[r, hs], w[hs].astype(np.float64),
                                                                  pooled[: (p + 1) // bs]), p, bs, R)
             assert gc[0, g, r] == len(want) and np.array_equal(got[0, g, r], want), (g, r)
+
+
+def test_quest_decode_full_every_row():
+    """Quest selection and paged attention at the full decode shapes, every row."""
+    wl = gen.WORKLOADS["quest_decode"]
+    say("[gpu] generating quest_decode inputs")
+    inp = gen.generate(wl)
+    hp = run(wl, inp)
+    rows = _all_rows(wl, inp)
+    res = oracle_rows(wl, inp, rows)
+    check_sets(hp, res, rows, wl)
+    check_out(hp, res, rows, 2e-3)
+
+
+def test_backward_full_size():
+    """The backward at the full window + global shapes (N = 4096, 8 heads,
+    tiled kernel): dq of sampled rows against the oracle's gradients, and for
+    every key head the identities that hold at any size: the value gradients
+    sum over keys to the sum of dO over the rows and heads that read them
+    (softmax rows sum to 1), and the key gradients sum to zero (each row's dS
+    sums to zero)."""
+    import oracle as orc
+    wl = gen.WORKLOADS["window_global_bwd"]
+    say("[gpu] generating window_global_bwd inputs")
+    inp = gen.generate(wl)
+    hp = run(wl, inp)
+    dq, dk, dv = hp.dq.cpu().numpy(), hp.dk.cpu().numpy(), hp.dv.cpu().numpy()
+    q = orc.decode(inp["q"][0], "bf16")
+    k = orc.decode(inp["k"][0], "bf16")
+    v = orc.decode(inp["v"][0], "bf16")
+    dO = np.asarray(inp["d_o"], dtype=np.float32).astype(np.float64)[0]
+    scale = 1.0 / math.sqrt(wl.d)
+    worst = 0.0
+    for (_, r) in _sample_rows(wl, 24, 13):
+        S_ = orc.window_global_set(r, wl.window, wl.n_global)
+        for h in range(0, wl.Hq, 3):
+            kvh = h // (wl.Hq // wl.Hkv)
+            gq, _, _ = orc.masked_attention_grads(q[h, r][None], k[kvh, :r + 1], v[kvh, :r + 1], S_, scale,
+                                                  dO[h, r][None])
+            worst = max(worst, float(np.abs(dq[0, h, r] - gq[0]).max()) / max(1.0, float(np.abs(gq).max())))
+    say(f"  dq relative max error {worst:.2e}")
+    assert worst <= 1e-4
+    g = wl.Hq // wl.Hkv
+    for kvh in range(wl.Hkv):
+        want_v = dO[kvh * g:(kvh + 1) * g].sum(axis=(0, 1))
+        got_v = dv[0, kvh].astype(np.float64).sum(axis=0)
+        assert np.abs(got_v - want_v).max() <= 1e-4 * max(1.0, float(np.abs(dv[0, kvh]).sum(axis=0).max()))
+        got_k = dk[0, kvh].astype(np.float64).sum(axis=0)
+        assert np.abs(got_k).max() <= 1e-4 * max(1.0, float(np.abs(dk[0, kvh]).sum(axis=0).max()))
