@@ -212,8 +212,8 @@ def main():
                     help="time separate indexer-scores and top-K calls instead of the fused call")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU runs are not part of "
-              "this build", file=sys.stderr)
+        print(f"bench.py measures one GPU (asked for {args.gpus}); the library has no sharded path, so "
+              "there is nothing to run across GPUs", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
