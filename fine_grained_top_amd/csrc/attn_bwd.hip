@@ -3,29 +3,34 @@
 //
 // One workgroup = 64 query rows of one (request, head), the key tiles of 64
 // keys visited as by the forward tile kernel (global tiles and the window's
-// band, or every past tile). Per key tile, with Q, dO, K, V tiles in LDS and
-// each thread holding a 4 x 4 block of (row, key) pairs in registers:
-//   S = Q K^T, dP = dO V^T (128-term dot products),
-//   P = exp(S * scale - lse) on visible pairs, dS = P (dP - D) * scale,
-// then with 4 x 8 blocks of outputs per thread:
-//   dQ += dS K     (kept in registers over the key tiles),
-//   dK  = dS^T Q,  dV = P^T dO  (this query tile's share, added to the
-//   key tile's rows with one float atomic per element).
-// D = rowsum(dO * O) per row. Float32 throughout; bf16 inputs are exact.
+// band, or every past tile). Wave w owns query rows 16w..16w+15. Per key tile:
+//   S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_16x16x32_bf16 (lane = query
+//   row, 4 keys per 16-key subtile); dO is float32, so it enters as the sum
+//   of three bf16 parts (an exact split), and every product is exact;
+//   P = exp(S * scale - lse) on visible pairs, dS = P (dP - D) * scale with
+//   D = rowsum(dO * O), formed in registers and written to LDS;
+//   dQ += dS K on the same MFMA (dS as three bf16 parts, K read transposed
+//   from an XOR-swizzled copy), kept in registers across key tiles;
+//   dK = dS^T Q and dV = P^T dO in float32 FMAs from LDS (4 keys x 8 dims per
+//   thread), the query tile's share added with one float atomic per element.
 #include "common.h"
 #include "internal.h"
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 namespace sp {
 
 constexpr int kBT = 64;         // rows per query tile, keys per key tile
 constexpr int kBD = 128;        // head dim
-constexpr int kBQs = kBD + 2;   // bf16 row stride of the Q/K/V tiles: 65 words, so rows fall in distinct banks
+constexpr int kBQs = kBD + 2;   // bf16 row stride of the Q tile read by the FMA phase (65 words: rows in distinct banks)
+constexpr int kBKs = 136;       // bf16 row stride of the K and V tiles read as MFMA operands (272 B)
 constexpr int kBPs = kBT + 1;   // float row stride of the P and dS tiles
 
 struct BwdSmem {
   uint16_t q[kBT * kBQs];
-  uint16_t k[kBT * kBQs];
-  uint16_t v[kBT * kBQs];
+  uint16_t ks[kBT * kBKs];
+  uint16_t vs[kBT * kBKs];
+  uint16_t kt[kBT * kBD];       // K row-major, 16-byte chunk c of row j at c ^ (j mod 16) (read transposed)
   float dO[kBT * (kBD + 1)];
   float P[kBT * kBPs];
   float dS[kBT * kBPs];
@@ -33,12 +38,20 @@ struct BwdSmem {
   uint32_t tiles[64];
 };
 
-SP_DEV float bfl(const uint16_t* t, int i) { return bf16_to_f32(t[i]); }
+// x = hi + mid + lo exactly: three round-to-nearest bf16 steps of a float32
+// (each remainder is exact in float32 and has at most 16, then 8, bits left)
+SP_DEV void split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = f32_to_bf16_rne(x);
+  const float r1 = x - bf16_to_f32(hi);
+  mid = f32_to_bf16_rne(r1);
+  lo = f32_to_bf16_rne(r1 - bf16_to_f32(mid));
+}
 
 __global__ __launch_bounds__(256) void attn_bwd_tile_kernel(AttnParams a, AttnBwd g) {
-  __shared__ BwdSmem sm;
+  __shared__ __attribute__((aligned(16))) BwdSmem sm;
   const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int qq = lane >> 4, c16 = lane & 15;
   const int kvh = h / (a.Hq / a.Hkv);
   const int L = min(a.ctx_len ? a.ctx_len[b] : a.ctx, a.ctx);
   const int q0 = qt * kBT;
@@ -88,16 +101,40 @@ __global__ __launch_bounds__(256) void attn_bwd_tile_kernel(AttnParams a, AttnBw
   }
   __syncthreads();
 
-  // thread blocks: pairs rows 4*(tid/16) + i, keys tid%16 + 16*j (keys 16 apart
-  // fall in distinct LDS banks); outputs rows/keys 4*(tid/16) + i, dims
-  // 8*(tid%16) + e
-  const int pr = 4 * (tid >> 4), pk = tid & 15;
+  // ---- MFMA phases: lane column c16 = query row 16 wid + c16; the operand
+  // dims of MFMA s are 32 qq + 8 s .. + 7 on both sides
+  const int rloc = 16 * wid + c16;
+  const bool rvalid = rloc < nrows;
+  const int prow = pbase + q0 + rloc;
+  const float lr = sm.lse[rloc], Dr = sm.D[rloc];
+  bf16x8 Qb[4];
+  u32x4 Ob[3][4];                  // the row's dO as three bf16 parts
+  if (rvalid) {
+    const uint16_t* qp = (const uint16_t*)a.q.p + b * a.q.s[0] + h * a.q.s[1] + (int64_t)(q0 + rloc) * a.q.s[2] + 32 * qq;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) Qb[s] = *(const bf16x8*)(qp + 8 * s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) Qb[s] = (bf16x8){};
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float* dr = &sm.dO[rloc * (kBD + 1) + 32 * qq + 8 * s + 2 * u];   // zero rows past nrows
+      uint32_t h0, m0, l0, h1, m1, l1;
+      split3(dr[0], h0, m0, l0);
+      split3(dr[1], h1, m1, l1);
+      Ob[0][s][u] = h0 | (h1 << 16);
+      Ob[1][s][u] = m0 | (m1 << 16);
+      Ob[2][s][u] = l0 | (l1 << 16);
+    }
+  f32x4 dQ[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) dQ[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  // FMA phase mapping: keys orow.., dims odim..
   const int orow = 4 * (tid >> 4), odim = 8 * (tid & 15);
-  float dq[4][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dq[i][e] = 0.f;
   const uint16_t* kbase = (const uint16_t*)a.k.p + b * a.k.s[0] + kvh * a.k.s[1];
   const uint16_t* vbase = (const uint16_t*)a.v.p + b * a.v.s[0] + kvh * a.v.s[1];
   float* dkb = g.dk + b * g.dks[0] + kvh * g.dks[1];
@@ -109,86 +146,84 @@ __global__ __launch_bounds__(256) void attn_bwd_tile_kernel(AttnParams a, AttnBw
       const int t = 32 * w + __builtin_ctz(bits);
       bits &= bits - 1;
       const int j0 = t * kBT;
-      // stage K and V tiles (keys past L read as row L-1, masked below)
+      // stage K (row-major and swizzled) and V (keys past L read as row L-1, masked below)
       for (int e = tid; e < kBT * kBD / 8; e += 256) {
-        const int kr = e >> 4, c8 = (e & 15) * 8;
-        const int j = min(j0 + kr, L - 1);
-        const u32x4 kv = *(const u32x4*)(kbase + (int64_t)j * a.k.s[2] + c8);
-        const u32x4 vv = *(const u32x4*)(vbase + (int64_t)j * a.v.s[2] + c8);
-        uint32_t* kd = (uint32_t*)&sm.k[kr * kBQs + c8];
-        uint32_t* vd = (uint32_t*)&sm.v[kr * kBQs + c8];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          kd[u] = kv[u];
-          vd[u] = vv[u];
-        }
+        const int key = e >> 4, col = e & 15;
+        const int j = min(j0 + key, L - 1);
+        const u32x4 kv = *(const u32x4*)(kbase + (int64_t)j * a.k.s[2] + 8 * col);
+        const u32x4 vv = *(const u32x4*)(vbase + (int64_t)j * a.v.s[2] + 8 * col);
+        *(u32x4*)&sm.ks[key * kBKs + 8 * col] = kv;
+        *(u32x4*)&sm.kt[key * kBD + 8 * (col ^ (key & 15))] = kv;
+        *(u32x4*)&sm.vs[key * kBKs + 8 * col] = vv;
       }
       __syncthreads();
-      // S and dP for the thread's 4 x 4 block
-      float s[4][4], dp[4][4];
+      // S^T and dP^T: lane holds row rloc, keys 16 st + 4 qq + v
+      f32x4 S[4], dP[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int st = 0; st < 4; ++st) {
+        S[st] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        dP[st] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        const uint16_t* kr = &sm.ks[(16 * st + c16) * kBKs + 32 * qq];
+        const uint16_t* vr = &sm.vs[(16 * st + c16) * kBKs + 32 * qq];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) s[i][jj] = dp[i][jj] = 0.f;
-      for (int c = 0; c < kBD; c += 2) {
-        float qa[4][2], oa[4][2], ka[4][2], va[4][2];
+        for (int s = 0; s < 4; ++s) {
+          S[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(kr + 8 * s), Qb[s], S[st], 0, 0, 0);
+          const bf16x8 vA = *(const bf16x8*)(vr + 8 * s);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t qw = *(const uint32_t*)&sm.q[(pr + i) * kBQs + c];
-          qa[i][0] = bf16_to_f32(qw & 0xFFFFu);
-          qa[i][1] = bf16_to_f32(qw >> 16);
-          oa[i][0] = sm.dO[(pr + i) * (kBD + 1) + c];
-          oa[i][1] = sm.dO[(pr + i) * (kBD + 1) + c + 1];
-          const uint32_t kw = *(const uint32_t*)&sm.k[(pk + 16 * i) * kBQs + c];
-          const uint32_t vw = *(const uint32_t*)&sm.v[(pk + 16 * i) * kBQs + c];
-          ka[i][0] = bf16_to_f32(kw & 0xFFFFu);
-          ka[i][1] = bf16_to_f32(kw >> 16);
-          va[i][0] = bf16_to_f32(vw & 0xFFFFu);
-          va[i][1] = bf16_to_f32(vw >> 16);
+          for (int pt = 0; pt < 3; ++pt)
+            dP[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, *(const bf16x8*)&Ob[pt][s], dP[st], 0, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            s[i][jj] = fmaf(qa[i][0], ka[jj][0], s[i][jj]);
-            s[i][jj] = fmaf(qa[i][1], ka[jj][1], s[i][jj]);
-            dp[i][jj] = fmaf(oa[i][0], va[jj][0], dp[i][jj]);
-            dp[i][jj] = fmaf(oa[i][1], va[jj][1], dp[i][jj]);
-          }
       }
-      // P and dS on visible pairs
+      // P and dS on visible pairs (registers for dQ, LDS for dK and dV)
+      float dz[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = pr + i;
-        const int prow = pbase + q0 + r;
-        const float lr = sm.lse[r], Dr = sm.D[r];
+      for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int j = j0 + pk + 16 * jj;
-          bool vis = r < nrows && j <= prow && lr > -INFINITY;
+        for (int v = 0; v < 4; ++v) {
+          const int kl = 16 * st + 4 * qq + v;
+          const int j = j0 + kl;
+          bool vis = rvalid && j <= prow && lr > -INFINITY;
           if (vis && a.mode == 2) vis = j >= prow - a.window + 1 || j < a.n_global;
-          const float p = vis ? expf(s[i][jj] * a.scale - lr) : 0.f;
-          sm.P[r * kBPs + pk + 16 * jj] = p;
-          sm.dS[r * kBPs + pk + 16 * jj] = p * (dp[i][jj] - Dr) * a.scale;
+          const float p = vis ? expf(S[st][v] * a.scale - lr) : 0.f;
+          const float ds = p * (dP[st][v] - Dr) * a.scale;
+          dz[4 * st + v] = ds;
+          sm.P[rloc * kBPs + kl] = p;
+          sm.dS[rloc * kBPs + kl] = ds;
+        }
+      // dQ += dS K: A = dS (three parts), k = 8 qq + v <-> keys 4 qq + v (v < 4), 16 + 4 qq + (v - 4),
+      // in two halves of 32 keys; B = K^T by transposed reads of the swizzled copy
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        u32x4 A0, A1, A2;
+#pragma unroll
+        for (int v2 = 0; v2 < 4; ++v2) {
+          const int i0 = (v2 < 2) ? (8 * hf + 2 * v2) : (8 * hf + 4 + 2 * (v2 - 2));
+          uint32_t h0, m0, l0, h1, m1, l1;
+          split3(dz[i0], h0, m0, l0);
+          split3(dz[i0 + 1], h1, m1, l1);
+          A0[v2] = h0 | (h1 << 16);
+          A1[v2] = m0 | (m1 << 16);
+          A2[v2] = l0 | (l1 << 16);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const int tr0 = 32 * hf + 4 * qq + (c16 >> 2), tr1 = tr0 + 16;
+          const int lch = 2 * nt + ((4 * (c16 & 3)) >> 3), wth = (4 * (c16 & 3)) & 7;
+          const v4i16 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)&sm.kt[tr0 * kBD + 8 * (lch ^ (tr0 & 15)) + wth]);
+          const v4i16 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)&sm.kt[tr1 * kBD + 8 * (lch ^ (tr1 & 15)) + wth]);
+          u32x4 Bk;
+          Bk[0] = (uint32_t)(uint16_t)b0[0] | ((uint32_t)(uint16_t)b0[1] << 16);
+          Bk[1] = (uint32_t)(uint16_t)b0[2] | ((uint32_t)(uint16_t)b0[3] << 16);
+          Bk[2] = (uint32_t)(uint16_t)b1[0] | ((uint32_t)(uint16_t)b1[1] << 16);
+          Bk[3] = (uint32_t)(uint16_t)b1[2] | ((uint32_t)(uint16_t)b1[3] << 16);
+          dQ[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&A0, *(const bf16x8*)&Bk, dQ[nt], 0, 0, 0);
+          dQ[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&A1, *(const bf16x8*)&Bk, dQ[nt], 0, 0, 0);
+          dQ[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&A2, *(const bf16x8*)&Bk, dQ[nt], 0, 0, 0);
         }
       }
       __syncthreads();
-      // dQ += dS K (rows orow.., dims odim..)
-      for (int jj = 0; jj < kBT; ++jj) {
-        float kv[8];
-        const uint32_t* kw = (const uint32_t*)&sm.k[jj * kBQs + odim];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          kv[2 * u] = bf16_to_f32(kw[u] & 0xFFFFu);
-          kv[2 * u + 1] = bf16_to_f32(kw[u] >> 16);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float d = sm.dS[(orow + i) * kBPs + jj];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) dq[i][e] = fmaf(d, kv[e], dq[i][e]);
-        }
-      }
       // dK = dS^T Q and dV = P^T dO for keys orow.., dims odim..
       float dk[4][8], dv[4][8];
 #pragma unroll
@@ -228,13 +263,14 @@ __global__ __launch_bounds__(256) void attn_bwd_tile_kernel(AttnParams a, AttnBw
       __syncthreads();
     }
   }
-  // ---- dQ
+  // ---- dQ: lane holds dims 16 nt + c16 of rows 16 wid + 4 qq + v
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (orow + i >= nrows) continue;
-    float* dqr = g.dq + b * g.dqs[0] + h * g.dqs[1] + (int64_t)(q0 + orow + i) * g.dqs[2] + odim;
+  for (int v = 0; v < 4; ++v) {
+    const int rr = 16 * wid + 4 * qq + v;
+    if (rr >= nrows) continue;
+    float* dqr = g.dq + b * g.dqs[0] + h * g.dqs[1] + (int64_t)(q0 + rr) * g.dqs[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dqr[e] = dq[i][e];
+    for (int nt = 0; nt < 8; ++nt) dqr[16 * nt + c16] = dQ[nt][v];
   }
 }
 
