@@ -40,9 +40,8 @@ What is computed (sources are the five pages on sparse attention):
   the top blocks chosen by the compression branch's own scores (the pooled-key
   dot products above), and a window branch; each branch has its own softmax
   and a gate weighs them: o = g_cmp o_cmp + g_sel o_sel + g_win o_win. A branch
-  with no visible entry contributes 0. The pages do not fix the precision of
-  the compressed entries; they are read as stored in the cache's format: the
-  exact block mean rounded to nearest-even bf16 (or float32).
+  with no visible entry contributes 0. The pages fix no precision for the
+  compressed entries, so they are the plain block means, exact in float64.
 * Two-level selection ("Sparse Attention Is Reshaping Production AI",
   per-token routing: a coarse block pass finds candidate regions, a fine pass
   picks the top-K tokens inside them). Read as: each complete block's indexer
@@ -397,42 +396,33 @@ def pages_set(pages: Sequence[int], p: int, P: int) -> np.ndarray:
     return s[s <= p].astype(np.int32)
 
 
-def round_to_format(x: np.ndarray, fmt: Optional[str]) -> np.ndarray:
-    """float64 values rounded to nearest-even bf16 or float32 (returned as float64)."""
-    if fmt is None:
-        return x
-    if fmt == "f32":
-        return x.astype(np.float32).astype(np.float64)
-    # bf16 keeps 7 of the 52 stored significand bits: round the float64 bit
-    # pattern at bit 45, ties to even (finite values in bf16's normal range)
-    bits = np.ascontiguousarray(x, dtype=np.float64).view(np.uint64)
-    lsb = (bits >> np.uint64(45)) & np.uint64(1)
-    bits = (bits + np.uint64((1 << 44) - 1) + lsb) & ~np.uint64((1 << 45) - 1)
-    return bits.view(np.float64)
-
-
 def pooled_blocks(X: np.ndarray, bs: int, n_blocks: int, fmt: Optional[str] = None) -> np.ndarray:
     """Mean of each complete block of bs rows (the compressed entries), summed
-    with math.fsum (correctly rounded) and, with fmt, rounded to that format."""
+    with math.fsum (correctly rounded) and, with fmt "f32", rounded once to
+    the nearest float32 (the indexer's per-block key cache)."""
     out = np.empty((n_blocks, X.shape[1]))
     for b in range(n_blocks):
         for c in range(X.shape[1]):
             out[b, c] = math.fsum(X[b * bs:(b + 1) * bs, c]) / bs
-    return round_to_format(out, fmt)
+    if fmt is None:
+        return out
+    if fmt != "f32":
+        raise ValueError(fmt)
+    return out.astype(np.float32).astype(np.float64)
 
 
 def nsa_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, p: int, bs: int, blocks: Sequence[int], w: int,
-                  gates: np.ndarray, scale: float, fmt: Optional[str] = None,
+                  gates: np.ndarray, scale: float,
                   pooled: Optional[Tuple[np.ndarray, np.ndarray]] = None) -> np.ndarray:
     """Gated sum of the compression, selection and window branches for one
-    query head q [d] at position p (keys K, V [>= p+1, d]); gates [3]; fmt:
-    the format the compressed entries are kept in; pooled: those entries
-    already formed (of at least the complete blocks up to p)."""
+    query head q [d] at position p (keys K, V [>= p+1, d]); gates [3];
+    pooled: the block means already formed (of at least the complete blocks
+    up to p)."""
     out = np.zeros(K.shape[1])
     nc = eligible_blocks(p, bs)
     branches = []
     if nc:
-        Kc, Vc = pooled if pooled is not None else (pooled_blocks(K, bs, nc, fmt), pooled_blocks(V, bs, nc, fmt))
+        Kc, Vc = pooled if pooled is not None else (pooled_blocks(K, bs, nc), pooled_blocks(V, bs, nc))
         branches.append((0, Kc[:nc], Vc[:nc], np.arange(nc)))
     sel = blocks_set(blocks, p, bs, 0)
     if len(sel):
@@ -635,8 +625,7 @@ def run(wl, inp: Dict[str, np.ndarray], rows: Iterable[Tuple[int, int]],
             nc = eligible_blocks(p, wl.block_size)
             for kvh in range(wl.Hkv):
                 Vh = decode(Vst[b, kvh, :n], wl.dtype)
-                pooled = (pooled_blocks(Kb[kvh], wl.block_size, nc, wl.dtype),
-                          pooled_blocks(Vh, wl.block_size, nc, wl.dtype))
+                pooled = (pooled_blocks(Kb[kvh], wl.block_size, nc), pooled_blocks(Vh, wl.block_size, nc))
                 for h in range(kvh * qpk, (kvh + 1) * qpk):
                     qh = decode(Q[b, h, r], wl.dtype)
                     O[h] = nsa_attention(qh, Kb[kvh], Vh, p, wl.block_size, res.blocks[(b, h, r)], wl.window,

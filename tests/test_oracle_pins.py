@@ -524,20 +524,23 @@ def test_nsa_pooling_is_the_block_mean():
     assert np.array_equal(orc.pooled_blocks(K2, 8, 1)[0], K[0])
 
 
-def test_nsa_entries_round_like_torch():
-    """Compressed entries kept in bf16 / float32: nearest-even rounding of the
-    exact means, checked against torch's casts from float64 (a cast that does
-    not round twice) on values at and near bf16 halfway points."""
+def test_block_key_cache_rounds_like_torch():
+    """The float32 block-key cache (two-level and per-group selection) is the
+    exact block mean rounded once to nearest-even float32, checked against
+    torch's float64 -> float32 cast of math.fsum means, on rows built so some
+    means sit exactly on a float32 halfway point."""
     rng = np.random.default_rng(16)
-    x = rng.standard_normal(4000)
-    # exact bf16 halfway points and their float64 neighbours
-    base = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(rng.standard_normal(200).astype(np.float32))).astype(np.float64)
-    half = base + np.abs(base) * 2.0 ** -8
-    x = np.concatenate([x, half, np.nextafter(half, np.inf), np.nextafter(half, -np.inf)])
-    for fmt, tdt in (("bf16", torch.bfloat16), ("f32", torch.float32)):
-        got = orc.round_to_format(x.copy(), fmt)
-        ref = torch.from_numpy(x).to(tdt).to(torch.float64).numpy()
-        assert np.array_equal(got, ref), fmt
+    X = rng.standard_normal((64, 5))
+    # block 1: every row holds an exact float32 halfway value (a float32 plus
+    # half its last unit), so the mean is that halfway value itself
+    f = rng.standard_normal(5).astype(np.float32).astype(np.float64)
+    half = f + np.abs(f) * 2.0 ** -24
+    X[16:32] = half
+    got = orc.pooled_blocks(X, 16, 4, "f32")
+    means = np.array([[math.fsum(X[16 * b:16 * b + 16, c]) / 16 for c in range(5)] for b in range(4)])
+    ref = torch.from_numpy(means).to(torch.float32).to(torch.float64).numpy()
+    assert np.array_equal(got, ref)
+    assert np.array_equal(orc.pooled_blocks(X, 16, 4), means)     # no format: the exact means
 
 
 def test_nsa_gates_pick_branches():
@@ -748,3 +751,57 @@ def test_group_blocks_full_coverage_is_causal_gqa():
         assert np.abs(res.O[(b, r)] - ref[:, r]).max() < 1e-12
         for g in range(wl.G_sel):
             assert res.sets[(b, g, r)].tolist() == list(range(r + 1))
+
+
+# ---------------------------------------------------------------- per-group wiring (hand-worked)
+def _wiring_case(g, G_k, score_mode, Hkv, kind="dsa_decode", **extra):
+    """A decode workload of one request built from the hand-worked fixture."""
+    wl = gen.Workload("wiring_hand", kind, B=1, Hq=4, Hkv=Hkv, N=5, Nq=1, d=5, dtype="f32", seed=0,
+                      H_I=4, d_I=2, G_sel=2, G_k=G_k, idx_q_dtype="f32", idx_k_dtype="f32",
+                      score_mode=score_mode, topk=g["K"], **extra)
+    keys = [g["k_idx_group0"], g["k_idx_group1"]][:G_k]
+    k_idx = np.stack([np.asarray(k, np.float32) for k in keys], axis=1)[None]        # [1, 5, G_k, 2]
+    v = np.stack([(c + 1) * np.eye(5, dtype=np.float32) for c in range(Hkv)])[None]   # [1, Hkv, 5, 5]
+    inp = {"ctx_len": np.array([5], np.int32), "q": np.zeros((1, 4, 1, 5), np.float32),
+           "k": np.zeros((1, Hkv, 5, 5), np.float32), "v": v,
+           "q_idx": np.asarray(g["q_idx"], np.float32)[None, None], "k_idx": k_idx,
+           "w": np.asarray(g["w"], np.float32)}
+    return wl, inp
+
+
+def test_group_wiring_hand_worked():
+    """Indexer heads, weights and key heads per selection group, and the query
+    head -> (selection group, KV head) map, against sets and outputs worked
+    out by hand (tests/golden/group_wiring_hand.json)."""
+    g = _gold("group_wiring_hand.json")
+    for case in g["cases"]:
+        wl, inp = _wiring_case(g, case["G_k"], case["score_mode"], Hkv=4)
+        res = orc.run(wl, inp, [(0, 0)], attention=False, keep_keys=True)
+        for grp in range(2):
+            assert res.sets[(0, grp, 0)].tolist() == case["sets"][grp], (case["name"], grp)
+            assert res.keys[(0, grp, 0)].tolist() == case["scores"][grp], (case["name"], grp)
+    att = g["attention"]
+    for Hkv, name in ((4, "O_shared_keys_Hkv4"), (1, "O_shared_keys_Hkv1")):
+        wl, inp = _wiring_case(g, 1, "weighted_relu", Hkv=Hkv)
+        res = orc.run(wl, inp, [(0, 0)])
+        assert np.array_equal(res.O[(0, 0)], np.asarray(att[name], np.float64)), name
+
+
+def test_group_blocks_wiring_hand_worked():
+    """MSA-style blocks per group with one-token blocks: each group's blocks
+    are its two best tokens, plus the query's own position from the window."""
+    g = _gold("group_wiring_hand.json")
+    m = g["msa"]
+    for G_k, tag in ((1, "shared_keys"), (2, "group_keys")):
+        wl, inp = _wiring_case(g, G_k, "weighted_relu", Hkv=2, kind="msa", block_size=m["block_size"],
+                               top_blocks=m["top_blocks"], window=m["window"])
+        res = orc.run(wl, inp, [(0, 0)], attention=False)
+        for grp in range(2):
+            assert res.blocks[(0, grp, 0)].tolist() == m["blocks_" + tag][grp], (tag, grp)
+            assert res.sets[(0, grp, 0)].tolist() == m["sets_" + tag][grp], (tag, grp)
+
+
+def test_blocks_set_hand_worked():
+    """Chosen blocks united with the window, nothing after the query."""
+    for c in _gold("group_wiring_hand.json")["blocks_set"]["cases"]:
+        assert orc.blocks_set(c["blocks"], c["p"], c["bs"], c["w"]).tolist() == c["set"], c
