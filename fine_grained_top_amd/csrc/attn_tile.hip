@@ -28,17 +28,24 @@ constexpr int kMaxBlkWords = 64;   // per-row block bitmap words (<= 2048 blocks
 constexpr float kLog2eT = 1.4426950408889634f;
 constexpr float kLn2T = 0.6931471805599453f;
 
+template <bool SPLIT>
 struct TileSmem {
   uint16_t ks[kTK * kKs];
   uint16_t vt[64 * 128];    // V tile row-major, XOR-swizzled 16-byte chunks
   uint32_t tiles[64];                    // tile bitmap (<= 2048 tiles)
   uint32_t rowblk[kTQ * kMaxBlkWords];   // BLOCKS: per-row selected-block bitmaps
+  uint16_t ks2[SPLIT ? kTK * kKs : 8];   // SPLIT: the low parts, laid out as ks / vt
+  uint16_t vt2[SPLIT ? 64 * 128 : 8];
 };
 
-// STRIDE: window/global mode with a dilated stride (the second key stream)
-template <bool STRIDE>
+// STRIDE: window/global mode with a dilated stride (the second key stream).
+// SPLIT: compressed entries held as two bf16 parts (hi in k/v, lo in
+// klo/vlo): S = K_hi Q^T + K_lo Q^T and O += P V_hi + P_hi V_lo (the term
+// P_lo V_lo is below 2^-16 of the product), so the entries keep ~16
+// significant bits instead of bf16's 8.
+template <bool STRIDE, bool SPLIT>
 __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
-  __shared__ __attribute__((aligned(16))) TileSmem sm;
+  __shared__ __attribute__((aligned(16))) TileSmem<SPLIT> sm;
   const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int qq = lane >> 4, c16 = lane & 15;
@@ -119,6 +126,8 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
 
   const uint16_t* kbase = (const uint16_t*)a.k.p + b * a.k.s[0] + kvh * a.k.s[1];
   const uint16_t* vbase = (const uint16_t*)a.v.p + b * a.v.s[0] + kvh * a.v.s[1];
+  const uint16_t* kbase2 = SPLIT ? (const uint16_t*)a.klo + b * a.k.s[0] + kvh * a.k.s[1] : nullptr;
+  const uint16_t* vbase2 = SPLIT ? (const uint16_t*)a.vlo + b * a.v.s[0] + kvh * a.v.s[1] : nullptr;
 
   // next tile after t (or -1)
   auto next_tile = [&](int t) -> int {
@@ -140,6 +149,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
   };
   // prefetch of one tile: chunk c = tid + 256u -> key c/16, 16-byte column c%16
   u32x4 pk[4], pv[4];
+  u32x4 pk2[SPLIT ? 4 : 1], pv2[SPLIT ? 4 : 1];
   auto load_tile = [&](int t) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -148,6 +158,10 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
       j = j < Lk ? j : Lk - 1;
       pk[u] = *(const u32x4*)(kbase + (int64_t)j * a.k.s[2] + 8 * (c & 15));
       pv[u] = *(const u32x4*)(vbase + (int64_t)j * a.v.s[2] + 8 * (c & 15));
+      if constexpr (SPLIT) {
+        pk2[u] = *(const u32x4*)(kbase2 + (int64_t)j * a.k.s[2] + 8 * (c & 15));
+        pv2[u] = *(const u32x4*)(vbase2 + (int64_t)j * a.v.s[2] + 8 * (c & 15));
+      }
     }
   };
   int t = next_any(-1);
@@ -161,6 +175,10 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
       *(u32x4*)&sm.ks[key * kKs + 8 * col] = pk[u];
       // V row-major, 16-byte chunk col of row key at col ^ (key mod 16)
       *(u32x4*)&sm.vt[key * 128 + 8 * (col ^ (key & 15))] = pv[u];
+      if constexpr (SPLIT) {
+        *(u32x4*)&sm.ks2[key * kKs + 8 * col] = pk2[u];
+        *(u32x4*)&sm.vt2[key * 128 + 8 * (col ^ (key & 15))] = pv2[u];
+      }
     }
     __syncthreads();
     const int tn = next_any(t);
@@ -192,6 +210,12 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           S[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(kr + 8 * s), Qb[s], S[st], 0, 0, 0);
+        if constexpr (SPLIT) {
+          const uint16_t* kr2 = &sm.ks2[(16 * st + c16) * kKs + 32 * qq];
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            S[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(kr2 + 8 * s), Qb[s], S[st], 0, 0, 0);
+        }
       }
       // masks: lane's keys j = j0 + 16*st + 4*qq + v for its row (column c16);
       // in a stride tile the keys are multiples (mb0 + 16*st + 4*qq + v) * stride
@@ -284,6 +308,18 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
           Bv[3] = (uint32_t)(uint16_t)a1[2] | ((uint32_t)(uint16_t)a1[3] << 16);
           O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&Ahi, *(const bf16x8*)&Bv, O[nt], 0, 0, 0);
           O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&Alo, *(const bf16x8*)&Bv, O[nt], 0, 0, 0);
+          if constexpr (SPLIT) {
+            const v4i16 c0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16*)&sm.vt2[tr0 * 128 + 8 * (lch ^ (tr0 & 15)) + wth]);
+            const v4i16 c1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16*)&sm.vt2[tr1 * 128 + 8 * (lch ^ (tr1 & 15)) + wth]);
+            u32x4 B2;
+            B2[0] = (uint32_t)(uint16_t)c0[0] | ((uint32_t)(uint16_t)c0[1] << 16);
+            B2[1] = (uint32_t)(uint16_t)c0[2] | ((uint32_t)(uint16_t)c0[3] << 16);
+            B2[2] = (uint32_t)(uint16_t)c1[0] | ((uint32_t)(uint16_t)c1[1] << 16);
+            B2[3] = (uint32_t)(uint16_t)c1[2] | ((uint32_t)(uint16_t)c1[3] << 16);
+            O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&Ahi, *(const bf16x8*)&B2, O[nt], 0, 0, 0);
+          }
         }
       }
     }
@@ -316,8 +352,9 @@ bool attn_tile_ok(const AttnParams& a) {
 
 hipError_t launch_attn_tile(const AttnParams& a, hipStream_t st) {
   dim3 grid((a.Nq + kTQ - 1) / kTQ, a.Hq, a.B);
-  if (a.mode == 2 && a.stride > 0) hipLaunchKernelGGL(attn_tile_kernel<true>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(attn_tile_kernel<false>, grid, dim3(256), 0, st, a);
+  if (a.mode == 2 && a.stride > 0) hipLaunchKernelGGL((attn_tile_kernel<true, false>), grid, dim3(256), 0, st, a);
+  else if (a.mode == 5 && a.klo) hipLaunchKernelGGL((attn_tile_kernel<false, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((attn_tile_kernel<false, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

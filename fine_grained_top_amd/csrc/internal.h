@@ -153,6 +153,10 @@ struct AttnParams {
   float* lse;              // [B, Hq, Nq] or null
   void* ws;
   size_t ws_bytes;
+  // mode 5 on the tile kernel: each entry is the bf16 pair k + klo (v + vlo),
+  // the low parts stored with the strides of k (v); null: one part
+  const void* klo;
+  const void* vlo;
 };
 size_t attn_ws_bytes(const AttnParams& p);
 // backward over the same visible sets: gradients of sum(dO * O)

@@ -2,9 +2,10 @@
 // "Sparse Attention" (completesystemdesign.dev), three parallel paths):
 //
 //  * compression: the K and V rows of every complete block are mean-pooled
-//    into one entry (nsa_pool: the exact mean rounded to nearest-even in the
-//    cache dtype), and each query attends over the entries of its complete
-//    past blocks (attention mode 5);
+//    into one entry (nsa_pool: the mean formed in float64, then kept as a
+//    pair of bf16 parts hi + lo for the MFMA tile kernel, about 2^-17 of the
+//    mean, or rounded once to float32 for the generic kernel), and each query
+//    attends over the entries of its complete past blocks (attention mode 5);
 //  * selection: attention over the tokens of the blocks chosen by
 //    spattn_block_select, whose scores are the compression branch's own
 //    logits q . mean(k) (attention mode 3 without a window);
@@ -30,9 +31,11 @@ SP_DEV uint32_t f64_to_bf16_rne(double x) {
 
 // One workgroup per (block, KV head, request), one thread per dimension: the
 // block's rows summed in float64 (exact for bf16/f32 rows spanning less than
-// 2^39 in magnitude), divided by the power-of-two block size (exact) and
-// rounded once to the cache dtype.
-__global__ __launch_bounds__(128) void nsa_pool_kernel(AttnParams a, void* kc, void* vc, int nbmax) {
+// 2^39 in magnitude), divided by the power-of-two block size (exact), then
+// written as hi = bf16(mean), lo = bf16(mean - hi) (kclo/vclo given) or as the
+// nearest float32.
+__global__ __launch_bounds__(128) void nsa_pool_kernel(AttnParams a, void* kc, void* vc, uint16_t* kclo,
+                                                       uint16_t* vclo, int nbmax) {
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int L = min(a.ctx_len ? a.ctx_len[b] : a.ctx, a.ctx);
   const int c = threadIdx.x;
@@ -59,12 +62,16 @@ __global__ __launch_bounds__(128) void nsa_pool_kernel(AttnParams a, void* kc, v
   }
   const double inv = 1.0 / (double)a.bs;              // a power of two: exact
   const int64_t o = (((int64_t)b * a.Hkv + h) * nbmax + blk) * a.d + c;
-  if (a.k.dt == DT_BF16) {
-    ((uint16_t*)kc)[o] = (uint16_t)f64_to_bf16_rne(sk * inv);
-    ((uint16_t*)vc)[o] = (uint16_t)f64_to_bf16_rne(sv * inv);
+  const double mk = sk * inv, mv = sv * inv;
+  if (kclo) {
+    const uint32_t hk = f64_to_bf16_rne(mk), hv = f64_to_bf16_rne(mv);
+    ((uint16_t*)kc)[o] = (uint16_t)hk;
+    ((uint16_t*)vc)[o] = (uint16_t)hv;
+    kclo[o] = (uint16_t)f64_to_bf16_rne(mk - (double)bf16_to_f32(hk));   // exact difference
+    vclo[o] = (uint16_t)f64_to_bf16_rne(mv - (double)bf16_to_f32(hv));
   } else {
-    ((float*)kc)[o] = (float)(sk * inv);
-    ((float*)vc)[o] = (float)(sv * inv);
+    ((float*)kc)[o] = (float)mk;
+    ((float*)vc)[o] = (float)mv;
   }
 }
 
@@ -87,25 +94,44 @@ __global__ __launch_bounds__(128) void nsa_combine_kernel(NsaParams p, const flo
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // The three branches' attention parameters, with the workspace laid out as
-// pooled K | pooled V | O of each branch [B, Hq, Nq, d] f32 | branch workspace.
+// pooled K | pooled V | (split: K low parts | V low parts) | O of each branch
+// [B, Hq, Nq, d] f32 | branch workspace.
 struct NsaLayout {
   AttnParams cmp, sel, win;
-  size_t kc, vc, oc, os, ow, attn, total;
+  size_t kc, vc, kclo, vclo, oc, os, ow, attn, total;
   int nbmax;
+  bool split;              // bf16 hi/lo entries on the tile kernel, else float32 entries
 };
 
 static NsaLayout nsa_layout(const NsaParams& p) {
   NsaLayout l;
   const AttnParams& a = p.a;
-  const int es = a.k.dt == DT_F32 ? 4 : 2;
   l.nbmax = a.ctx / a.bs;
-  const size_t pooled = (size_t)a.B * a.Hkv * l.nbmax * a.d * es;
+  l.cmp = a;
+  l.cmp.mode = 5;
+  for (View4* vw : {&l.cmp.k, &l.cmp.v}) {
+    vw->n[2] = l.nbmax;
+    vw->s[3] = 1;
+    vw->s[2] = a.d;
+    vw->s[1] = (int64_t)l.nbmax * a.d;
+    vw->s[0] = (int64_t)a.Hkv * l.nbmax * a.d;
+  }
+  l.split = a.k.dt == DT_BF16 && attn_tile_ok(l.cmp);
+  if (!l.split) l.cmp.k.dt = l.cmp.v.dt = DT_F32;
+  const size_t pooled = (size_t)a.B * a.Hkv * l.nbmax * a.d * (l.split ? 2 : 4);
   const size_t obytes = (size_t)a.B * a.Hq * a.Nq * a.d * sizeof(float);
   size_t off = 0;
   l.kc = off;
   off += al256(pooled);
   l.vc = off;
   off += al256(pooled);
+  l.kclo = l.vclo = 0;
+  if (l.split) {
+    l.kclo = off;
+    off += al256(pooled);
+    l.vclo = off;
+    off += al256(pooled);
+  }
   l.oc = off;
   off += al256(obytes);
   l.os = off;
@@ -120,15 +146,6 @@ static NsaLayout nsa_layout(const NsaParams& p) {
     x.os[0] = (int64_t)a.Hq * a.Nq * a.d;
     x.lse = nullptr;
   };
-  l.cmp = a;
-  l.cmp.mode = 5;
-  for (View4* vw : {&l.cmp.k, &l.cmp.v}) {
-    vw->n[2] = l.nbmax;
-    vw->s[3] = 1;
-    vw->s[2] = a.d;
-    vw->s[1] = (int64_t)l.nbmax * a.d;
-    vw->s[0] = (int64_t)a.Hkv * l.nbmax * a.d;
-  }
   dense_out(l.cmp);
   l.sel = a;
   l.sel.mode = 3;
@@ -158,12 +175,17 @@ hipError_t launch_nsa(const NsaParams& p, hipStream_t st) {
   float* osel = (float*)(w + l.os);
   float* ow = (float*)(w + l.ow);
   hipError_t e;
+  uint16_t* kclo = l.split ? (uint16_t*)(w + l.kclo) : nullptr;
+  uint16_t* vclo = l.split ? (uint16_t*)(w + l.vclo) : nullptr;
   if (l.nbmax > 0) {
-    hipLaunchKernelGGL(nsa_pool_kernel, dim3(l.nbmax, a.Hkv, a.B), dim3(128), 0, st, a, kc, vc, l.nbmax);
+    hipLaunchKernelGGL(nsa_pool_kernel, dim3(l.nbmax, a.Hkv, a.B), dim3(128), 0, st, a, kc, vc, kclo, vclo,
+                       l.nbmax);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   l.cmp.k.p = kc;
   l.cmp.v.p = vc;
+  l.cmp.klo = kclo;
+  l.cmp.vlo = vclo;
   l.cmp.o = oc;
   l.sel.o = osel;
   l.win.o = ow;

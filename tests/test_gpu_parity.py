@@ -812,13 +812,13 @@ def test_nsa_branches_one_at_a_time():
     worst = 0.0
     qpk = H // wl.Hkv
     nb = Nq // wl.block_size
-    pooled = [(orc.pooled_blocks(k64[x], wl.block_size, nb, "bf16"), orc.pooled_blocks(v64[x], wl.block_size, nb, "bf16"))
+    pooled = [(orc.pooled_blocks(k64[x], wl.block_size, nb), orc.pooled_blocks(v64[x], wl.block_size, nb))
               for x in range(wl.Hkv)]
     for r in list(range(0, 70)) + list(range(70, Nq, 37)):
         for h in range(H):
             got = O[0, h, r]
             want = orc.nsa_attention(q64[h, r], k64[h // qpk], v64[h // qpk], r, wl.block_size, [], wl.window,
-                                     np.array([1.0, 0.0, 0.0]), 1 / math.sqrt(d), fmt="bf16",
+                                     np.array([1.0, 0.0, 0.0]), 1 / math.sqrt(d),
                                      pooled=pooled[h // qpk])
             worst = max(worst, float(np.abs(got - want).max()))
     say(f"  compression branch vs oracle {worst:.3e}")
