@@ -13,6 +13,7 @@
 
 #include "../../include/spattn.h"
 #include "internal.h"
+#include "api_internal.h"
 
 namespace {
 
@@ -665,10 +666,17 @@ SPATTN_API size_t spattn_sparse_attn_fwd_workspace(const spattn_tensor* q, const
   return sp::attn_ws_bytes(p);
 }
 
-static int attn_fwd(const spattn_tensor* q, const spattn_tensor* k, const spattn_tensor* v,
-                    const spattn_kv_pages* pages, const int32_t* ctx_len, float scale, const spattn_selection* sel,
-                    const spattn_tensor* o_out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
-  sp::AttnParams p;
+}  // extern "C"
+
+namespace spapi {
+
+int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
+int device_check() { return device_ok(); }
+
+int attn_fwd_prepare(const spattn_tensor* q, const spattn_tensor* k, const spattn_tensor* v,
+                     const spattn_kv_pages* pages, const int32_t* ctx_len, float scale, const spattn_selection* sel,
+                     const spattn_tensor* o_out, float* lse_out, sp::AttnParams& p, size_t& need) {
   int rc;
   if ((rc = attn_setup(q, k, v, sel, p, true, pages))) return rc;
   if ((rc = check_tensor(o_out, "o_out", 4, false))) return rc;
@@ -681,12 +689,31 @@ static int attn_fwd(const spattn_tensor* q, const spattn_tensor* k, const spattn
   p.o = (float*)o_out->data;
   for (int i = 0; i < 4; ++i) p.os[i] = o_out->stride[i];
   p.lse = lse_out;
-  const size_t need = sp::attn_ws_bytes(p);
-  if (ws_bytes < need || (need && !ws)) return fail(SPATTN_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  need = sp::attn_ws_bytes(p);
+  return SPATTN_OK;
+}
+
+int attn_fwd_launch(sp::AttnParams& p, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
   p.ws = ws;
   p.ws_bytes = ws_bytes;
   if ((rc = device_ok())) return rc;
   return launched(sp::launch_attention(p, (hipStream_t)stream));
+}
+
+}  // namespace spapi
+
+extern "C" {
+
+static int attn_fwd(const spattn_tensor* q, const spattn_tensor* k, const spattn_tensor* v,
+                    const spattn_kv_pages* pages, const int32_t* ctx_len, float scale, const spattn_selection* sel,
+                    const spattn_tensor* o_out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+  sp::AttnParams p;
+  size_t need = 0;
+  int rc;
+  if ((rc = spapi::attn_fwd_prepare(q, k, v, pages, ctx_len, scale, sel, o_out, lse_out, p, need))) return rc;
+  if (ws_bytes < need || (need && !ws)) return fail(SPATTN_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  return spapi::attn_fwd_launch(p, ws, ws_bytes, stream);
 }
 
 SPATTN_API int spattn_sparse_attn_fwd(const spattn_tensor* q, const spattn_tensor* k, const spattn_tensor* v,

@@ -75,6 +75,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "spattn_sparse_attn_fwd_workspace": (sz, [P(Tensor), P(Tensor), P(Selection)]),
         "spattn_sparse_attn_fwd": (ctypes.c_int, [P(Tensor), P(Tensor), P(Tensor), vp, ctypes.c_float,
                                                   P(Selection), P(Tensor), vp, vp, sz, vp]),
+        "spattn_noalloc_scratch_bytes": (sz, []),
+        "spattn_sparse_attn_fwd_noalloc": (ctypes.c_int, [P(Tensor), P(Tensor), P(Tensor), vp, ctypes.c_float,
+                                                          P(Selection), P(Tensor), vp, vp]),
         "spattn_sparse_attn_fwd_paged_workspace": (sz, [P(Tensor), P(Tensor), P(KvPages), P(Selection)]),
         "spattn_sparse_attn_fwd_paged": (ctypes.c_int, [P(Tensor), P(Tensor), P(Tensor), P(KvPages), vp,
                                                         ctypes.c_float, P(Selection), P(Tensor), vp, vp, sz, vp]),
@@ -290,6 +293,16 @@ def spattn_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ct
     _check(LIB.spattn_sparse_attn_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), _ptr(ctx_len),
                                       scale, ctypes.byref(sel), ctypes.byref(to), _ptr(lse_out), _ptr(ws),
                                       0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def spattn_sparse_attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                   ctx_len: Optional[torch.Tensor], scale: float, sel: Selection,
+                                   o_out: torch.Tensor, lse_out: Optional[torch.Tensor] = None,
+                                   stream=None) -> None:
+    tq, tk, tv, to = tensor(q), tensor(k), tensor(v), tensor(o_out)
+    _check(LIB.spattn_sparse_attn_fwd_noalloc(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), _ptr(ctx_len),
+                                              scale, ctypes.byref(sel), ctypes.byref(to), _ptr(lse_out),
+                                              _stream(stream)))
 
 
 def spattn_sparse_attn_fwd_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, pages: KvPages,

@@ -330,6 +330,28 @@ SPATTN_API int spattn_sparse_attn_fwd(const spattn_tensor* q, const spattn_tenso
                                       size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * spattn_sparse_attn_fwd_noalloc — spattn_sparse_attn_fwd for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation. It takes no workspace:
+ * the kernels' scratch (the decode gather's split partials) lives in a fixed
+ * per-device array of spattn_noalloc_scratch_bytes() bytes (32 MiB) that
+ * the library holds on every device it runs on until the process ends.
+ *
+ * Arguments, layouts and results are those of spattn_sparse_attn_fwd (the
+ * same kernels run). A call whose workspace query exceeds the array's size
+ * returns SPATTN_ERR_WORKSPACE before touching the device (routed blocks at
+ * prefill sizes do; decode index lists do not). Nothing is allocated and
+ * nothing is synchronized. All calls on one device share the array: calls
+ * ordered on one stream are safe, calls that overlap in time on one device
+ * (other streams or host threads) race on it.
+ * ---------------------------------------------------------------------- */
+SPATTN_API size_t spattn_noalloc_scratch_bytes(void);
+SPATTN_API int spattn_sparse_attn_fwd_noalloc(const spattn_tensor* q, const spattn_tensor* k,
+                                              const spattn_tensor* v, const int32_t* ctx_len,
+                                              float scale, const spattn_selection* sel,
+                                              const spattn_tensor* o_out, float* lse_out, void* stream);
+
+/* ------------------------------------------------------------------------
  * spattn_sparse_attn_fwd_paged — the same attention over paged K/V storage
  * (the serving layout in which the pages of "Sparse Attention in 2026", DSA
  * list, are the unit of selection and of reading).
