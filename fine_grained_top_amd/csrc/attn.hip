@@ -293,14 +293,16 @@ __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int 
   __shared__ __attribute__((aligned(16))) uint16_t vs[4][32 * kVStride];
   __shared__ int idxs[4][kMaxTilesPerWave * 32];
 
-  // Q^T as the B operand: lane holds head c16, dims 32*qq + 8*ks + v
+  // Q^T as the B operand: lane holds head c16, dims 8 * (4 ks + qq) + v for
+  // k-step ks (the K rows below use the same order of the dims, so the four
+  // lanes of a key row read 64 contiguous bytes per load instruction)
   bf16x8 Qb[4];
   {
     const int hh = c16;
     if (hh < Hg) {
-      const uint16_t* qp = (const uint16_t*)a.q.p + b * a.q.s[0] + (h0 + hh) * a.q.s[1] + r * a.q.s[2] + 32 * qq;
+      const uint16_t* qp = (const uint16_t*)a.q.p + b * a.q.s[0] + (h0 + hh) * a.q.s[1] + r * a.q.s[2] + 8 * qq;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) Qb[ks] = *(const bf16x8*)(qp + 8 * ks);
+      for (int ks = 0; ks < 4; ++ks) Qb[ks] = *(const bf16x8*)(qp + 32 * ks);
     } else {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) Qb[ks] = (bf16x8){};
@@ -346,17 +348,18 @@ __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int 
   }
   __builtin_amdgcn_wave_barrier();
 
-  // K rows for the two 16-key subtiles (row c16 and 16 + c16, dims 32*qq..+32)
-  // and V rows (chunk u: key qq + 4u, 16-byte column c16) of tile i
+  // K rows for the two 16-key subtiles (row c16 and 16 + c16; k-step ks:
+  // dims 8 * (4 ks + qq) .. +8, so one instruction reads 64 contiguous bytes
+  // of each row) and V rows (chunk u: key qq + 4u, 16-byte column c16) of tile i
   auto issue = [&](int i, u32x4 (&kr)[2][4], u32x4 (&vr)[8]) {
     const int* ix = wix + 32 * i;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       int j = ix[16 * st + c16];
       j = j < 0 ? 0 : j;
-      const uint16_t* kp = kbase + krow(j) + 32 * qq;
+      const uint16_t* kp = kbase + krow(j) + 8 * qq;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kr[st][ks] = *(const u32x4*)(kp + 8 * ks);
+      for (int ks = 0; ks < 4; ++ks) kr[st][ks] = *(const u32x4*)(kp + 32 * ks);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {

@@ -31,41 +31,51 @@ SP_DEV float load_val(const void* p, int dt, int64_t i) {
 }
 
 // ----------------------------------------------------------------------------
-// MODE: 0 scores, 1 threshold filter (candidate lists), 2 scores and page keys
-template <int KT, int NMB, int HPG, bool RELU, int MODE>
+// MODE: 0 scores, 1 threshold filter (candidate lists), 2 scores and page keys.
+// CPW: consecutive 512-key chunks per workgroup (one request); PD: tiles of
+// 32 keys each wave keeps in flight. Each wave walks its CPW * 4 tiles in
+// order, the key bytes of tile t + PD requested as tile t is scored, so the
+// loads of a workgroup stream while it computes (PD = CPW * 4: all at once).
+template <int KT, int NMB, int HPG, bool RELU, int MODE, int CPW, int PD>
 __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
   constexpr bool FILTER = MODE == 1;
   constexpr bool PM = MODE == 2;
+  constexpr int TPW = kMfmaChunk / 32 / 4;   // tiles per wave and chunk
+  constexpr int NT = CPW * TPW;              // tiles per wave
+  constexpr int RW = KT == DT_FP8 ? 2 : 4;   // 16-byte loads per lane and tile
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int L = min(p.ctx_len ? p.ctx_len[b] : p.ctx, p.ctx);
-  const int j0 = blockIdx.x * kMfmaChunk;
-  if (j0 >= L) return;
+  const int jw = blockIdx.x * CPW * kMfmaChunk;        // first key of the workgroup
+  if (jw >= L) return;
   const int M = p.Nq * p.H_I;
   const int hshift = __builtin_ctz(p.H_I);
   const int mbase = 128 * blockIdx.z;                 // first (row, head) slot of this workgroup
-  // causal skip: no row of this slot block sees any key of the chunk
+  // causal skip: no row of this slot block sees any key of the chunks
   {
     const int rmax = min(p.Nq - 1, (mbase + 32 * NMB - 1) >> hshift);
-    if (j0 > L - p.Nq + rmax) return;
+    if (jw > L - p.Nq + rmax) return;
   }
-  __shared__ uint32_t lcount[128];
-  __shared__ float wsl[128];
-  __shared__ float tsl[128];          // filter threshold of each slot's selection row
-  __shared__ uint32_t pml[PM ? 128 * 16 : 1];   // page keys: [slot][page of the chunk]
-  if (PM)
-    for (int i = threadIdx.x; i < 128 * 16; i += 256) pml[i] = 0u;
-  for (int i = threadIdx.x; i < 128; i += 256) {
-    if (FILTER) lcount[i] = 0;
-    float wv = 0.f, tv = INFINITY;
-    const int ms = mbase + i;
-    if (RELU && ms < M) wv = p.w[b * p.ws_[0] + (ms >> hshift) * p.ws_[1] + (ms & (p.H_I - 1)) * p.ws_[2]];
-    if (FILTER && ms < M) tv = p.tau[(b * p.G_sel + (ms & (p.H_I - 1)) / HPG) * p.Nq + (ms >> hshift)];
-    wsl[i] = wv;
-    tsl[i] = tv;
-  }
-  __syncthreads();
+  // key bytes of tile t: key jw + (t / 4) * 512 + (wid + 4 (t % 4)) * 32 + col,
+  // dims 32 half .. 32 half + 31
+  auto tile_key = [&](int t) { return jw + (t / TPW) * kMfmaChunk + (wid + 4 * (t % TPW)) * 32 + col; };
+  auto load = [&](int t, u32x4 (&dst)[RW]) {
+    const int j = tile_key(t);
+    const int jc = j < L ? j : L - 1;
+    if (KT == DT_FP8) {
+      const uint8_t* kp = (const uint8_t*)p.k.p + b * p.k.s[0] + (int64_t)jc * p.k.s[1] + 32 * half;
+      dst[0] = *(const u32x4*)kp;
+      dst[1] = *(const u32x4*)(kp + 16);
+    } else {
+      const uint16_t* kp = (const uint16_t*)p.k.p + b * p.k.s[0] + (int64_t)jc * p.k.s[1] + 32 * half;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dst[c] = *(const u32x4*)(kp + 8 * c);
+    }
+  };
+  u32x4 raw[PD][RW];
+#pragma unroll
+  for (int t = 0; t < PD && t < NT; ++t) load(t, raw[t]);
 
   // A operands: query slot m = mbase + 32*mb + col, dims 32*half + 8*s + v (s = k-step)
   bf16x8 A[NMB][4];
@@ -83,15 +93,33 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
     }
   }
 
+  __shared__ uint32_t lcount[FILTER ? CPW : 1][128];
+  __shared__ float wsl[128];
+  __shared__ float tsl[128];          // filter threshold of each slot's selection row
+  __shared__ uint32_t pml[PM ? 128 * 16 : 1];   // page keys: [slot][page of the chunk]
+  if (PM)
+    for (int i = threadIdx.x; i < 128 * 16; i += 256) pml[i] = 0u;
+  for (int i = threadIdx.x; i < 128; i += 256) {
+    if (FILTER)
+#pragma unroll
+      for (int cc = 0; cc < CPW; ++cc) lcount[cc][i] = 0;
+    float wv = 0.f, tv = INFINITY;
+    const int ms = mbase + i;
+    if (RELU && ms < M) wv = p.w[b * p.ws_[0] + (ms >> hshift) * p.ws_[1] + (ms & (p.H_I - 1)) * p.ws_[2]];
+    if (FILTER && ms < M) tv = p.tau[(b * p.G_sel + (ms & (p.H_I - 1)) / HPG) * p.Nq + (ms >> hshift)];
+    wsl[i] = wv;
+    tsl[i] = tv;
+  }
+  __syncthreads();
+
   // per (slot block, head group) constants of the filter, when they fit in
   // registers: last visible key of the half-wave's slot row (-1: no row), its
-  // threshold, its LDS counter and the base of its output slots
+  // threshold and its selection row within the request
   constexpr int G4 = 16 / HPG;
   constexpr bool HOIST = FILTER && NMB * G4 <= 8;
   constexpr int NH = HOIST ? NMB * G4 : 1;
   int hlim[NH], hlrow[NH];
   float hthr[NH];
-  int llrow = 0;   // leader lanes 2 e + hf (e = mb * G4 + gi): slot row of (mb, gi, half hf)
   if constexpr (HOIST) {
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
@@ -105,43 +133,34 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
         hthr[e] = tsl[(m0 - mbase) & 127];
         hlrow[e] = g * p.Nq + r;
       }
-    const int e = lane >> 1, hf = lane & 1;
-    const int mb = e / G4, v0 = (e % G4) * HPG;
-    const int m0 = mbase + 32 * mb + 8 * (v0 >> 2) + 4 * hf + (v0 & 3);
-    llrow = (((m0 & (p.H_I - 1)) / HPG) * p.Nq + (m0 >> hshift)) & 127;
   }
-  // this workgroup's candidate slots: [selection row of the request][cap]
+  // candidate slots of chunk cc: [selection row of the request][cap]
   const int nrl = p.G_sel * p.Nq;
-  u32x2* const cw = FILTER ? (u32x2*)p.cand + ((int64_t)b * p.nchunk + blockIdx.x) * nrl * p.cap : nullptr;
+  auto chunk_cand = [&](int cc) -> u32x2* {
+    return (u32x2*)p.cand + ((int64_t)b * p.nchunk + blockIdx.x * CPW + cc) * nrl * p.cap;
+  };
+  u32x2* cwc[CPW];
+#pragma unroll
+  for (int cc = 0; cc < CPW; ++cc) cwc[cc] = FILTER ? chunk_cand(cc) : nullptr;
 
-  u16x2 kmx = {0, 0};
-  constexpr int TPW = kMfmaChunk / 32 / 4;   // tiles per wave
-  // raw key bytes for all tiles of this wave
-  u32x4 raw[TPW][KT == DT_FP8 ? 2 : 4];
+  u16x2 kmx[CPW];
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int j = j0 + (wid + 4 * i) * 32 + col;
-    const int jc = j < L ? j : L - 1;
-    if (KT == DT_FP8) {
-      const uint8_t* kp = (const uint8_t*)p.k.p + b * p.k.s[0] + (int64_t)jc * p.k.s[1] + 32 * half;
-      raw[i][0] = *(const u32x4*)kp;
-      raw[i][1] = *(const u32x4*)(kp + 16);
-    } else {
-      const uint16_t* kp = (const uint16_t*)p.k.p + b * p.k.s[0] + (int64_t)jc * p.k.s[1] + 32 * half;
+  for (int cc = 0; cc < CPW; ++cc) kmx[cc] = u16x2{0, 0};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) raw[i][c] = *(const u32x4*)(kp + 8 * c);
-    }
-  }
-
+  for (int t = 0; t < NT; ++t) {
+    const int cc = t / TPW, i = t % TPW;
+    u32x4 cur[RW];
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int j = j0 + (wid + 4 * i) * 32 + col;
+    for (int c = 0; c < RW; ++c) cur[c] = raw[t % PD][c];
+    if (t + PD < NT) load(t + PD, raw[t % PD]);
+    if (jw + cc * kMfmaChunk >= L) continue;            // the chunk lies past the context
+    const int j = tile_key(t);
     // B operands (bf16) for the 4 k-steps
     u32x4 Bw[4];
     if (KT == DT_FP8) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const uint32_t w0 = raw[i][s >> 1][2 * (s & 1)], w1 = raw[i][s >> 1][2 * (s & 1) + 1];
+        const uint32_t w0 = cur[s >> 1][2 * (s & 1)], w1 = cur[s >> 1][2 * (s & 1) + 1];
         Bw[s][0] = fp8x2_to_bf16x2<false>(w0);
         Bw[s][1] = fp8x2_to_bf16x2<true>(w0);
         Bw[s][2] = fp8x2_to_bf16x2<false>(w1);
@@ -149,7 +168,7 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
       }
     } else {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) Bw[s] = raw[i][s];
+      for (int s = 0; s < 4; ++s) Bw[s] = cur[s];
     }
     if (j < L) {
 #pragma unroll
@@ -157,7 +176,7 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const uint32_t a = Bw[s][c] & 0x7FFF7FFFu;
-          kmx = __builtin_elementwise_max(kmx, *(const u16x2*)&a);
+          kmx[cc] = __builtin_elementwise_max(kmx[cc], *(const u16x2*)&a);
         }
     }
 #pragma unroll
@@ -173,8 +192,8 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
       for (int gi = 0; gi < G4; ++gi) {
         float sc = 0.f;
 #pragma unroll
-        for (int t = 0; t < HPG; ++t) {
-          const int v = gi * HPG + t;
+        for (int tt = 0; tt < HPG; ++tt) {
+          const int v = gi * HPG + tt;
           const float wv = RELU ? wsl[32 * mb + 8 * (v >> 2) + 4 * half + (v & 3)] : 0.f;
           // ReLU on the bit pattern: a negative float is a negative int
           const float rl = __int_as_float(max(__float_as_int(acc[v]), 0));
@@ -209,43 +228,20 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
           }
         }
       } else if constexpr (HOIST) {
-        // survivors of all head groups at once: leader lane 2 e + hf reserves
-        // the slots of (group e, half hf) with one LDS atomic for all leaders
-        bool cdv[G4];
-        uint64_t bmv[G4], any = 0;
+        // survivors: each surviving lane takes its slot with one LDS atomic
+        // (about one survivor per selection row and tile: little contention)
 #pragma unroll
         for (int gi = 0; gi < G4; ++gi) {
           const int e = mb * G4 + gi;
-          cdv[gi] = j <= hlim[e] && scv[gi] >= hthr[e];
-          bmv[gi] = ballot(cdv[gi]);
-          any |= bmv[gi];
-        }
-        if (any) {
-          uint32_t cnt = 0;
-#pragma unroll
-          for (int gi = 0; gi < G4; ++gi) {
-            const int e = mb * G4 + gi;
-            const uint32_t c0 = __popc((uint32_t)bmv[gi]), c1 = __popc((uint32_t)(bmv[gi] >> 32));
-            if ((lane >> 1) == e) cnt = (lane & 1) ? c1 : c0;
-          }
-          uint32_t base = 0;
-          if (cnt) base = atomicAdd(&lcount[llrow], cnt);
-#pragma unroll
-          for (int gi = 0; gi < G4; ++gi) {
-            if (!bmv[gi]) continue;
-            const int e = mb * G4 + gi;
-            const uint32_t b0 = __builtin_amdgcn_readlane(base, 2 * e);
-            const uint32_t b1 = __builtin_amdgcn_readlane(base, 2 * e + 1);
-            const uint32_t below = lanes_below(bmv[gi]) - (half ? (uint32_t)__popc((uint32_t)bmv[gi]) : 0u);
-            const uint32_t slot = (half ? b1 : b0) + below;
-            if (cdv[gi] && slot < (uint32_t)p.cap) {
-              const uint32_t o = (uint32_t)hlrow[e] * (uint32_t)p.cap + slot;
-              cw[o] = u32x2{f32_order_key(scv[gi]), (uint32_t)j};
-            }
+          if (j <= hlim[e] && scv[gi] >= hthr[e]) {
+            const uint32_t slot = atomicAdd(&lcount[cc][hlrow[e]], 1u);
+            if (slot < (uint32_t)p.cap)
+              cwc[cc][(uint32_t)hlrow[e] * (uint32_t)p.cap + slot] = u32x2{f32_order_key(scv[gi]), (uint32_t)j};
           }
         }
       } else {
         // many head groups: one half-wave append per group
+        u32x2* const cw = chunk_cand(cc);
 #pragma unroll
         for (int gi = 0; gi < G4; ++gi) {
           const int v0 = gi * HPG;
@@ -258,7 +254,7 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
           if (bm) {
             const uint32_t mh = (uint32_t)(bm >> (32 * half));
             uint32_t base = 0;
-            if (col == 0 && mh) base = atomicAdd(&lcount[lrow], (uint32_t)__popc(mh));
+            if (col == 0 && mh) base = atomicAdd(&lcount[cc][lrow], (uint32_t)__popc(mh));
             base = (uint32_t)__shfl((int)base, 32 * half, 64);
             const uint32_t slot = base + (uint32_t)__popc(mh & ((1u << col) - 1u));
             if (cand && slot < (uint32_t)p.cap) {
@@ -271,15 +267,19 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
     }
   }
 
-  // largest |k| element of this chunk (valid keys only)
-  __shared__ uint32_t red[4];
-  uint32_t km = max((uint32_t)kmx[0], (uint32_t)kmx[1]);
-  km = wave_max_u32(km);
-  if (lane == 0) red[wid] = km;
+  // largest |k| element of each chunk (valid keys only)
+  __shared__ uint32_t red[CPW][4];
+#pragma unroll
+  for (int cc = 0; cc < CPW; ++cc) {
+    uint32_t km = max((uint32_t)kmx[cc][0], (uint32_t)kmx[cc][1]);
+    km = wave_max_u32(km);
+    if (lane == 0) red[cc][wid] = km;
+  }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t m4 = max(max(red[0], red[1]), max(red[2], red[3]));
-    p.kmax[(int64_t)b * p.nchunk + blockIdx.x] = bf16_to_f32(m4);
+  if (threadIdx.x < CPW) {
+    const int cx = blockIdx.x * CPW + threadIdx.x;
+    const uint32_t m4 = max(max(red[threadIdx.x][0], red[threadIdx.x][1]), max(red[threadIdx.x][2], red[threadIdx.x][3]));
+    if (cx < p.nchunk) p.kmax[(int64_t)b * p.nchunk + cx] = bf16_to_f32(m4);
   }
   if (PM) {
     // one key per (selection row, page of the chunk), from the row's first slot
@@ -291,14 +291,19 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
       if (m >= M || h % HPG) continue;
       const int r = m >> hshift, g = h / HPG;
       const int64_t row = ((int64_t)b * p.G_sel + g) * p.Nq + r;
-      const int page = (j0 >> p.pk_lgP) + pl;
+      const int page = (jw >> p.pk_lgP) + pl;
       if (page < p.pk_stride) p.pkeys[row * p.pk_stride + page] = pml[sl * 16 + pl];
     }
   }
   if (FILTER) {
     const int nrows = p.G_sel * p.Nq;
-    for (int i = threadIdx.x; i < nrows; i += 256)
-      p.cand_n[((int64_t)b * p.nchunk + blockIdx.x) * nrows + i] = lcount[i];
+#pragma unroll
+    for (int cc = 0; cc < CPW; ++cc) {
+      const int cx = blockIdx.x * CPW + cc;
+      if (cx < p.nchunk)
+        for (int i = threadIdx.x; i < nrows; i += 256)
+          p.cand_n[((int64_t)b * p.nchunk + cx) * nrows + i] = lcount[cc][i];
+    }
   }
 }
 
@@ -391,8 +396,15 @@ size_t indexer_ws_bytes(int B, int G_k, int ctx) {
 
 template <int KT, int NMB, int HPG, bool RELU, int MODE>
 static void launch_mfma(const IndexerParams& p, hipStream_t st) {
-  dim3 grid((p.ctx + kMfmaChunk - 1) / kMfmaChunk, p.B, (p.Nq * p.H_I + 127) / 128);
-  hipLaunchKernelGGL((idx_mfma64_kernel<KT, NMB, HPG, RELU, MODE>), grid, dim3(256), 0, st, p);
+  // the filter (decode: few rows, long contexts) streams two chunks per
+  // workgroup, three tiles in flight per wave; the other modes load a
+  // chunk's tiles at once
+  constexpr bool STREAM = MODE == 1 && NMB == 1;
+  constexpr int CPW = STREAM ? 2 : 1;
+  constexpr int PD = STREAM ? 3 : kMfmaChunk / 32 / 4;
+  const int nchunk = (p.ctx + kMfmaChunk - 1) / kMfmaChunk;
+  dim3 grid((nchunk + CPW - 1) / CPW, p.B, (p.Nq * p.H_I + 127) / 128);
+  hipLaunchKernelGGL((idx_mfma64_kernel<KT, NMB, HPG, RELU, MODE, CPW, PD>), grid, dim3(256), 0, st, p);
 }
 
 template <int KT, int NMB, int MODE>

@@ -942,110 +942,110 @@ SP_DEV float recompute_score(const IndexerRow& r, int64_t j) {
   return s;
 }
 
-// Pilot, stage 1: one thread per (sampled key, selection row): the row's
-// heads score the key in float32; a key the row cannot see (after its
-// position) gets the order key 0, which no finite score has.
-constexpr int kPsThreads = 256;
-__global__ __launch_bounds__(kPsThreads) void fz_pilot_score_kernel(TopkParams p, uint32_t* skeys, int slots) {
-  const IndexerParams& x = p.ix;
-  const int b = blockIdx.y;
-  const int rowl = blockIdx.z;                      // (g, r) within the request
-  const int g = rowl / x.Nq, r = rowl % x.Nq;
-  const int i = blockIdx.x * kPsThreads + threadIdx.x;
-  __shared__ float qs[4 * 64];                      // <= 4 heads per group, d_I = 64
-  __shared__ float wsh[4];
-  // the sampled key's bytes are requested first, so that their latency
-  // overlaps the staging of the group's queries
-  const int L = min(p.ctx_len ? p.ctx_len[b] : p.ctx, p.ctx);
-  const int j = (i / kPilotRun) * kPilotStride + (i % kPilotRun);
-  const bool vis = i < slots && j <= L - x.Nq + r;
-  u32x4 raw[8];
-  if (vis) {
-    if (x.k.dt == DT_FP8) {
-      const u32x4* kp = (const u32x4*)((const uint8_t*)x.k.p + b * x.k.s[0] + (int64_t)j * x.k.s[1]);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) raw[u] = kp[u];
-    } else {
-      const u32x4* kp = (const u32x4*)((const uint16_t*)x.k.p + b * x.k.s[0] + (int64_t)j * x.k.s[1]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) raw[u] = kp[u];
-    }
-  }
-  for (int e = threadIdx.x; e < x.hpg * 64; e += kPsThreads) {
-    const int h = g * x.hpg + (e >> 6);
-    qs[e] = (float)load_f64(x.q.p, x.q.dt, b * x.q.s[0] + r * x.q.s[1] + h * x.q.s[2] + (e & 63));
-  }
-  if ((int)threadIdx.x < x.hpg)
-    wsh[threadIdx.x] = x.relu ? x.w[b * x.ws_[0] + r * x.ws_[1] + (g * x.hpg + threadIdx.x) * x.ws_[2]] : 1.f;
-  __syncthreads();
-  if (i >= slots) return;
-  uint32_t key = 0u;
-  if (vis) {
-    float kv[64];
-    if (x.k.dt == DT_FP8) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u][v], false);
-          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u][v], true);
-          kv[16 * u + 4 * v + 0] = lo[0];
-          kv[16 * u + 4 * v + 1] = lo[1];
-          kv[16 * u + 4 * v + 2] = hi[0];
-          kv[16 * u + 4 * v + 3] = hi[1];
-        }
-    } else {
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          kv[8 * u + 2 * v] = __uint_as_float(raw[u][v] << 16);
-          kv[8 * u + 2 * v + 1] = __uint_as_float(raw[u][v] & 0xFFFF0000u);
-        }
-    }
-    float sc = 0.f;
-    for (int h = 0; h < x.hpg; ++h) {
-      const f32x4* qh = (const f32x4*)(qs + h * 64);
-      float d = 0.f;
-#pragma unroll
-      for (int c4 = 0; c4 < 16; ++c4) {
-        const f32x4 qv = qh[c4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d = fmaf(qv[e], kv[4 * c4 + e], d);
-      }
-      sc = x.relu ? fmaf(wsh[h], fmaxf(d, 0.f), sc) : d;
-    }
-    key = f32_order_key(sc);
-  }
-  skeys[((int64_t)(b * x.G_sel + g) * x.Nq + r) * slots + i] = key;
-}
-
-// Pilot, stage 2: per row, tau = a score with at least about 1.5 K sampled
-// survivors in proportion (sample count scaled to the row's length): one
-// histogram pass of 4096 bins over the range of the sampled order keys; tau
-// is the lower edge of the bin where the count from the top reaches that
-// number. Any tau is correct (the final stage checks and can fall back);
-// this one only has to leave a little over 1.5 K keys.
-__global__ __launch_bounds__(kTkThreads) void fz_pilot_select_kernel(TopkParams p, const uint32_t* skeys,
-                                                                     int slots, float* tau) {
+// Pilot: one workgroup per selection row. The row's heads score a 1/32
+// sample of its keys (runs of 64 keys every 2048) on MFMA, laid out as in
+// the indexer (32x32x16 bf16: A = the row's heads as slot rows, B = 32 keys,
+// fp8 keys converted to bf16 exactly), so lanes 0..31 each hold every head's
+// product for one key and form its score in-lane. The order keys stay in
+// LDS; tau is the lower edge of the 4096-bin histogram bin (over the range of
+// the sampled keys) where about 1.5 K survivors in proportion are reached
+// (sample count scaled to the row's length). Any tau is correct: the final
+// stage checks it and can fall back; this one only has to leave a little
+// over 1.5 K keys. Requires d_I = 64, bf16 queries, bf16 or fp8 keys.
+constexpr int kPilotTB = 8;       // sampled tiles of 32 keys per wave and load batch
+__global__ __launch_bounds__(kTkThreads) void fz_pilot_kernel(TopkParams p, float* tau) {
   constexpr int T = kTkThreads;
   constexpr int NW = T / 64;
+  __shared__ uint32_t sk[kPilotCap];
   __shared__ uint32_t hist[4096];
   __shared__ uint32_t sc[16];
   __shared__ uint32_t red[2 * NW + 2];
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
   RowCtx c = row_ctx(p, row);
   if (c.n <= p.K) {
     if (tid == 0) tau[row] = INFINITY;   // every key is selected; nothing to filter
     return;
   }
-  const uint32_t* src = skeys + (int64_t)row * slots;
+  const IndexerRow& ir = c.ir;
+  const int nruns = (c.n + kPilotStride - 1) / kPilotStride;
+  const int ntiles = 2 * nruns;                  // two tiles of 32 keys per run
+  const int slots = nruns * kPilotRun;
+  const bool fp8 = ir.kt == DT_FP8;
+  // A operand: slot row col = head col (< H), dims 32 half + 8 s + v
+  bf16x8 A[4];
+  if (col < ir.H) {
+    const uint16_t* qp = (const uint16_t*)ir.q + col * ir.qh_stride + 32 * half;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) A[s4] = *(const bf16x8*)(qp + 8 * s4);
+  } else {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) A[s4] = (bf16x8){};
+  }
+  float wv[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) wv[t] = (ir.relu && t < ir.H) ? ir.w[t * ir.w_stride] : 0.f;
+  const int tbstep = NW * (fp8 ? kPilotTB : kPilotTB / 2);
+  for (int tb = wid; tb < ntiles; tb += tbstep) {
+    // key bytes of this wave's batch: tile tt = tb + NW u covers keys
+    // (tt / 2) * 2048 + 32 (tt % 2) + col, lane half: dims 32 half .. +31
+    u32x4 raw[kPilotTB][4];
+#pragma unroll
+    for (int u = 0; u < kPilotTB; ++u) {
+      const int tt = tb + NW * u;
+      int j = (tt >> 1) * kPilotStride + 32 * (tt & 1) + col;
+      j = j < c.n ? j : c.n - 1;
+      if (tt < ntiles) {
+        if (fp8) {
+          const u32x4* kp = (const u32x4*)((const uint8_t*)ir.k + (int64_t)j * ir.k_stride + 32 * half);
+          raw[u][0] = kp[0];
+          raw[u][1] = kp[1];
+        } else if (u < kPilotTB / 2) {           // bf16 rows are twice as long: half the batch
+          const u32x4* kp = (const u32x4*)((const uint16_t*)ir.k + (int64_t)j * ir.k_stride + 32 * half);
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) raw[u][q4] = kp[q4];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPilotTB; ++u) {
+      const int tt = tb + NW * u;
+      if (tt >= ntiles || (!fp8 && u >= kPilotTB / 2)) continue;
+      u32x4 Bw[4];
+      if (fp8) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const uint32_t w0 = raw[u][s4 >> 1][2 * (s4 & 1)], w1 = raw[u][s4 >> 1][2 * (s4 & 1) + 1];
+          Bw[s4][0] = fp8x2_to_bf16x2<false>(w0);
+          Bw[s4][1] = fp8x2_to_bf16x2<true>(w0);
+          Bw[s4][2] = fp8x2_to_bf16x2<false>(w1);
+          Bw[s4][3] = fp8x2_to_bf16x2<true>(w1);
+        }
+      } else {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) Bw[s4] = raw[u][s4];
+      }
+      f32x16 acc = {};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s4], *(const bf16x8*)&Bw[s4], acc, 0, 0, 0);
+      // lanes of half 0 hold slot rows 0..3 (the heads) of key col
+      float sv = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        sv = ir.relu ? fmaf(wv[t], __int_as_float(max(__float_as_int(acc[t]), 0)), sv) : acc[0];
+      const int j = (tt >> 1) * kPilotStride + 32 * (tt & 1) + col;
+      if (half == 0) sk[32 * tt + col] = j < c.n ? f32_order_key(sv) : 0u;
+    }
+  }
+  __syncthreads();
+  // tau from the sampled keys (0 marks a key after the row's position)
   constexpr int U = kPilotCap / T;
   uint32_t v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int i = tid + u * T;
-    v[u] = i < slots ? src[i] : 0u;
+    v[u] = i < slots ? sk[i] : 0u;
   }
   for (int i = tid; i < 4096; i += T) hist[i] = 0u;
   uint32_t m = 0, kmin = 0xFFFFFFFFu, kmax = 0u;
@@ -1068,11 +1068,12 @@ __global__ __launch_bounds__(kTkThreads) void fz_pilot_select_kernel(TopkParams 
   uint32_t mt = 0;
   kmin = 0xFFFFFFFFu;
   kmax = 0u;
-  for (int w = 0; w < NW; ++w) {
-    mt += sc[w];
-    kmin = min(kmin, red[w]);
-    kmax = max(kmax, red[NW + w]);
+  for (int x = 0; x < NW; ++x) {
+    mt += sc[x];
+    kmin = min(kmin, red[x]);
+    kmax = max(kmax, red[NW + x]);
   }
+  __syncthreads();                                          // sc is reused by the scan below
   const uint64_t want = ((uint64_t)3 * p.K * mt + 2ull * c.n - 1) / (2ull * c.n) + 16;   // ~1.5 K survivors
   const uint32_t R = (uint32_t)min((uint64_t)mt, want);
   if (R == 0) {
@@ -1296,8 +1297,7 @@ bool topk_fused_ok(const TopkParams& p) {
 size_t topk_fused_ws_bytes(const TopkParams& p) {
   const int64_t rows = (int64_t)p.B * p.G * p.Nq;
   const int64_t nchunk = (p.ctx + 511) / 512;
-  const int64_t slots = (int64_t)(p.ctx + kPilotStride - 1) / kPilotStride * kPilotRun;
-  return (size_t)(rows + (int64_t)p.B * nchunk + rows * nchunk * (1 + 2 * kFzCap) + rows * slots) * 4;
+  return (size_t)(rows + (int64_t)p.B * nchunk + rows * nchunk * (1 + 2 * kFzCap)) * 4;
 }
 
 hipError_t launch_topk_fused(const TopkParams& p, hipStream_t st) {
@@ -1309,11 +1309,7 @@ hipError_t launch_topk_fused(const TopkParams& p, hipStream_t st) {
   w.tau = (float*)(w.cand + (int64_t)rows * w.nchunk * w.cap);
   w.kmax = w.tau + rows;
   w.cand_n = (uint32_t*)(w.kmax + (int64_t)p.B * w.nchunk);
-  const int slots = (p.ctx + kPilotStride - 1) / kPilotStride * kPilotRun;
-  uint32_t* skeys = w.cand_n + (int64_t)rows * w.nchunk;
-  hipLaunchKernelGGL(fz_pilot_score_kernel, dim3((slots + kPsThreads - 1) / kPsThreads, p.B, p.G * p.Nq),
-                     dim3(kPsThreads), 0, st, p, skeys, slots);
-  hipLaunchKernelGGL(fz_pilot_select_kernel, dim3(rows), dim3(kTkThreads), 0, st, p, skeys, slots, w.tau);
+  hipLaunchKernelGGL(fz_pilot_kernel, dim3(rows), dim3(kTkThreads), 0, st, p, w.tau);
   IndexerParams ix = p.ix;
   ix.kmax = w.kmax;
   ix.tau = w.tau;

@@ -1232,3 +1232,135 @@ def test_backward_full_size():
         assert np.abs(got_v - want_v).max() <= 1e-4 * max(1.0, float(np.abs(dv[0, kvh]).sum(axis=0).max()))
         got_k = dk[0, kvh].astype(np.float64).sum(axis=0)
         assert np.abs(got_k).max() <= 1e-4 * max(1.0, float(np.abs(dk[0, kvh]).sum(axis=0).max()))
+
+
+# ---------------------------------------------------------------- every row at full size
+def _golden_digests():
+    import importlib.util
+    import json
+    import os
+    here = os.path.join(os.path.dirname(__file__), "golden")
+    spec = importlib.util.spec_from_file_location("make_set_digests", os.path.join(here, "make_set_digests.py"))
+    mk = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mk)
+    with open(os.path.join(here, "set_digests.json")) as f:
+        return mk, json.load(f)
+
+
+def _block_digests(lists, rpb):
+    import hashlib
+    lists = np.ascontiguousarray(lists.astype(np.int32))
+    return [hashlib.sha256(lists[i:i + rpb].tobytes()).hexdigest()[:16] for i in range(0, len(lists), rpb)]
+
+
+def test_prefill_sets_every_row():
+    """Every one of the 65,536 prefill rows: the GPU's index lists hash to the
+    oracle's (digests of 256-row blocks written by tests/golden/
+    make_set_digests.py); a differing block is recomputed row by row with the
+    oracle to name its rows. Then O on a stratified sample of 1024+ rows that
+    includes every row the top-K's redo kernel took."""
+    mk, gold = _golden_digests()
+    g = gold["dsa_prefill"]
+    wl = gen.WORKLOADS["dsa_prefill"]
+    say("[gpu] generating dsa_prefill inputs")
+    inp = gen.generate(wl)
+    assert mk.prefill_sha(inp) == g["input_sha256"], "the fixture was written for other inputs"
+    hp = run(wl, inp)
+    idx = hp.idx[0, 0].cpu().numpy()
+    rpb = gold["rows_per_block"]
+    got = _block_digests(idx, rpb)
+    bad = [i for i, (a, b) in enumerate(zip(got, g["digests"])) if a != b]
+    if bad:
+        mk._setup_prefill()
+        for bi in bad[:2]:
+            for r in range(bi * rpb, min(wl.Nq, (bi + 1) * rpb)):
+                want = mk.padded(mk.prefill_row_set(r), wl.topk)
+                if not np.array_equal(idx[r], want):
+                    say(f"  row {r}: extra {sorted(set(idx[r]) - set(want))[:6]} missing {sorted(set(want) - set(idx[r]))[:6]}")
+    say(f"  {len(got)} blocks of {rpb} rows, {len(bad)} differ")
+    assert not bad
+    # O parity: strata over positions, the redo rows, the needles' rows
+    redo = np.nonzero(hp.ws[:4 * wl.Nq].view(torch.int32).cpu().numpy())[0]
+    rng = np.random.default_rng(17)
+    strata = np.linspace(0, wl.Nq, 65).astype(int)
+    rows = set(int(x) for x in redo)
+    for a, b in zip(strata[:-1], strata[1:]):
+        rows |= set(int(x) for x in rng.integers(a, b, size=16))
+    rows |= {0, 1, 2047, 2048, wl.Nq - 1}
+    rows |= set(int(i) for i in inp["needles"][:16, 1])
+    rows = [(0, r) for r in sorted(rows)]
+    say(f"  O on {len(rows)} rows ({len(redo)} redo rows: {list(redo[:8])})")
+    assert len(rows) >= 1024
+    res = oracle_rows(wl, inp, rows)
+    check_sets(hp, res, rows, wl)
+    check_out(hp, res, rows, 2e-3)
+
+
+def test_block_sparse_sets_every_row():
+    """Every row of two heads of the block-sparse workload (2 x 32,768 rows):
+    block lists hashed against the oracle's, by 256-row blocks."""
+    mk, gold = _golden_digests()
+    g = gold["block_sparse"]
+    wl = gen.WORKLOADS["block_sparse"]
+    say("[gpu] generating block_sparse inputs")
+    inp = gen.generate(wl)
+    assert mk.blocks_sha(inp) == g["input_sha256"], "the fixture was written for other inputs"
+    from fine_grained_top_amd.hotpath import HotPath
+    hp = HotPath(wl, inp)
+    hp.block_select()
+    torch.cuda.synchronize()
+    rpb = gold["rows_per_block"]
+    bad_all = 0
+    for h in g["heads"]:
+        lists = hp.idx[0, h].cpu().numpy()
+        got = _block_digests(lists, rpb)
+        bad = [i for i, (a, b) in enumerate(zip(got, g["digests"][str(h)])) if a != b]
+        if bad:
+            mk._setup_blocks()
+            for bi in bad[:2]:
+                for r in range(bi * rpb, min(wl.Nq, (bi + 1) * rpb)):
+                    want = mk.padded(mk.blocks_row_list(h, r), wl.top_blocks)
+                    if not np.array_equal(lists[r], want):
+                        say(f"  head {h} row {r}: got {list(lists[r])} want {list(want)}")
+        say(f"  head {h}: {len(got)} blocks of {rpb} rows, {len(bad)} differ")
+        bad_all += len(bad)
+    assert bad_all == 0
+
+
+def test_backward_full_size_key_rows():
+    """Key and value gradients element by element at the full window + global
+    backward shapes, for sampled band key rows (only rows j..j+w-1 see such a
+    key) and for global key 0 (every row sees it): the oracle's gradient of
+    each row that sees the key, summed."""
+    import oracle as orc
+    wl = gen.WORKLOADS["window_global_bwd"]
+    say("[gpu] generating window_global_bwd inputs")
+    inp = gen.generate(wl)
+    hp = run(wl, inp)
+    dk, dv = hp.dk.cpu().numpy(), hp.dv.cpu().numpy()
+    q = orc.decode(inp["q"][0], "bf16")
+    k = orc.decode(inp["k"][0], "bf16")
+    v = orc.decode(inp["v"][0], "bf16")
+    dO = np.asarray(inp["d_o"], dtype=np.float32).astype(np.float64)[0]
+    scale = 1.0 / math.sqrt(wl.d)
+    g = wl.Hq // wl.Hkv
+    worst = 0.0
+    rng = np.random.default_rng(23)
+    keys = [0] + [int(x) for x in rng.integers(wl.n_global, wl.N, size=3)] + [wl.N - 1]
+    for kvh in (0, wl.Hkv - 1):
+        for j in keys:
+            rows = range(j, wl.N) if j < wl.n_global else range(j, min(wl.N, j + wl.window))
+            want_k = np.zeros(wl.d)
+            want_v = np.zeros(wl.d)
+            for r in rows:
+                S_ = orc.window_global_set(r, wl.window, wl.n_global)
+                for h in range(kvh * g, (kvh + 1) * g):
+                    _, gk, gv = orc.masked_attention_grads(q[h, r][None], k[kvh, :r + 1], v[kvh, :r + 1], S_,
+                                                           scale, dO[h, r][None])
+                    want_k += gk[j]
+                    want_v += gv[j]
+            ek = float(np.abs(dk[0, kvh, j] - want_k).max()) / max(1.0, float(np.abs(want_k).max()))
+            ev = float(np.abs(dv[0, kvh, j] - want_v).max()) / max(1.0, float(np.abs(want_v).max()))
+            worst = max(worst, ek, ev)
+    say(f"  dk/dv relative max error over key rows {keys}: {worst:.2e}")
+    assert worst <= 1e-4
