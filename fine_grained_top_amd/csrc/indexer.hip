@@ -36,7 +36,10 @@ SP_DEV float load_val(const void* p, int dt, int64_t i) {
 // 32 keys each wave keeps in flight. Each wave walks its CPW * 4 tiles in
 // order, the key bytes of tile t + PD requested as tile t is scored, so the
 // loads of a workgroup stream while it computes (PD = CPW * 4: all at once).
-template <int KT, int NMB, int HPG, bool RELU, int MODE, int CPW, int PD>
+// RL (filter, one selection group): survivors go to per-row lists, staged in
+// LDS per row of the workgroup and written out after every second tile with
+// one global atomic per row that has any.
+template <int KT, int NMB, int HPG, bool RELU, int MODE, int CPW, int PD, bool RL = false>
 __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
   constexpr bool FILTER = MODE == 1;
   constexpr bool PM = MODE == 2;
@@ -94,6 +97,16 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
   }
 
   __shared__ uint32_t lcount[FILTER ? CPW : 1][128];
+  // RL: the survivors of two tiles per wave (256 keys) of each row of the
+  // workgroup fit their row's stage whatever the rate, so the stage is
+  // flushed after every second tile and never overflows
+  constexpr int kRlTiles = 2;
+  constexpr int kRlRows = 128 / HPG;                  // rows of a 128-slot block (one group per row)
+  constexpr int kRlCap = 4 * 32 * kRlTiles;           // keys per row between flushes
+  __shared__ u32x2 stage[RL ? kRlRows * kRlCap : 1];
+  __shared__ uint32_t gbase[RL ? kRlRows : 1];
+  __shared__ uint32_t rstart[RL ? kRlRows + 1 : 1];  // running start of each row's staged entries
+  const int rbase = mbase >> hshift;                  // RL: first row of the workgroup
   __shared__ float wsl[128];
   __shared__ float tsl[128];          // filter threshold of each slot's selection row
   __shared__ uint32_t pml[PM ? 128 * 16 : 1];   // page keys: [slot][page of the chunk]
@@ -201,7 +214,21 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
         }
         scv[gi] = sc;
       }
-      if constexpr (!FILTER) {
+      if constexpr (RL) {
+        // one selection group: the group of a slot is its row; each surviving
+        // lane takes its stage slot with one LDS atomic
+#pragma unroll
+        for (int gi = 0; gi < G4; ++gi) {
+          const int v0 = gi * HPG;
+          const int m0 = mbase + 32 * mb + 8 * (v0 >> 2) + 4 * half + (v0 & 3);
+          const int r = m0 >> hshift;
+          if (m0 < M && j <= L - p.Nq + r && scv[gi] >= tsl[(m0 - mbase) & 127]) {
+            const int rr = r - rbase;
+            const uint32_t slot = atomicAdd(&lcount[0][rr], 1u);
+            stage[rr * kRlCap + slot] = u32x2{f32_order_key(scv[gi]), (uint32_t)j};
+          }
+        }
+      } else if constexpr (!FILTER) {
 #pragma unroll
         for (int gi = 0; gi < G4; ++gi) {
           const int v0 = gi * HPG;
@@ -265,6 +292,45 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
         }
       }
     }
+    if constexpr (RL) {
+      if ((t + 1) % kRlTiles == 0 || t + 1 == NT) {
+        // the stage to the rows' lists: one reservation per row
+        // (wave 0: the rows' counts, their running total and the list offsets)
+        __syncthreads();
+        if (threadIdx.x < 64) {
+          const int rr = threadIdx.x;
+          const uint32_t n = (rr < kRlRows && rbase + rr < p.Nq) ? lcount[0][rr] : 0u;
+          const uint32_t incl = wave_prefix_incl_u32(n);
+          if (rr < kRlRows) {
+            gbase[rr] = n ? atomicAdd(&p.cand_n[(int64_t)b * p.Nq + rbase + rr], n) : 0u;
+            rstart[rr] = incl - n;
+          }
+          if (rr == 63) rstart[kRlRows] = incl;
+        }
+        __syncthreads();
+        // entry x of the staged entries belongs to the row whose running
+        // start is the largest <= x
+        const uint32_t ntot = rstart[kRlRows];
+        for (uint32_t x = threadIdx.x; x < ntot; x += 256) {
+          int lo = 0;
+#pragma unroll
+          for (int step = kRlRows / 2; step >= 1; step >>= 1)
+            if (rstart[lo + step] <= x) lo += step;
+          const uint32_t e = x - rstart[lo];
+          const uint32_t gs = gbase[lo] + e;
+          const int64_t rowg = (int64_t)b * p.Nq + rbase + lo;
+          if (gs < (uint32_t)p.cap) {
+            const u32x2 v = stage[lo * kRlCap + e];
+            p.cand[rowg * p.cap + gs] = v[0];
+            p.cand_j[rowg * p.cap + gs] = v[1];
+          }
+        }
+        __syncthreads();
+        for (int rr = threadIdx.x; rr < kRlRows; rr += 256) lcount[0][rr] = 0u;
+        __syncthreads();
+      }
+    }
+
   }
 
   // largest |k| element of each chunk (valid keys only)
@@ -295,7 +361,7 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
       if (page < p.pk_stride) p.pkeys[row * p.pk_stride + page] = pml[sl * 16 + pl];
     }
   }
-  if (FILTER) {
+  if (FILTER && !RL) {
     const int nrows = p.G_sel * p.Nq;
 #pragma unroll
     for (int cc = 0; cc < CPW; ++cc) {
@@ -404,6 +470,13 @@ static void launch_mfma(const IndexerParams& p, hipStream_t st) {
   constexpr int PD = STREAM ? 3 : kMfmaChunk / 32 / 4;
   const int nchunk = (p.ctx + kMfmaChunk - 1) / kMfmaChunk;
   dim3 grid((nchunk + CPW - 1) / CPW, p.B, (p.Nq * p.H_I + 127) / 128);
+  if constexpr (MODE == 1 && NMB == 4 && HPG == 4 && RELU) {
+    if (p.cand_j) {      // per-row lists (many rows)
+      hipLaunchKernelGGL((idx_mfma64_kernel<KT, NMB, HPG, RELU, MODE, 1, kMfmaChunk / 32 / 4, true>),
+                         dim3(nchunk, p.B, (p.Nq * p.H_I + 127) / 128), dim3(256), 0, st, p);
+      return;
+    }
+  }
   hipLaunchKernelGGL((idx_mfma64_kernel<KT, NMB, HPG, RELU, MODE, CPW, PD>), grid, dim3(256), 0, st, p);
 }
 
@@ -463,6 +536,11 @@ hipError_t launch_index_scores(const IndexerParams& p0, hipStream_t st) {
 }
 
 bool index_filter_ok(const IndexerParams& p) { return mfma_ok(p) && p.Nq * p.H_I <= 128; }
+
+// per-row survivor lists: one selection group of four weighted-ReLU heads
+bool index_filter_rows_ok(const IndexerParams& p) {
+  return mfma_ok(p) && p.G_sel == 1 && p.H_I == 4 && p.hpg == 4 && p.relu && p.Nq * p.H_I > 128;
+}
 
 hipError_t launch_index_filter(const IndexerParams& p0, hipStream_t st) {
   IndexerParams p = p0;

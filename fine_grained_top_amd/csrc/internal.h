@@ -31,6 +31,10 @@ struct IndexerParams {
   uint32_t* cand;          // [B][nchunk][G_sel * Nq][cap][2]: (order key, key position), 8-byte aligned
   uint32_t* cand_n;        // [B][nchunk][G_sel * Nq] number found (may exceed cap)
   int cap;
+  // per-row lists instead (many rows, one selection group): order keys
+  // cand[row][cap], positions cand_j[row][cap], counts cand_n[row] (zeroed
+  // before the call; a count may exceed cap, the excess is dropped)
+  uint32_t* cand_j;
   // page keys (MFMA path only): the largest score of each (selection row, page)
   // as an order key, [B * G_sel * Nq][pk_stride], pages of 1 << pk_lgP keys
   uint32_t* pkeys;
@@ -40,6 +44,7 @@ struct IndexerParams {
 bool index_pagekeys_ok(const IndexerParams& p, int lgP);   // pages of 32..512 keys
 int index_chunk(const IndexerParams& p);   // keys per chunk of the chunk maxima (kmax)
 bool index_filter_ok(const IndexerParams& p);
+bool index_filter_rows_ok(const IndexerParams& p);   // per-row lists (cand_j given)
 hipError_t launch_index_filter(const IndexerParams& p, hipStream_t st);   // chunk = 512
 size_t indexer_ws_bytes(int B, int G_k, int ctx);
 hipError_t launch_index_scores(const IndexerParams& p, hipStream_t st);

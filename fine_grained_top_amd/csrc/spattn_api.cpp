@@ -269,8 +269,9 @@ static int topk_setup(const spattn_tensor* scores, const float* err, const spatt
   p.ctx_len = ctx_len;
   if ((flags & SPATTN_TOPK_FUSED_INDEX) && !sp::topk_fused_ok(p))
     return fail(SPATTN_ERR_UNSUPPORTED,
-                "fused selection needs d_I = 64, bf16 q_idx, bf16/fp8 k_idx shared by all groups, "
-                "<= 4 heads per group, Nq * H_I <= 128 (power-of-two H_I) and ctx <= 262144");
+                "fused selection needs d_I = 64, bf16 q_idx, bf16/fp8 k_idx shared by all groups and either "
+                "<= 4 heads per group, Nq * H_I <= 128 (power-of-two H_I), ctx <= 262144, or one group of "
+                "4 weighted-ReLU heads with ctx <= 65536");
   return SPATTN_OK;
 }
 

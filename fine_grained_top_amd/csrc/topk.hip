@@ -942,6 +942,28 @@ SP_DEV float recompute_score(const IndexerRow& r, int64_t j) {
   return s;
 }
 
+// The same float32 score with the row's queries and weights already in LDS
+// (qs [H][d], wsg [H]) and the key read four elements per load.
+SP_DEV float recompute_score_lds(const IndexerRow& r, const float* qs, const float* wsg, int64_t j) {
+  const int64_t koff = j * r.k_stride;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < r.d; c += 4) {
+    double kv[4];
+    load_run_f64<4>(r.k, r.kt, koff + c, r.d - c, kv);
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      if (h < r.H)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c + e < r.d) acc[h] = fmaf(qs[h * r.d + c + e], (float)kv[e], acc[h]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+    if (h < r.H) s = r.relu ? fmaf(wsg[h], fmaxf(acc[h], 0.f), s) : acc[h];
+  return s;
+}
+
 // Pilot: one workgroup per selection row. The row's heads score a 1/32
 // sample of its keys (runs of 64 keys every 2048) on MFMA, laid out as in
 // the indexer (32x32x16 bf16: A = the row's heads as slot rows, B = 32 keys,
@@ -1287,20 +1309,373 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
 
 static constexpr int kFzCap = 512;   // = keys per indexer chunk: a chunk can never overflow
 
-bool topk_fused_ok(const TopkParams& p) {
+// Zero-fill of counters by a kernel (a memset node would not be safe under
+// graph capture).
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* x, int n, uint32_t v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) x[i] = v;
+}
+
+// ---------------------------------------------------------------- fused, many rows (prefill)
+// One selection group of four weighted-ReLU heads, contexts up to 65536.
+// (1) fzr_pilot: a workgroup takes 8 consecutive rows (their 4 heads are the
+//     32 slot rows of the 32x32x16 MFMA) and scores the sampled keys (runs of
+//     64 every 2048, the decode pilot's sample) for all of them; per row, a
+//     wave finds the R-th largest sampled key (R for about 1.25 K survivors in
+//     proportion, plus a margin) by three 8-bit radix passes over a per-wave
+//     histogram, and tau is the lower edge of its 24-bit bin; a row short
+//     enough for its list keeps every key (tau = -inf).
+// (2) the filtered indexer appends survivors (order key, position) to
+//     per-row lists (kFzrCap per row).
+// (3) fzr_final: one 256-thread workgroup per row: the list into LDS, then the
+//     certified selection over it (radix select, band, exact band keys,
+//     bitmap); rows it cannot settle (too few or too many survivors, a band
+//     reaching below tau, a band key that needs the wide accumulator) are
+//     flagged, and fzr_redo recomputes them from the inputs.
+constexpr int kFzrRows = 8;        // pilot rows per workgroup (4 heads each)
+constexpr int kFzrSamples = 2048;  // sampled keys per row (contexts up to 65536)
+constexpr int kFzrCap = 6144;      // survivors kept per row
+constexpr int kFzrCtx = 65536;
+
+__global__ __launch_bounds__(256) void fzr_pilot_kernel(TopkParams p, float* tau) {
+  __shared__ uint32_t sk[kFzrRows][kFzrSamples];
+  __shared__ uint32_t hist[4][256];
+  const IndexerParams& x = p.ix;
+  const int b = blockIdx.y, r0 = blockIdx.x * kFzrRows;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int L = min(p.ctx_len ? p.ctx_len[b] : p.ctx, p.ctx);
+  const int pos0 = L - p.Nq + r0;                             // position of the first row
+  const int rlast = min(p.Nq - 1, r0 + kFzrRows - 1);
+  const int nmax = min(L - p.Nq + rlast + 1, kFzrCtx);        // keys seen by the last row
+  const int nruns = nmax > 0 ? (nmax + kPilotStride - 1) / kPilotStride : 0;
+  const int ntiles = 2 * nruns;
+  const bool fp8 = x.k.dt == DT_FP8;
+  // A operand: slot col = 4 (row) + head, dims 32 half + 8 s + v
+  bf16x8 A[4];
+  {
+    const int rr = col >> 2, h = col & 3;
+    if (r0 + rr < p.Nq) {
+      const uint16_t* qp =
+          (const uint16_t*)x.q.p + b * x.q.s[0] + (int64_t)(r0 + rr) * x.q.s[1] + h * x.q.s[2] + 32 * half;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) A[s4] = *(const bf16x8*)(qp + 8 * s4);
+    } else {
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) A[s4] = (bf16x8){};
+    }
+  }
+  // lane (key col, half): accumulator v holds slot 8 (v / 4) + 4 half + v % 4,
+  // i.e. row 2 (v / 4) + half, head v % 4
+  float wv[4][4];
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = min(r0 + 2 * gi + half, p.Nq - 1);
+      wv[gi][t] = x.w[b * x.ws_[0] + (int64_t)r * x.ws_[1] + t * x.ws_[2]];
+    }
+  for (int i = tid; i < kFzrRows * kFzrSamples; i += 256) sk[i / kFzrSamples][i % kFzrSamples] = 0u;
+  __syncthreads();
+  constexpr int TB = 4;
+  for (int tb = wid; tb < ntiles; tb += 4 * TB) {
+    u32x4 raw[TB][4];
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      const int tt = tb + 4 * u;
+      int j = (tt >> 1) * kPilotStride + 32 * (tt & 1) + col;
+      j = j < nmax ? j : nmax - 1;
+      if (tt < ntiles) {
+        if (fp8) {
+          const uint8_t* kp = (const uint8_t*)x.k.p + b * x.k.s[0] + (int64_t)j * x.k.s[1] + 32 * half;
+          raw[u][0] = *(const u32x4*)kp;
+          raw[u][1] = *(const u32x4*)(kp + 16);
+        } else {
+          const uint16_t* kp = (const uint16_t*)x.k.p + b * x.k.s[0] + (int64_t)j * x.k.s[1] + 32 * half;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) raw[u][q4] = *(const u32x4*)(kp + 8 * q4);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      const int tt = tb + 4 * u;
+      if (tt >= ntiles) break;
+      u32x4 Bw[4];
+      if (fp8) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const uint32_t w0 = raw[u][s4 >> 1][2 * (s4 & 1)], w1 = raw[u][s4 >> 1][2 * (s4 & 1) + 1];
+          Bw[s4][0] = fp8x2_to_bf16x2<false>(w0);
+          Bw[s4][1] = fp8x2_to_bf16x2<true>(w0);
+          Bw[s4][2] = fp8x2_to_bf16x2<false>(w1);
+          Bw[s4][3] = fp8x2_to_bf16x2<true>(w1);
+        }
+      } else {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) Bw[s4] = raw[u][s4];
+      }
+      f32x16 acc = {};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s4], *(const bf16x8*)&Bw[s4], acc, 0, 0, 0);
+      const int j = (tt >> 1) * kPilotStride + 32 * (tt & 1) + col;
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        float sv = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sv = fmaf(wv[gi][t], __int_as_float(max(__float_as_int(acc[4 * gi + t]), 0)), sv);
+        const int rr = 2 * gi + half;
+        if (j <= pos0 + rr) sk[rr][32 * tt + col] = f32_order_key(sv);
+      }
+    }
+  }
+  __syncthreads();
+  // per row (wave w: rows 2w, 2w + 1): the R-th largest sampled key
+  for (int rr = 2 * wid; rr < 2 * wid + 2; ++rr) {
+    const int r = r0 + rr;
+    if (r >= p.Nq) break;
+    const int n = min(pos0 + rr + 1, kFzrCtx);
+    if (n <= p.K) {
+      if (lane == 0) tau[(int64_t)b * p.Nq + r] = INFINITY;
+      continue;
+    }
+    if (n <= kFzrCap) {          // the whole row fits the list: keep every key
+      if (lane == 0) tau[(int64_t)b * p.Nq + r] = -INFINITY;
+      continue;
+    }
+    const int slots = 2 * 32 * ((n + kPilotStride - 1) / kPilotStride);
+    uint32_t m = 0;
+    for (int i = lane; i < slots; i += 64) m += sk[rr][i] != 0u;
+    m = (uint32_t)__builtin_amdgcn_readlane((int)wave_prefix_incl_u32(m), 63);
+    const uint64_t want = ((uint64_t)5 * p.K * m + 4ull * n - 1) / (4ull * n) + 16;  // ~1.25 K survivors
+    uint32_t need = (uint32_t)min((uint64_t)m, want);
+    if (need == 0) {
+      if (lane == 0) tau[(int64_t)b * p.Nq + r] = -INFINITY;
+      continue;
+    }
+    uint32_t prefix = 0;
+    for (int pass = 0; pass < 3; ++pass) {
+      const int sh = 24 - 8 * pass;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hist[wid][4 * lane + q] = 0u;
+      __builtin_amdgcn_wave_barrier();
+      for (int i = lane; i < slots; i += 64) {
+        const uint32_t v = sk[rr][i];
+        if (v != 0u && (pass == 0 || (v >> (sh + 8)) == prefix)) atomicAdd(&hist[wid][(v >> sh) & 255u], 1u);
+      }
+      __builtin_amdgcn_wave_barrier();
+      uint32_t hb[4], cnt = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        hb[q] = hist[wid][4 * lane + q];
+        cnt += hb[q];
+      }
+      const uint32_t incl = wave_prefix_incl_u32(cnt);
+      const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+      const uint32_t above = total - incl;                  // members in higher lanes' bins
+      uint32_t digit = 0, ab = 0;
+      const bool mine = above < need && need <= above + cnt;
+      if (mine) {
+        uint32_t acc = above;
+        for (int q = 3; q >= 0; --q) {
+          if (acc + hb[q] >= need) {
+            digit = 4 * lane + q;
+            ab = acc;
+            break;
+          }
+          acc += hb[q];
+        }
+      }
+      const uint64_t bm = ballot(mine);
+      const int src = bm ? __builtin_ctzll(bm) : 0;
+      digit = (uint32_t)__builtin_amdgcn_readlane((int)digit, src);
+      ab = (uint32_t)__builtin_amdgcn_readlane((int)ab, src);
+      prefix = (prefix << 8) | digit;
+      need -= ab;
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (lane == 0) tau[(int64_t)b * p.Nq + r] = order_key_f32(prefix << 8);
+  }
+}
+
+struct FzrWs {
+  float* tau;          // [rows]
+  float* kmax;         // [B][nchunk]
+  uint32_t* cnt;       // [rows]
+  uint32_t* ck;        // [rows][kFzrCap] order keys
+  uint32_t* cj;        // [rows][kFzrCap] positions
+  uint32_t* redo;      // [rows]
+  int nchunk;
+};
+
+struct FzrSmem {
+  RowSmemC row;
+  float qs[4 * 64];
+  float wsg[4];
+  uint32_t ck[kFzrCap];
+  uint32_t cj[kFzrCap];
+  uint32_t bm[kFzrCtx / 32];
+  float red[2 * (kR2Threads / 64)];
+};
+
+__global__ __launch_bounds__(kR2Threads) void fzr_final_kernel(TopkParams p, FzrWs w) {
+  constexpr int T = kR2Threads;
+  constexpr int NW = T / 64;
+  __shared__ FzrSmem sm;
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  RowCtx c = row_ctx(p, row);
+  if (c.n <= p.K) {
+    write_all(p, c, T);
+    if (tid == 0) w.redo[row] = 0u;
+    return;
+  }
+  const uint32_t n_cand = w.cnt[row];
+  const float tau = w.tau[row];
+  const int L = min(p.ctx_len ? p.ctx_len[c.b] : p.ctx, p.ctx);
+  const int nch_k = min(w.nchunk, (L + 511) / 512);
+  float km = 0.f, coef = 0.f;
+  for (int i = tid; i < nch_k; i += T) km = fmaxf(km, w.kmax[(int64_t)c.b * w.nchunk + i]);
+  for (int e = tid; e < c.ir.H * c.ir.d; e += T) {
+    const int hh = e / c.ir.d;
+    const float qv = (float)load_f64(c.ir.q, c.ir.qt, hh * c.ir.qh_stride + e % c.ir.d);
+    sm.qs[e] = qv;
+    coef = fmaf(fabsf(c.ir.w[hh * c.ir.w_stride]), fabsf(qv), coef);
+  }
+  if (tid < c.ir.H) sm.wsg[tid] = c.ir.w[tid * c.ir.w_stride];
+  const bool fits = n_cand >= (uint32_t)p.K && n_cand <= (uint32_t)kFzrCap;
+  uint32_t kmx = 0;
+  if (fits) {
+    const uint32_t* gk = w.ck + (int64_t)row * kFzrCap;
+    const uint32_t* gj = w.cj + (int64_t)row * kFzrCap;
+    for (uint32_t i = tid; i < n_cand; i += T) {
+      const uint32_t k = gk[i];
+      sm.ck[i] = k;
+      sm.cj[i] = gj[i];
+      kmx = max(kmx, k);
+    }
+  }
+  km = wave_max_dpp(km);
+  coef = wave_sum_dpp(coef);
+  kmx = wave_max_u32_dpp(kmx);
+  if (lane == 63) {
+    sm.red[wid] = km;
+    sm.red[NW + wid] = coef;
+    sm.row.sc[wid] = kmx;
+  }
+  const int nwords = (c.n + 31) >> 5;
+  for (int i = tid; i < nwords; i += T) sm.bm[i] = 0u;
+  __syncthreads();
+  float KM = 0.f, CO = 0.f;
+  uint32_t KX = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    KM = fmaxf(KM, sm.red[v]);
+    CO += sm.red[NW + v];
+    KX = max(KX, sm.row.sc[v]);
+  }
+  c.eps = eps_of(p.ix, CO, KM);
+  __syncthreads();
+  bool ok = fits;
+  if (ok) {
+    // the certification band around the K-th largest key must lie above tau:
+    // a K-th key below tau + 2 E (rounded up) fails the row
+    const float E = 2.0f * c.eps * 1.0001f + 1e-30f;
+    const uint32_t base = f32_order_key(tau);
+    const uint32_t tlo = f32_order_key(nextafterf(nextafterf(tau + 2.0f * E, INFINITY), INFINITY));
+    ok = resolve_candidates<T, RowSmemC, 4, true>(p, c, sm.row, sm.ck, sm.cj, sm.bm, n_cand, (uint32_t)p.K, base,
+                                                 max(KX, base), tlo, 0xFFFFFFFFu, sm.qs, sm.wsg);
+  }
+  if (ok) emit_bitmap<T, kFzrCtx / 32>(p, c, sm.row, sm.bm, nwords);
+  if (tid == 0) w.redo[row] = ok ? 0u : 1u;
+}
+
+// Rows flagged by fzr_final: recomputed from the indexer inputs by the
+// ordered single-pass routine (every score formed again by one thread). Every
+// workgroup scans all flags in row order; the k-th flagged row goes to
+// workgroup k mod gridDim.x, so flagged rows spread over the grid.
+__global__ __launch_bounds__(kR2Threads) void fzr_redo_kernel(TopkParams p, const uint32_t* redo, int rows) {
+  __shared__ RowSmem sm;
+  __shared__ uint32_t list[kR2Threads];
+  __shared__ uint32_t nlist;
+  __shared__ float qs[4 * 64];
+  __shared__ float wsg[4];
+  uint32_t seen = 0;                       // flagged rows before this block of rows
+  for (int r0 = 0; r0 < rows; r0 += kR2Threads) {
+    if (threadIdx.x == 0) nlist = 0u;
+    const int row = r0 + (int)threadIdx.x;
+    const bool f = row < rows && redo[row] != 0u;
+    uint32_t tot;
+    const uint32_t k = seen + block_prefix<kR2Threads>(f, sm.sc, tot);
+    if (f && k % gridDim.x == blockIdx.x) list[atomicAdd(&nlist, 1u)] = (uint32_t)row;
+    seen += tot;
+    __syncthreads();
+    const uint32_t nl = nlist;
+    for (uint32_t q = 0; q < nl; ++q) {
+      RowCtx c = row_ctx(p, (int)list[q]);
+      for (int e = threadIdx.x; e < c.ir.H * c.ir.d; e += kR2Threads)
+        qs[e] = (float)load_f64(c.ir.q, c.ir.qt, (e / c.ir.d) * c.ir.qh_stride + e % c.ir.d);
+      if ((int)threadIdx.x < c.ir.H) wsg[threadIdx.x] = c.ir.relu ? c.ir.w[threadIdx.x * c.ir.w_stride] : 1.f;
+      __syncthreads();
+      row_topk_single<kR2Threads>(p, c, sm, [&](int i) { return recompute_score_lds(c.ir, qs, wsg, i); });
+      if (p.count && threadIdx.x == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = p.K;
+      __syncthreads();
+    }
+  }
+}
+
+static bool fused_rows_ok(const TopkParams& p) {
+  return p.certified && index_filter_rows_ok(p.ix) && p.ctx <= kFzrCtx && p.G == 1;
+}
+
+
+static bool fused_few_ok(const TopkParams& p) {
   const int64_t nchunk = (p.ctx + 511) / 512;
   return index_filter_ok(p.ix) && p.ctx <= kPilotCap / kPilotRun * kPilotStride &&
          (p.ctx + 31) / 32 <= kMaxWords && nchunk <= kTkThreads &&
          nchunk * p.G * p.Nq * kFzCap < ((int64_t)1 << 31);   // 32-bit candidate offsets per request
 }
 
+bool topk_fused_ok(const TopkParams& p) { return fused_few_ok(p) || fused_rows_ok(p); }
+
 size_t topk_fused_ws_bytes(const TopkParams& p) {
   const int64_t rows = (int64_t)p.B * p.G * p.Nq;
   const int64_t nchunk = (p.ctx + 511) / 512;
+  if (!fused_few_ok(p))    // per-row lists: keys and positions, counts, tau, chunk bounds, redo flags
+    return (size_t)(rows * 2 * kFzrCap + rows * 3 + (int64_t)p.B * nchunk) * 4;
   return (size_t)(rows + (int64_t)p.B * nchunk + rows * nchunk * (1 + 2 * kFzCap)) * 4;
 }
 
+static hipError_t launch_topk_fused_rows(const TopkParams& p, hipStream_t st) {
+  const int rows = p.B * p.G * p.Nq;
+  FzrWs w;
+  w.nchunk = (p.ctx + 511) / 512;
+  w.ck = (uint32_t*)p.ws;
+  w.cj = w.ck + (int64_t)rows * kFzrCap;
+  w.cnt = w.cj + (int64_t)rows * kFzrCap;
+  w.redo = w.cnt + rows;
+  w.tau = (float*)(w.redo + rows);
+  w.kmax = w.tau + rows;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, w.cnt, rows, 0u);
+  hipLaunchKernelGGL(fzr_pilot_kernel, dim3((p.Nq + kFzrRows - 1) / kFzrRows, p.B), dim3(256), 0, st, p, w.tau);
+  IndexerParams ix = p.ix;
+  ix.kmax = w.kmax;
+  ix.tau = w.tau;
+  ix.cand = w.ck;
+  ix.cand_j = w.cj;
+  ix.cand_n = w.cnt;
+  ix.cap = kFzrCap;
+  ix.err = nullptr;
+  hipError_t e = launch_index_filter(ix, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fzr_final_kernel, dim3(rows), dim3(kR2Threads), 0, st, p, w);
+  hipLaunchKernelGGL(fzr_redo_kernel, dim3(min((rows + kR2Threads - 1) / kR2Threads, kRedoGrid)), dim3(kR2Threads),
+                     0, st, p, w.redo, rows);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk_fused(const TopkParams& p, hipStream_t st) {
+  if (!fused_few_ok(p)) return launch_topk_fused_rows(p, st);
   const int rows = p.B * p.G * p.Nq;
   FzWs w;
   w.nchunk = (p.ctx + 511) / 512;

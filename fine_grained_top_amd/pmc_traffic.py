@@ -23,11 +23,12 @@ import sqlite3
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 # kernels of each stage, by name fragment; the plain, filtering and page-key
-# indexer are one template whose last argument (0, 1, 2) tells them apart
+# indexer are one template whose fifth argument (0, 1, 2) tells them apart
+# (followed by the chunks per workgroup and the tiles in flight per wave)
 STAGES = {
-    "index_topk_fused": ["fz_pilot_score", "fz_pilot_select", "1>(sp::IndexerParams)", "fz_final"],
-    "index_scores": ["0>(sp::IndexerParams)", "idx_generic", "idx_err"],
-    "index_page_fused": ["2>(sp::IndexerParams)", "idx_err", "page_keys", "page_select"],
+    "index_topk_fused": ["fz_pilot", "1, 2, 3>(sp::IndexerParams)", "1, 1, 4>(sp::IndexerParams)", "fz_final"],
+    "index_scores": ["0, 1, 4>(sp::IndexerParams)", "idx_generic", "idx_err"],
+    "index_page_fused": ["2, 1, 4>(sp::IndexerParams)", "idx_err", "page_keys", "page_select"],
     "topk": ["topk_row", "topk_redo", "mt_zero", "mt_hist", "mt_collect", "mt_finalize"],
     "page_select": ["page_keys_kernel", "page_select_kernel"],
     "two_level_select": ["two_level_kernel"],

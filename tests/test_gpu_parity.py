@@ -398,7 +398,7 @@ def run_fused(wl, inp):
     return hp
 
 
-@pytest.mark.parametrize("name", ["dsa_decode_small", "dsa_decode"])
+@pytest.mark.parametrize("name", ["dsa_decode_small", "dsa_decode", "dsa_prefill_small"])
 def test_fused_index_topk(name):
     wl = gen.WORKLOADS[name]
     inp = gen.generate(wl)
@@ -1253,7 +1253,8 @@ def _block_digests(lists, rpb):
     return [hashlib.sha256(lists[i:i + rpb].tobytes()).hexdigest()[:16] for i in range(0, len(lists), rpb)]
 
 
-def test_prefill_sets_every_row():
+@pytest.mark.parametrize("fused", [False, True])
+def test_prefill_sets_every_row(fused):
     """Every one of the 65,536 prefill rows: the GPU's index lists hash to the
     oracle's (digests of 256-row blocks written by tests/golden/
     make_set_digests.py); a differing block is recomputed row by row with the
@@ -1265,7 +1266,8 @@ def test_prefill_sets_every_row():
     say("[gpu] generating dsa_prefill inputs")
     inp = gen.generate(wl)
     assert mk.prefill_sha(inp) == g["input_sha256"], "the fixture was written for other inputs"
-    hp = run(wl, inp)
+    hp = run_fused(wl, inp) if fused else run(wl, inp)
+    assert hp.fused == fused
     idx = hp.idx[0, 0].cpu().numpy()
     rpb = gold["rows_per_block"]
     got = _block_digests(idx, rpb)
@@ -1280,7 +1282,19 @@ def test_prefill_sets_every_row():
     say(f"  {len(got)} blocks of {rpb} rows, {len(bad)} differ")
     assert not bad
     # O parity: strata over positions, the redo rows, the needles' rows
-    redo = np.nonzero(hp.ws[:4 * wl.Nq].view(torch.int32).cpu().numpy())[0]
+    if fused:
+        # the finalize kernel's redo flags follow the survivor lists (order
+        # keys and positions, cap per row) and the counts in the workspace;
+        # the cap follows from the workspace size: 4 (2 cap rows + 3 rows + chunks)
+        sp = S()
+        need = sp.LIB.spattn_topk_workspace(None, sp.ctypes.byref(hp.ix), wl.topk, sp.TOPK_FUSED_INDEX)
+        nchunk = (wl.N + 511) // 512
+        cap = (need // 4 - 3 * wl.Nq - nchunk) // (2 * wl.Nq)
+        off = 4 * (2 * cap * wl.Nq + wl.Nq)
+        redo = np.nonzero(hp.ws[off:off + 4 * wl.Nq].view(torch.int32).cpu().numpy())[0]
+        say(f"  survivor lists of {cap} per row")
+    else:
+        redo = np.nonzero(hp.ws[:4 * wl.Nq].view(torch.int32).cpu().numpy())[0]
     rng = np.random.default_rng(17)
     strata = np.linspace(0, wl.Nq, 65).astype(int)
     rows = set(int(x) for x in redo)
@@ -1364,3 +1378,21 @@ def test_backward_full_size_key_rows():
             worst = max(worst, ek, ev)
     say(f"  dk/dv relative max error over key rows {keys}: {worst:.2e}")
     assert worst <= 1e-4
+
+
+def test_fused_rows_fall_back_when_the_sample_misleads():
+    """Prefill-shaped fused selection with the pilot's sampled keys zeroed:
+    every sampled score is 0, so tau does not filter; rows with more keys than
+    the survivor lists hold take the redo kernel, shorter rows the lists. The
+    result must still be exact on every row."""
+    wl = dataclasses.replace(gen.WORKLOADS["dsa_prefill_small"], N=6000, Nq=6000, topk=256, needles=0)
+    inp = gen.generate(wl)
+    codes = inp["k_idx"]
+    pos = np.arange(wl.N)
+    codes[:, (pos % 2048) < 64, 0, :] = 0
+    hp = run_fused(wl, inp)
+    assert hp.fused
+    rows = [(0, r) for r in list(range(0, 300, 7)) + list(range(300, wl.N, 97)) + [wl.N - 1]]
+    res = oracle_rows(wl, inp, rows)
+    check_sets(hp, res, rows, wl)
+    check_out(hp, res, rows, 2e-3)
