@@ -9,17 +9,24 @@
 // softmax statistics (the decomposition MoBA uses: attention over a union of
 // disjoint key sets is the log-sum-exp merge of the parts).
 //
+// Block lists belong to selection groups (one per query head, or one per
+// GQA group whose query heads share a KV head and a list, as MSA's index
+// branch picks blocks per group); the bookkeeping runs per (request, group)
+// and a work item serves every query head of its group, so a chosen key
+// block is staged once for the group (KV-outer, queries gathered):
+//
 //   count   per 256-row chunk: which (row, slot) entries contribute (valid,
 //           not a repeat of an earlier slot, some key before the row's window
 //           and not after the row), a per-block histogram and each entry's
 //           rank within its chunk's bin
-//   scan    per (request, head): per-chunk offsets of every block's list,
-//           list bases, 64-row work items per block and their prefix
-//   table   the flat list of work items (request-head, block, 64-row chunk)
+//   scan    per (request, group): per-chunk offsets of every block's list,
+//           list bases, work items per block and their prefix
+//   table   the flat list of work items (request-group, block, row chunk)
 //   scatter each contributing (row, slot) into its block's row list
 //   attn    one workgroup per work item: the block's keys staged in LDS, the
-//           item's rows gathered, S^T = K Q^T and O += P V on MFMA, partial
-//           (m, l, O) per (row, slot)
+//           item's 64 / hpg rows of each of the group's hpg query heads
+//           gathered as the 64 MFMA rows, S^T = K Q^T and O += P V on MFMA,
+//           partial (m, l, O) per (row, head, slot)
 //   window  the tiled kernel in window mode (O and LSE of the window part)
 //   combine per row: merge the window part with the block partials
 //
@@ -40,24 +47,26 @@ constexpr float kBcLog2e = 1.4426950408889634f;
 constexpr float kBcLn2 = 0.6931471805599453f;
 
 struct BcWs {
-  int32_t* rank;      // [B*Hq][Nq][nb]: rank within the chunk's bin, -1 = no contribution
-  int32_t* hist;      // [B*Hq][nch][nbk]: chunk counts, then exclusive offsets over chunks
-  int32_t* tot;       // [B*Hq][nbk]: rows per block
-  int32_t* lbase;     // [B*Hq][nbk]: list base of each block
-  int32_t* ioff;      // [B*Hq][nbk]: first work item of each block within its (request, head)
-  int32_t* icnt;      // [B*Hq]: work items per (request, head)
+  int32_t* rank;      // [B*G][Nq][nb]: rank within the chunk's bin, -1 = no contribution
+  int32_t* hist;      // [B*G][nch][nbk]: chunk counts, then exclusive offsets over chunks
+  int32_t* tot;       // [B*G][nbk]: rows per block
+  int32_t* lbase;     // [B*G][nbk]: list base of each block
+  int32_t* ioff;      // [B*G][nbk]: first work item of each block within its (request, group)
+  int32_t* icnt;      // [B*G]: work items per (request, group)
   int32_t* nitems;    // [1]: total work items
-  uint32_t* item_bk;  // [maxitems]: (request, head) * nbk + block
-  uint32_t* item_c;   // [maxitems]: 64-row chunk of the block's list
-  uint32_t* list;     // [B*Hq][Nq*nb]: row | slot << 24
+  uint32_t* item_bk;  // [maxitems]: (request, group) * nbk + block
+  uint32_t* item_c;   // [maxitems]: row chunk of the block's list
+  uint32_t* list;     // [B*G][Nq*nb]: row | slot << 24
   float* part;        // [B*Hq][Nq][nb][130]: O (128), m, l
   float* lse_w;       // [B*Hq][Nq]: LSE of the window part
   int nch, nbk, maxitems;
+  int hpg, rpi;       // query heads per selection group, rows per work item (64 / hpg)
 };
 
 static int bc_max_items(const AttnParams& a, int nbk) {
-  const int64_t bh = (int64_t)a.B * a.Hq;
-  return (int)(bh * (((int64_t)a.Nq * a.K + kBcTM - 1) / kBcTM + nbk));
+  const int64_t bg = (int64_t)a.B * a.G_sel;
+  const int rpi = kBcTM / (a.Hq / a.G_sel);
+  return (int)(bg * (((int64_t)a.Nq * a.K + rpi - 1) / rpi + nbk));
 }
 
 static BcWs bc_layout(const AttnParams& a, void* base, size_t* bytes) {
@@ -65,8 +74,12 @@ static BcWs bc_layout(const AttnParams& a, void* base, size_t* bytes) {
   w.nbk = (a.ctx + a.bs - 1) / a.bs;
   w.nch = (a.Nq + kBcRows - 1) / kBcRows;
   w.maxitems = bc_max_items(a, w.nbk);
+  w.hpg = a.Hq / a.G_sel;
+  w.rpi = kBcTM / w.hpg;
   const int64_t bh = (int64_t)a.B * a.Hq;
+  const int64_t bg = (int64_t)a.B * a.G_sel;
   const int64_t ent = bh * a.Nq * a.K;
+  const int64_t gent = bg * a.Nq * a.K;
   size_t off = 0;
   auto take = [&](size_t n) {
     char* p = (char*)base + off;
@@ -74,13 +87,13 @@ static BcWs bc_layout(const AttnParams& a, void* base, size_t* bytes) {
     return (void*)p;
   };
   w.part = (float*)take((size_t)ent * 130 * sizeof(float));
-  w.rank = (int32_t*)take((size_t)ent * 4);
-  w.list = (uint32_t*)take((size_t)ent * 4);
-  w.hist = (int32_t*)take((size_t)bh * w.nch * w.nbk * 4);
-  w.tot = (int32_t*)take((size_t)bh * w.nbk * 4);
-  w.lbase = (int32_t*)take((size_t)bh * w.nbk * 4);
-  w.ioff = (int32_t*)take((size_t)bh * w.nbk * 4);
-  w.icnt = (int32_t*)take((size_t)bh * 4);
+  w.rank = (int32_t*)take((size_t)gent * 4);
+  w.list = (uint32_t*)take((size_t)gent * 4);
+  w.hist = (int32_t*)take((size_t)bg * w.nch * w.nbk * 4);
+  w.tot = (int32_t*)take((size_t)bg * w.nbk * 4);
+  w.lbase = (int32_t*)take((size_t)bg * w.nbk * 4);
+  w.ioff = (int32_t*)take((size_t)bg * w.nbk * 4);
+  w.icnt = (int32_t*)take((size_t)bg * 4);
   w.nitems = (int32_t*)take(4);
   w.item_bk = (uint32_t*)take((size_t)w.maxitems * 4);
   w.item_c = (uint32_t*)take((size_t)w.maxitems * 4);
@@ -89,9 +102,12 @@ static BcWs bc_layout(const AttnParams& a, void* base, size_t* bytes) {
   return w;
 }
 
+// a selection group's query heads (a power of two up to 64 of them) share
+// one KV head
 bool attn_blocks_ok(const AttnParams& a) {
+  const int hpg = a.Hq / a.G_sel;
   return a.mode == 3 && attn_tile_ok(a) && (a.ctx + a.bs - 1) / a.bs <= kBcMaxBlocks && a.K <= 255 &&
-         a.Nq < (1 << 24);
+         a.Nq < (1 << 24) && hpg <= kBcTM && (hpg & (hpg - 1)) == 0 && (a.Hq / a.Hkv) % hpg == 0;
 }
 
 size_t attn_blocks_ws_bytes(const AttnParams& a) {
@@ -114,8 +130,8 @@ SP_DEV bool bc_contributes(const AttnParams& a, const int32_t* sel, int s, int n
 
 __global__ __launch_bounds__(kBcRows) void bc_count_kernel(AttnParams a, BcWs w) {
   __shared__ int hist[kBcMaxBlocks];
-  const int ch = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int bh = b * a.Hq + h;
+  const int ch = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int bh = b * a.G_sel + g;
   for (int i = threadIdx.x; i < w.nbk; i += kBcRows) hist[i] = 0;
   __syncthreads();
   const int r = ch * kBcRows + threadIdx.x;
@@ -123,7 +139,7 @@ __global__ __launch_bounds__(kBcRows) void bc_count_kernel(AttnParams a, BcWs w)
   if (r < a.Nq) {
     const int p = L - a.Nq + r;
     const int wstart = p - a.window + 1;
-    const int32_t* sel = a.sel + b * a.sels[0] + (h / (a.Hq / a.G_sel)) * a.sels[1] + (int64_t)r * a.sels[2];
+    const int32_t* sel = a.sel + b * a.sels[0] + g * a.sels[1] + (int64_t)r * a.sels[2];
     int32_t* rk = w.rank + ((int64_t)bh * a.Nq + r) * a.K;
     for (int s = 0; s < a.K; ++s) {
       int v = -1;
@@ -157,7 +173,7 @@ __global__ __launch_bounds__(256) void bc_scan_kernel(AttnParams a, BcWs w) {
       }
     }
     tot[u] = run;
-    items[u] = (run + kBcTM - 1) / kBcTM;
+    items[u] = (run + w.rpi - 1) / w.rpi;
     st += run;
     si += items[u];
   }
@@ -202,7 +218,7 @@ __global__ __launch_bounds__(256) void bc_table_kernel(AttnParams a, BcWs w) {
   }
   __syncthreads();
   for (int blk = threadIdx.x; blk < w.nbk; blk += 256) {
-    const int n = (w.tot[(int64_t)bh * w.nbk + blk] + kBcTM - 1) / kBcTM;
+    const int n = (w.tot[(int64_t)bh * w.nbk + blk] + w.rpi - 1) / w.rpi;
     const int o = base + w.ioff[(int64_t)bh * w.nbk + blk];
     for (int c = 0; c < n; ++c) {
       w.item_bk[o + c] = (uint32_t)(bh * w.nbk + blk);
@@ -212,11 +228,11 @@ __global__ __launch_bounds__(256) void bc_table_kernel(AttnParams a, BcWs w) {
 }
 
 __global__ __launch_bounds__(kBcRows) void bc_scatter_kernel(AttnParams a, BcWs w) {
-  const int ch = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int bh = b * a.Hq + h;
+  const int ch = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int bh = b * a.G_sel + g;
   const int r = ch * kBcRows + threadIdx.x;
   if (r >= a.Nq) return;
-  const int32_t* sel = a.sel + b * a.sels[0] + (h / (a.Hq / a.G_sel)) * a.sels[1] + (int64_t)r * a.sels[2];
+  const int32_t* sel = a.sel + b * a.sels[0] + g * a.sels[1] + (int64_t)r * a.sels[2];
   const int32_t* rk = w.rank + ((int64_t)bh * a.Nq + r) * a.K;
   const int32_t* hg = w.hist + ((int64_t)bh * w.nch + ch) * w.nbk;
   uint32_t* lst = w.list + (int64_t)bh * a.Nq * a.K;
@@ -234,24 +250,27 @@ struct BcSmem {
   uint16_t vt[64 * 128];    // V tile row-major, XOR-swizzled 16-byte chunks
 };
 
-// One work item: up to 64 rows that chose block blk of (request, head) bh.
-// Wave wv holds rows 16 wv .. 16 wv + 15 of the item (lane column c16).
+// One work item: up to rpi = 64 / hpg rows that chose block blk of (request,
+// group) bg, for each of the group's hpg query heads: MFMA row q = 16 wv + c16
+// (wave wv, lane column c16) is row q / hpg of the item, head q % hpg.
 __global__ __launch_bounds__(256) void bc_attn_kernel(AttnParams a, BcWs w) {
   if ((int)blockIdx.x >= *w.nitems) return;
   __shared__ __attribute__((aligned(16))) BcSmem sm;
   const uint32_t bk = w.item_bk[blockIdx.x];
   const int c = (int)w.item_c[blockIdx.x];
-  const int bh = bk / w.nbk, blk = bk % w.nbk;
-  const int b = bh / a.Hq, h = bh % a.Hq;
-  const int kvh = h / (a.Hq / a.Hkv);
+  const int bg = bk / w.nbk, blk = bk % w.nbk;
+  const int b = bg / a.G_sel, g = bg % a.G_sel;
+  const int kvh = (g * w.hpg) / (a.Hq / a.Hkv);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int qq = lane >> 4, c16 = lane & 15;
   const int L = min(a.ctx_len ? a.ctx_len[b] : a.ctx, a.ctx);
-  const int nrow = min(kBcTM, w.tot[bk] - kBcTM * c);
-  const uint32_t* lst = w.list + (int64_t)bh * a.Nq * a.K + w.lbase[bk] + kBcTM * c;
+  const int nrow = min(w.rpi, w.tot[bk] - w.rpi * c);
+  const uint32_t* lst = w.list + (int64_t)bg * a.Nq * a.K + w.lbase[bk] + w.rpi * c;
 
-  // this lane's row
-  const int ri = 16 * wid + c16;
+  // this lane's (row, head)
+  const int qi = 16 * wid + c16;
+  const int ri = qi / w.hpg;
+  const int h = g * w.hpg + qi % w.hpg;
   const bool rvalid = ri < nrow;
   const uint32_t ent = rvalid ? lst[ri] : 0u;
   const int r = (int)(ent & 0xFFFFFFu);
@@ -387,13 +406,14 @@ __global__ __launch_bounds__(256) void bc_attn_kernel(AttnParams a, BcWs w) {
   // partial (O, m, l) of each row: lane holds dims 16 nt + c16 of rows 4 qq + v of this wave
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int rr = 4 * qq + v;                   // row within the wave (lane column rr holds its state)
+    const int rr = 4 * qq + v;                   // MFMA row within the wave (lane column rr holds its state)
     const float lr = __shfl(l, rr, 64);
     const float mr = __shfl(m, rr, 64);
     const uint32_t er = (uint32_t)__shfl((int)ent, rr, 64);
-    if (16 * wid + rr >= nrow) continue;
+    const int hr = __shfl(h, rr, 64);
+    if ((16 * wid + rr) / w.hpg >= nrow) continue;
     const int rw = (int)(er & 0xFFFFFFu), sw = (int)(er >> 24);
-    float* pp = w.part + (((int64_t)bh * a.Nq + rw) * a.K + sw) * 130;
+    float* pp = w.part + ((((int64_t)b * a.Hq + hr) * a.Nq + rw) * a.K + sw) * 130;
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) pp[16 * nt + c16] = O[nt][v];
     if (c16 == 0) {
@@ -415,10 +435,12 @@ __global__ __launch_bounds__(256) void bc_combine_kernel(AttnParams a, BcWs w) {
   const int64_t nrows = (int64_t)a.B * a.Hq * a.Nq;
   const bool live = row < nrows;
   const int K = a.K;
+  // the row's group list ranks: row = ((b Hq + h) Nq + r), group g = h / hpg
+  const int64_t grow = live ? ((row / a.Nq / a.Hq) * a.G_sel + (row / a.Nq % a.Hq) / w.hpg) * a.Nq + row % a.Nq : 0;
   if (live)
     for (int s = dd; s < K; s += 128) {
       float ms = -INFINITY, ls = 0.f;
-      if (w.rank[row * K + s] >= 0) {
+      if (w.rank[grow * K + s] >= 0) {
         const float* pp = w.part + (row * K + s) * 130;
         ms = pp[128];
         ls = pp[129];
@@ -470,11 +492,12 @@ hipError_t launch_attn_blocks(const AttnParams& a0, hipStream_t st) {
   AttnParams a = a0;
   size_t need = 0;
   BcWs w = bc_layout(a, a.ws, &need);
-  const dim3 gc(w.nch, a.Hq, a.B);
+  const dim3 gc(w.nch, a.G_sel, a.B);
   const int bh = a.B * a.Hq;
+  const int bg = a.B * a.G_sel;
   hipLaunchKernelGGL(bc_count_kernel, gc, dim3(kBcRows), 0, st, a, w);
-  hipLaunchKernelGGL(bc_scan_kernel, dim3(bh), dim3(256), 0, st, a, w);
-  hipLaunchKernelGGL(bc_table_kernel, dim3(bh), dim3(256), 0, st, a, w);
+  hipLaunchKernelGGL(bc_scan_kernel, dim3(bg), dim3(256), 0, st, a, w);
+  hipLaunchKernelGGL(bc_table_kernel, dim3(bg), dim3(256), 0, st, a, w);
   hipLaunchKernelGGL(bc_scatter_kernel, gc, dim3(kBcRows), 0, st, a, w);
   hipLaunchKernelGGL(bc_attn_kernel, dim3(w.maxitems), dim3(256), 0, st, a, w);
   // window part: the tiled kernel, its LSE into the workspace

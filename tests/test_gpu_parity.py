@@ -1047,12 +1047,15 @@ def test_quest_bounds_and_ties(dtype, d):
 
 
 # ---------------------------------------------------------------- blocks per GQA group
-def test_group_block_lists_equal_repeated_head_lists():
+@pytest.mark.parametrize("Hq,Hkv,G", [(8, 2, 2), (8, 1, 1), (16, 1, 1)])
+def test_group_block_lists_equal_repeated_head_lists(Hq, Hkv, G):
     """A BLOCKS selection with one list per KV group gives the same output as
     the same lists repeated for every query head (bitwise), on the block-sparse
-    small shapes with four query heads per group."""
+    small shapes with 4, 8 and 16 query heads per group: the group's heads
+    share one staging of each chosen block, the repeated lists stage it once
+    per head."""
     sp = S()
-    wl = dataclasses.replace(gen.WORKLOADS["msa_prefill_small"], Hq=8, Hkv=2, H_I=4, G_sel=2)
+    wl = dataclasses.replace(gen.WORKLOADS["msa_prefill_small"], Hq=Hq, Hkv=Hkv, H_I=4, G_sel=G)
     say(f"[gpu] group block lists {wl.name} Hq={wl.Hq} G={wl.G_sel}")
     inp = gen.generate(wl)
     hp = run(wl, inp)
