@@ -179,6 +179,63 @@ def algorithmic(wl, inp, hp, fused):
     return out
 
 
+def selection_stats(wl, inp, hp):
+    """Pairs the selection keeps against the causal candidates, summed over
+    (request, query head, query row): coverage = sum |S| / sum |C| and the
+    skipped-KV ratio 1 - coverage ("A Guide to Sparse Attention in Large
+    Models", production deployment: monitor coverage and skipped KV)."""
+    import numpy as np
+    from fine_grained_top_amd import metrics
+    lens = inp["ctx_len"].astype(np.int64)
+    pos = np.stack([L - wl.Nq + np.arange(wl.Nq) for L in lens])            # [B, Nq]
+    causal = float((pos + 1).sum()) * wl.Hq
+    if wl.kind == "window_global":
+        sel = float(metrics.window_stride_pairs(wl.N, wl.window, wl.n_global, wl.stride)) * wl.Hq * wl.B
+    elif wl.kind in ("dsa_pages", "quest"):
+        P = wl.page_size
+        pg = hp.idx.cpu().numpy().astype(np.int64)
+        tok = np.clip(np.minimum(pg * P + P, pos[:, None, :, None] + 1) - pg * P, 0, None) * (pg >= 0)
+        sel = float(tok.sum()) * (wl.Hq // wl.G_sel)
+    elif wl.kind in ("blocks", "nsa", "msa"):
+        # chosen blocks' tokens union the window (no window: the NSA selection branch alone)
+        blk = hp.idx.cpu().numpy().astype(np.int64)                            # [B, G or Hq, Nq, nb]
+        p = pos[:, None, :]
+        win = wl.window if wl.kind != "nsa" else 0
+        ws = np.maximum(0, p - win + 1) if win else p + 1
+        lo = blk * wl.block_size
+        tok = np.clip(np.minimum(lo + wl.block_size, p[..., None] + 1) - lo, 0, None) * (blk >= 0)
+        in_win = np.clip(np.minimum(lo + wl.block_size, p[..., None] + 1) - np.maximum(lo, ws[..., None]), 0, None)
+        size = tok.sum(-1) - ((blk >= 0) * in_win).sum(-1) + (p - ws + 1)
+        sel = float(size.sum()) * (wl.Hq // blk.shape[1])
+    elif wl.H_I:
+        cnt = hp.count.cpu().numpy().astype(np.int64) if hp.count is not None else None
+        if cnt is None:
+            cnt = np.broadcast_to(np.minimum(pos + 1, wl.topk)[:, None, :], (wl.B, wl.G_sel, wl.Nq))
+        sel = float(cnt.sum()) * (wl.Hq // wl.G_sel)
+    else:
+        sel = causal
+    return {"pairs_selected": sel, "pairs_causal": causal, "coverage": round(sel / causal, 6),
+            "skipped_kv_ratio": round(1.0 - sel / causal, 6)}
+
+
+def pct(ts):
+    import numpy as np
+    a = np.asarray(ts, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 5), "p10": round(float(np.percentile(a, 10)), 5),
+            "median": round(float(np.median(a)), 5), "p90": round(float(np.percentile(a, 90)), 5)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def measured_traffic(workload, stage):
     """HBM bytes per launch of a stage from the committed counter record of
     this workload, or None when there is none or the kernels changed since."""
@@ -291,10 +348,19 @@ def main():
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
-    stage_ms = {}
+    stage_ms, stage_pct = {}, {}
     for si, (name, _) in enumerate(stages):
         ts = [evs[i][si][0].elapsed_time(evs[i][si][1]) for i in range(args.steps)]
         stage_ms[name] = float(np.mean(ts))
+        stage_pct[name] = pct(ts)
+    # one event pair around each whole step (a third pass of the same steps)
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        sev[i][0].record(stream)
+        step(i)
+        sev[i][1].record(stream)
+    torch.cuda.synchronize()
+    step_pct = pct([a.elapsed_time(b) for a, b in sev])
 
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -315,7 +381,8 @@ def main():
         roof["traffic"] = measured_traffic(wl.name, dom)
     per_stage = {}
     for name, ms in stage_ms.items():
-        e = {"ms": round(ms, 5)}
+        e = {"ms": round(ms, 5), "ms_p10": stage_pct[name]["p10"], "ms_median": stage_pct[name]["median"],
+             "ms_p90": stage_pct[name]["p90"]}
         if name in alg:
             a = alg[name]
             e["alg_bytes"] = a["bytes"]
@@ -362,7 +429,23 @@ def main():
         dt = time.perf_counter() - t0
         cpu = {"value": round(done / dt, 4), "unit": "queries/s", "cores": cores, "kind": "oracle",
                "sample": f"{done} of {wl.B * wl.Nq} query rows of {wl.name} (all heads and groups per row), "
-                         f"{dt:.1f}s"}
+                         f"{dt:.1f}s",
+               "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0))}
+        # the same oracle held to one thread, on the first rows of the sample
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                d1, t1 = 0, time.perf_counter()
+                for (b, r) in rows:
+                    orc.run(wl, inp, [(b, r)])
+                    d1 += 1
+                    if time.perf_counter() - t1 > args.cpu_seconds / 2:
+                        break
+                dt1 = time.perf_counter() - t1
+            cpu["one_thread"] = {"value": round(d1 / dt1, 4), "unit": "queries/s", "cores": 1,
+                                 "sample": f"{d1} query rows, {dt1:.1f}s"}
+        except ImportError:
+            cpu["one_thread"] = None
         parity = bool(ok)
 
     from fine_grained_top_amd import metrics
@@ -393,7 +476,9 @@ def main():
                    "idx_k_dtype": wl.idx_k_dtype, "len_range": wl.len_range, "replicas": args.replicas},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "step_ms": step_pct,
         "stages": per_stage,
+        "selection": selection_stats(wl, inp, paths[(args.steps - 1) % len(paths)]),
         "oracle_spot_parity": parity,
         "kv_cache_gb_per_layer": round(metrics.kv_cache_memory_gb(wl.B, wl.N, wl.Hkv * wl.d, 1), 3),
     }

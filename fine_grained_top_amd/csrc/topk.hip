@@ -1141,168 +1141,257 @@ struct FzWs {
 };
 
 struct FzSmem {
-  float qs[4 * 64];       // the row's indexer queries (<= 4 heads, d_I = 64) and weights
-  float wsg[4];
-  RowSmem row;
-  uint32_t ck[kCandCap];
-  uint32_t cj[kCandCap];
+  RowSmem row;             // histogram and band lists (also used by the fallback)
   uint32_t bm[kMaxWords];
-  uint32_t coff[kTkThreads + 1];
-  float red[5 * (kTkThreads / 64)];   // per-wave partials: key bound, 1-norm, count, overflow, largest key
+  float qs[4 * 64];        // the row's indexer queries (<= 4 heads, d_I = 64) and weights
+  float wsg[4];
+  float red[4 * (kTkThreads / 64)];   // per-wave partials
+  uint32_t sel[4];         // band: smallest and largest key of the chosen bin
 };
 
-__global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs w) {
-  constexpr int T = kTkThreads;
-  __shared__ FzSmem sm;
-  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
-  RowCtx c = row_ctx(p, row);
-  if (c.n <= p.K) return write_all(p, c, T);
-  // one pass over the inputs: the row's queries and weights (into LDS for the
-  // exact band keys, and the weighted 1-norm of the queries for the error
-  // bound), the key bounds of the request's chunks, the candidate counts of
-  // the chunks covering keys 0..p (nch <= T) and the pilot threshold; one
-  // barrier publishes the per-wave partials
+// In a 4096-bin histogram (bins ordered low to high), the bin holding the
+// R-th largest element and the number of elements in higher bins. Thread t
+// owns bins [8t, 8t + 8). Two barriers; hist may be rewritten afterwards.
+template <int T>
+SP_DEV void hist_find(const uint32_t* hist, uint32_t R, uint32_t* sc, uint32_t& bin, uint32_t& above) {
+  static_assert(T * 8 == 4096, "eight bins per thread");
   constexpr int NW = T / 64;
-  const int wid = tid >> 6;
-  const int nch = (c.n + 511) / 512;
-  const int L = min(p.ctx_len ? p.ctx_len[c.b] : p.ctx, p.ctx);
-  const int nch_k = min(w.nchunk, (L + 511) / 512);
-  // candidate arrays: [request][chunk][selection row of the request][cap]
-  const int nrl = p.G * p.Nq, rowl = c.g * p.Nq + c.r;
-  const uint32_t my = tid < nch ? w.cand_n[((int64_t)c.b * w.nchunk + tid) * nrl + rowl] : 0u;
-  float km = 0.f, coef = 0.f;
-  for (int i = tid; i < nch_k; i += T) km = fmaxf(km, w.kmax[(int64_t)c.b * w.nchunk + i]);
-  const float tau = w.tau[row];
-  for (int e = tid; e < c.ir.H * c.ir.d; e += T) {
-    const int hh = e / c.ir.d;
-    const float qv = (float)load_f64(c.ir.q, c.ir.qt, hh * c.ir.qh_stride + e % c.ir.d);
-    sm.qs[e] = qv;
-    coef = fmaf(c.ir.relu ? fabsf(c.ir.w[hh * c.ir.w_stride]) : 1.f, fabsf(qv), coef);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  uint32_t hb[8], mine = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    hb[e] = hist[8 * tid + e];
+    mine += hb[e];
   }
-  if (tid < c.ir.H) sm.wsg[tid] = c.ir.relu ? c.ir.w[tid * c.ir.w_stride] : 1.f;
-  const uint32_t incl = wave_prefix_incl_u32(my);
+  const uint32_t pin = wave_prefix_incl_u32(mine);
+  const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)pin, 63) - pin + mine;   // this lane and above
+  if (lane == 0) sc[wid] = v;
+  __syncthreads();
+  uint32_t cum = v - mine;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) cum += x > wid ? sc[x] : 0u;
+  if (cum < R && cum + mine >= R) {
+#pragma unroll
+    for (int e = 7; e >= 0; --e) {
+      if (cum + hb[e] >= R) {
+        sc[NW] = (uint32_t)(8 * tid + e);
+        sc[NW + 1] = cum;
+        break;
+      }
+      cum += hb[e];
+    }
+  }
+  __syncthreads();
+  bin = sc[NW];
+  above = sc[NW + 1];
+}
+
+// first-round reads of the final selection: 16 lanes per chunk, one 16-byte
+// pair of candidate slots each (the first 32 slots of 32 chunks per
+// instruction); slots past 32 of a chunk are read from global memory in
+// every pass (a chunk rarely holds that many)
+constexpr int kFzLanes = 16;
+constexpr int kFzRounds = 8;      // instructions held in registers: 256 chunks
+
+// Final selection, one workgroup per row. Every load of the row is issued in
+// one round, none waiting on another: the first 32 candidate slots of every
+// chunk (consecutive lanes read consecutive pairs of a chunk's slots) with
+// the chunk counts, the chunk key bounds, the threshold, the row's queries
+// and weights. One barrier then publishes the error bound's inputs, the
+// number of candidates and the largest candidate score. The K-th largest
+// score is located by a histogram of 4096 bins over [tau, largest score]
+// (bins as wide as the certification band or wider; a second pass splits the
+// bin when it is much wider); the smallest and largest scores of that bin
+// give the band; scores above it set bitmap bits, band members are listed
+// and, unless all of them are needed to fill the K slots, scored exactly and
+// ranked; the bitmap is written out as ascending positions. Checks (enough
+// candidates, the band above tau) send a row to recomputed scores, so the
+// result never depends on the pilot's sample.
+__global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs w) {
+  constexpr int T = kTkThreads, NW = T / 64, S = kFzRounds, CPI = T / kFzLanes;
+  __shared__ FzSmem sm;
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nrl = p.G * p.Nq, rowl = row % nrl, b = row / nrl;
+  const int cq = tid / kFzLanes, pr = tid % kFzLanes;     // chunk within an instruction, slot pair
+  // candidate slots of chunk ch for this row; counts
+  auto cslot = [&](int ch) { return w.cand + (((int64_t)b * w.nchunk + ch) * nrl + rowl) * w.cap; };
+  auto ccount = [&](int ch) { return w.cand_n[((int64_t)b * w.nchunk + ch) * nrl + rowl]; };
+  u32x4 cv4[S];
+  uint32_t cn[S];
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const int ch = CPI * i + cq;
+    if (ch < w.nchunk) {
+      cv4[i] = ((const u32x4*)cslot(ch))[pr];
+      cn[i] = ccount(ch);
+    }
+  }
+  float km = tid < w.nchunk ? w.kmax[(int64_t)b * w.nchunk + tid] : 0.f;
+  const float tau = w.tau[row];
+  RowCtx c = row_ctx(p, row);
+  const int H = c.ir.H, d = c.ir.d;
+  float qv = 0.f, wq = 0.f;
+  if (tid < H * d) {
+    qv = (float)load_f64(c.ir.q, c.ir.qt, (tid / d) * c.ir.qh_stride + tid % d);
+    wq = c.ir.relu ? c.ir.w[(tid / d) * c.ir.w_stride] : 1.f;
+  }
+  if (c.n <= p.K) return write_all(p, c, T);
+  if (tid < H * d) sm.qs[tid] = qv;
+  if (tid < H * d && tid % d == 0) sm.wsg[tid / d] = wq;
+  float coef = tid < H * d ? fabsf(wq) * fabsf(qv) : 0.f;
+  const int nch = (c.n + 511) / 512;                 // chunks holding keys 0..n-1
+  if (tid >= nch) km = 0.f;
+  // register pairs: bit 2 i + h set when entry h of pair i is a candidate
+  uint32_t vm = 0u;
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const int ch = CPI * i + cq;
+    const uint32_t nn = ch < nch ? min(cn[i], 32u) : 0u;
+    vm |= ((uint32_t)(2 * pr) < nn ? 1u : 0u) << (2 * i);
+    vm |= ((uint32_t)(2 * pr + 1) < nn ? 1u : 0u) << (2 * i + 1);
+  }
+  // visit every candidate of this thread: register pairs, then (rare) the
+  // slots past 32 of this thread's chunks and the chunks past the registers
+  bool xs = false;                                     // a register chunk holds more than 32
+#pragma unroll
+  for (int i = 0; i < S; ++i) xs |= CPI * i + cq < nch && cn[i] > 32u;
+  auto each = [&](auto f) {
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      if (vm & (1u << (2 * i))) f(cv4[i][0], cv4[i][1]);
+      if (vm & (2u << (2 * i))) f(cv4[i][2], cv4[i][3]);
+    }
+    if (xs) {
+#pragma unroll
+      for (int i = 0; i < S; ++i) {
+        const int ch = CPI * i + cq;
+        if (ch < nch && cn[i] > 32u)
+          for (int e = 32 + pr; e < (int)min(cn[i], (uint32_t)w.cap); e += kFzLanes) {
+            const u32x2 v = cslot(ch)[e];
+            f(v[0], v[1]);
+          }
+      }
+    }
+    for (int ch = CPI * S + cq; ch < nch; ch += CPI) {   // chunks past the registers (long contexts)
+      const int nn = (int)min(ccount(ch), (uint32_t)w.cap);
+      for (int e = pr; e < nn; e += kFzLanes) {
+        const u32x2 v = cslot(ch)[e];
+        f(v[0], v[1]);
+      }
+    }
+  };
+  uint32_t kmx = 0u, mine = 0u;
+  bool over = false;
+#pragma unroll
+  for (int i = 0; i < S; ++i) over |= CPI * i + cq < nch && cn[i] > (uint32_t)w.cap;
+  each([&](uint32_t k, uint32_t) {
+    kmx = max(kmx, k);
+    ++mine;
+  });
+  for (int i = tid; i < 4096; i += T) sm.row.hist[i] = 0u;
+  const int nwords = (c.n + 31) >> 5;
+  for (int i = tid; i < nwords; i += T) sm.bm[i] = 0u;
+  if (tid == 0) {
+    sm.row.run[0] = 0u;
+    sm.row.run[1] = 0u;
+    sm.sel[2] = 0xFFFFFFFFu;
+    sm.sel[3] = 0u;
+  }
   km = wave_max_dpp(km);
   coef = wave_sum_dpp(coef);
-  const bool wover = __any(my > (uint32_t)w.cap);
-  if (lane == 63) {
+  kmx = wave_max_u32_dpp(kmx);
+  const uint32_t wn = (uint32_t)__builtin_amdgcn_readlane((int)wave_prefix_incl_u32(mine), 63);
+  const bool wover = __any(over);
+  if (lane == 0) {
     sm.red[wid] = km;
     sm.red[NW + wid] = coef;
-    sm.red[2 * NW + wid] = __uint_as_float(incl);
-    sm.red[3 * NW + wid] = wover ? 1.f : 0.f;
+    sm.red[2 * NW + wid] = __uint_as_float(kmx);
+    sm.red[3 * NW + wid] = __uint_as_float(wn | (wover ? 0x80000000u : 0u));
   }
   __syncthreads();
   float KM = 0.f, CO = 0.f;
-  uint32_t wbase = 0, n_cand = 0;
+  uint32_t KX = 0u, n_cand = 0u;
   bool any_over = false;
 #pragma unroll
   for (int v = 0; v < NW; ++v) {
     KM = fmaxf(KM, sm.red[v]);
     CO += sm.red[NW + v];
-    const uint32_t tv = __float_as_uint(sm.red[2 * NW + v]);
-    wbase += v < wid ? tv : 0u;
-    n_cand += tv;
-    any_over |= sm.red[3 * NW + v] != 0.f;
+    KX = max(KX, __float_as_uint(sm.red[2 * NW + v]));
+    const uint32_t x = __float_as_uint(sm.red[3 * NW + v]);
+    n_cand += x & 0x7FFFFFFFu;
+    any_over |= (x >> 31) != 0u;
   }
   c.eps = eps_of(p.ix, CO, KM);
-  const float eps = c.eps;
   auto fallback = [&]() {
     row_topk_single<T>(p, c, sm.row, [&](int i) { return recompute_score(c.ir, i); });
     if (p.count && tid == 0) p.count[((int64_t)c.b * p.G + c.g) * p.Nq + c.r] = p.K;
   };
-  if (any_over || n_cand < (uint32_t)p.K || n_cand > (uint32_t)kCandCap) return fallback();
-  if (tid < nch) sm.coff[tid] = wbase + incl - my;
-  if (tid == 0) sm.coff[nch] = n_cand;
+  if (any_over || n_cand < (uint32_t)p.K || !(fabsf(tau) <= 3.0e38f)) return fallback();
+  const float E = 2.0f * c.eps * 1.0001f + 1e-30f;            // half-width of the band
+  // bins of [tau, largest score]: bin(s) = floor((s - tau) / W), monotone in s
+  const float W = fmaxf(E, (order_key_f32(KX) - tau) * (1.0f / 4096.0f) * 1.001f);
+  const float iW = 1.0f / W;
+  auto bin1 = [&](uint32_t k) { return (uint32_t)fminf((order_key_f32(k) - tau) * iW, 4095.0f); };
+  each([&](uint32_t k, uint32_t) { atomicAdd(&sm.row.hist[bin1(k)], 1u); });
   __syncthreads();
-  // compact into LDS: wave w copies chunks w, w + NW, ..., two chunks per
-  // load instruction (32 lanes each, lane l: slot l mod 32) and 32 chunks per
-  // batch, whose offsets and counts are read first; candidate offsets within
-  // the request's arrays fit 32 bits (checked at launch)
-  uint32_t kmx = 0;      // the largest candidate key, from the copied keys
-  {
-    constexpr int CPI = 2, IT = 16;
-    const int sub = lane >> 5;
-    const uint32_t sl = (uint32_t)(lane & 31);
-    const u32x2* cb = w.cand + (int64_t)c.b * w.nchunk * nrl * w.cap + (int64_t)rowl * w.cap;
-    const uint32_t cstep = (uint32_t)(nrl * w.cap);     // pairs between a row's slots of consecutive chunks
-    for (int c0 = wid; c0 < nch; c0 += NW * CPI * IT) {
-      uint32_t oo[IT], nn[IT];
-#pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        const int ch = c0 + NW * (CPI * it + sub);
-        oo[it] = ch < nch ? sm.coff[ch] : 0u;
-        nn[it] = ch < nch ? sm.coff[ch + 1] - oo[it] : 0u;
-      }
-      u32x2 cv[IT];
-#pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        const uint32_t ch = (uint32_t)(c0 + NW * (CPI * it + sub));
-        cv[it] = sl < nn[it] ? cb[ch * cstep + sl] : u32x2{0u, 0u};
-      }
-#pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        if (sl < nn[it]) {
-          sm.ck[oo[it] + sl] = cv[it][0];
-          sm.cj[oo[it] + sl] = cv[it][1];
-          kmx = max(kmx, cv[it][0]);
-        }
-      }
-#pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        const uint32_t ch = (uint32_t)(c0 + NW * (CPI * it + sub));
-        for (uint32_t e = sl + 32; e < nn[it]; e += 32) {   // more than 32 in a chunk
-          const u32x2 v = cb[ch * cstep + e];
-          sm.ck[oo[it] + e] = v[0];
-          sm.cj[oo[it] + e] = v[1];
-          kmx = max(kmx, v[0]);
-        }
-      }
-    }
+  uint32_t b1, above;
+  hist_find<T>(sm.row.hist, (uint32_t)p.K, sm.row.sc, b1, above);
+  // a bin much wider than the band: split it into 4096 once more
+  const bool two = W > 4.0f * E;
+  uint32_t b2 = 0u;
+  const float lo2 = tau + (float)b1 * W, iW2 = 4096.0f / (W * 1.01f);
+  auto bin2 = [&](uint32_t k) { return (uint32_t)fminf(fmaxf((order_key_f32(k) - lo2) * iW2, 0.0f), 4095.0f); };
+  if (two) {
+    for (int i = tid; i < 4096; i += T) sm.row.hist[i] = 0u;
+    __syncthreads();
+    each([&](uint32_t k, uint32_t) {
+      if (bin1(k) == b1) atomicAdd(&sm.row.hist[bin2(k)], 1u);
+    });
+    __syncthreads();
+    uint32_t above2;
+    hist_find<T>(sm.row.hist, (uint32_t)p.K - above, sm.row.sc, b2, above2);
   }
-  kmx = wave_max_u32_dpp(kmx);
-  if (lane == 63) sm.red[4 * NW + wid] = __uint_as_float(kmx);
-  const int nwords = (c.n + 31) >> 5;
-  for (int i = tid; i < nwords; i += T) sm.bm[i] = 0u;
+  // smallest and largest score of the chosen bin: the K-th largest lies between
+  each([&](uint32_t k, uint32_t) {
+    if (bin1(k) == b1 && (!two || bin2(k) == b2)) {
+      atomicMin(&sm.sel[2], k);
+      atomicMax(&sm.sel[3], k);
+    }
+  });
   __syncthreads();
-  const uint32_t base = f32_order_key(tau);
-#pragma unroll
-  for (int v = 0; v < NW; ++v) kmx = max(kmx, __float_as_uint(sm.red[4 * NW + v]));
-  const int bits = 32 - __builtin_clz((kmx - base) | 1u);
-  // the K-th largest key lies in [t, thi]; the radix passes stop once that
-  // bin spans at most E as floats (the band below grows by at most that)
-  const float E = 2.0f * eps * 1.0001f + 1e-30f;
-  uint32_t t, thi, above;
-  radix_select<T>((int)n_cand, (uint32_t)p.K, [&](int i, uint32_t& k) { k = sm.ck[i]; return true; },
-                  sm.row.hist, sm.row.sc, t, above, base, bits, &thi, E);
-  const uint32_t klo = f32_order_key(nextafterf(order_key_f32(t) - E, -INFINITY));
-  const uint32_t khi = f32_order_key(nextafterf(order_key_f32(thi) + E, INFINITY));
-  if (klo < base) return fallback();        // part of the band may lie below tau
-  uint32_t n_in = 0;
-  if (tid == 0) sm.row.run[0] = 0;
-  __syncthreads();
-  for (uint32_t i = tid; i < n_cand; i += T) {
-    const uint32_t ks = sm.ck[i];
-    if (ks > khi) {
-      atomicOr(&sm.bm[sm.cj[i] >> 5], 1u << (sm.cj[i] & 31));
+  const uint32_t klo = f32_order_key(nextafterf(order_key_f32(sm.sel[2]) - E, -INFINITY));
+  const uint32_t khi = f32_order_key(nextafterf(order_key_f32(sm.sel[3]) + E, INFINITY));
+  if (klo < f32_order_key(tau)) return fallback();   // part of the band may lie below tau
+  uint32_t n_in = 0u;
+  each([&](uint32_t k, uint32_t j) {
+    if (k > khi) {
+      atomicOr(&sm.bm[j >> 5], 1u << (j & 31));
       ++n_in;
-    } else if (ks >= klo) {
+    } else if (k >= klo) {
       const uint32_t slot = atomicAdd(&sm.row.run[0], 1u);
       if (slot < (uint32_t)kBandCap) {
-        sm.row.band_j[slot] = sm.cj[i];
-        sm.row.band_k[slot] = ks;
+        sm.row.band_j[slot] = j;
+        sm.row.band_k[slot] = k;
       }
     }
-  }
-  uint32_t tot_in;
-  block_scan_sum<T>(n_in, sm.row.sc, tot_in);
-  const uint32_t nb = sm.row.run[0];
-  if (nb > (uint32_t)kBandCap) return fallback();
-  const uint32_t R2 = (uint32_t)p.K - tot_in;
-  for (uint32_t e = tid >> 4; e < nb; e += T / 16) {   // a quarter-wave per band member
-    const float key = group_exact_key<16>(c.ir, sm.row.band_j[e], sm.qs, sm.wsg);
-    if ((lane & 15) == 0) sm.row.band_k[e] = f32_order_key(key);
-  }
+  });
+  n_in = (uint32_t)__builtin_amdgcn_readlane((int)wave_prefix_incl_u32(n_in), 63);
+  if (lane == 0 && n_in) atomicAdd(&sm.row.run[1], n_in);
   __syncthreads();
-  band_mark<T>(sm.row.band_k, sm.row.band_j, nb, R2, sm.bm);
+  const uint32_t nb = sm.row.run[0], tot_in = sm.row.run[1];
+  if (nb > (uint32_t)kBandCap) return fallback();
+  const uint32_t R2 = (uint32_t)p.K - tot_in;      // 1 <= R2 <= nb
+  if (nb == R2) {
+    // every band member is needed: no exact keys
+    for (uint32_t e = tid; e < nb; e += T) atomicOr(&sm.bm[sm.row.band_j[e] >> 5], 1u << (sm.row.band_j[e] & 31));
+  } else {
+    for (uint32_t e = tid >> 4; e < nb; e += T / 16) {   // a quarter-wave per band member
+      const float key = group_exact_key<16>(c.ir, sm.row.band_j[e], sm.qs, sm.wsg);
+      if ((lane & 15) == 0) sm.row.band_k[e] = f32_order_key(key);
+    }
+    __syncthreads();
+    band_mark<T>(sm.row.band_k, sm.row.band_j, nb, R2, sm.bm);
+  }
   __syncthreads();
   emit_bitmap<T, kMaxWords>(p, c, sm.row, sm.bm, nwords);
 }

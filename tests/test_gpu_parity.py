@@ -424,6 +424,29 @@ def test_fused_falls_back_when_the_sample_misleads():
     check_sets(hp, res, rows, wl)
 
 
+@pytest.mark.parametrize("kfmt", ["fp8", "bf16"])
+def test_fused_decode_clustered_extreme_keys(kfmt):
+    """Decode rows whose survivors crowd into a few 512-key chunks (more than
+    a thread of the final selection loads in its first round) and whose
+    largest scores are far above the rest (so the score range is split twice
+    by the selection histogram): a run of large indexer keys, distinct by
+    position, is planted in every request; fp8 and bf16 indexer keys."""
+    wl = dataclasses.replace(gen.WORKLOADS["dsa_decode_small"], B=2, N=40000, len_range=(36000, 40000), topk=512,
+                             idx_k_dtype=kfmt)
+    inp = gen.generate(wl)
+    codes = inp["k_idx"]
+    run = np.arange(5000, 5300)
+    if kfmt == "fp8":
+        codes[:, run, 0, :] = (0x68 + (run % 8)).astype(codes.dtype)[:, None]      # 64 .. 120
+    else:
+        codes[:, run, 0, :] = (0x4200 + (run % 128)).astype(codes.dtype)[:, None]    # 32 .. 63.75
+    hp = run_fused(wl, inp)
+    rows = _all_rows(wl, inp)
+    res = oracle_rows(wl, inp, rows)
+    check_sets(hp, res, rows, wl)
+    check_out(hp, res, rows, 2e-3)
+
+
 # ---------------------------------------------------------------- modes agree
 def test_dense_mode_small():
     wl = gen.WORKLOADS["dense_small"]
