@@ -45,6 +45,14 @@ constexpr int kBcMaxBlocks = 2048;
 constexpr int kBcKs = 136;       // K tile row stride in 16-bit words
 constexpr float kBcLog2e = 1.4426950408889634f;
 constexpr float kBcLn2 = 0.6931471805599453f;
+// One (row, head, slot) partial: m, l and a scale (4 words with a pad), then
+// the 128 dims of the normalized output O / l as 16-bit fixed point relative
+// to the scale (the largest |O / l| of the partial): 272 bytes instead of
+// 520 for float32. The merged output is a convex combination of the
+// normalized partials, so its error from this rounding is at most
+// scale / 65534, below 1e-4 for values of |v| up to 6.
+constexpr int kBcPart = 4 + 64;   // 32-bit words
+constexpr int kBcListMax = 32;    // list slots held in registers by count/scatter
 
 struct BcWs {
   int32_t* rank;      // [B*G][Nq][nb]: rank within the chunk's bin, -1 = no contribution
@@ -57,7 +65,7 @@ struct BcWs {
   uint32_t* item_bk;  // [maxitems]: (request, group) * nbk + block
   uint32_t* item_c;   // [maxitems]: row chunk of the block's list
   uint32_t* list;     // [B*G][Nq*nb]: row | slot << 24
-  float* part;        // [B*Hq][Nq][nb][130]: O (128), m, l
+  float* part;        // [B*Hq][Nq][nb][kBcPart]: m, l, scale, pad, 128 x int16 O / l
   float* lse_w;       // [B*Hq][Nq]: LSE of the window part
   int nch, nbk, maxitems;
   int hpg, rpi;       // query heads per selection group, rows per work item (64 / hpg)
@@ -86,7 +94,7 @@ static BcWs bc_layout(const AttnParams& a, void* base, size_t* bytes) {
     off += (n + 255) & ~(size_t)255;
     return (void*)p;
   };
-  w.part = (float*)take((size_t)ent * 130 * sizeof(float));
+  w.part = (float*)take((size_t)ent * kBcPart * sizeof(float));
   w.rank = (int32_t*)take((size_t)gent * 4);
   w.list = (uint32_t*)take((size_t)gent * 4);
   w.hist = (int32_t*)take((size_t)bg * w.nch * w.nbk * 4);
@@ -128,6 +136,25 @@ SP_DEV bool bc_contributes(const AttnParams& a, const int32_t* sel, int s, int n
   return hi >= lo;
 }
 
+// a row's block list into registers (entries past K read as -1): four
+// entries per load when the list is contiguous and 16-byte aligned
+SP_DEV void bc_load_list(const AttnParams& a, const int32_t* sel, int (&blk)[kBcListMax]) {
+  if (a.sels[3] == 1 && (a.K & 3) == 0 && (((uintptr_t)sel) & 15) == 0) {
+#pragma unroll
+    for (int s4 = 0; s4 < kBcListMax / 4; ++s4) {
+      int4 v = make_int4(-1, -1, -1, -1);
+      if (4 * s4 < a.K) v = *(const int4*)(sel + 4 * s4);
+      blk[4 * s4] = v.x;
+      blk[4 * s4 + 1] = v.y;
+      blk[4 * s4 + 2] = v.z;
+      blk[4 * s4 + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < kBcListMax; ++s) blk[s] = s < a.K ? sel[s * a.sels[3]] : -1;
+  }
+}
+
 __global__ __launch_bounds__(kBcRows) void bc_count_kernel(AttnParams a, BcWs w) {
   __shared__ int hist[kBcMaxBlocks];
   const int ch = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -141,10 +168,34 @@ __global__ __launch_bounds__(kBcRows) void bc_count_kernel(AttnParams a, BcWs w)
     const int wstart = p - a.window + 1;
     const int32_t* sel = a.sel + b * a.sels[0] + g * a.sels[1] + (int64_t)r * a.sels[2];
     int32_t* rk = w.rank + ((int64_t)bh * a.Nq + r) * a.K;
-    for (int s = 0; s < a.K; ++s) {
-      int v = -1;
-      if (p >= 0 && bc_contributes(a, sel, s, w.nbk, p, wstart)) v = atomicAdd(&hist[sel[s * a.sels[3]]], 1);
-      rk[s] = v;
+    if (a.K <= kBcListMax) {
+      // the list in registers; the same contribution rule as bc_contributes
+      int blk[kBcListMax], rv[kBcListMax];
+      bc_load_list(a, sel, blk);
+#pragma unroll
+      for (int s = 0; s < kBcListMax; ++s) {
+        bool c = s < a.K && p >= 0 && blk[s] >= 0 && blk[s] < w.nbk;
+#pragma unroll
+        for (int s2 = 0; s2 < s; ++s2) c = c && blk[s2] != blk[s];
+        const int lo = blk[s] * a.bs;
+        c = c && min(min(lo + a.bs - 1, p), wstart - 1) >= lo;
+        rv[s] = c ? atomicAdd(&hist[blk[s]], 1) : -1;
+      }
+      if ((a.K & 3) == 0) {
+#pragma unroll
+        for (int s4 = 0; s4 < kBcListMax / 4; ++s4)
+          if (4 * s4 < a.K) *(int4*)(rk + 4 * s4) = make_int4(rv[4 * s4], rv[4 * s4 + 1], rv[4 * s4 + 2], rv[4 * s4 + 3]);
+      } else {
+#pragma unroll
+        for (int s = 0; s < kBcListMax; ++s)
+          if (s < a.K) rk[s] = rv[s];
+      }
+    } else {
+      for (int s = 0; s < a.K; ++s) {
+        int v = -1;
+        if (p >= 0 && bc_contributes(a, sel, s, w.nbk, p, wstart)) v = atomicAdd(&hist[sel[s * a.sels[3]]], 1);
+        rk[s] = v;
+      }
     }
   }
   __syncthreads();
@@ -236,6 +287,24 @@ __global__ __launch_bounds__(kBcRows) void bc_scatter_kernel(AttnParams a, BcWs 
   const int32_t* rk = w.rank + ((int64_t)bh * a.Nq + r) * a.K;
   const int32_t* hg = w.hist + ((int64_t)bh * w.nch + ch) * w.nbk;
   uint32_t* lst = w.list + (int64_t)bh * a.Nq * a.K;
+  if (a.K <= kBcListMax && (a.K & 3) == 0) {
+    int blk[kBcListMax];
+    bc_load_list(a, sel, blk);
+#pragma unroll
+    for (int s4 = 0; s4 < kBcListMax / 4; ++s4) {
+      if (4 * s4 >= a.K) break;
+      const int4 v4 = *(const int4*)(rk + 4 * s4);
+      const int vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = 4 * s4 + e;
+        if (vv[e] < 0) continue;
+        const int pos = w.lbase[(int64_t)bh * w.nbk + blk[s]] + hg[blk[s]] + vv[e];
+        lst[pos] = (uint32_t)r | ((uint32_t)s << 24);
+      }
+    }
+    return;
+  }
   for (int s = 0; s < a.K; ++s) {
     const int v = rk[s];
     if (v < 0) continue;
@@ -253,11 +322,14 @@ struct BcSmem {
 // One work item: up to rpi = 64 / hpg rows that chose block blk of (request,
 // group) bg, for each of the group's hpg query heads: MFMA row q = 16 wv + c16
 // (wave wv, lane column c16) is row q / hpg of the item, head q % hpg.
-__global__ __launch_bounds__(256) void bc_attn_kernel(AttnParams a, BcWs w) {
-  if ((int)blockIdx.x >= *w.nitems) return;
+__global__ __launch_bounds__(256) void bc_attn_kernel(AttnParams a, BcWs w, int xper) {
+  // the items of one block are consecutive, and each XCD takes a run of
+  // items: a block's keys staged by its items come from one XCD's L2
+  const int item = xcd_item(blockIdx.x, xper);
+  if (item >= *w.nitems) return;
   __shared__ __attribute__((aligned(16))) BcSmem sm;
-  const uint32_t bk = w.item_bk[blockIdx.x];
-  const int c = (int)w.item_c[blockIdx.x];
+  const uint32_t bk = w.item_bk[item];
+  const int c = (int)w.item_c[item];
   const int bg = bk / w.nbk, blk = bk % w.nbk;
   const int b = bg / a.G_sel, g = bg % a.G_sel;
   const int kvh = (g * w.hpg) / (a.Hq / a.Hkv);
@@ -403,7 +475,9 @@ __global__ __launch_bounds__(256) void bc_attn_kernel(AttnParams a, BcWs w) {
     }
   }
 
-  // partial (O, m, l) of each row: lane holds dims 16 nt + c16 of rows 4 qq + v of this wave
+  // partial of each row: lane holds dims 16 nt + c16 of rows 4 qq + v of
+  // this wave; O / l in 16-bit fixed point against the row's largest |O / l|
+  // (a maximum over the 16 lanes of the lane's DPP row), then m, l, scale
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int rr = 4 * qq + v;                   // MFMA row within the wave (lane column rr holds its state)
@@ -411,15 +485,26 @@ __global__ __launch_bounds__(256) void bc_attn_kernel(AttnParams a, BcWs w) {
     const float mr = __shfl(m, rr, 64);
     const uint32_t er = (uint32_t)__shfl((int)ent, rr, 64);
     const int hr = __shfl(h, rr, 64);
+    const float il = lr > 0.f ? 1.0f / lr : 0.f;
+    float on[8], mx = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      on[nt] = O[nt][v] * il;
+      mx = fmaxf(mx, fabsf(on[nt]));
+    }
+    mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, mx), 0x128, 0xf, 0xf, false)));
+    mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, mx), 0x124, 0xf, 0xf, false)));
+    mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, mx), 0x122, 0xf, 0xf, false)));
+    mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, mx), 0x121, 0xf, 0xf, false)));
     if ((16 * wid + rr) / w.hpg >= nrow) continue;
     const int rw = (int)(er & 0xFFFFFFu), sw = (int)(er >> 24);
-    float* pp = w.part + ((((int64_t)b * a.Hq + hr) * a.Nq + rw) * a.K + sw) * 130;
+    float* pp = w.part + ((((int64_t)b * a.Hq + hr) * a.Nq + rw) * a.K + sw) * kBcPart;
+    const float sc = mx > 0.f ? mx : 1.f;
+    const float qs = 32767.0f / sc;
+    int16_t* pq = (int16_t*)(pp + 4);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) pp[16 * nt + c16] = O[nt][v];
-    if (c16 == 0) {
-      pp[128] = mr;
-      pp[129] = lr;
-    }
+    for (int nt = 0; nt < 8; ++nt) pq[16 * nt + c16] = (int16_t)__float2int_rn(fminf(fmaxf(on[nt] * qs, -32767.f), 32767.f));
+    if (c16 == 0) *(f32x4*)pp = (f32x4){mr, lr, sc, 0.f};
   }
 }
 
@@ -428,7 +513,7 @@ __global__ __launch_bounds__(256) void bc_attn_kernel(AttnParams a, BcWs w) {
 // loaded by one thread per slot, the output columns by one thread per column
 // with 16 slots' loads in flight
 __global__ __launch_bounds__(256) void bc_combine_kernel(AttnParams a, BcWs w) {
-  __shared__ float sm_m[2][256], sm_l[2][256];
+  __shared__ float sm_m[2][256], sm_l[2][256], sm_s[2][256];
   const int half = threadIdx.x >> 7;
   const int64_t row = (int64_t)blockIdx.x * 2 + half;
   const int dd = threadIdx.x & 127;
@@ -439,14 +524,16 @@ __global__ __launch_bounds__(256) void bc_combine_kernel(AttnParams a, BcWs w) {
   const int64_t grow = live ? ((row / a.Nq / a.Hq) * a.G_sel + (row / a.Nq % a.Hq) / w.hpg) * a.Nq + row % a.Nq : 0;
   if (live)
     for (int s = dd; s < K; s += 128) {
-      float ms = -INFINITY, ls = 0.f;
+      float ms = -INFINITY, ls = 0.f, ss = 0.f;
       if (w.rank[grow * K + s] >= 0) {
-        const float* pp = w.part + (row * K + s) * 130;
-        ms = pp[128];
-        ls = pp[129];
+        const f32x4 hd = *(const f32x4*)(w.part + (row * K + s) * kBcPart);
+        ms = hd[0];
+        ls = hd[1];
+        ss = hd[2] * (1.0f / 32767.0f);
       }
       sm_m[half][s] = ms;
       sm_l[half][s] = ls;
+      sm_s[half][s] = ss;
     }
   __syncthreads();
   if (!live) return;
@@ -465,22 +552,21 @@ __global__ __launch_bounds__(256) void bc_combine_kernel(AttnParams a, BcWs w) {
       Ls = f;
       Os = o[dd] * f;
     }
-    const float* base = w.part + row * K * 130 + dd;
+    // a partial holds O / l: its weight is l e^(m - M)
+    const int16_t* base = (const int16_t*)(w.part + row * K * kBcPart + 4) + dd;
     for (int s0 = 0; s0 < K; s0 += 16) {
+      // every slot's value is loaded (an int16 is always finite; a slot
+      // that does not contribute gets weight 0), so the 16 loads are in
+      // flight together
       float x[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int s = s0 + u;
-        x[u] = (s < K && sm_m[half][s] > -INFINITY) ? base[(int64_t)s * 130] : 0.f;
-      }
+      for (int u = 0; u < 16; ++u) x[u] = (float)base[(int64_t)min(s0 + u, K - 1) * (2 * kBcPart)];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int s = s0 + u;
-        if (s < K && sm_m[half][s] > -INFINITY) {
-          const float f = exp2f(sm_m[half][s] - M);
-          Ls += sm_l[half][s] * f;
-          Os += x[u] * f;
-        }
+        const float f = (s < K && sm_m[half][s] > -INFINITY) ? exp2f(sm_m[half][s] - M) * sm_l[half][s] : 0.f;
+        Ls += f;
+        Os += x[u] * sm_s[half][s < K ? s : 0] * f;
       }
     }
   }
@@ -499,7 +585,8 @@ hipError_t launch_attn_blocks(const AttnParams& a0, hipStream_t st) {
   hipLaunchKernelGGL(bc_scan_kernel, dim3(bg), dim3(256), 0, st, a, w);
   hipLaunchKernelGGL(bc_table_kernel, dim3(bg), dim3(256), 0, st, a, w);
   hipLaunchKernelGGL(bc_scatter_kernel, gc, dim3(kBcRows), 0, st, a, w);
-  hipLaunchKernelGGL(bc_attn_kernel, dim3(w.maxitems), dim3(256), 0, st, a, w);
+  const int per = (w.maxitems + 7) / 8;
+  hipLaunchKernelGGL(bc_attn_kernel, dim3(8 * per), dim3(256), 0, st, a, w, per);
   // window part: the tiled kernel, its LSE into the workspace
   AttnParams aw = a;
   aw.mode = 2;

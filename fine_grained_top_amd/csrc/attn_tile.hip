@@ -44,9 +44,14 @@ struct TileSmem {
 // P_lo V_lo is below 2^-16 of the product), so the entries keep ~16
 // significant bits instead of bf16's 8.
 template <bool STRIDE, bool SPLIT>
-__global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a) {
+__global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a, int xper) {
   __shared__ __attribute__((aligned(16))) TileSmem<SPLIT> sm;
-  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // query tiles of a head are consecutive items, and each XCD takes a run of
+  // them: the key tiles that neighbouring query tiles share stay in its L2
+  const int nqt = (a.Nq + kTQ - 1) / kTQ;
+  const int item = xcd_item(blockIdx.x, xper);
+  if (item >= nqt * a.Hq * a.B) return;
+  const int qt = item % nqt, h = (item / nqt) % a.Hq, b = item / (nqt * a.Hq);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int qq = lane >> 4, c16 = lane & 15;
   const int kvh = h / (a.Hq / a.Hkv);
@@ -351,10 +356,12 @@ bool attn_tile_ok(const AttnParams& a) {
 }
 
 hipError_t launch_attn_tile(const AttnParams& a, hipStream_t st) {
-  dim3 grid((a.Nq + kTQ - 1) / kTQ, a.Hq, a.B);
-  if (a.mode == 2 && a.stride > 0) hipLaunchKernelGGL((attn_tile_kernel<true, false>), grid, dim3(256), 0, st, a);
-  else if (a.mode == 5 && a.klo) hipLaunchKernelGGL((attn_tile_kernel<false, true>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((attn_tile_kernel<false, false>), grid, dim3(256), 0, st, a);
+  const int items = (a.Nq + kTQ - 1) / kTQ * a.Hq * a.B;
+  const int per = (items + 7) / 8;
+  const dim3 grid(8 * per);
+  if (a.mode == 2 && a.stride > 0) hipLaunchKernelGGL((attn_tile_kernel<true, false>), grid, dim3(256), 0, st, a, per);
+  else if (a.mode == 5 && a.klo) hipLaunchKernelGGL((attn_tile_kernel<false, true>), grid, dim3(256), 0, st, a, per);
+  else hipLaunchKernelGGL((attn_tile_kernel<false, false>), grid, dim3(256), 0, st, a, per);
   return hipGetLastError();
 }
 

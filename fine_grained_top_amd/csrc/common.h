@@ -15,6 +15,13 @@ namespace sp {
 
 constexpr int kWave = 64;
 
+// Workgroup id -> work item such that each of the 8 XCDs (workgroups go to
+// them round-robin by id) takes a contiguous range of items, so that
+// neighbouring items, which read the same data, meet in one XCD's L2. The
+// grid holds 8 * per workgroups, per = ceil(items / 8); ids that map past
+// the last item have nothing to do.
+SP_DEV int xcd_item(int wg, int per) { return (wg & 7) * per + (wg >> 3); }
+
 SP_DEV float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
 // float -> bf16 bits, round to nearest even (finite inputs).
