@@ -140,10 +140,12 @@ def algorithmic(wl, inp, hp, fused):
                             "bound": "mfma" if wl.stride else "hbm"}
         if wl.backward:
             # q, k, v, O, dO read once; dq, dk, dv written once; five products of 2 flops per
-            # (pair, dim): s = q.k, dp = dO.v, dq += ds k, dk += ds q, dv += p dO; computed by
-            # float32 FMAs, so the vector float32 peak bounds it
+            # (pair, dim): s = q.k, dp = dO.v and dq += ds k run on bf16 MFMA (dO and dS as exact
+            # three-part splits), dk += ds q and dv += p dO in float32 FMAs; the float32 part is
+            # priced against the vector peak (the roofline), the MFMA part against the bf16 peak
             gbytes = wl.B * (wl.Hq * wl.Nq * wl.d * (e + 4 + 4 + 4 + 4) + wl.Hkv * wl.N * wl.d * (2 * e + 8))
-            out["attention_bwd"] = {"bytes": gbytes, "flops": 10.0 * pairs * wl.d, "bound": "alu"}
+            out["attention_bwd"] = {"bytes": gbytes, "flops": 4.0 * pairs * wl.d, "bound": "alu",
+                                    "mfma_flops": 6.0 * pairs * wl.d, "all_flops": 10.0 * pairs * wl.d}
     elif wl.kind == "nsa":
         # three branches: pooled entries of complete blocks, the chosen blocks' tokens, the window
         blk = hp.idx.cpu().numpy().astype(np.int64)          # [B, Hq, Nq, nb]
@@ -392,6 +394,10 @@ def main():
                 e["TFLOP_s"] = round(a["flops"] / (ms * 1e-3) / 1e12, 3)
                 vec = a.get("bound") == "alu" or wl.dtype != "bf16"
                 e["mfma_frac" if not vec else "alu_frac"] = round(e["TFLOP_s"] / (F32_PEAK_TFS if vec else MFMA_PEAK_TFS), 4)
+            if a.get("mfma_flops"):
+                e["mfma_part_TFLOP_s"] = round(a["mfma_flops"] / (ms * 1e-3) / 1e12, 3)
+                e["mfma_part_frac"] = round(e["mfma_part_TFLOP_s"] / MFMA_PEAK_TFS, 4)
+                e["all_TFLOP_s"] = round(a["all_flops"] / (ms * 1e-3) / 1e12, 3)
             if a.get("rows"):
                 e["rows_per_s"] = round(a["rows"] / (ms * 1e-3), 1)
         per_stage[name] = e

@@ -252,6 +252,12 @@ __global__ __launch_bounds__(64) void attn_bwd_generic_kernel(AttnParams a, Attn
   if (lane + 64 < a.d) dq[lane + 64] = acc1;
 }
 
+size_t attn_bwd_ws_bytes(const AttnParams& a) {
+  const int ns = attn_bwd_tile_ok(a) ? attn_bwd_slots(a) : 0;
+  if (ns == 0) return 0;
+  return (size_t)a.B * a.Hq * ((a.ctx + 63) / 64) * ns * (64 * 128 * 2) * sizeof(float);
+}
+
 hipError_t launch_attention_bwd(const AttnParams& a, const AttnBwd& g, hipStream_t st) {
   hipLaunchKernelGGL(attn_bwd_zero_kernel, dim3(a.ctx, a.Hkv, a.B), dim3(128), 0, st, a, g);
   hipError_t e = hipGetLastError();

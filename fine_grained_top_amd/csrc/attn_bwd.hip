@@ -12,7 +12,11 @@
 //   dQ += dS K on the same MFMA (dS as three bf16 parts, K read transposed
 //   from an XOR-swizzled copy), kept in registers across key tiles;
 //   dK = dS^T Q and dV = P^T dO in float32 FMAs from LDS (4 keys x 8 dims per
-//   thread), the query tile's share added with one float atomic per element.
+//   thread). The query tile's share of a key tile of the window's band goes
+//   to a slot of its own in the workspace (plain stores) and
+//   attn_bwd_reduce_kernel sums each key tile's slots; the share of a global
+//   tile (seen by every query tile) and, without a workspace or in the dense
+//   pattern, every share is added with one float atomic per element.
 #include "common.h"
 #include "internal.h"
 
@@ -91,10 +95,11 @@ __global__ __launch_bounds__(256) void attn_bwd_tile_kernel(AttnParams a, AttnBw
   }
   // ---- key tiles any row of the tile can see
   const int last_tile = min(ntiles_all - 1, prow_last / kBT);
+  const int gt = a.mode == 0 ? 0 : (min(a.n_global, L) + kBT - 1) / kBT;   // global tiles
+  const int ntc = (a.ctx + kBT - 1) / kBT;
   if (a.mode == 0) {
     for (int t = tid; t <= last_tile; t += 256) atomicOr(&sm.tiles[t >> 5], 1u << (t & 31));
   } else {
-    const int gt = (min(a.n_global, L) + kBT - 1) / kBT;
     const int wt = max(0, prow_first - a.window + 1) / kBT;
     for (int t = tid; t <= last_tile; t += 256)
       if (t < gt || t >= wt) atomicOr(&sm.tiles[t >> 5], 1u << (t & 31));
@@ -250,14 +255,28 @@ __global__ __launch_bounds__(256) void attn_bwd_tile_kernel(AttnParams a, AttnBw
           }
         }
       }
+      const int slot = last_tile - t;
+      if (g.part && t >= gt && slot < g.nslot) {
+        // band tile: this query tile's share into its slot ([key][dim] dK, then dV)
+        float* pp = g.part + ((((int64_t)b * a.Hq + h) * ntc + t) * g.nslot + slot) * (kBT * kBD * 2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = j0 + orow + i;
-        if (j >= L) continue;
+        for (int i = 0; i < 4; ++i) {
+          float* pk = pp + (orow + i) * kBD + odim;
+          *(f32x4*)pk = (f32x4){dk[i][0], dk[i][1], dk[i][2], dk[i][3]};
+          *(f32x4*)(pk + 4) = (f32x4){dk[i][4], dk[i][5], dk[i][6], dk[i][7]};
+          *(f32x4*)(pk + kBT * kBD) = (f32x4){dv[i][0], dv[i][1], dv[i][2], dv[i][3]};
+          *(f32x4*)(pk + kBT * kBD + 4) = (f32x4){dv[i][4], dv[i][5], dv[i][6], dv[i][7]};
+        }
+      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (dk[i][e] != 0.f) atomicAdd(&dkb[(int64_t)j * g.dks[2] + odim + e], dk[i][e]);
-          if (dv[i][e] != 0.f) atomicAdd(&dvb[(int64_t)j * g.dvs[2] + odim + e], dv[i][e]);
+        for (int i = 0; i < 4; ++i) {
+          const int j = j0 + orow + i;
+          if (j >= L) continue;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (dk[i][e] != 0.f) atomicAdd(&dkb[(int64_t)j * g.dks[2] + odim + e], dk[i][e]);
+            if (dv[i][e] != 0.f) atomicAdd(&dvb[(int64_t)j * g.dvs[2] + odim + e], dv[i][e]);
+          }
         }
       }
       __syncthreads();
@@ -274,6 +293,79 @@ __global__ __launch_bounds__(256) void attn_bwd_tile_kernel(AttnParams a, AttnBw
   }
 }
 
+// Sums the slots of one band key tile: workgroup (t, quarter) x (KV head,
+// request) takes 16 keys x 128 dims of dK and dV; the (query head, query
+// tile) pairs that wrote a slot for tile t follow from the same tile sets as
+// in the tile kernel and are listed in LDS, then read four at a time with
+// every load of a batch in flight together.
+__global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(AttnParams a, AttnBwd g) {
+  __shared__ uint32_t lst[1024];
+  __shared__ uint32_t nl;
+  const int t = blockIdx.x >> 2, quarter = blockIdx.x & 3, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int L = min(a.ctx_len ? a.ctx_len[b] : a.ctx, a.ctx);
+  const int ntiles_all = (L + kBT - 1) / kBT;
+  const int gt = (min(a.n_global, L) + kBT - 1) / kBT;
+  if (t >= ntiles_all || t < gt) return;
+  const int pbase = L - a.Nq, nqt = (a.Nq + kBT - 1) / kBT, G = a.Hq / a.Hkv;
+  const int ntc = (a.ctx + kBT - 1) / kBT;
+  if (tid == 0) nl = 0u;
+  __syncthreads();
+  for (int e = tid; e < G * nqt; e += 256) {
+    const int hq = kvh * G + e / nqt, qt = e % nqt;
+    const int q0 = qt * kBT, nrows = min(kBT, a.Nq - q0);
+    const int prow_first = pbase + q0, prow_last = prow_first + nrows - 1;
+    const int last_tile = min(ntiles_all - 1, prow_last / kBT);
+    const int wt = max(0, prow_first - a.window + 1) / kBT;
+    const int slot = last_tile - t;
+    if (prow_last >= 0 && t >= wt && t <= last_tile && slot < g.nslot) {
+      const uint32_t x = atomicAdd(&nl, 1u);
+      if (x < 1024u) lst[x] = (uint32_t)(((hq * ntc + t) * g.nslot + slot));
+    }
+  }
+  __syncthreads();
+  const int n = (int)min(nl, 1024u);
+  if (n == 0) return;
+  // thread: key 16 quarter + tid / 16, dims 8 (tid % 16) .. +7 of dK and of dV
+  const int kr = 16 * quarter + (tid >> 4), dd = 8 * (tid & 15);
+  const int64_t base = (int64_t)b * a.Hq * ntc * g.nslot;
+  f32x4 ak0 = {0.f, 0.f, 0.f, 0.f}, ak1 = ak0, av0 = ak0, av1 = ak0;
+  for (int i = 0; i < n; i += 4) {
+    f32x4 x[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float* pp = g.part + (base + lst[min(i + u, n - 1)]) * (kBT * kBD * 2) + kr * kBD + dd;
+      x[u][0] = *(const f32x4*)pp;
+      x[u][1] = *(const f32x4*)(pp + 4);
+      x[u][2] = *(const f32x4*)(pp + kBT * kBD);
+      x[u][3] = *(const f32x4*)(pp + kBT * kBD + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float wu = i + u < n ? 1.f : 0.f;   // past the list: loaded again, weight 0
+      ak0 += x[u][0] * wu;
+      ak1 += x[u][1] * wu;
+      av0 += x[u][2] * wu;
+      av1 += x[u][3] * wu;
+    }
+  }
+  const int j = t * kBT + kr;
+  if (j >= L) return;
+  float* dkr = g.dk + b * g.dks[0] + kvh * g.dks[1] + (int64_t)j * g.dks[2] + dd;
+  float* dvr = g.dv + b * g.dvs[0] + kvh * g.dvs[1] + (int64_t)j * g.dvs[2] + dd;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    dkr[e] = ak0[e];
+    dkr[4 + e] = ak1[e];
+    dvr[e] = av0[e];
+    dvr[4 + e] = av1[e];
+  }
+}
+
+// slots per band key tile: the band of a query tile spans at most
+// window / 64 + 3 key tiles (a query tile need not start on a key tile)
+int attn_bwd_slots(const AttnParams& a) { return a.mode == 2 && a.stride == 0 ? a.window / kBT + 3 : 0; }
+
 bool attn_bwd_tile_ok(const AttnParams& a) {
   return a.q.dt == DT_BF16 && a.d == kBD && !a.ptab && (a.mode == 0 || (a.mode == 2 && a.stride == 0)) &&
          (a.ctx + kBT - 1) / kBT <= 2048;
@@ -282,6 +374,9 @@ bool attn_bwd_tile_ok(const AttnParams& a) {
 hipError_t launch_attn_bwd_tile(const AttnParams& a, const AttnBwd& g, hipStream_t st) {
   dim3 grid((a.Nq + kBT - 1) / kBT, a.Hq, a.B);
   hipLaunchKernelGGL(attn_bwd_tile_kernel, grid, dim3(256), 0, st, a, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !g.part) return e;
+  hipLaunchKernelGGL(attn_bwd_reduce_kernel, dim3(4 * ((a.ctx + kBT - 1) / kBT), a.Hkv, a.B), dim3(256), 0, st, a, g);
   return hipGetLastError();
 }
 

@@ -177,11 +177,19 @@ struct AttnBwd {
   int64_t dks[4];
   float* dv;
   int64_t dvs[4];
+  // window pattern on the tile kernel: each query tile's share of a band key
+  // tile's dK/dV goes to its own slot here ([B][Hq][ctx tiles][nslot][64 keys
+  // x 128 dims x 2], float32) and a reduce kernel sums the slots; null:
+  // float atomics instead
+  float* part;
+  int nslot;
 };
 hipError_t launch_attention_bwd(const AttnParams& a, const AttnBwd& g, hipStream_t st);
+size_t attn_bwd_ws_bytes(const AttnParams& a);
 // tiled backward of the dense and window/global patterns (bf16, d = 128)
 bool attn_bwd_tile_ok(const AttnParams& a);
 hipError_t launch_attn_bwd_tile(const AttnParams& a, const AttnBwd& g, hipStream_t st);
+int attn_bwd_slots(const AttnParams& a);   // slots per band key tile (0: no partials for this pattern)
 // three-branch NSA attention: compression (mode 5 over the pooled blocks),
 // selection (mode 3 without window), window (mode 2), combined by gates
 struct NsaParams {

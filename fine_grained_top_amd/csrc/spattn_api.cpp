@@ -660,6 +660,13 @@ static int attn_setup(const spattn_tensor* q, const spattn_tensor* k, const spat
   return SPATTN_OK;
 }
 
+SPATTN_API size_t spattn_sparse_attn_bwd_workspace(const spattn_tensor* q, const spattn_tensor* k,
+                                                   const spattn_selection* sel) {
+  sp::AttnParams p;
+  if (attn_setup(q, k, nullptr, sel, p, false)) return (size_t)-1;
+  return sp::attn_bwd_ws_bytes(p);
+}
+
 SPATTN_API size_t spattn_sparse_attn_fwd_workspace(const spattn_tensor* q, const spattn_tensor* k,
                                                    const spattn_selection* sel) {
   sp::AttnParams p;
@@ -738,7 +745,7 @@ SPATTN_API int spattn_sparse_attn_bwd(const spattn_tensor* q, const spattn_tenso
                                       const int32_t* ctx_len, float scale, const spattn_selection* sel,
                                       const spattn_tensor* o, const float* lse, const spattn_tensor* d_o,
                                       const spattn_tensor* dq_out, const spattn_tensor* dk_out,
-                                      const spattn_tensor* dv_out, void* stream) {
+                                      const spattn_tensor* dv_out, void* ws, size_t ws_bytes, void* stream) {
   sp::AttnParams p;
   sp::AttnBwd g{};
   int rc;
@@ -758,6 +765,10 @@ SPATTN_API int spattn_sparse_attn_bwd(const spattn_tensor* q, const spattn_tenso
   g.dq = (float*)dq_out->data;
   g.dk = (float*)dk_out->data;
   g.dv = (float*)dv_out->data;
+  const size_t need = sp::attn_bwd_ws_bytes(p);
+  if (ws_bytes < need || (need && !ws)) return fail(SPATTN_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  g.part = need ? (float*)ws : nullptr;
+  g.nslot = need ? sp::attn_bwd_slots(p) : 0;
   for (int i = 0; i < 4; ++i) {
     g.os[i] = o->stride[i];
     g.dos[i] = d_o->stride[i];

@@ -146,6 +146,8 @@ class HotPath:
         if self.wl.kind in ("blocks", "nsa"):
             q.append(S.LIB.spattn_block_select_workspace(byref(tq), byref(tk), self.wl.block_size,
                                                          self.wl.top_blocks))
+        if self.wl.backward:
+            q.append(S.LIB.spattn_sparse_attn_bwd_workspace(byref(tq), byref(tk), byref(self.sel)))
         if self.wl.kind == "nsa":
             q.append(S.LIB.spattn_nsa_fwd_workspace(byref(tq), byref(tk), self.wl.block_size,
                                                     byref(S.tensor(self.idx)), self.wl.window))
@@ -208,7 +210,7 @@ class HotPath:
 
     def attention_bwd(self, stream=None):
         S.spattn_sparse_attn_bwd(self.q, self.k, self.v, self.ctx_len, 0.0, self.sel, self.o, self.lse, self.d_o,
-                                 self.dq, self.dk, self.dv, stream)
+                                 self.dq, self.dk, self.dv, self.ws, stream)
 
     def step(self, stream=None):
         if self.wl.H_I and self.fused and self.wl.kind == "dsa_pages":

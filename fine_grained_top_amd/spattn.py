@@ -81,8 +81,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "spattn_sparse_attn_fwd_paged_workspace": (sz, [P(Tensor), P(Tensor), P(KvPages), P(Selection)]),
         "spattn_sparse_attn_fwd_paged": (ctypes.c_int, [P(Tensor), P(Tensor), P(Tensor), P(KvPages), vp,
                                                         ctypes.c_float, P(Selection), P(Tensor), vp, vp, sz, vp]),
+        "spattn_sparse_attn_bwd_workspace": (sz, [P(Tensor), P(Tensor), P(Selection)]),
         "spattn_sparse_attn_bwd": (ctypes.c_int, [P(Tensor), P(Tensor), P(Tensor), vp, ctypes.c_float, P(Selection),
-                                                  P(Tensor), vp, P(Tensor), P(Tensor), P(Tensor), P(Tensor), vp]),
+                                                  P(Tensor), vp, P(Tensor), P(Tensor), P(Tensor), P(Tensor), vp, sz,
+                                                  vp]),
         "spattn_nsa_fwd_workspace": (sz, [P(Tensor), P(Tensor), i32, P(Tensor), i32]),
         "spattn_nsa_fwd": (ctypes.c_int, [P(Tensor), P(Tensor), P(Tensor), vp, ctypes.c_float, i32, P(Tensor), i32,
                                           P(Tensor), P(Tensor), vp, sz, vp]),
@@ -321,13 +323,20 @@ def spattn_sparse_attn_fwd_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: 
                                             0 if ws is None else ws.numel(), _stream(stream)))
 
 
+def spattn_sparse_attn_bwd_workspace(q: torch.Tensor, k: torch.Tensor, sel: Selection) -> int:
+    tq, tk = tensor(q), tensor(k)
+    return int(LIB.spattn_sparse_attn_bwd_workspace(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(sel)))
+
+
 def spattn_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ctx_len: Optional[torch.Tensor],
                            scale: float, sel: Selection, o: torch.Tensor, lse: torch.Tensor, d_o: torch.Tensor,
-                           dq_out: torch.Tensor, dk_out: torch.Tensor, dv_out: torch.Tensor, stream=None) -> None:
+                           dq_out: torch.Tensor, dk_out: torch.Tensor, dv_out: torch.Tensor,
+                           ws: Optional[torch.Tensor] = None, stream=None) -> None:
     t = [tensor(x) for x in (q, k, v, o, d_o, dq_out, dk_out, dv_out)]
     _check(LIB.spattn_sparse_attn_bwd(ctypes.byref(t[0]), ctypes.byref(t[1]), ctypes.byref(t[2]), _ptr(ctx_len), scale,
                                       ctypes.byref(sel), ctypes.byref(t[3]), _ptr(lse), ctypes.byref(t[4]),
-                                      ctypes.byref(t[5]), ctypes.byref(t[6]), ctypes.byref(t[7]), _stream(stream)))
+                                      ctypes.byref(t[5]), ctypes.byref(t[6]), ctypes.byref(t[7]), _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def spattn_nsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ctx_len: Optional[torch.Tensor], scale: float,

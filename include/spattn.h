@@ -391,14 +391,24 @@ SPATTN_API int spattn_sparse_attn_fwd_paged(const spattn_tensor* q, const spattn
  *     every selection mode); o f32 [B, H_q, Nq, d] and lse f32 [B, H_q, Nq]:
  *     the forward's outputs; d_o, dq_out f32 [B, H_q, Nq, d];
  *     dk_out, dv_out f32 [B, H_kv, ctx, d] (overwritten).
- *  float32 arithmetic; dk/dv are accumulated with float atomics, so their
- *  low bits depend on the order in which rows finish. No workspace.
+ *  ws, ws_bytes: device workspace of at least
+ *     spattn_sparse_attn_bwd_workspace(q, k, sel) bytes (caller-owned, no
+ *     initial contents needed; null with 0 when that is 0). The window
+ *     pattern (WINDOW_GLOBAL without stride, bf16, d = 128) needs one slot
+ *     of 64 keys x 128 dims x 2 floats per (request, query head, key tile,
+ *     band position): each query tile writes its share of a band key tile's
+ *     dK/dV to its slot and a second kernel sums them; every other case
+ *     needs none. SPATTN_ERR_WORKSPACE if it is too small (nothing launched).
+ *  float32 arithmetic; the other shares of dk/dv are accumulated with float
+ *  atomics, so their low bits depend on the order in which rows finish.
  * ---------------------------------------------------------------------- */
+SPATTN_API size_t spattn_sparse_attn_bwd_workspace(const spattn_tensor* q, const spattn_tensor* k,
+                                                   const spattn_selection* sel);
 SPATTN_API int spattn_sparse_attn_bwd(const spattn_tensor* q, const spattn_tensor* k, const spattn_tensor* v,
                                       const int32_t* ctx_len, float scale, const spattn_selection* sel,
                                       const spattn_tensor* o, const float* lse, const spattn_tensor* d_o,
                                       const spattn_tensor* dq_out, const spattn_tensor* dk_out,
-                                      const spattn_tensor* dv_out, void* stream);
+                                      const spattn_tensor* dv_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * spattn_nsa_fwd — three-branch NSA attention.

@@ -286,10 +286,24 @@ def test_backward_validation():
         return S.LIB.spattn_sparse_attn_bwd(ctypes.byref(t[0]), ctypes.byref(t[1]), ctypes.byref(t[2]), None, 0.0,
                                             ctypes.byref(sel), ctypes.byref(t[3]), None if lp is None else lp.data_ptr(),
                                             ctypes.byref(t[4]), ctypes.byref(t[5]), ctypes.byref(t[6]),
-                                            ctypes.byref(t[7]), None)
+                                            ctypes.byref(t[7]), None, 0, None)
 
     assert call() == 4
     assert call(S.selection(S.SEL_WINDOW_GLOBAL, window=4, stride=2)) == 4
+    # window pattern on the bf16 tile path: a workspace of slots per band key tile
+    qb = torch.zeros(1, 4, 200, 128, dtype=torch.bfloat16)
+    kb = torch.zeros(1, 2, 200, 128, dtype=torch.bfloat16)
+    selw = S.selection(S.SEL_WINDOW_GLOBAL, window=100, n_global=3)
+    need = S.spattn_sparse_attn_bwd_workspace(qb, kb, selw)
+    assert need == 1 * 4 * 4 * (100 // 64 + 3) * 64 * 128 * 2 * 4    # B * Hq * key tiles * slots * slot bytes
+    assert S.spattn_sparse_attn_bwd_workspace(qb, kb, S.selection(S.SEL_DENSE)) == 0
+    tb = [S.tensor(x) for x in (qb, kb, kb, torch.zeros(1, 4, 200, 128), torch.zeros(1, 4, 200, 128),
+                                torch.zeros(1, 4, 200, 128), torch.zeros(1, 2, 200, 128), torch.zeros(1, 2, 200, 128))]
+    lsew = torch.zeros(1, 4, 200)
+    rc = S.LIB.spattn_sparse_attn_bwd(ctypes.byref(tb[0]), ctypes.byref(tb[1]), ctypes.byref(tb[2]), None, 0.0,
+                                      ctypes.byref(selw), ctypes.byref(tb[3]), lsew.data_ptr(), ctypes.byref(tb[4]),
+                                      ctypes.byref(tb[5]), ctypes.byref(tb[6]), ctypes.byref(tb[7]), None, 0, None)
+    assert rc == 3                                                # workspace too small, before any device use
     assert call(lp=None) == 1                                     # the forward's LSE is required
     assert call(oo=torch.zeros(1, 4, 8, 64)) == 1
     assert call(dkk=torch.zeros(1, 2, 16, 128, dtype=torch.bfloat16)) == 1

@@ -993,7 +993,10 @@ def test_attention_backward(mode, dtype):
     dq = torch.empty(B, Hq, Nq, d, device="cuda")
     dk = torch.full((B, Hkv, ctx, d), float("nan"), device="cuda")
     dv = torch.full((B, Hkv, ctx, d), float("nan"), device="cuda")
-    sp.spattn_sparse_attn_bwd(qd, kd, vd, cl, 0.0, sel, o, lse, dOd, dq, dk, dv)
+    # workspace filled with NaN: a slot the reduce reads but nobody wrote would show
+    nws = sp.spattn_sparse_attn_bwd_workspace(qd, kd, sel)
+    ws = torch.full((nws,), 0xFF, dtype=torch.uint8, device="cuda") if nws else None
+    sp.spattn_sparse_attn_bwd(qd, kd, vd, cl, 0.0, sel, o, lse, dOd, dq, dk, dv, ws)
     torch.cuda.synchronize()
     rq, rk, rv = _grads_oracle(q.double().numpy(), k.double().numpy(), v.double().numpy(), dO.double().numpy(),
                                sets, ctx_len, Nq, 1.0 / math.sqrt(d))
