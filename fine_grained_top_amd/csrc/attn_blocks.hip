@@ -287,22 +287,29 @@ __global__ __launch_bounds__(kBcRows) void bc_scatter_kernel(AttnParams a, BcWs 
   const int32_t* rk = w.rank + ((int64_t)bh * a.Nq + r) * a.K;
   const int32_t* hg = w.hist + ((int64_t)bh * w.nch + ch) * w.nbk;
   uint32_t* lst = w.list + (int64_t)bh * a.Nq * a.K;
-  if (a.K <= kBcListMax && (a.K & 3) == 0) {
-    int blk[kBcListMax];
+  if (a.K <= 16 && (a.K & 3) == 0) {
+    // the row's list and ranks, then every slot's list base and chunk offset
+    // loaded together (index clamped for slots that do not contribute)
+    int blk[kBcListMax], vv[16], lb[16], ho[16];
     bc_load_list(a, sel, blk);
 #pragma unroll
-    for (int s4 = 0; s4 < kBcListMax / 4; ++s4) {
-      if (4 * s4 >= a.K) break;
-      const int4 v4 = *(const int4*)(rk + 4 * s4);
-      const int vv[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int s = 4 * s4 + e;
-        if (vv[e] < 0) continue;
-        const int pos = w.lbase[(int64_t)bh * w.nbk + blk[s]] + hg[blk[s]] + vv[e];
-        lst[pos] = (uint32_t)r | ((uint32_t)s << 24);
-      }
+    for (int s4 = 0; s4 < 4; ++s4) {
+      int4 v4 = make_int4(-1, -1, -1, -1);
+      if (4 * s4 < a.K) v4 = *(const int4*)(rk + 4 * s4);
+      vv[4 * s4] = v4.x;
+      vv[4 * s4 + 1] = v4.y;
+      vv[4 * s4 + 2] = v4.z;
+      vv[4 * s4 + 3] = v4.w;
     }
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int bb = vv[s] >= 0 ? blk[s] : 0;
+      lb[s] = w.lbase[(int64_t)bh * w.nbk + bb];
+      ho[s] = hg[bb];
+    }
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      if (vv[s] >= 0) lst[lb[s] + ho[s] + vv[s]] = (uint32_t)r | ((uint32_t)s << 24);
     return;
   }
   for (int s = 0; s < a.K; ++s) {
@@ -508,70 +515,81 @@ __global__ __launch_bounds__(256) void bc_attn_kernel(AttnParams a, BcWs w, int 
   }
 }
 
-// per row (128 threads, two rows per workgroup): merge the window part (O
-// normalized, LSE) with the block partials; the partials' statistics are
-// loaded by one thread per slot, the output columns by one thread per column
-// with 16 slots' loads in flight
+// per row (16 threads, 16 rows per workgroup): merge the window part (O
+// normalized, LSE) with the block partials. Thread part of a row loads the
+// header (m, l, scale) and the rank of slots part, part + 16, ... into LDS;
+// then each thread takes 8 dims of every slot with one 16-byte load per
+// slot, all of a row's slots in flight together.
+constexpr int kBcCombRows = 16;
 __global__ __launch_bounds__(256) void bc_combine_kernel(AttnParams a, BcWs w) {
-  __shared__ float sm_m[2][256], sm_l[2][256], sm_s[2][256];
-  const int half = threadIdx.x >> 7;
-  const int64_t row = (int64_t)blockIdx.x * 2 + half;
-  const int dd = threadIdx.x & 127;
+  __shared__ float sm_m[kBcCombRows][256], sm_w[kBcCombRows][256], sm_s[kBcCombRows][256];
+  const int rl = threadIdx.x >> 4, part = threadIdx.x & 15;
+  const int64_t row = (int64_t)blockIdx.x * kBcCombRows + rl;
   const int64_t nrows = (int64_t)a.B * a.Hq * a.Nq;
   const bool live = row < nrows;
   const int K = a.K;
   // the row's group list ranks: row = ((b Hq + h) Nq + r), group g = h / hpg
   const int64_t grow = live ? ((row / a.Nq / a.Hq) * a.G_sel + (row / a.Nq % a.Hq) / w.hpg) * a.Nq + row % a.Nq : 0;
+  const float lw = live ? w.lse_w[row] : -INFINITY;   // with the headers: one round of loads
   if (live)
-    for (int s = dd; s < K; s += 128) {
-      float ms = -INFINITY, ls = 0.f, ss = 0.f;
-      if (w.rank[grow * K + s] >= 0) {
-        const f32x4 hd = *(const f32x4*)(w.part + (row * K + s) * kBcPart);
-        ms = hd[0];
-        ls = hd[1];
-        ss = hd[2] * (1.0f / 32767.0f);
-      }
-      sm_m[half][s] = ms;
-      sm_l[half][s] = ls;
-      sm_s[half][s] = ss;
+    for (int s = part; s < K; s += 16) {
+      // rank and header loaded together (a header of a slot that does not
+      // contribute is read but not used)
+      const int rk = w.rank[grow * K + s];
+      const f32x4 hd = *(const f32x4*)(w.part + (row * K + s) * kBcPart);
+      const bool c = rk >= 0;
+      const float ms = c ? hd[0] : -INFINITY, ls = c ? hd[1] : 0.f, ss = c ? hd[2] * (1.0f / 32767.0f) : 0.f;
+      sm_m[rl][s] = ms;
+      sm_w[rl][s] = ls;              // l, then the weight once M is known
+      sm_s[rl][s] = ss;              // scale / 32767
     }
   __syncthreads();
   if (!live) return;
   const int r = (int)(row % a.Nq), bh = (int)(row / a.Nq);
   const int h = bh % a.Hq, b = bh / a.Hq;
-  float* o = a.o + b * a.os[0] + h * a.os[1] + (int64_t)r * a.os[2];
-  const float lw = w.lse_w[row];
+  float* o = a.o + b * a.os[0] + h * a.os[1] + (int64_t)r * a.os[2] + 8 * part;
   // window part as (m, l, O) in base-2 units: m = LSE / ln 2, l = 1, O normalized
   const float mw = lw > -INFINITY ? lw * kBcLog2e : -INFINITY;
   float M = mw;
-  for (int s = 0; s < K; ++s) M = fmaxf(M, sm_m[half][s]);
-  float Ls = 0.f, Os = 0.f;
+  for (int s = 0; s < K; ++s) M = fmaxf(M, sm_m[rl][s]);
+  float Ls = 0.f, Os[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (M > -INFINITY) {
-    if (mw > -INFINITY) {
-      const float f = exp2f(mw - M);
-      Ls = f;
-      Os = o[dd] * f;
-    }
-    // a partial holds O / l: its weight is l e^(m - M)
-    const int16_t* base = (const int16_t*)(w.part + row * K * kBcPart + 4) + dd;
+    // a partial holds O / l: its weight is l e^(m - M); every slot's values
+    // are loaded (an int16 is always finite; a slot that does not contribute
+    // gets weight 0), and the window part's output after the first slots'
+    const char* base = (const char*)(w.part + row * K * kBcPart + 4) + 16 * part;
     for (int s0 = 0; s0 < K; s0 += 16) {
-      // every slot's value is loaded (an int16 is always finite; a slot
-      // that does not contribute gets weight 0), so the 16 loads are in
-      // flight together
-      float x[16];
+      u32x4 x[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) x[u] = (float)base[(int64_t)min(s0 + u, K - 1) * (2 * kBcPart)];
+      for (int u = 0; u < 16; ++u) x[u] = *(const u32x4*)(base + (int64_t)min(s0 + u, K - 1) * (4 * kBcPart));
+      if (s0 == 0) {
+        float ov[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ov[e] = o[e];
+        const float f = mw > -INFINITY ? exp2f(mw - M) : 0.f;
+        Ls = f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Os[e] = f > 0.f ? ov[e] * f : 0.f;
+      }
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int s = s0 + u;
-        const float f = (s < K && sm_m[half][s] > -INFINITY) ? exp2f(sm_m[half][s] - M) * sm_l[half][s] : 0.f;
+        const bool c = s < K && sm_m[rl][s < K ? s : 0] > -INFINITY;
+        const float f = c ? exp2f(sm_m[rl][s] - M) * sm_w[rl][s] : 0.f;
+        const float fs = c ? f * sm_s[rl][s] : 0.f;
         Ls += f;
-        Os += x[u] * sm_s[half][s < K ? s : 0] * f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Os[2 * e] += (float)(int16_t)(x[u][e] & 0xFFFFu) * fs;
+          Os[2 * e + 1] += (float)(int16_t)(x[u][e] >> 16) * fs;
+        }
       }
     }
   }
-  o[dd] = Ls > 0.f ? Os / Ls : 0.f;
-  if (a.lse && dd == 0) a.lse[row] = Ls > 0.f ? (M + log2f(Ls)) * kBcLn2 : -INFINITY;
+  const float il = Ls > 0.f ? 1.0f / Ls : 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = Os[e] * il;
+  if (a.lse && part == 0) a.lse[row] = Ls > 0.f ? (M + log2f(Ls)) * kBcLn2 : -INFINITY;
 }
 
 hipError_t launch_attn_blocks(const AttnParams& a0, hipStream_t st) {
@@ -595,7 +613,8 @@ hipError_t launch_attn_blocks(const AttnParams& a0, hipStream_t st) {
   hipError_t e = launch_attn_tile(aw, st);
   if (e != hipSuccess) return e;
   const int64_t nrows = (int64_t)bh * a.Nq;
-  hipLaunchKernelGGL(bc_combine_kernel, dim3((unsigned)((nrows + 1) / 2)), dim3(256), 0, st, a, w);
+  hipLaunchKernelGGL(bc_combine_kernel, dim3((unsigned)((nrows + kBcCombRows - 1) / kBcCombRows)), dim3(256), 0, st, a,
+                     w);
   return hipGetLastError();
 }
 
