@@ -43,7 +43,9 @@ struct TileSmem {
 // klo/vlo): S = K_hi Q^T + K_lo Q^T and O += P V_hi + P_hi V_lo (the term
 // P_lo V_lo is below 2^-16 of the product), so the entries keep ~16
 // significant bits instead of bf16's 8.
-template <bool STRIDE, bool SPLIT>
+// MODE: the selection mode, fixed per instance so that the per-element masks
+// carry no tests of other modes.
+template <int MODE, bool STRIDE, bool SPLIT>
 __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a, int xper) {
   __shared__ __attribute__((aligned(16))) TileSmem<SPLIT> sm;
   // query tiles of a head are consecutive items, and each XCD takes a run of
@@ -62,17 +64,17 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a, int xper) 
   const int prow_last = pbase + min(q0 + kTQ, a.Nq) - 1;
   // mode 5 (compressed entries): key rows are the request's complete blocks,
   // entry c visible at position p when c <= (p + 1) / bs - 1
-  const int Lk = a.mode == 5 ? L / a.bs : L;
+  const int Lk = MODE == 5 ? L / a.bs : L;
   const int ntiles_all = (Lk + kTK - 1) / kTK;
-  const int nbk = a.mode == 3 ? (a.ctx + a.bs - 1) / a.bs : 0;
+  const int nbk = MODE == 3 ? (a.ctx + a.bs - 1) / a.bs : 0;
   const int bwords = (nbk + 31) >> 5;
 
   // ---- tile set of this query tile
   for (int i = tid; i < 64; i += 256) sm.tiles[i] = 0;
-  if (a.mode == 3)
+  if (MODE == 3)
     for (int i = tid; i < kTQ * bwords; i += 256) sm.rowblk[i] = 0;
   __syncthreads();
-  const int plast_v = a.mode == 5 ? (prow_last + 1) / a.bs - 1 : prow_last;
+  const int plast_v = MODE == 5 ? (prow_last + 1) / a.bs - 1 : prow_last;
   const int last_tile = plast_v >= 0 ? min(ntiles_all - 1, plast_v / kTK) : -1;
   // dilated stride: multiples m * stride, m in [m_lo, m_hi], below the latest
   // window start of the tile and outside the global prefix, as nvt virtual
@@ -85,9 +87,9 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a, int xper) 
     const int m_hi = (prow_last - a.window) / sd;
     if (m_hi >= m_lo) nvt = (m_hi - m_lo + kTK) / kTK;
   }
-  if (a.mode == 0 || a.mode == 5) {
+  if (MODE == 0 || MODE == 5) {
     for (int t = tid; t <= last_tile; t += 256) atomicOr(&sm.tiles[t >> 5], 1u << (t & 31));
-  } else if (a.mode == 2) {
+  } else if (MODE == 2) {
     const int gt = (min(a.n_global, L) + kTK - 1) / kTK;
     const int wt = max(0, prow_first - a.window + 1) / kTK;
     for (int t = tid; t <= last_tile; t += 256)
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a, int xper) 
   const int rq = q0 + rloc;
   const bool rvalid = rq < a.Nq;
   const int prow = pbase + rq;
-  const int prow_v = a.mode == 5 ? (prow + 1) / a.bs - 1 : prow;   // last visible key row
+  const int prow_v = MODE == 5 ? (prow + 1) / a.bs - 1 : prow;   // last visible key row
   const int wstart = prow - a.window + 1;
   bf16x8 Qb[4];
   if (rvalid) {
@@ -195,8 +197,8 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a, int xper) 
     // does any row of this wave see this tile?
     bool see = rvalid && prow_v >= j0;
     if (sv) see = rvalid && mb0 * sd <= prow && mb0 * sd < wstart;
-    else if (see && a.mode == 2) see = (j0 + kTK - 1 >= wstart) || (j0 < a.n_global);
-    if (see && a.mode == 3) {
+    else if (see && MODE == 2) see = (j0 + kTK - 1 >= wstart) || (j0 < a.n_global);
+    if (see && MODE == 3) {
       bool any = j0 + kTK - 1 >= wstart;
       if (!any) {
         const int b0 = j0 / a.bs, b1 = min(nbk - 1, (j0 + kTK - 1) / a.bs);
@@ -233,8 +235,8 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a, int xper) 
           for (int v = 0; v < 4; ++v) {
             const int j = j0 + 16 * st + 4 * qq + v;
             bool vis = rvalid && j <= prow_v;
-            if (vis && a.mode == 2) vis = j >= wstart || j < a.n_global;
-            if (vis && a.mode == 3) {
+            if (vis && MODE == 2) vis = j >= wstart || j < a.n_global;
+            if (vis && MODE == 3) {
               const int bb = j / a.bs;
               vis = j >= wstart || ((sm.rowblk[rloc * bwords + (bb >> 5)] >> (bb & 31)) & 1u);
             }
@@ -359,9 +361,12 @@ hipError_t launch_attn_tile(const AttnParams& a, hipStream_t st) {
   const int items = (a.Nq + kTQ - 1) / kTQ * a.Hq * a.B;
   const int per = (items + 7) / 8;
   const dim3 grid(8 * per);
-  if (a.mode == 2 && a.stride > 0) hipLaunchKernelGGL((attn_tile_kernel<true, false>), grid, dim3(256), 0, st, a, per);
-  else if (a.mode == 5 && a.klo) hipLaunchKernelGGL((attn_tile_kernel<false, true>), grid, dim3(256), 0, st, a, per);
-  else hipLaunchKernelGGL((attn_tile_kernel<false, false>), grid, dim3(256), 0, st, a, per);
+  if (a.mode == 2 && a.stride > 0) hipLaunchKernelGGL((attn_tile_kernel<2, true, false>), grid, dim3(256), 0, st, a, per);
+  else if (a.mode == 2) hipLaunchKernelGGL((attn_tile_kernel<2, false, false>), grid, dim3(256), 0, st, a, per);
+  else if (a.mode == 5 && a.klo) hipLaunchKernelGGL((attn_tile_kernel<5, false, true>), grid, dim3(256), 0, st, a, per);
+  else if (a.mode == 5) hipLaunchKernelGGL((attn_tile_kernel<5, false, false>), grid, dim3(256), 0, st, a, per);
+  else if (a.mode == 3) hipLaunchKernelGGL((attn_tile_kernel<3, false, false>), grid, dim3(256), 0, st, a, per);
+  else hipLaunchKernelGGL((attn_tile_kernel<0, false, false>), grid, dim3(256), 0, st, a, per);
   return hipGetLastError();
 }
 
