@@ -37,8 +37,9 @@ SP_DEV float load_val(const void* p, int dt, int64_t i) {
 // order, the key bytes of tile t + PD requested as tile t is scored, so the
 // loads of a workgroup stream while it computes (PD = CPW * 4: all at once).
 // RL (filter, one selection group): survivors go to per-row lists, staged in
-// LDS per row of the workgroup and written out after every second tile with
-// one global atomic per row that has any.
+// LDS per (row, wave) and moved out by each wave on its own (one global
+// reservation per row with entries) when a region could overflow, and at the
+// wave's end.
 template <int KT, int NMB, int HPG, bool RELU, int MODE, int CPW, int PD, bool RL = false>
 __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
   constexpr bool FILTER = MODE == 1;
@@ -97,15 +98,19 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
   }
 
   __shared__ uint32_t lcount[FILTER ? CPW : 1][128];
-  // RL: the survivors of two tiles per wave (256 keys) of each row of the
-  // workgroup fit their row's stage whatever the rate, so the stage is
-  // flushed after every second tile and never overflows
-  constexpr int kRlTiles = 2;
+  // RL: every (row, wave) pair owns a stage region of two tiles' keys (a
+  // tile adds at most 32 entries to it); the wave counts its entries of each
+  // row in scalar registers (no LDS atomics), writes every lane's candidate
+  // unconditionally (lanes that fail the threshold into a discard slot of
+  // their own), and moves its stage to the rows' lists by itself (one global
+  // reservation per row, no workgroup barrier) when a region could overflow
+  // on the next tile, and once at its end
   constexpr int kRlRows = 128 / HPG;                  // rows of a 128-slot block (one group per row)
-  constexpr int kRlCap = 4 * 32 * kRlTiles;           // keys per row between flushes
-  __shared__ u32x2 stage[RL ? kRlRows * kRlCap : 1];
-  __shared__ uint32_t gbase[RL ? kRlRows : 1];
-  __shared__ uint32_t rstart[RL ? kRlRows + 1 : 1];  // running start of each row's staged entries
+  constexpr int kRlSlots = 64;                        // stage entries per (row, wave)
+  constexpr int kRlDiscard = kRlRows * 4 * kRlSlots;  // first discard slot
+  __shared__ u32x2 stage[RL ? kRlDiscard + 256 : 1];
+  __shared__ uint32_t wpre[RL ? 4 : 1][RL ? kRlRows + 1 : 1];   // per wave: running start of each row's entries
+  __shared__ uint32_t wbase[RL ? 4 : 1][RL ? kRlRows : 1];      // per wave: the rows' reserved list offsets
   const int rbase = mbase >> hshift;                  // RL: first row of the workgroup
   __shared__ float wsl[128];
   __shared__ float tsl[128];          // filter threshold of each slot's selection row
@@ -125,6 +130,24 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
   }
   __syncthreads();
 
+  // RL: threshold of each of the lane's rows (row 8 mb + 2 gi + half of the
+  // block: slot 32 mb + 8 gi + 4 half), the scalar entry counts of the wave,
+  // and the lane's visibility offsets: key j is visible to row rbase + c +
+  // half when j - (L - Nq + rbase) - half <= c, and the row exists when
+  // c < Nq - rbase - half
+  constexpr int NRT = RL ? NMB * (16 / HPG) : 1;
+  float rthr[NRT];
+  uint32_t rcnt[RL ? kRlRows : 1];
+  const int rb_lim = L - p.Nq + (mbase >> hshift) + half;
+  const int rb_hv = p.Nq - (mbase >> hshift) - half;
+  if constexpr (RL) {
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int gi = 0; gi < 16 / HPG; ++gi) rthr[mb * (16 / HPG) + gi] = tsl[32 * mb + 8 * gi + 4 * half];
+#pragma unroll
+    for (int x = 0; x < kRlRows; ++x) rcnt[x] = 0u;
+  }
   // per (slot block, head group) constants of the filter, when they fit in
   // registers: last visible key of the half-wave's slot row (-1: no row), its
   // threshold and its selection row within the request
@@ -155,6 +178,46 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
   u32x2* cwc[CPW];
 #pragma unroll
   for (int cc = 0; cc < CPW; ++cc) cwc[cc] = FILTER ? chunk_cand(cc) : nullptr;
+
+  // RL: the wave's staged entries to the rows' lists (wave-local: lanes
+  // 0..kRlRows-1 reserve their row's space, then the entries are copied in
+  // the order of the rows' running starts)
+  auto rl_flush = [&]() {
+    if constexpr (RL) {
+      uint32_t n = 0u;
+#pragma unroll
+      for (int x = 0; x < kRlRows; ++x) n = lane == x ? rcnt[x] : n;
+      if (lane >= kRlRows || rbase + lane >= p.Nq) n = 0u;
+      const uint32_t incl = wave_prefix_incl_u32(n);
+      const uint32_t ntot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+      if (ntot > 0u) {
+        const uint32_t gb = n ? atomicAdd(&p.cand_n[(int64_t)b * p.Nq + rbase + lane], n) : 0u;
+        if (lane < kRlRows) {
+          wpre[wid][lane] = incl - n;
+          wbase[wid][lane] = gb;
+        }
+        if (lane == 0) wpre[wid][kRlRows] = ntot;
+        __builtin_amdgcn_wave_barrier();
+        for (uint32_t x = lane; x < ntot; x += 64) {
+          int lo = 0;
+#pragma unroll
+          for (int step = kRlRows / 2; step >= 1; step >>= 1)
+            if (wpre[wid][lo + step] <= x) lo += step;
+          const uint32_t e = x - wpre[wid][lo];
+          const uint32_t gs = wbase[wid][lo] + e;
+          const int64_t rowg = (int64_t)b * p.Nq + rbase + lo;
+          if (gs < (uint32_t)p.cap) {
+            const u32x2 v = stage[(lo * 4 + wid) * kRlSlots + (int)e];
+            p.cand[rowg * p.cap + gs] = f32_order_key(__uint_as_float(v[0]));
+            p.cand_j[rowg * p.cap + gs] = v[1];
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+#pragma unroll
+      for (int x = 0; x < kRlRows; ++x) rcnt[x] = 0u;
+    }
+  };
 
   u16x2 kmx[CPW];
 #pragma unroll
@@ -215,18 +278,24 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
         scv[gi] = sc;
       }
       if constexpr (RL) {
-        // one selection group: the group of a slot is its row; each surviving
-        // lane takes its stage slot with one LDS atomic
+        // one selection group of four heads: half-wave half holds row
+        // c + half of the block (c = 8 mb + 2 gi); a survivor's place in its
+        // (row, wave) region is the wave's count of that row plus its rank
+        // among the half-wave's survivors
+        const int dj = j - rb_lim;
 #pragma unroll
         for (int gi = 0; gi < G4; ++gi) {
-          const int v0 = gi * HPG;
-          const int m0 = mbase + 32 * mb + 8 * (v0 >> 2) + 4 * half + (v0 & 3);
-          const int r = m0 >> hshift;
-          if (m0 < M && j <= L - p.Nq + r && scv[gi] >= tsl[(m0 - mbase) & 127]) {
-            const int rr = r - rbase;
-            const uint32_t slot = atomicAdd(&lcount[0][rr], 1u);
-            stage[rr * kRlCap + slot] = u32x2{f32_order_key(scv[gi]), (uint32_t)j};
-          }
+          const int c = 8 * mb + 2 * gi;
+          const bool pass = dj <= c && c < rb_hv && scv[gi] >= rthr[mb * G4 + gi];
+          const uint64_t mk = ballot(pass);
+          const uint32_t lo32 = (uint32_t)mk, hi32 = (uint32_t)(mk >> 32);
+          const uint32_t c0 = (uint32_t)__builtin_popcount(lo32), c1 = (uint32_t)__builtin_popcount(hi32);
+          const uint32_t pre = __builtin_amdgcn_mbcnt_hi(hi32, __builtin_amdgcn_mbcnt_lo(lo32, 0u));
+          const uint32_t slot = half ? pre - c0 + rcnt[c + 1] : pre + rcnt[c];
+          const int idx = pass ? ((c + half) * 4 + wid) * kRlSlots + (int)slot : kRlDiscard + (int)threadIdx.x;
+          stage[idx] = u32x2{__float_as_uint(scv[gi]), (uint32_t)j};
+          rcnt[c] += c0;
+          rcnt[c + 1] += c1;
         }
       } else if constexpr (!FILTER) {
 #pragma unroll
@@ -293,45 +362,13 @@ __global__ __launch_bounds__(256) void idx_mfma64_kernel(IndexerParams p) {
       }
     }
     if constexpr (RL) {
-      if ((t + 1) % kRlTiles == 0 || t + 1 == NT) {
-        // the stage to the rows' lists: one reservation per row
-        // (wave 0: the rows' counts, their running total and the list offsets)
-        __syncthreads();
-        if (threadIdx.x < 64) {
-          const int rr = threadIdx.x;
-          const uint32_t n = (rr < kRlRows && rbase + rr < p.Nq) ? lcount[0][rr] : 0u;
-          const uint32_t incl = wave_prefix_incl_u32(n);
-          if (rr < kRlRows) {
-            gbase[rr] = n ? atomicAdd(&p.cand_n[(int64_t)b * p.Nq + rbase + rr], n) : 0u;
-            rstart[rr] = incl - n;
-          }
-          if (rr == 63) rstart[kRlRows] = incl;
-        }
-        __syncthreads();
-        // entry x of the staged entries belongs to the row whose running
-        // start is the largest <= x
-        const uint32_t ntot = rstart[kRlRows];
-        for (uint32_t x = threadIdx.x; x < ntot; x += 256) {
-          int lo = 0;
+      uint32_t mx = 0u;
 #pragma unroll
-          for (int step = kRlRows / 2; step >= 1; step >>= 1)
-            if (rstart[lo + step] <= x) lo += step;
-          const uint32_t e = x - rstart[lo];
-          const uint32_t gs = gbase[lo] + e;
-          const int64_t rowg = (int64_t)b * p.Nq + rbase + lo;
-          if (gs < (uint32_t)p.cap) {
-            const u32x2 v = stage[lo * kRlCap + e];
-            p.cand[rowg * p.cap + gs] = v[0];
-            p.cand_j[rowg * p.cap + gs] = v[1];
-          }
-        }
-        __syncthreads();
-        for (int rr = threadIdx.x; rr < kRlRows; rr += 256) lcount[0][rr] = 0u;
-        __syncthreads();
-      }
+      for (int x = 0; x < kRlRows; ++x) mx = max(mx, rcnt[x]);
+      if (mx > (uint32_t)(kRlSlots - 32)) rl_flush();
     }
-
   }
+  if constexpr (RL) rl_flush();
 
   // largest |k| element of each chunk (valid keys only)
   __shared__ uint32_t red[CPW][4];
@@ -471,9 +508,10 @@ static void launch_mfma(const IndexerParams& p, hipStream_t st) {
   const int nchunk = (p.ctx + kMfmaChunk - 1) / kMfmaChunk;
   dim3 grid((nchunk + CPW - 1) / CPW, p.B, (p.Nq * p.H_I + 127) / 128);
   if constexpr (MODE == 1 && NMB == 4 && HPG == 4 && RELU) {
-    if (p.cand_j) {      // per-row lists (many rows)
-      hipLaunchKernelGGL((idx_mfma64_kernel<KT, NMB, HPG, RELU, MODE, 1, kMfmaChunk / 32 / 4, true>),
-                         dim3(nchunk, p.B, (p.Nq * p.H_I + 127) / 128), dim3(256), 0, st, p);
+    if (p.cand_j) {      // per-row lists (many rows): one chunk per workgroup, its loads at once
+      constexpr int kRlCpw = 1;
+      hipLaunchKernelGGL((idx_mfma64_kernel<KT, NMB, HPG, RELU, MODE, kRlCpw, kMfmaChunk / 32 / 4, true>),
+                         dim3((nchunk + kRlCpw - 1) / kRlCpw, p.B, (p.Nq * p.H_I + 127) / 128), dim3(256), 0, st, p);
       return;
     }
   }

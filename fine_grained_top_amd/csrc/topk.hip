@@ -1425,6 +1425,7 @@ constexpr int kFzrRows = 8;        // pilot rows per workgroup (4 heads each)
 constexpr int kFzrSamples = 2048;  // sampled keys per row (contexts up to 65536)
 constexpr int kFzrCap = 6144;      // survivors kept per row
 constexpr int kFzrCtx = 65536;
+constexpr int kFzrThreads = 256;   // final kernel: four waves per row
 
 __global__ __launch_bounds__(256) void fzr_pilot_kernel(TopkParams p, float* tau) {
   __shared__ uint32_t sk[kFzrRows][kFzrSamples];
@@ -1605,11 +1606,11 @@ struct FzrSmem {
   uint32_t ck[kFzrCap];
   uint32_t cj[kFzrCap];
   uint32_t bm[kFzrCtx / 32];
-  float red[2 * (kR2Threads / 64)];
+  float red[2 * (kFzrThreads / 64)];
 };
 
-__global__ __launch_bounds__(kR2Threads) void fzr_final_kernel(TopkParams p, FzrWs w) {
-  constexpr int T = kR2Threads;
+__global__ __launch_bounds__(kFzrThreads) void fzr_final_kernel(TopkParams p, FzrWs w) {
+  constexpr int T = kFzrThreads;
   constexpr int NW = T / 64;
   __shared__ FzrSmem sm;
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -1757,7 +1758,7 @@ static hipError_t launch_topk_fused_rows(const TopkParams& p, hipStream_t st) {
   ix.err = nullptr;
   hipError_t e = launch_index_filter(ix, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fzr_final_kernel, dim3(rows), dim3(kR2Threads), 0, st, p, w);
+  hipLaunchKernelGGL(fzr_final_kernel, dim3(rows), dim3(kFzrThreads), 0, st, p, w);
   hipLaunchKernelGGL(fzr_redo_kernel, dim3(min((rows + kR2Threads - 1) / kR2Threads, kRedoGrid)), dim3(kR2Threads),
                      0, st, p, w.redo, rows);
   return hipGetLastError();
