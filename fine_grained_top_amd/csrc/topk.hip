@@ -56,6 +56,22 @@ struct RowSmemC {
   uint32_t run[4];
 };
 
+// A row area whose histogram, once the radix passes are done, holds the band
+// lists in its first half and the selected-position bitmap (positions below
+// 65536) in its second half.
+struct RowSmemF {
+  union {
+    uint32_t hist[4096];
+    struct {
+      uint32_t band_j[1024];
+      uint32_t band_k[1024];
+      uint32_t bm[2048];
+    };
+  };
+  uint32_t sc[16];
+  uint32_t run[4];
+};
+
 struct RowCtx {
   int b, g, r, n;
   const float* s;
@@ -289,11 +305,11 @@ SP_DEV void band_mark(const uint32_t* band_k, const uint32_t* band_j, uint32_t n
 // the remaining R slots; sets the selected bits in bm. Returns false when the
 // band is too wide for the short list or an exact band key needs the wide
 // accumulator (caller redoes the row).
-template <int T, typename SM, int HB = 4, bool SLOW = false>
-SP_DEV bool resolve_candidates(const TopkParams& p, RowCtx& c, SM& rs, uint32_t* ck, uint32_t* cj,
+template <int T, typename SM, int HB = 4, bool SLOW = false, typename CJ = uint32_t>
+SP_DEV bool resolve_candidates(const TopkParams& p, RowCtx& c, SM& rs, uint32_t* ck, CJ* cj,
                                uint32_t* bm, uint32_t n_cand, uint32_t R, uint32_t wlo, uint32_t whi,
                                uint32_t tlo = 0u, uint32_t thi = 0xFFFFFFFFu, const float* qs = nullptr,
-                               const float* wsg = nullptr) {
+                               const float* wsg = nullptr, int bm_clear = 0) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int bits = 32 - __builtin_clz((whi - wlo) | 1u);
   uint32_t t, above;
@@ -304,17 +320,19 @@ SP_DEV bool resolve_candidates(const TopkParams& p, RowCtx& c, SM& rs, uint32_t*
   uint32_t klo, khi;
   band_limits(p, c, tf, tf, tf, klo, khi);
   uint32_t n_in = 0;
+  // a bitmap that shares the histogram's memory is cleared only now
+  for (int i = tid; i < bm_clear; i += T) bm[i] = 0u;
   if (tid == 0) rs.run[0] = 0;
   __syncthreads();
   for (uint32_t i = tid; i < n_cand; i += T) {
-    const uint32_t ks = ck[i];
+    const uint32_t ks = ck[i], js = (uint32_t)cj[i];
     if (ks > khi) {
-      atomicOr(&bm[cj[i] >> 5], 1u << (cj[i] & 31));
+      atomicOr(&bm[js >> 5], 1u << (js & 31));
       ++n_in;
     } else if (ks >= klo) {
       const uint32_t slot = atomicAdd(&rs.run[0], 1u);
       if (slot < (uint32_t)(sizeof(rs.band_j) / sizeof(uint32_t))) {
-        rs.band_j[slot] = cj[i];
+        rs.band_j[slot] = js;
         rs.band_k[slot] = ks;
       }
     }
@@ -1423,7 +1441,7 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* x, int n, uint3
 //     flagged, and fzr_redo recomputes them from the inputs.
 constexpr int kFzrRows = 8;        // pilot rows per workgroup (4 heads each)
 constexpr int kFzrSamples = 2048;  // sampled keys per row (contexts up to 65536)
-constexpr int kFzrCap = 6144;      // survivors kept per row
+constexpr int kFzrCap = 5632;      // survivors kept per row
 constexpr int kFzrCtx = 65536;
 constexpr int kFzrThreads = 256;   // final kernel: four waves per row
 
@@ -1599,17 +1617,19 @@ struct FzrWs {
   int nchunk;
 };
 
+// about 50 KB: three workgroups per CU
 struct FzrSmem {
-  RowSmemC row;
+  RowSmemF row;        // radix histogram, then band lists and the selected-position bitmap
   float qs[4 * 64];
   float wsg[4];
   uint32_t ck[kFzrCap];
-  uint32_t cj[kFzrCap];
-  uint32_t bm[kFzrCtx / 32];
+  uint16_t cj[kFzrCap];   // positions < kFzrCtx
   float red[2 * (kFzrThreads / 64)];
 };
+static_assert(kFzrCtx / 32 <= 2048, "the bitmap fits the row area");
 
-__global__ __launch_bounds__(kFzrThreads) void fzr_final_kernel(TopkParams p, FzrWs w) {
+__global__ __launch_bounds__(kFzrThreads) __attribute__((amdgpu_waves_per_eu(3))) void fzr_final_kernel(TopkParams p,
+                                                                                           FzrWs w) {
   constexpr int T = kFzrThreads;
   constexpr int NW = T / 64;
   __shared__ FzrSmem sm;
@@ -1641,7 +1661,7 @@ __global__ __launch_bounds__(kFzrThreads) void fzr_final_kernel(TopkParams p, Fz
     for (uint32_t i = tid; i < n_cand; i += T) {
       const uint32_t k = gk[i];
       sm.ck[i] = k;
-      sm.cj[i] = gj[i];
+      sm.cj[i] = (uint16_t)gj[i];
       kmx = max(kmx, k);
     }
   }
@@ -1654,7 +1674,6 @@ __global__ __launch_bounds__(kFzrThreads) void fzr_final_kernel(TopkParams p, Fz
     sm.row.sc[wid] = kmx;
   }
   const int nwords = (c.n + 31) >> 5;
-  for (int i = tid; i < nwords; i += T) sm.bm[i] = 0u;
   __syncthreads();
   float KM = 0.f, CO = 0.f;
   uint32_t KX = 0;
@@ -1673,10 +1692,10 @@ __global__ __launch_bounds__(kFzrThreads) void fzr_final_kernel(TopkParams p, Fz
     const float E = 2.0f * c.eps * 1.0001f + 1e-30f;
     const uint32_t base = f32_order_key(tau);
     const uint32_t tlo = f32_order_key(nextafterf(nextafterf(tau + 2.0f * E, INFINITY), INFINITY));
-    ok = resolve_candidates<T, RowSmemC, 4, true>(p, c, sm.row, sm.ck, sm.cj, sm.bm, n_cand, (uint32_t)p.K, base,
-                                                 max(KX, base), tlo, 0xFFFFFFFFu, sm.qs, sm.wsg);
+    ok = resolve_candidates<T, RowSmemF, 4, true>(p, c, sm.row, sm.ck, sm.cj, sm.row.bm, n_cand, (uint32_t)p.K, base,
+                                                 max(KX, base), tlo, 0xFFFFFFFFu, sm.qs, sm.wsg, nwords);
   }
-  if (ok) emit_bitmap<T, kFzrCtx / 32>(p, c, sm.row, sm.bm, nwords);
+  if (ok) emit_bitmap<T, kFzrCtx / 32>(p, c, sm.row, sm.row.bm, nwords);
   if (tid == 0) w.redo[row] = ok ? 0u : 1u;
 }
 
