@@ -28,15 +28,22 @@ constexpr int kMaxBlkWords = 64;   // per-row block bitmap words (<= 2048 blocks
 constexpr float kLog2eT = 1.4426950408889634f;
 constexpr float kLn2T = 0.6931471805599453f;
 
-template <bool SPLIT>
+// Every tile array starts on a 16-byte boundary (16-byte LDS stores, 8-byte
+// transposed reads), whatever the sizes of the arrays before it.
+template <bool SPLIT, bool BLK>
 struct TileSmem {
-  uint16_t ks[kTK * kKs];
-  uint16_t vt[64 * 128];    // V tile row-major, XOR-swizzled 16-byte chunks
+  alignas(16) uint16_t ks[kTK * kKs];
+  alignas(16) uint16_t vt[64 * 128];    // V tile row-major, XOR-swizzled 16-byte chunks
   uint32_t tiles[64];                    // tile bitmap (<= 2048 tiles)
-  uint32_t rowblk[kTQ * kMaxBlkWords];   // BLOCKS: per-row selected-block bitmaps
-  uint16_t ks2[SPLIT ? kTK * kKs : 8];   // SPLIT: the low parts, laid out as ks / vt
-  uint16_t vt2[SPLIT ? 64 * 128 : 8];
+  uint32_t rowblk[BLK ? kTQ * kMaxBlkWords : 1];   // BLOCKS: per-row selected-block bitmaps
+  alignas(16) uint16_t ks2[SPLIT ? kTK * kKs : 8];   // SPLIT: the low parts, laid out as ks / vt
+  alignas(16) uint16_t vt2[SPLIT ? 64 * 128 : 8];
 };
+using TileSmemSplit = TileSmem<true, false>;
+using TileSmemSplitBlk = TileSmem<true, true>;
+static_assert(__builtin_offsetof(TileSmemSplit, ks2) % 16 == 0 && __builtin_offsetof(TileSmemSplit, vt2) % 16 == 0 &&
+                  __builtin_offsetof(TileSmemSplitBlk, ks2) % 16 == 0,
+              "tile arrays on 16-byte boundaries");
 
 // STRIDE: window/global mode with a dilated stride (the second key stream).
 // SPLIT: compressed entries held as two bf16 parts (hi in k/v, lo in
@@ -45,9 +52,11 @@ struct TileSmem {
 // significant bits instead of bf16's 8.
 // MODE: the selection mode, fixed per instance so that the per-element masks
 // carry no tests of other modes.
+// Three waves per SIMD (at most 168 VGPRs, no spills) and, outside BLOCKS
+// mode, no per-row block bitmaps in LDS (34 KB): three workgroups per CU.
 template <int MODE, bool STRIDE, bool SPLIT>
-__global__ __launch_bounds__(256) void attn_tile_kernel(AttnParams a, int xper) {
-  __shared__ __attribute__((aligned(16))) TileSmem<SPLIT> sm;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_tile_kernel(AttnParams a, int xper) {
+  __shared__ __attribute__((aligned(16))) TileSmem<SPLIT, MODE == 3> sm;
   // query tiles of a head are consecutive items, and each XCD takes a run of
   // them: the key tiles that neighbouring query tiles share stay in its L2
   const int nqt = (a.Nq + kTQ - 1) / kTQ;
