@@ -18,27 +18,37 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sqlite3
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
-# kernels of each stage, by name fragment; the plain, filtering and page-key
-# indexer are one template whose fifth argument (0, 1, 2) tells them apart
-# (followed by the chunks per workgroup and the tiles in flight per wave)
+# kernels of each stage, by regular expression on the kernel name; the plain,
+# filtering and page-key indexer are one template whose fifth argument (0, 1,
+# 2) tells them apart
+_IDX = r"idx_mfma64_kernel<\d+, \d+, \d+, (true|false), %d, "
 STAGES = {
-    "index_topk_fused": ["fz_pilot", "1, 2, 3>(sp::IndexerParams)", "1, 1, 4>(sp::IndexerParams)", "fz_final"],
-    "index_scores": ["0, 1, 4>(sp::IndexerParams)", "idx_generic", "idx_err"],
-    "index_page_fused": ["2, 1, 4>(sp::IndexerParams)", "idx_err", "page_keys", "page_select"],
-    "topk": ["topk_row", "topk_redo", "mt_zero", "mt_hist", "mt_collect", "mt_finalize"],
-    "page_select": ["page_keys_kernel", "page_select_kernel"],
-    "two_level_select": ["two_level_kernel"],
-    "index_block_select": ["two_level_kernel"],
-    "quest_select": ["quest_keys_kernel", "page_select_kernel"],
-    "attention_bwd": ["attn_bwd_zero", "attn_bwd_generic", "attn_bwd_tile"],
-    "block_select": ["pool_kernel", "block_select_kernel"],
-    "attention": ["attn_index_mfma", "attn_combine", "attn_tile", "attn_generic_kernel", "bc_count", "bc_scan", "bc_table",
-                  "bc_scatter", "bc_attn", "bc_combine"],
+    "index_topk_fused": [r"fz_pilot", r"fz_final", r"fzr_pilot", r"fzr_final", r"fzr_redo", r"fill_u32", _IDX % 1],
+    "index_scores": [_IDX % 0, r"idx_generic", r"idx_err"],
+    "index_page_fused": [_IDX % 2, r"idx_err", r"page_keys", r"page_select"],
+    "topk": [r"topk_row", r"topk_redo", r"mt_zero", r"mt_hist", r"mt_collect", r"mt_finalize"],
+    "page_select": [r"page_keys_kernel", r"page_select_kernel"],
+    "two_level_select": [r"tl_pool_kernel", r"two_level_kernel"],
+    "index_block_select": [r"tl_pool_kernel", r"two_level_kernel", r"group_block_pick"],
+    "quest_select": [r"quest_bounds", r"quest_keys_kernel", r"page_select_kernel"],
+    "attention_bwd": [r"attn_bwd_zero", r"attn_bwd_generic", r"attn_bwd_tile", r"attn_bwd_reduce"],
+    "block_select": [r"sp::pool_kernel", r"block_select_kernel"],
+    "attention": [r"attn_index_mfma", r"attn_combine", r"attn_tile", r"attn_generic_kernel", r"bc_count", r"bc_scan",
+                  r"bc_table", r"bc_scatter", r"bc_attn", r"bc_combine", r"nsa_pool", r"nsa_combine"],
 }
+
+
+def stage_kernels(stage: str, names) -> list:
+    """The kernels among `names` that belong to `stage`."""
+    pats = [re.compile(x) for x in STAGES.get(stage, [])]
+    return [n for n in names if any(pt.search(n) for pt in pats)]
+
+
 CALIB_BYTES = 1 << 30
 
 
@@ -87,8 +97,8 @@ def main():
         kernels[name] = {"dispatches": len(vs), "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
                          "read_bytes": round(fk * 1024 * kf), "write_bytes": round(wk * 1024 * kw)}
     stages = {}
-    for st, frags in STAGES.items():
-        ks = [k for k in kernels if any(fr in k for fr in frags)]
+    for st in STAGES:
+        ks = stage_kernels(st, kernels)
         if args.stages and st not in args.stages.split(","):
             continue
         if ks:
