@@ -49,6 +49,17 @@ def stage_kernels(stage: str, names) -> list:
     return [n for n in names if any(pt.search(n) for pt in pats)]
 
 
+def split_setup(ks, calls):
+    """(per-call kernels, setup kernels, calls of the stage): a kernel with fewer
+    than half the stage's dispatches (the most common count among its kernels)
+    builds per-input data once (page bounds, pooled block keys) and is not part
+    of a call."""
+    if not ks:
+        return [], [], 0
+    n = collections.Counter(calls[k] for k in ks).most_common(1)[0][0]
+    return [k for k in ks if 2 * calls[k] >= n], [k for k in ks if 2 * calls[k] < n], n
+
+
 CALIB_BYTES = 1 << 30
 
 
@@ -98,11 +109,13 @@ def main():
                          "read_bytes": round(fk * 1024 * kf), "write_bytes": round(wk * 1024 * kw)}
     stages = {}
     for st in STAGES:
-        ks = stage_kernels(st, kernels)
+        ks, setup, _ = split_setup(stage_kernels(st, kernels), {k: v["dispatches"] for k, v in kernels.items()})
         if args.stages and st not in args.stages.split(","):
             continue
         if ks:
             stages[st] = {"kernels": ks, "bytes": sum(kernels[k]["read_bytes"] + kernels[k]["write_bytes"] for k in ks)}
+            if setup:
+                stages[st]["setup_kernels"] = setup
     out = {"workload": args.workload, "sources": sources_hash(), "fetch_scale": kf, "write_scale": kw,
            "calibration": {"bytes_each_way": CALIB_BYTES, "fetch_kib": calib_f, "write_kib": calib_w},
            "kernels": kernels, "stages": stages}

@@ -11,12 +11,11 @@ runs. The workload's description line is kept from the summary being replaced.
 from __future__ import annotations
 
 import argparse
-import collections
 import json
 import os
 import sqlite3
 
-from fine_grained_top_amd.pmc_traffic import stage_kernels
+from fine_grained_top_amd.pmc_traffic import split_setup, stage_kernels
 
 PROFILE_ARGS = "--steps 20 --warmup 5 --no-cpu --calib-copy"
 
@@ -66,15 +65,17 @@ def main():
     rl = bench.get("roofline") or {}
     stage = rl.get("kernel")
     if stage and stage in bench.get("stages", {}):
-        ks = stage_kernels(stage, [k for k in stats if "copyBuffer" not in k])
+        ks, setup, ncall = split_setup(stage_kernels(stage, [k for k in stats if "copyBuffer" not in k]),
+                                       {k: v[0] for k, v in stats.items()})
         if ks:
-            # calls of the stage: the most common call count among its kernels
-            ncall = collections.Counter(stats[k][0] for k in ks).most_common(1)[0][0]
             per_call = sum(stats[k][0] * stats[k][1] for k in ks) / ncall
             ev = bench["stages"][stage]["ms"] * 1000.0
             out += [f"Roofline stage `{stage}` = kernels " + ", ".join(f"`{k}`" for k in ks) +
                     f": {per_call:.2f} µs of kernel time per call ({ncall} calls); the bench line's HIP-event time"
                     f" of the stage is {ev:.2f} µs.", ""]
+            if setup:
+                out += ["Run once per input before the timed calls (not part of the stage): " +
+                        ", ".join(f"`{k}`" for k in setup) + ".", ""]
 
     # ---- traffic
     cal = traffic["calibration"]
