@@ -937,8 +937,8 @@ __global__ __launch_bounds__(kTkThreads) void mt_finalize_kernel(TopkParams p, M
 }
 
 // ---------------------------------------------------------------- fused indexer + top-K
-// The score matrix is never written. A pilot scores a 1/32 sample of each
-// row's keys (runs of 64 keys every 2048) and sets a threshold tau whose
+// The score matrix is never written. A pilot scores a sample of each row's
+// keys (runs of 64 keys at a fixed stride) and sets a threshold tau whose
 // expected number of survivors is about 1.5 K; the MFMA indexer then keeps
 // only (key, index) pairs with score >= tau; the finalize kernel selects the
 // exact top-K among them (certified, as above) after checking that every key
@@ -946,6 +946,9 @@ __global__ __launch_bounds__(kTkThreads) void mt_finalize_kernel(TopkParams p, M
 // check fails the row is redone by recomputing scores, so the result never
 // depends on the sample.
 constexpr int kPilotStride = 2048, kPilotRun = 64, kPilotCap = 8192;
+// the decode pilot's sample (few rows: the pilot's span is set by the keys
+// one workgroup scores): runs of 64 keys every 4096
+constexpr int kDecStride = 4096, kDecRun = 64, kDecCap = 4096;
 
 // float32 score recomputed by one thread (FMA chains; within the same bound)
 SP_DEV float recompute_score(const IndexerRow& r, int64_t j) {
@@ -982,21 +985,21 @@ SP_DEV float recompute_score_lds(const IndexerRow& r, const float* qs, const flo
   return s;
 }
 
-// Pilot: one workgroup per selection row. The row's heads score a 1/32
-// sample of its keys (runs of 64 keys every 2048) on MFMA, laid out as in
+// Pilot: one workgroup per selection row. The row's heads score a 1/64
+// sample of its keys (runs of 64 keys every 4096) on MFMA, laid out as in
 // the indexer (32x32x16 bf16: A = the row's heads as slot rows, B = 32 keys,
 // fp8 keys converted to bf16 exactly), so lanes 0..31 each hold every head's
 // product for one key and form its score in-lane. The order keys stay in
 // LDS; tau is the lower edge of the 4096-bin histogram bin (over the range of
-// the sampled keys) where about 1.5 K survivors in proportion are reached
-// (sample count scaled to the row's length). Any tau is correct: the final
+// the sampled keys) where about 1.5 K survivors in proportion (plus 8
+// sampled keys) are reached. Any tau is correct: the final
 // stage checks it and can fall back; this one only has to leave a little
 // over 1.5 K keys. Requires d_I = 64, bf16 queries, bf16 or fp8 keys.
 constexpr int kPilotTB = 8;       // sampled tiles of 32 keys per wave and load batch
 __global__ __launch_bounds__(kTkThreads) void fz_pilot_kernel(TopkParams p, float* tau) {
   constexpr int T = kTkThreads;
   constexpr int NW = T / 64;
-  __shared__ uint32_t sk[kPilotCap];
+  __shared__ uint32_t sk[kDecCap];
   __shared__ uint32_t hist[4096];
   __shared__ uint32_t sc[16];
   __shared__ uint32_t red[2 * NW + 2];
@@ -1008,9 +1011,9 @@ __global__ __launch_bounds__(kTkThreads) void fz_pilot_kernel(TopkParams p, floa
     return;
   }
   const IndexerRow& ir = c.ir;
-  const int nruns = (c.n + kPilotStride - 1) / kPilotStride;
+  const int nruns = (c.n + kDecStride - 1) / kDecStride;
   const int ntiles = 2 * nruns;                  // two tiles of 32 keys per run
-  const int slots = nruns * kPilotRun;
+  const int slots = nruns * kDecRun;
   const bool fp8 = ir.kt == DT_FP8;
   // A operand: slot row col = head col (< H), dims 32 half + 8 s + v
   bf16x8 A[4];
@@ -1028,12 +1031,12 @@ __global__ __launch_bounds__(kTkThreads) void fz_pilot_kernel(TopkParams p, floa
   const int tbstep = NW * (fp8 ? kPilotTB : kPilotTB / 2);
   for (int tb = wid; tb < ntiles; tb += tbstep) {
     // key bytes of this wave's batch: tile tt = tb + NW u covers keys
-    // (tt / 2) * 2048 + 32 (tt % 2) + col, lane half: dims 32 half .. +31
+    // (tt / 2) * 4096 + 32 (tt % 2) + col, lane half: dims 32 half .. +31
     u32x4 raw[kPilotTB][4];
 #pragma unroll
     for (int u = 0; u < kPilotTB; ++u) {
       const int tt = tb + NW * u;
-      int j = (tt >> 1) * kPilotStride + 32 * (tt & 1) + col;
+      int j = (tt >> 1) * kDecStride + 32 * (tt & 1) + col;
       j = j < c.n ? j : c.n - 1;
       if (tt < ntiles) {
         if (fp8) {
@@ -1074,13 +1077,13 @@ __global__ __launch_bounds__(kTkThreads) void fz_pilot_kernel(TopkParams p, floa
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         sv = ir.relu ? fmaf(wv[t], __int_as_float(max(__float_as_int(acc[t]), 0)), sv) : acc[0];
-      const int j = (tt >> 1) * kPilotStride + 32 * (tt & 1) + col;
+      const int j = (tt >> 1) * kDecStride + 32 * (tt & 1) + col;
       if (half == 0) sk[32 * tt + col] = j < c.n ? f32_order_key(sv) : 0u;
     }
   }
   __syncthreads();
   // tau from the sampled keys (0 marks a key after the row's position)
-  constexpr int U = kPilotCap / T;
+  constexpr int U = kDecCap / T;
   uint32_t v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -1114,7 +1117,7 @@ __global__ __launch_bounds__(kTkThreads) void fz_pilot_kernel(TopkParams p, floa
     kmax = max(kmax, red[NW + x]);
   }
   __syncthreads();                                          // sc is reused by the scan below
-  const uint64_t want = ((uint64_t)3 * p.K * mt + 2ull * c.n - 1) / (2ull * c.n) + 16;   // ~1.5 K survivors
+  const uint64_t want = ((uint64_t)3 * p.K * mt + 2ull * c.n - 1) / (2ull * c.n) + 8;   // ~1.5 K survivors
   const uint32_t R = (uint32_t)min((uint64_t)mt, want);
   if (R == 0) {
     if (tid == 0) tau[row] = -INFINITY;
@@ -1158,13 +1161,16 @@ struct FzWs {
   int nchunk, cap;
 };
 
+constexpr int kFzOvf = 1024;
+
 struct FzSmem {
   RowSmem row;             // histogram and band lists (also used by the fallback)
   uint32_t bm[kMaxWords];
   float qs[4 * 64];        // the row's indexer queries (<= 4 heads, d_I = 64) and weights
   float wsg[4];
   float red[4 * (kTkThreads / 64)];   // per-wave partials
-  uint32_t sel[4];         // band: smallest and largest key of the chosen bin
+  u32x2 ovf[kFzOvf];       // candidate slots past the first 32 of a chunk, per wave, read once
+  uint32_t ovn[kTkThreads / 64];   // entries of each wave's region (all ones: it did not fit)
 };
 
 // In a 4096-bin histogram (bins ordered low to high), the bin holding the
@@ -1215,16 +1221,18 @@ constexpr int kFzRounds = 8;      // instructions held in registers: 256 chunks
 // one round, none waiting on another: the first 32 candidate slots of every
 // chunk (consecutive lanes read consecutive pairs of a chunk's slots) with
 // the chunk counts, the chunk key bounds, the threshold, the row's queries
-// and weights. One barrier then publishes the error bound's inputs, the
-// number of candidates and the largest candidate score. The K-th largest
-// score is located by a histogram of 4096 bins over [tau, largest score]
-// (bins as wide as the certification band or wider; a second pass splits the
-// bin when it is much wider); the smallest and largest scores of that bin
-// give the band; scores above it set bitmap bits, band members are listed
-// and, unless all of them are needed to fill the K slots, scored exactly and
-// ranked; the bitmap is written out as ascending positions. Checks (enough
-// candidates, the band above tau) send a row to recomputed scores, so the
-// result never depends on the pilot's sample.
+// and weights; a thread whose chunk holds more reads the rest into its
+// wave's LDS list. Each thread counts its candidates and their largest score
+// on the way, so one barrier publishes the error bound's inputs, the number
+// of candidates and the largest score. The K-th largest score is located by
+// a histogram of 4096 bins over [tau, largest score] (bins as wide as the
+// certification band or wider; a second pass splits the bin when it is much
+// wider); the band is that bin's range widened by the certification margin;
+// scores above it set bitmap bits, band members are listed and, unless all
+// of them are needed to fill the K slots, scored exactly and ranked; the
+// bitmap is written out as ascending positions. Checks (enough candidates,
+// the band above tau) send a row to recomputed scores, so the result never
+// depends on the pilot's sample.
 __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs w) {
   constexpr int T = kTkThreads, NW = T / 64, S = kFzRounds, CPI = T / kFzLanes;
   __shared__ FzSmem sm;
@@ -1273,13 +1281,67 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
   bool xs = false;                                     // a register chunk holds more than 32
 #pragma unroll
   for (int i = 0; i < S; ++i) xs |= CPI * i + cq < nch && cn[i] > 32u;
+  // The slots past 32 of the register chunks are read once, by the thread
+  // that owns them, into its wave's region of an LDS list (the wave's
+  // offsets from a prefix sum of the per-thread counts); every pass below
+  // visits the list. A wave whose slots exceed its region reads them from
+  // global memory in every pass instead.
+  constexpr int kOvfW = kFzOvf / (T / 64);
+  uint32_t nov = 0u;
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const int ch = CPI * i + cq;
+    const int lim = ch < nch ? (int)min(cn[i], (uint32_t)w.cap) : 0;
+    if (lim > 32 + pr) nov += (uint32_t)((lim - 32 - pr + kFzLanes - 1) / kFzLanes);
+  }
+  const uint32_t ov_incl = wave_prefix_incl_u32(nov);
+  const uint32_t ov_wave = (uint32_t)__builtin_amdgcn_readlane((int)ov_incl, 63);
+  const bool ov_fit = ov_wave <= (uint32_t)kOvfW;
+  // the counting pass: this thread's candidates (registers, its slots past
+  // 32, the chunks past the registers)
+  uint32_t kmx = 0u, mine = 0u;
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    if (vm & (1u << (2 * i))) { kmx = max(kmx, cv4[i][0]); ++mine; }
+    if (vm & (2u << (2 * i))) { kmx = max(kmx, cv4[i][2]); ++mine; }
+  }
+  if (xs) {
+    uint32_t o = (uint32_t)wid * kOvfW + ov_incl - nov;
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      const int ch = CPI * i + cq;
+      if (ch < nch && cn[i] > 32u)
+        for (int e = 32 + pr; e < (int)min(cn[i], (uint32_t)w.cap); e += kFzLanes) {
+          const u32x2 v = cslot(ch)[e];
+          kmx = max(kmx, v[0]);
+          ++mine;
+          if (ov_fit) sm.ovf[o++] = v;
+        }
+    }
+  }
+  for (int ch = CPI * S + cq; ch < nch; ch += CPI) {   // chunks past the registers (long contexts)
+    const int nn = (int)min(ccount(ch), (uint32_t)w.cap);
+    for (int e = pr; e < nn; e += kFzLanes) {
+      kmx = max(kmx, cslot(ch)[e][0]);
+      ++mine;
+    }
+  }
+  if (lane == 0) sm.ovn[wid] = ov_fit ? ov_wave : 0xFFFFFFFFu;
+  bool ovf_lds = true;                                 // set after the barrier below
   auto each = [&](auto f) {
 #pragma unroll
     for (int i = 0; i < S; ++i) {
       if (vm & (1u << (2 * i))) f(cv4[i][0], cv4[i][1]);
       if (vm & (2u << (2 * i))) f(cv4[i][2], cv4[i][3]);
     }
-    if (xs) {
+    if (ovf_lds) {
+#pragma unroll
+      for (int v = 0; v < T / 64; ++v)
+        for (uint32_t e = tid; e < sm.ovn[v]; e += T) {
+          const u32x2 x = sm.ovf[v * kOvfW + e];
+          f(x[0], x[1]);
+        }
+    } else if (xs) {
 #pragma unroll
       for (int i = 0; i < S; ++i) {
         const int ch = CPI * i + cq;
@@ -1298,22 +1360,15 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
       }
     }
   };
-  uint32_t kmx = 0u, mine = 0u;
   bool over = false;
 #pragma unroll
   for (int i = 0; i < S; ++i) over |= CPI * i + cq < nch && cn[i] > (uint32_t)w.cap;
-  each([&](uint32_t k, uint32_t) {
-    kmx = max(kmx, k);
-    ++mine;
-  });
   for (int i = tid; i < 4096; i += T) sm.row.hist[i] = 0u;
   const int nwords = (c.n + 31) >> 5;
   for (int i = tid; i < nwords; i += T) sm.bm[i] = 0u;
   if (tid == 0) {
     sm.row.run[0] = 0u;
     sm.row.run[1] = 0u;
-    sm.sel[2] = 0xFFFFFFFFu;
-    sm.sel[3] = 0u;
   }
   km = wave_max_dpp(km);
   coef = wave_sum_dpp(coef);
@@ -1339,6 +1394,8 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
     n_cand += x & 0x7FFFFFFFu;
     any_over |= (x >> 31) != 0u;
   }
+#pragma unroll
+  for (int v = 0; v < NW; ++v) ovf_lds &= sm.ovn[v] != 0xFFFFFFFFu;
   c.eps = eps_of(p.ix, CO, KM);
   auto fallback = [&]() {
     row_topk_single<T>(p, c, sm.row, [&](int i) { return recompute_score(c.ir, i); });
@@ -1369,16 +1426,19 @@ __global__ __launch_bounds__(kTkThreads) void fz_final_kernel(TopkParams p, FzWs
     uint32_t above2;
     hist_find<T>(sm.row.hist, (uint32_t)p.K - above, sm.row.sc, b2, above2);
   }
-  // smallest and largest score of the chosen bin: the K-th largest lies between
-  each([&](uint32_t k, uint32_t) {
-    if (bin1(k) == b1 && (!two || bin2(k) == b2)) {
-      atomicMin(&sm.sel[2], k);
-      atomicMax(&sm.sel[3], k);
-    }
-  });
-  __syncthreads();
-  const uint32_t klo = f32_order_key(nextafterf(order_key_f32(sm.sel[2]) - E, -INFINITY));
-  const uint32_t khi = f32_order_key(nextafterf(order_key_f32(sm.sel[3]) + E, INFINITY));
+  // the band: the chosen bin's score range (from its edges, widened by 1 %
+  // of a bin on each side, far more than the rounding of the bin
+  // arithmetic; the top bin reaches the largest score), then E on each
+  // side; the K-th largest lies in the bin
+  double blo = (double)tau + ((double)b1 - 0.01) * (double)W;
+  double bhi = b1 >= 4095u ? (double)order_key_f32(KX) : (double)tau + ((double)b1 + 1.01) * (double)W;
+  if (two) {
+    const double W2 = 1.0 / (double)iW2;
+    if (b2 > 0u) blo = fmax(blo, (double)lo2 + ((double)b2 - 0.01) * W2);
+    if (b2 < 4095u) bhi = fmin(bhi, (double)lo2 + ((double)b2 + 1.01) * W2);
+  }
+  const uint32_t klo = f32_order_key(nextafterf((float)(blo - (double)E), -INFINITY));
+  const uint32_t khi = f32_order_key(nextafterf((float)(bhi + (double)E), INFINITY));
   if (klo < f32_order_key(tau)) return fallback();   // part of the band may lie below tau
   uint32_t n_in = 0u;
   each([&](uint32_t k, uint32_t j) {
@@ -1427,7 +1487,7 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* x, int n, uint3
 // One selection group of four weighted-ReLU heads, contexts up to 65536.
 // (1) fzr_pilot: a workgroup takes 8 consecutive rows (their 4 heads are the
 //     32 slot rows of the 32x32x16 MFMA) and scores the sampled keys (runs of
-//     64 every 2048, the decode pilot's sample) for all of them; per row, a
+//     64 every 2048) for all of them; per row, a
 //     wave finds the R-th largest sampled key (R for about 1.25 K survivors in
 //     proportion, plus a margin) by three 8-bit radix passes over a per-wave
 //     histogram, and tau is the lower edge of its 24-bit bin; a row short
@@ -1740,7 +1800,7 @@ static bool fused_rows_ok(const TopkParams& p) {
 
 static bool fused_few_ok(const TopkParams& p) {
   const int64_t nchunk = (p.ctx + 511) / 512;
-  return index_filter_ok(p.ix) && p.ctx <= kPilotCap / kPilotRun * kPilotStride &&
+  return index_filter_ok(p.ix) && p.ctx <= kDecCap / kDecRun * kDecStride &&
          (p.ctx + 31) / 32 <= kMaxWords && nchunk <= kTkThreads &&
          nchunk * p.G * p.Nq * kFzCap < ((int64_t)1 << 31);   // 32-bit candidate offsets per request
 }

@@ -424,18 +424,25 @@ def test_fused_falls_back_when_the_sample_misleads():
     check_sets(hp, res, rows, wl)
 
 
-@pytest.mark.parametrize("kfmt", ["fp8", "bf16"])
-def test_fused_decode_clustered_extreme_keys(kfmt):
+@pytest.mark.parametrize("kfmt,layout", [("fp8", "one_run"), ("bf16", "one_run"), ("fp8", "short_runs")])
+def test_fused_decode_clustered_extreme_keys(kfmt, layout):
     """Decode rows whose survivors crowd into a few 512-key chunks (more than
     a thread of the final selection loads in its first round) and whose
     largest scores are far above the rest (so the score range is split twice
-    by the selection histogram): a run of large indexer keys, distinct by
-    position, is planted in every request; fp8 and bf16 indexer keys."""
+    by the selection histogram): runs of large indexer keys, distinct by
+    position, are planted in every request; fp8 and bf16 indexer keys. One
+    run of 300 keys puts more extra slots in one wave of the final selection
+    than its LDS region holds (they are read from global memory in every
+    pass); three runs of 50 keys in chunks of different waves fit the
+    regions."""
     wl = dataclasses.replace(gen.WORKLOADS["dsa_decode_small"], B=2, N=40000, len_range=(36000, 40000), topk=512,
                              idx_k_dtype=kfmt)
     inp = gen.generate(wl)
     codes = inp["k_idx"]
-    run = np.arange(5000, 5300)
+    if layout == "one_run":
+        run = np.arange(5000, 5300)
+    else:
+        run = np.concatenate([np.arange(1030, 1080), np.arange(9230, 9280), np.arange(20030, 20080)])
     if kfmt == "fp8":
         codes[:, run, 0, :] = (0x68 + (run % 8)).astype(codes.dtype)[:, None]      # 64 .. 120
     else:
