@@ -947,8 +947,8 @@ __global__ __launch_bounds__(kTkThreads) void mt_finalize_kernel(TopkParams p, M
 // depends on the sample.
 constexpr int kPilotStride = 2048, kPilotRun = 64, kPilotCap = 8192;
 // the decode pilot's sample (few rows: the pilot's span is set by the keys
-// one workgroup scores): runs of 64 keys every 4096
-constexpr int kDecStride = 4096, kDecRun = 64, kDecCap = 4096;
+// one workgroup scores): runs of 64 keys every 8192
+constexpr int kDecStride = 8192, kDecRun = 64, kDecCap = 4096;
 
 // float32 score recomputed by one thread (FMA chains; within the same bound)
 SP_DEV float recompute_score(const IndexerRow& r, int64_t j) {
@@ -985,8 +985,8 @@ SP_DEV float recompute_score_lds(const IndexerRow& r, const float* qs, const flo
   return s;
 }
 
-// Pilot: one workgroup per selection row. The row's heads score a 1/64
-// sample of its keys (runs of 64 keys every 4096) on MFMA, laid out as in
+// Pilot: one workgroup per selection row. The row's heads score a 1/128
+// sample of its keys (runs of 64 keys every 8192) on MFMA, laid out as in
 // the indexer (32x32x16 bf16: A = the row's heads as slot rows, B = 32 keys,
 // fp8 keys converted to bf16 exactly), so lanes 0..31 each hold every head's
 // product for one key and form its score in-lane. The order keys stay in
@@ -1031,7 +1031,7 @@ __global__ __launch_bounds__(kTkThreads) void fz_pilot_kernel(TopkParams p, floa
   const int tbstep = NW * (fp8 ? kPilotTB : kPilotTB / 2);
   for (int tb = wid; tb < ntiles; tb += tbstep) {
     // key bytes of this wave's batch: tile tt = tb + NW u covers keys
-    // (tt / 2) * 4096 + 32 (tt % 2) + col, lane half: dims 32 half .. +31
+    // (tt / 2) * 8192 + 32 (tt % 2) + col, lane half: dims 32 half .. +31
     u32x4 raw[kPilotTB][4];
 #pragma unroll
     for (int u = 0; u < kPilotTB; ++u) {

@@ -27,6 +27,17 @@ def trace_stats(db: str):
     return {name: (int(n), float(avg) / 1000.0) for name, n, avg in rows}
 
 
+def counter_means(db: str):
+    """(kernel name, counter, mean value per dispatch) of one counter database."""
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, dispatch_id, counter_name, sum(counter_value) from pmc_events "
+                       "group by name, dispatch_id, counter_name").fetchall()
+    acc = {}
+    for name, _, c, v in rows:
+        acc.setdefault((name, c), []).append(float(v))
+    return [(n, c, sum(v) / len(v)) for (n, c), v in acc.items()]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
@@ -34,6 +45,9 @@ def main():
     ap.add_argument("--trace", required=True)
     ap.add_argument("--traffic", required=True)
     ap.add_argument("--out", required=True)
+    ap.add_argument("--counters", nargs="*", default=[],
+                    help="databases of further `rocprofv3 --pmc` runs of the same command (COUNTERS=DB, the"
+                         " counters comma-separated)")
     args = ap.parse_args()
     w = args.workload
     line = [x for x in open(args.bench).read().splitlines() if x.startswith("{")][-1]
@@ -100,6 +114,23 @@ def main():
     for st in bench.get("stages", {}):
         if st in traffic.get("stages", {}):
             out.append(f"* `{st}`: {traffic['stages'][st]['bytes'] / 1e6:.2f} MB")
+    if args.counters:
+        out += ["", "## Instruction and request counters", "",
+                "Mean per dispatch of each kernel, one `rocprofv3 --pmc` run per line of counters:", ""]
+        names, per = [], {}
+        for spec in args.counters:
+            ctrs, db = spec.split("=", 1)
+            out.append(f"    rocprofv3 --pmc {ctrs.replace(',', ' ')} -d <out> -o run -- {prof}")
+            for name, c, v in counter_means(db):
+                if "copyBuffer" in name:
+                    continue
+                per.setdefault(name, {})[c] = v
+                if c not in names:
+                    names.append(c)
+        out += ["", "| kernel | " + " | ".join(names) + " |", "|---" * (len(names) + 1) + "|"]
+        for name in sorted(per):
+            out.append(f"| `{name}` | " + " | ".join(f"{per[name].get(c, float('nan')):.0f}" for c in names) + " |")
+        out.append("")
     with open(args.out, "w") as fh:
         fh.write("\n".join(out) + "\n")
     print("wrote", args.out)
