@@ -306,12 +306,12 @@ __global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(AttnParams a, Attn
   const int L = min(a.ctx_len ? a.ctx_len[b] : a.ctx, a.ctx);
   const int ntiles_all = (L + kBT - 1) / kBT;
   const int gt = (min(a.n_global, L) + kBT - 1) / kBT;
-  if (t >= ntiles_all || t < gt) return;
+  if (t < gt) return;   // global tiles: float atomics onto rows zeroed before the tile kernel
   const int pbase = L - a.Nq, nqt = (a.Nq + kBT - 1) / kBT, G = a.Hq / a.Hkv;
   const int ntc = (a.ctx + kBT - 1) / kBT;
   if (tid == 0) nl = 0u;
   __syncthreads();
-  for (int e = tid; e < G * nqt; e += 256) {
+  for (int e = tid; t < ntiles_all && e < G * nqt; e += 256) {
     const int hq = kvh * G + e / nqt, qt = e % nqt;
     const int q0 = qt * kBT, nrows = min(kBT, a.Nq - q0);
     const int prow_first = pbase + q0, prow_last = prow_first + nrows - 1;
@@ -324,8 +324,9 @@ __global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(AttnParams a, Attn
     }
   }
   __syncthreads();
+  // a tile past the context or seen by no query tile has no slots: its rows
+  // are written as zeros
   const int n = (int)min(nl, 1024u);
-  if (n == 0) return;
   // thread: key 16 quarter + tid / 16, dims 8 (tid % 16) .. +7 of dK and of dV
   const int kr = 16 * quarter + (tid >> 4), dd = 8 * (tid & 15);
   const int64_t base = (int64_t)b * a.Hq * ntc * g.nslot;
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(AttnParams a, Attn
     }
   }
   const int j = t * kBT + kr;
-  if (j >= L) return;
+  if (j >= a.ctx) return;   // rows L .. ctx - 1 get zeros (no query sees them)
   float* dkr = g.dk + b * g.dks[0] + kvh * g.dks[1] + (int64_t)j * g.dks[2] + dd;
   float* dvr = g.dv + b * g.dvs[0] + kvh * g.dvs[1] + (int64_t)j * g.dvs[2] + dd;
 #pragma unroll
@@ -360,6 +361,14 @@ __global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(AttnParams a, Attn
     dvr[e] = av0[e];
     dvr[4 + e] = av1[e];
   }
+}
+
+// rows of dK/dV to zero before the backward: with workspace slots only the
+// global tiles' rows (the reduce kernel writes every other row, zeros
+// included), otherwise every row
+int attn_bwd_zero_rows(const AttnParams& a, const AttnBwd& g) {
+  if (!(attn_bwd_tile_ok(a) && g.part && attn_bwd_slots(a) > 0)) return a.ctx;
+  return min(a.ctx, (a.n_global + kBT - 1) / kBT * kBT);
 }
 
 // slots per band key tile: the band of a query tile spans at most

@@ -190,6 +190,7 @@ size_t attn_bwd_ws_bytes(const AttnParams& a);
 bool attn_bwd_tile_ok(const AttnParams& a);
 hipError_t launch_attn_bwd_tile(const AttnParams& a, const AttnBwd& g, hipStream_t st);
 int attn_bwd_slots(const AttnParams& a);   // slots per band key tile (0: no partials for this pattern)
+int attn_bwd_zero_rows(const AttnParams& a, const AttnBwd& g);   // dK/dV rows zeroed before the backward
 // three-branch NSA attention: compression (mode 5 over the pooled blocks),
 // selection (mode 3 without window), window (mode 2), combined by gates
 struct NsaParams {
