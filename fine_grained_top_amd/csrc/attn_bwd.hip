@@ -255,9 +255,12 @@ __global__ __launch_bounds__(256) void attn_bwd_tile_kernel(AttnParams a, AttnBw
           }
         }
       }
-      const int slot = last_tile - t;
-      if (g.part && t >= gt && slot < g.nslot) {
-        // band tile: this query tile's share into its slot ([key][dim] dK, then dV)
+      if (g.part && t >= gt) {
+        // band tile: this query tile's share into its slot ([key][dim] dK,
+        // then dV); the query tiles that see a band key tile are
+        // consecutive and at most nslot of them, so qt mod nslot tells
+        // them apart
+        const int slot = qt % g.nslot;
         float* pp = g.part + ((((int64_t)b * a.Hq + h) * ntc + t) * g.nslot + slot) * (kBT * kBD * 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -317,8 +320,8 @@ __global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(AttnParams a, Attn
     const int prow_first = pbase + q0, prow_last = prow_first + nrows - 1;
     const int last_tile = min(ntiles_all - 1, prow_last / kBT);
     const int wt = max(0, prow_first - a.window + 1) / kBT;
-    const int slot = last_tile - t;
-    if (prow_last >= 0 && t >= wt && t <= last_tile && slot < g.nslot) {
+    const int slot = qt % g.nslot;
+    if (prow_last >= 0 && t >= wt && t <= last_tile) {
       const uint32_t x = atomicAdd(&nl, 1u);
       if (x < 1024u) lst[x] = (uint32_t)(((hq * ntc + t) * g.nslot + slot));
     }
@@ -371,8 +374,11 @@ int attn_bwd_zero_rows(const AttnParams& a, const AttnBwd& g) {
   return min(a.ctx, (a.n_global + kBT - 1) / kBT * kBT);
 }
 
-// slots per band key tile: the band of a query tile spans at most
-// window / 64 + 3 key tiles (a query tile need not start on a key tile)
+// slots per band key tile: the query tiles that see a band key tile t have
+// their first positions P0 (64 apart) in [64 t - 63, 64 t + 62 + window],
+// so there are at most floor((125 + window) / 64) + 1 <= window / 64 + 3 of
+// them, consecutive (a query tile need not start on a key tile, and the
+// last one may be short)
 int attn_bwd_slots(const AttnParams& a) { return a.mode == 2 && a.stride == 0 ? a.window / kBT + 3 : 0; }
 
 bool attn_bwd_tile_ok(const AttnParams& a) {

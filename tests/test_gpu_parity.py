@@ -938,28 +938,31 @@ def _grads_oracle(q, k, v, dO, sets, ctx_len, Nq, scale):
     return dq, dk, dv
 
 
-@pytest.mark.parametrize("mode,dtype", [("window", "bf16"), ("window_wide", "bf16"), ("stride", "f32"),
+@pytest.mark.parametrize("mode,dtype", [("window", "bf16"), ("window_wide", "bf16"), ("window_long", "bf16"), ("stride", "f32"),
                                         ("index", "bf16"), ("blocks", "bf16"), ("dense", "f32"), ("dense", "bf16")])
 def test_attention_backward(mode, dtype):
     """dq, dk, dv over every selection mode, GQA, ragged lengths, against the
     oracle's gradients (float32 accumulation with float atomics). The bf16
     dense and window cases run the tiled kernel (query tiles of 64 rows, one
-    full and one ragged, over ragged key tiles), the others the per-row one."""
+    full and one ragged, over ragged key tiles), the others the per-row one.
+    window_long has room for 320 keys and requests of 300 and 130: a band key
+    tile that no query tile sees and key tiles past a request's length, whose
+    gradient rows are written as zeros by the slot reduce."""
     import oracle as orc
     sp = S()
     say(f"[gpu] backward {mode} {dtype}")
     g_ = torch.Generator().manual_seed(61)
-    B, Hq, Hkv, Nq, ctx = 2, 4, 2, 96, 160
+    B, Hq, Hkv, Nq, ctx = 2, 4, 2, 96, (320 if mode == "window_long" else 160)
     d = 128 if dtype == "bf16" else 64
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     q = torch.randn(B, Hq, Nq, d, generator=g_).to(tdt)
     k = torch.randn(B, Hkv, ctx, d, generator=g_).to(tdt)
     v = torch.randn(B, Hkv, ctx, d, generator=g_).to(tdt)
     dO = torch.randn(B, Hq, Nq, d, generator=g_)
-    ctx_len = [160, 130]
+    ctx_len = [300, 130] if mode == "window_long" else [160, 130]
     rng = np.random.default_rng(62)
     keep = []
-    if mode in ("window", "window_wide", "stride"):
+    if mode in ("window", "window_wide", "window_long", "stride"):
         w, gl, st = (70, 17, 0) if mode == "window_wide" else (20, 3, (7 if mode == "stride" else 0))
         sel = sp.selection(sp.SEL_WINDOW_GLOBAL, window=w, n_global=gl, stride=st)
         sets = lambda b, h, r, p: orc.window_global_set(p, w, gl, st)
