@@ -566,11 +566,14 @@ __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int 
   }
 }
 
-// merge splits: one workgroup of 128 threads per (b, r, gather group, head)
+// merge splits: one workgroup of 128 threads per (b, r, gather group, head).
+// Up to kCombineRegs splits, every thread loads every split's (max, sum)
+// pair and its own output element in one round (split indices past the last
+// are clamped and weighted 0, so no load waits on a condition) and merges in
+// registers; more splits take a loop.
+constexpr int kCombineRegs = 8;
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnParams a, int Hg, SplitInfo si,
                                                            const float* part) {
-  __shared__ float fw[256];
-  __shared__ float stat[2];
   const int ngg = a.Hq / Hg;
   const int rowid = blockIdx.x, hh = blockIdx.y;
   const int gg = rowid % ngg;
@@ -579,26 +582,37 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnParams a, int Hg,
   const int dd = threadIdx.x;
   const float* base = part + ((int64_t)rowid * si.nsplit * Hg + hh) * 130;
   const int64_t sstride = (int64_t)Hg * 130;
-  // split maxima and sums
-  float mv = -INFINITY, lv = 0.f;
-  if (dd < si.nsplit) {
-    mv = base[dd * sstride + 128];
-    lv = base[dd * sstride + 129];
+  float M = -INFINITY, Ls = 0.f, Os = 0.f;
+  if (si.nsplit <= kCombineRegs) {
+    float mv[kCombineRegs], lv[kCombineRegs], ov[kCombineRegs];
+#pragma unroll
+    for (int s = 0; s < kCombineRegs; ++s) {
+      const float* ps = base + min(s, si.nsplit - 1) * sstride;
+      mv[s] = ps[128];
+      lv[s] = ps[129];
+      ov[s] = ps[dd];
+    }
+#pragma unroll
+    for (int s = 0; s < kCombineRegs; ++s)
+      if (s < si.nsplit) M = fmaxf(M, mv[s]);
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int s = 0; s < kCombineRegs; ++s) {
+        const float f = (s < si.nsplit && mv[s] > -INFINITY) ? exp2f(mv[s] - M) : 0.f;
+        Ls += lv[s] * f;
+        Os += ov[s] * f;
+      }
+    }
+  } else {
+    for (int s = 0; s < si.nsplit; ++s) M = fmaxf(M, base[s * sstride + 128]);
+    if (M > -INFINITY)
+      for (int s = 0; s < si.nsplit; ++s) {
+        const float mv = base[s * sstride + 128];
+        const float f = mv > -INFINITY ? exp2f(mv - M) : 0.f;
+        Ls += base[s * sstride + 129] * f;
+        Os += base[s * sstride + dd] * f;
+      }
   }
-  float M = wave_max(mv);
-  if (dd >= 64) M = -INFINITY;        // second wave holds no splits when nsplit <= 64
-  if (dd == 0) stat[0] = M;
-  __syncthreads();
-  M = stat[0];
-  const float f = (dd < si.nsplit && mv > -INFINITY) ? exp2f(mv - M) : 0.f;
-  if (dd < si.nsplit) fw[dd] = f;
-  float Lp = wave_sum(f * lv);
-  if (dd == 0) stat[1] = Lp;
-  __syncthreads();
-  const float Ls = stat[1];
-  float Os = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < si.nsplit; ++s) Os += base[s * sstride + dd] * fw[s];
   const int h = gg * Hg + hh;
   float* o = a.o + b * a.os[0] + h * a.os[1] + r * a.os[2];
   o[dd] = (M > -INFINITY && Ls > 0.f) ? Os / Ls : 0.f;
