@@ -83,6 +83,13 @@ has one value whatever order a machine sums in, which is what makes index sets
 comparable bit for bit. It is obtained by a certified float64 evaluation (the
 float32 rounding of every point of a rigorous error interval agrees) and, when
 that fails, by exact rational arithmetic.
+
+Pins (tests/test_oracle_pins.py and the fixtures in tests/golden/): index
+sets against exact brute force, hand-worked cases and closed forms; masked
+attention against torch's scaled-dot-product attention with the same mask;
+gradients against torch autograd in float64. The pages print no worked
+attention outputs, so the outputs O of the bf16 workloads are parity
+unpinned beyond this definition and those identities.
 """
 from __future__ import annotations
 
