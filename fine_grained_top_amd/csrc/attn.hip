@@ -399,13 +399,20 @@ __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int 
     for (int v = 1; v < 8; ++v) tm = fmaxf(tm, z[v]);
     tm = rows4_max(tm);
     const float mn = fmaxf(m, tm);
+    // lazy rescale: P is formed against the reference maximum m, which moves
+    // (rescaling O and l) only when some head's maximum has grown past it by
+    // more than 8 (log2 units), so P stays below 2^8 (exact in the bf16
+    // hi/lo pair as before, far from float32 overflow); the branch is the
+    // same for the whole wave, and after the first tiles it is rarely taken
+    const bool up = __any(mn > m + 8.f);
+    const float mr = up ? mn : m;
     float alpha = 1.f, ps = 0.f;
     float pv[8];
-    if (mn > -INFINITY) {
-      alpha = exp2f(m - mn);
+    if (mr > -INFINITY) {
+      if (up) alpha = exp2f(m - mr);
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
-        pv[v] = exp2f(z[v] - mn);
+        pv[v] = exp2f(z[v] - mr);
         ps += pv[v];
       }
     } else {
@@ -414,12 +421,12 @@ __global__ __launch_bounds__(256) void attn_index_mfma_kernel(AttnParams a, int 
     }
     ps = rows4_sum(ps);
     l = l * alpha + ps;
-    m = mn;
+    m = mr;
     // rescale O: lane holds rows (heads) 4*qq + v; alpha of head hh lives in
     // lane hh (read with readlane, then picked by the lane's row group; with
     // PACKLO rows 8..15 repeat heads 0..7)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < 4 && up; ++v) {
       const float a0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), v));
       const float a1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), 4 + v));
       float av;
