@@ -267,12 +267,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       }
       tm = rows4_max(tm);
       const float mn = fmaxf(m, tm);
+      // lazy rescale: P is formed against the reference maximum m, which
+      // moves (rescaling O and l) only when some row's maximum has grown past
+      // it by more than 8 (log2 units), so P stays below 2^8 (exact in the
+      // bf16 hi/lo pair, far from float32 overflow); the branch is the same
+      // for the whole wave and rarely taken after the first tiles
+      const bool up = __any(mn > m + 8.f);
+      const float mr = up ? mn : m;
       float alpha = 1.f, ps = 0.f;
-      if (mn > -INFINITY) {
-        alpha = exp2f(m - mn);
+      if (mr > -INFINITY) {
+        if (up) alpha = exp2f(m - mr);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          z[i] = exp2f(z[i] - mn);
+          z[i] = exp2f(z[i] - mr);
           ps += z[i];
         }
       } else {
@@ -281,9 +288,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       }
       ps = rows4_sum(ps);
       l = l * alpha + ps;
-      m = mn;
+      m = mr;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
+      for (int v = 0; v < 4 && up; ++v) {
         // alpha of row r lives in lane r: four readlanes, picked by the lane's row group
         const int ai = __builtin_bit_cast(int, alpha);
         const float a0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ai, v));
