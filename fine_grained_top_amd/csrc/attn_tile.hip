@@ -271,8 +271,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       // moves (rescaling O and l) only when some row's maximum has grown past
       // it by more than 8 (log2 units), so P stays below 2^8 (exact in the
       // bf16 hi/lo pair, far from float32 overflow); the branch is the same
-      // for the whole wave and rarely taken after the first tiles
-      const bool up = __any(mn > m + 8.f);
+      // for the whole wave and rarely taken after the first tiles. The split
+      // compressed-entry instance keeps the per-tile rescale: the lazy form
+      // costs it registers and an occupancy step.
+      constexpr bool kLazy = !(MODE == 5 && SPLIT);
+      const bool up = kLazy ? __any(mn > m + 8.f) : true;
       const float mr = up ? mn : m;
       float alpha = 1.f, ps = 0.f;
       if (mr > -INFINITY) {
